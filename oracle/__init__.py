@@ -1,0 +1,308 @@
+"""CPU oracle for the rotate-then-quantize KV-cache path (test infrastructure).
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg use this
+package.  It wraps ``kvq_oracle.c`` (plain C, IEEE double) through ctypes and
+shares no code with the GPU library.  See the header of ``kvq_oracle.c`` for the
+page sections each routine follows.
+
+Array conventions: fp16 inputs are widened exactly to float64 here; codes are
+packed LSB-first per vector (coordinate i in bits [b*i, b*i+b)).
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kvq_oracle.c")
+_LIB = os.path.join(_HERE, "libkvq_oracle.so")
+
+BAND = 1e-5  # decision-boundary band inside which code mismatches are allowed
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (fast; no GPU needed)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        _lib = C.CDLL(build())
+        _setup(_lib)
+    return _lib
+
+
+_D = C.POINTER(C.c_double)
+_F = C.POINTER(C.c_float)
+_U8 = C.POINTER(C.c_uint8)
+_I8 = C.POINTER(C.c_int8)
+_I32 = C.POINTER(C.c_int32)
+_I64 = C.POINTER(C.c_int64)
+i64 = C.c_int64
+
+
+def _setup(L):
+    L.kvqo_lloyd_max.argtypes = [C.c_int, _D, C.c_int, C.c_double, _D, C.POINTER(C.c_int)]
+    L.kvqo_gauss_mse.argtypes = [C.c_int, _D, _D]
+    L.kvqo_gauss_mse.restype = C.c_double
+    L.kvqo_tables_f32.argtypes = [C.c_int, _F, _F]
+    L.kvqo_hadamard_entry.argtypes = [C.c_int, C.c_int]
+    L.kvqo_hadamard_dense.argtypes = [_D, _D, C.c_int]
+    L.kvqo_fwht.argtypes = [_D, C.c_int]
+    L.kvqo_pack.argtypes = [_I32, C.c_int, C.c_int, _U8]
+    L.kvqo_unpack.argtypes = [_U8, C.c_int, C.c_int, _I32]
+    L.kvqo_scalar_quantize.argtypes = [_D, i64, C.c_int, _F, _F, _I32, _D]
+    L.kvqo_quantize.argtypes = [C.c_int, C.c_int, i64, i64, i64, _D, _I8, _F, C.c_double,
+                                _U8, _D, _D, _I32, _U8]
+    L.kvqo_dequant.argtypes = [C.c_int, C.c_int, _U8, C.c_double, _I8, _F, _D]
+    L.kvqo_logits.argtypes = [C.c_int, C.c_int, C.c_int, i64, i64, i64, i64, _D, _U8, _D, _I8,
+                              _F, _U8, _D, _D, C.c_int, _D]
+    L.kvqo_attention.argtypes = [C.c_int, C.c_int, i64, i64, i64, i64, _D, _U8, _D, _U8, _D,
+                                 _I8, _I8, _F, C.c_double, _D]
+    L.kvqo_qjl.argtypes = [C.c_int, C.c_int, i64, _D, _I32, _F, _D, C.c_double, _U8, _D, _U8]
+    L.kvqo_nsn_vq.argtypes = [C.c_int, C.c_int, C.c_int, i64, i64, _D, _D, C.c_double, _U8, _D,
+                              _D, _D, _D, _U8]
+    L.kvqo_nsn_reconstruct.argtypes = [C.c_int, _D, C.c_double, C.c_double, _D, _D]
+    L.kvqo_kmeans.argtypes = [i64, C.c_int, C.c_int, _D, _I64, C.c_int, _D, _D]
+    L.kvqo_kmeans.restype = C.c_int
+
+
+def _p(a, ty):
+    return a.ctypes.data_as(ty) if a is not None else None
+
+
+def _f64(a):
+    return np.ascontiguousarray(np.asarray(a), dtype=np.float64)
+
+
+def _chk(rc):
+    if rc != 0:
+        raise ValueError("oracle routine rejected its arguments (rc=%d)" % rc)
+
+
+# --------------------------------------------------------------------------- tables
+def lloyd_max(bits: int, init=None, max_iter: int = 1_000_000, tol: float = 1e-13):
+    """Fixed point of Lloyd's conditions for N(0,1); returns (centroids, iterations)."""
+    L = 1 << bits
+    c = np.zeros(L)
+    it = C.c_int(0)
+    ini = None if init is None else _f64(init)
+    _chk(lib().kvqo_lloyd_max(bits, _p(ini, _D), max_iter, tol, _p(c, _D), C.byref(it)))
+    return c, it.value
+
+
+def gauss_mse(bits: int, c, t) -> float:
+    return lib().kvqo_gauss_mse(bits, _p(_f64(c), _D), _p(_f64(t), _D))
+
+
+def tables_f32(bits: int):
+    """Canonical fp32 centroids [2^b] and thresholds [2^b - 1]."""
+    L = 1 << bits
+    c = np.zeros(L, np.float32)
+    t = np.zeros(L - 1, np.float32)
+    _chk(lib().kvqo_tables_f32(bits, _p(c, _F), _p(t, _F)))
+    return c, t
+
+
+# --------------------------------------------------------------------------- Hadamard
+def hadamard_dense(x):
+    x = _f64(x)
+    y = np.zeros_like(x)
+    lib().kvqo_hadamard_dense(_p(x, _D), _p(y, _D), x.shape[0])
+    return y
+
+
+def hadamard_matrix(n: int):
+    return np.array([[lib().kvqo_hadamard_entry(i, j) for j in range(n)] for i in range(n)],
+                    dtype=np.int64)
+
+
+def fwht(x):
+    y = _f64(x).copy()
+    lib().kvqo_fwht(_p(y, _D), y.shape[0])
+    return y
+
+
+# --------------------------------------------------------------------------- packing
+def pack(idx, bits: int):
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    d = idx.shape[-1]
+    flat = idx.reshape(-1, d)
+    out = np.zeros((flat.shape[0], d * bits // 8), np.uint8)
+    for v in range(flat.shape[0]):
+        row = np.ascontiguousarray(flat[v])
+        rec = np.zeros(d * bits // 8, np.uint8)
+        lib().kvqo_pack(_p(row, _I32), d, bits, _p(rec, _U8))
+        out[v] = rec
+    return out.reshape(idx.shape[:-1] + (d * bits // 8,))
+
+
+def unpack(codes, d: int, bits: int):
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    rec = d * bits // 8
+    flat = codes.reshape(-1, rec)
+    out = np.zeros((flat.shape[0], d), np.int32)
+    for v in range(flat.shape[0]):
+        r = np.ascontiguousarray(flat[v])
+        o = np.zeros(d, np.int32)
+        lib().kvqo_unpack(_p(r, _U8), d, bits, _p(o, _I32))
+        out[v] = o
+    return out.reshape(codes.shape[:-1] + (d,))
+
+
+def scalar_quantize(y, bits: int):
+    c, t = tables_f32(bits)
+    y = _f64(y).ravel()
+    idx = np.zeros(y.size, np.int32)
+    yh = np.zeros(y.size)
+    lib().kvqo_scalar_quantize(_p(y, _D), y.size, bits, _p(c, _F), _p(t, _F), _p(idx, _I32),
+                               _p(yh, _D))
+    return idx, yh
+
+
+# --------------------------------------------------------------------------- quantize
+def quantize(x, signs, bits: int, band: float = BAND, want_y: bool = False):
+    """x [B,H,T,d] (any float dtype; fp16 widened exactly); signs [H,d] (+-1).
+
+    Returns dict(codes [B,H,T,d*b/8] u8, norms [B,H,T] f64, idx [B,H,T,d],
+    flags [B,H,T,d] u8, y [B,H,T,d] (rotated coordinates) if want_y)."""
+    x = _f64(x)
+    B, H, T, d = x.shape
+    signs = np.ascontiguousarray(signs, dtype=np.int8)
+    assert signs.shape == (H, d)
+    _, t = tables_f32(bits)
+    codes = np.zeros((B, H, T, d * bits // 8), np.uint8)
+    norms = np.zeros((B, H, T))
+    idx = np.zeros((B, H, T, d), np.int32)
+    flags = np.zeros((B, H, T, d), np.uint8)
+    y = np.zeros((B, H, T, d)) if want_y else None
+    _chk(lib().kvqo_quantize(d, bits, B, H, T, _p(x, _D), _p(signs, _I8), _p(t, _F), band,
+                             _p(codes, _U8), _p(norms, _D), _p(y, _D), _p(idx, _I32),
+                             _p(flags, _U8)))
+    out = dict(codes=codes, norms=norms, idx=idx, flags=flags)
+    if want_y:
+        out["y"] = y
+    return out
+
+
+def dequant(rec, rho, signs_row, bits: int, d: int = 128):
+    c, _ = tables_f32(bits)
+    rec = np.ascontiguousarray(rec, dtype=np.uint8)
+    s = np.ascontiguousarray(signs_row, dtype=np.int8)
+    out = np.zeros(d)
+    lib().kvqo_dequant(d, bits, _p(rec, _U8), float(rho), _p(s, _I8), _p(c, _F), _p(out, _D))
+    return out
+
+
+def logits(q, codes, norms, signs, bits: int, route: int = 1, qjl_signs=None, gamma=None,
+           S=None):
+    """q [B,Hq,d]; codes [B,Hkv,T,rec]; norms [B,Hkv,T]; signs [Hkv,d] -> [B,Hq,T]."""
+    q = _f64(q)
+    B, Hq, d = q.shape
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    _, Hkv, T, _ = codes.shape
+    norms = _f64(norms)
+    signs = np.ascontiguousarray(signs, dtype=np.int8)
+    c, _ = tables_f32(bits)
+    out = np.zeros((B, Hq, T))
+    m = 0
+    if qjl_signs is not None:
+        qjl_signs = np.ascontiguousarray(qjl_signs, dtype=np.uint8)
+        gamma = _f64(gamma)
+        S = _f64(S)
+        m = S.shape[0]
+    _chk(lib().kvqo_logits(route, d, bits, B, Hq, Hkv, T, _p(q, _D), _p(codes, _U8),
+                           _p(norms, _D), _p(signs, _I8), _p(c, _F), _p(qjl_signs, _U8),
+                           _p(gamma, _D), _p(S, _D), m, _p(out, _D)))
+    return out
+
+
+def attention(q, kc, kn, vc, vn, signs_k, signs_v, bits: int, sm_scale: float | None = None):
+    q = _f64(q)
+    B, Hq, d = q.shape
+    kc = np.ascontiguousarray(kc, dtype=np.uint8)
+    vc = np.ascontiguousarray(vc, dtype=np.uint8)
+    _, Hkv, T, _ = kc.shape
+    kn, vn = _f64(kn), _f64(vn)
+    sk = np.ascontiguousarray(signs_k, dtype=np.int8)
+    sv = np.ascontiguousarray(signs_v, dtype=np.int8)
+    c, _ = tables_f32(bits)
+    if sm_scale is None:
+        sm_scale = 1.0 / np.sqrt(d)
+    out = np.zeros((B, Hq, d))
+    _chk(lib().kvqo_attention(d, bits, B, Hq, Hkv, T, _p(q, _D), _p(kc, _U8), _p(kn, _D),
+                              _p(vc, _U8), _p(vn, _D), _p(sk, _I8), _p(sv, _I8), _p(c, _F),
+                              float(sm_scale), _p(out, _D)))
+    return out
+
+
+def qjl(y, idx, S, bits: int, band: float = BAND):
+    """y, idx [..., d]; S [m, d] -> dict(signs [..., m/8] u8, gamma [...], flags [..., m])."""
+    y = _f64(y)
+    d = y.shape[-1]
+    lead = y.shape[:-1]
+    n = int(np.prod(lead))
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    S = _f64(S)
+    m = S.shape[0]
+    c, _ = tables_f32(bits)
+    sg = np.zeros((n, m // 8), np.uint8)
+    gm = np.zeros(n)
+    fl = np.zeros((n, m), np.uint8)
+    _chk(lib().kvqo_qjl(d, m, n, _p(y, _D), _p(idx, _I32), _p(c, _F), _p(S, _D), band,
+                        _p(sg, _U8), _p(gm, _D), _p(fl, _U8)))
+    return dict(signs=sg.reshape(lead + (m // 8,)), gamma=gm.reshape(lead),
+                flags=fl.reshape(lead + (m,)))
+
+
+def nsn_vq(x, codebook, band: float = BAND, want_z: bool = False):
+    """x [H,T,d]; codebook [K, sub] -> dict(codes [H,T,d/sub], s1, s2 [H,T], o [H,d], flags)."""
+    x = _f64(x)
+    H, T, d = x.shape
+    cb = _f64(codebook)
+    K, sub = cb.shape
+    codes = np.zeros((H, T, d // sub), np.uint8)
+    s1 = np.zeros((H, T))
+    s2 = np.zeros((H, T))
+    o = np.zeros((H, d))
+    z = np.zeros((H, T, d)) if want_z else None
+    fl = np.zeros((H, T, d // sub), np.uint8)
+    _chk(lib().kvqo_nsn_vq(d, sub, K, H, T, _p(x, _D), _p(cb, _D), band, _p(codes, _U8),
+                           _p(s1, _D), _p(s2, _D), _p(o, _D), _p(z, _D), _p(fl, _U8)))
+    out = dict(codes=codes, s1=s1, s2=s2, o=o, flags=fl)
+    if want_z:
+        out["z"] = z
+    return out
+
+
+def nsn_reconstruct(zq, s1, s2, o):
+    zq = _f64(zq)
+    o = _f64(o)
+    d = zq.shape[0]
+    out = np.zeros(d)
+    lib().kvqo_nsn_reconstruct(d, _p(zq, _D), float(s1), float(s2), _p(o, _D), _p(out, _D))
+    return out
+
+
+def kmeans(samples, init_idx, max_iter: int = 100):
+    """Lloyd's k-means; returns (codebook [K, dim], distortion per pass, passes)."""
+    s = _f64(samples)
+    n, dim = s.shape
+    init_idx = np.ascontiguousarray(init_idx, dtype=np.int64)
+    K = init_idx.shape[0]
+    cb = np.zeros((K, dim))
+    dist = np.zeros(max_iter)
+    it = lib().kvqo_kmeans(n, dim, K, _p(s, _D), _p(init_idx, _I64), max_iter, _p(cb, _D),
+                           _p(dist, _D))
+    return cb, dist[:it], it

@@ -1,0 +1,631 @@
+/*
+ * kvq_oracle.c -- plain, slow CPU reference of the rotate-then-quantize KV
+ * cache path.  TEST INFRASTRUCTURE ONLY: it is built and called by the tests,
+ * by the smoke check and by the CPU-baseline leg of the benchmark, never by the
+ * library.  It shares no source, header, table or constant with the GPU path.
+ *
+ * All arithmetic is IEEE double.  Inputs arrive as doubles (fp16 inputs are
+ * widened exactly by the caller).  Every routine follows the step order of
+ * the method as the pages state it; no blocking, fusion or reordering.
+ *
+ * Sources (page title / section):
+ *  - "PolarQuant: Optimal Gaussian Weight Quantization via Hadamard Rotation"
+ *    (gist.science 2603.29078), Technical summary sec. 2 "Methodology":
+ *    block L2 normalisation keeping the norm r_i, normalised Walsh-Hadamard
+ *    rotation, scaling to unit variance, Lloyd-Max centroids for N(0,1);
+ *    dequantisation = centroid lookup, scale, Hadamard (self-inverse), norm.
+ *  - "O Que E TurboQuant?" (a2a-mcp.org), "Como Funciona", Stage 1 (random
+ *    rotation, per-coordinate Lloyd-Max codes) and Stage 2 (1-bit QJL sign
+ *    residual that corrects inner-product bias); "Como Implementar" (codebooks
+ *    precomputed per dimension and bit width; query rotated once, scores read
+ *    from the indices).
+ *  - "NSNQuant: A Double Normalization Approach ..." (gist.science
+ *    2505.18231), Technical summary "Metodologia" sec. 1 (Normalize-Shift-
+ *    Normalize with byproducts s1, o, s2), sec. 2 (Hadamard), sec. 3 (one
+ *    global codebook for N(0,1), k-means on synthetic normal samples).
+ *
+ * Readings where the pages are silent (each also listed in the design notes):
+ *  rotation y = H (D .* u) with the unnormalised +-1 Sylvester matrix
+ *  H_ij = (-1)^popcount(i&j) on the unit vector u, which gives coordinates of
+ *  unit variance; bucket index = #{j : t_j < y}; codes packed LSB-first per
+ *  vector (coordinate i in bits [b*i, b*i+b)); zero vector -> u = 0.
+ */
+#define _DEFAULT_SOURCE
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_API __attribute__((visibility("default")))
+
+/* ------------------------------------------------------------------------ */
+/* Standard normal density and probability mass                              */
+/* ------------------------------------------------------------------------ */
+
+static double npdf(double x)
+{
+    if (isinf(x)) return 0.0;
+    return exp(-0.5 * x * x) / sqrt(2.0 * M_PI);
+}
+
+/* P(a < X < b) for X ~ N(0,1), written so that tail masses do not cancel. */
+static double nmass(double a, double b)
+{
+    const double r2 = sqrt(2.0);
+    if (a >= 0.0) return 0.5 * (erfc(a / r2) - erfc(b / r2));
+    if (b <= 0.0) return 0.5 * (erfc(-b / r2) - erfc(-a / r2));
+    return 1.0 - 0.5 * erfc(-a / r2) - 0.5 * erfc(b / r2);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Lloyd-Max scalar quantiser for N(0,1)                                      */
+/* Lloyd's two optimality conditions iterated to their fixed point:           */
+/*   thresholds t_j = (c_j + c_{j+1}) / 2                                     */
+/*   centroids  c_j = E[X | t_{j-1} < X < t_j]                                */
+/*             = (phi(t_{j-1}) - phi(t_j)) / (Phi(t_j) - Phi(t_{j-1}))        */
+/* ------------------------------------------------------------------------ */
+
+ORC_API int kvqo_lloyd_max(int bits, const double *init, int max_iter, double tol,
+                           double *c_out, int *iters_out)
+{
+    if (bits < 1 || bits > 8) return -1;
+    const int L = 1 << bits;
+    double *c = (double *)malloc(sizeof(double) * L);
+    double *t = (double *)malloc(sizeof(double) * (L + 1));
+    for (int j = 0; j < L; ++j)
+        c[j] = init ? init[j] : (-2.5 + 5.0 * (j + 0.5) / L);
+    int it = 0;
+    for (; it < max_iter; ++it) {
+        t[0] = -INFINITY;
+        t[L] = INFINITY;
+        for (int j = 1; j < L; ++j) t[j] = 0.5 * (c[j - 1] + c[j]);
+        double delta = 0.0;
+        for (int j = 0; j < L; ++j) {
+            double m = nmass(t[j], t[j + 1]);
+            double cn = (npdf(t[j]) - npdf(t[j + 1])) / m;
+            double dd = fabs(cn - c[j]);
+            if (dd > delta) delta = dd;
+            c[j] = cn;
+        }
+        if (delta < tol) { ++it; break; }
+    }
+    memcpy(c_out, c, sizeof(double) * L);
+    if (iters_out) *iters_out = it;
+    free(c);
+    free(t);
+    return 0;
+}
+
+/* Mean squared error of a scalar quantiser (levels c, decision thresholds t
+ * between them) on N(0,1), by the exact integral per cell:
+ *   int_a^b (x-c)^2 phi = (1+c^2) dPhi - 2c (phi(a)-phi(b)) + a phi(a) - b phi(b)
+ */
+ORC_API double kvqo_gauss_mse(int bits, const double *c, const double *t)
+{
+    const int L = 1 << bits;
+    double mse = 0.0;
+    for (int j = 0; j < L; ++j) {
+        double a = (j == 0) ? -INFINITY : t[j - 1];
+        double b = (j == L - 1) ? INFINITY : t[j];
+        double pa = npdf(a), pb = npdf(b);
+        double apa = isinf(a) ? 0.0 : a * pa;
+        double bpb = isinf(b) ? 0.0 : b * pb;
+        mse += (1.0 + c[j] * c[j]) * nmass(a, b) - 2.0 * c[j] * (pa - pb) + apa - bpb;
+    }
+    return mse;
+}
+
+/* Canonical stored tables: centroids rounded to fp32; thresholds are the
+ * fp32 rounding of the midpoint of adjacent fp32 centroids (computed in
+ * double, where the sum of two floats is exact). */
+ORC_API int kvqo_tables_f32(int bits, float *c32, float *t32)
+{
+    const int L = 1 << bits;
+    double c[256];
+    int rc = kvqo_lloyd_max(bits, NULL, 1000000, 1e-13, c, NULL);
+    if (rc) return rc;
+    for (int j = 0; j < L; ++j) c32[j] = (float)c[j];
+    for (int j = 0; j + 1 < L; ++j)
+        t32[j] = (float)(((double)c32[j] + (double)c32[j + 1]) * 0.5);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Walsh-Hadamard                                                             */
+/* ------------------------------------------------------------------------ */
+
+static int popcount_u32(uint32_t v)
+{
+    int n = 0;
+    while (v) { n += (int)(v & 1u); v >>= 1; }
+    return n;
+}
+
+/* Dense Sylvester matrix entry H_ij = (-1)^popcount(i & j). */
+ORC_API int kvqo_hadamard_entry(int i, int j)
+{
+    return (popcount_u32((uint32_t)(i & j)) & 1) ? -1 : 1;
+}
+
+/* y = H x with the dense matrix (n^2 work). */
+ORC_API void kvqo_hadamard_dense(const double *x, double *y, int n)
+{
+    for (int i = 0; i < n; ++i) {
+        double s = 0.0;
+        for (int j = 0; j < n; ++j) s += kvqo_hadamard_entry(i, j) * x[j];
+        y[i] = s;
+    }
+}
+
+/* In-place fast transform: log2(n) butterfly stages, natural order.  Gives
+ * the same vector as kvqo_hadamard_dense. */
+ORC_API void kvqo_fwht(double *x, int n)
+{
+    for (int h = 1; h < n; h <<= 1)
+        for (int i = 0; i < n; i += 2 * h)
+            for (int j = i; j < i + h; ++j) {
+                double a = x[j], b = x[j + h];
+                x[j] = a + b;
+                x[j + h] = a - b;
+            }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Bit packing: LSB-first stream per vector.                                  */
+/* ------------------------------------------------------------------------ */
+
+ORC_API void kvqo_pack(const int32_t *idx, int d, int bits, uint8_t *rec)
+{
+    memset(rec, 0, (size_t)(d * bits + 7) / 8);
+    for (int i = 0; i < d; ++i)
+        for (int k = 0; k < bits; ++k) {
+            int p = i * bits + k;
+            if ((idx[i] >> k) & 1) rec[p / 8] |= (uint8_t)(1u << (p % 8));
+        }
+}
+
+ORC_API void kvqo_unpack(const uint8_t *rec, int d, int bits, int32_t *idx)
+{
+    for (int i = 0; i < d; ++i) {
+        int v = 0;
+        for (int k = 0; k < bits; ++k) {
+            int p = i * bits + k;
+            v |= ((rec[p / 8] >> (p % 8)) & 1) << k;
+        }
+        idx[i] = v;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Scalar bucketisation against thresholds t[0..L-2]: idx = #{j : t_j < y}.   */
+/* flag = 1 when y lies within `band` of any threshold.                       */
+/* ------------------------------------------------------------------------ */
+
+static int bucket(double y, const double *t, int L, double band, int *flag)
+{
+    int idx = 0;
+    int f = 0;
+    for (int j = 0; j + 1 < L; ++j) {
+        if (t[j] < y) ++idx;
+        if (fabs(y - t[j]) < band) f = 1;
+    }
+    if (flag) *flag = f;
+    return idx;
+}
+
+/* Quantise an array of scalars with a given fp32 table (for MSE checks). */
+ORC_API void kvqo_scalar_quantize(const double *y, int64_t n, int bits, const float *c32,
+                                  const float *t32, int32_t *idx, double *yhat)
+{
+    const int L = 1 << bits;
+    double t[255];
+    for (int j = 0; j + 1 < L; ++j) t[j] = t32[j];
+    for (int64_t i = 0; i < n; ++i) {
+        int k = bucket(y[i], t, L, 0.0, NULL);
+        if (idx) idx[i] = k;
+        if (yhat) yhat[i] = c32[k];
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Quantise KV vectors (MSE codes).                                           */
+/* x: [B, H, T, d]; signs: [H, d] (+-1), the random diagonal D of the head.   */
+/* Per vector: rho = ||x||; u = x / rho (u = 0 if rho = 0); y = H (D .* u);   */
+/* idx_i = #{j : t_j < y_i}; packed record of d*bits/8 bytes.                 */
+/* Outputs (any may be NULL except codes/norms): rotated y [.., d], idx       */
+/* [.., d], flags [.., d] (1 = within `band` of a threshold).                 */
+/* ------------------------------------------------------------------------ */
+
+ORC_API int kvqo_quantize(int d, int bits, int64_t B, int64_t H, int64_t T,
+                          const double *x, const int8_t *signs, const float *t32,
+                          double band, uint8_t *codes, double *norms, double *y_out,
+                          int32_t *idx_out, uint8_t *flags)
+{
+    if (d <= 0 || (d & (d - 1)) || bits < 1 || bits > 8) return -1;
+    const int L = 1 << bits;
+    const int rec = d * bits / 8;
+    double t[255];
+    for (int j = 0; j + 1 < L; ++j) t[j] = t32[j];
+    double *u = (double *)malloc(sizeof(double) * d);
+    int32_t *idx = (int32_t *)malloc(sizeof(int32_t) * d);
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t h = 0; h < H; ++h)
+            for (int64_t tt = 0; tt < T; ++tt) {
+                int64_t v = (b * H + h) * T + tt;
+                const double *xv = x + v * d;
+                double ss = 0.0;
+                for (int i = 0; i < d; ++i) ss += xv[i] * xv[i];
+                double rho = sqrt(ss);
+                for (int i = 0; i < d; ++i) {
+                    double ui = (rho > 0.0) ? xv[i] / rho : 0.0;
+                    u[i] = signs[h * d + i] * ui;
+                }
+                kvqo_fwht(u, d);
+                for (int i = 0; i < d; ++i) {
+                    int f = 0;
+                    idx[i] = bucket(u[i], t, L, band, &f);
+                    if (flags) flags[v * d + i] = (uint8_t)f;
+                    if (y_out) y_out[v * d + i] = u[i];
+                    if (idx_out) idx_out[v * d + i] = idx[i];
+                }
+                norms[v] = rho;
+                kvqo_pack(idx, d, bits, codes + v * rec);
+            }
+    free(u);
+    free(idx);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Dequantisation (PolarQuant, Methodology: centroid lookup, Hadamard is its  */
+/* own inverse up to d, restore the norm):                                    */
+/*   k_hat = rho * D .* (H c[idx]) / d                                        */
+/* ------------------------------------------------------------------------ */
+
+ORC_API void kvqo_dequant(int d, int bits, const uint8_t *rec, double rho,
+                          const int8_t *signs, const float *c32, double *out)
+{
+    int32_t idx[1024];
+    kvqo_unpack(rec, d, bits, idx);
+    for (int i = 0; i < d; ++i) out[i] = c32[idx[i]];
+    kvqo_fwht(out, d);
+    for (int i = 0; i < d; ++i) out[i] = rho * signs[i] * out[i] / d;
+}
+
+/* QJL residual reconstruction added to a dequantised key:                    */
+/*   r_hat = gamma * sqrt(pi/2) / m * S^T sgn,  k_hat += rho * D .* H r_hat / sqrt(d) */
+static void qjl_dequant_add(int d, int m, const uint8_t *sg, double gamma, double rho,
+                            const int8_t *signs, const double *S, double *k)
+{
+    double *r = (double *)calloc((size_t)d, sizeof(double));
+    const double coef = gamma * sqrt(M_PI / 2.0) / m;
+    for (int j = 0; j < m; ++j) {
+        double s = ((sg[j / 8] >> (j % 8)) & 1) ? 1.0 : -1.0;
+        for (int i = 0; i < d; ++i) r[i] += coef * s * S[(int64_t)j * d + i];
+    }
+    kvqo_fwht(r, d);
+    for (int i = 0; i < d; ++i) k[i] += rho * signs[i] * r[i] / sqrt((double)d);
+    free(r);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Logits <q_h, k_t> for grouped-query heads: q head h reads KV head          */
+/* g = h / (Hq / Hkv).  Two independent routes:                               */
+/*  route 0: dequantise every key, then a plain dot product;                  */
+/*  route 1: rotate the query once, q' = H (D .* q), and score against the    */
+/*           centroids directly: rho <q', c[idx]> / d  (+ QJL term           */
+/*           rho gamma sqrt(pi/2)/m sum_j sgn_j (S q')_j / sqrt(d)).           */
+/* q: [B, Hq, d]; codes [B, Hkv, T, rec]; norms [B, Hkv, T];                   */
+/* qjl_signs [B, Hkv, T, m/8] and gamma [B, Hkv, T] or NULL; S [m, d].         */
+/* logits: [B, Hq, T].                                                        */
+/* ------------------------------------------------------------------------ */
+
+ORC_API int kvqo_logits(int route, int d, int bits, int64_t B, int64_t Hq, int64_t Hkv,
+                        int64_t T, const double *q, const uint8_t *codes, const double *norms,
+                        const int8_t *signs, const float *c32, const uint8_t *qjl_signs,
+                        const double *gamma, const double *S, int m, double *logits)
+{
+    if (Hkv <= 0 || Hq % Hkv) return -1;
+    const int64_t G = Hq / Hkv;
+    const int rec = d * bits / 8;
+    double *kh = (double *)malloc(sizeof(double) * d);
+    double *qr = (double *)malloc(sizeof(double) * d);
+    double *pq = (double *)malloc(sizeof(double) * (m > 0 ? m : 1));
+    int32_t *idx = (int32_t *)malloc(sizeof(int32_t) * d);
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t h = 0; h < Hq; ++h) {
+            const int64_t g = h / G;
+            const double *qh = q + (b * Hq + h) * d;
+            const int8_t *sg = signs + g * d;
+            if (route == 1) {
+                for (int i = 0; i < d; ++i) qr[i] = sg[i] * qh[i];
+                kvqo_fwht(qr, d);
+                if (qjl_signs)
+                    for (int j = 0; j < m; ++j) {
+                        double s = 0.0;
+                        for (int i = 0; i < d; ++i) s += S[(int64_t)j * d + i] * qr[i];
+                        pq[j] = s / sqrt((double)d);
+                    }
+            }
+            for (int64_t t = 0; t < T; ++t) {
+                const int64_t v = (b * Hkv + g) * T + t;
+                double acc = 0.0;
+                if (route == 0) {
+                    kvqo_dequant(d, bits, codes + v * rec, norms[v], sg, c32, kh);
+                    if (qjl_signs)
+                        qjl_dequant_add(d, m, qjl_signs + v * (m / 8), gamma[v], norms[v], sg, S, kh);
+                    for (int i = 0; i < d; ++i) acc += qh[i] * kh[i];
+                } else {
+                    kvqo_unpack(codes + v * rec, d, bits, idx);
+                    for (int i = 0; i < d; ++i) acc += qr[i] * c32[idx[i]];
+                    acc *= norms[v] / d;
+                    if (qjl_signs) {
+                        const uint8_t *sv = qjl_signs + v * (m / 8);
+                        double s = 0.0;
+                        for (int j = 0; j < m; ++j)
+                            s += (((sv[j / 8] >> (j % 8)) & 1) ? 1.0 : -1.0) * pq[j];
+                        acc += norms[v] * gamma[v] * sqrt(M_PI / 2.0) / m * s;
+                    }
+                }
+                logits[(b * Hq + h) * T + t] = acc;
+            }
+        }
+    free(kh);
+    free(qr);
+    free(pq);
+    free(idx);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Decode attention over the quantised cache, by definition: dequantise each  */
+/* key and value, logits <q, k_hat>, softmax with scale sm_scale (two passes: */
+/* maximum, then exponentials), output = sum_t w_t v_hat_t / sum_t w_t.       */
+/* q [B,Hq,d]; k/v codes [B,Hkv,T,rec]; norms [B,Hkv,T]; out [B,Hq,d].        */
+/* ------------------------------------------------------------------------ */
+
+ORC_API int kvqo_attention(int d, int bits, int64_t B, int64_t Hq, int64_t Hkv, int64_t T,
+                           const double *q, const uint8_t *kc, const double *kn,
+                           const uint8_t *vc, const double *vn, const int8_t *signs_k,
+                           const int8_t *signs_v, const float *c32, double sm_scale,
+                           double *out)
+{
+    if (Hkv <= 0 || Hq % Hkv || T <= 0) return -1;
+    const int64_t G = Hq / Hkv;
+    const int rec = d * bits / 8;
+    double *K = (double *)malloc(sizeof(double) * T * d);
+    double *V = (double *)malloc(sizeof(double) * T * d);
+    double *s = (double *)malloc(sizeof(double) * T);
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t g = 0; g < Hkv; ++g) {
+            for (int64_t t = 0; t < T; ++t) {
+                const int64_t v = (b * Hkv + g) * T + t;
+                kvqo_dequant(d, bits, kc + v * rec, kn[v], signs_k + g * d, c32, K + t * d);
+                kvqo_dequant(d, bits, vc + v * rec, vn[v], signs_v + g * d, c32, V + t * d);
+            }
+            for (int64_t hh = 0; hh < G; ++hh) {
+                const int64_t h = g * G + hh;
+                const double *qh = q + (b * Hq + h) * d;
+                double mx = -INFINITY;
+                for (int64_t t = 0; t < T; ++t) {
+                    double a = 0.0;
+                    for (int i = 0; i < d; ++i) a += qh[i] * K[t * d + i];
+                    s[t] = sm_scale * a;
+                    if (s[t] > mx) mx = s[t];
+                }
+                double l = 0.0;
+                for (int64_t t = 0; t < T; ++t) {
+                    s[t] = exp(s[t] - mx);
+                    l += s[t];
+                }
+                double *o = out + (b * Hq + h) * d;
+                for (int i = 0; i < d; ++i) o[i] = 0.0;
+                for (int64_t t = 0; t < T; ++t)
+                    for (int i = 0; i < d; ++i) o[i] += s[t] * V[t * d + i];
+                for (int i = 0; i < d; ++i) o[i] /= l;
+            }
+        }
+    free(K);
+    free(V);
+    free(s);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* QJL 1-bit residual (TurboQuant, Stage 2).  Reading: the residual lives in  */
+/* the orthonormal rotated space, r = (y - c[idx]) / sqrt(d); gamma = ||r||;  */
+/* z = S r with S [m, d] of N(0,1) entries; sign bit sgn_j = [z_j >= 0].      */
+/* y [n, d] rotated coordinates, idx [n, d] the MSE codes actually stored.    */
+/* Outputs: packed sign bits [n, m/8] (LSB-first), gamma [n], flags [n, m]    */
+/* (1 when |z_j| < band * gamma).                                             */
+/* ------------------------------------------------------------------------ */
+
+ORC_API int kvqo_qjl(int d, int m, int64_t n, const double *y, const int32_t *idx,
+                     const float *c32, const double *S, double band, uint8_t *sgn,
+                     double *gamma, uint8_t *flags)
+{
+    if (m % 8) return -1;
+    double *r = (double *)malloc(sizeof(double) * d);
+    for (int64_t v = 0; v < n; ++v) {
+        double g2 = 0.0;
+        for (int i = 0; i < d; ++i) {
+            r[i] = (y[v * d + i] - c32[idx[v * d + i]]) / sqrt((double)d);
+            g2 += r[i] * r[i];
+        }
+        double gm = sqrt(g2);
+        gamma[v] = gm;
+        uint8_t *out = sgn + v * (m / 8);
+        memset(out, 0, (size_t)(m / 8));
+        for (int j = 0; j < m; ++j) {
+            double z = 0.0;
+            for (int i = 0; i < d; ++i) z += S[(int64_t)j * d + i] * r[i];
+            if (z >= 0.0) out[j / 8] |= (uint8_t)(1u << (j % 8));
+            if (flags) flags[v * m + j] = (uint8_t)(fabs(z) < band * gm);
+        }
+    }
+    free(r);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* NSN + Hadamard + vector quantisation (NSNQuant, Metodologia 1-3).          */
+/* x [H, T, d].  Per head, over the T tokens of the call:                     */
+/*   a_t = sqrt(d) x_t / ||x_t||,   s1_t = ||x_t|| / sqrt(d)   (normalise)    */
+/*   o   = mean_t a_t                                          (shift)        */
+/*   b_t = a_t - o,  s2_t = ||b_t|| / sqrt(d),  xt_t = b_t / s2_t (normalise) */
+/*   z_t = H xt_t / sqrt(d)                                   (Hadamard)      */
+/* then each sub-vector of `sub` coordinates is replaced by the index of the  */
+/* nearest of K codebook entries (squared Euclidean distance, lowest index on */
+/* exact ties).  flags: 1 when z is within `band` of the bisecting hyperplane */
+/* of the winner and some other entry.  Degenerate tokens: ||x_t|| = 0 gives  */
+/* a_t = 0; s2_t = 0 gives xt_t = 0.                                          */
+/* ------------------------------------------------------------------------ */
+
+ORC_API int kvqo_nsn_vq(int d, int sub, int K, int64_t H, int64_t T, const double *x,
+                        const double *codebook, double band, uint8_t *codes, double *s1,
+                        double *s2, double *o, double *z_out, uint8_t *flags)
+{
+    if (d % sub || T <= 0) return -1;
+    const int nsub = d / sub;
+    const double sd = sqrt((double)d);
+    double *a = (double *)malloc(sizeof(double) * T * d);
+    double *z = (double *)malloc(sizeof(double) * d);
+    double *dist = (double *)malloc(sizeof(double) * K);
+    for (int64_t h = 0; h < H; ++h) {
+        const double *xh = x + h * T * d;
+        double *oh = o + h * d;
+        for (int i = 0; i < d; ++i) oh[i] = 0.0;
+        for (int64_t t = 0; t < T; ++t) {
+            double ss = 0.0;
+            for (int i = 0; i < d; ++i) ss += xh[t * d + i] * xh[t * d + i];
+            double nx = sqrt(ss);
+            s1[h * T + t] = nx / sd;
+            for (int i = 0; i < d; ++i) a[t * d + i] = nx > 0.0 ? sd * xh[t * d + i] / nx : 0.0;
+        }
+        for (int64_t t = 0; t < T; ++t)
+            for (int i = 0; i < d; ++i) oh[i] += a[t * d + i];
+        for (int i = 0; i < d; ++i) oh[i] /= (double)T;
+        for (int64_t t = 0; t < T; ++t) {
+            double ss = 0.0;
+            for (int i = 0; i < d; ++i) {
+                double bi = a[t * d + i] - oh[i];
+                z[i] = bi;
+                ss += bi * bi;
+            }
+            double nb = sqrt(ss);
+            s2[h * T + t] = nb / sd;
+            for (int i = 0; i < d; ++i) z[i] = nb > 0.0 ? z[i] / (nb / sd) : 0.0;
+            kvqo_fwht(z, d);
+            for (int i = 0; i < d; ++i) z[i] /= sd;
+            if (z_out)
+                for (int i = 0; i < d; ++i) z_out[(h * T + t) * d + i] = z[i];
+            for (int s = 0; s < nsub; ++s) {
+                int best = 0;
+                for (int j = 0; j < K; ++j) {
+                    double dd = 0.0;
+                    for (int k = 0; k < sub; ++k) {
+                        double e = z[s * sub + k] - codebook[j * sub + k];
+                        dd += e * e;
+                    }
+                    dist[j] = dd;
+                    if (dd < dist[best]) best = j;
+                }
+                codes[(h * T + t) * nsub + s] = (uint8_t)best;
+                if (flags) {
+                    double mind = INFINITY;
+                    for (int j = 0; j < K; ++j) {
+                        if (j == best) continue;
+                        double cc = 0.0;
+                        for (int k = 0; k < sub; ++k) {
+                            double e = codebook[j * sub + k] - codebook[best * sub + k];
+                            cc += e * e;
+                        }
+                        double md = cc > 0.0 ? (dist[j] - dist[best]) / (2.0 * sqrt(cc)) : 0.0;
+                        if (md < mind) mind = md;
+                    }
+                    flags[(h * T + t) * nsub + s] = (uint8_t)(mind < band);
+                }
+            }
+        }
+    }
+    free(a);
+    free(z);
+    free(dist);
+    return 0;
+}
+
+/* Reconstruction from the NSN byproducts and a rotated vector zq [d]:        */
+/*   x_hat = s1 * (s2 * H zq / sqrt(d) + o)                                   */
+ORC_API void kvqo_nsn_reconstruct(int d, const double *zq, double s1, double s2,
+                                  const double *o, double *x_hat)
+{
+    for (int i = 0; i < d; ++i) x_hat[i] = zq[i];
+    kvqo_fwht(x_hat, d);
+    for (int i = 0; i < d; ++i) x_hat[i] = s1 * (s2 * x_hat[i] / sqrt((double)d) + o[i]);
+}
+
+/* ------------------------------------------------------------------------ */
+/* k-means (Lloyd's algorithm) for the NSN vector codebook, on synthetic      */
+/* N(0, I) samples (NSNQuant, Metodologia 3).  samples [n, dim]; init [K]     */
+/* distinct sample indices; stops when no assignment changes or after         */
+/* max_iter passes; an empty cluster is re-seeded with the sample farthest    */
+/* from its current centroid.  distortion[it] = mean squared distance per     */
+/* dimension after the assignment step of pass it.  Returns passes done.      */
+/* ------------------------------------------------------------------------ */
+
+ORC_API int kvqo_kmeans(int64_t n, int dim, int K, const double *samples, const int64_t *init,
+                        int max_iter, double *codebook, double *distortion)
+{
+    int32_t *asg = (int32_t *)malloc(sizeof(int32_t) * n);
+    double *dmin = (double *)malloc(sizeof(double) * n);
+    double *sum = (double *)malloc(sizeof(double) * K * dim);
+    int64_t *cnt = (int64_t *)malloc(sizeof(int64_t) * K);
+    for (int j = 0; j < K; ++j)
+        for (int k = 0; k < dim; ++k) codebook[j * dim + k] = samples[init[j] * dim + k];
+    for (int64_t i = 0; i < n; ++i) asg[i] = -1;
+    int it = 0;
+    for (; it < max_iter; ++it) {
+        int64_t changed = 0;
+        double tot = 0.0;
+        for (int64_t i = 0; i < n; ++i) {
+            int best = 0;
+            double bd = INFINITY;
+            for (int j = 0; j < K; ++j) {
+                double dd = 0.0;
+                for (int k = 0; k < dim; ++k) {
+                    double e = samples[i * dim + k] - codebook[j * dim + k];
+                    dd += e * e;
+                }
+                if (dd < bd) { bd = dd; best = j; }
+            }
+            if (best != asg[i]) ++changed;
+            asg[i] = best;
+            dmin[i] = bd;
+            tot += bd;
+        }
+        if (distortion) distortion[it] = tot / ((double)n * dim);
+        if (changed == 0) { ++it; break; }
+        memset(sum, 0, sizeof(double) * K * dim);
+        memset(cnt, 0, sizeof(int64_t) * K);
+        for (int64_t i = 0; i < n; ++i) {
+            ++cnt[asg[i]];
+            for (int k = 0; k < dim; ++k) sum[asg[i] * dim + k] += samples[i * dim + k];
+        }
+        for (int j = 0; j < K; ++j) {
+            if (cnt[j] > 0) {
+                for (int k = 0; k < dim; ++k) codebook[j * dim + k] = sum[j * dim + k] / cnt[j];
+            } else {
+                int64_t far = 0;
+                for (int64_t i = 1; i < n; ++i)
+                    if (dmin[i] > dmin[far]) far = i;
+                for (int k = 0; k < dim; ++k) codebook[j * dim + k] = samples[far * dim + k];
+                dmin[far] = 0.0;
+            }
+        }
+    }
+    free(asg);
+    free(dmin);
+    free(sum);
+    free(cnt);
+    return it;
+}

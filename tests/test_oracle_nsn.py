@@ -1,0 +1,87 @@
+"""Pins of the oracle's NSN transform, vector search and k-means (CPU only).
+
+Normalize-Shift-Normalize with byproducts (s1, o, s2), Hadamard, one global
+codebook for N(0,1) built by k-means on synthetic normal samples (NSNQuant
+page, Metodologia sec. 1-3)."""
+import os
+
+import numpy as np
+import pytest
+
+import oracle as O
+from calibration_free_kv_amd import synth
+
+GOLDEN_CB = os.path.join(os.path.dirname(__file__), "golden", "vq_codebook_256x8.txt")
+
+
+def _codebook():
+    return np.loadtxt(GOLDEN_CB, dtype=np.float32).reshape(256, 8)
+
+
+def test_nsn_identities_and_reconstruction():
+    x = synth.make("nsn_vq", T=64)["x"].astype(np.float64)
+    x[1, 3] = 0.0  # a zero token
+    r = O.nsn_vq(x, _codebook(), want_z=True)
+    H, T, d = x.shape
+    nx = np.linalg.norm(x, axis=-1)
+    np.testing.assert_allclose(r["s1"], nx / np.sqrt(d), rtol=1e-14)
+    a = np.where(nx[..., None] > 0, np.sqrt(d) * x / np.where(nx > 0, nx, 1)[..., None], 0.0)
+    np.testing.assert_allclose(r["o"], a.mean(axis=1), atol=1e-13)
+    b = a - r["o"][:, None, :]
+    np.testing.assert_allclose(b.sum(axis=1), 0.0, atol=1e-11)  # shifted tokens sum to zero
+    np.testing.assert_allclose(r["s2"], np.linalg.norm(b, axis=-1) / np.sqrt(d), rtol=1e-13)
+    # ||z|| = sqrt(d): the Hadamard step is orthonormal after the /sqrt(d)
+    np.testing.assert_allclose(np.linalg.norm(r["z"], axis=-1), np.sqrt(d), rtol=1e-12)
+    # exact reconstruction from the byproducts: x = s1 (s2 H z / sqrt(d) + o)
+    for h in range(H):
+        for t in range(T):
+            if nx[h, t] == 0:
+                continue
+            xr = O.nsn_reconstruct(r["z"][h, t], r["s1"][h, t], r["s2"][h, t], r["o"][h])
+            np.testing.assert_allclose(xr, x[h, t], rtol=1e-11, atol=1e-11)
+
+
+def test_vq_brute_force():
+    x = synth.make("nsn_vq", T=48)["x"]
+    cb = _codebook()
+    r = O.nsn_vq(x, cb, want_z=True)
+    z = r["z"].reshape(-1, 8)
+    d2 = ((z[:, None, :] - cb[None].astype(np.float64)) ** 2).sum(-1)
+    assert np.array_equal(r["codes"].reshape(-1), np.argmin(d2, axis=1))
+
+
+def test_vq_ties_and_flags():
+    """z exactly on a codebook entry picks it; an exact tie picks the lower
+    index and is flagged; a point far from every bisector is not flagged."""
+    cb = np.zeros((4, 8))
+    cb[1, 0], cb[2, 0], cb[3, 0] = 2.0, -2.0, 2.0  # entry 3 duplicates entry 1
+    x = np.zeros((1, 2, 128))
+    x[0, 0, 0] = 1.0
+    x[0, 1, :] = np.arange(128) - 63.5
+    r = O.nsn_vq(x, cb, want_z=True)
+    z = r["z"].reshape(-1, 8)
+    d2 = ((z[:, None, :] - cb[None]) ** 2).sum(-1)
+    best = np.argmin(d2, axis=1)  # numpy returns the first minimum
+    assert np.array_equal(r["codes"].reshape(-1), best)
+    assert not np.any(r["codes"].reshape(-1) == 3)  # the duplicate never wins
+    fl = r["flags"].reshape(-1)
+    # a sub-vector whose best entry is 1 ties exactly with 3 -> flagged
+    assert np.all(fl[best == 1] == 1)
+
+
+def test_kmeans_distortion_bounds():
+    n = 1 << 14
+    s = synth.gaussian_samples(123, n)
+    cb, dist, it = O.kmeans(s, synth.kmeans_init(123, n), max_iter=15)
+    assert np.all(np.diff(dist) <= 1e-12)  # Lloyd iterations never increase distortion
+    # 256 entries in 8 dims = 1 bit per dimension: at or above the Shannon bound
+    # 2^-2 = 0.25, and at most the 1-bit scalar Lloyd-Max product code 1 - 2/pi
+    assert 0.25 <= dist[-1] <= 1 - 2 / np.pi
+
+
+def test_golden_codebook():
+    cb = _codebook()
+    assert cb.shape == (256, 8) and np.isfinite(cb).all()
+    s = synth.gaussian_samples(999, 1 << 15)
+    d2 = ((s[:, None, :] - cb[None].astype(np.float64)) ** 2).sum(-1).min(1)
+    assert 0.25 <= d2.mean() / 8 <= 0.33
