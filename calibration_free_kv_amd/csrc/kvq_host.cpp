@@ -1,0 +1,327 @@
+// libkvq host side: context lifetime, the Gaussian Lloyd-Max table builder,
+// argument validation and kernel launches behind the C ABI of kvq.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+
+#include "kvq_internal.h"
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// Lloyd-Max quantiser for N(0,1) ("PolarQuant", Methodology: Lloyd-Max
+// centroids, optimal in MSE for the Gaussian; "TurboQuant", Como Implementar:
+// tables precomputed per bit width).  The Gaussian is symmetric, so only the
+// 2^(b-1) positive levels m_k are iterated; cell k of the positive half is
+// [tau_k, tau_{k+1}) with tau_0 = 0, tau_k = (m_{k-1} + m_k)/2 and
+// tau_{half} = +inf, and each level is moved to its cell's conditional mean
+//   m_k = (phi(tau_k) - phi(tau_{k+1})) / (Q(tau_k) - Q(tau_{k+1})),
+// Q the upper tail.  The negative half is the mirror image, so the table is
+// exactly antisymmetric.
+// ---------------------------------------------------------------------------
+double phi(double x) { return std::isinf(x) ? 0.0 : std::exp(-0.5 * x * x) * 0.3989422804014327; }
+double upper_tail(double x) { return std::isinf(x) ? 0.0 : 0.5 * std::erfc(x * 0.7071067811865476); }
+
+void build_codebook(int bits, kvq::Codebook *cb)
+{
+    const int L = 1 << bits, half = L / 2;
+    double m[8];
+    for (int k = 0; k < half; ++k) m[k] = 3.0 * (k + 0.5) / half;  // spread over [0, 3]
+    for (int it = 0; it < 200000; ++it) {
+        double tau[9];
+        tau[0] = 0.0;
+        for (int k = 1; k < half; ++k) tau[k] = 0.5 * (m[k - 1] + m[k]);
+        tau[half] = INFINITY;
+        double change = 0.0;
+        for (int k = 0; k < half; ++k) {
+            double nm = (phi(tau[k]) - phi(tau[k + 1])) / (upper_tail(tau[k]) - upper_tail(tau[k + 1]));
+            change = std::fmax(change, std::fabs(nm - m[k]));
+            m[k] = nm;
+        }
+        if (change <= 1e-16) break;
+    }
+    std::memset(cb, 0, sizeof(*cb));
+    cb->bits = bits;
+    for (int k = 0; k < half; ++k) {
+        cb->c[half + k] = (float)m[k];
+        cb->c[half - 1 - k] = -(float)m[k];
+    }
+    // Stored thresholds: fp32 midpoints of adjacent fp32 centroids.
+    for (int j = 0; j + 1 < L; ++j) cb->t[j] = (float)(((double)cb->c[j] + (double)cb->c[j + 1]) * 0.5);
+}
+
+struct DeviceGuard {
+    int prev = -1;
+    bool ok = false;
+    explicit DeviceGuard(int dev)
+    {
+        if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+        ok = hipSetDevice(dev) == hipSuccess;
+    }
+    ~DeviceGuard()
+    {
+        if (prev >= 0) (void)hipSetDevice(prev);
+    }
+};
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+void free_ctx(kvq_ctx *c)
+{
+    if (!c) return;
+    (void)hipFree(c->d_sgnmask);
+    (void)hipFree(c->d_signs);
+    (void)hipFree(c->d_S);
+    (void)hipFree(c->d_vq);
+    (void)hipFree(c->d_vqnorm);
+    delete c;
+}
+
+template <class T>
+kvq_status upload(T **dst, const T *src, size_t n)
+{
+    if (hipMalloc((void **)dst, n * sizeof(T)) != hipSuccess) {
+        *dst = nullptr;
+        return KVQ_E_NOMEM;
+    }
+    if (hipMemcpy(*dst, src, n * sizeof(T), hipMemcpyHostToDevice) != hipSuccess) return KVQ_E_DEVICE;
+    return KVQ_OK;
+}
+
+kvq_status launch_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_E_DEVICE; }
+
+}  // namespace
+
+extern "C" {
+
+const char *kvq_strerror(kvq_status s)
+{
+    switch (s) {
+    case KVQ_OK: return "ok";
+    case KVQ_E_INVAL: return "invalid argument";
+    case KVQ_E_UNSUPPORTED: return "unsupported configuration";
+    case KVQ_E_DEVICE: return "device or HIP runtime error";
+    case KVQ_E_NOMEM: return "out of memory";
+    case KVQ_E_WORKSPACE: return "workspace too small";
+    }
+    return "unknown status";
+}
+
+kvq_status kvq_create(const kvq_config *cfg, kvq_ctx **out)
+{
+    if (!out) return KVQ_E_INVAL;
+    *out = nullptr;
+    if (!cfg) return KVQ_E_INVAL;
+    if (cfg->d != kvq::kD || cfg->n_kv_heads < 1 || cfg->n_kv_heads > 4096) return KVQ_E_INVAL;
+    const int mode = cfg->mode;
+    if (mode != KVQ_MODE_MSE && mode != KVQ_MODE_MSE_QJL && mode != KVQ_MODE_NSN_VQ) return KVQ_E_INVAL;
+    const int H = cfg->n_kv_heads;
+    if (mode != KVQ_MODE_NSN_VQ) {
+        if (cfg->bits < 1 || cfg->bits > 4) return KVQ_E_INVAL;
+        if (!cfg->signs_k || !cfg->signs_v) return KVQ_E_INVAL;
+        for (int i = 0; i < H * kvq::kD; ++i) {
+            if (cfg->signs_k[i] != 1 && cfg->signs_k[i] != -1) return KVQ_E_INVAL;
+            if (cfg->signs_v[i] != 1 && cfg->signs_v[i] != -1) return KVQ_E_INVAL;
+        }
+    }
+    if (mode == KVQ_MODE_MSE_QJL && !cfg->qjl_S) return KVQ_E_INVAL;
+    if (mode == KVQ_MODE_NSN_VQ && !cfg->vq_codebook) return KVQ_E_INVAL;
+
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || cfg->device < 0 || cfg->device >= ndev)
+        return KVQ_E_DEVICE;
+    DeviceGuard g(cfg->device);
+    if (!g.ok) return KVQ_E_DEVICE;
+
+    kvq_ctx *c = new (std::nothrow) kvq_ctx();
+    if (!c) return KVQ_E_NOMEM;
+    c->d = cfg->d;
+    c->bits = mode == KVQ_MODE_NSN_VQ ? 1 : cfg->bits;
+    c->mode = mode;
+    c->H = H;
+    c->device = cfg->device;
+    build_codebook(c->bits, &c->cb);
+
+    kvq_status st = KVQ_OK;
+    if (mode != KVQ_MODE_NSN_VQ) {
+        const size_t n = (size_t)H * kvq::kD;
+        uint32_t *mask = (uint32_t *)std::calloc(2 * n / 2, sizeof(uint32_t));
+        float *sg = (float *)std::malloc(2 * n * sizeof(float));
+        if (!mask || !sg) st = KVQ_E_NOMEM;
+        for (int kind = 0; st == KVQ_OK && kind < 2; ++kind) {
+            const int8_t *src = kind ? cfg->signs_v : cfg->signs_k;
+            for (size_t i = 0; i < n; ++i) {
+                sg[kind * n + i] = (float)src[i];
+                if (src[i] < 0) mask[(kind * n + i) / 2] |= (i & 1) ? 0x80000000u : 0x8000u;
+            }
+        }
+        if (st == KVQ_OK) st = upload(&c->d_sgnmask, mask, n);
+        if (st == KVQ_OK) st = upload(&c->d_signs, sg, 2 * n);
+        std::free(mask);
+        std::free(sg);
+    }
+    if (st == KVQ_OK && mode == KVQ_MODE_MSE_QJL)
+        st = upload(&c->d_S, cfg->qjl_S, (size_t)kvq::kD * kvq::kD);
+    if (st == KVQ_OK && mode == KVQ_MODE_NSN_VQ) {
+        float nrm[kvq::kVqK];
+        for (int j = 0; j < kvq::kVqK; ++j) {
+            double s = 0.0;
+            for (int k = 0; k < kvq::kVqSub; ++k) {
+                double v = cfg->vq_codebook[j * kvq::kVqSub + k];
+                if (!std::isfinite(v)) st = KVQ_E_INVAL;
+                s += v * v;
+            }
+            nrm[j] = (float)s;
+        }
+        if (st == KVQ_OK) st = upload(&c->d_vq, cfg->vq_codebook, (size_t)kvq::kVqK * kvq::kVqSub);
+        if (st == KVQ_OK) st = upload(&c->d_vqnorm, nrm, (size_t)kvq::kVqK);
+    }
+    if (st != KVQ_OK) {
+        free_ctx(c);
+        return st;
+    }
+    *out = c;
+    return KVQ_OK;
+}
+
+kvq_status kvq_destroy(kvq_ctx *ctx)
+{
+    if (!ctx) return KVQ_OK;
+    DeviceGuard g(ctx->device);
+    free_ctx(ctx);
+    return KVQ_OK;
+}
+
+kvq_status kvq_get_tables(const kvq_ctx *ctx, float *centroids, float *thresholds)
+{
+    if (!ctx) return KVQ_E_INVAL;
+    const int L = 1 << ctx->bits;
+    if (centroids) std::memcpy(centroids, ctx->cb.c, L * sizeof(float));
+    if (thresholds) std::memcpy(thresholds, ctx->cb.t, (L - 1) * sizeof(float));
+    return KVQ_OK;
+}
+
+kvq_status kvq_codebook(int32_t bits, float *centroids, float *thresholds)
+{
+    if (bits < 1 || bits > 4 || !centroids || !thresholds) return KVQ_E_INVAL;
+    kvq::Codebook cb;
+    build_codebook(bits, &cb);
+    std::memcpy(centroids, cb.c, (1 << bits) * sizeof(float));
+    std::memcpy(thresholds, cb.t, ((1 << bits) - 1) * sizeof(float));
+    return KVQ_OK;
+}
+
+int64_t kvq_code_bytes_per_vec(const kvq_ctx *ctx)
+{
+    if (!ctx) return 0;
+    return ctx->mode == KVQ_MODE_NSN_VQ ? kvq::kD / kvq::kVqSub : 16 * ctx->bits;
+}
+
+kvq_status kvq_quantize(kvq_ctx *ctx, int32_t kind, const void *x_f16, int64_t B, int64_t H_kv,
+                        int64_t T, uint8_t *codes, float *norms, uint8_t *qjl_signs,
+                        float *qjl_gamma, void *stream)
+{
+    if (!ctx || ctx->mode == KVQ_MODE_NSN_VQ) return KVQ_E_INVAL;
+    if (kind != KVQ_KIND_K && kind != KVQ_KIND_V) return KVQ_E_INVAL;
+    if (B < 0 || T < 0 || H_kv != ctx->H) return KVQ_E_INVAL;
+    const bool want_qjl = ctx->mode == KVQ_MODE_MSE_QJL && kind == KVQ_KIND_K;
+    if (want_qjl != (qjl_signs != nullptr) || want_qjl != (qjl_gamma != nullptr)) return KVQ_E_INVAL;
+    if (B == 0 || T == 0) return KVQ_OK;
+    if (!x_f16 || !codes || !norms) return KVQ_E_INVAL;
+    if (!aligned(x_f16, 16) || !aligned(codes, 16) || !aligned(norms, 4)) return KVQ_E_INVAL;
+    if (want_qjl && (!aligned(qjl_signs, 16) || !aligned(qjl_gamma, 4))) return KVQ_E_INVAL;
+    if (B * H_kv > (int64_t(1) << 40) || T > (int64_t(1) << 31)) return KVQ_E_INVAL;
+    DeviceGuard g(ctx->device);
+    if (!g.ok) return KVQ_E_DEVICE;
+    return launch_status(kvq::launch_quantize(ctx, kind, x_f16, B, T, codes, norms, qjl_signs,
+                                              qjl_gamma, (hipStream_t)stream));
+}
+
+kvq_status kvq_logits(kvq_ctx *ctx, const void *q_f16, int64_t B, int64_t H_q, int64_t T,
+                      const uint8_t *codes, const float *norms, const uint8_t *qjl_signs,
+                      const float *qjl_gamma, float *logits, void *stream)
+{
+    if (!ctx || ctx->mode == KVQ_MODE_NSN_VQ) return KVQ_E_INVAL;
+    if (B < 0 || T < 0 || H_q < 1 || H_q % ctx->H || H_q / ctx->H > kvq::kMaxGroup) return KVQ_E_INVAL;
+    const bool want_qjl = ctx->mode == KVQ_MODE_MSE_QJL;
+    if (want_qjl != (qjl_signs != nullptr) || want_qjl != (qjl_gamma != nullptr)) return KVQ_E_INVAL;
+    if (B == 0 || T == 0) return KVQ_OK;
+    if (!q_f16 || !codes || !norms || !logits) return KVQ_E_INVAL;
+    if (!aligned(q_f16, 16) || !aligned(codes, 16) || !aligned(norms, 4) || !aligned(logits, 4))
+        return KVQ_E_INVAL;
+    if (want_qjl && (!aligned(qjl_signs, 16) || !aligned(qjl_gamma, 4))) return KVQ_E_INVAL;
+    if (T > (int64_t(1) << 31)) return KVQ_E_INVAL;
+    DeviceGuard g(ctx->device);
+    if (!g.ok) return KVQ_E_DEVICE;
+    return launch_status(kvq::launch_logits(ctx, q_f16, B, H_q, T, codes, norms, qjl_signs, qjl_gamma,
+                                            logits, (hipStream_t)stream));
+}
+
+size_t kvq_attn_decode_ws_bytes(const kvq_ctx *ctx, int64_t B, int64_t H_q, int64_t T)
+{
+    if (!ctx || B < 1 || T < 1 || H_q < 1) return 0;
+    return kvq::decode_ws_bytes(B, H_q, ctx->H, T);
+}
+
+kvq_status kvq_attn_decode_splits(kvq_ctx *ctx, const void *q_f16, int64_t B, int64_t H_q,
+                                  int64_t T, const uint8_t *k_codes, const float *k_norms,
+                                  const uint8_t *v_codes, const float *v_norms, float sm_scale,
+                                  float *out, void *ws, size_t ws_bytes, int32_t n_split,
+                                  void *stream)
+{
+    if (!ctx || ctx->mode != KVQ_MODE_MSE) return KVQ_E_INVAL;
+    if (B < 0 || T < 1 || H_q < 1 || H_q % ctx->H || H_q / ctx->H > kvq::kMaxGroup) return KVQ_E_INVAL;
+    if (n_split < 0 || !std::isfinite(sm_scale) || sm_scale < 0.f) return KVQ_E_INVAL;
+    if (B == 0) return KVQ_OK;
+    if (!q_f16 || !k_codes || !k_norms || !v_codes || !v_norms || !out || !ws) return KVQ_E_INVAL;
+    if (!aligned(q_f16, 16) || !aligned(k_codes, 16) || !aligned(v_codes, 16) || !aligned(k_norms, 4) ||
+        !aligned(v_norms, 4) || !aligned(out, 16) || !aligned(ws, 256))
+        return KVQ_E_INVAL;
+    if (T > (int64_t(1) << 31)) return KVQ_E_INVAL;
+    if (ws_bytes < kvq::decode_ws_bytes(B, H_q, ctx->H, T)) return KVQ_E_WORKSPACE;
+    const int64_t max_split = (T + 63) / 64;
+    int ns = n_split == 0 ? kvq::decode_auto_splits(B, ctx->H, T) : n_split;
+    if (ns > max_split) ns = (int)max_split;
+    if (ns < 1) ns = 1;
+    if (sm_scale == 0.f) sm_scale = 1.0f / std::sqrt((float)kvq::kD);
+    DeviceGuard g(ctx->device);
+    if (!g.ok) return KVQ_E_DEVICE;
+    return launch_status(kvq::launch_decode(ctx, q_f16, B, H_q, T, k_codes, k_norms, v_codes, v_norms,
+                                            sm_scale, out, ws, ns, (hipStream_t)stream));
+}
+
+kvq_status kvq_attn_decode(kvq_ctx *ctx, const void *q_f16, int64_t B, int64_t H_q, int64_t T,
+                           const uint8_t *k_codes, const float *k_norms, const uint8_t *v_codes,
+                           const float *v_norms, float sm_scale, float *out, void *ws,
+                           size_t ws_bytes, void *stream)
+{
+    return kvq_attn_decode_splits(ctx, q_f16, B, H_q, T, k_codes, k_norms, v_codes, v_norms, sm_scale,
+                                  out, ws, ws_bytes, 0, stream);
+}
+
+size_t kvq_nsn_vq_ws_bytes(const kvq_ctx *ctx, int64_t H, int64_t T)
+{
+    if (!ctx || H < 1 || T < 1) return 0;
+    return kvq::nsn_ws_bytes(H, T);
+}
+
+kvq_status kvq_nsn_vq_quantize(kvq_ctx *ctx, const void *x_f16, int64_t H, int64_t T, uint8_t *codes,
+                               float *s1, float *s2, float *o, void *ws, size_t ws_bytes,
+                               void *stream)
+{
+    if (!ctx || ctx->mode != KVQ_MODE_NSN_VQ) return KVQ_E_INVAL;
+    if (H < 1 || T < 1 || T > (int64_t(1) << 31) || H > (int64_t(1) << 20)) return KVQ_E_INVAL;
+    if (!x_f16 || !codes || !s1 || !s2 || !o || !ws) return KVQ_E_INVAL;
+    if (!aligned(x_f16, 16) || !aligned(codes, 16) || !aligned(s1, 4) || !aligned(s2, 4) ||
+        !aligned(o, 4) || !aligned(ws, 256))
+        return KVQ_E_INVAL;
+    if (ws_bytes < kvq::nsn_ws_bytes(H, T)) return KVQ_E_WORKSPACE;
+    DeviceGuard g(ctx->device);
+    if (!g.ok) return KVQ_E_DEVICE;
+    return launch_status(kvq::launch_nsn_vq(ctx, x_f16, H, T, codes, s1, s2, o, ws, (hipStream_t)stream));
+}
+
+}  // extern "C"

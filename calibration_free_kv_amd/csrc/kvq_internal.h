@@ -1,0 +1,59 @@
+// Internal declarations shared by the libkvq host code and its HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "kvq.h"
+
+namespace kvq {
+
+constexpr int kD = 128;       // head dimension
+constexpr int kVqSub = 8;     // NSN sub-vector length
+constexpr int kVqK = 256;     // NSN codebook entries
+constexpr int kMaxGroup = 8;  // query heads per KV head supported by the score kernels
+
+// Scalar codebook of one bit width, passed to kernels by value.
+struct Codebook {
+    float c[16];  // centroids c_0 < ... < c_{2^b - 1}
+    float t[16];  // thresholds t_0 < ... < t_{2^b - 2}
+    int bits;
+};
+
+}  // namespace kvq
+
+struct kvq_ctx {
+    int d, bits, mode, H, device;
+    kvq::Codebook cb;
+    uint32_t *d_sgnmask;  // [2][H][64]: fp16-pair sign masks of D_K, D_V
+    float *d_signs;       // [2][H][128]: D_K, D_V as +-1.0f
+    float *d_S;           // [128][128] QJL projection (MSE_QJL)
+    float *d_vq;          // [256][8] NSN codebook (NSN_VQ)
+    float *d_vqnorm;      // [256] squared norms of the codebook entries
+};
+
+namespace kvq {
+
+hipError_t launch_quantize(const kvq_ctx *ctx, int kind, const void *x, int64_t B, int64_t T,
+                           uint8_t *codes, float *norms, uint8_t *qjl_signs, float *qjl_gamma,
+                           hipStream_t s);
+
+hipError_t launch_logits(const kvq_ctx *ctx, const void *q, int64_t B, int64_t Hq, int64_t T,
+                         const uint8_t *codes, const float *norms, const uint8_t *qjl_signs,
+                         const float *qjl_gamma, float *logits, hipStream_t s);
+
+size_t decode_ws_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t T);
+int decode_auto_splits(int64_t B, int64_t Hkv, int64_t T);
+
+hipError_t launch_decode(const kvq_ctx *ctx, const void *q, int64_t B, int64_t Hq, int64_t T,
+                         const uint8_t *kc, const float *kn, const uint8_t *vc, const float *vn,
+                         float sm_scale, float *out, void *ws, int n_split, hipStream_t s);
+
+size_t nsn_ws_bytes(int64_t H, int64_t T);
+
+hipError_t launch_nsn_vq(const kvq_ctx *ctx, const void *x, int64_t H, int64_t T, uint8_t *codes,
+                         float *s1, float *s2, float *o, void *ws, hipStream_t s);
+
+}  // namespace kvq

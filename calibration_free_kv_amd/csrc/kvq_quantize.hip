@@ -1,0 +1,230 @@
+// kvq_quantize: per-vector norm, random-sign Walsh-Hadamard rotation, Gaussian
+// Lloyd-Max bucketing and LSB-first bit packing of fp16 K/V vectors
+// ("PolarQuant", Technical summary sec. 2; "TurboQuant", Como Funciona,
+// Estagio 1).
+//
+// Mapping on gfx950: one wave quantises a tile of 64 consecutive vectors of
+// one (batch, KV head), one vector per lane.  The tile (16 KiB of fp16) is
+// read with fully coalesced 16-byte loads (each load instruction covers 1 KiB
+// of contiguous memory), staged through a padded LDS tile and read back one
+// row per lane.  Each lane then holds its whole vector in VGPRs, so the 7
+// butterfly stages of the transform (896 add/sub) need no cross-lane traffic.
+// The random signs D of the head are wave-uniform and applied as an XOR on
+// the fp16 sign bits; the norm is a chain of packed fp16 dot products with
+// fp32 accumulation.  Instead of dividing the 128 coordinates by the norm,
+// the rotated coordinates of x itself are compared with the thresholds
+// scaled by ||x|| (same decisions up to fp32 rounding, 128 fewer multiplies).
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kTile = 64;     // vectors per wave
+constexpr int kWaves = 4;     // waves per block
+constexpr int kRowU4 = 17;    // LDS row stride in 16-byte units (one pad slot)
+
+struct HalfThresholds {
+    float p[8];  // positive thresholds t_{L/2}, ..., t_{L-2} (L/2 - 1 of them)
+};
+
+// fp16 pair -> fp32 (lo + hi) and (lo - hi) in one mixed-precision FMA each:
+// the first butterfly stage fused with the widening.
+__device__ __forceinline__ float pair_sum(uint32_t p)
+{
+    float r;
+    asm("v_fma_mix_f32 %0, %1, 1.0, %1 op_sel:[0,0,1] op_sel_hi:[1,0,1]" : "=v"(r) : "v"(p));
+    return r;
+}
+__device__ __forceinline__ float pair_diff(uint32_t p)
+{
+    float r;
+    asm("v_fma_mix_f32 %0, %1, 1.0, -%1 op_sel:[0,0,1] op_sel_hi:[1,0,1]" : "=v"(r) : "v"(p));
+    return r;
+}
+
+// acc = 2 * acc + (bit of this lane in the wave mask m): appends one bit to a
+// dword that is filled most-significant bit first.
+__device__ __forceinline__ uint32_t append_bit(uint32_t acc, uint64_t m)
+{
+    uint32_t r;
+    uint64_t carry;
+    asm("v_addc_co_u32_e64 %0, %1, %2, %2, %3" : "=v"(r), "=s"(carry) : "v"(acc), "s"(m));
+    return r;
+}
+
+// Bits of the index of coordinate y (unnormalised) as wave lane masks,
+// M[k] = bit k.  idx = #{j : t_j < y} for the antisymmetric table: with
+// a = |y| and h = #{k : a > p_k} (p = positive thresholds scaled by ||x||),
+// idx = L/2 + h if y > 0 else L/2 - 1 - h; so the top bit is [y > 0] and the
+// low bits are the bits of h, inverted when y <= 0.  h comes from a binary
+// search over the positive thresholds.
+template <int BITS>
+__device__ __forceinline__ void index_bits(float y, const float *P, uint64_t *M)
+{
+    const float a = __builtin_fabsf(y);
+    const uint64_t s = __builtin_amdgcn_ballot_w64(y > 0.0f);
+    M[BITS - 1] = s;
+    if constexpr (BITS == 2) {
+        M[0] = ~(__builtin_amdgcn_ballot_w64(a > P[0]) ^ s);
+    } else if constexpr (BITS == 3) {
+        const bool c1 = a > P[1];
+        const bool c2 = a > (c1 ? P[2] : P[0]);
+        M[1] = ~(__builtin_amdgcn_ballot_w64(c1) ^ s);
+        M[0] = ~(__builtin_amdgcn_ballot_w64(c2) ^ s);
+    } else if constexpr (BITS == 4) {
+        const bool c1 = a > P[3];
+        const float t2 = c1 ? P[5] : P[1];
+        const float tA = c1 ? P[6] : P[2];
+        const float tB = c1 ? P[4] : P[0];
+        const bool c2 = a > t2;
+        const bool c3 = a > (c2 ? tA : tB);
+        M[2] = ~(__builtin_amdgcn_ballot_w64(c1) ^ s);
+        M[1] = ~(__builtin_amdgcn_ballot_w64(c2) ^ s);
+        M[0] = ~(__builtin_amdgcn_ballot_w64(c3) ^ s);
+    }
+}
+
+template <int BITS>
+__global__ __launch_bounds__(kWaves * 64) void k_quantize(
+    const u4_t *__restrict__ x, u4_t *__restrict__ codes, float *__restrict__ norms,
+    const uint32_t *__restrict__ sgnmask, HalfThresholds ht, int64_t T, int H,
+    int64_t tiles_per_bh, int64_t n_tiles)
+{
+    __shared__ u4_t lds[kWaves][kTile * kRowU4];
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;
+    const int64_t tile = (int64_t)blockIdx.x * kWaves + wv;
+    int64_t bh = 0, t0 = 0;
+    int nv = 0;
+    if (tile < n_tiles) {
+        bh = tile / tiles_per_bh;
+        t0 = (tile - bh * tiles_per_bh) * kTile;
+        nv = (int)min((int64_t)kTile, T - t0);
+    }
+    const int64_t v0 = bh * T + t0;
+    u4_t *L = lds[wv];
+
+    // Coalesced load of the tile into LDS: element e = 16-byte chunk e%16 of
+    // vector e/16.
+    {
+        const u4_t *src = x + v0 * 16;
+        const int lim = nv * 16;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int e = j * 64 + lane;
+            if (e < lim) L[(e >> 4) * kRowU4 + (e & 15)] = __builtin_nontemporal_load(src + e);
+        }
+    }
+    __syncthreads();
+    if (lane >= nv) return;
+
+    const int h = (int)(bh % H);
+    const uint32_t *sg = sgnmask + h * 64;
+    uint32_t w[64];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const u4_t v = L[lane * kRowU4 + j];
+        w[4 * j + 0] = v.x;
+        w[4 * j + 1] = v.y;
+        w[4 * j + 2] = v.z;
+        w[4 * j + 3] = v.w;
+    }
+
+    // ||x||^2 with fp16 products (exact in fp32) accumulated in fp32, and D.
+    float ss = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 64; ++k) {
+        const h2_t p = __builtin_bit_cast(h2_t, w[k]);
+        ss = __builtin_amdgcn_fdot2(p, p, ss, false);
+        w[k] ^= sg[k];
+    }
+
+    // First butterfly stage fused with the fp16 -> fp32 widening.
+    float y[128];
+#pragma unroll
+    for (int k = 0; k < 64; ++k) {
+        y[2 * k] = pair_sum(w[k]);
+        y[2 * k + 1] = pair_diff(w[k]);
+    }
+#pragma unroll
+    for (int s = 2; s < 128; s <<= 1) {
+#pragma unroll
+        for (int i = 0; i < 128; i += 2 * s) {
+#pragma unroll
+            for (int j = i; j < i + s; ++j) {
+                const float a = y[j], b = y[j + s];
+                y[j] = a + b;
+                y[j + s] = a - b;
+            }
+        }
+    }
+
+    const float rho = __builtin_sqrtf(ss);
+    const float r = rho > 0.0f ? rho : 1.0f;  // zero vector: y = 0 -> index L/2 - 1
+    float P[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) P[k] = ht.p[k] * r;
+
+    // Emit the LSB-first stream from its last bit backwards: bit p = BITS*i + k
+    // goes to dword p/32, which is filled most-significant bit first.
+    uint32_t out[4 * BITS];
+#pragma unroll
+    for (int k = 0; k < 4 * BITS; ++k) out[k] = 0u;
+#pragma unroll
+    for (int i = 127; i >= 0; --i) {
+        uint64_t M[BITS];
+        index_bits<BITS>(y[i], P, M);
+#pragma unroll
+        for (int k = BITS - 1; k >= 0; --k) {
+            const int wd = (BITS * i + k) >> 5;
+            out[wd] = append_bit(out[wd], M[k]);
+        }
+    }
+
+    const int64_t v = v0 + lane;
+    u4_t *dst = codes + v * BITS;
+#pragma unroll
+    for (int q = 0; q < BITS; ++q) {
+        u4_t o = {out[4 * q], out[4 * q + 1], out[4 * q + 2], out[4 * q + 3]};
+        dst[q] = o;
+    }
+    norms[v] = rho;
+}
+
+template <int BITS>
+hipError_t run(const kvq_ctx *ctx, int kind, const void *x, int64_t B, int64_t T, uint8_t *codes,
+               float *norms, hipStream_t s)
+{
+    HalfThresholds ht{};
+    const int L = 1 << BITS;
+    for (int k = 0; k < L / 2 - 1; ++k) ht.p[k] = ctx->cb.t[L / 2 + k];
+    const int64_t tiles_per_bh = (T + kTile - 1) / kTile;
+    const int64_t n_tiles = tiles_per_bh * B * ctx->H;
+    const int64_t blocks = (n_tiles + kWaves - 1) / kWaves;
+    hipLaunchKernelGGL(k_quantize<BITS>, dim3((unsigned)blocks), dim3(kWaves * 64), 0, s,
+                       (const u4_t *)x, (u4_t *)codes, norms,
+                       ctx->d_sgnmask + (size_t)kind * ctx->H * 64, ht, T, ctx->H, tiles_per_bh,
+                       n_tiles);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const kvq_ctx *ctx, int kind, const void *x, int64_t B, int64_t T,
+                           uint8_t *codes, float *norms, uint8_t *qjl_signs, float *qjl_gamma,
+                           hipStream_t s)
+{
+    if (qjl_signs || qjl_gamma) return hipErrorNotSupported;
+    switch (ctx->bits) {
+    case 1: return run<1>(ctx, kind, x, B, T, codes, norms, s);
+    case 2: return run<2>(ctx, kind, x, B, T, codes, norms, s);
+    case 3: return run<3>(ctx, kind, x, B, T, codes, norms, s);
+    case 4: return run<4>(ctx, kind, x, B, T, codes, norms, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace kvq

@@ -1,0 +1,258 @@
+"""Thin Python binding of libkvq (C ABI in include/kvq.h).
+
+Every function here only checks tensor placement/dtype/shape, allocates
+outputs with torch on the tensors' device and forwards plain pointers to the
+library; all computation happens in the HIP kernels of libkvq.so.  There is no
+CPU fallback: if the library cannot be loaded, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkvq.so")
+
+KVQ_OK, KVQ_E_INVAL, KVQ_E_UNSUPPORTED, KVQ_E_DEVICE, KVQ_E_NOMEM, KVQ_E_WORKSPACE = range(6)
+KVQ_MODE_MSE, KVQ_MODE_MSE_QJL, KVQ_MODE_NSN_VQ = 0, 1, 2
+KVQ_KIND_K, KVQ_KIND_V = 0, 1
+D = 128
+
+EXPORTS = [
+    "kvq_create", "kvq_destroy", "kvq_get_tables", "kvq_codebook", "kvq_code_bytes_per_vec", "kvq_strerror",
+    "kvq_quantize", "kvq_logits", "kvq_attn_decode_ws_bytes", "kvq_attn_decode",
+    "kvq_attn_decode_splits", "kvq_nsn_vq_ws_bytes", "kvq_nsn_vq_quantize",
+]
+
+
+class KvqError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__("%s: %s (status %d)" % (what, strerror(status), status))
+
+
+class kvq_config(C.Structure):
+    _fields_ = [
+        ("d", C.c_int32), ("bits", C.c_int32), ("mode", C.c_int32), ("n_kv_heads", C.c_int32),
+        ("signs_k", C.POINTER(C.c_int8)), ("signs_v", C.POINTER(C.c_int8)),
+        ("qjl_S", C.POINTER(C.c_float)), ("vq_codebook", C.POINTER(C.c_float)),
+        ("device", C.c_int32),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    """Load libkvq.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libkvq.so not found at %s; build it with "
+                               "`python -c 'import __graft_entry__ as g; g.build()'`" % LIB_PATH)
+        L = C.CDLL(LIB_PATH)
+        vp, i64, i32, sz = C.c_void_p, C.c_int64, C.c_int32, C.c_size_t
+        L.kvq_create.argtypes = [C.POINTER(kvq_config), C.POINTER(vp)]
+        L.kvq_destroy.argtypes = [vp]
+        L.kvq_get_tables.argtypes = [vp, vp, vp]
+        L.kvq_codebook.argtypes = [i32, vp, vp]
+        L.kvq_code_bytes_per_vec.argtypes = [vp]
+        L.kvq_code_bytes_per_vec.restype = i64
+        L.kvq_strerror.argtypes = [C.c_int]
+        L.kvq_strerror.restype = C.c_char_p
+        L.kvq_quantize.argtypes = [vp, i32, vp, i64, i64, i64, vp, vp, vp, vp, vp]
+        L.kvq_logits.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, vp, vp, vp]
+        L.kvq_attn_decode_ws_bytes.argtypes = [vp, i64, i64, i64]
+        L.kvq_attn_decode_ws_bytes.restype = sz
+        L.kvq_attn_decode.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, vp, C.c_float, vp, vp, sz, vp]
+        L.kvq_attn_decode_splits.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, vp, C.c_float, vp, vp,
+                                             sz, i32, vp]
+        L.kvq_nsn_vq_ws_bytes.argtypes = [vp, i64, i64]
+        L.kvq_nsn_vq_ws_bytes.restype = sz
+        L.kvq_nsn_vq_quantize.argtypes = [vp, vp, i64, i64, vp, vp, vp, vp, vp, sz, vp]
+        _lib = L
+    return _lib
+
+
+def kvq_codebook(bits: int):
+    """fp32 (centroids, thresholds) of the b-bit N(0,1) Lloyd-Max quantiser (no device needed)."""
+    c = np.zeros(1 << bits, np.float32)
+    t = np.zeros((1 << bits) - 1, np.float32)
+    _check(lib().kvq_codebook(bits, c.ctypes.data_as(C.c_void_p), t.ctypes.data_as(C.c_void_p)),
+           "kvq_codebook")
+    return c, t
+
+
+def strerror(status: int) -> str:
+    return lib().kvq_strerror(status).decode()
+
+
+def _check(status: int, what: str):
+    if status != KVQ_OK:
+        raise KvqError(status, what)
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(dev):
+    return C.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _dev_tensor(t, dtype, name):
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError("%s must be a CUDA (HIP) tensor" % name)
+    if t.dtype != dtype:
+        raise ValueError("%s must have dtype %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t
+
+
+class Context:
+    """A libkvq context (kvq_create/kvq_destroy) holding the b-bit tables, the
+    random-sign diagonals of K and V per KV head, the QJL projection and the
+    NSN codebook, resident on one GPU."""
+
+    def __init__(self, n_kv_heads: int, bits: int = 3, signs_k=None, signs_v=None, mode: int = KVQ_MODE_MSE,
+                 qjl_S=None, vq_codebook=None, device: int = 0):
+        self.n_kv_heads, self.bits, self.mode, self.device = n_kv_heads, bits, mode, device
+        cfg = kvq_config()
+        cfg.d, cfg.bits, cfg.mode, cfg.n_kv_heads, cfg.device = D, bits, mode, n_kv_heads, device
+        keep = []
+
+        def arr(a, dt, cty):
+            if a is None:
+                return None
+            a = np.ascontiguousarray(np.asarray(a), dtype=dt)
+            keep.append(a)
+            return a.ctypes.data_as(C.POINTER(cty))
+
+        cfg.signs_k = arr(signs_k, np.int8, C.c_int8)
+        cfg.signs_v = arr(signs_v, np.int8, C.c_int8)
+        cfg.qjl_S = arr(qjl_S, np.float32, C.c_float)
+        cfg.vq_codebook = arr(vq_codebook, np.float32, C.c_float)
+        h = C.c_void_p()
+        _check(lib().kvq_create(C.byref(cfg), C.byref(h)), "kvq_create")
+        self.handle = h
+
+    def close(self):
+        if getattr(self, "handle", None):
+            lib().kvq_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def dev(self):
+        return torch.device("cuda", self.device)
+
+    def tables(self):
+        L = 1 << self.bits
+        c = np.zeros(L, np.float32)
+        t = np.zeros(L - 1, np.float32)
+        _check(lib().kvq_get_tables(self.handle, c.ctypes.data_as(C.c_void_p), t.ctypes.data_as(C.c_void_p)),
+               "kvq_get_tables")
+        return c, t
+
+    def code_bytes(self) -> int:
+        return int(lib().kvq_code_bytes_per_vec(self.handle))
+
+    # ------------------------------------------------------------------ quantize
+    def quantize(self, kind: int, x, out=None):
+        """x [B,H_kv,T,128] fp16 -> dict(codes, norms[, qjl_signs, qjl_gamma])."""
+        _dev_tensor(x, torch.float16, "x")
+        B, H, T, d = x.shape
+        if d != D:
+            raise ValueError("last dimension must be 128")
+        qjl = self.mode == KVQ_MODE_MSE_QJL and kind == KVQ_KIND_K
+        if out is None:
+            out = dict(codes=torch.empty((B, H, T, self.code_bytes()), dtype=torch.uint8, device=x.device),
+                       norms=torch.empty((B, H, T), dtype=torch.float32, device=x.device))
+            if qjl:
+                out["qjl_signs"] = torch.empty((B, H, T, 16), dtype=torch.uint8, device=x.device)
+                out["qjl_gamma"] = torch.empty((B, H, T), dtype=torch.float32, device=x.device)
+        kvq_quantize(self, kind, x, B, H, T, out["codes"], out["norms"], out.get("qjl_signs"),
+                     out.get("qjl_gamma"))
+        return out
+
+    def logits(self, q, codes, norms, qjl_signs=None, qjl_gamma=None, out=None):
+        _dev_tensor(q, torch.float16, "q")
+        B, Hq, _ = q.shape
+        T = codes.shape[2]
+        if out is None:
+            out = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+        kvq_logits(self, q, B, Hq, T, codes, norms, qjl_signs, qjl_gamma, out)
+        return out
+
+    def decode_ws(self, B, Hq, T):
+        n = int(lib().kvq_attn_decode_ws_bytes(self.handle, B, Hq, T))
+        return torch.zeros(n, dtype=torch.uint8, device=self.dev)
+
+    def attn_decode(self, q, k_codes, k_norms, v_codes, v_norms, sm_scale: float = 0.0, ws=None, out=None,
+                    n_split: int = 0):
+        _dev_tensor(q, torch.float16, "q")
+        B, Hq, _ = q.shape
+        T = k_codes.shape[2]
+        if ws is None:
+            ws = self.decode_ws(B, Hq, T)
+        if out is None:
+            out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+        kvq_attn_decode_splits(self, q, B, Hq, T, k_codes, k_norms, v_codes, v_norms, sm_scale, out, ws,
+                               n_split)
+        return out
+
+    def nsn_vq_quantize(self, x, out=None, ws=None):
+        _dev_tensor(x, torch.float16, "x")
+        H, T, _ = x.shape
+        if ws is None:
+            ws = torch.empty(int(lib().kvq_nsn_vq_ws_bytes(self.handle, H, T)), dtype=torch.uint8,
+                             device=x.device)
+        if out is None:
+            out = dict(codes=torch.empty((H, T, 16), dtype=torch.uint8, device=x.device),
+                       s1=torch.empty((H, T), dtype=torch.float32, device=x.device),
+                       s2=torch.empty((H, T), dtype=torch.float32, device=x.device),
+                       o=torch.empty((H, D), dtype=torch.float32, device=x.device))
+        kvq_nsn_vq_quantize(self, x, H, T, out["codes"], out["s1"], out["s2"], out["o"], ws)
+        return out
+
+
+# ---------------------------------------------------------------------- C-ABI mirrors
+def kvq_quantize(ctx: Context, kind, x, B, H_kv, T, codes, norms, qjl_signs=None, qjl_gamma=None):
+    _dev_tensor(codes, torch.uint8, "codes")
+    _dev_tensor(norms, torch.float32, "norms")
+    _check(lib().kvq_quantize(ctx.handle, kind, _ptr(x), B, H_kv, T, _ptr(codes), _ptr(norms),
+                              _ptr(qjl_signs), _ptr(qjl_gamma), _stream(x.device)), "kvq_quantize")
+
+
+def kvq_logits(ctx: Context, q, B, H_q, T, codes, norms, qjl_signs, qjl_gamma, logits):
+    _dev_tensor(logits, torch.float32, "logits")
+    _check(lib().kvq_logits(ctx.handle, _ptr(q), B, H_q, T, _ptr(codes), _ptr(norms), _ptr(qjl_signs),
+                            _ptr(qjl_gamma), _ptr(logits), _stream(q.device)), "kvq_logits")
+
+
+def kvq_attn_decode(ctx: Context, q, B, H_q, T, k_codes, k_norms, v_codes, v_norms, sm_scale, out, ws):
+    kvq_attn_decode_splits(ctx, q, B, H_q, T, k_codes, k_norms, v_codes, v_norms, sm_scale, out, ws, 0)
+
+
+def kvq_attn_decode_splits(ctx: Context, q, B, H_q, T, k_codes, k_norms, v_codes, v_norms, sm_scale, out,
+                           ws, n_split):
+    _dev_tensor(out, torch.float32, "out")
+    _check(lib().kvq_attn_decode_splits(ctx.handle, _ptr(q), B, H_q, T, _ptr(k_codes), _ptr(k_norms),
+                                        _ptr(v_codes), _ptr(v_norms), float(sm_scale), _ptr(out), _ptr(ws),
+                                        ws.numel() * ws.element_size(), int(n_split), _stream(q.device)),
+           "kvq_attn_decode")
+
+
+def kvq_nsn_vq_quantize(ctx: Context, x, H, T, codes, s1, s2, o, ws):
+    _check(lib().kvq_nsn_vq_quantize(ctx.handle, _ptr(x), H, T, _ptr(codes), _ptr(s1), _ptr(s2), _ptr(o),
+                                     _ptr(ws), ws.numel() * ws.element_size(), _stream(x.device)),
+           "kvq_nsn_vq_quantize")

@@ -1,0 +1,199 @@
+/*
+ * kvq.h -- C ABI of libkvq: calibration-free rotate-then-quantize compression
+ * of LLM KV-cache vectors, and attention read directly from the packed codes,
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow these pages:
+ *  [PQ]  "PolarQuant: Optimal Gaussian Weight Quantization via Hadamard
+ *        Rotation" (gist.science 2603.29078), Technical summary sec. 2
+ *        Methodology: per-block L2 norm kept, Walsh-Hadamard rotation, scale
+ *        to unit variance, Gaussian Lloyd-Max centroids; dequantisation is
+ *        centroid lookup, inverse (self-inverse) Hadamard, norm restore.
+ *  [TQ]  "O Que E TurboQuant?" (a2a-mcp.org), Como Funciona: Estagio 1
+ *        (random rotation, per-coordinate Lloyd-Max code), Estagio 2 (1-bit
+ *        QJL sign residual for unbiased inner products, attention logits
+ *        computed from the compressed indices); Como Implementar (codebooks
+ *        precomputed per dimension and bit width, query rotated once).
+ *  [NSN] "NSNQuant: A Double Normalization Approach for Calibration-Free
+ *        Low-Bit Vector Quantization of KV Cache" (gist.science 2505.18231),
+ *        Metodologia sec. 1 (Normalize-Shift-Normalize, byproducts s1, o,
+ *        s2), sec. 2 (Hadamard), sec. 3 (one global N(0,1) vector codebook).
+ *
+ * Conventions for every call
+ *  - d = 128 (head dimension).  Vectors are fp16, row-major, tokens
+ *    contiguous: a K or V tensor is [B, H_kv, T, d].
+ *  - Rotation of a vector u: y = H (D .* u) with the +-1 Sylvester Hadamard
+ *    matrix H_ij = (-1)^popcount(i & j) and the random-sign diagonal D of the
+ *    tensor (K or V) and KV head; for a unit vector u this gives coordinates
+ *    of unit variance.
+ *  - b-bit MSE codes: index i of a coordinate y_i is #{j : t_j < y_i} over the
+ *    2^b - 1 thresholds t_j (midpoints of the N(0,1) Lloyd-Max centroids
+ *    c_j, both stored as fp32).  A vector's record is 16*b bytes holding its
+ *    128 indices as an LSB-first bit stream: coordinate i occupies bits
+ *    [b*i, b*i + b).  Records are [B, H_kv, T, 16*b] bytes; the norms
+ *    rho = ||x||_2 are fp32 [B, H_kv, T].  A zero vector has rho = 0 and all
+ *    indices 2^(b-1) - 1.
+ *  - Grouped-query attention: query head h reads KV head h / (H_q / H_kv).
+ *  - All tensor arguments are DEVICE pointers on the context's device,
+ *    16-byte aligned, contiguous, owned by the caller.  `stream` is a
+ *    hipStream_t (NULL = the null stream); every compute call only enqueues
+ *    work on it and returns without synchronising.
+ *  - Errors: arguments are validated on the host before anything is
+ *    launched; a rejected call launches nothing and leaves outputs untouched.
+ *    Launch failures are reported as KVQ_E_DEVICE.  Faults during kernel
+ *    execution surface at the caller's next synchronisation of the stream.
+ *  - A context is immutable after kvq_create: calls on different streams may
+ *    run concurrently as long as their output buffers do not overlap.
+ */
+#ifndef KVQ_H_
+#define KVQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct kvq_ctx kvq_ctx;
+
+typedef enum {
+    KVQ_OK = 0,
+    KVQ_E_INVAL = 1,       /* bad pointer, size, shape or combination      */
+    KVQ_E_UNSUPPORTED = 2, /* valid request this build does not implement  */
+    KVQ_E_DEVICE = 3,      /* no usable GPU, or a HIP runtime/launch error   */
+    KVQ_E_NOMEM = 4,       /* host or device allocation failed              */
+    KVQ_E_WORKSPACE = 5    /* caller workspace smaller than required        */
+} kvq_status;
+
+enum { KVQ_MODE_MSE = 0, KVQ_MODE_MSE_QJL = 1, KVQ_MODE_NSN_VQ = 2 };
+enum { KVQ_KIND_K = 0, KVQ_KIND_V = 1 };
+
+/* Configuration of a context.  Host arrays are copied by kvq_create. */
+typedef struct {
+    int32_t d;                 /* head dimension; must be 128                         */
+    int32_t bits;              /* MSE code width b in {1,2,3,4} (MSE, MSE_QJL modes)  */
+    int32_t mode;              /* KVQ_MODE_*                                          */
+    int32_t n_kv_heads;        /* H_kv >= 1                                           */
+    const int8_t *signs_k;     /* host [n_kv_heads, d], entries +1/-1: D of K  (MSE*) */
+    const int8_t *signs_v;     /* host [n_kv_heads, d], entries +1/-1: D of V  (MSE*) */
+    const float *qjl_S;        /* host [d, d] row-major Gaussian projection (MSE_QJL) */
+    const float *vq_codebook;  /* host [256, 8] fp32 codebook (NSN_VQ)                */
+    int32_t device;            /* HIP device ordinal                                  */
+} kvq_config;
+
+/* Create a context: validates the configuration, builds the b-bit N(0,1)
+ * Lloyd-Max tables ([PQ] sec. 2, [TQ] Como Implementar: codebooks
+ * precomputed per bit width) and uploads them with D, S and the codebook to
+ * the device.  *out receives the context (NULL on failure).
+ * Errors: KVQ_E_INVAL (NULL pointers, d != 128, bits outside 1..4, a sign
+ * entry not +-1, missing table for the mode), KVQ_E_DEVICE (no such device),
+ * KVQ_E_NOMEM. */
+kvq_status kvq_create(const kvq_config *cfg, kvq_ctx **out);
+
+/* Release a context and its device tables.  NULL is accepted (no-op).
+ * The caller must not destroy a context while its work is in flight. */
+kvq_status kvq_destroy(kvq_ctx *ctx);
+
+/* Copy the context's fp32 tables to host memory: centroids [2^b],
+ * thresholds [2^b - 1] (either pointer may be NULL). */
+kvq_status kvq_get_tables(const kvq_ctx *ctx, float *centroids, float *thresholds);
+
+/* The fp32 tables of a bit width without a context or a device: centroids
+ * [2^b] and thresholds [2^b - 1] of the N(0,1) Lloyd-Max quantiser, exactly
+ * as kvq_create stores them ([PQ] sec. 2; [TQ] Como Implementar).
+ * Errors: KVQ_E_INVAL for bits outside 1..4 or NULL outputs. */
+kvq_status kvq_codebook(int32_t bits, float *centroids, float *thresholds);
+
+/* Bytes of one packed record (16*b for MSE modes, 16 for NSN_VQ); 0 if ctx
+ * is NULL. */
+int64_t kvq_code_bytes_per_vec(const kvq_ctx *ctx);
+
+/* Static description of a status code (never NULL). */
+const char *kvq_strerror(kvq_status s);
+
+/* Quantise T tokens of K or V ([PQ] sec. 2 and [TQ] Estagio 1; QJL residual:
+ * [TQ] Estagio 2).
+ *   kind        KVQ_KIND_K or KVQ_KIND_V (selects D)
+ *   x_f16       [B, H_kv, T, d] fp16, H_kv == cfg.n_kv_heads
+ *   codes       out [B, H_kv, T, 16*b] bytes
+ *   norms       out [B, H_kv, T] fp32, rho = ||x||
+ *   qjl_signs   out [B, H_kv, T, 16] bytes, or NULL.  Required for kind K in
+ *               MSE_QJL mode, must be NULL otherwise.  Bit j (LSB-first) is
+ *               [z_j >= 0], z = S r, r = (y - c[idx]) / sqrt(d).
+ *   qjl_gamma   out [B, H_kv, T] fp32 residual norms ||r||, with qjl_signs.
+ * T == 0 or B == 0 is a valid empty call. */
+kvq_status kvq_quantize(kvq_ctx *ctx, int32_t kind, const void *x_f16, int64_t B,
+                        int64_t H_kv, int64_t T, uint8_t *codes, float *norms,
+                        uint8_t *qjl_signs, float *qjl_gamma, void *stream);
+
+/* Attention logits from the packed codes ([TQ] Estagio 2 and Como
+ * Implementar: the query is rotated once, q' = H (D_K .* q), and each key is
+ * scored from its indices without dequantising it):
+ *   logits[b,h,t] = rho_t / d * sum_i q'_i c[idx_t,i]
+ *                 (+ rho_t gamma_t sqrt(pi/2)/d * sum_j (2 sgn_t,j - 1) (S q')_j / sqrt(d)
+ *                    in MSE_QJL mode)
+ *   q_f16       [B, H_q, d] fp16 queries; H_q a multiple of H_kv, H_q/H_kv <= 8
+ *   codes, norms, qjl_signs, qjl_gamma   the K outputs of kvq_quantize
+ *               (qjl_* required in MSE_QJL mode, NULL otherwise)
+ *   logits      out [B, H_q, T] fp32 (raw inner products, no softmax scale) */
+kvq_status kvq_logits(kvq_ctx *ctx, const void *q_f16, int64_t B, int64_t H_q, int64_t T,
+                      const uint8_t *codes, const float *norms, const uint8_t *qjl_signs,
+                      const float *qjl_gamma, float *logits, void *stream);
+
+/* Workspace bytes kvq_attn_decode needs for these sizes (split-K partials
+ * and per-(batch, KV head) arrival counters). */
+size_t kvq_attn_decode_ws_bytes(const kvq_ctx *ctx, int64_t B, int64_t H_q, int64_t T);
+
+/* One decode step of attention over the quantised cache (MSE mode): logits
+ * from the K codes as in kvq_logits, softmax with scale sm_scale (0 means
+ * 1/sqrt(d)), and the V codes dequantised and accumulated:
+ *   out[b,h] = sum_t softmax_t * v_hat_t,  v_hat = rho_V D_V .* (H c[idx_V]) / d
+ * ([PQ] sec. 2 dequantisation; [NSN] Resultados: decode is memory-bound).
+ *   q_f16       [B, H_q, d] fp16
+ *   k_codes/k_norms, v_codes/v_norms   outputs of kvq_quantize for K and V
+ *   out         [B, H_q, d] fp32
+ *   ws          device workspace of at least kvq_attn_decode_ws_bytes() bytes.
+ *               Its counter words must be zero before the first call that
+ *               uses it (e.g. allocate it zero-filled); every completed call
+ *               leaves them zero again.  Calls that share a workspace must be
+ *               ordered on one stream.
+ * T must be >= 1.  Errors: KVQ_E_WORKSPACE if ws_bytes is too small. */
+kvq_status kvq_attn_decode(kvq_ctx *ctx, const void *q_f16, int64_t B, int64_t H_q, int64_t T,
+                           const uint8_t *k_codes, const float *k_norms,
+                           const uint8_t *v_codes, const float *v_norms, float sm_scale,
+                           float *out, void *ws, size_t ws_bytes, void *stream);
+
+/* As kvq_attn_decode with an explicit number of token splits per (batch, KV
+ * head) (0 = automatic).  The result does not depend on n_split beyond fp32
+ * rounding.  n_split is clamped to [1, ceil(T / 64)]. */
+kvq_status kvq_attn_decode_splits(kvq_ctx *ctx, const void *q_f16, int64_t B, int64_t H_q,
+                                  int64_t T, const uint8_t *k_codes, const float *k_norms,
+                                  const uint8_t *v_codes, const float *v_norms, float sm_scale,
+                                  float *out, void *ws, size_t ws_bytes, int32_t n_split,
+                                  void *stream);
+
+/* Workspace bytes kvq_nsn_vq_quantize needs for H heads of T tokens. */
+size_t kvq_nsn_vq_ws_bytes(const kvq_ctx *ctx, int64_t H, int64_t T);
+
+/* NSN vector quantisation ([NSN] Metodologia 1-3), per head over the T
+ * tokens of the call:
+ *   a_t = sqrt(d) x_t/||x_t||, s1_t = ||x_t||/sqrt(d);  o = mean_t a_t;
+ *   b_t = a_t - o, s2_t = ||b_t||/sqrt(d);  z_t = H (b_t / s2_t) / sqrt(d);
+ *   each 8-dim sub-vector of z_t -> index of the nearest codebook entry
+ *   (squared Euclidean distance; lowest index on ties).
+ *   x_f16   [H, T, d] fp16
+ *   codes   out [H, T, 16] bytes (one per sub-vector)
+ *   s1, s2  out [H, T] fp32;  o  out [H, d] fp32
+ *   ws      device workspace, kvq_nsn_vq_ws_bytes() bytes (no init needed).
+ * Degenerate tokens: ||x_t|| = 0 gives a_t = 0; s2_t = 0 gives z_t = 0.
+ * T must be >= 1.  Requires a context in KVQ_MODE_NSN_VQ. */
+kvq_status kvq_nsn_vq_quantize(kvq_ctx *ctx, const void *x_f16, int64_t H, int64_t T,
+                               uint8_t *codes, float *s1, float *s2, float *o, void *ws,
+                               size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H_ */

@@ -1,0 +1,89 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol that
+include/kvq.h declares, validates arguments on the host and builds the same
+fp32 Lloyd-Max tables as the oracle."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+from calibration_free_kv_amd import kvq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    src = open(os.path.join(ROOT, "include", "kvq.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvq_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    L = kvq.lib()
+    names = declared_symbols()
+    assert len(names) >= 13
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(kvq.EXPORTS) == names
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_library_tables_equal_oracle_tables(bits):
+    c, t = kvq.kvq_codebook(bits)
+    co, to = O.tables_f32(bits)
+    assert np.array_equal(c, co) and np.array_equal(t, to)
+
+
+def test_codebook_rejects_bad_bits():
+    buf = np.zeros(32, np.float32)
+    for b in (0, 5, -1):
+        assert kvq.lib().kvq_codebook(b, buf.ctypes.data_as(C.c_void_p), buf.ctypes.data_as(C.c_void_p)) == kvq.KVQ_E_INVAL
+
+
+def _cfg(**kw):
+    cfg = kvq.kvq_config()
+    cfg.d, cfg.bits, cfg.mode, cfg.n_kv_heads, cfg.device = 128, 3, 0, 2, 0
+    s = np.ones((2, 128), np.int8)
+    cfg.signs_k = s.ctypes.data_as(C.POINTER(C.c_int8))
+    cfg.signs_v = s.ctypes.data_as(C.POINTER(C.c_int8))
+    for k, v in kw.items():
+        setattr(cfg, k, v)
+    return cfg, s
+
+
+def test_create_validation():
+    L = kvq.lib()
+    h = C.c_void_p()
+    assert L.kvq_create(None, C.byref(h)) == kvq.KVQ_E_INVAL
+    for bad in (dict(d=64), dict(bits=0), dict(bits=5), dict(n_kv_heads=0), dict(mode=7)):
+        cfg, keep = _cfg(**bad)
+        assert L.kvq_create(C.byref(cfg), C.byref(h)) == kvq.KVQ_E_INVAL, bad
+        assert not h.value
+    cfg, keep = _cfg()
+    bad_signs = np.zeros((2, 128), np.int8)  # 0 is not a sign
+    cfg.signs_k = bad_signs.ctypes.data_as(C.POINTER(C.c_int8))
+    assert L.kvq_create(C.byref(cfg), C.byref(h)) == kvq.KVQ_E_INVAL
+    cfg, keep = _cfg(mode=1)  # QJL mode needs S
+    assert L.kvq_create(C.byref(cfg), C.byref(h)) == kvq.KVQ_E_INVAL
+    cfg, keep = _cfg(mode=2)  # NSN mode needs a codebook
+    assert L.kvq_create(C.byref(cfg), C.byref(h)) == kvq.KVQ_E_INVAL
+    cfg, keep = _cfg(device=999)  # no such device (no device at all on a CPU host)
+    assert L.kvq_create(C.byref(cfg), C.byref(h)) == kvq.KVQ_E_DEVICE
+    assert not h.value
+
+
+def test_null_context_calls():
+    L = kvq.lib()
+    assert L.kvq_destroy(None) == kvq.KVQ_OK
+    assert L.kvq_code_bytes_per_vec(None) == 0
+    assert L.kvq_get_tables(None, None, None) == kvq.KVQ_E_INVAL
+    assert L.kvq_quantize(None, 0, None, 1, 1, 1, None, None, None, None, None) == kvq.KVQ_E_INVAL
+    assert L.kvq_logits(None, None, 1, 1, 1, None, None, None, None, None, None) == kvq.KVQ_E_INVAL
+    assert L.kvq_attn_decode(None, None, 1, 1, 1, None, None, None, None, 0.0, None, None, 0, None) == kvq.KVQ_E_INVAL
+    assert L.kvq_attn_decode_ws_bytes(None, 1, 1, 1) == 0
+    assert L.kvq_nsn_vq_ws_bytes(None, 1, 1) == 0
+    assert L.kvq_nsn_vq_quantize(None, None, 1, 1, None, None, None, None, None, 0, None) == kvq.KVQ_E_INVAL
+    for s in range(6):
+        assert kvq.strerror(s)
