@@ -143,6 +143,9 @@ kvq_status kvq_create(const kvq_config *cfg, kvq_ctx **out)
     c->mode = mode;
     c->H = H;
     c->device = cfg->device;
+    if (hipDeviceGetAttribute(&c->n_cu, hipDeviceAttributeMultiprocessorCount, cfg->device) != hipSuccess ||
+        c->n_cu < 1)
+        c->n_cu = 256;
     build_codebook(c->bits, &c->cb);
 
     kvq_status st = KVQ_OK;
@@ -240,6 +243,24 @@ kvq_status kvq_quantize(kvq_ctx *ctx, int32_t kind, const void *x_f16, int64_t B
                                               qjl_gamma, (hipStream_t)stream));
 }
 
+kvq_status kvq_quantize_kv(kvq_ctx *ctx, const void *k_f16, const void *v_f16, int64_t B, int64_t H_kv,
+                           int64_t T, uint8_t *k_codes, float *k_norms, uint8_t *v_codes, float *v_norms,
+                           void *stream)
+{
+    if (!ctx || ctx->mode != KVQ_MODE_MSE) return KVQ_E_INVAL;
+    if (B < 0 || T < 0 || H_kv != ctx->H) return KVQ_E_INVAL;
+    if (B == 0 || T == 0) return KVQ_OK;
+    if (!k_f16 || !v_f16 || !k_codes || !k_norms || !v_codes || !v_norms) return KVQ_E_INVAL;
+    if (!aligned(k_f16, 16) || !aligned(v_f16, 16) || !aligned(k_codes, 16) || !aligned(v_codes, 16) ||
+        !aligned(k_norms, 4) || !aligned(v_norms, 4))
+        return KVQ_E_INVAL;
+    if (B * H_kv > (int64_t(1) << 40) || T > (int64_t(1) << 31)) return KVQ_E_INVAL;
+    DeviceGuard g(ctx->device);
+    if (!g.ok) return KVQ_E_DEVICE;
+    return launch_status(kvq::launch_quantize_kv(ctx, k_f16, v_f16, B, T, k_codes, k_norms, v_codes, v_norms,
+                                                 (hipStream_t)stream));
+}
+
 kvq_status kvq_logits(kvq_ctx *ctx, const void *q_f16, int64_t B, int64_t H_q, int64_t T,
                       const uint8_t *codes, const float *norms, const uint8_t *qjl_signs,
                       const float *qjl_gamma, float *logits, void *stream)
@@ -282,7 +303,7 @@ kvq_status kvq_attn_decode_splits(kvq_ctx *ctx, const void *q_f16, int64_t B, in
         return KVQ_E_INVAL;
     if (T > (int64_t(1) << 31)) return KVQ_E_INVAL;
     if (ws_bytes < kvq::decode_ws_bytes(B, H_q, ctx->H, T)) return KVQ_E_WORKSPACE;
-    const int64_t max_split = (T + 63) / 64;
+    const int64_t max_split = kvq::decode_max_splits(T);
     int ns = n_split == 0 ? kvq::decode_auto_splits(B, ctx->H, T) : n_split;
     if (ns > max_split) ns = (int)max_split;
     if (ns < 1) ns = 1;

@@ -26,6 +26,7 @@ struct Codebook {
 
 struct kvq_ctx {
     int d, bits, mode, H, device;
+    int n_cu;             // compute units of the device
     kvq::Codebook cb;
     uint32_t *d_sgnmask;  // [2][H][64]: fp16-pair sign masks of D_K, D_V
     float *d_signs;       // [2][H][128]: D_K, D_V as +-1.0f
@@ -40,10 +41,20 @@ hipError_t launch_quantize(const kvq_ctx *ctx, int kind, const void *x, int64_t 
                            uint8_t *codes, float *norms, uint8_t *qjl_signs, float *qjl_gamma,
                            hipStream_t s);
 
+hipError_t launch_quantize_kv(const kvq_ctx *ctx, const void *k, const void *v, int64_t B, int64_t T,
+                              uint8_t *k_codes, float *k_norms, uint8_t *v_codes, float *v_norms,
+                              hipStream_t s);
+
 hipError_t launch_logits(const kvq_ctx *ctx, const void *q, int64_t B, int64_t Hq, int64_t T,
                          const uint8_t *codes, const float *norms, const uint8_t *qjl_signs,
                          const float *qjl_gamma, float *logits, hipStream_t s);
 
+constexpr int kMaxSplits = 512;  // token splits per (batch, KV head) in decode
+inline int64_t decode_max_splits(int64_t T)
+{
+    const int64_t m = (T + 63) / 64;
+    return m < kMaxSplits ? m : kMaxSplits;
+}
 size_t decode_ws_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t T);
 int decode_auto_splits(int64_t B, int64_t Hkv, int64_t T);
 

@@ -218,8 +218,9 @@ struct DecSmem {
     static constexpr int red = vrec + kDecTile * (FD::W + 1);   // [16][G] reductions
     static constexpr int c2 = red + 16 * G;                      // [2^(2b)][2] centroid pairs
     static constexpr int total = c2 + 2 * (1 << (2 * BITS));
-    // the phase reduction at the end reuses pw and vrec
+    // the phase reduction and the split merge at the end reuse pw and vrec
     static_assert(red - pw >= kVPhases * G * kD, "phase buffer does not fit");
+    static_assert(red - pw >= 2 * kMaxSplits * G, "merge buffer does not fit kMaxSplits splits");
 };
 
 template <int BITS, int G>
@@ -397,20 +398,39 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
     if (!last) return;
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 
-    float *o = qr;  // reuse: [G][128]
+    // Merge weights per (split, head): f = 2^(m_s - M) / (d L), L = sum_s l_s 2^(m_s - M).
+    float *ms = pw;                   // reuse: [n_split][G] split maxima, then weights
+    float *ls = pw + n_split * G;     // [n_split][G] split sums
+    float *o = qr;                    // reuse: [G][128]
     const float *all = part + (bh * n_split) * G * (kD + 2);
+    for (int idx = tid; idx < n_split * G; idx += kDecThreads) {
+        ms[idx] = all[idx * (kD + 2)];
+        ls[idx] = all[idx * (kD + 2) + 1];
+    }
+    __syncthreads();
+    if (tid < G) {
+        float M = -INFINITY;
+        for (int sp = 0; sp < n_split; ++sp) M = fmaxf(M, ms[sp * G + tid]);
+        float L = 0.0f;
+        for (int sp = 0; sp < n_split; ++sp) L += ls[sp * G + tid] * exp2f(ms[sp * G + tid] - M);
+        const float inv = 1.0f / (L * kD);
+        for (int sp = 0; sp < n_split; ++sp) ms[sp * G + tid] = exp2f(ms[sp * G + tid] - M) * inv;
+    }
+    __syncthreads();
     for (int idx = tid; idx < G * kD; idx += kDecThreads) {
         const int h = idx >> 7, i = idx & (kD - 1);
-        float M = -INFINITY;
-        for (int sp = 0; sp < n_split; ++sp) M = fmaxf(M, all[(sp * G + h) * (kD + 2)]);
-        float L = 0.0f, A = 0.0f;
-        for (int sp = 0; sp < n_split; ++sp) {
-            const float *r = all + (sp * G + h) * (kD + 2);
-            const float f = exp2f(r[0] - M);
-            L += r[1] * f;
-            A += r[2 + i] * f;
+        const float *col = all + h * (kD + 2) + 2 + i;
+        float A = 0.0f;
+        int sp = 0;
+        for (; sp + 8 <= n_split; sp += 8) {  // 8 independent loads in flight
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = col[(int64_t)(sp + u) * G * (kD + 2)];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) A = fmaf(ms[(sp + u) * G + h], v[u], A);
         }
-        o[idx] = A / (L * kD);
+        for (; sp < n_split; ++sp) A = fmaf(ms[sp * G + h], col[(int64_t)sp * G * (kD + 2)], A);
+        o[idx] = A;
     }
     // inverse rotation: out = D_V .* H o
     for (int s2 = 1; s2 < kD; s2 <<= 1) {
@@ -537,7 +557,7 @@ hipError_t launch_logits(const kvq_ctx *ctx, const void *q, int64_t B, int64_t H
 size_t decode_ws_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t T)
 {
     const int64_t bhs = B * Hkv;
-    const int64_t max_split = (T + 63) / 64;
+    const int64_t max_split = decode_max_splits(T);
     return ((bhs * sizeof(unsigned) + 255) / 256) * 256 +
            (size_t)(B * Hq) * (size_t)max_split * (kD + 2) * sizeof(float);
 }

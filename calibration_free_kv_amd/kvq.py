@@ -23,7 +23,7 @@ D = 128
 
 EXPORTS = [
     "kvq_create", "kvq_destroy", "kvq_get_tables", "kvq_codebook", "kvq_code_bytes_per_vec", "kvq_strerror",
-    "kvq_quantize", "kvq_logits", "kvq_attn_decode_ws_bytes", "kvq_attn_decode",
+    "kvq_quantize", "kvq_quantize_kv", "kvq_logits", "kvq_attn_decode_ws_bytes", "kvq_attn_decode",
     "kvq_attn_decode_splits", "kvq_nsn_vq_ws_bytes", "kvq_nsn_vq_quantize",
 ]
 
@@ -64,6 +64,7 @@ def lib():
         L.kvq_strerror.argtypes = [C.c_int]
         L.kvq_strerror.restype = C.c_char_p
         L.kvq_quantize.argtypes = [vp, i32, vp, i64, i64, i64, vp, vp, vp, vp, vp]
+        L.kvq_quantize_kv.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, vp, vp, vp]
         L.kvq_logits.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, vp, vp, vp]
         L.kvq_attn_decode_ws_bytes.argtypes = [vp, i64, i64, i64]
         L.kvq_attn_decode_ws_bytes.restype = sz
@@ -184,6 +185,16 @@ class Context:
                      out.get("qjl_gamma"))
         return out
 
+    def quantize_kv(self, k, v):
+        """K and V [B,H_kv,T,128] fp16 in one launch -> (K outputs, V outputs)."""
+        _dev_tensor(k, torch.float16, "k")
+        B, H, T, _ = k.shape
+        mk = lambda: dict(codes=torch.empty((B, H, T, self.code_bytes()), dtype=torch.uint8, device=k.device),  # noqa: E731
+                          norms=torch.empty((B, H, T), dtype=torch.float32, device=k.device))
+        ko, vo = mk(), mk()
+        kvq_quantize_kv(self, k, v, B, H, T, ko["codes"], ko["norms"], vo["codes"], vo["norms"])
+        return ko, vo
+
     def logits(self, q, codes, norms, qjl_signs=None, qjl_gamma=None, out=None):
         _dev_tensor(q, torch.float16, "q")
         B, Hq, _ = q.shape
@@ -231,6 +242,15 @@ def kvq_quantize(ctx: Context, kind, x, B, H_kv, T, codes, norms, qjl_signs=None
     _dev_tensor(norms, torch.float32, "norms")
     _check(lib().kvq_quantize(ctx.handle, kind, _ptr(x), B, H_kv, T, _ptr(codes), _ptr(norms),
                               _ptr(qjl_signs), _ptr(qjl_gamma), _stream(x.device)), "kvq_quantize")
+
+
+def kvq_quantize_kv(ctx: Context, k, v, B, H_kv, T, k_codes, k_norms, v_codes, v_norms):
+    for t, dt, n in ((k, torch.float16, "k"), (v, torch.float16, "v"), (k_codes, torch.uint8, "k_codes"),
+                     (v_codes, torch.uint8, "v_codes"), (k_norms, torch.float32, "k_norms"),
+                     (v_norms, torch.float32, "v_norms")):
+        _dev_tensor(t, dt, n)
+    _check(lib().kvq_quantize_kv(ctx.handle, _ptr(k), _ptr(v), B, H_kv, T, _ptr(k_codes), _ptr(k_norms),
+                                 _ptr(v_codes), _ptr(v_norms), _stream(k.device)), "kvq_quantize_kv")
 
 
 def kvq_logits(ctx: Context, q, B, H_q, T, codes, norms, qjl_signs, qjl_gamma, logits):

@@ -127,6 +127,14 @@ kvq_status kvq_quantize(kvq_ctx *ctx, int32_t kind, const void *x_f16, int64_t B
                         int64_t H_kv, int64_t T, uint8_t *codes, float *norms,
                         uint8_t *qjl_signs, float *qjl_gamma, void *stream);
 
+/* kvq_quantize of K (with D_K) and of V (with D_V) of the same shape in one
+ * launch, e.g. the K and V of the tokens just produced by a layer (MSE mode
+ * only).  Arguments and outputs as in kvq_quantize; the results are
+ * identical to two kvq_quantize calls. */
+kvq_status kvq_quantize_kv(kvq_ctx *ctx, const void *k_f16, const void *v_f16, int64_t B, int64_t H_kv,
+                           int64_t T, uint8_t *k_codes, float *k_norms, uint8_t *v_codes, float *v_norms,
+                           void *stream);
+
 /* Attention logits from the packed codes ([TQ] Estagio 2 and Como
  * Implementar: the query is rotated once, q' = H (D_K .* q), and each key is
  * scored from its indices without dequantising it):
@@ -166,7 +174,7 @@ kvq_status kvq_attn_decode(kvq_ctx *ctx, const void *q_f16, int64_t B, int64_t H
 
 /* As kvq_attn_decode with an explicit number of token splits per (batch, KV
  * head) (0 = automatic).  The result does not depend on n_split beyond fp32
- * rounding.  n_split is clamped to [1, ceil(T / 64)]. */
+ * rounding.  n_split is clamped to [1, min(512, ceil(T / 64))]. */
 kvq_status kvq_attn_decode_splits(kvq_ctx *ctx, const void *q_f16, int64_t B, int64_t H_q,
                                   int64_t T, const uint8_t *k_codes, const float *k_norms,
                                   const uint8_t *v_codes, const float *v_norms, float sm_scale,

@@ -96,3 +96,18 @@ def test_deterministic():
     b = ctx.quantize(0, x)
     torch.cuda.synchronize()
     assert torch.equal(a["codes"], b["codes"]) and torch.equal(a["norms"], b["norms"])
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_quantize_kv_fused_equals_separate(bits):
+    inp = synth.make("l8b32k", T=1500, B=2)
+    ctx = kvq.Context(8, bits, inp["signs_k"], inp["signs_v"])
+    k = torch.from_numpy(inp["k"]).cuda()
+    v = torch.from_numpy(inp["v"]).cuda()
+    ko, vo = ctx.quantize_kv(k, v)
+    ks = ctx.quantize(kvq.KVQ_KIND_K, k)
+    vs = ctx.quantize(kvq.KVQ_KIND_V, v)
+    torch.cuda.synchronize()
+    for a, b in ((ko, ks), (vo, vs)):
+        assert torch.equal(a["codes"], b["codes"]) and torch.equal(a["norms"], b["norms"])
+    check_codes(inp["v"], inp["signs_v"], bits, to_np(vo["codes"]), to_np(vo["norms"]), label="fused V")

@@ -112,3 +112,12 @@ def test_decode_workspace_reuse_and_too_small():
     with pytest.raises(kvq.KvqError) as e:
         ctx.attn_decode(q, k["codes"], k["norms"], v["codes"], v["norms"], ws=ws[:16])
     assert e.value.status == kvq.KVQ_E_WORKSPACE
+
+
+def test_decode_split_request_is_clamped():
+    """More splits than 512 (or than 64-token chunks) are clamped, not overrun."""
+    inp, ctx, k, v = quantized("l8b32k", 2, T=33000)
+    q = torch.from_numpy(inp["q"]).cuda()
+    ref = to_np(ctx.attn_decode(q, k["codes"], k["norms"], v["codes"], v["norms"]))
+    big = to_np(ctx.attn_decode(q, k["codes"], k["norms"], v["codes"], v["norms"], n_split=100000))
+    np.testing.assert_allclose(big, ref, rtol=1e-4, atol=1e-5)
