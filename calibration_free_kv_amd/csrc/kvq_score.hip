@@ -19,6 +19,8 @@ namespace {
 
 typedef _Float16 half_t;
 typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+typedef float f2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
 
@@ -71,8 +73,9 @@ __device__ void rotate_queries(const half_t *__restrict__ q, const float *__rest
     __syncthreads();
 }
 
+// ctab: the 2^b centroids already in LDS.
 template <int BITS, int G>
-__device__ void build_tables(const float *qr, const Codebook &cb, float *lut)
+__device__ void build_tables(const float *qr, const float *ctab, float *lut)
 {
     using FD = Fields<BITS>;
     constexpr uint32_t mask = (1u << BITS) - 1u;
@@ -83,12 +86,18 @@ __device__ void build_tables(const float *qr, const Codebook &cb, float *lut)
         const int f = idx / (G * FD::E);
         float v = 0.0f;
 #pragma unroll
-        for (int k = 0; k < FD::F; ++k) v += qr[h * kD + FD::F * f + k] * cb.c[(e >> (BITS * k)) & mask];
+        for (int k = 0; k < FD::F; ++k) v += qr[h * kD + FD::F * f + k] * ctab[(e >> (BITS * k)) & mask];
         lut[idx] = v * inv_d;
     }
 }
 
-// Sum of the table entries of one record for the G heads.
+__device__ __forceinline__ void stage_centroids(const Codebook &cb, float *ctab)
+{
+    if (threadIdx.x < 16) ctab[threadIdx.x] = cb.c[threadIdx.x];
+}
+
+// Sum of the table entries of one record for the G heads (the G entries of a
+// (field, value) pair are read with one 16- or 8-byte LDS load).
 template <int BITS, int G>
 __device__ __forceinline__ void score_record(const uint32_t *Wd, const float *lut, float *acc)
 {
@@ -97,9 +106,23 @@ __device__ __forceinline__ void score_record(const uint32_t *Wd, const float *lu
     for (int h = 0; h < G; ++h) acc[h] = 0.0f;
 #pragma unroll
     for (int f = 0; f < FD::NF; ++f) {
-        const float *e = lut + (f * FD::E + (int)field<BITS>(Wd, f)) * G;
+        const int e = f * FD::E + (int)field<BITS>(Wd, f);
+        if constexpr (G % 4 == 0) {
 #pragma unroll
-        for (int h = 0; h < G; ++h) acc[h] += e[h];
+            for (int h4 = 0; h4 < G / 4; ++h4) {
+                const f4_t x = reinterpret_cast<const f4_t *>(lut)[e * (G / 4) + h4];
+                acc[4 * h4] += x.x;
+                acc[4 * h4 + 1] += x.y;
+                acc[4 * h4 + 2] += x.z;
+                acc[4 * h4 + 3] += x.w;
+            }
+        } else if constexpr (G == 2) {
+            const f2_t x = reinterpret_cast<const f2_t *>(lut)[e];
+            acc[0] += x.x;
+            acc[1] += x.y;
+        } else {
+            acc[0] += lut[e];
+        }
     }
 }
 
@@ -132,19 +155,21 @@ __global__ __launch_bounds__(kThreads) void k_logits(
     int64_t blocks_per_bh)
 {
     using FD = Fields<BITS>;
-    extern __shared__ float smem[];
+    extern __shared__ __align__(16) float smem[];
     float *qr = smem;                       // [G][128]
     float *lut = qr + G * kD;               // [NF][E][G]
     float *slut = lut + FD::NF * FD::E * G; // [32][16][G] (QJL)
     float *pq = slut + (QJL ? 32 * 16 * G : 0);  // [G][128] (QJL)
+    float *ctab = pq + (QJL ? G * kD : 0);       // [16] centroids
 
     const int64_t bh = blockIdx.x / blocks_per_bh;
     const int64_t part = blockIdx.x - bh * blocks_per_bh;
     const int64_t b = bh / H;
     const int g = (int)(bh - b * H);
 
+    stage_centroids(cb, ctab);
     rotate_queries<BITS, G>(q, signs, b, g, Hq, qr);
-    build_tables<BITS, G>(qr, cb, lut);
+    build_tables<BITS, G>(qr, ctab, lut);
     if constexpr (QJL) {
         const float inv_sqrt_d = 0.08838834764831845f;
         for (int idx = threadIdx.x; idx < G * kD; idx += kThreads) {
@@ -196,32 +221,73 @@ __global__ __launch_bounds__(kThreads) void k_logits(
 }
 
 // ---------------------------------------------------------------------------
-// kvq_attn_decode: split-K flash decoding.  Block (b, g, split) scores its
-// token range tile by tile (one key per thread), keeps a running max m and
-// sum l per head (base-2 exponentials of the logits scaled by
-// sm_scale*log2(e)), and accumulates the V codes in the rotated domain:
-// acc_h[i] += p_h,t rho_t c[idx_t,i].  Each block writes (m, l, acc) for its
-// G heads; the last block of a (b, g) to finish (arrival counter) merges the
-// splits and applies the inverse rotation once: out_h = D_V .* H acc / (d l).
+// kvq_attn_decode: split-K flash decoding.  Block (b, g, split) owns a token
+// range of one (batch, KV head).  After the shared prologue (rotated queries,
+// K field tables) every wave works alone on 64-token tiles of the range:
+//  K  lane = token: logit from the field tables, scaled by rho_K and by
+//     sm_scale*log2(e); wave max / sum give a running (m, l) per head
+//     (base-2 exponentials);
+//  V  lane = 4 consecutive coordinates and one token parity: the weights
+//     p_h,t rho_V,t and the staged V records are read from the wave's LDS and
+//     accumulated in the rotated domain, acc_h[i] += p rho_V c[idx_t,i].
+// The block's waves merge once at the end; the block writes (m, l, acc) for
+// its G heads and the last block of a (b, g) to finish (arrival counter)
+// merges the splits and applies the inverse rotation once:
+// out_h = D_V .* H acc / (d l).
 // ---------------------------------------------------------------------------
-constexpr int kDecThreads = 512;
-constexpr int kDecTile = kDecThreads;  // tokens per tile, one per thread for K
-constexpr int kVPhases = kDecThreads / 64;  // V: 64 coordinate pairs x phases
+constexpr int kDecWaves = 16;
+constexpr int kDecThreads = kDecWaves * 64;
 
 template <int BITS, int G>
 struct DecSmem {
     using FD = Fields<BITS>;
-    static constexpr int qr = 0;
-    static constexpr int lut = qr + G * kD;
-    static constexpr int pw = lut + FD::NF * FD::E * G;          // [tile][G] weights p*rho_V
-    static constexpr int vrec = pw + kDecTile * G;               // [tile][W+1] V records (dwords)
-    static constexpr int red = vrec + kDecTile * (FD::W + 1);   // [16][G] reductions
-    static constexpr int c2 = red + 16 * G;                      // [2^(2b)][2] centroid pairs
-    static constexpr int total = c2 + 2 * (1 << (2 * BITS));
-    // the phase reduction and the split merge at the end reuse pw and vrec
-    static_assert(red - pw >= kVPhases * G * kD, "phase buffer does not fit");
-    static_assert(red - pw >= 2 * kMaxSplits * G, "merge buffer does not fit kMaxSplits splits");
+    static constexpr int RW = FD::W + 1;                          // staged record words (+ guard)
+    static constexpr int qr = 0;                                  // [G][128]
+    static constexpr int lut = qr + G * kD;                       // [NF][E][G]
+    static constexpr int c2 = lut + FD::NF * FD::E * G;           // [2^(2b)][2] centroid pairs
+    static constexpr int vbuf = c2 + 2 * (1 << (2 * BITS));       // [waves][64][RW] V records
+    static constexpr int wbuf = vbuf + kDecWaves * 64 * RW;       // [waves][64][G] weights
+    static constexpr int wm = wbuf + kDecWaves * 64 * G;          // [waves][G] wave maxima
+    static constexpr int wl = wm + kDecWaves * G;                 // [waves][G] wave sums
+    static constexpr int ctab = wl + kDecWaves * G;               // [16] centroids
+    static constexpr int total = ctab + 16;
+    // end-of-block reuse of vbuf..wbuf: per-wave accumulators, split merge
+    static_assert(wm - vbuf >= kDecWaves * G * kD, "wave merge buffer does not fit");
+    static_assert(wm - vbuf >= 2 * kMaxSplits * G, "split merge buffer does not fit");
 };
+
+// Wave-wide max / sum, result in every lane: four DPP steps inside each row
+// of 16 lanes, then two exchanges across rows.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float wave_max(float x)
+{
+    x = fmaxf(x, dpp<0xB1>(x));   // quad_perm [1,0,3,2]
+    x = fmaxf(x, dpp<0x4E>(x));   // quad_perm [2,3,0,1]
+    x = fmaxf(x, dpp<0x141>(x));  // row_half_mirror
+    x = fmaxf(x, dpp<0x140>(x));  // row_mirror
+    x = fmaxf(x, __shfl_xor(x, 16));
+    return fmaxf(x, __shfl_xor(x, 32));
+}
+__device__ __forceinline__ float wave_sum(float x)
+{
+    x += dpp<0xB1>(x);
+    x += dpp<0x4E>(x);
+    x += dpp<0x141>(x);
+    x += dpp<0x140>(x);
+    x += __shfl_xor(x, 16);
+    return x + __shfl_xor(x, 32);
+}
+// LDS written by some lanes of a wave is read by other lanes of the same wave.
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
 template <int BITS, int G>
 __global__ __launch_bounds__(kDecThreads) void k_decode(
@@ -233,22 +299,24 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
 {
     using FD = Fields<BITS>;
     using SM = DecSmem<BITS, G>;
-    extern __shared__ float smem[];
+    constexpr int RW = SM::RW;
+    extern __shared__ __align__(16) float smem[];
     float *qr = smem + SM::qr;
     float *lut = smem + SM::lut;
-    float *pw = smem + SM::pw;
-    uint32_t *vrec = reinterpret_cast<uint32_t *>(smem + SM::vrec);
-    float *red = smem + SM::red;
     float *c2 = smem + SM::c2;
 
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    uint32_t *vbuf = reinterpret_cast<uint32_t *>(smem + SM::vbuf) + wv * 64 * RW;
+    float *wbuf = smem + SM::wbuf + wv * 64 * G;
     const int64_t bh = blockIdx.x / n_split;
     const int split = (int)(blockIdx.x - bh * n_split);
     const int64_t b = bh / H;
     const int g = (int)(bh - b * H);
 
+    stage_centroids(cb, smem + SM::ctab);
     rotate_queries<BITS, G>(q, signs_k, b, g, Hq, qr);
-    build_tables<BITS, G>(qr, cb, lut);
+    build_tables<BITS, G>(qr, smem + SM::ctab, lut);
     constexpr uint32_t cm = (1u << BITS) - 1u;
     for (int e = tid; e < (1 << (2 * BITS)); e += kDecThreads) {
         c2[2 * e] = cb.c[e & cm];
@@ -256,151 +324,166 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
     }
     __syncthreads();
 
-    // V work split: thread -> coordinate pair cp (coordinates 2cp, 2cp+1) and
-    // token phase ph (tokens ph, ph + kVPhases, ... of the tile).
-    const int cp = tid & 63, ph = tid >> 6;
-    float m_run[G], l_run[G], acc0[G], acc1[G];
+    // V lane roles: coordinate quad cq (coordinates 4cq .. 4cq+3), token parity.
+    const int cq = lane & 31, par = lane >> 5;
+    constexpr int QB = 4 * BITS;                  // bits of a quad
+    const int qbit = QB * cq, qwd = qbit >> 5, qsh = qbit & 31;
+    constexpr uint32_t fmask = (1u << (2 * BITS)) - 1u;
+
+    float m_run[G], l_run[G], acc[G][4];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
         m_run[h] = -INFINITY;
         l_run[h] = 0.0f;
-        acc0[h] = 0.0f;
-        acc1[h] = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) acc[h][k] = 0.0f;
     }
 
     const int64_t t_begin = (int64_t)split * chunk;
     const int64_t t_end = min(T, t_begin + chunk);
-    for (int64_t t0 = t_begin; t0 < t_end; t0 += kDecTile) {
-        const int nt = (int)min((int64_t)kDecTile, t_end - t0);
-        // K: one key per thread.
-        float s[G];
-        const bool valid = tid < nt;
-        if (valid) {
-            const int64_t v = bh * T + t0 + tid;
-            uint32_t Wd[FD::W + 1];
-            load_record<BITS>(kc, v, Wd);
-            score_record<BITS, G>(Wd, lut, s);
-            const float rs = kn[v] * scale_log2;
-#pragma unroll
-            for (int h = 0; h < G; ++h) s[h] *= rs;
-            // stage the V record of this token
+    // Records of the wave's current tile are held in registers; the next
+    // tile's loads are issued before the current tile is processed.
+    uint32_t Kw[FD::W + 1], Vw[FD::W];
+    float rk = 0.0f, rv = 0.0f;
+    auto fetch = [&](int64_t t0) {
+        const int64_t t = t0 + lane;
+        if (t0 < t_end && t < t_end) {
+            const int64_t v = bh * T + t;
+            load_record<BITS>(kc, v, Kw);
             const u4_t *src = reinterpret_cast<const u4_t *>(vc) + v * BITS;
 #pragma unroll
             for (int k = 0; k < BITS; ++k) {
                 const u4_t x = src[k];
-                uint32_t *d = vrec + tid * (FD::W + 1) + 4 * k;
-                d[0] = x.x;
-                d[1] = x.y;
-                d[2] = x.z;
-                d[3] = x.w;
+                Vw[4 * k] = x.x;
+                Vw[4 * k + 1] = x.y;
+                Vw[4 * k + 2] = x.z;
+                Vw[4 * k + 3] = x.w;
             }
-            vrec[tid * (FD::W + 1) + FD::W] = 0u;
+            rk = kn[v];
+            rv = vn[v];
+        }
+    };
+    constexpr int64_t kStride = (int64_t)kDecWaves * 64;
+    fetch(t_begin + (int64_t)wv * 64);
+    for (int64_t t0 = t_begin + (int64_t)wv * 64; t0 < t_end; t0 += kStride) {
+        const int nt = (int)min((int64_t)64, t_end - t0);
+        const bool valid = lane < nt;
+        uint32_t Kc[FD::W + 1], Vc[FD::W];
+#pragma unroll
+        for (int k = 0; k <= FD::W; ++k) Kc[k] = Kw[k];
+#pragma unroll
+        for (int k = 0; k < FD::W; ++k) Vc[k] = Vw[k];
+        const float rkc = rk, rvc = rv;
+        fetch(t0 + kStride);
+        float s[G];
+        if (valid) {
+#pragma unroll
+            for (int k = 0; k < FD::W; ++k) vbuf[lane * RW + k] = Vc[k];
+            vbuf[lane * RW + FD::W] = 0u;
+            score_record<BITS, G>(Kc, lut, s);
+            const float rs = rkc * scale_log2;
+#pragma unroll
+            for (int h = 0; h < G; ++h) s[h] *= rs;
         } else {
 #pragma unroll
             for (int h = 0; h < G; ++h) s[h] = -INFINITY;
         }
-        // tile maximum per head
-        float mt[G];
+        float alpha[G];
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-            float x = s[h];
+            const float mn = fmaxf(m_run[h], wave_max(s[h]));
+            alpha[h] = __builtin_amdgcn_exp2f(m_run[h] - mn);  // 0 on the first tile (m_run = -inf)
+            m_run[h] = mn;
+            const float p = valid ? __builtin_amdgcn_exp2f(s[h] - mn) : 0.0f;
+            l_run[h] = l_run[h] * alpha[h] + wave_sum(p);
+            wbuf[lane * G + h] = p * rvc;
 #pragma unroll
-            for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-            mt[h] = x;
+            for (int k = 0; k < 4; ++k) acc[h][k] *= alpha[h];
         }
-        if (lane == 0)
-#pragma unroll
-            for (int h = 0; h < G; ++h) red[wv * G + h] = mt[h];
-        __syncthreads();
-        float alpha[G], mnew[G];
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            float x = red[h];
-            for (int w = 1; w < kDecThreads / 64; ++w) x = fmaxf(x, red[w * G + h]);
-            mnew[h] = fmaxf(m_run[h], x);
-            alpha[h] = exp2f(m_run[h] - mnew[h]);  // m_run = -inf on the first tile -> 0
-            m_run[h] = mnew[h];
-        }
-        // weights and tile sums
-        const float rv = valid ? vn[bh * T + t0 + tid] : 0.0f;
-        float ps[G];
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            const float p = valid ? exp2f(s[h] - mnew[h]) : 0.0f;
-            pw[tid * G + h] = p * rv;
-            float x = p;
-#pragma unroll
-            for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-            ps[h] = x;
-        }
-        __syncthreads();  // red (max) consumed, pw and vrec written
-        if (lane == 0)
-#pragma unroll
-            for (int h = 0; h < G; ++h) red[wv * G + h] = ps[h];
-        // V accumulation in the rotated domain
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            acc0[h] *= alpha[h];
-            acc1[h] *= alpha[h];
-        }
-        for (int tt = ph; tt < nt; tt += kVPhases) {
-            const uint32_t *r = vrec + tt * (FD::W + 1);
-            const int p = 2 * BITS * cp, wd = p >> 5, sh = p & 31;
-            const uint32_t fv = __builtin_amdgcn_alignbit(r[wd + 1], r[wd], (uint32_t)sh) &
-                                ((1u << (2 * BITS)) - 1u);
-            const float ca = c2[2 * fv], cb2 = c2[2 * fv + 1];
-            const float *w = pw + tt * G;
+        wave_lds_sync();
+        for (int tt = par; tt < nt; tt += 2) {
+            const uint32_t *r = vbuf + tt * RW;
+            uint32_t bitsq = __builtin_amdgcn_alignbit(r[qwd + 1], r[qwd], (uint32_t)qsh);
+            const uint32_t f0 = bitsq & fmask, f1 = (bitsq >> (2 * BITS)) & fmask;
+            const float c00 = c2[2 * f0], c01 = c2[2 * f0 + 1], c10 = c2[2 * f1], c11 = c2[2 * f1 + 1];
+            const float *w = wbuf + tt * G;
 #pragma unroll
             for (int h = 0; h < G; ++h) {
-                acc0[h] = fmaf(w[h], ca, acc0[h]);
-                acc1[h] = fmaf(w[h], cb2, acc1[h]);
+                const float wh = w[h];
+                acc[h][0] = fmaf(wh, c00, acc[h][0]);
+                acc[h][1] = fmaf(wh, c01, acc[h][1]);
+                acc[h][2] = fmaf(wh, c10, acc[h][2]);
+                acc[h][3] = fmaf(wh, c11, acc[h][3]);
             }
         }
-        __syncthreads();  // red (sums) written; vrec/pw free for the next tile
+        wave_lds_sync();  // vbuf / wbuf are rewritten by the next tile
+    }
+    // the two token parities hold partial sums of the same coordinates
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) acc[h][k] += __shfl_xor(acc[h][k], 32);
+
+    // Block merge of the waves: M = max_w m_w, acc = sum_w 2^(m_w - M) acc_w, same for l.
+    float *wacc = smem + SM::vbuf;  // reuse: [waves][G][128]
+    float *wm = smem + SM::wm;
+    float *wl = smem + SM::wl;
+    __syncthreads();  // all waves done with vbuf / wbuf
+    if (lane < 32)
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) wacc[(wv * G + h) * kD + 4 * cq + k] = acc[h][k];
+    if (lane == 0)
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-            float x = 0.0f;
-            for (int w = 0; w < kDecThreads / 64; ++w) x += red[w * G + h];
-            l_run[h] = l_run[h] * alpha[h] + x;
+            wm[wv * G + h] = m_run[h];
+            wl[wv * G + h] = l_run[h];
         }
-        __syncthreads();  // red consumed before the next tile reuses it
-    }
-
-    // Reduce the token phases: partial acc of coordinate pair cp, phase ph.
-    float *accs = pw;  // reuse: [phases][G][128]
-    for (int h = 0; h < G; ++h) {
-        accs[(ph * G + h) * kD + 2 * cp] = acc0[h];
-        accs[(ph * G + h) * kD + 2 * cp + 1] = acc1[h];
-    }
     __syncthreads();
     float *my = part + ((bh * n_split + split) * G) * (kD + 2);
     for (int idx = tid; idx < G * kD; idx += kDecThreads) {
         const int h = idx >> 7, i = idx & (kD - 1);
-        float x = 0.0f;
-        for (int p2 = 0; p2 < kVPhases; ++p2) x += accs[(p2 * G + h) * kD + i];
-        my[h * (kD + 2) + 2 + i] = x;
-    }
-    if (tid < G) {
-        my[tid * (kD + 2)] = m_run[tid];
-        my[tid * (kD + 2) + 1] = l_run[tid];
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, wm[w * G + h]);
+        float A = 0.0f, L = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kDecWaves; ++w) {
+            const float f = __builtin_amdgcn_exp2f(wm[w * G + h] - M);  // empty wave: 2^-inf = 0
+            A = fmaf(f, wacc[(w * G + h) * kD + i], A);
+            L = fmaf(f, wl[w * G + h], L);
+        }
+        my[h * (kD + 2) + 2 + i] = A;
+        if (i == 0) {
+            my[h * (kD + 2)] = M;
+            my[h * (kD + 2) + 1] = L;
+        }
     }
 
-    // Arrival: the last split of (b, g) merges.  Every thread publishes its own
-    // partial stores at device scope before the block signals arrival.
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    // Arrival: the last split of (b, g) merges.  Each wave waits for its own
+    // partial stores, the barrier joins the waves, and one device-scope release by thread 0 then
+    // publishes them (the L2 write-back it implies is a whole-cache operation,
+    // so one per block suffices) before the counter is incremented.  The last
+    // block performs one device-scope acquire (L2 invalidate) before reading
+    // the other blocks' partials.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's stores have reached L2
     __syncthreads();
     __shared__ unsigned last;
-    if (tid == 0) {
-        const unsigned prev = atomicAdd(counters + bh, 1u);
-        last = (prev == (unsigned)(n_split - 1)) ? 1u : 0u;
+    if (wv == 0) {  // wave-uniform: cache write-back / invalidate act per wave
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        unsigned prev = 0;
+        if (lane == 0) prev = atomicAdd(counters + bh, 1u);
+        const unsigned is_last = __builtin_amdgcn_readfirstlane(prev) == (unsigned)(n_split - 1);
+        if (is_last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        if (lane == 0) last = is_last;
     }
     __syncthreads();
     if (!last) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 
     // Merge weights per (split, head): f = 2^(m_s - M) / (d L), L = sum_s l_s 2^(m_s - M).
-    float *ms = pw;                   // reuse: [n_split][G] split maxima, then weights
-    float *ls = pw + n_split * G;     // [n_split][G] split sums
+    float *ms = smem + SM::vbuf;      // reuse: [n_split][G] split maxima, then weights
+    float *ls = ms + n_split * G;     // [n_split][G] split sums
     float *o = qr;                    // reuse: [G][128]
     const float *all = part + (bh * n_split) * G * (kD + 2);
     for (int idx = tid; idx < n_split * G; idx += kDecThreads) {
@@ -412,9 +495,9 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
         float M = -INFINITY;
         for (int sp = 0; sp < n_split; ++sp) M = fmaxf(M, ms[sp * G + tid]);
         float L = 0.0f;
-        for (int sp = 0; sp < n_split; ++sp) L += ls[sp * G + tid] * exp2f(ms[sp * G + tid] - M);
+        for (int sp = 0; sp < n_split; ++sp) L += ls[sp * G + tid] * __builtin_amdgcn_exp2f(ms[sp * G + tid] - M);
         const float inv = 1.0f / (L * kD);
-        for (int sp = 0; sp < n_split; ++sp) ms[sp * G + tid] = exp2f(ms[sp * G + tid] - M) * inv;
+        for (int sp = 0; sp < n_split; ++sp) ms[sp * G + tid] = __builtin_amdgcn_exp2f(ms[sp * G + tid] - M) * inv;
     }
     __syncthreads();
     for (int idx = tid; idx < G * kD; idx += kDecThreads) {
@@ -422,12 +505,12 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
         const float *col = all + h * (kD + 2) + 2 + i;
         float A = 0.0f;
         int sp = 0;
-        for (; sp + 8 <= n_split; sp += 8) {  // 8 independent loads in flight
-            float v[8];
+        for (; sp + 16 <= n_split; sp += 16) {  // 16 independent loads in flight
+            float v[16];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) v[u] = col[(int64_t)(sp + u) * G * (kD + 2)];
+            for (int u = 0; u < 16; ++u) v[u] = col[(int64_t)(sp + u) * G * (kD + 2)];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) A = fmaf(ms[(sp + u) * G + h], v[u], A);
+            for (int u = 0; u < 16; ++u) A = fmaf(ms[(sp + u) * G + h], v[u], A);
         }
         for (; sp < n_split; ++sp) A = fmaf(ms[sp * G + h], col[(int64_t)sp * G * (kD + 2)], A);
         o[idx] = A;
@@ -467,7 +550,7 @@ hipError_t run_logits(const kvq_ctx *ctx, const void *q, int64_t B, int64_t Hq, 
     if (per < 1) per = 1;
     const int64_t tpb = (T + per - 1) / per;
     const int64_t blocks_per_bh = (T + tpb - 1) / tpb;
-    const size_t shm = sizeof(float) * (G * kD + FD::NF * FD::E * G + (QJL ? 32 * 16 * G + G * kD : 0));
+    const size_t shm = sizeof(float) * (G * kD + FD::NF * FD::E * G + (QJL ? 32 * 16 * G + G * kD : 0) + 16);
     static bool attr_set = false;
     if (!attr_set) {
         (void)hipFuncSetAttribute((const void *)k_logits<BITS, G, QJL>,
@@ -564,9 +647,9 @@ size_t decode_ws_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t T)
 
 int decode_auto_splits(int64_t B, int64_t Hkv, int64_t T)
 {
-    // about two blocks per compute unit, and at least 1024 tokens per block
+    // about one block (16 waves) per compute unit, and at least 1024 tokens per block
     const int64_t bhs = B * Hkv;
-    int64_t ns = (512 + bhs - 1) / bhs;
+    int64_t ns = (256 + bhs - 1) / bhs;
     const int64_t cap = (T + 1023) / 1024;
     if (ns > cap) ns = cap;
     return (int)(ns < 1 ? 1 : ns);
