@@ -75,6 +75,7 @@ void free_ctx(kvq_ctx *c)
     (void)hipFree(c->d_sgnmask);
     (void)hipFree(c->d_signs);
     (void)hipFree(c->d_S);
+    (void)hipFree(c->d_S16);
     (void)hipFree(c->d_vq);
     (void)hipFree(c->d_vqnorm);
     delete c;
@@ -166,8 +167,25 @@ kvq_status kvq_create(const kvq_config *cfg, kvq_ctx **out)
         std::free(mask);
         std::free(sg);
     }
-    if (st == KVQ_OK && mode == KVQ_MODE_MSE_QJL)
-        st = upload(&c->d_S, cfg->qjl_S, (size_t)kvq::kD * kvq::kD);
+    if (st == KVQ_OK && mode == KVQ_MODE_MSE_QJL) {
+        const size_t n = (size_t)kvq::kD * kvq::kD;
+        _Float16 *s16 = (_Float16 *)std::malloc(2 * n * sizeof(_Float16));
+        if (!s16) st = KVQ_E_NOMEM;
+        bool exact = true;
+        for (size_t i = 0; st == KVQ_OK && i < n; ++i) {
+            const float v = cfg->qjl_S[i];
+            if (!std::isfinite(v) || std::fabs(v) > 60000.f) st = KVQ_E_INVAL;
+            const _Float16 hi = (_Float16)v;
+            const _Float16 lo = (_Float16)(v - (float)hi);
+            s16[i] = hi;
+            s16[n + i] = lo;
+            if ((float)lo != 0.0f) exact = false;
+        }
+        c->S_exact_f16 = exact;
+        if (st == KVQ_OK) st = upload(&c->d_S, cfg->qjl_S, n);
+        if (st == KVQ_OK) st = upload(&c->d_S16, s16, 2 * n);
+        std::free(s16);
+    }
     if (st == KVQ_OK && mode == KVQ_MODE_NSN_VQ) {
         float nrm[kvq::kVqK];
         for (int j = 0; j < kvq::kVqK; ++j) {

@@ -16,6 +16,8 @@
 // scaled by ||x|| (same decisions up to fp32 rounding, 128 fewer multiplies).
 #include "kvq_internal.h"
 
+#include <type_traits>
+
 namespace kvq {
 namespace {
 
@@ -271,6 +273,276 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
     }
 }
 
+// ---------------------------------------------------------------------------
+// Quantise with the 1-bit QJL residual ("TurboQuant", Como Funciona,
+// Estagio 2).  Per key, besides the MSE codes: the residual in the orthonormal
+// rotated space r = (y/rho - c[idx]) / sqrt(d), its norm gamma = ||r|| and
+// the 128 sign bits [(S r)_j >= 0] of its Gaussian projection.  Only the signs
+// are stored, and they do not depend on the positive factor 1/sqrt(d), so the
+// kernel projects e = y/rho - c[idx].
+//
+// The projection is a dense 64 x 128 x 128 contraction per tile and runs on
+// the matrix cores (v_mfma_f32_16x16x32_f16).  The sign decisions need the
+// product to about 1e-6 of ||e||, so e is split into fp16 hi + lo parts and
+// accumulated in fp32 over two passes (a third pass adds e_hi * S_lo when S
+// is not exactly representable in fp16).  e of the 64 keys is staged in LDS
+// as fp16 hi and lo rows (16-byte chunks XOR-swizzled by row so that the
+// operand reads are conflict-free) and read back in the operand layout: lane
+// l holds row l%16, k = 8 (l/16) .. +7.  The
+// 16 x 16 result blocks (lane l: rows 4 (l/16) .. +3, column l%16) are turned
+// into sign bits with wave ballots; each key's 16-bit chunks are gathered on
+// the scalar unit and written into its own lane with v_writelane.
+// ---------------------------------------------------------------------------
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+
+struct QjlArgs {
+    const u4_t *x;
+    u4_t *codes;
+    float *norms;
+    u4_t *signs;        // [n][16 bytes]
+    float *gamma;       // [n]
+    const uint32_t *sgnmask;
+    const u4_t *S_hi;   // [128][128] fp16, row-major (row j = output j)
+    const u4_t *S_lo;   // same, or nullptr when S is exactly fp16
+    float mags[8];      // positive centroids c_{L/2}, ..., c_{L-1}
+};
+
+// Magnitude |c[idx]| of coordinate y from the same binary search as the codes.
+template <int BITS>
+__device__ __forceinline__ float centroid_mag(float a, const float *P, const float *Mg)
+{
+    if constexpr (BITS == 1) {
+        return Mg[0];
+    } else if constexpr (BITS == 2) {
+        return a > P[0] ? Mg[1] : Mg[0];
+    } else if constexpr (BITS == 3) {
+        const bool c1 = a > P[1];
+        const bool c2 = a > (c1 ? P[2] : P[0]);
+        const float lo = c2 ? Mg[1] : Mg[0], hi = c2 ? Mg[3] : Mg[2];
+        return c1 ? hi : lo;
+    } else {
+        const bool c1 = a > P[3];
+        const float t2 = c1 ? P[5] : P[1];
+        const float tA = c1 ? P[6] : P[2];
+        const float tB = c1 ? P[4] : P[0];
+        const bool c2 = a > t2;
+        const bool c3 = a > (c2 ? tA : tB);
+        const int h = (c1 ? 4 : 0) + (c2 ? 2 : 0) + (c3 ? 1 : 0);
+        float m = Mg[0];
+#pragma unroll
+        for (int k = 1; k < 8; ++k) m = h == k ? Mg[k] : m;
+        return m;
+    }
+}
+
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 16 + (chunk ^ (row & 15)); }
+
+// Write a wave-uniform value into lane KEY of v (other lanes unchanged).
+template <int KEY>
+__device__ __forceinline__ uint32_t write_lane(uint32_t v, uint32_t val)
+{
+    asm("v_writelane_b32 %0, %1, %2" : "+v"(v) : "s"(val), "n"(KEY));
+    return v;
+}
+
+template <int K0, int N>
+struct StaticFor {
+    template <class F>
+    __device__ __forceinline__ static void run(F &&f)
+    {
+        if constexpr (N > 0) {
+            f(std::integral_constant<int, K0>{});
+            StaticFor<K0 + 1, N - 1>::run(f);
+        }
+    }
+};
+
+template <int BITS>
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_quantize_qjl(
+    QjlArgs a, HalfThresholds ht, int64_t T, int H, int64_t tiles_per_bh, int64_t n_tiles)
+{
+    __shared__ u4_t lds[kWaves][kTile * 16];     // tile of x, then fp16 hi rows of e
+    __shared__ u4_t Elo[kWaves][kTile * 16];     // fp16 lo rows of e
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    u4_t *L = lds[wv];
+    const int64_t stride = (int64_t)gridDim.x * kWaves;
+    for (int64_t tile = (int64_t)blockIdx.x * kWaves + wv; tile < n_tiles; tile += stride) {
+        const TileGeom g = geom(tile, T, H, tiles_per_bh);
+        tile_to_lds(a.x + g.v0 * 16, g.nv, L, lane);
+        wait_vm();
+        uint32_t w[64];
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+            const u4_t v = L[lane * 16 + ((c + lane) & 15)];
+            w[4 * c + 0] = v.x;
+            w[4 * c + 1] = v.y;
+            w[4 * c + 2] = v.z;
+            w[4 * c + 3] = v.w;
+        }
+        wait_lgkm();
+        const bool active = lane < g.nv;
+        const uint32_t *sg = a.sgnmask + g.h * 64;
+        float ss = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 64; ++k) {
+            const h2_t p = __builtin_bit_cast(h2_t, w[k]);
+            ss = __builtin_amdgcn_fdot2(p, p, ss, false);
+            w[k] ^= sg[k];
+        }
+        float y[128];
+#pragma unroll
+        for (int k = 0; k < 64; ++k) {
+            y[2 * k] = pair_sum(w[k]);
+            y[2 * k + 1] = pair_diff(w[k]);
+        }
+#pragma unroll
+        for (int s = 2; s < 128; s <<= 1) {
+#pragma unroll
+            for (int i = 0; i < 128; i += 2 * s) {
+#pragma unroll
+                for (int j = i; j < i + s; ++j) {
+                    const float p0 = y[j], p1 = y[j + s];
+                    y[j] = p0 + p1;
+                    y[j + s] = p0 - p1;
+                }
+            }
+        }
+        const float rho = __builtin_sqrtf(ss);
+        const float r = rho > 0.0f ? rho : 1.0f;
+        const float inv = rho > 0.0f ? 1.0f / rho : 0.0f;
+        float P[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) P[k] = ht.p[k] * r;
+
+        uint32_t out[4 * BITS];
+#pragma unroll
+        for (int k = 0; k < 4 * BITS; ++k) out[k] = 0u;
+#pragma unroll
+        for (int i = 127; i >= 0; --i) {
+            uint64_t M[BITS];
+            index_bits<BITS>(y[i], P, M);
+#pragma unroll
+            for (int k = BITS - 1; k >= 0; --k) {
+                const int wd = (BITS * i + k) >> 5;
+                out[wd] = append_bit(out[wd], M[k]);
+            }
+        }
+        // residual e = y / rho - c[idx] (the sign of c[idx] is [y > 0]), and gamma
+        float g2 = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 128; ++i) {
+            const float mg = centroid_mag<BITS>(__builtin_fabsf(y[i]), P, a.mags);
+            const float e = fmaf(y[i], inv, y[i] > 0.0f ? -mg : mg);
+            y[i] = e;
+            g2 = fmaf(e, e, g2);
+        }
+
+        // Stage e of all 64 keys as fp16 hi / lo rows (16-byte chunks swizzled).
+        u4_t *Lhi = L, *Llo = Elo[wv];  // the x tile has been read into registers
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+            h8_t hv, lv;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const _Float16 hi = (_Float16)y[8 * c + j];
+                hv[j] = hi;
+                lv[j] = (_Float16)(y[8 * c + j] - (float)hi);
+            }
+            Lhi[swz(lane, c)] = __builtin_bit_cast(u4_t, hv);
+            Llo[swz(lane, c)] = __builtin_bit_cast(u4_t, lv);
+        }
+        wait_lgkm();
+        __builtin_amdgcn_wave_barrier();
+
+        uint32_t sgn[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int np = 0; np < 4; ++np) {  // pairs of 16-output blocks -> one sign dword per key
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb) {
+                f4_t z[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) {
+                    const int row = 16 * mb + (lane & 15), chunk = 4 * kb + (lane >> 4);
+                    const h8_t Ah = __builtin_bit_cast(h8_t, Lhi[swz(row, chunk)]);
+                    const h8_t Al = __builtin_bit_cast(h8_t, Llo[swz(row, chunk)]);
+#pragma unroll
+                    for (int t2 = 0; t2 < 2; ++t2) {
+                        const int srow = 16 * (2 * np + t2) + (lane & 15);
+                        const h8_t Bh = __builtin_bit_cast(h8_t, a.S_hi[srow * 16 + chunk]);
+                        z[t2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, Bh, z[t2], 0, 0, 0);
+                        z[t2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Al, Bh, z[t2], 0, 0, 0);
+                        if (a.S_lo) {
+                            const h8_t Bl = __builtin_bit_cast(h8_t, a.S_lo[srow * 16 + chunk]);
+                            z[t2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, Bl, z[t2], 0, 0, 0);
+                        }
+                    }
+                }
+                uint64_t m[2][4];
+#pragma unroll
+                for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) m[t2][rr] = __builtin_amdgcn_ballot_w64(z[t2][rr] >= 0.0f);
+                // key 16 mb + 4 q + rr: bits 16 q .. 16 q + 15 of m[t2][rr] are its sign bits
+                // 16 nb .. 16 nb + 15 (nb = 2 np + t2); both halves form its dword np.
+                uint32_t acc_np = sgn[np];
+                StaticFor<0, 16>::run([&](auto kk) {
+                    constexpr int k = decltype(kk)::value;
+                    constexpr int q = k / 4, rr = k % 4;
+                    const uint32_t lo16 = (uint32_t)(m[0][rr] >> (16 * q)) & 0xFFFFu;
+                    const uint32_t hi16 = (uint32_t)(m[1][rr] >> (16 * q)) & 0xFFFFu;
+                    const uint32_t val = __builtin_amdgcn_readfirstlane(lo16 | (hi16 << 16));
+                    if (mb == 0) acc_np = write_lane<k>(acc_np, val);
+                    if (mb == 1) acc_np = write_lane<16 + k>(acc_np, val);
+                    if (mb == 2) acc_np = write_lane<32 + k>(acc_np, val);
+                    if (mb == 3) acc_np = write_lane<48 + k>(acc_np, val);
+                });
+                sgn[np] = acc_np;
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+        if (!active) continue;
+        const int64_t v = g.v0 + lane;
+        u4_t *dst = a.codes + v * BITS;
+#pragma unroll
+        for (int q = 0; q < BITS; ++q) {
+            u4_t o = {out[4 * q], out[4 * q + 1], out[4 * q + 2], out[4 * q + 3]};
+            dst[q] = o;
+        }
+        a.norms[v] = rho;
+        u4_t so = {sgn[0], sgn[1], sgn[2], sgn[3]};
+        a.signs[v] = so;
+        a.gamma[v] = __builtin_sqrtf(g2) * 0.08838834764831845f;  // ||e|| / sqrt(d)
+    }
+}
+
+template <int BITS>
+hipError_t run_qjl(const kvq_ctx *ctx, const void *x, int64_t B, int64_t T, uint8_t *codes, float *norms,
+                   uint8_t *signs, float *gamma, hipStream_t s)
+{
+    HalfThresholds ht{};
+    const int L = 1 << BITS;
+    for (int k = 0; k < L / 2 - 1; ++k) ht.p[k] = ctx->cb.t[L / 2 + k];
+    QjlArgs a{};
+    a.x = (const u4_t *)x;
+    a.codes = (u4_t *)codes;
+    a.norms = norms;
+    a.signs = (u4_t *)signs;
+    a.gamma = gamma;
+    a.sgnmask = ctx->d_sgnmask;
+    a.S_hi = (const u4_t *)ctx->d_S16;
+    a.S_lo = ctx->S_exact_f16 ? nullptr : (const u4_t *)(ctx->d_S16 + kD * kD);
+    for (int k = 0; k < L / 2; ++k) a.mags[k] = ctx->cb.c[L / 2 + k];
+    const int64_t tiles_per_bh = (T + kTile - 1) / kTile;
+    const int64_t n_tiles = tiles_per_bh * B * ctx->H;
+    int64_t blocks = (n_tiles + kWaves - 1) / kWaves;
+    if (blocks > (int64_t)ctx->n_cu) blocks = ctx->n_cu;  // one wave per SIMD (512 registers each)
+    hipLaunchKernelGGL(k_quantize_qjl<BITS>, dim3((unsigned)blocks), dim3(kWaves * 64), 0, s, a, ht, T, ctx->H,
+                       tiles_per_bh, n_tiles);
+    return hipGetLastError();
+}
+
 template <int BITS>
 hipError_t run(const kvq_ctx *ctx, const QArgs &a, int n_tensors, int64_t B, int64_t T, hipStream_t s)
 {
@@ -303,7 +575,15 @@ hipError_t launch_quantize(const kvq_ctx *ctx, int kind, const void *x, int64_t 
                            uint8_t *codes, float *norms, uint8_t *qjl_signs, float *qjl_gamma,
                            hipStream_t s)
 {
-    if (qjl_signs || qjl_gamma) return hipErrorNotSupported;
+    if (qjl_signs) {
+        switch (ctx->bits) {
+        case 1: return run_qjl<1>(ctx, x, B, T, codes, norms, qjl_signs, qjl_gamma, s);
+        case 2: return run_qjl<2>(ctx, x, B, T, codes, norms, qjl_signs, qjl_gamma, s);
+        case 3: return run_qjl<3>(ctx, x, B, T, codes, norms, qjl_signs, qjl_gamma, s);
+        case 4: return run_qjl<4>(ctx, x, B, T, codes, norms, qjl_signs, qjl_gamma, s);
+        }
+        return hipErrorInvalidValue;
+    }
     QArgs a{};
     a.x[0] = a.x[1] = (const u4_t *)x;
     a.codes[0] = a.codes[1] = (u4_t *)codes;

@@ -26,7 +26,8 @@ Recipe: each workload has a seed (its position in the list above);
 streams for [K data, V data, K scales, V scales, query, D_K, D_V, S].  Values
 are drawn in float64 and cast once to float16 (round to nearest even).  The
 lognormal scale is one factor per (tensor, KV head, channel), shared by all
-tokens and batch entries.  The tiny workload's 4 outlier channels are the
+tokens and batch entries.  The QJL projection S has N(0,1) entries rounded to
+the nearest fp16 value.  The tiny workload's 4 outlier channels are the
 first 4 entries of a permutation of 128 drawn with seed 0.
 """
 from __future__ import annotations
@@ -110,7 +111,8 @@ def make(name: str, T: int | None = None, B: int | None = None, with_v: bool | N
     out["signs_k"] = random_signs(r[5], w.Hkv)
     out["signs_v"] = random_signs(r[6], w.Hkv)
     if w.qjl:
-        out["S"] = r[7].standard_normal((D, D)).astype(np.float32)
+        # N(0,1) entries rounded to the nearest fp16 value (then held as fp32)
+        out["S"] = r[7].standard_normal((D, D)).astype(np.float16).astype(np.float32)
     return out
 
 

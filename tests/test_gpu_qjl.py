@@ -1,0 +1,107 @@
+"""GPU parity of the QJL residual path (kvq_quantize in MSE_QJL mode and
+kvq_logits with the QJL term) against the CPU oracle.
+
+Sign bits are compared on the GPU's own MSE codes (the oracle recomputes the
+residual from its double-precision rotation and the GPU's indices): exact
+except bits whose projection lies within 1e-5 * gamma of zero."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from calibration_free_kv_amd import kvq, synth
+from tests.gpu_util import check_codes, needs_gpu, to_np, unpack_np
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+
+
+def run_qjl(inp, bits, S):
+    ctx = kvq.Context(inp["Hkv"], bits, inp["signs_k"], inp["signs_v"], mode=kvq.KVQ_MODE_MSE_QJL, qjl_S=S)
+    k = torch.from_numpy(inp["k"]).cuda()
+    out = ctx.quantize(kvq.KVQ_KIND_K, k)
+    return ctx, {n: to_np(t) for n, t in out.items()}, out
+
+
+def check_qjl(inp, bits, S, o, where=None):
+    x = inp["k"]
+    B, H, T, _ = x.shape
+    if where is None:
+        bb, hh, tt = [a.ravel() for a in np.meshgrid(np.arange(B), np.arange(H), np.arange(T), indexing="ij")]
+    else:
+        bb, hh, tt = where
+    mism = 0
+    for h in np.unique(hh):
+        sel = hh == h
+        xs = x[bb[sel], h, tt[sel]][None, None]
+        ref = O.quantize(xs, inp["signs_k"][h:h + 1], bits, want_y=True)
+        gi = unpack_np(o["codes"][bb[sel], h, tt[sel]], bits)[None, None]
+        q = O.qjl(ref["y"], gi, S, bits)
+        np.testing.assert_allclose(o["qjl_gamma"][bb[sel], h, tt[sel]], q["gamma"][0, 0], rtol=1e-5, atol=1e-7)
+        gs = np.unpackbits(o["qjl_signs"][bb[sel], h, tt[sel]], axis=-1, bitorder="little")
+        rs = np.unpackbits(q["signs"][0, 0], axis=-1, bitorder="little")
+        bad = (gs != rs) & (q["flags"][0, 0] == 0)
+        assert not bad.any(), "%d sign bits differ outside the 1e-5*gamma band" % int(bad.sum())
+        mism += int((gs != rs).sum())
+    return mism
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3])
+def test_qjl_quantize_ragged(bits):
+    inp = synth.make("long128k_qjl", T=700)
+    ctx, o, _ = run_qjl(inp, bits, inp["S"])
+    check_codes(inp["k"], inp["signs_k"], bits, o["codes"], o["norms"], label="qjl codes")
+    print("boundary sign mismatches", check_qjl(inp, bits, inp["S"], o))
+
+
+def test_qjl_general_fp32_projection():
+    """S not representable in fp16: the kernel adds the e_hi * S_lo pass."""
+    inp = synth.make("long128k_qjl", T=300)
+    S = np.random.default_rng(5).standard_normal((128, 128)).astype(np.float32)
+    ctx, o, _ = run_qjl(inp, 2, S)
+    check_qjl(inp, 2, S, o)
+
+
+def test_qjl_full_size_sampled():
+    inp = synth.make("long128k_qjl")
+    ctx, o, _ = run_qjl(inp, 2, inp["S"])
+    rng = np.random.default_rng(3)
+    n = 4096
+    where = (np.zeros(n, int), rng.integers(0, 8, n), rng.integers(0, inp["T"], n))
+    check_codes(inp["k"], inp["signs_k"], 2, o["codes"], o["norms"], where=where, label="qjl full")
+    check_qjl(inp, 2, inp["S"], o, where=where)
+
+
+def test_qjl_zero_vector():
+    inp = synth.make("long128k_qjl", T=65)
+    inp["k"][0, 3, 7] = 0
+    ctx, o, _ = run_qjl(inp, 2, inp["S"])
+    check_qjl(inp, 2, inp["S"], o)
+    assert o["norms"][0, 3, 7] == 0
+
+
+@pytest.mark.parametrize("T", [1000, 4097])
+def test_qjl_logits(T):
+    inp = synth.make("long128k_qjl", T=T)
+    ctx, o, out = run_qjl(inp, 2, inp["S"])
+    q = torch.from_numpy(inp["q"]).cuda()
+    lg = to_np(ctx.logits(q, out["codes"], out["norms"], out["qjl_signs"], out["qjl_gamma"]))
+    ref = O.logits(inp["q"], o["codes"], o["norms"].astype(np.float64), inp["signs_k"], 2,
+                   qjl_signs=o["qjl_signs"], gamma=o["qjl_gamma"].astype(np.float64), S=inp["S"])
+    G = inp["Hq"] // inp["Hkv"]
+    scale = np.linalg.norm(inp["q"].astype(np.float64), axis=-1)[..., None] * np.repeat(o["norms"], G, axis=1)
+    err = np.abs(lg - ref) / np.maximum(scale, 1e-30)
+    assert err.max() <= 1e-3
+    assert err.max() <= 1e-5, err.max()
+
+
+def test_qjl_logits_full_size_sampled():
+    inp = synth.make("long128k_qjl")
+    ctx, o, out = run_qjl(inp, 2, inp["S"])
+    q = torch.from_numpy(inp["q"]).cuda()
+    lg = to_np(ctx.logits(q, out["codes"], out["norms"], out["qjl_signs"], out["qjl_gamma"]))
+    t = np.random.default_rng(9).integers(0, inp["T"], 2048)
+    ref = O.logits(inp["q"], o["codes"][:, :, t], o["norms"][:, :, t].astype(np.float64), inp["signs_k"], 2,
+                   qjl_signs=o["qjl_signs"][:, :, t], gamma=o["qjl_gamma"][:, :, t].astype(np.float64), S=inp["S"])
+    G = inp["Hq"] // inp["Hkv"]
+    scale = np.linalg.norm(inp["q"].astype(np.float64), axis=-1)[..., None] * np.repeat(o["norms"][:, :, t], G, axis=1)
+    assert (np.abs(lg[:, :, t] - ref) / scale).max() <= 1e-5
