@@ -77,7 +77,8 @@ void free_ctx(kvq_ctx *c)
     (void)hipFree(c->d_S);
     (void)hipFree(c->d_S16);
     (void)hipFree(c->d_vq);
-    (void)hipFree(c->d_vqnorm);
+    (void)hipFree(c->d_vq16);
+    (void)hipFree(c->d_vqbias);
     delete c;
 }
 
@@ -187,18 +188,30 @@ kvq_status kvq_create(const kvq_config *cfg, kvq_ctx **out)
         std::free(s16);
     }
     if (st == KVQ_OK && mode == KVQ_MODE_NSN_VQ) {
-        float nrm[kvq::kVqK];
-        for (int j = 0; j < kvq::kVqK; ++j) {
-            double s = 0.0;
+        const size_t n = (size_t)kvq::kVqK * kvq::kVqSub;
+        float bias[kvq::kVqK];
+        _Float16 *c16 = (_Float16 *)std::malloc(2 * n * sizeof(_Float16));
+        if (!c16) st = KVQ_E_NOMEM;
+        bool exact = true;
+        for (int j = 0; st == KVQ_OK && j < kvq::kVqK; ++j) {
+            double sq = 0.0;
             for (int k = 0; k < kvq::kVqSub; ++k) {
-                double v = cfg->vq_codebook[j * kvq::kVqSub + k];
-                if (!std::isfinite(v)) st = KVQ_E_INVAL;
-                s += v * v;
+                const float v = cfg->vq_codebook[j * kvq::kVqSub + k];
+                if (!std::isfinite(v) || std::fabs(v) > 60000.f) st = KVQ_E_INVAL;
+                sq += (double)v * v;
+                const _Float16 hi = (_Float16)v;
+                const _Float16 lo = (_Float16)(v - (float)hi);
+                c16[j * kvq::kVqSub + k] = hi;
+                c16[n + j * kvq::kVqSub + k] = lo;
+                if ((float)lo != 0.0f) exact = false;
             }
-            nrm[j] = (float)s;
+            bias[j] = (float)(-0.5 * sq);
         }
-        if (st == KVQ_OK) st = upload(&c->d_vq, cfg->vq_codebook, (size_t)kvq::kVqK * kvq::kVqSub);
-        if (st == KVQ_OK) st = upload(&c->d_vqnorm, nrm, (size_t)kvq::kVqK);
+        c->vq_exact_f16 = exact;
+        if (st == KVQ_OK) st = upload(&c->d_vq, cfg->vq_codebook, n);
+        if (st == KVQ_OK) st = upload(&c->d_vq16, c16, 2 * n);
+        if (st == KVQ_OK) st = upload(&c->d_vqbias, bias, (size_t)kvq::kVqK);
+        std::free(c16);
     }
     if (st != KVQ_OK) {
         free_ctx(c);
@@ -353,6 +366,7 @@ kvq_status kvq_nsn_vq_quantize(kvq_ctx *ctx, const void *x_f16, int64_t H, int64
 {
     if (!ctx || ctx->mode != KVQ_MODE_NSN_VQ) return KVQ_E_INVAL;
     if (H < 1 || T < 1 || T > (int64_t(1) << 31) || H > (int64_t(1) << 20)) return KVQ_E_INVAL;
+    if (H * ((T + 1023) / 1024) > INT32_MAX) return KVQ_E_INVAL;  // one stats block per 1024 tokens
     if (!x_f16 || !codes || !s1 || !s2 || !o || !ws) return KVQ_E_INVAL;
     if (!aligned(x_f16, 16) || !aligned(codes, 16) || !aligned(s1, 4) || !aligned(s2, 4) ||
         !aligned(o, 4) || !aligned(ws, 256))

@@ -336,6 +336,21 @@ __device__ __forceinline__ float centroid_mag(float a, const float *P, const flo
     }
 }
 
+// v = hi + lo (hi returned) with hi exactly representable in fp16: hi keeps the 11 leading
+// significant bits of v (values below the fp16 normal range go wholly to lo),
+// so its conversion is exact under any rounding and v - hi is exact in fp32;
+// only lo is rounded (|error| <= 2^-21 |v|).  Rounding hi to nearest instead
+// lets the compiler emit two different conversions for it (one for the stored
+// hi, one for the hi subtracted to form lo) that break exact ties differently,
+// leaving an error of one fp16 ulp.
+__device__ __forceinline__ _Float16 split_f16(float v, _Float16 &lo)
+{
+    float h = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, v) & 0xFFFFE000u);
+    h = __builtin_fabsf(v) < 0x1p-14f ? 0.0f : h;
+    lo = (_Float16)(v - h);
+    return (_Float16)h;
+}
+
 __device__ __forceinline__ int swz(int row, int chunk) { return row * 16 + (chunk ^ (row & 15)); }
 
 // Write a wave-uniform value into lane KEY of v (other lanes unchanged).
@@ -446,9 +461,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 
             h8_t hv, lv;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const _Float16 hi = (_Float16)y[8 * c + j];
-                hv[j] = hi;
-                lv[j] = (_Float16)(y[8 * c + j] - (float)hi);
+                _Float16 lo;
+                hv[j] = split_f16(y[8 * c + j], lo);
+                lv[j] = lo;
             }
             Lhi[swz(lane, c)] = __builtin_bit_cast(u4_t, hv);
             Llo[swz(lane, c)] = __builtin_bit_cast(u4_t, lv);

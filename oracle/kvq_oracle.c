@@ -479,11 +479,14 @@ ORC_API int kvqo_qjl(int d, int m, int64_t n, const double *y, const int32_t *id
 /* exact ties).  flags: 1 when z is within `band` of the bisecting hyperplane */
 /* of the winner and some other entry.  Degenerate tokens: ||x_t|| = 0 gives  */
 /* a_t = 0; s2_t = 0 gives xt_t = 0.                                          */
+/* o_given: NULL, or a mean [H, d] to use instead of the mean of these T      */
+/* tokens (to encode a sample of a longer sequence).                         */
 /* ------------------------------------------------------------------------ */
 
 ORC_API int kvqo_nsn_vq(int d, int sub, int K, int64_t H, int64_t T, const double *x,
                         const double *codebook, double band, uint8_t *codes, double *s1,
-                        double *s2, double *o, double *z_out, uint8_t *flags)
+                        double *s2, double *o, double *z_out, uint8_t *flags,
+                        const double *o_given)
 {
     if (d % sub || T <= 0) return -1;
     const int nsub = d / sub;
@@ -504,7 +507,7 @@ ORC_API int kvqo_nsn_vq(int d, int sub, int K, int64_t H, int64_t T, const doubl
         }
         for (int64_t t = 0; t < T; ++t)
             for (int i = 0; i < d; ++i) oh[i] += a[t * d + i];
-        for (int i = 0; i < d; ++i) oh[i] /= (double)T;
+        for (int i = 0; i < d; ++i) oh[i] = o_given ? o_given[h * d + i] : oh[i] / (double)T;
         for (int64_t t = 0; t < T; ++t) {
             double ss = 0.0;
             for (int i = 0; i < d; ++i) {

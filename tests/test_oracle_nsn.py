@@ -85,3 +85,12 @@ def test_golden_codebook():
     s = synth.gaussian_samples(999, 1 << 15)
     d2 = ((s[:, None, :] - cb[None].astype(np.float64)) ** 2).sum(-1).min(1)
     assert 0.25 <= d2.mean() / 8 <= 0.33
+
+
+def test_given_mean_reproduces_full_encoding():
+    x = synth.make("nsn_vq", T=96)["x"]
+    cb = _codebook()
+    full = O.nsn_vq(x, cb)
+    part = O.nsn_vq(x[:, 10:40], cb, o_given=full["o"])
+    assert np.array_equal(part["codes"], full["codes"][:, 10:40])
+    np.testing.assert_allclose(part["s2"], full["s2"][:, 10:40], rtol=1e-15)
