@@ -1,25 +1,35 @@
 """Throughput of the KV-cache quantisation hot path on one MI355X.
 
-One step = quantise the K and the V cache of one Llama-3-8B-shaped attention
-layer (batch 1, 8 KV heads x 128, 32768 tokens, fp16) to b-bit codes with
-kvq_quantize, then one decode step of attention for its 32 query heads
-(GQA 4) read straight from the codes with kvq_attn_decode.  Inputs are
-synthetic (seeded N(0,1) x per-channel lognormal(0,1) scales) and resident in
-HBM before timing starts; the step rotates over several input/output sets
-larger than twice the 256 MiB last-level cache, so data are not served from it.
+Main line (one step): quantise the K and the V cache of one Llama-3-8B-shaped
+attention layer (batch 1, 8 KV heads x 128, 32768 tokens, fp16) to 3-bit codes
+with kvq_quantize_kv, then one decode step of attention for its 32 query heads
+(GQA 4) read straight from codes with kvq_attn_decode.  Inputs are synthetic
+(seeded N(0,1) x per-channel lognormal(0,1) scales) and resident in HBM before
+timing starts.  The steps rotate over 4 input/output sets (645 MB, more than
+twice the 256 MB last-level cache); the decode of step s reads the codes of
+set s + 2, written two steps earlier, so they are not served from that cache.
 
-Prints one JSON line.  value = (K and V vectors quantised + keys scored) per
-second of the whole step.  The roofline object refers to kvq_quantize, the
-dominant kernel: algorithmic bytes per launch (fp16 input, packed codes and
-fp32 norms) divided by its mean launch duration from HIP events recorded on
-the kernels' stream during the timed steps.  cpu_baseline times the CPU
-oracle (plain C, double precision, one thread) on the same workload.
+value = (K and V vectors quantised + keys scored) per second of the whole step.
+roofline = the dominant kernel (kvq_quantize_kv): algorithmic bytes per launch
+(fp16 input, packed codes, fp32 norms) / mean launch duration from HIP events
+recorded on the stream the kernels run on.  traffic = HBM bytes per launch
+from the committed rocprofv3 counter record for the same kernel source, or
+null when the kernel source has changed since the counters were taken.
+
+rows = every step of the path on its own workload (all sizes full), timed the
+same way, each with its algorithmic bytes (and flops where the matrix cores
+do the work) and the fraction of the matching MI355X peak.
+
+cpu_baseline = the CPU oracle (plain C, double precision, one thread) on a
+bounded sample of the same step; rows carry their own oracle sample rates.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -28,15 +38,99 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, GB/s
+FP16_MFMA_TFLOPS = 2500.0  # MI355X dense fp16 matrix peak
+D = 128
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "kvq_quantize_kv_l8b32k_b3_traffic.md")
+QUANT_SRC = os.path.join(ROOT, "calibration_free_kv_amd", "csrc", "kvq_quantize.hip")
 
 
-def algorithmic_bytes(n_vec, bits):
-    quant = 2 * n_vec * (256 + 16 * bits + 4)      # per launch (K and V together)
-    decode = n_vec * 2 * (16 * bits + 4)           # K and V records of every token
-    return quant, decode
+def rec_bytes(bits):
+    return 16 * bits + 4  # packed codes + fp32 norm per vector
 
 
+def quant_bytes(n_vec, bits, qjl=False):
+    """fp16 read + codes and norm written (+ 16 B signs and 4 B gamma with QJL)."""
+    return n_vec * (2 * D + rec_bytes(bits) + (20 if qjl else 0))
+
+
+def decode_bytes(n_tok_heads, bits):
+    return n_tok_heads * 2 * rec_bytes(bits)  # K and V records of every (token, KV head)
+
+
+def logits_bytes(n_keys, Hq_per_kv, bits, qjl=False):
+    return n_keys * (rec_bytes(bits) + (20 if qjl else 0) + 4 * Hq_per_kv)
+
+
+def nsn_bytes(n_vec):
+    return n_vec * (2 * D + 16 + 8)  # x read once (algorithmic), codes + s1 + s2 written
+
+
+def source_sha(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+
+
+def read_traffic():
+    """Bytes per launch from the committed counter record, if it is current."""
+    try:
+        txt = open(TRAFFIC_RECORD).read()
+    except OSError:
+        return None
+    m = dict(re.findall(r"^- (\w+): `?([^`\n]+)`?$", txt, re.M))
+    if m.get("source_sha256") != source_sha(QUANT_SRC):
+        return None
+    try:
+        return float(m["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+class Timer:
+    """Mean duration of launches, from HIP events on the launching stream."""
+
+    def __init__(self, torch, stream):
+        self.torch, self.stream = torch, stream
+
+    def run(self, launch, reps, warmup):
+        torch = self.torch
+        for i in range(warmup):
+            launch(i)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for i in range(reps):
+            ev[i][0].record(self.stream)
+            launch(warmup + i)
+            ev[i][1].record(self.stream)
+        torch.cuda.synchronize()
+        ms = np.array([a.elapsed_time(b) for a, b in ev])
+        return float(ms.mean()), float(np.percentile(ms, 10)), float(np.percentile(ms, 90))
+
+
+def row(ms, p10, p90, nbytes=None, flops=None, **extra):
+    r = {"ms": ms, "p10_ms": p10, "p90_ms": p90}
+    if nbytes is not None:
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        r.update({"bytes_per_launch": nbytes, "GB/s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS})
+    if flops is not None:
+        tf = flops / (ms * 1e-3) / 1e12
+        r.update({"flops_per_launch": flops, "TFLOP/s": tf, "frac_fp16_mfma": tf / FP16_MFMA_TFLOPS})
+    r.update(extra)
+    return r
+
+
+def oracle_rate(fn, units, budget_s=2.0):
+    """units per second of the oracle on a bounded sample (repeats until budget_s)."""
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        fn()
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= 3:
+            return reps * units / el
+
+
+# --------------------------------------------------------------------------- main step
 def cpu_baseline(inp, bits, budget_s=10.0):
     import oracle as O
     B, Hkv, T = inp["k"].shape[:3]
@@ -57,57 +151,43 @@ def cpu_baseline(inp, bits, budget_s=10.0):
                       "attention over %d keys), %.1f s, single thread" % (reps, n, n, n, el)}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--bits", type=int, default=3, choices=[2, 3, 4])
-    ap.add_argument("--sets", type=int, default=4)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d refused)" % args.gpus,
-              file=sys.stderr)
-        sys.exit(2)
-
-    import torch
-
-    from calibration_free_kv_amd import kvq, synth
-
-    dev = torch.device("cuda", 0)
-    bits = args.bits
+def main_step(torch, kvq, synth, args, dev, timer):
+    bits = 3
     inp = synth.make("l8b32k")
     B, Hkv, T = inp["k"].shape[:3]
     Hq = inp["Hq"]
     n = B * Hkv * T
-    ctx = kvq.Context(Hkv, bits, inp["signs_k"], inp["signs_v"], device=0)
+    ctx = kvq.Context(Hkv, bits, inp["signs_k"], inp["signs_v"], device=dev.index)
     k0 = torch.from_numpy(inp["k"]).to(dev)
     v0 = torch.from_numpy(inp["v"]).to(dev)
     q = torch.from_numpy(inp["q"]).to(dev)
+    nset = 4
     sets = []
-    for i in range(args.sets):
+    for _ in range(nset):
         sets.append(dict(k=k0.clone(), v=v0.clone(),
                          kc=torch.empty((B, Hkv, T, 16 * bits), dtype=torch.uint8, device=dev),
                          kn=torch.empty((B, Hkv, T), dtype=torch.float32, device=dev),
                          vc=torch.empty((B, Hkv, T, 16 * bits), dtype=torch.uint8, device=dev),
                          vn=torch.empty((B, Hkv, T), dtype=torch.float32, device=dev)))
     del k0, v0
-    out = torch.empty((B, Hq, 128), dtype=torch.float32, device=dev)
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
     ws = ctx.decode_ws(B, Hq, T)
+    stream = torch.cuda.current_stream(dev)
+    for st in sets:  # every set holds valid codes before the first timed decode
+        kvq.kvq_quantize_kv(ctx, st["k"], st["v"], B, Hkv, T, st["kc"], st["kn"], st["vc"], st["vn"])
     torch.cuda.synchronize()
 
     E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-    stream = torch.cuda.current_stream(dev)
 
     def step(s, ev=None):
-        st = sets[s % len(sets)]
+        st = sets[s % nset]
+        sd = sets[(s + nset // 2) % nset]
         if ev is not None:
             ev[0].record(stream)
         kvq.kvq_quantize_kv(ctx, st["k"], st["v"], B, Hkv, T, st["kc"], st["kn"], st["vc"], st["vn"])
         if ev is not None:
             ev[1].record(stream)
-        kvq.kvq_attn_decode(ctx, q, B, Hq, T, st["kc"], st["kn"], st["vc"], st["vn"], 0.0, out, ws)
+        kvq.kvq_attn_decode(ctx, q, B, Hq, T, sd["kc"], sd["kn"], sd["vc"], sd["vn"], 0.0, out, ws)
         if ev is not None:
             ev[2].record(stream)
 
@@ -116,22 +196,23 @@ def main():
     torch.cuda.synchronize()
     evs = [[E() for _ in range(3)] for _ in range(args.steps)]
     t_start, t_end = E(), E()
+    torch.cuda.synchronize()
     t_start.record(stream)
     for s in range(args.steps):
-        step(s, evs[s])
+        step(args.warmup + s, evs[s])
     t_end.record(stream)
     torch.cuda.synchronize()
     ms_step = t_start.elapsed_time(t_end) / args.steps
-    q_ms = np.mean([e[0].elapsed_time(e[1]) for e in evs])
-    d_ms = np.mean([e[1].elapsed_time(e[2]) for e in evs])
+    q_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    d_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
 
-    qb, db = algorithmic_bytes(n, bits)
+    qb = quant_bytes(2 * n, bits)
+    db = decode_bytes(n, bits)
     q_gbs = qb / (q_ms * 1e-3) / 1e9
     d_gbs = db / (d_ms * 1e-3) / 1e9
-    value = 3 * n / (ms_step * 1e-3)
     res = {
         "metric": "KV vectors quantized/s + keys scored/s (decode), % of HBM roofline, 1 GPU",
-        "value": value,
+        "value": 3 * n / (ms_step * 1e-3),
         "unit": "vectors/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -142,23 +223,225 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": "Llama-3-8B-shaped layer: batch %d, %d KV heads x 128, %d query heads, "
-                               "%d tokens, %d-bit codes; quantise K+V, one decode step" % (B, Hkv, Hq, T, bits),
-                   "bits": bits, "tokens": T, "kv_heads": Hkv, "q_heads": Hq, "batch": B,
-                   "buffer_sets": args.sets},
+        "config": {"workload": "Llama-3-8B-shaped layer: batch %d, %d KV heads x 128, %d query heads, %d tokens, "
+                               "%d-bit codes; quantise K+V, one decode step" % (B, Hkv, Hq, T, bits),
+                   "bits": bits, "tokens": T, "kv_heads": Hkv, "q_heads": Hq, "batch": B, "buffer_sets": nset},
         "roofline": {"bound": "hbm", "achieved": q_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": q_gbs / HBM_PEAK_GBS, "traffic": None, "kernel": "kvq_quantize",
+                     "frac": q_gbs / HBM_PEAK_GBS, "traffic": read_traffic(), "kernel": "kvq_quantize_kv",
                      "bytes_per_launch": qb, "ms_per_launch": q_ms},
         "kernels": {
-            "kvq_quantize": {"ms": q_ms, "GB/s": q_gbs, "frac_hbm": q_gbs / HBM_PEAK_GBS,
-                             "vectors_per_s": 2 * n / (q_ms * 1e-3), "launch": "kvq_quantize_kv (K and V)"},
+            "kvq_quantize_kv": {"ms": q_ms, "GB/s": q_gbs, "frac_hbm": q_gbs / HBM_PEAK_GBS,
+                                "vectors_per_s": 2 * n / (q_ms * 1e-3)},
             "kvq_attn_decode": {"ms": d_ms, "GB/s": d_gbs, "frac_hbm": d_gbs / HBM_PEAK_GBS,
                                 "keys_per_s": n / (d_ms * 1e-3), "bytes_per_launch": db},
         },
         "step_frac_hbm": (qb + db) / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
     }
+    cpu_inp = inp
+    del sets
+    torch.cuda.empty_cache()
+    return res, cpu_inp
+
+
+# --------------------------------------------------------------------------- rows
+def rows(torch, kvq, synth, dev, timer, reps, oracle_rates):
+    import oracle as O
+    out = {}
+    rng_sets = lambda total_bytes: max(2, int(np.ceil(600e6 / max(total_bytes, 1))))  # noqa: E731
+
+    # l8b32k: quantize K+V and decode at b = 2, 3, 4
+    inp = synth.make("l8b32k")
+    B, Hkv, T = inp["k"].shape[:3]
+    Hq, n = inp["Hq"], B * Hkv * T
+    k0 = torch.from_numpy(inp["k"]).to(dev)
+    v0 = torch.from_numpy(inp["v"]).to(dev)
+    q = torch.from_numpy(inp["q"]).to(dev)
+    xs = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(3)]
+    for bits in (2, 3, 4):
+        ctx = kvq.Context(Hkv, bits, inp["signs_k"], inp["signs_v"], device=dev.index)
+        ns = rng_sets(decode_bytes(n, bits))
+        cs = [[torch.empty((B, Hkv, T, 16 * bits), dtype=torch.uint8, device=dev),
+               torch.empty((B, Hkv, T), dtype=torch.float32, device=dev),
+               torch.empty((B, Hkv, T, 16 * bits), dtype=torch.uint8, device=dev),
+               torch.empty((B, Hkv, T), dtype=torch.float32, device=dev)] for _ in range(ns)]
+
+        def quant(i):
+            k, v = xs[i % len(xs)]
+            c = cs[i % ns]
+            kvq.kvq_quantize_kv(ctx, k, v, B, Hkv, T, c[0], c[1], c[2], c[3])
+        out["quantize_kv_l8b32k_b%d" % bits] = row(*timer.run(quant, reps, 4 + ns), nbytes=quant_bytes(2 * n, bits),
+                                                    units_per_launch=2 * n, unit="vectors")
+        outb = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+        ws = ctx.decode_ws(B, Hq, T)
+
+        def dec(i):
+            c = cs[i % ns]
+            kvq.kvq_attn_decode(ctx, q, B, Hq, T, c[0], c[1], c[2], c[3], 0.0, outb, ws)
+        out["attn_decode_l8b32k_b%d" % bits] = row(*timer.run(dec, reps, 5), nbytes=decode_bytes(n, bits),
+                                                    units_per_launch=n, unit="keys", buffer_sets=ns)
+        del cs, ctx
+    sub = {k: v[:, :, :2048] for k, v in inp.items() if k in ("k", "v")}
+    oracle_rates["quantize_kv_l8b32k_b3"] = oracle_rate(
+        lambda: O.quantize(sub["k"], inp["signs_k"], 3), B * Hkv * 2048)
+    rq = O.quantize(sub["k"], inp["signs_k"], 3)
+    rv = O.quantize(sub["v"], inp["signs_v"], 3)
+    oracle_rates["attn_decode_l8b32k_b3"] = oracle_rate(
+        lambda: O.attention(inp["q"], rq["codes"], rq["norms"], rv["codes"], rv["norms"], inp["signs_k"],
+                            inp["signs_v"], 3), B * Hkv * 2048)
+    del xs, k0, v0
+    torch.cuda.empty_cache()
+
+    # batch16: decode at b = 3 (and its quantize)
+    inp = synth.make("batch16")
+    B, Hkv, T = inp["k"].shape[:3]
+    Hq, n = inp["Hq"], B * Hkv * T
+    ctx = kvq.Context(Hkv, 3, inp["signs_k"], inp["signs_v"], device=dev.index)
+    k0 = torch.from_numpy(inp["k"]).to(dev)
+    v0 = torch.from_numpy(inp["v"]).to(dev)
+    q = torch.from_numpy(inp["q"]).to(dev)
+    ns = rng_sets(decode_bytes(n, 3))
+    cs = [[torch.empty((B, Hkv, T, 48), dtype=torch.uint8, device=dev),
+           torch.empty((B, Hkv, T), dtype=torch.float32, device=dev),
+           torch.empty((B, Hkv, T, 48), dtype=torch.uint8, device=dev),
+           torch.empty((B, Hkv, T), dtype=torch.float32, device=dev)] for _ in range(ns)]
+
+    def quant16(i):
+        c = cs[i % ns]
+        kvq.kvq_quantize_kv(ctx, k0, v0, B, Hkv, T, c[0], c[1], c[2], c[3])
+    out["quantize_kv_batch16_b3"] = row(*timer.run(quant16, reps, ns), nbytes=quant_bytes(2 * n, 3),
+                                        units_per_launch=2 * n, unit="vectors")
+    outb = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    ws = ctx.decode_ws(B, Hq, T)
+
+    def dec16(i):
+        c = cs[i % ns]
+        kvq.kvq_attn_decode(ctx, q, B, Hq, T, c[0], c[1], c[2], c[3], 0.0, outb, ws)
+    out["attn_decode_batch16_b3"] = row(*timer.run(dec16, reps, 5), nbytes=decode_bytes(n, 3),
+                                        units_per_launch=n, unit="keys", buffer_sets=ns)
+    del cs, k0, v0, ctx
+    torch.cuda.empty_cache()
+
+    # long128k_qjl: quantize K with the QJL residual, logits for 32 query heads
+    inp = synth.make("long128k_qjl")
+    B, Hkv, T = inp["k"].shape[:3]
+    Hq, n = inp["Hq"], B * Hkv * T
+    ctx = kvq.Context(Hkv, 2, inp["signs_k"], inp["signs_v"], mode=kvq.KVQ_MODE_MSE_QJL, qjl_S=inp["S"],
+                      device=dev.index)
+    k0 = torch.from_numpy(inp["k"]).to(dev)
+    ks = [k0, k0.clone()]
+    q = torch.from_numpy(inp["q"]).to(dev)
+    lb = logits_bytes(n, Hq // Hkv, 2, qjl=True)
+    ns = rng_sets(lb)
+    cs = [dict(codes=torch.empty((B, Hkv, T, 32), dtype=torch.uint8, device=dev),
+               norms=torch.empty((B, Hkv, T), dtype=torch.float32, device=dev),
+               qjl_signs=torch.empty((B, Hkv, T, 16), dtype=torch.uint8, device=dev),
+               qjl_gamma=torch.empty((B, Hkv, T), dtype=torch.float32, device=dev)) for _ in range(ns)]
+
+    def qjl(i):
+        c = cs[i % ns]
+        kvq.kvq_quantize(ctx, kvq.KVQ_KIND_K, ks[i % 2], B, Hkv, T, c["codes"], c["norms"], c["qjl_signs"],
+                         c["qjl_gamma"])
+    out["quantize_qjl_long128k_b2"] = row(*timer.run(qjl, reps, ns), nbytes=quant_bytes(n, 2, qjl=True),
+                                          flops=n * 2 * D * D, units_per_launch=n, unit="vectors",
+                                          note="flops = the S r projection, 2 d^2 per key")
+    lo = [torch.empty((B, Hq, T), dtype=torch.float32, device=dev) for _ in range(2)]
+
+    def lg(i):
+        c = cs[i % ns]
+        kvq.kvq_logits(ctx, q, B, Hq, T, c["codes"], c["norms"], c["qjl_signs"], c["qjl_gamma"], lo[i % 2])
+    out["logits_qjl_long128k_b2"] = row(*timer.run(lg, reps, 5), nbytes=lb, units_per_launch=n * Hq,
+                                        unit="logits", buffer_sets=ns)
+    kk = inp["k"][:, :, :1024]
+
+    def oracle_qjl():
+        r = O.quantize(kk, inp["signs_k"], 2, want_y=True)
+        return r, O.qjl(r["y"], r["idx"], inp["S"], 2)
+    oracle_rates["quantize_qjl_long128k_b2"] = oracle_rate(oracle_qjl, B * Hkv * 1024)
+    r, rj = oracle_qjl()
+    oracle_rates["logits_qjl_long128k_b2"] = oracle_rate(
+        lambda: O.logits(inp["q"], r["codes"], r["norms"], inp["signs_k"], 2, 1, rj["signs"], rj["gamma"], inp["S"]),
+        B * Hq * 1024)
+    del ks, k0, cs, lo, ctx
+    torch.cuda.empty_cache()
+
+    # tiny: latency of quantize and logits (one head, 4096 keys)
+    inp = synth.make("tiny")
+    B, Hkv, T = inp["k"].shape[:3]
+    ctx = kvq.Context(Hkv, 3, inp["signs_k"], inp["signs_v"], device=dev.index)
+    k0 = torch.from_numpy(inp["k"]).to(dev)
+    q = torch.from_numpy(inp["q"]).to(dev)
+    c = ctx.quantize(kvq.KVQ_KIND_K, k0)
+    lt = torch.empty((B, inp["Hq"], T), dtype=torch.float32, device=dev)
+    out["quantize_tiny_b3"] = row(*timer.run(lambda i: ctx.quantize(kvq.KVQ_KIND_K, k0, out=c), reps, 5),
+                                  nbytes=quant_bytes(T, 3), note="latency-bound (4096 vectors)")
+    out["logits_tiny_b3"] = row(*timer.run(lambda i: kvq.kvq_logits(ctx, q, B, inp["Hq"], T, c["codes"], c["norms"],
+                                                                    None, None, lt), reps, 5),
+                                nbytes=logits_bytes(T, 1, 3), note="latency-bound (4096 logits)")
+    del ctx
+
+    # nsn_vq: NSN + Hadamard + 8-dim VQ over 8 heads x 65536 tokens
+    inp = synth.make("nsn_vq")
+    H, T = inp["x"].shape[:2]
+    cb = np.loadtxt(os.path.join(ROOT, "tests", "golden", "vq_codebook_256x8.txt"), dtype=np.float32).reshape(256, 8)
+    ctx = kvq.Context(H, 1, mode=kvq.KVQ_MODE_NSN_VQ, vq_codebook=cb, device=dev.index)
+    x0 = torch.from_numpy(inp["x"]).to(dev)
+    xsn = [x0] + [x0.clone() for _ in range(3)]
+    o = ctx.nsn_vq_quantize(x0)
+    ws = torch.empty(int(kvq.lib().kvq_nsn_vq_ws_bytes(ctx.handle, H, T)), dtype=torch.uint8, device=dev)
+    out["nsn_vq_8x65536"] = row(*timer.run(lambda i: ctx.nsn_vq_quantize(xsn[i % 4], out=o, ws=ws), reps, 4),
+                                nbytes=nsn_bytes(H * T), flops=H * T * 16 * 256 * 8 * 2, units_per_launch=H * T,
+                                unit="vectors", note="three launches (stats, mean, search); x is read twice; "
+                                "flops = exhaustive distances 16 x 256 x 8 x 2 per vector")
+    oracle_rates["nsn_vq_8x65536"] = oracle_rate(lambda: O.nsn_vq(inp["x"][:1, :1024], cb), 1024)
+    del xsn, x0, ctx
+    torch.cuda.empty_cache()
+    return out
+
+
+def calibrate_copy(torch, dev, nbytes=256 << 20, reps=3):
+    """A plain device copy of known size, for scaling rocprofv3's byte counters."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy": {"bytes_read_per_copy": nbytes, "bytes_written_per_copy": nbytes,
+                                         "copies": reps}}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--row-reps", type=int, default=20)
+    ap.add_argument("--no-rows", action="store_true", help="time only the main step")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true", help="run a 256 MiB device copy and exit")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the library has no multi-GPU path (--gpus %d refused)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from calibration_free_kv_amd import kvq, synth
+
+    dev = torch.device("cuda", 0)
+    if args.calibrate_copy:
+        calibrate_copy(torch, dev)
+        return
+    timer = Timer(torch, torch.cuda.current_stream(dev))
+    res, cpu_inp = main_step(torch, kvq, synth, args, dev, timer)
+    if not args.no_rows:
+        orates = {}
+        res["rows"] = rows(torch, kvq, synth, dev, timer, args.row_reps, orates)
+        for k, v in orates.items():
+            res["rows"][k]["oracle_units_per_s"] = v
+            res["rows"][k]["oracle_cores"] = 1
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(inp, bits)
+        res["cpu_baseline"] = cpu_baseline(cpu_inp, 3)
     print(json.dumps(res))
 
 
