@@ -115,21 +115,73 @@ __device__ __forceinline__ void index_bits(float y, const float *P, uint64_t *M)
 // up in slot (c + v) mod 16: a skewed layout in which the later per-lane row
 // reads (lane v, chunk c) fall into distinct LDS banks.  Each instruction
 // still reads one contiguous KiB of HBM.
+// The chunk a lane fetches depends on j only through j mod 4, so the address
+// is a wave-uniform base (src + 256 (j/4), in 16-byte units) plus one of four
+// per-lane offsets: 4 VGPRs instead of 16 64-bit addresses held across the
+// persistent loop.  Every call issues exactly 16 load instructions with all
+// lanes active (waits count them); rows past a ragged tail re-read the last
+// valid row, and are never stored.
 __device__ __forceinline__ void tile_to_lds(const u4_t *src, int nv, u4_t *L, int lane)
 {
+    // lane is made opaque so that the offsets are recomputed here (a few
+    // VALU ops) rather than hoisted out of the persistent loop and spilled
+    asm volatile("" : "+v"(lane));
+    if (nv == kTile) {
+        uint32_t off[4];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        const int v = 4 * j + (lane >> 4);
-        const int c = ((lane & 15) - v) & 15;
-        if (v < nv)
+        for (int r = 0; r < 4; ++r) {
+            const int v = 4 * r + (lane >> 4);
+            off[r] = (uint32_t)(v * 16 + (((lane & 15) - v) & 15));
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
             __builtin_amdgcn_global_load_lds(
-                (const __attribute__((address_space(1))) void *)(src + v * 16 + c),
+                (const __attribute__((address_space(1))) void *)(src + 256 * (j >> 2) + off[j & 3]),
                 (__attribute__((address_space(3))) void *)(L + j * 64), 16, 0, 0);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int v = 4 * j + (lane >> 4);
+            const int c = ((lane & 15) - v) & 15;
+            const int row = v < nv ? v : nv - 1;
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void *)(src + row * 16 + c),
+                (__attribute__((address_space(3))) void *)(L + j * 64), 16, 0, 0);
+        }
     }
 }
 
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
+// vmcnt(N): all but the N most recently issued vector memory operations have
+// completed (they complete in issue order); lgkmcnt and expcnt not waited on.
+template <int N>
+__device__ __forceinline__ void wait_vm_n()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
 __device__ __forceinline__ void wait_lgkm() { __builtin_amdgcn_s_waitcnt(0xC07F); } // lgkmcnt(0)
+
+// Wait for the wave's tile copy and read row `lane` (its vector) into w.
+template <int N>
+__device__ __forceinline__ void take_rows(const u4_t *L, int lane, uint32_t *w)
+{
+    // the row reads stay after the preceding arithmetic: moved up into it
+    // they would hold 64 more VGPRs live through the transform
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" : "+v"(lane));  // addresses recomputed per tile, not hoisted and spilled
+    wait_vm_n<N>();
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+        const u4_t v = L[lane * 16 + ((c + lane) & 15)];
+        w[4 * c + 0] = v.x;
+        w[4 * c + 1] = v.y;
+        w[4 * c + 2] = v.z;
+        w[4 * c + 3] = v.w;
+    }
+    wait_lgkm();
+    __builtin_amdgcn_wave_barrier();
+}
 
 struct TileGeom {
     int64_t v0;  // first vector of the tile
@@ -148,58 +200,53 @@ __device__ __forceinline__ TileGeom geom(int64_t tile, int64_t T, int H, int64_t
     return g;
 }
 
-// Persistent waves: wave w processes tiles w, w + W, w + 2W, ... (W = waves in
-// the grid).  The next tile's loads are issued as soon as the current tile
-// has been read from LDS into registers, so they overlap the transform.
-// One launch may cover two tensors of the same shape (K and V): tiles
-// [0, n_tiles) belong to tensor 0 and [n_tiles, 2 n_tiles) to tensor 1.
+// Persistent waves, two per SIMD: wave w processes tiles w, w + W, w + 2W, ...
+// (W = waves in the grid).  The next tile's copy into the wave's LDS buffer
+// is issued before this tile is encoded; after encoding, the wave waits for
+// it (vmcnt(0): it had the whole encode to complete), reads it into
+// registers, issues the copy of the tile after it and only then stores this
+// tile's codes, so that no wait sits right behind the wave's own stores (vmcnt
+// counts stores too).  One launch may cover two tensors of the same shape (K
+// and V): tiles [0, n_tiles) belong to tensor 0 and [n_tiles, 2 n_tiles) to
+// tensor 1.
 struct QArgs {
     const u4_t *x[2];
     u4_t *codes[2];
     float *norms[2];
-    const uint32_t *sgnmask[2];
+    int kind[2];  // K (0) or V (1): selects the random signs of each tensor
 };
 
+// sgn: sign masks [2][H][64] of D_K and D_V; a separate read-only, non-aliased
+// argument so that (with a wave-uniform index) the masks are scalar loads.
 template <int BITS>
-__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_quantize(QArgs a, HalfThresholds ht, int64_t T, int H,
-                                                          int64_t tiles_per_bh, int64_t n_tiles,
-                                                          int n_tensors)
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_quantize(
+    QArgs a, const uint32_t *__restrict__ sgn, HalfThresholds ht, int64_t T, int H, int64_t tiles_per_bh,
+    int64_t n_tiles, int n_tensors)
 {
-    __shared__ u4_t lds[kWaves][kTile * 16];
+    __shared__ u4_t lds[kWaves][kTile * 16];  // 64 KiB
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
     u4_t *L = lds[wv];
     const int64_t total = n_tiles * n_tensors;
     const int64_t stride = (int64_t)gridDim.x * kWaves;
     int64_t tile = (int64_t)blockIdx.x * kWaves + wv;
-    if (tile < total) {
-        const int k = tile >= n_tiles;
-        const TileGeom g = geom(tile - k * n_tiles, T, H, tiles_per_bh);
-        tile_to_lds(a.x[k] + g.v0 * 16, g.nv, L, lane);
-    }
-    for (; tile < total; tile += stride) {
+    if (tile >= total) return;  // wave-uniform
+    auto issue = [&](int64_t t) {
+        const int k = t >= n_tiles;
+        const TileGeom gg = geom(t - k * n_tiles, T, H, tiles_per_bh);
+        tile_to_lds(a.x[k] + gg.v0 * 16, gg.nv, L, lane);
+    };
+    uint32_t w[64];
+    issue(tile);
+    take_rows<0>(L, lane, w);
+    if (tile + stride < total) issue(tile + stride);
+    for (;;) {
         const int kt = tile >= n_tiles;
         const TileGeom g = geom(tile - kt * n_tiles, T, H, tiles_per_bh);
-        wait_vm();
-        uint32_t w[64];
-#pragma unroll
-        for (int c = 0; c < 16; ++c) {
-            const u4_t v = L[lane * 16 + ((c + lane) & 15)];
-            w[4 * c + 0] = v.x;
-            w[4 * c + 1] = v.y;
-            w[4 * c + 2] = v.z;
-            w[4 * c + 3] = v.w;
-        }
-        wait_lgkm();
-        const int64_t next = tile + stride;
-        if (next < total) {
-            const int kn = next >= n_tiles;
-            const TileGeom gn = geom(next - kn * n_tiles, T, H, tiles_per_bh);
-            tile_to_lds(a.x[kn] + gn.v0 * 16, gn.nv, L, lane);
-        }
-        if (lane >= g.nv) continue;
 
-        const uint32_t *sg = a.sgnmask[kt] + g.h * 64;
+        // wave-uniform head: the masks come through the scalar cache (lgkmcnt),
+        // so waiting for them does not wait for the next tile's copy (vmcnt)
+        const uint32_t *sg = sgn + __builtin_amdgcn_readfirstlane((a.kind[kt] * H + g.h) * 64);
         // ||x||^2 with fp16 products (exact in fp32) accumulated in fp32, and D.
         float ss = 0.0f;
 #pragma unroll
@@ -262,14 +309,26 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
             }
         }
 
-        const int64_t v = g.v0 + lane;
-        u4_t *dst = a.codes[kt] + v * BITS;
-#pragma unroll
-        for (int q = 0; q < BITS; ++q) {
-            u4_t o = {out[4 * q], out[4 * q + 1], out[4 * q + 2], out[4 * q + 3]};
-            dst[q] = o;
+        // The next tile's rows, then the copy of the tile after it, then this
+        // tile's stores: the only wait comes right after the encode.
+        const int64_t next = tile + stride;
+        const bool has_next = next < total;
+        if (has_next) {
+            take_rows<0>(L, lane, w);
+            if (next + stride < total) issue(next + stride);
         }
-        a.norms[kt][v] = rho;
+        if (lane < g.nv) {  // lanes past a ragged tail encoded stale rows
+            const int64_t v = g.v0 + lane;
+            u4_t *dst = a.codes[kt] + v * BITS;
+#pragma unroll
+            for (int q = 0; q < BITS; ++q) {
+                u4_t o = {out[4 * q], out[4 * q + 1], out[4 * q + 2], out[4 * q + 3]};
+                dst[q] = o;
+            }
+            a.norms[kt][v] = rho;
+        }
+        if (!has_next) break;
+        tile = next;
     }
 }
 
@@ -568,8 +627,8 @@ hipError_t run(const kvq_ctx *ctx, const QArgs &a, int n_tensors, int64_t B, int
     const int64_t n_tiles = tiles_per_bh * B * ctx->H;
     int64_t blocks = (n_tiles * n_tensors + kWaves - 1) / kWaves;
     if (blocks > 2 * (int64_t)ctx->n_cu) blocks = 2 * (int64_t)ctx->n_cu;  // 8 resident waves per CU
-    hipLaunchKernelGGL(k_quantize<BITS>, dim3((unsigned)blocks), dim3(kWaves * 64), 0, s, a, ht, T, ctx->H,
-                       tiles_per_bh, n_tiles, n_tensors);
+    hipLaunchKernelGGL(k_quantize<BITS>, dim3((unsigned)blocks), dim3(kWaves * 64), 0, s, a,
+                       (const uint32_t *)ctx->d_sgnmask, ht, T, ctx->H, tiles_per_bh, n_tiles, n_tensors);
     return hipGetLastError();
 }
 
@@ -603,7 +662,7 @@ hipError_t launch_quantize(const kvq_ctx *ctx, int kind, const void *x, int64_t 
     a.x[0] = a.x[1] = (const u4_t *)x;
     a.codes[0] = a.codes[1] = (u4_t *)codes;
     a.norms[0] = a.norms[1] = norms;
-    a.sgnmask[0] = a.sgnmask[1] = ctx->d_sgnmask + (size_t)kind * ctx->H * 64;
+    a.kind[0] = a.kind[1] = kind;
     return dispatch(ctx, a, 1, B, T, s);
 }
 
@@ -618,8 +677,8 @@ hipError_t launch_quantize_kv(const kvq_ctx *ctx, const void *k, const void *v, 
     a.codes[1] = (u4_t *)v_codes;
     a.norms[0] = k_norms;
     a.norms[1] = v_norms;
-    a.sgnmask[0] = ctx->d_sgnmask;
-    a.sgnmask[1] = ctx->d_sgnmask + (size_t)ctx->H * 64;
+    a.kind[0] = 0;
+    a.kind[1] = 1;
     return dispatch(ctx, a, 2, B, T, s);
 }
 

@@ -21,6 +21,7 @@ typedef _Float16 half_t;
 typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
 typedef float f2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
 
@@ -47,28 +48,39 @@ __device__ __forceinline__ uint32_t field(const uint32_t *Wd, int f)
     return v & ((1u << nb) - 1u);
 }
 
+// One Walsh-Hadamard transform of 128 values held two per lane (lane l holds
+// coordinates 2l and 2l+1): the first stage inside the lane, the other six
+// across lanes with shuffles.
+__device__ __forceinline__ void wave_fwht(float &x0, float &x1, int lane)
+{
+    const float a = x0 + x1;
+    x1 = x0 - x1;
+    x0 = a;
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+        const float p0 = __shfl_xor(x0, m), p1 = __shfl_xor(x1, m);
+        const bool up = (lane & m) != 0;
+        x0 = up ? p0 - x0 : x0 + p0;
+        x1 = up ? p1 - x1 : x1 + p1;
+    }
+}
+
 // Prologue shared by the score kernels: qr[G][128] <- H (D .* q_h) for the G
-// query heads of KV head g of batch b, then the field tables.  All threads of
-// the block participate; ends with a barrier.
-template <int BITS, int G>
+// query heads of KV head g of batch b, one wave per head.  Ends with a barrier.
+template <int G>
 __device__ void rotate_queries(const half_t *__restrict__ q, const float *__restrict__ signs,
                                int64_t b, int g, int Hq, float *qr)
 {
-    const int tid = threadIdx.x, nthr = blockDim.x;
-    for (int idx = tid; idx < G * kD; idx += nthr) {
-        const int h = idx >> 7, i = idx & (kD - 1);
-        qr[idx] = (float)q[((int64_t)b * Hq + (int64_t)g * G + h) * kD + i] * signs[g * kD + i];
-    }
-    for (int s = 1; s < kD; s <<= 1) {
-        __syncthreads();
-        for (int pidx = tid; pidx < G * kD / 2; pidx += nthr) {
-            const int h = pidx >> 6, j = pidx & 63;
-            const int i0 = (j / s) * 2 * s + (j % s);
-            float *r = qr + h * kD;
-            const float a = r[i0], c = r[i0 + s];
-            r[i0] = a + c;
-            r[i0 + s] = a - c;
-        }
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    for (int h = wv; h < G; h += nw) {
+        const uint32_t pr =
+            reinterpret_cast<const uint32_t *>(q + ((int64_t)b * Hq + (int64_t)g * G + h) * kD)[lane];
+        const f2_t sg = reinterpret_cast<const f2_t *>(signs + g * kD)[lane];
+        float x0 = (float)__builtin_bit_cast(h2_t, pr).x * sg.x;
+        float x1 = (float)__builtin_bit_cast(h2_t, pr).y * sg.y;
+        wave_fwht(x0, x1, lane);
+        reinterpret_cast<f2_t *>(qr + h * kD)[lane] = f2_t{x0, x1};
     }
     __syncthreads();
 }
@@ -168,7 +180,7 @@ __global__ __launch_bounds__(kThreads) void k_logits(
     const int g = (int)(bh - b * H);
 
     stage_centroids(cb, ctab);
-    rotate_queries<BITS, G>(q, signs, b, g, Hq, qr);
+    rotate_queries<G>(q, signs, b, g, Hq, qr);
     build_tables<BITS, G>(qr, ctab, lut);
     if constexpr (QJL) {
         const float inv_sqrt_d = 0.08838834764831845f;
@@ -314,15 +326,6 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
     const int64_t b = bh / H;
     const int g = (int)(bh - b * H);
 
-    stage_centroids(cb, smem + SM::ctab);
-    rotate_queries<BITS, G>(q, signs_k, b, g, Hq, qr);
-    build_tables<BITS, G>(qr, smem + SM::ctab, lut);
-    constexpr uint32_t cm = (1u << BITS) - 1u;
-    for (int e = tid; e < (1 << (2 * BITS)); e += kDecThreads) {
-        c2[2 * e] = cb.c[e & cm];
-        c2[2 * e + 1] = cb.c[(e >> BITS) & cm];
-    }
-    __syncthreads();
 
     // V lane roles: coordinate quad cq (coordinates 4cq .. 4cq+3), token parity.
     const int cq = lane & 31, par = lane >> 5;
@@ -364,7 +367,18 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
         }
     };
     constexpr int64_t kStride = (int64_t)kDecWaves * 64;
+    // The first tile's loads go out before the prologue, so their latency
+    // overlaps the query rotation and the table build.
     fetch(t_begin + (int64_t)wv * 64);
+    stage_centroids(cb, smem + SM::ctab);
+    rotate_queries<G>(q, signs_k, b, g, Hq, qr);
+    build_tables<BITS, G>(qr, smem + SM::ctab, lut);
+    constexpr uint32_t cm = (1u << BITS) - 1u;
+    for (int e = tid; e < (1 << (2 * BITS)); e += kDecThreads) {
+        c2[2 * e] = cb.c[e & cm];
+        c2[2 * e + 1] = cb.c[(e >> BITS) & cm];
+    }
+    __syncthreads();
     for (int64_t t0 = t_begin + (int64_t)wv * 64; t0 < t_end; t0 += kStride) {
         const int nt = (int)min((int64_t)64, t_end - t0);
         const bool valid = lane < nt;
@@ -481,56 +495,59 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
     __syncthreads();
     if (!last) return;
 
-    // Merge weights per (split, head): f = 2^(m_s - M) / (d L), L = sum_s l_s 2^(m_s - M).
-    float *ms = smem + SM::vbuf;      // reuse: [n_split][G] split maxima, then weights
-    float *ls = ms + n_split * G;     // [n_split][G] split sums
-    float *o = qr;                    // reuse: [G][128]
+    // Merge of the splits, one wave per head (the other waves are done):
+    // f_s = 2^(m_s - M) / (d L) with M = max_s m_s, L = sum_s l_s 2^(m_s - M);
+    // lane l accumulates coordinates 2l, 2l+1 over the splits, then the
+    // inverse rotation out = D_V .* H (sum_s f_s acc_s) in the same wave.
+    float *fw = smem + SM::vbuf;  // reuse: [G][n_split] merge weights
     const float *all = part + (bh * n_split) * G * (kD + 2);
-    for (int idx = tid; idx < n_split * G; idx += kDecThreads) {
-        ms[idx] = all[idx * (kD + 2)];
-        ls[idx] = all[idx * (kD + 2) + 1];
-    }
-    __syncthreads();
-    if (tid < G) {
+    const int64_t sst = (int64_t)G * (kD + 2);  // split stride
+    constexpr int kPerLane = kMaxSplits / 64;
+    for (int h = wv; h < G; h += kDecWaves) {
+        const float *ah = all + h * (kD + 2);
+        float mv[kPerLane], lv[kPerLane];
         float M = -INFINITY;
-        for (int sp = 0; sp < n_split; ++sp) M = fmaxf(M, ms[sp * G + tid]);
+#pragma unroll
+        for (int k = 0; k < kPerLane; ++k) {
+            const int sp = lane + 64 * k;
+            mv[k] = sp < n_split ? ah[sp * sst] : -INFINITY;
+            lv[k] = sp < n_split ? ah[sp * sst + 1] : 0.0f;
+            M = fmaxf(M, mv[k]);
+        }
+        M = wave_max(M);
         float L = 0.0f;
-        for (int sp = 0; sp < n_split; ++sp) L += ls[sp * G + tid] * __builtin_amdgcn_exp2f(ms[sp * G + tid] - M);
+#pragma unroll
+        for (int k = 0; k < kPerLane; ++k) L = fmaf(lv[k], __builtin_amdgcn_exp2f(mv[k] - M), L);
+        L = wave_sum(L);
         const float inv = 1.0f / (L * kD);
-        for (int sp = 0; sp < n_split; ++sp) ms[sp * G + tid] = __builtin_amdgcn_exp2f(ms[sp * G + tid] - M) * inv;
-    }
-    __syncthreads();
-    for (int idx = tid; idx < G * kD; idx += kDecThreads) {
-        const int h = idx >> 7, i = idx & (kD - 1);
-        const float *col = all + h * (kD + 2) + 2 + i;
-        float A = 0.0f;
+        float *fh = fw + h * n_split;
+#pragma unroll
+        for (int k = 0; k < kPerLane; ++k) {
+            const int sp = lane + 64 * k;
+            if (sp < n_split) fh[sp] = __builtin_amdgcn_exp2f(mv[k] - M) * inv;
+        }
+        wave_lds_sync();
+        const float *col = ah + 2 + 2 * lane;
+        float a0 = 0.0f, a1 = 0.0f;
         int sp = 0;
         for (; sp + 16 <= n_split; sp += 16) {  // 16 independent loads in flight
-            float v[16];
+            f2_t v[16];
 #pragma unroll
-            for (int u = 0; u < 16; ++u) v[u] = col[(int64_t)(sp + u) * G * (kD + 2)];
+            for (int u = 0; u < 16; ++u) v[u] = *reinterpret_cast<const f2_t *>(col + (sp + u) * sst);
 #pragma unroll
-            for (int u = 0; u < 16; ++u) A = fmaf(ms[(sp + u) * G + h], v[u], A);
+            for (int u = 0; u < 16; ++u) {
+                a0 = fmaf(fh[sp + u], v[u].x, a0);
+                a1 = fmaf(fh[sp + u], v[u].y, a1);
+            }
         }
-        for (; sp < n_split; ++sp) A = fmaf(ms[sp * G + h], col[(int64_t)sp * G * (kD + 2)], A);
-        o[idx] = A;
-    }
-    // inverse rotation: out = D_V .* H o
-    for (int s2 = 1; s2 < kD; s2 <<= 1) {
-        __syncthreads();
-        for (int pidx = tid; pidx < G * kD / 2; pidx += kDecThreads) {
-            const int h = pidx >> 6, j = pidx & 63;
-            const int i0 = (j / s2) * 2 * s2 + (j % s2);
-            float *r = o + h * kD;
-            const float a = r[i0], c = r[i0 + s2];
-            r[i0] = a + c;
-            r[i0 + s2] = a - c;
+        for (; sp < n_split; ++sp) {
+            const f2_t v = *reinterpret_cast<const f2_t *>(col + sp * sst);
+            a0 = fmaf(fh[sp], v.x, a0);
+            a1 = fmaf(fh[sp], v.y, a1);
         }
-    }
-    __syncthreads();
-    for (int idx = tid; idx < G * kD; idx += kDecThreads) {
-        const int h = idx >> 7, i = idx & (kD - 1);
-        out[((b * Hq) + (int64_t)g * G + h) * kD + i] = o[idx] * signs_v[g * kD + i];
+        wave_fwht(a0, a1, lane);
+        const f2_t sv = reinterpret_cast<const f2_t *>(signs_v + g * kD)[lane];
+        reinterpret_cast<f2_t *>(out + ((b * Hq) + (int64_t)g * G + h) * kD)[lane] = f2_t{a0 * sv.x, a1 * sv.y};
     }
     if (tid == 0) counters[bh] = 0u;  // leave the counter ready for the next call
 }
