@@ -327,19 +327,22 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
     const int g = (int)(bh - b * H);
 
 
-    // V lane roles: coordinate quad cq (coordinates 4cq .. 4cq+3), token parity.
-    const int cq = lane & 31, par = lane >> 5;
-    constexpr int QB = 4 * BITS;                  // bits of a quad
-    const int qbit = QB * cq, qwd = qbit >> 5, qsh = qbit & 31;
+    // V lane roles: coordinate octet co (coordinates 8co .. 8co+7) and token
+    // phase ph (tokens ph, ph+4, ...): the 8b bits of an octet come from one
+    // funnel shift of two record dwords, its four centroid pairs from four
+    // 8-byte LDS reads.
+    const int co = lane & 15, ph = lane >> 4;
+    constexpr int OB = 8 * BITS;                  // bits of an octet
+    const int obit = OB * co, owd = obit >> 5, osh = obit & 31;
     constexpr uint32_t fmask = (1u << (2 * BITS)) - 1u;
 
-    float m_run[G], l_run[G], acc[G][4];
+    float m_run[G], l_run[G], acc[G][8];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
         m_run[h] = -INFINITY;
         l_run[h] = 0.0f;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) acc[h][k] = 0.0f;
+        for (int k = 0; k < 8; ++k) acc[h][k] = 0.0f;
     }
 
     const int64_t t_begin = (int64_t)split * chunk;
@@ -412,42 +415,59 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
             l_run[h] = l_run[h] * alpha[h] + wave_sum(p);
             wbuf[lane * G + h] = p * rvc;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) acc[h][k] *= alpha[h];
+            for (int k = 0; k < 8; ++k) acc[h][k] *= alpha[h];
         }
         wave_lds_sync();
-        for (int tt = par; tt < nt; tt += 2) {
+        for (int tt = ph; tt < nt; tt += 4) {
             const uint32_t *r = vbuf + tt * RW;
-            uint32_t bitsq = __builtin_amdgcn_alignbit(r[qwd + 1], r[qwd], (uint32_t)qsh);
-            const uint32_t f0 = bitsq & fmask, f1 = (bitsq >> (2 * BITS)) & fmask;
-            const float c00 = c2[2 * f0], c01 = c2[2 * f0 + 1], c10 = c2[2 * f1], c11 = c2[2 * f1 + 1];
-            const float *w = wbuf + tt * G;
+            const uint32_t bits = __builtin_amdgcn_alignbit(r[owd + 1], r[owd], (uint32_t)osh);
+            f2_t cp[4];
 #pragma unroll
-            for (int h = 0; h < G; ++h) {
-                const float wh = w[h];
-                acc[h][0] = fmaf(wh, c00, acc[h][0]);
-                acc[h][1] = fmaf(wh, c01, acc[h][1]);
-                acc[h][2] = fmaf(wh, c10, acc[h][2]);
-                acc[h][3] = fmaf(wh, c11, acc[h][3]);
+            for (int k = 0; k < 4; ++k)
+                cp[k] = reinterpret_cast<const f2_t *>(c2)[(bits >> (2 * BITS * k)) & fmask];
+            float wv4[G];
+            if constexpr (G % 4 == 0) {
+#pragma unroll
+                for (int h4 = 0; h4 < G / 4; ++h4) {
+                    const f4_t x = reinterpret_cast<const f4_t *>(wbuf + tt * G)[h4];
+                    wv4[4 * h4] = x.x;
+                    wv4[4 * h4 + 1] = x.y;
+                    wv4[4 * h4 + 2] = x.z;
+                    wv4[4 * h4 + 3] = x.w;
+                }
+            } else {
+#pragma unroll
+                for (int h = 0; h < G; ++h) wv4[h] = wbuf[tt * G + h];
             }
+#pragma unroll
+            for (int h = 0; h < G; ++h)
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    acc[h][2 * k] = fmaf(wv4[h], cp[k].x, acc[h][2 * k]);
+                    acc[h][2 * k + 1] = fmaf(wv4[h], cp[k].y, acc[h][2 * k + 1]);
+                }
         }
         wave_lds_sync();  // vbuf / wbuf are rewritten by the next tile
     }
-    // the two token parities hold partial sums of the same coordinates
+    // the four token phases hold partial sums of the same coordinates
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-        for (int k = 0; k < 4; ++k) acc[h][k] += __shfl_xor(acc[h][k], 32);
+        for (int k = 0; k < 8; ++k) {
+            acc[h][k] += __shfl_xor(acc[h][k], 16);
+            acc[h][k] += __shfl_xor(acc[h][k], 32);
+        }
 
     // Block merge of the waves: M = max_w m_w, acc = sum_w 2^(m_w - M) acc_w, same for l.
     float *wacc = smem + SM::vbuf;  // reuse: [waves][G][128]
     float *wm = smem + SM::wm;
     float *wl = smem + SM::wl;
     __syncthreads();  // all waves done with vbuf / wbuf
-    if (lane < 32)
+    if (lane < 16)
 #pragma unroll
         for (int h = 0; h < G; ++h)
 #pragma unroll
-            for (int k = 0; k < 4; ++k) wacc[(wv * G + h) * kD + 4 * cq + k] = acc[h][k];
+            for (int k = 0; k < 8; ++k) wacc[(wv * G + h) * kD + 8 * co + k] = acc[h][k];
     if (lane == 0)
 #pragma unroll
         for (int h = 0; h < G; ++h) {
