@@ -119,14 +119,34 @@ __global__ __launch_bounds__(256) void k_nsn_stats(const u4_t *__restrict__ x, f
     }
 }
 
-// (2) o[h][i] = sum over chunks (in order) / T.
-__global__ __launch_bounds__(kD) void k_nsn_mean(const float *__restrict__ part, float *__restrict__ o, int64_t T,
-                                                  int n_chunks)
+// (2) o[h][i] = sum over chunks / T, in a fixed order (deterministic): thread
+// group j (of 8) sums chunks j, j + 8, ... with its loads in flight together,
+// then the 8 group sums are added in order.
+constexpr int kMeanGroups = 8;
+__global__ __launch_bounds__(kD * kMeanGroups) void k_nsn_mean(const float *__restrict__ part,
+                                                              float *__restrict__ o, int64_t T, int n_chunks)
 {
-    const int h = blockIdx.x, i = threadIdx.x;
+    __shared__ float red[kMeanGroups][kD];
+    const int h = blockIdx.x, i = threadIdx.x & (kD - 1), j = threadIdx.x >> 7;
+    const float *ph = part + (int64_t)h * n_chunks * kD + i;
     float s = 0.0f;
-    for (int c = 0; c < n_chunks; ++c) s += part[((int64_t)h * n_chunks + c) * kD + i];
-    o[h * kD + i] = s / (float)T;
+    int c = j;
+    for (; c + 7 * kMeanGroups < n_chunks; c += 8 * kMeanGroups) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = ph[(int64_t)(c + u * kMeanGroups) * kD];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) s += v[u];
+    }
+    for (; c < n_chunks; c += kMeanGroups) s += ph[(int64_t)c * kD];
+    red[j][i] = s;
+    __syncthreads();
+    if (j == 0) {
+        float t = 0.0f;
+#pragma unroll
+        for (int g = 0; g < kMeanGroups; ++g) t += red[g][i];
+        o[h * kD + i] = t / (float)T;
+    }
 }
 
 // v = hi + lo (hi returned) with hi exactly representable in fp16: hi keeps the 11 leading
@@ -317,7 +337,7 @@ hipError_t launch_nsn_vq(const kvq_ctx *ctx, const void *x, int64_t H, int64_t T
     float *part = (float *)ws;
     hipLaunchKernelGGL(k_nsn_stats, dim3((unsigned)(H * n_chunks)), dim3(256), 0, s, (const u4_t *)x, part, T,
                        n_chunks);
-    hipLaunchKernelGGL(k_nsn_mean, dim3((unsigned)H), dim3(kD), 0, s, part, o, T, n_chunks);
+    hipLaunchKernelGGL(k_nsn_mean, dim3((unsigned)H), dim3(kD * kMeanGroups), 0, s, part, o, T, n_chunks);
     VqArgs a{};
     a.x = (const u4_t *)x;
     a.o = o;

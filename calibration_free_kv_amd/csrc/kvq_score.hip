@@ -85,21 +85,36 @@ __device__ void rotate_queries(const half_t *__restrict__ q, const float *__rest
     __syncthreads();
 }
 
-// ctab: the 2^b centroids already in LDS.
+// ctab: the 2^b centroids already in LDS.  One thread per (field, value)
+// pair computes the G heads' entries together (the field's query values and
+// the pair's centroids are read once) and writes them contiguously.
 template <int BITS, int G>
 __device__ void build_tables(const float *qr, const float *ctab, float *lut)
 {
     using FD = Fields<BITS>;
     constexpr uint32_t mask = (1u << BITS) - 1u;
     const float inv_d = 1.0f / kD;
-    for (int idx = threadIdx.x; idx < FD::NF * FD::E * G; idx += blockDim.x) {
-        const int h = idx % G;
-        const int e = (idx / G) % FD::E;
-        const int f = idx / (G * FD::E);
-        float v = 0.0f;
+    for (int fe = threadIdx.x; fe < FD::NF * FD::E; fe += blockDim.x) {
+        const int e = fe % FD::E, f = fe / FD::E;
+        float c[FD::F];
 #pragma unroll
-        for (int k = 0; k < FD::F; ++k) v += qr[h * kD + FD::F * f + k] * ctab[(e >> (BITS * k)) & mask];
-        lut[idx] = v * inv_d;
+        for (int k = 0; k < FD::F; ++k) c[k] = ctab[(e >> (BITS * k)) & mask] * inv_d;
+        float v[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            v[h] = 0.0f;
+#pragma unroll
+            for (int k = 0; k < FD::F; ++k) v[h] = fmaf(qr[h * kD + FD::F * f + k], c[k], v[h]);
+        }
+        if constexpr (G % 4 == 0) {
+#pragma unroll
+            for (int h4 = 0; h4 < G / 4; ++h4)
+                reinterpret_cast<f4_t *>(lut)[fe * (G / 4) + h4] =
+                    f4_t{v[4 * h4], v[4 * h4 + 1], v[4 * h4 + 2], v[4 * h4 + 3]};
+        } else {
+#pragma unroll
+            for (int h = 0; h < G; ++h) lut[fe * G + h] = v[h];
+        }
     }
 }
 
