@@ -19,8 +19,17 @@ FLAGS = [
     "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,
     # keep the compiler from forming packed fp32 instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core accumulators in ordinary VGPRs: their results feed VALU code
+    # directly, without a v_accvgpr_read per value
+    "-mllvm", "--amdgpu-mfma-vgpr-form",
     "-Wno-unused-command-line-argument",
 ]
+
+
+# Per-file additions.  kvq_nsn.hip: its arg max runs over finite scores (sums
+# of finite products), and without NaN semantics a maximum of four is one
+# v_max3 and one v_max with no canonicalising moves in between.
+FILE_FLAGS = {"kvq_nsn.hip": ["-fno-honor-nans"]}
 
 
 def sources():
@@ -29,7 +38,7 @@ def sources():
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))

@@ -13,13 +13,9 @@
 // the per-token transform and the search.  The search is a contraction of
 // the 16 sub-vectors of 32 tokens with the codebook: score_j = <z_s, C_j> -
 // ||C_j||^2 / 2 (the nearest entry has the largest score), on the matrix
-// cores with v_mfma_f32_32x32x8_f16, codewords as rows and tokens as columns,
-// the bias preloaded in the accumulator.  Each lane then holds, for one
-// token, the scores of 16 codewords of every 32-codeword block and takes the
-// arg-max in registers; one exchange with the lane holding the other 16
-// codewords finishes it.  The scores must be exact to about 1e-6, so z is
-// split into fp16 hi + lo parts (two passes) and a third pass adds z_hi * C_lo
-// when the codebook is not exactly representable in fp16.
+// cores, codewords as rows and tokens as columns, the bias preloaded in the
+// accumulator (details at k_nsn_vq).  The scores must be exact to about 1e-6,
+// so z and the codebook are split into fp16 hi + lo parts.
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -31,6 +27,7 @@ typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u2_t __attribute__((ext_vector_type(2)));
 typedef float f16v_t __attribute__((ext_vector_type(16)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kTile = 64;
 constexpr int kChunk = 1024;  // tokens per stats block
@@ -164,13 +161,20 @@ __device__ __forceinline__ _Float16 split_f16(float v, _Float16 &lo)
     return (_Float16)h;
 }
 
+// max of four scores (v_max3 + v_max: this file is compiled without NaN
+// semantics, the scores being finite sums of finite products)
+__device__ __forceinline__ float max4(float a, float b, float c, float d)
+{
+    return fmaxf(fmaxf(fmaxf(a, b), c), d);
+}
+
 __device__ __forceinline__ int swz(int row, int chunk) { return row * 16 + (chunk ^ (row & 15)); }
 
 struct VqArgs {
     const u4_t *x;
-    const float *o;       // [H][128]
-    const u2_t *cb_hi;    // [256][8] fp16 as 4-byte pairs: entry j, k = 4 q .. 4 q + 3 at index 2 j + q
-    const u2_t *cb_lo;    // same, or nullptr when the codebook is exactly fp16
+    const u4_t *cb_hi;    // [256] entries of 8 fp16 (hi parts)
+    const u2_t *cb_lo;    // [256][2] lo parts, dims 4q .. 4q + 3 at index 2 j + q (unused if exactly fp16)
+    const float *cb;      // [256][8] fp32 codebook
     const float *bias;    // [256] -||C_j||^2 / 2
     u4_t *codes;          // [H][T][16 bytes]
     float *s1, *s2;       // [H][T]
@@ -178,44 +182,84 @@ struct VqArgs {
 
 // (3) per-token transform and nearest-entry search.  One wave per SIMD:
 // 16 KiB of LDS for the x tile (reused for the fp16 hi rows of z) and 16 KiB
-// for the lo rows.
+// for the lo rows; the block also stages the codebook (hi, lo, fp32, biases).
+//
+// Search, per block of 32 tokens (MFMA columns) and 32 codewords (rows):
+// one v_mfma_f32_32x32x16_f16 gives C_hi . (z_hi + z_lo) + bias (k = 0..7
+// pairs the hi parts of z with C_hi, k = 8..15 the lo parts with C_hi again),
+// and one v_mfma_f32_32x32x8_f16 adds C_lo . z_hi when the codebook is not
+// fp16-exact.  A lane then holds 16 scores of one token: four groups of four
+// consecutive codewords.  It keeps, per sub-vector, only the best group (its
+// maximum, strictly larger in increasing codeword order), and at the end
+// recomputes the group's four scores in fp32 from z = z_hi + z_lo and the
+// fp32 codebook to pick the entry; the lane holding the other 16 codewords of
+// each block does the same, and the better of the two (lower index on ties)
+// is the code.  Keeping groups instead of single entries takes the arg max
+// bookkeeping from 3 VALU operations per (sub-vector, codeword) to about 1.3.
+template <bool CB_LO>
+// o: channel means [H][128], a separate read-only argument so that (read
+// with a wave-uniform head) it comes through the scalar cache.
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_nsn_vq(
-    VqArgs a, int64_t T, int H, int64_t tiles_per_h, int64_t n_tiles)
+    VqArgs a, const float *__restrict__ o, int64_t T, int H, int64_t tiles_per_h, int64_t n_tiles)
 {
+    static_assert(kVqK == 256, "one codebook entry per thread when staging");
     __shared__ u4_t lds[4][kTile * 16];
     __shared__ u4_t zlo[4][kTile * 16];
-    const int lane = threadIdx.x & 63;
-    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    __shared__ u4_t s_cbh[kVqK];
+    __shared__ u2_t s_cbl[2 * kVqK];
+    __shared__ f4_t s_cb[2 * kVqK];
+    __shared__ float s_bias[kVqK];
+    const int tid = threadIdx.x;
+    s_cbh[tid] = a.cb_hi[tid];
+    if constexpr (CB_LO) {
+        s_cbl[2 * tid] = a.cb_lo[2 * tid];
+        s_cbl[2 * tid + 1] = a.cb_lo[2 * tid + 1];
+    }
+    s_cb[2 * tid] = reinterpret_cast<const f4_t *>(a.cb)[2 * tid];
+    s_cb[2 * tid + 1] = reinterpret_cast<const f4_t *>(a.cb)[2 * tid + 1];
+    s_bias[tid] = a.bias[tid];
+    __syncthreads();
+
+    const int lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     u4_t *L = lds[wv];
     u4_t *Llo = zlo[wv];
     const int half = lane >> 5, col = lane & 31;
 
-    // codebook operands (A: row = entry 32 mb + col, k = 4 half .. 4 half + 3)
-    u2_t Ahi[8], Alo[8];
-#pragma unroll
-    for (int mb = 0; mb < 8; ++mb) {
-        Ahi[mb] = a.cb_hi[2 * (32 * mb + col) + half];
-        Alo[mb] = a.cb_lo ? a.cb_lo[2 * (32 * mb + col) + half] : u2_t{0u, 0u};
-    }
-
+    // Each lane loads its own token's row straight into registers; the next
+    // tile's rows are requested before the current tile's search, which hides
+    // their latency (the LDS buffers then only hold the z rows).
     const int64_t stride = (int64_t)gridDim.x * 4;
-    for (int64_t tile = (int64_t)blockIdx.x * 4 + wv; tile < n_tiles; tile += stride) {
+    int64_t tile = (int64_t)blockIdx.x * 4 + wv;
+    u4_t xr[16];
+    auto load_rows = [&](int64_t t) {
+        const int64_t hq = t / tiles_per_h;
+        const int64_t tq = (t - hq * tiles_per_h) * kTile;
+        const int nq = (int)min((int64_t)kTile, T - tq);
+        const u4_t *src = a.x + (hq * T + tq + min(lane, nq - 1)) * 16;  // rows past a tail: last valid row
+#pragma unroll
+        for (int c = 0; c < 16; ++c) xr[c] = __builtin_nontemporal_load(src + c);
+    };
+    if (tile < n_tiles) load_rows(tile);
+    for (; tile < n_tiles; tile += stride) {
         const int64_t hh = tile / tiles_per_h;
         const int64_t t0 = (tile - hh * tiles_per_h) * kTile;
         const int nv = (int)min((int64_t)kTile, T - t0);
         const int h = (int)hh;
         const int64_t v0 = hh * T + t0;
-        tile_to_lds(a.x + v0 * 16, nv, L, lane);
-        wait_vm();
         uint32_t w[64];
-        read_row(L, lane, w);
-        wait_lgkm();
-        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+            w[4 * c + 0] = xr[c].x;
+            w[4 * c + 1] = xr[c].y;
+            w[4 * c + 2] = xr[c].z;
+            w[4 * c + 3] = xr[c].w;
+        }
 
         const float ss = norm2_f16(w);
         const float nx = __builtin_sqrtf(ss);
         const float inv = ss > 0.0f ? kSqrtD / nx : 0.0f;
-        const float *oh = a.o + h * kD;
+        const float *oh = o + __builtin_amdgcn_readfirstlane(h) * kD;
         float y[128];
         float nb2 = 0.0f;
         {
@@ -232,14 +276,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
         for (int k = 0; k < 128; ++k) nb2 = fmaf(y[k], y[k], nb2);
 #pragma unroll
-        for (int s = 1; s < 128; s <<= 1) {
+        for (int st = 1; st < 128; st <<= 1) {
 #pragma unroll
-            for (int i = 0; i < 128; i += 2 * s) {
+            for (int i = 0; i < 128; i += 2 * st) {
 #pragma unroll
-                for (int j = i; j < i + s; ++j) {
-                    const float p0 = y[j], p1 = y[j + s];
+                for (int j = i; j < i + st; ++j) {
+                    const float p0 = y[j], p1 = y[j + st];
                     y[j] = p0 + p1;
-                    y[j + s] = p0 - p1;
+                    y[j + st] = p0 - p1;
                 }
             }
         }
@@ -260,55 +304,101 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         }
         wait_lgkm();
         __builtin_amdgcn_wave_barrier();
+        if (tile + stride < n_tiles) load_rows(tile + stride);
 
         uint32_t code[4] = {0u, 0u, 0u, 0u};  // codes of token `lane` (sub-vector s in byte s)
 #pragma unroll 1
         for (int tb = 0; tb < 2; ++tb) {
             const int row = 32 * tb + col;  // token of this lane's column
-            float best[16];
-            int bidx[16];
+            const u4_t *Lz = half ? Llo : L;  // B of the x16 pass: z_hi (k < 8) or z_lo (k >= 8)
+            float bm[16];
+            int bg[16];
 #pragma unroll
             for (int s = 0; s < 16; ++s) {
-                best[s] = -INFINITY;
-                bidx[s] = 0;
+                bm[s] = -INFINITY;
+                bg[s] = 0;
             }
 #pragma unroll 1
             for (int mb = 0; mb < 8; ++mb) {
-                // accumulator rows of this lane: entry 32 mb + 8 (r/4) + 4 half + r%4
+                const int ent = 32 * mb + col;  // codeword row of this lane's A operand
+                const h8_t A16 = __builtin_bit_cast(h8_t, s_cbh[ent]);
+                h4_t A8 = {};
+                if constexpr (CB_LO) A8 = __builtin_bit_cast(h4_t, s_cbl[2 * ent + half]);
+                // accumulator rows of this lane: codeword 32 mb + 8 (r/4) + 4 half + r%4
                 f16v_t bias;
 #pragma unroll
                 for (int r4 = 0; r4 < 4; ++r4) {
-                    const float *bp = a.bias + 32 * mb + 8 * r4 + 4 * half;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) bias[4 * r4 + r] = bp[r];
+                    const f4_t bq = reinterpret_cast<const f4_t *>(s_bias)[(32 * mb + 8 * r4 + 4 * half) >> 2];
+                    bias[4 * r4] = bq.x;
+                    bias[4 * r4 + 1] = bq.y;
+                    bias[4 * r4 + 2] = bq.z;
+                    bias[4 * r4 + 3] = bq.w;
                 }
-                const h4_t Ah = __builtin_bit_cast(h4_t, Ahi[mb]);
-                const h4_t Al = __builtin_bit_cast(h4_t, Alo[mb]);
+                // four sub-vectors at a time in independent accumulators, so
+                // that the matrix cores run while earlier results are scanned
 #pragma unroll
-                for (int s = 0; s < 16; ++s) {
-                    // B: token `row`, k = 8 s + 4 half .. + 3 (fp16 hi / lo)
-                    const h4_t Bh = __builtin_bit_cast(h4_t, reinterpret_cast<const u2_t *>(L + swz(row, s))[half]);
-                    const h4_t Bl = __builtin_bit_cast(h4_t, reinterpret_cast<const u2_t *>(Llo + swz(row, s))[half]);
-                    f16v_t acc = __builtin_amdgcn_mfma_f32_32x32x8f16(Ah, Bh, bias, 0, 0, 0);
-                    acc = __builtin_amdgcn_mfma_f32_32x32x8f16(Ah, Bl, acc, 0, 0, 0);
-                    if (a.cb_lo) acc = __builtin_amdgcn_mfma_f32_32x32x8f16(Al, Bh, acc, 0, 0, 0);
-                    // entries of this lane in increasing order: strict > keeps the lowest index
+                for (int s4 = 0; s4 < 16; s4 += 4) {
+                    f16v_t acc[4];
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int j = 32 * mb + 8 * (r / 4) + 4 * half + (r % 4);
-                        const bool better = acc[r] > best[s];
-                        best[s] = better ? acc[r] : best[s];
-                        bidx[s] = better ? j : bidx[s];
+                    for (int u = 0; u < 4; ++u) {
+                        const h8_t B16 = __builtin_bit_cast(h8_t, Lz[swz(row, s4 + u)]);
+                        acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A16, B16, bias, 0, 0, 0);
+                    }
+                    if constexpr (CB_LO) {
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            const h4_t B8 =
+                                __builtin_bit_cast(h4_t, reinterpret_cast<const u2_t *>(L + swz(row, s4 + u))[half]);
+                            acc[u] = __builtin_amdgcn_mfma_f32_32x32x8f16(A8, B8, acc[u], 0, 0, 0);
+                        }
+                    }
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int s = s4 + u;
+#pragma unroll
+                        for (int r4 = 0; r4 < 4; ++r4) {
+                            const float m = max4(acc[u][4 * r4], acc[u][4 * r4 + 1], acc[u][4 * r4 + 2], acc[u][4 * r4 + 3]);
+                            const bool better = m > bm[s];
+                            bm[s] = better ? m : bm[s];
+                            bg[s] = better ? 4 * mb + r4 : bg[s];
+                        }
                     }
                 }
             }
+            // resolve the best group of each sub-vector in fp32, then merge with
+            // the lane holding the other half of every codeword block
 #pragma unroll
             for (int s = 0; s < 16; ++s) {
-                // merge with the lane holding the other 16 entries of each block
-                const float ob = __shfl_xor(best[s], 32);
-                const int oi = __shfl_xor(bidx[s], 32);
-                const int bi = (ob > best[s] || (ob == best[s] && oi < bidx[s])) ? oi : bidx[s];
-                if (half == tb) code[s >> 2] |= (uint32_t)bi << (8 * (s & 3));
+                const h8_t zh = __builtin_bit_cast(h8_t, L[swz(row, s)]);
+                const h8_t zl = __builtin_bit_cast(h8_t, Llo[swz(row, s)]);
+                float z[8];
+#pragma unroll
+                for (int t = 0; t < 8; ++t) z[t] = (float)zh[t] + (float)zl[t];
+                const int g = bg[s];
+                const int j0 = 32 * (g >> 2) + 8 * (g & 3) + 4 * half;
+                float best = -INFINITY;
+                int bi = j0;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int j = j0 + r;
+                    const f4_t c0 = s_cb[2 * j], c1 = s_cb[2 * j + 1];
+                    float sc = s_bias[j];
+                    sc = fmaf(z[0], c0.x, sc);
+                    sc = fmaf(z[1], c0.y, sc);
+                    sc = fmaf(z[2], c0.z, sc);
+                    sc = fmaf(z[3], c0.w, sc);
+                    sc = fmaf(z[4], c1.x, sc);
+                    sc = fmaf(z[5], c1.y, sc);
+                    sc = fmaf(z[6], c1.z, sc);
+                    sc = fmaf(z[7], c1.w, sc);
+                    const bool better = sc > best;  // increasing index: strict > keeps the lowest
+                    best = better ? sc : best;
+                    bi = better ? j : bi;
+                }
+                const float ob = __shfl_xor(best, 32);
+                const int oi = __shfl_xor(bi, 32);
+                const int win = (ob > best || (ob == best && oi < bi)) ? oi : bi;
+                if (half == tb) code[s >> 2] |= (uint32_t)win << (8 * (s & 3));
             }
         }
         if (lane < nv) {
@@ -340,9 +430,9 @@ hipError_t launch_nsn_vq(const kvq_ctx *ctx, const void *x, int64_t H, int64_t T
     hipLaunchKernelGGL(k_nsn_mean, dim3((unsigned)H), dim3(kD * kMeanGroups), 0, s, part, o, T, n_chunks);
     VqArgs a{};
     a.x = (const u4_t *)x;
-    a.o = o;
-    a.cb_hi = (const u2_t *)ctx->d_vq16;
-    a.cb_lo = ctx->vq_exact_f16 ? nullptr : (const u2_t *)(ctx->d_vq16 + kVqK * kVqSub);
+    a.cb_hi = (const u4_t *)ctx->d_vq16;
+    a.cb_lo = (const u2_t *)(ctx->d_vq16 + kVqK * kVqSub);
+    a.cb = ctx->d_vq;
     a.bias = ctx->d_vqbias;
     a.codes = (u4_t *)codes;
     a.s1 = s1;
@@ -351,7 +441,12 @@ hipError_t launch_nsn_vq(const kvq_ctx *ctx, const void *x, int64_t H, int64_t T
     const int64_t n_tiles = tiles_per_h * H;
     int64_t blocks = (n_tiles + 3) / 4;
     if (blocks > ctx->n_cu) blocks = ctx->n_cu;
-    hipLaunchKernelGGL(k_nsn_vq, dim3((unsigned)blocks), dim3(256), 0, s, a, T, (int)H, tiles_per_h, n_tiles);
+    if (ctx->vq_exact_f16)
+        hipLaunchKernelGGL(k_nsn_vq<false>, dim3((unsigned)blocks), dim3(256), 0, s, a, (const float *)o, T, (int)H,
+                           tiles_per_h, n_tiles);
+    else
+        hipLaunchKernelGGL(k_nsn_vq<true>, dim3((unsigned)blocks), dim3(256), 0, s, a, (const float *)o, T, (int)H,
+                           tiles_per_h, n_tiles);
     return hipGetLastError();
 }
 
