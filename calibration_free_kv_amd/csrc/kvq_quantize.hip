@@ -361,7 +361,6 @@ struct QjlArgs {
     float *norms;
     u4_t *signs;        // [n][16 bytes]
     float *gamma;       // [n]
-    const uint32_t *sgnmask;
     const u4_t *S_hi;   // [128][128] fp16, row-major (row j = output j)
     const u4_t *S_lo;   // same, or nullptr when S is exactly fp16
     float mags[8];      // positive centroids c_{L/2}, ..., c_{L-1}
@@ -434,30 +433,41 @@ struct StaticFor {
 
 template <int BITS>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_quantize_qjl(
-    QjlArgs a, HalfThresholds ht, int64_t T, int H, int64_t tiles_per_bh, int64_t n_tiles)
+    QjlArgs a, const uint32_t *__restrict__ sgn, HalfThresholds ht, int64_t T, int H, int64_t tiles_per_bh,
+    int64_t n_tiles)
 {
-    __shared__ u4_t lds[kWaves][kTile * 16];     // tile of x, then fp16 hi rows of e
-    __shared__ u4_t Elo[kWaves][kTile * 16];     // fp16 lo rows of e
+    __shared__ u4_t Ehi[kWaves][kTile * 16];  // fp16 hi rows of e (16-byte chunks swizzled)
+    __shared__ u4_t Elo[kWaves][kTile * 16];  // fp16 lo rows of e
+    __shared__ u4_t Ss[kD * 16];              // S_hi, row j chunk c at slot j*16 + (c ^ (j & 15))
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    u4_t *L = lds[wv];
+    for (int i = threadIdx.x; i < kD * 16; i += kWaves * 64) Ss[swz(i >> 4, i & 15)] = a.S_hi[i];
+    __syncthreads();
+    u4_t *Lhi = Ehi[wv], *Llo = Elo[wv];
     const int64_t stride = (int64_t)gridDim.x * kWaves;
-    for (int64_t tile = (int64_t)blockIdx.x * kWaves + wv; tile < n_tiles; tile += stride) {
+    int64_t tile = (int64_t)blockIdx.x * kWaves + wv;
+    // Each lane loads its key's row straight into registers; the next tile's
+    // rows are requested before the current tile's projection.
+    u4_t xr[16];
+    auto load_rows = [&](int64_t t) {
+        const TileGeom gq = geom(t, T, H, tiles_per_bh);
+        const u4_t *src = a.x + (gq.v0 + min(lane, gq.nv - 1)) * 16;  // rows past a tail: last valid row
+#pragma unroll
+        for (int c = 0; c < 16; ++c) xr[c] = __builtin_nontemporal_load(src + c);
+    };
+    if (tile < n_tiles) load_rows(tile);
+    for (; tile < n_tiles; tile += stride) {
         const TileGeom g = geom(tile, T, H, tiles_per_bh);
-        tile_to_lds(a.x + g.v0 * 16, g.nv, L, lane);
-        wait_vm();
         uint32_t w[64];
 #pragma unroll
         for (int c = 0; c < 16; ++c) {
-            const u4_t v = L[lane * 16 + ((c + lane) & 15)];
-            w[4 * c + 0] = v.x;
-            w[4 * c + 1] = v.y;
-            w[4 * c + 2] = v.z;
-            w[4 * c + 3] = v.w;
+            w[4 * c + 0] = xr[c].x;
+            w[4 * c + 1] = xr[c].y;
+            w[4 * c + 2] = xr[c].z;
+            w[4 * c + 3] = xr[c].w;
         }
-        wait_lgkm();
         const bool active = lane < g.nv;
-        const uint32_t *sg = a.sgnmask + g.h * 64;
+        const uint32_t *sg = sgn + __builtin_amdgcn_readfirstlane(g.h * 64);
         float ss = 0.0f;
 #pragma unroll
         for (int k = 0; k < 64; ++k) {
@@ -514,7 +524,6 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 
         }
 
         // Stage e of all 64 keys as fp16 hi / lo rows (16-byte chunks swizzled).
-        u4_t *Lhi = L, *Llo = Elo[wv];  // the x tile has been read into registers
 #pragma unroll
         for (int c = 0; c < 16; ++c) {
             h8_t hv, lv;
@@ -529,38 +538,45 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 
         }
         wait_lgkm();
         __builtin_amdgcn_wave_barrier();
+        if (tile + stride < n_tiles) load_rows(tile + stride);
 
-        uint32_t sgn[4] = {0u, 0u, 0u, 0u};
+        // Projection of 16 keys at a time against all 128 rows of S: eight
+        // independent 16 x 16 accumulators (output blocks nb) per key block.
+        uint32_t sgnw[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int np = 0; np < 4; ++np) {  // pairs of 16-output blocks -> one sign dword per key
+        for (int mb = 0; mb < 4; ++mb) {
+            f4_t z[8];
 #pragma unroll
-            for (int mb = 0; mb < 4; ++mb) {
-                f4_t z[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+            for (int nb = 0; nb < 8; ++nb) z[nb] = f4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kb = 0; kb < 4; ++kb) {
-                    const int row = 16 * mb + (lane & 15), chunk = 4 * kb + (lane >> 4);
-                    const h8_t Ah = __builtin_bit_cast(h8_t, Lhi[swz(row, chunk)]);
-                    const h8_t Al = __builtin_bit_cast(h8_t, Llo[swz(row, chunk)]);
+            for (int kb = 0; kb < 4; ++kb) {
+                const int row = 16 * mb + (lane & 15), chunk = 4 * kb + (lane >> 4);
+                const h8_t Ah = __builtin_bit_cast(h8_t, Lhi[swz(row, chunk)]);
+                const h8_t Al = __builtin_bit_cast(h8_t, Llo[swz(row, chunk)]);
 #pragma unroll
-                    for (int t2 = 0; t2 < 2; ++t2) {
-                        const int srow = 16 * (2 * np + t2) + (lane & 15);
-                        const h8_t Bh = __builtin_bit_cast(h8_t, a.S_hi[srow * 16 + chunk]);
-                        z[t2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, Bh, z[t2], 0, 0, 0);
-                        z[t2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Al, Bh, z[t2], 0, 0, 0);
-                        if (a.S_lo) {
-                            const h8_t Bl = __builtin_bit_cast(h8_t, a.S_lo[srow * 16 + chunk]);
-                            z[t2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, Bl, z[t2], 0, 0, 0);
-                        }
+                for (int nb = 0; nb < 8; ++nb) {
+                    const int srow = 16 * nb + (lane & 15);
+                    const h8_t Bh = __builtin_bit_cast(h8_t, Ss[swz(srow, chunk)]);
+                    z[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, Bh, z[nb], 0, 0, 0);
+                    z[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Al, Bh, z[nb], 0, 0, 0);
+                    if (a.S_lo) {
+                        const h8_t Bl = __builtin_bit_cast(h8_t, a.S_lo[srow * 16 + chunk]);
+                        z[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, Bl, z[nb], 0, 0, 0);
                     }
                 }
+            }
+            // Output block nb, row 4 q + rr of the 16 x 16 result (lane: q = lane/16, column
+            // lane%16 = output j - 16 nb): ballot bit 16 q + c is the sign of output
+            // 16 nb + c of key 16 mb + 4 q + rr.  Dword np of a key holds outputs
+            // 32 np .. 32 np + 31: blocks 2 np (low half) and 2 np + 1 (high half).
+#pragma unroll
+            for (int np = 0; np < 4; ++np) {
                 uint64_t m[2][4];
 #pragma unroll
                 for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
-                    for (int rr = 0; rr < 4; ++rr) m[t2][rr] = __builtin_amdgcn_ballot_w64(z[t2][rr] >= 0.0f);
-                // key 16 mb + 4 q + rr: bits 16 q .. 16 q + 15 of m[t2][rr] are its sign bits
-                // 16 nb .. 16 nb + 15 (nb = 2 np + t2); both halves form its dword np.
-                uint32_t acc_np = sgn[np];
+                    for (int rr = 0; rr < 4; ++rr) m[t2][rr] = __builtin_amdgcn_ballot_w64(z[2 * np + t2][rr] >= 0.0f);
+                uint32_t acc_np = sgnw[np];
                 StaticFor<0, 16>::run([&](auto kk) {
                     constexpr int k = decltype(kk)::value;
                     constexpr int q = k / 4, rr = k % 4;
@@ -572,22 +588,23 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 
                     if (mb == 2) acc_np = write_lane<32 + k>(acc_np, val);
                     if (mb == 3) acc_np = write_lane<48 + k>(acc_np, val);
                 });
-                sgn[np] = acc_np;
+                sgnw[np] = acc_np;
             }
         }
         __builtin_amdgcn_wave_barrier();
-        if (!active) continue;
-        const int64_t v = g.v0 + lane;
-        u4_t *dst = a.codes + v * BITS;
+        if (active) {
+            const int64_t v = g.v0 + lane;
+            u4_t *dst = a.codes + v * BITS;
 #pragma unroll
-        for (int q = 0; q < BITS; ++q) {
-            u4_t o = {out[4 * q], out[4 * q + 1], out[4 * q + 2], out[4 * q + 3]};
-            dst[q] = o;
+            for (int q = 0; q < BITS; ++q) {
+                u4_t o = {out[4 * q], out[4 * q + 1], out[4 * q + 2], out[4 * q + 3]};
+                dst[q] = o;
+            }
+            a.norms[v] = rho;
+            u4_t so = {sgnw[0], sgnw[1], sgnw[2], sgnw[3]};
+            a.signs[v] = so;
+            a.gamma[v] = __builtin_sqrtf(g2) * 0.08838834764831845f;  // ||e|| / sqrt(d)
         }
-        a.norms[v] = rho;
-        u4_t so = {sgn[0], sgn[1], sgn[2], sgn[3]};
-        a.signs[v] = so;
-        a.gamma[v] = __builtin_sqrtf(g2) * 0.08838834764831845f;  // ||e|| / sqrt(d)
     }
 }
 
@@ -604,7 +621,6 @@ hipError_t run_qjl(const kvq_ctx *ctx, const void *x, int64_t B, int64_t T, uint
     a.norms = norms;
     a.signs = (u4_t *)signs;
     a.gamma = gamma;
-    a.sgnmask = ctx->d_sgnmask;
     a.S_hi = (const u4_t *)ctx->d_S16;
     a.S_lo = ctx->S_exact_f16 ? nullptr : (const u4_t *)(ctx->d_S16 + kD * kD);
     for (int k = 0; k < L / 2; ++k) a.mags[k] = ctx->cb.c[L / 2 + k];
@@ -612,8 +628,8 @@ hipError_t run_qjl(const kvq_ctx *ctx, const void *x, int64_t B, int64_t T, uint
     const int64_t n_tiles = tiles_per_bh * B * ctx->H;
     int64_t blocks = (n_tiles + kWaves - 1) / kWaves;
     if (blocks > (int64_t)ctx->n_cu) blocks = ctx->n_cu;  // one wave per SIMD (512 registers each)
-    hipLaunchKernelGGL(k_quantize_qjl<BITS>, dim3((unsigned)blocks), dim3(kWaves * 64), 0, s, a, ht, T, ctx->H,
-                       tiles_per_bh, n_tiles);
+    hipLaunchKernelGGL(k_quantize_qjl<BITS>, dim3((unsigned)blocks), dim3(kWaves * 64), 0, s, a,
+                       (const uint32_t *)ctx->d_sgnmask, ht, T, ctx->H, tiles_per_bh, n_tiles);
     return hipGetLastError();
 }
 
