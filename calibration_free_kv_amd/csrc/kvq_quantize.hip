@@ -3,17 +3,19 @@
 // ("PolarQuant", Technical summary sec. 2; "TurboQuant", Como Funciona,
 // Estagio 1).
 //
-// Mapping on gfx950: one wave quantises a tile of 64 consecutive vectors of
-// one (batch, KV head), one vector per lane.  The tile (16 KiB of fp16) is
-// read with fully coalesced 16-byte loads (each load instruction covers 1 KiB
-// of contiguous memory), staged through a padded LDS tile and read back one
-// row per lane.  Each lane then holds its whole vector in VGPRs, so the 7
-// butterfly stages of the transform (896 add/sub) need no cross-lane traffic.
-// The random signs D of the head are wave-uniform and applied as an XOR on
-// the fp16 sign bits; the norm is a chain of packed fp16 dot products with
-// fp32 accumulation.  Instead of dividing the 128 coordinates by the norm,
-// the rotated coordinates of x itself are compared with the thresholds
-// scaled by ||x|| (same decisions up to fp32 rounding, 128 fewer multiplies).
+// Mapping on gfx950: a wave quantises a tile of 32 consecutive vectors of one
+// (batch, KV head) with two lanes per vector: lane 2v + h holds coordinates
+// [64 h, 64 h + 64) of vector v, so a wave needs about 100 VGPRs and four
+// waves share each SIMD.  The tile (8 KiB of fp16) is copied from HBM straight
+// into LDS (each copy instruction reads one contiguous KiB) and read back as
+// half rows.  Six of the seven butterfly stages of the transform run inside
+// the lane; the stage that pairs coordinate i with i + 64 is one DPP lane swap
+// fused into an FMA.  The random signs D of the head travel with the tile and
+// are applied as an XOR on the fp16 sign bits; the norm is a chain of packed
+// fp16 dot products with fp32 accumulation, completed across the lane pair.
+// Instead of dividing the coordinates by the norm, the rotated coordinates of
+// x itself are compared with the thresholds scaled by ||x|| (same decisions up
+// to fp32 rounding, no per-coordinate multiply).
 #include "kvq_internal.h"
 
 #include <type_traits>
@@ -24,7 +26,8 @@ namespace {
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kTile = 64;     // vectors per wave
+constexpr int kTile = 64;     // vectors per wave tile, one per lane (QJL kernel)
+constexpr int kTileH = 32;    // vectors per wave tile, two lanes each (MSE kernel)
 constexpr int kWaves = 4;     // waves per block
 
 struct HalfThresholds {
@@ -108,49 +111,6 @@ __device__ __forceinline__ void index_bits(float y, const float *P, uint64_t *M)
     }
 }
 
-// Direct global -> LDS copy of one tile (no VGPR staging).  Load instruction j
-// writes LDS bytes [1024 j, 1024 j + 1024) of the wave's buffer, lane l at
-// offset 16 l, i.e. vector v = 4 j + l/16, slot s = l % 16.  The lane fetches
-// 16-byte chunk c = (s - v) mod 16 of that vector, so chunk c of vector v ends
-// up in slot (c + v) mod 16: a skewed layout in which the later per-lane row
-// reads (lane v, chunk c) fall into distinct LDS banks.  Each instruction
-// still reads one contiguous KiB of HBM.
-// The chunk a lane fetches depends on j only through j mod 4, so the address
-// is a wave-uniform base (src + 256 (j/4), in 16-byte units) plus one of four
-// per-lane offsets: 4 VGPRs instead of 16 64-bit addresses held across the
-// persistent loop.  Every call issues exactly 16 load instructions with all
-// lanes active (waits count them); rows past a ragged tail re-read the last
-// valid row, and are never stored.
-__device__ __forceinline__ void tile_to_lds(const u4_t *src, int nv, u4_t *L, int lane)
-{
-    // lane is made opaque so that the offsets are recomputed here (a few
-    // VALU ops) rather than hoisted out of the persistent loop and spilled
-    asm volatile("" : "+v"(lane));
-    if (nv == kTile) {
-        uint32_t off[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int v = 4 * r + (lane >> 4);
-            off[r] = (uint32_t)(v * 16 + (((lane & 15) - v) & 15));
-        }
-#pragma unroll
-        for (int j = 0; j < 16; ++j)
-            __builtin_amdgcn_global_load_lds(
-                (const __attribute__((address_space(1))) void *)(src + 256 * (j >> 2) + off[j & 3]),
-                (__attribute__((address_space(3))) void *)(L + j * 64), 16, 0, 0);
-    } else {
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int v = 4 * j + (lane >> 4);
-            const int c = ((lane & 15) - v) & 15;
-            const int row = v < nv ? v : nv - 1;
-            __builtin_amdgcn_global_load_lds(
-                (const __attribute__((address_space(1))) void *)(src + row * 16 + c),
-                (__attribute__((address_space(3))) void *)(L + j * 64), 16, 0, 0);
-        }
-    }
-}
-
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
 // vmcnt(N): all but the N most recently issued vector memory operations have
 // completed (they complete in issue order); lgkmcnt and expcnt not waited on.
@@ -162,53 +122,161 @@ __device__ __forceinline__ void wait_vm_n()
 }
 __device__ __forceinline__ void wait_lgkm() { __builtin_amdgcn_s_waitcnt(0xC07F); } // lgkmcnt(0)
 
-// Wait for the wave's tile copy and read row `lane` (its vector) into w.
-template <int N>
-__device__ __forceinline__ void take_rows(const u4_t *L, int lane, uint32_t *w)
-{
-    // the row reads stay after the preceding arithmetic: moved up into it
-    // they would hold 64 more VGPRs live through the transform
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("" : "+v"(lane));  // addresses recomputed per tile, not hoisted and spilled
-    wait_vm_n<N>();
-#pragma unroll
-    for (int c = 0; c < 16; ++c) {
-        const u4_t v = L[lane * 16 + ((c + lane) & 15)];
-        w[4 * c + 0] = v.x;
-        w[4 * c + 1] = v.y;
-        w[4 * c + 2] = v.z;
-        w[4 * c + 3] = v.w;
-    }
-    wait_lgkm();
-    __builtin_amdgcn_wave_barrier();
-}
-
 struct TileGeom {
     int64_t v0;  // first vector of the tile
     int nv;      // vectors in the tile (ragged at the end of a head)
     int h;       // KV head
 };
 
+template <int TILE = kTile>
 __device__ __forceinline__ TileGeom geom(int64_t tile, int64_t T, int H, int64_t tiles_per_bh)
 {
     TileGeom g;
+    // opaque divisors: the compiler would otherwise hoist their float
+    // conversions (for the division) out of the persistent loop and spill them,
+    // and every reload would wait for all outstanding memory operations
+    asm volatile("" : "+s"(tiles_per_bh), "+s"(H));
     const int64_t bh = tile / tiles_per_bh;
-    const int64_t t0 = (tile - bh * tiles_per_bh) * kTile;
+    const int64_t t0 = (tile - bh * tiles_per_bh) * TILE;
     g.v0 = bh * T + t0;
-    g.nv = (int)min((int64_t)kTile, T - t0);
+    g.nv = (int)min((int64_t)TILE, T - t0);
     g.h = (int)(bh % H);
     return g;
 }
 
-// Persistent waves, two per SIMD: wave w processes tiles w, w + W, w + 2W, ...
-// (W = waves in the grid).  The next tile's copy into the wave's LDS buffer
-// is issued before this tile is encoded; after encoding, the wave waits for
-// it (vmcnt(0): it had the whole encode to complete), reads it into
-// registers, issues the copy of the tile after it and only then stores this
-// tile's codes, so that no wait sits right behind the wave's own stores (vmcnt
-// counts stores too).  One launch may cover two tensors of the same shape (K
-// and V): tiles [0, n_tiles) belong to tensor 0 and [n_tiles, 2 n_tiles) to
-// tensor 1.
+// LDS image of one wave tile: 32 rows of 16 chunks (16 bytes = 8 coordinates
+// each), then the 64 sign-mask dwords of the tile's head.  Half h of row v
+// (chunks 8h .. 8h+7) sits in slots [16 v + 8 h, 16 v + 8 h + 8), chunk
+// 8h + k at slot 16 v + 8 h + (k ^ m) with m = (v mod 8) ^ 4h.  At each of its
+// eight reads, lane 2v + h asks for slot k ^ m of its half row; over any 8 (or
+// 16) consecutive lanes these fall into distinct 16-byte bank groups, so the
+// half-row reads are free of bank conflicts.
+constexpr int kRowsH = kTileH * 16;   // 16-byte chunks of rows per tile
+constexpr int kBufH = kRowsH + 16;    // + 256 bytes of sign masks
+
+// Direct global -> LDS copy of one tile and its head's sign masks (no VGPR
+// staging).  Row-copy instruction j writes slots [64 j, 64 j + 64) of the
+// buffer, lane l at slot 64 j + l: vector v = 4 j + l/16, slot q = l % 16 of
+// its row, i.e. half h = q/8 and chunk 8h + ((q mod 8) ^ m).  Each such
+// instruction reads one contiguous KiB (four whole rows).  The chunk depends
+// on j only through j mod 2, so the address is a wave-uniform base plus one
+// of two per-lane offsets.  A ninth instruction copies the 64 mask dwords.
+// Every call issues exactly 9 load instructions with all lanes active (waits
+// count them); rows past a ragged tail re-read the last valid row, and are
+// never stored.
+__device__ __forceinline__ int half_chunk(int v, int q)
+{
+    const int h = q >> 3;
+    return 8 * h + ((q & 7) ^ ((v & 7) ^ (4 * h)));
+}
+
+__device__ __forceinline__ void tile_to_lds(const u4_t *src, int nv, const uint32_t *msk, u4_t *L, int lane)
+{
+    // lane is made opaque so that the offsets are recomputed here (a few
+    // VALU ops) rather than hoisted out of the persistent loop and spilled
+    asm volatile("" : "+v"(lane));
+    if (nv == kTileH) {
+        uint32_t off[2];
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const int v = 4 * p + (lane >> 4);
+            off[p] = (uint32_t)((lane >> 4) * 16 + half_chunk(v, lane & 15));
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void *)(src + 64 * j + off[j & 1]),
+                (__attribute__((address_space(3))) void *)(L + j * 64), 16, 0, 0);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int v = 4 * j + (lane >> 4);
+            const int row = v < nv ? v : nv - 1;
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void *)(src + row * 16 + half_chunk(v, lane & 15)),
+                (__attribute__((address_space(3))) void *)(L + j * 64), 16, 0, 0);
+        }
+    }
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(msk + lane),
+                                     (__attribute__((address_space(3))) void *)(L + kRowsH), 4, 0, 0);
+}
+
+// Wait for the wave's tile copy, read half row h of vector v into w (lane
+// 2v + h) and apply the signs of D.  Also draws the wave's next ticket from
+// the workgroup's LDS counter: the atomic goes out with the row reads, after
+// the copy has landed (the compiler makes any LDS access wait for all copies
+// into LDS that are still in flight).
+template <int N>
+__device__ __forceinline__ int take_rows(const u4_t *L, int lane, uint32_t *w, int *counter)
+{
+    // the row reads stay after the preceding arithmetic: moved up into it
+    // they would hold 32 more VGPRs live through the transform
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" : "+v"(lane));  // addresses recomputed per tile, not hoisted and spilled
+    wait_vm_n<N>();
+    const int v = lane >> 1, h = lane & 1;
+    const int b = 16 * v + 8 * h + ((v & 7) ^ (4 * h));  // slot of chunk k: b ^ k
+    const u4_t *M = L + kRowsH + 8 * h;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const u4_t x = L[b ^ k];
+        const u4_t m = M[k];
+        w[4 * k + 0] = x.x ^ m.x;
+        w[4 * k + 1] = x.y ^ m.y;
+        w[4 * k + 2] = x.z ^ m.z;
+        w[4 * k + 3] = x.w ^ m.w;
+    }
+    int t = 0;
+    if (lane == 0) t = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    wait_lgkm();
+    __builtin_amdgcn_wave_barrier();
+    return __builtin_amdgcn_readfirstlane(t);
+}
+
+// The value of x in the other lane of the pair (lanes 2v, 2v + 1).
+__device__ __forceinline__ float pair_swap(float x)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+}
+
+// y[i] += c * (y[i] of the other lane of the pair), i = 0..7, as one
+// v_fmac_f32 with a DPP source each (the compiler keeps the lane swap as a
+// separate move).  Every read of y[i] in the block happens before any lane
+// writes it, and each instruction reads a register no earlier instruction of
+// the block wrote; the leading s_nop 4 provides the wait states a DPP source
+// needs after a VALU write of that register (2) or a write of EXEC (5) by the
+// code before the block.
+__device__ __forceinline__ void pair_fmac8(float *y, float c)
+{
+    asm volatile(
+        "s_nop 4\n\t"
+        "v_fmac_f32_dpp %0, %0, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %1, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %2, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %3, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %4, %4, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %5, %5, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %6, %6, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %7, %7, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf"
+        : "+v"(y[0]), "+v"(y[1]), "+v"(y[2]), "+v"(y[3]), "+v"(y[4]), "+v"(y[5]), "+v"(y[6]), "+v"(y[7])
+        : "v"(c));
+}
+
+// One workgroup of 16 waves per CU (four per SIMD) owns every G-th tile (G =
+// workgroups in the grid).  Each wave starts on one of them; after that the
+// waves take the remaining ones in order from a counter in LDS, so a wave whose first
+// copy arrives late (every wave requests one at the same moment, and the last
+// ones arrive several microseconds after the first) simply processes fewer
+// tiles.  The next tile's copy into the wave's LDS buffer is issued before
+// this tile is encoded; after encoding, the wave waits for it (vmcnt(0): it
+// had the whole encode to complete), reads it into registers, issues the copy
+// of the tile after it and only then stores this tile's codes, so that no
+// wait sits right behind the wave's own stores (vmcnt counts stores too).  The
+// ticket for the tile after next is drawn along with the row reads.  One launch may
+// cover two tensors of the same shape (K and V): tiles [0, n_tiles) belong to
+// tensor 0 and [n_tiles, 2 n_tiles) to tensor 1.
+constexpr int kWavesQ = 16;  // waves per workgroup of the MSE kernel
+
 struct QArgs {
     const u4_t *x[2];
     u4_t *codes[2];
@@ -216,64 +284,76 @@ struct QArgs {
     int kind[2];  // K (0) or V (1): selects the random signs of each tensor
 };
 
-// sgn: sign masks [2][H][64] of D_K and D_V; a separate read-only, non-aliased
-// argument so that (with a wave-uniform index) the masks are scalar loads.
+// sgnh: sign masks [2][H][64] of D_K and D_V as fp16-pair XOR masks, with the
+// masks of coordinates 64..127 also flipping every sign: the upper lane of a
+// pair transforms -x[64..127], which lets one FMA form both outputs of the
+// cross-lane butterfly stage (lower lane: a - (-b), upper lane: -b + a).
 template <int BITS>
-__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_quantize(
-    QArgs a, const uint32_t *__restrict__ sgn, HalfThresholds ht, int64_t T, int H, int64_t tiles_per_bh,
+__global__ __launch_bounds__(kWavesQ * 64) __attribute__((amdgpu_waves_per_eu(4, 4))) void k_quantize(
+    QArgs a, const uint32_t *__restrict__ sgnh, HalfThresholds ht, int64_t T, int H, int64_t tiles_per_bh,
     int64_t n_tiles, int n_tensors)
 {
-    __shared__ u4_t lds[kWaves][kTile * 16];  // 64 KiB
+    __shared__ u4_t lds[kWavesQ][kBufH];  // 132 KiB
+    __shared__ int next_tile;             // next unclaimed tile of the range, relative to its start
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
     u4_t *L = lds[wv];
     const int64_t total = n_tiles * n_tensors;
-    const int64_t stride = (int64_t)gridDim.x * kWaves;
-    int64_t tile = (int64_t)blockIdx.x * kWaves + wv;
+    // ticket k of this workgroup is tile blockIdx.x + k * gridDim.x: at any
+    // moment the workgroups read one window of consecutive tiles
+    const int64_t G = gridDim.x;
+    if (threadIdx.x == 0) next_tile = kWavesQ;
+    __syncthreads();
+    int64_t tile = blockIdx.x + wv * G;
     if (tile >= total) return;  // wave-uniform
     auto issue = [&](int64_t t) {
         const int k = t >= n_tiles;
-        const TileGeom gg = geom(t - k * n_tiles, T, H, tiles_per_bh);
-        tile_to_lds(a.x[k] + gg.v0 * 16, gg.nv, L, lane);
+        const TileGeom gg = geom<kTileH>(t - k * n_tiles, T, H, tiles_per_bh);
+        tile_to_lds(a.x[k] + gg.v0 * 16, gg.nv, sgnh + (a.kind[k] * H + gg.h) * 64, L, lane);
     };
-    uint32_t w[64];
+    // cross-lane stage: lower lane a - (-b) = a + b, upper lane -b + a = a - b
+    const float cross = (lane & 1) ? 1.0f : -1.0f;
+    uint32_t w[32];
     issue(tile);
-    take_rows<0>(L, lane, w);
-    if (tile + stride < total) issue(tile + stride);
+    int64_t next = blockIdx.x + take_rows<0>(L, lane, w, &next_tile) * G;
+    if (next < total) issue(next);
     for (;;) {
         const int kt = tile >= n_tiles;
-        const TileGeom g = geom(tile - kt * n_tiles, T, H, tiles_per_bh);
+        const TileGeom g = geom<kTileH>(tile - kt * n_tiles, T, H, tiles_per_bh);
 
-        // wave-uniform head: the masks come through the scalar cache (lgkmcnt),
-        // so waiting for them does not wait for the next tile's copy (vmcnt)
-        const uint32_t *sg = sgn + __builtin_amdgcn_readfirstlane((a.kind[kt] * H + g.h) * 64);
-        // ||x||^2 with fp16 products (exact in fp32) accumulated in fp32, and D.
+        // ||x||^2 of the half row with fp16 products (exact in fp32)
+        // accumulated in fp32; D is already applied (signs do not change it).
         float ss = 0.0f;
 #pragma unroll
-        for (int k = 0; k < 64; ++k) {
+        for (int k = 0; k < 32; ++k) {
             const h2_t p = __builtin_bit_cast(h2_t, w[k]);
             ss = __builtin_amdgcn_fdot2(p, p, ss, false);
-            w[k] ^= sg[k];
         }
-        // First butterfly stage fused with the fp16 -> fp32 widening.
-        float y[128];
+        // First butterfly stage fused with the fp16 -> fp32 widening, then the
+        // other in-lane stages (strides 2 .. 32).
+        float y[64];
 #pragma unroll
-        for (int k = 0; k < 64; ++k) {
+        for (int k = 0; k < 32; ++k) {
             y[2 * k] = pair_sum(w[k]);
             y[2 * k + 1] = pair_diff(w[k]);
         }
 #pragma unroll
-        for (int s = 2; s < 128; s <<= 1) {
+        for (int s = 2; s < 64; s <<= 1) {
 #pragma unroll
-            for (int i = 0; i < 128; i += 2 * s) {
+            for (int i = 0; i < 64; i += 2 * s) {
 #pragma unroll
                 for (int j = i; j < i + s; ++j) {
-                    const float a = y[j], b = y[j + s];
-                    y[j] = a + b;
-                    y[j + s] = a - b;
+                    const float p = y[j], q = y[j + s];
+                    y[j] = p + q;
+                    y[j + s] = p - q;
                 }
             }
         }
+        // Stride-64 stage across the lane pair.
+#pragma unroll
+        for (int i = 0; i < 64; i += 8) pair_fmac8(y + i, cross);
+        // Both lanes form the same sum (fp32 addition commutes).
+        ss += pair_swap(ss);
 
         const float rho = __builtin_sqrtf(ss);
         const float r = rho > 0.0f ? rho : 1.0f;  // zero vector: y = 0 -> index L/2 - 1
@@ -281,13 +361,14 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
         for (int k = 0; k < 8; ++k) P[k] = ht.p[k] * r;
 
-        // Emit the LSB-first stream from its last bit backwards: bit p = BITS*i + k
-        // goes to dword p/32, which is filled most-significant bit first.
-        uint32_t out[4 * BITS];
+        // Emit this lane's 64 BITS-bit indices (bits [64 BITS h, 64 BITS (h+1))
+        // of the vector's LSB-first stream) from the last bit backwards: local
+        // bit p = BITS*i + k goes to dword p/32, filled most-significant first.
+        uint32_t out[2 * BITS];
 #pragma unroll
-        for (int k = 0; k < 4 * BITS; ++k) out[k] = 0u;
+        for (int k = 0; k < 2 * BITS; ++k) out[k] = 0u;
 #pragma unroll
-        for (int i = 127; i >= 0; --i) {
+        for (int i = 63; i >= 0; --i) {
             uint64_t M[BITS];
             index_bits<BITS>(y[i], P, M);
             const int lo = (BITS * i) >> 5, hi = (BITS * i + BITS - 1) >> 5;
@@ -311,24 +392,22 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
 
         // The next tile's rows, then the copy of the tile after it, then this
         // tile's stores: the only wait comes right after the encode.
-        const int64_t next = tile + stride;
         const bool has_next = next < total;
+        int64_t after = total;
         if (has_next) {
-            take_rows<0>(L, lane, w);
-            if (next + stride < total) issue(next + stride);
+            after = blockIdx.x + take_rows<0>(L, lane, w, &next_tile) * G;
+            if (after < total) issue(after);
         }
-        if (lane < g.nv) {  // lanes past a ragged tail encoded stale rows
-            const int64_t v = g.v0 + lane;
-            u4_t *dst = a.codes[kt] + v * BITS;
+        if ((lane >> 1) < g.nv) {  // lanes past a ragged tail encoded stale rows
+            // the lanes of the tile write 64 * 8 BITS contiguous bytes
+            uint2 *dst = (uint2 *)(a.codes[kt] + g.v0 * BITS) + lane * BITS;
 #pragma unroll
-            for (int q = 0; q < BITS; ++q) {
-                u4_t o = {out[4 * q], out[4 * q + 1], out[4 * q + 2], out[4 * q + 3]};
-                dst[q] = o;
-            }
-            a.norms[kt][v] = rho;
+            for (int q = 0; q < BITS; ++q) dst[q] = make_uint2(out[2 * q], out[2 * q + 1]);
+            if (!(lane & 1)) a.norms[kt][g.v0 + (lane >> 1)] = rho;
         }
         if (!has_next) break;
         tile = next;
+        next = after;
     }
 }
 
@@ -639,12 +718,13 @@ hipError_t run(const kvq_ctx *ctx, const QArgs &a, int n_tensors, int64_t B, int
     HalfThresholds ht{};
     const int L = 1 << BITS;
     for (int k = 0; k < L / 2 - 1; ++k) ht.p[k] = ctx->cb.t[L / 2 + k];
-    const int64_t tiles_per_bh = (T + kTile - 1) / kTile;
+    const int64_t tiles_per_bh = (T + kTileH - 1) / kTileH;
     const int64_t n_tiles = tiles_per_bh * B * ctx->H;
-    int64_t blocks = (n_tiles * n_tensors + kWaves - 1) / kWaves;
-    if (blocks > 2 * (int64_t)ctx->n_cu) blocks = 2 * (int64_t)ctx->n_cu;  // 8 resident waves per CU
-    hipLaunchKernelGGL(k_quantize<BITS>, dim3((unsigned)blocks), dim3(kWaves * 64), 0, s, a,
-                       (const uint32_t *)ctx->d_sgnmask, ht, T, ctx->H, tiles_per_bh, n_tiles, n_tensors);
+    // one workgroup per CU, each with at least one tile
+    int64_t blocks = n_tiles * n_tensors;
+    if (blocks > (int64_t)ctx->n_cu) blocks = ctx->n_cu;
+    hipLaunchKernelGGL(k_quantize<BITS>, dim3((unsigned)blocks), dim3(kWavesQ * 64), 0, s, a,
+                       (const uint32_t *)ctx->d_sgnmask_h, ht, T, ctx->H, tiles_per_bh, n_tiles, n_tensors);
     return hipGetLastError();
 }
 

@@ -58,7 +58,7 @@ def test_batch16_full_size_sampled():
 
 
 @pytest.mark.parametrize("bits", [1, 2, 3, 4])
-@pytest.mark.parametrize("T", [1, 63, 64, 65, 129])
+@pytest.mark.parametrize("T", [1, 31, 32, 33, 63, 64, 65, 129])
 def test_edges(bits, T):
     rng = np.random.default_rng(T * 10 + bits)
     x = (rng.standard_normal((2, 3, T, 128)) * np.exp(rng.standard_normal((3, 1, 128)))).astype(np.float16)
