@@ -153,6 +153,39 @@ __device__ __forceinline__ void score_record(const uint32_t *Wd, const float *lu
     }
 }
 
+// score_record in groups of 8 fields: the scheduler may not move address
+// computations or reads across groups, so at most 8 entries are in flight
+// (all 64 at once would not fit in the registers of a wave).
+template <int BITS, int G>
+__device__ __forceinline__ void score_record_grouped(const uint32_t *Wd, const float *lut, float *acc)
+{
+    using FD = Fields<BITS>;
+#pragma unroll
+    for (int h = 0; h < G; ++h) acc[h] = 0.0f;
+#pragma unroll
+    for (int f = 0; f < FD::NF; ++f) {
+        if (f % 8 == 0) __builtin_amdgcn_sched_barrier(0);
+        const int e = f * FD::E + (int)field<BITS>(Wd, f);
+        if constexpr (G % 4 == 0) {
+#pragma unroll
+            for (int h4 = 0; h4 < G / 4; ++h4) {
+                const f4_t x = reinterpret_cast<const f4_t *>(lut)[e * (G / 4) + h4];
+                acc[4 * h4] += x.x;
+                acc[4 * h4 + 1] += x.y;
+                acc[4 * h4 + 2] += x.z;
+                acc[4 * h4 + 3] += x.w;
+            }
+        } else if constexpr (G == 2) {
+            const f2_t x = reinterpret_cast<const f2_t *>(lut)[e];
+            acc[0] += x.x;
+            acc[1] += x.y;
+        } else {
+            acc[0] += lut[e];
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 template <int BITS>
 __device__ __forceinline__ void load_record(const uint8_t *codes, int64_t v, uint32_t *Wd)
 {
@@ -254,9 +287,10 @@ __global__ __launch_bounds__(kThreads) void k_logits(
 //  K  lane = token: logit from the field tables, scaled by rho_K and by
 //     sm_scale*log2(e); wave max / sum give a running (m, l) per head
 //     (base-2 exponentials);
-//  V  lane = 4 consecutive coordinates and one token parity: the weights
-//     p_h,t rho_V,t and the staged V records are read from the wave's LDS and
-//     accumulated in the rotated domain, acc_h[i] += p rho_V c[idx_t,i].
+//  V  lane = 8 consecutive coordinates (an octet) and one of four token
+//     phases: the weights p_h,t rho_V,t and the staged V records are read
+//     from the wave's LDS and accumulated in the rotated domain,
+//     acc_h[i] += p rho_V c[idx_t,i].
 // The block's waves merge once at the end; the block writes (m, l, acc) for
 // its G heads and the last block of a (b, g) to finish (arrival counter)
 // merges the splits and applies the inverse rotation once:
@@ -268,23 +302,45 @@ constexpr int kDecThreads = kDecWaves * 64;
 template <int BITS, int G>
 struct DecSmem {
     using FD = Fields<BITS>;
-    static constexpr int RW = FD::W + 1;                          // staged record words (+ guard)
-    static constexpr int qr = 0;                                  // [G][128]
-    static constexpr int lut = qr + G * kD;                       // [NF][E][G]
+    // staged V record stride in dwords: at least one word past the record
+    // (the funnel shift of the last octet reads it), 16 when that suffices
+    static constexpr int RW = FD::W + 1 <= 16 ? 16 : FD::W + 1;
+    // the field tables come first: with a constant base, every field's part
+    // of an entry address fits the 16-bit offset of an LDS instruction
+    static constexpr int lut = 0;                                 // [NF][E][G]
     static constexpr int c2 = lut + FD::NF * FD::E * G;           // [2^(2b)][2] centroid pairs
     static constexpr int vbuf = c2 + 2 * (1 << (2 * BITS));       // [waves][64][RW] V records
     static constexpr int wbuf = vbuf + kDecWaves * 64 * RW;       // [waves][64][G] weights
-    static constexpr int wm = wbuf + kDecWaves * 64 * G;          // [waves][G] wave maxima
+    static constexpr int qr = wbuf + kDecWaves * 64 * G;          // [G][128] rotated queries
+    static constexpr int wm = qr + G * kD;                        // [waves][G] wave maxima
     static constexpr int wl = wm + kDecWaves * G;                 // [waves][G] wave sums
     static constexpr int ctab = wl + kDecWaves * G;               // [16] centroids
-    static constexpr int total = ctab + 16;
+    static constexpr int flag = ctab + 16;                        // [1] last-arrival flag
+    static constexpr int total = flag + 4;
     // end-of-block reuse of vbuf..wbuf: per-wave accumulators, split merge
-    static_assert(wm - vbuf >= kDecWaves * G * kD, "wave merge buffer does not fit");
-    static_assert(wm - vbuf >= 2 * kMaxSplits * G, "split merge buffer does not fit");
+    static_assert(qr - vbuf >= kDecWaves * G * kD, "wave merge buffer does not fit");
+    static_assert(qr - vbuf >= 2 * kMaxSplits * G, "split merge buffer does not fit");
+    static_assert(FD::NF * FD::E * G * 4 <= 65536, "field offsets must fit an LDS immediate");
 };
 
+// Cross-row exchanges on the VALU (gfx950 lane swaps): with the same value in
+// both operands, the swap of odd and even rows yields lane l ^ 16 in one
+// result and lane l in the other, and likewise for halves (l ^ 32).
+__device__ __forceinline__ float2 swap16(float x)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x),
+                                                    false, false);
+    return float2{__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1])};
+}
+__device__ __forceinline__ float2 swap32(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x),
+                                                    false, false);
+    return float2{__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1])};
+}
+
 // Wave-wide max / sum, result in every lane: four DPP steps inside each row
-// of 16 lanes, then two exchanges across rows.
+// of 16 lanes, then the exchanges across rows and halves.
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x)
 {
@@ -296,8 +352,10 @@ __device__ __forceinline__ float wave_max(float x)
     x = fmaxf(x, dpp<0x4E>(x));   // quad_perm [2,3,0,1]
     x = fmaxf(x, dpp<0x141>(x));  // row_half_mirror
     x = fmaxf(x, dpp<0x140>(x));  // row_mirror
-    x = fmaxf(x, __shfl_xor(x, 16));
-    return fmaxf(x, __shfl_xor(x, 32));
+    float2 p = swap16(x);
+    x = fmaxf(p.x, p.y);
+    p = swap32(x);
+    return fmaxf(p.x, p.y);
 }
 __device__ __forceinline__ float wave_sum(float x)
 {
@@ -305,8 +363,15 @@ __device__ __forceinline__ float wave_sum(float x)
     x += dpp<0x4E>(x);
     x += dpp<0x141>(x);
     x += dpp<0x140>(x);
-    x += __shfl_xor(x, 16);
-    return x + __shfl_xor(x, 32);
+    float2 p = swap16(x);
+    x = p.x + p.y;
+    p = swap32(x);
+    return p.x + p.y;
+}
+// A value that is the same in every lane, moved to a scalar register.
+__device__ __forceinline__ float uniform(float x)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
 }
 // LDS written by some lanes of a wave is read by other lanes of the same wave.
 __device__ __forceinline__ void wave_lds_sync()
@@ -314,6 +379,41 @@ __device__ __forceinline__ void wave_lds_sync()
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// One V step of a lane: the octet of token tt's staged record (bits of 8
+// coordinates, as four fields of two), its four centroid pairs, the G weights
+// of the token, 8 G multiply-adds.
+template <int BITS, int G>
+__device__ __forceinline__ void v_step(const uint32_t *rec, const float *wrow, const float *c2, int owd, int osh,
+                                       float (&acc)[G][8])
+{
+    constexpr uint32_t fmask = (1u << (2 * BITS)) - 1u;
+    const uint32_t bits = __builtin_amdgcn_alignbit(rec[owd + 1], rec[owd], (uint32_t)osh);
+    f2_t cp[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) cp[k] = reinterpret_cast<const f2_t *>(c2)[(bits >> (2 * BITS * k)) & fmask];
+    float wv[G];
+    if constexpr (G % 4 == 0) {
+#pragma unroll
+        for (int h4 = 0; h4 < G / 4; ++h4) {
+            const f4_t x = reinterpret_cast<const f4_t *>(wrow)[h4];
+            wv[4 * h4] = x.x;
+            wv[4 * h4 + 1] = x.y;
+            wv[4 * h4 + 2] = x.z;
+            wv[4 * h4 + 3] = x.w;
+        }
+    } else {
+#pragma unroll
+        for (int h = 0; h < G; ++h) wv[h] = wrow[h];
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            acc[h][2 * k] = fmaf(wv[h], cp[k].x, acc[h][2 * k]);
+            acc[h][2 * k + 1] = fmaf(wv[h], cp[k].y, acc[h][2 * k + 1]);
+        }
 }
 
 template <int BITS, int G>
@@ -341,15 +441,13 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
     const int64_t b = bh / H;
     const int g = (int)(bh - b * H);
 
-
     // V lane roles: coordinate octet co (coordinates 8co .. 8co+7) and token
     // phase ph (tokens ph, ph+4, ...): the 8b bits of an octet come from one
     // funnel shift of two record dwords, its four centroid pairs from four
     // 8-byte LDS reads.
     const int co = lane & 15, ph = lane >> 4;
-    constexpr int OB = 8 * BITS;                  // bits of an octet
+    constexpr int OB = 8 * BITS;  // bits of an octet
     const int obit = OB * co, owd = obit >> 5, osh = obit & 31;
-    constexpr uint32_t fmask = (1u << (2 * BITS)) - 1u;
 
     float m_run[G], l_run[G], acc[G][8];
 #pragma unroll
@@ -362,127 +460,177 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
 
     const int64_t t_begin = (int64_t)split * chunk;
     const int64_t t_end = min(T, t_begin + chunk);
-    // Records of the wave's current tile are held in registers; the next
-    // tile's loads are issued before the current tile is processed.
+    // The query loads go out first: memory operations complete in issue order,
+    // so loads issued after the records would make the prologue wait for them.
+    uint32_t qv = 0u;
+    f2_t qs = f2_t{0.0f, 0.0f};
+    if (wv < G) {
+        qv = reinterpret_cast<const uint32_t *>(q + ((int64_t)b * Hq + (int64_t)g * G + wv) * kD)[lane];
+        qs = reinterpret_cast<const f2_t *>(signs_k + g * kD)[lane];
+    }
+    // The records of the wave's next tile are held in registers: loaded before
+    // the prologue for the first tile, and right after the current tile's
+    // records have been consumed for the others.
     uint32_t Kw[FD::W + 1], Vw[FD::W];
     float rk = 0.0f, rv = 0.0f;
+    // Every lane loads (tokens past the end re-read the last one of the
+    // range), so the loads carry no lane-dependent branch and the compiler's
+    // wait for the query values counts exactly the loads issued after them.
+    // Addresses: a wave-uniform 64-bit base for the tile plus a 32-bit lane
+    // offset (scalar-base loads; one VGPR of address per load).
     auto fetch = [&](int64_t t0) {
-        const int64_t t = t0 + lane;
-        if (t0 < t_end && t < t_end) {
-            const int64_t v = bh * T + t;
-            load_record<BITS>(kc, v, Kw);
-            const u4_t *src = reinterpret_cast<const u4_t *>(vc) + v * BITS;
+        t0 = min(t0, t_end - 1);  // a wave without a tile loads the range's last token
+        const int64_t v0 = bh * T + t0;
+        const uint32_t l = (uint32_t)min((int64_t)lane, t_end - 1 - t0);  // >= 0
+        const uint32_t off = l * (16u * BITS);  // bytes
+        const char *ks = reinterpret_cast<const char *>(kc) + v0 * (16 * BITS) + off;
+        const char *vs = reinterpret_cast<const char *>(vc) + v0 * (16 * BITS) + off;
 #pragma unroll
-            for (int k = 0; k < BITS; ++k) {
-                const u4_t x = src[k];
-                Vw[4 * k] = x.x;
-                Vw[4 * k + 1] = x.y;
-                Vw[4 * k + 2] = x.z;
-                Vw[4 * k + 3] = x.w;
-            }
-            rk = kn[v];
-            rv = vn[v];
+        for (int k = 0; k < BITS; ++k) {
+            const u4_t x = reinterpret_cast<const u4_t *>(ks)[k], y = reinterpret_cast<const u4_t *>(vs)[k];
+            Kw[4 * k] = x.x;
+            Kw[4 * k + 1] = x.y;
+            Kw[4 * k + 2] = x.z;
+            Kw[4 * k + 3] = x.w;
+            Vw[4 * k] = y.x;
+            Vw[4 * k + 1] = y.y;
+            Vw[4 * k + 2] = y.z;
+            Vw[4 * k + 3] = y.w;
         }
+        Kw[4 * BITS] = 0u;  // guard word for fields that end on the last dword
+        rk = *reinterpret_cast<const float *>(reinterpret_cast<const char *>(kn + v0) + 4 * l);
+        rv = *reinterpret_cast<const float *>(reinterpret_cast<const char *>(vn + v0) + 4 * l);
     };
     constexpr int64_t kStride = (int64_t)kDecWaves * 64;
-    // The first tile's loads go out before the prologue, so their latency
-    // overlaps the query rotation and the table build.
+    // the centroids too: indexed at run time, they are read from memory
+    float cen = 0.0f;
+    if (tid < 16) cen = cb.c[tid];
+    __builtin_amdgcn_sched_barrier(0);  // keep the prologue's loads ahead of the records
     fetch(t_begin + (int64_t)wv * 64);
-    stage_centroids(cb, smem + SM::ctab);
-    rotate_queries<G>(q, signs_k, b, g, Hq, qr);
-    build_tables<BITS, G>(qr, smem + SM::ctab, lut);
-    constexpr uint32_t cm = (1u << BITS) - 1u;
-    for (int e = tid; e < (1 << (2 * BITS)); e += kDecThreads) {
-        c2[2 * e] = cb.c[e & cm];
-        c2[2 * e + 1] = cb.c[(e >> BITS) & cm];
+    float *ctab = smem + SM::ctab;
+    if (tid < 16) ctab[tid] = cen;
+    if (wv < G) {  // one wave per head: qr[h] = H (D_K .* q_h)
+        float x0 = (float)__builtin_bit_cast(h2_t, qv).x * qs.x;
+        float x1 = (float)__builtin_bit_cast(h2_t, qv).y * qs.y;
+        wave_fwht(x0, x1, lane);
+        reinterpret_cast<f2_t *>(qr + wv * kD)[lane] = f2_t{x0, x1};
     }
     __syncthreads();
+    constexpr uint32_t cm = (1u << BITS) - 1u;
+    for (int e = tid; e < (1 << (2 * BITS)); e += kDecThreads) {
+        c2[2 * e] = ctab[e & cm];
+        c2[2 * e + 1] = ctab[(e >> BITS) & cm];
+    }
+    build_tables<BITS, G>(qr, ctab, lut);
+    __syncthreads();
+
+    const uint32_t *vrow = vbuf + ph * RW;  // this lane's token phase in the staged records
+    const float *wrow = wbuf + ph * G;
     for (int64_t t0 = t_begin + (int64_t)wv * 64; t0 < t_end; t0 += kStride) {
         const int nt = (int)min((int64_t)64, t_end - t0);
         const bool valid = lane < nt;
-        uint32_t Kc[FD::W + 1], Vc[FD::W];
-#pragma unroll
-        for (int k = 0; k <= FD::W; ++k) Kc[k] = Kw[k];
-#pragma unroll
-        for (int k = 0; k < FD::W; ++k) Vc[k] = Vw[k];
-        const float rkc = rk, rvc = rv;
-        fetch(t0 + kStride);
         float s[G];
-        if (valid) {
+        const float rvc = rv;
+        // lanes past the end hold a copy of the last record: staged (never
+        // read) and scored (then discarded)
+        if constexpr (RW % 4 == 0) {  // 16-byte aligned rows
 #pragma unroll
-            for (int k = 0; k < FD::W; ++k) vbuf[lane * RW + k] = Vc[k];
-            vbuf[lane * RW + FD::W] = 0u;
-            score_record<BITS, G>(Kc, lut, s);
-            const float rs = rkc * scale_log2;
-#pragma unroll
-            for (int h = 0; h < G; ++h) s[h] *= rs;
+            for (int k = 0; k < FD::W / 4; ++k)
+                reinterpret_cast<u4_t *>(vbuf + lane * RW)[k] = u4_t{Vw[4 * k], Vw[4 * k + 1], Vw[4 * k + 2], Vw[4 * k + 3]};
         } else {
 #pragma unroll
-            for (int h = 0; h < G; ++h) s[h] = -INFINITY;
+            for (int k = 0; k < FD::W; ++k) vbuf[lane * RW + k] = Vw[k];
         }
+        score_record_grouped<BITS, G>(Kw, lut, s);
+        const float rs = rk * scale_log2;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            s[h] = valid ? s[h] * rs : -INFINITY;
+            // the sums are formed here, not sunk past the loads below (which
+            // would keep all 64 table entries live in registers meanwhile)
+            asm volatile("" : : "v"(s[h]));
+        }
+        if (t0 + kStride < t_end) fetch(t0 + kStride);  // this tile's records are consumed
+        // m, l and the rescale factor are the same in every lane: kept in
+        // scalar registers
         float alpha[G];
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-            const float mn = fmaxf(m_run[h], wave_max(s[h]));
-            alpha[h] = __builtin_amdgcn_exp2f(m_run[h] - mn);  // 0 on the first tile (m_run = -inf)
+            const float mn = uniform(fmaxf(m_run[h], wave_max(s[h])));
+            alpha[h] = uniform(__builtin_amdgcn_exp2f(m_run[h] - mn));  // 0 on the first tile (m_run = -inf)
             m_run[h] = mn;
             const float p = valid ? __builtin_amdgcn_exp2f(s[h] - mn) : 0.0f;
-            l_run[h] = l_run[h] * alpha[h] + wave_sum(p);
-            wbuf[lane * G + h] = p * rvc;
+            l_run[h] = uniform(l_run[h] * alpha[h] + wave_sum(p));
+            s[h] = p * rvc;
 #pragma unroll
             for (int k = 0; k < 8; ++k) acc[h][k] *= alpha[h];
         }
+        if constexpr (G % 4 == 0) {
+#pragma unroll
+            for (int h4 = 0; h4 < G / 4; ++h4)
+                reinterpret_cast<f4_t *>(wbuf + lane * G)[h4] = f4_t{s[4 * h4], s[4 * h4 + 1], s[4 * h4 + 2], s[4 * h4 + 3]};
+        } else {
+#pragma unroll
+            for (int h = 0; h < G; ++h) wbuf[lane * G + h] = s[h];
+        }
         wave_lds_sync();
-        for (int tt = ph; tt < nt; tt += 4) {
-            const uint32_t *r = vbuf + tt * RW;
-            const uint32_t bits = __builtin_amdgcn_alignbit(r[owd + 1], r[owd], (uint32_t)osh);
-            f2_t cp[4];
+        if (nt == 64) {  // full tile: 16 steps with constant LDS offsets
 #pragma unroll
-            for (int k = 0; k < 4; ++k)
-                cp[k] = reinterpret_cast<const f2_t *>(c2)[(bits >> (2 * BITS * k)) & fmask];
-            float wv4[G];
-            if constexpr (G % 4 == 0) {
-#pragma unroll
-                for (int h4 = 0; h4 < G / 4; ++h4) {
-                    const f4_t x = reinterpret_cast<const f4_t *>(wbuf + tt * G)[h4];
-                    wv4[4 * h4] = x.x;
-                    wv4[4 * h4 + 1] = x.y;
-                    wv4[4 * h4 + 2] = x.z;
-                    wv4[4 * h4 + 3] = x.w;
-                }
-            } else {
-#pragma unroll
-                for (int h = 0; h < G; ++h) wv4[h] = wbuf[tt * G + h];
+            for (int j = 0; j < 16; ++j) {
+                // at most two steps' loads in flight: hoisting all sixteen
+                // would need far more registers than a wave has
+                __builtin_amdgcn_sched_barrier(0);
+                v_step<BITS, G>(vrow + 4 * j * RW, wrow + 4 * j * G, c2, owd, osh, acc);
             }
-#pragma unroll
-            for (int h = 0; h < G; ++h)
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    acc[h][2 * k] = fmaf(wv4[h], cp[k].x, acc[h][2 * k]);
-                    acc[h][2 * k + 1] = fmaf(wv4[h], cp[k].y, acc[h][2 * k + 1]);
-                }
+        } else {
+            for (int tt = ph; tt < nt; tt += 4) v_step<BITS, G>(vbuf + tt * RW, wbuf + tt * G, c2, owd, osh, acc);
         }
         wave_lds_sync();  // vbuf / wbuf are rewritten by the next tile
     }
-    // the four token phases hold partial sums of the same coordinates
+
+    // Sum the four token phases (lanes l, l^16, l^32, l^48 hold partial sums
+    // of the same coordinates) with lane swaps: one swap and one add per
+    // register and level.  Afterwards register r of red[] holds in row k
+    // (lanes 16k .. 16k+15, coordinate octet co) the total of accumulator
+    // 4r + k, accumulator a = 8h + j being coordinate 8co + j of head h.
+    constexpr int NA = 8 * G;
+    float red[NA / 4];
+    {
+        float s1[NA / 2];
 #pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            acc[h][k] += __shfl_xor(acc[h][k], 16);
-            acc[h][k] += __shfl_xor(acc[h][k], 32);
+        for (int i = 0; i < NA / 2; ++i) {  // level 1: pairs (2i, 2i+1) across halves
+            const float a = acc[(2 * i) / 8][(2 * i) % 8], c = acc[(2 * i + 1) / 8][(2 * i + 1) % 8];
+            const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, a),
+                                                            __builtin_bit_cast(unsigned, c), false, false);
+            // lanes 0-31: a's halves summed; lanes 32-63: c's
+            s1[i] = __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
         }
+#pragma unroll
+        for (int i = 0; i < NA / 4; ++i) {  // level 2: pairs (2i, 2i+1) across rows
+            const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, s1[2 * i]),
+                                                            __builtin_bit_cast(unsigned, s1[2 * i + 1]), false, false);
+            red[i] = __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+        }
+    }
 
     // Block merge of the waves: M = max_w m_w, acc = sum_w 2^(m_w - M) acc_w, same for l.
     float *wacc = smem + SM::vbuf;  // reuse: [waves][G][128]
     float *wm = smem + SM::wm;
     float *wl = smem + SM::wl;
     __syncthreads();  // all waves done with vbuf / wbuf
-    if (lane < 16)
+    {
+        // level-1 result i holds accumulator 2i (lanes 0-31) and 2i+1 (lanes
+        // 32-63); level 2 combined level-1 results 2i (rows 0, 2 -> rows 0, 2)
+        // and 2i+1 (rows 1, 3): row k of red[i] is accumulator
+        // {4i, 4i+2, 4i+1, 4i+3}[k]
+        const int k = ph;
+        const int sel = (k == 0) ? 0 : (k == 1) ? 2 : (k == 2) ? 1 : 3;
 #pragma unroll
-        for (int h = 0; h < G; ++h)
-#pragma unroll
-            for (int k = 0; k < 8; ++k) wacc[(wv * G + h) * kD + 8 * co + k] = acc[h][k];
+        for (int i = 0; i < NA / 4; ++i) {
+            const int a = 4 * i + sel, h = a >> 3, j = a & 7;
+            wacc[(wv * G + h) * kD + 8 * co + j] = red[i];
+        }
+    }
     if (lane == 0)
 #pragma unroll
         for (int h = 0; h < G; ++h) {
@@ -518,7 +666,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
     // the other blocks' partials.
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's stores have reached L2
     __syncthreads();
-    __shared__ unsigned last;
+    unsigned &last = *reinterpret_cast<unsigned *>(smem + SM::flag);
     if (wv == 0) {  // wave-uniform: cache write-back / invalidate act per wave
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
         unsigned prev = 0;
