@@ -433,6 +433,7 @@ __global__ __launch_bounds__(kWavesQ * 64) __attribute__((amdgpu_waves_per_eu(4,
 // ---------------------------------------------------------------------------
 typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
+typedef float f16_t __attribute__((ext_vector_type(16)));
 
 struct QjlArgs {
     const u4_t *x;
@@ -490,11 +491,18 @@ __device__ __forceinline__ _Float16 split_f16(float v, _Float16 &lo)
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * 16 + (chunk ^ (row & 15)); }
 
-// Write a wave-uniform value into lane KEY of v (other lanes unchanged).
-template <int KEY>
-__device__ __forceinline__ uint32_t write_lane(uint32_t v, uint32_t val)
+// Write the low and high halves of a lane mask into lanes KLO and KHI of v.
+// The leading s_nop 4 gives the wait states a read of an SGPR pair needs right
+// after a VALU instruction (the compare that made the mask) wrote it: the
+// compiler cannot see into the asm, and without them the first read returned
+// the previous value.
+template <int KLO, int KHI>
+__device__ __forceinline__ uint32_t write_lane_pair(uint32_t v, uint64_t m)
 {
-    asm("v_writelane_b32 %0, %1, %2" : "+v"(v) : "s"(val), "n"(KEY));
+    asm("s_nop 4\n\t"
+        "v_writelane_b32 %0, %1, %3\n\t"
+        "v_writelane_b32 %0, %2, %4"
+        : "+v"(v) : "s"((uint32_t)m), "s"((uint32_t)(m >> 32)), "n"(KLO), "n"(KHI));
     return v;
 }
 
@@ -510,67 +518,201 @@ struct StaticFor {
     }
 };
 
+// Tile of 32 keys for the QJL kernel, two lanes per key: lane 32h + v holds
+// coordinates [64 h, 64 h + 64) of key v (so that the residual can feed the
+// matrix cores straight from registers, see below).  Chunk c of row v sits at
+// LDS slot 16 v + ((c + v) mod 16): the 16 lanes of one half that read chunk
+// 8h + k of 16 consecutive rows hit 16 different bank groups.  Copy
+// instruction j writes slots [64 j, 64 j + 64) (rows 4j .. 4j+3, one
+// contiguous KiB of HBM); the chunk a lane fetches depends on j only through
+// j mod 4.  A ninth instruction copies the head's 64 sign-mask dwords.
+__device__ __forceinline__ void qjl_tile_to_lds(const u4_t *src, int nv, const uint32_t *msk, u4_t *L, int lane)
+{
+    asm volatile("" : "+v"(lane));
+    if (nv == kTileH) {
+        uint32_t off[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int v = 4 * r + (lane >> 4);
+            off[r] = (uint32_t)((lane >> 4) * 16 + (((lane & 15) - v) & 15));
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void *)(src + 64 * j + off[j & 3]),
+                (__attribute__((address_space(3))) void *)(L + j * 64), 16, 0, 0);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int v = 4 * j + (lane >> 4);
+            const int row = v < nv ? v : nv - 1;
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void *)(src + row * 16 + (((lane & 15) - v) & 15)),
+                (__attribute__((address_space(3))) void *)(L + j * 64), 16, 0, 0);
+        }
+    }
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(msk + lane),
+                                     (__attribute__((address_space(3))) void *)(L + kRowsH), 4, 0, 0);
+}
+
+// Wait for the tile copy, read half row h of key v into w (lane 32h + v),
+// apply D, and draw the wave's next ticket from the LDS counter (see
+// take_rows).
+__device__ __forceinline__ int qjl_take_rows(const u4_t *L, int lane, uint32_t *w, int *counter)
+{
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" : "+v"(lane));
+    wait_vm_n<0>();
+    const int v = lane & 31, h = lane >> 5;
+    const u4_t *M = L + kRowsH + 8 * h;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const u4_t x = L[16 * v + ((8 * h + k + v) & 15)];
+        const u4_t m = M[k];
+        w[4 * k + 0] = x.x ^ m.x;
+        w[4 * k + 1] = x.y ^ m.y;
+        w[4 * k + 2] = x.z ^ m.z;
+        w[4 * k + 3] = x.w ^ m.w;
+    }
+    int t = 0;
+    if (lane == 0) t = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    wait_lgkm();
+    __builtin_amdgcn_wave_barrier();
+    return __builtin_amdgcn_readfirstlane(t);
+}
+
+// Swap of lanes 32..63 of x with lanes 0..31 of y (gfx950): returns
+// (x', y') with x' = [x_lo | y_lo] and y' = [x_hi | y_hi].
+__device__ __forceinline__ void swap_halves(float &x, float &y)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, y),
+                                                    false, false);
+    x = __builtin_bit_cast(float, (unsigned)r[0]);
+    y = __builtin_bit_cast(float, (unsigned)r[1]);
+}
+
+// Append the BITS-bit indices of 32 coordinates y[0..31] (LSB-first stream of
+// 32 BITS bits) to out[0 .. BITS), from the last bit backwards, and replace
+// each y[i] by its residual y[i] / rho - c[idx] (inv = 1 / rho; the sign of
+// c[idx] is [y > 0]).
 template <int BITS>
-__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_quantize_qjl(
+__device__ __forceinline__ void encode32(float *y, const float *P, const float *Mg, float inv, uint32_t *out)
+{
+#pragma unroll
+    for (int i = 31; i >= 0; --i) {
+        uint64_t M[BITS];
+        index_bits<BITS>(y[i], P, M);
+        const float mg = centroid_mag<BITS>(__builtin_fabsf(y[i]), P, Mg);
+        y[i] = fmaf(y[i], inv, y[i] > 0.0f ? -mg : mg);
+        const int lo = (BITS * i) >> 5, hi = (BITS * i + BITS - 1) >> 5;
+        if constexpr (BITS == 1) {
+            out[lo] = append_bit(out[lo], M[0]);
+        } else if (lo == hi) {
+            if constexpr (BITS == 2) out[lo] = append_bits(out[lo], M[1], M[0]);
+            if constexpr (BITS == 3) out[lo] = append_bits(out[lo], M[2], M[1], M[0]);
+            if constexpr (BITS == 4) {
+                out[lo] = append_bits(out[lo], M[3], M[2]);
+                out[lo] = append_bits(out[lo], M[1], M[0]);
+            }
+        } else {
+#pragma unroll
+            for (int k = BITS - 1; k >= 0; --k) {
+                const int wd = (BITS * i + k) >> 5;
+                out[wd] = append_bit(out[wd], M[k]);
+            }
+        }
+    }
+}
+
+// Quantise with the 1-bit QJL residual, one workgroup of 12 waves per CU
+// (three per SIMD), tiles of 32 keys claimed as in k_quantize.
+//  - MSE part as in k_quantize, except that the stride-64 butterfly pairs
+//    lanes l and l ^ 32: one gfx950 half swap of registers (i, i + 32) and an
+//    add and a subtract give coordinates i, i + 64 (lanes 0-31) and 32 + i,
+//    96 + i (lanes 32-63).  So register r of half h holds coordinate
+//    C(h, r) = 32 h + r for r < 32 and 64 + 32 h + (r - 32) for r >= 32, and
+//    each half packs two runs of 32 coordinates.
+//  - e = y / rho - c[idx] per coordinate (the factor 1/sqrt(d) of r does not
+//    change a sign), gamma = ||e|| / sqrt(d); e is split exactly into fp16
+//    hi + lo (hi by round-toward-zero conversion, i.e. its 11 leading
+//    significant bits; lo = e - hi exactly, then rounded once).
+//  - The projection S e of the 32 keys runs on v_mfma_f32_32x32x16_f16 with
+//    the A operand straight from registers: the contraction may visit the
+//    coordinates in any order as long as both operands agree, so k-step s
+//    takes, in lane half h, registers 8s .. 8s+7 (coordinates C(h, 8s) ..
+//    +7, contiguous), and the B operand reads the same coordinates of the
+//    rows of S staged in LDS.  Each accumulator register of a 32 x 32 block
+//    (rows = keys, columns = outputs) gives, with one ballot, two keys' 32
+//    sign bits of the block, which are written into the key's lane.
+constexpr int kWavesJ = 12;  // waves per workgroup of the QJL kernel
+
+template <int BITS, bool S_LO>
+__global__ __launch_bounds__(kWavesJ * 64) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_quantize_qjl(
     QjlArgs a, const uint32_t *__restrict__ sgn, HalfThresholds ht, int64_t T, int H, int64_t tiles_per_bh,
     int64_t n_tiles)
 {
-    __shared__ u4_t Ehi[kWaves][kTile * 16];  // fp16 hi rows of e (16-byte chunks swizzled)
-    __shared__ u4_t Elo[kWaves][kTile * 16];  // fp16 lo rows of e
-    __shared__ u4_t Ss[kD * 16];              // S_hi, row j chunk c at slot j*16 + (c ^ (j & 15))
+    __shared__ u4_t Ss[kD * 16];              // S_hi, row n chunk c at slot n*16 + (c ^ (n & 15))
+    __shared__ u4_t lds[kWavesJ][kBufH];      // tiles of the waves
+    __shared__ int next_tile;
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    for (int i = threadIdx.x; i < kD * 16; i += kWaves * 64) Ss[swz(i >> 4, i & 15)] = a.S_hi[i];
+    for (int i = threadIdx.x; i < kD * 16; i += kWavesJ * 64) Ss[swz(i >> 4, i & 15)] = a.S_hi[i];
+    if (threadIdx.x == 0) next_tile = kWavesJ;
     __syncthreads();
-    u4_t *Lhi = Ehi[wv], *Llo = Elo[wv];
-    const int64_t stride = (int64_t)gridDim.x * kWaves;
-    int64_t tile = (int64_t)blockIdx.x * kWaves + wv;
-    // Each lane loads its key's row straight into registers; the next tile's
-    // rows are requested before the current tile's projection.
-    u4_t xr[16];
-    auto load_rows = [&](int64_t t) {
-        const TileGeom gq = geom(t, T, H, tiles_per_bh);
-        const u4_t *src = a.x + (gq.v0 + min(lane, gq.nv - 1)) * 16;  // rows past a tail: last valid row
-#pragma unroll
-        for (int c = 0; c < 16; ++c) xr[c] = __builtin_nontemporal_load(src + c);
+    u4_t *L = lds[wv];
+    const int64_t G = gridDim.x;
+    int64_t tile = blockIdx.x + wv * G;
+    if (tile >= n_tiles) return;  // wave-uniform
+    auto issue = [&](int64_t t) {
+        const TileGeom gg = geom<kTileH>(t, T, H, tiles_per_bh);
+        qjl_tile_to_lds(a.x + gg.v0 * 16, gg.nv, sgn + gg.h * 64, L, lane);
     };
-    if (tile < n_tiles) load_rows(tile);
-    for (; tile < n_tiles; tile += stride) {
-        const TileGeom g = geom(tile, T, H, tiles_per_bh);
-        uint32_t w[64];
+    const int v = lane & 31, h = lane >> 5;
+    float Mg[8];
 #pragma unroll
-        for (int c = 0; c < 16; ++c) {
-            w[4 * c + 0] = xr[c].x;
-            w[4 * c + 1] = xr[c].y;
-            w[4 * c + 2] = xr[c].z;
-            w[4 * c + 3] = xr[c].w;
-        }
-        const bool active = lane < g.nv;
-        const uint32_t *sg = sgn + __builtin_amdgcn_readfirstlane(g.h * 64);
+    for (int k = 0; k < 8; ++k) Mg[k] = a.mags[k];
+    uint32_t w[32];
+    issue(tile);
+    int64_t next = blockIdx.x + qjl_take_rows(L, lane, w, &next_tile) * G;
+    if (next < n_tiles) issue(next);
+    for (;;) {
+        const TileGeom g = geom<kTileH>(tile, T, H, tiles_per_bh);
         float ss = 0.0f;
 #pragma unroll
-        for (int k = 0; k < 64; ++k) {
+        for (int k = 0; k < 32; ++k) {
             const h2_t p = __builtin_bit_cast(h2_t, w[k]);
             ss = __builtin_amdgcn_fdot2(p, p, ss, false);
-            w[k] ^= sg[k];
         }
-        float y[128];
+        float y[64];
 #pragma unroll
-        for (int k = 0; k < 64; ++k) {
+        for (int k = 0; k < 32; ++k) {
             y[2 * k] = pair_sum(w[k]);
             y[2 * k + 1] = pair_diff(w[k]);
         }
 #pragma unroll
-        for (int s = 2; s < 128; s <<= 1) {
+        for (int s = 2; s < 64; s <<= 1) {
 #pragma unroll
-            for (int i = 0; i < 128; i += 2 * s) {
+            for (int i = 0; i < 64; i += 2 * s) {
 #pragma unroll
                 for (int j = i; j < i + s; ++j) {
-                    const float p0 = y[j], p1 = y[j + s];
-                    y[j] = p0 + p1;
-                    y[j + s] = p0 - p1;
+                    const float p = y[j], q = y[j + s];
+                    y[j] = p + q;
+                    y[j + s] = p - q;
                 }
             }
+        }
+        // stride-64 stage across the halves
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            float p = y[i], q = y[i + 32];
+            swap_halves(p, q);
+            y[i] = p + q;
+            y[i + 32] = p - q;
+        }
+        {
+            float p = ss, q = ss;
+            swap_halves(p, q);
+            ss = p + q;  // the same sum in both halves
         }
         const float rho = __builtin_sqrtf(ss);
         const float r = rho > 0.0f ? rho : 1.0f;
@@ -579,111 +721,87 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 
 #pragma unroll
         for (int k = 0; k < 8; ++k) P[k] = ht.p[k] * r;
 
-        uint32_t out[4 * BITS];
+        // codes: run 0 = coordinates 32h .. 32h+31, run 1 = 64+32h .. 64+32h+31
+        uint32_t out[2 * BITS];
 #pragma unroll
-        for (int k = 0; k < 4 * BITS; ++k) out[k] = 0u;
-#pragma unroll
-        for (int i = 127; i >= 0; --i) {
-            uint64_t M[BITS];
-            index_bits<BITS>(y[i], P, M);
-#pragma unroll
-            for (int k = BITS - 1; k >= 0; --k) {
-                const int wd = (BITS * i + k) >> 5;
-                out[wd] = append_bit(out[wd], M[k]);
-            }
-        }
-        // residual e = y / rho - c[idx] (the sign of c[idx] is [y > 0]), and gamma
+        for (int k = 0; k < 2 * BITS; ++k) out[k] = 0u;
+        encode32<BITS>(y, P, Mg, inv, out);
+        encode32<BITS>(y + 32, P, Mg, inv, out + BITS);
+
+        // y now holds the residual e: gamma and the exact fp16 split
         float g2 = 0.0f;
+        uint32_t eh[32], el[32];
 #pragma unroll
-        for (int i = 0; i < 128; ++i) {
-            const float mg = centroid_mag<BITS>(__builtin_fabsf(y[i]), P, a.mags);
-            const float e = fmaf(y[i], inv, y[i] > 0.0f ? -mg : mg);
-            y[i] = e;
-            g2 = fmaf(e, e, g2);
+        for (int m = 0; m < 32; ++m) {
+            const float e0 = y[2 * m], e1 = y[2 * m + 1];
+            g2 = fmaf(e0, e0, g2);
+            g2 = fmaf(e1, e1, g2);
+            const h2_t hp = __builtin_bit_cast(h2_t, __builtin_amdgcn_cvt_pkrtz(e0, e1));
+            const h2_t lp = h2_t{(_Float16)(e0 - (float)hp.x), (_Float16)(e1 - (float)hp.y)};
+            eh[m] = __builtin_bit_cast(uint32_t, hp);
+            el[m] = __builtin_bit_cast(uint32_t, lp);
+        }
+        {
+            float p = g2, q = g2;
+            swap_halves(p, q);
+            g2 = p + q;
         }
 
-        // Stage e of all 64 keys as fp16 hi / lo rows (16-byte chunks swizzled).
-#pragma unroll
-        for (int c = 0; c < 16; ++c) {
-            h8_t hv, lv;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                _Float16 lo;
-                hv[j] = split_f16(y[8 * c + j], lo);
-                lv[j] = lo;
-            }
-            Lhi[swz(lane, c)] = __builtin_bit_cast(u4_t, hv);
-            Llo[swz(lane, c)] = __builtin_bit_cast(u4_t, lv);
-        }
-        wait_lgkm();
-        __builtin_amdgcn_wave_barrier();
-        if (tile + stride < n_tiles) load_rows(tile + stride);
-
-        // Projection of 16 keys at a time against all 128 rows of S: eight
-        // independent 16 x 16 accumulators (output blocks nb) per key block.
         uint32_t sgnw[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
-            f4_t z[8];
+        for (int nb = 0; nb < 4; ++nb) {
+            f16_t z = {};
+            const int n = 32 * nb + v;  // output row of S read by this lane
 #pragma unroll
-            for (int nb = 0; nb < 8; ++nb) z[nb] = f4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                const int row = 16 * mb + (lane & 15), chunk = 4 * kb + (lane >> 4);
-                const h8_t Ah = __builtin_bit_cast(h8_t, Lhi[swz(row, chunk)]);
-                const h8_t Al = __builtin_bit_cast(h8_t, Llo[swz(row, chunk)]);
-#pragma unroll
-                for (int nb = 0; nb < 8; ++nb) {
-                    const int srow = 16 * nb + (lane & 15);
-                    const h8_t Bh = __builtin_bit_cast(h8_t, Ss[swz(srow, chunk)]);
-                    z[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, Bh, z[nb], 0, 0, 0);
-                    z[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Al, Bh, z[nb], 0, 0, 0);
-                    if (a.S_lo) {
-                        const h8_t Bl = __builtin_bit_cast(h8_t, a.S_lo[srow * 16 + chunk]);
-                        z[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, Bl, z[nb], 0, 0, 0);
-                    }
+            for (int s = 0; s < 8; ++s) {
+                const int ch = (s < 4 ? s : s + 4) + 4 * h;  // 16-byte chunk of the coordinates C(h, 8s..8s+7)
+                const h8_t B = __builtin_bit_cast(h8_t, Ss[swz(n, ch)]);
+                const h8_t Ah = __builtin_bit_cast(h8_t, u4_t{eh[4 * s], eh[4 * s + 1], eh[4 * s + 2], eh[4 * s + 3]});
+                const h8_t Al = __builtin_bit_cast(h8_t, u4_t{el[4 * s], el[4 * s + 1], el[4 * s + 2], el[4 * s + 3]});
+                z = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ah, B, z, 0, 0, 0);
+                z = __builtin_amdgcn_mfma_f32_32x32x16_f16(Al, B, z, 0, 0, 0);
+                if constexpr (S_LO) {  // S not exactly fp16: third pass with its lo part
+                    const h8_t Bl = __builtin_bit_cast(h8_t, a.S_lo[n * 16 + ch]);
+                    z = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ah, Bl, z, 0, 0, 0);
                 }
             }
-            // Output block nb, row 4 q + rr of the 16 x 16 result (lane: q = lane/16, column
-            // lane%16 = output j - 16 nb): ballot bit 16 q + c is the sign of output
-            // 16 nb + c of key 16 mb + 4 q + rr.  Dword np of a key holds outputs
-            // 32 np .. 32 np + 31: blocks 2 np (low half) and 2 np + 1 (high half).
+            // register rr: lanes 0-31 hold key 8(rr/4) + rr%4, lanes 32-63 key
+            // 8(rr/4) + 4 + rr%4, columns = outputs 32 nb + (lane % 32)
+            uint32_t acc = sgnw[nb];
+            StaticFor<0, 16>::run([&](auto kk) {
+                constexpr int rr = decltype(kk)::value;
+                constexpr int k0 = 8 * (rr / 4) + rr % 4;
+                const uint64_t m = __builtin_amdgcn_ballot_w64(z[rr] >= 0.0f);
+                acc = write_lane_pair<k0, k0 + 4>(acc, m);
+            });
+            sgnw[nb] = acc;
+        }
+        // The next tile's rows, then the copy of the tile after it, then this
+        // tile's stores (as in k_quantize).  The rows are read only now: held
+        // through the projection they would not fit in the registers.
+        const bool has_next = next < n_tiles;
+        int64_t after = n_tiles;
+        if (has_next) {
+            after = blockIdx.x + qjl_take_rows(L, lane, w, &next_tile) * G;
+            if (after < n_tiles) issue(after);
+        }
+        if (v < g.nv) {  // lanes of keys past a ragged tail encoded stale rows
+            const int64_t key = g.v0 + v;
+            uint32_t *dst = reinterpret_cast<uint32_t *>(a.codes + key * BITS);
 #pragma unroll
-            for (int np = 0; np < 4; ++np) {
-                uint64_t m[2][4];
-#pragma unroll
-                for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-                    for (int rr = 0; rr < 4; ++rr) m[t2][rr] = __builtin_amdgcn_ballot_w64(z[2 * np + t2][rr] >= 0.0f);
-                uint32_t acc_np = sgnw[np];
-                StaticFor<0, 16>::run([&](auto kk) {
-                    constexpr int k = decltype(kk)::value;
-                    constexpr int q = k / 4, rr = k % 4;
-                    const uint32_t lo16 = (uint32_t)(m[0][rr] >> (16 * q)) & 0xFFFFu;
-                    const uint32_t hi16 = (uint32_t)(m[1][rr] >> (16 * q)) & 0xFFFFu;
-                    const uint32_t val = __builtin_amdgcn_readfirstlane(lo16 | (hi16 << 16));
-                    if (mb == 0) acc_np = write_lane<k>(acc_np, val);
-                    if (mb == 1) acc_np = write_lane<16 + k>(acc_np, val);
-                    if (mb == 2) acc_np = write_lane<32 + k>(acc_np, val);
-                    if (mb == 3) acc_np = write_lane<48 + k>(acc_np, val);
-                });
-                sgnw[np] = acc_np;
+            for (int k = 0; k < BITS; ++k) {
+                dst[h * BITS + k] = out[k];
+                dst[(2 + h) * BITS + k] = out[BITS + k];
+            }
+            if (h == 0) {
+                a.norms[key] = rho;
+                a.signs[key] = u4_t{sgnw[0], sgnw[1], sgnw[2], sgnw[3]};
+                a.gamma[key] = __builtin_sqrtf(g2) * 0.08838834764831845f;  // ||e|| / sqrt(d)
             }
         }
-        __builtin_amdgcn_wave_barrier();
-        if (active) {
-            const int64_t v = g.v0 + lane;
-            u4_t *dst = a.codes + v * BITS;
-#pragma unroll
-            for (int q = 0; q < BITS; ++q) {
-                u4_t o = {out[4 * q], out[4 * q + 1], out[4 * q + 2], out[4 * q + 3]};
-                dst[q] = o;
-            }
-            a.norms[v] = rho;
-            u4_t so = {sgnw[0], sgnw[1], sgnw[2], sgnw[3]};
-            a.signs[v] = so;
-            a.gamma[v] = __builtin_sqrtf(g2) * 0.08838834764831845f;  // ||e|| / sqrt(d)
-        }
+        if (!has_next) break;
+        tile = next;
+        next = after;
     }
 }
 
@@ -703,12 +821,17 @@ hipError_t run_qjl(const kvq_ctx *ctx, const void *x, int64_t B, int64_t T, uint
     a.S_hi = (const u4_t *)ctx->d_S16;
     a.S_lo = ctx->S_exact_f16 ? nullptr : (const u4_t *)(ctx->d_S16 + kD * kD);
     for (int k = 0; k < L / 2; ++k) a.mags[k] = ctx->cb.c[L / 2 + k];
-    const int64_t tiles_per_bh = (T + kTile - 1) / kTile;
+    const int64_t tiles_per_bh = (T + kTileH - 1) / kTileH;
     const int64_t n_tiles = tiles_per_bh * B * ctx->H;
-    int64_t blocks = (n_tiles + kWaves - 1) / kWaves;
-    if (blocks > (int64_t)ctx->n_cu) blocks = ctx->n_cu;  // one wave per SIMD (512 registers each)
-    hipLaunchKernelGGL(k_quantize_qjl<BITS>, dim3((unsigned)blocks), dim3(kWaves * 64), 0, s, a,
-                       (const uint32_t *)ctx->d_sgnmask, ht, T, ctx->H, tiles_per_bh, n_tiles);
+    // one workgroup per CU, each with at least one tile
+    int64_t blocks = n_tiles;
+    if (blocks > (int64_t)ctx->n_cu) blocks = ctx->n_cu;
+    if (a.S_lo)
+        hipLaunchKernelGGL((k_quantize_qjl<BITS, true>), dim3((unsigned)blocks), dim3(kWavesJ * 64), 0, s, a,
+                           (const uint32_t *)ctx->d_sgnmask, ht, T, ctx->H, tiles_per_bh, n_tiles);
+    else
+        hipLaunchKernelGGL((k_quantize_qjl<BITS, false>), dim3((unsigned)blocks), dim3(kWavesJ * 64), 0, s, a,
+                           (const uint32_t *)ctx->d_sgnmask, ht, T, ctx->H, tiles_per_bh, n_tiles);
     return hipGetLastError();
 }
 

@@ -45,7 +45,7 @@ def check_qjl(inp, bits, S, o, where=None):
     return mism
 
 
-@pytest.mark.parametrize("bits", [1, 2, 3])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
 def test_qjl_quantize_ragged(bits):
     inp = synth.make("long128k_qjl", T=700)
     ctx, o, _ = run_qjl(inp, bits, inp["S"])
