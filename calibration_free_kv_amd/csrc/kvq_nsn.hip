@@ -62,15 +62,19 @@ __device__ __forceinline__ void read_row(const u4_t *L, int lane, uint32_t *w)
     }
 }
 
+// ||x||^2 of a row as two chains over its halves, then their sum: the search
+// kernel holds the halves in two lanes and must obtain the same value (a_t is
+// rounded identically in both passes).
 __device__ __forceinline__ float norm2_f16(const uint32_t *w)
 {
-    float ss = 0.0f;
+    float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
-    for (int k = 0; k < 64; ++k) {
-        const h2_t p = __builtin_bit_cast(h2_t, w[k]);
-        ss = __builtin_amdgcn_fdot2(p, p, ss, false);
+    for (int k = 0; k < 32; ++k) {
+        const h2_t p = __builtin_bit_cast(h2_t, w[k]), q = __builtin_bit_cast(h2_t, w[32 + k]);
+        s0 = __builtin_amdgcn_fdot2(p, p, s0, false);
+        s1 = __builtin_amdgcn_fdot2(q, q, s1, false);
     }
-    return ss;
+    return s0 + s1;
 }
 
 // (1) partial sums over token chunks of a_t = sqrt(d) x_t / ||x_t||.
@@ -180,105 +184,225 @@ struct VqArgs {
     float *s1, *s2;       // [H][T]
 };
 
-// (3) per-token transform and nearest-entry search.  One wave per SIMD:
-// 16 KiB of LDS for the x tile (reused for the fp16 hi rows of z) and 16 KiB
-// for the lo rows; the block also stages the codebook (hi, lo, fp32, biases).
+// (3) per-token transform and nearest-entry search.  Tiles of 32 tokens of
+// one head, two lanes per token: lane 32h + v holds coordinates
+// [64 h, 64 h + 64) of token v while they are transformed.  One workgroup of
+// 8 waves per CU (two per SIMD) claims tiles from an LDS counter as the
+// quantize kernels do; each tile is copied straight into LDS together with
+// the head's channel means.  The block also stages the codebook.
 //
-// Search, per block of 32 tokens (MFMA columns) and 32 codewords (rows):
-// one v_mfma_f32_32x32x16_f16 gives C_hi . (z_hi + z_lo) + bias (k = 0..7
-// pairs the hi parts of z with C_hi, k = 8..15 the lo parts with C_hi again),
-// and one v_mfma_f32_32x32x8_f16 adds C_lo . z_hi when the codebook is not
-// fp16-exact.  A lane then holds 16 scores of one token: four groups of four
-// consecutive codewords.  It keeps, per sub-vector, only the best group (its
-// maximum, strictly larger in increasing codeword order), and at the end
-// recomputes the group's four scores in fp32 from z = z_hi + z_lo and the
-// fp32 codebook to pick the entry; the lane holding the other 16 codewords of
+// Transform: a = sqrt(d) x / ||x|| (||x||^2 summed as norm2_f16 does, so that
+// a is rounded exactly as in the stats pass), b = a - o, then six butterfly
+// stages inside the lane and the stride-64 stage across the halves with
+// gfx950 half swaps.  The swap pairs register 8t + k with 8t + 4 + k
+// (k < 4), so that afterwards both halves hold sub-vector s in registers
+// R(s) = 8 (s mod 8) + 4 (s / 8) .. + 3: half 0 its dims 0..3, half 1 its
+// dims 4..7.
+//
+// Search, per block of 32 codewords (MFMA rows; tokens are the columns): one
+// v_mfma_f32_32x32x16_f16 gives C_hi . (z_hi + z_lo) + bias.  Its k slots
+// are split between the lane halves exactly as the dims of z are: half h
+// supplies dims 4h .. 4h+3 of z_hi (k = 8h .. 8h+3) and of z_lo (k = 8h+4
+// .. 8h+7), and the A operand holds dims 4h .. 4h+3 of C_hi twice, so the
+// operands come straight from registers.  One v_mfma_f32_32x32x8_f16 adds
+// C_lo . z_hi when the codebook is not fp16-exact.  A lane then holds 16
+// scores of its token: four groups of four consecutive codewords.  It keeps,
+// per sub-vector, only the best group (its maximum, strictly larger in
+// increasing codeword order), and at the end recomputes the group's four
+// scores in fp32 (z = z_hi + z_lo, the other half's four dims fetched with a
+// half swap) to pick the entry; the lane holding the other 16 codewords of
 // each block does the same, and the better of the two (lower index on ties)
 // is the code.  Keeping groups instead of single entries takes the arg max
 // bookkeeping from 3 VALU operations per (sub-vector, codeword) to about 1.3.
+constexpr int kTileN = 32;           // tokens per tile of the search
+constexpr int kWavesN = 8;           // waves per workgroup (two per SIMD)
+constexpr int kRowsN = kTileN * 16;  // 16-byte chunks of x per tile
+constexpr int kBufN = kRowsN + 64;   // + two slots of the head's 128 channel means
+
+// Rows of the tile: chunk c of row v at slot 16 v + ((c + v) mod 16), so the
+// 16 lanes of a half that read chunk 8h + k of 16 consecutive rows hit 16
+// different bank groups.  Copy instruction j writes slots [64 j, 64 j + 64)
+// (rows 4j .. 4j+3, one contiguous KiB); the chunk a lane fetches depends on
+// j only through j mod 4.  Two more instructions copy the 128 means.  Every
+// call issues exactly 10 load instructions with all lanes active; rows past a
+// ragged tail re-read the last valid row and are never stored.  The means go
+// to slot Lo: a wave alternates between two slots, so that the copy of the
+// tile after next never writes the means the current tile is still reading.
+__device__ __forceinline__ void nsn_tile_to_lds(const u4_t *src, int nv, const float *oh, u4_t *L, u4_t *Lo, int lane)
+{
+    asm volatile("" : "+v"(lane));
+    if (nv == kTileN) {
+        uint32_t off[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int v = 4 * r + (lane >> 4);
+            off[r] = (uint32_t)((lane >> 4) * 16 + (((lane & 15) - v) & 15));
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void *)(src + 64 * j + off[j & 3]),
+                (__attribute__((address_space(3))) void *)(L + j * 64), 16, 0, 0);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int v = 4 * j + (lane >> 4);
+            const int row = v < nv ? v : nv - 1;
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void *)(src + row * 16 + (((lane & 15) - v) & 15)),
+                (__attribute__((address_space(3))) void *)(L + j * 64), 16, 0, 0);
+        }
+    }
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(oh + lane),
+                                     (__attribute__((address_space(3))) void *)(Lo), 4, 0, 0);
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(oh + 64 + lane),
+                                     (__attribute__((address_space(3))) void *)(Lo + 16), 4, 0, 0);
+}
+
+// Wait for the tile copy, read half row h of token v into w (lane 32h + v),
+// and draw the wave's next ticket (the atomic goes out with the row reads:
+// the compiler makes any LDS access wait for all copies into LDS in flight).
+__device__ __forceinline__ int nsn_take_rows(const u4_t *L, int lane, uint32_t *w, int *counter)
+{
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" : "+v"(lane));
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    const int v = lane & 31, h = lane >> 5;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const u4_t x = L[16 * v + ((8 * h + k + v) & 15)];
+        w[4 * k + 0] = x.x;
+        w[4 * k + 1] = x.y;
+        w[4 * k + 2] = x.z;
+        w[4 * k + 3] = x.w;
+    }
+    int t = 0;
+    if (lane == 0) t = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    wait_lgkm();
+    __builtin_amdgcn_wave_barrier();
+    return __builtin_amdgcn_readfirstlane(t);
+}
+
+// x' = [x_lo | y_lo], y' = [x_hi | y_hi] (gfx950 swap of lanes 32..63 of x
+// with lanes 0..31 of y)
+__device__ __forceinline__ void swap_halves(float &x, float &y)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, y),
+                                                    false, false);
+    x = __builtin_bit_cast(float, (unsigned)r[0]);
+    y = __builtin_bit_cast(float, (unsigned)r[1]);
+}
+// value of x in lane l ^ 32
+__device__ __forceinline__ float other_half(float x, bool upper)
+{
+    float p = x, q = x;
+    swap_halves(p, q);
+    return upper ? p : q;
+}
+__device__ __forceinline__ int other_half_i(int x, bool upper)
+{
+    return __builtin_bit_cast(int, other_half(__builtin_bit_cast(float, x), upper));
+}
+
 template <bool CB_LO>
-// o: channel means [H][128], a separate read-only argument so that (read
-// with a wave-uniform head) it comes through the scalar cache.
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_nsn_vq(
+// o: channel means [H][128]
+__global__ __launch_bounds__(kWavesN * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_nsn_vq(
     VqArgs a, const float *__restrict__ o, int64_t T, int H, int64_t tiles_per_h, int64_t n_tiles)
 {
-    static_assert(kVqK == 256, "one codebook entry per thread when staging");
-    __shared__ u4_t lds[4][kTile * 16];
-    __shared__ u4_t zlo[4][kTile * 16];
-    __shared__ u4_t s_cbh[kVqK];
-    __shared__ u2_t s_cbl[2 * kVqK];
-    __shared__ f4_t s_cb[2 * kVqK];
+    __shared__ u4_t s_cbA[2 * kVqK];  // entry j, half q: dims 4q .. 4q+3 of C_hi, twice
+    __shared__ u2_t s_cbl[2 * kVqK];  // lo parts, dims 4q .. 4q+3 at 2 j + q
+    __shared__ f4_t s_cb[2 * kVqK];   // fp32 codebook, dims 4q .. 4q+3 at 2 j + q
     __shared__ float s_bias[kVqK];
+    __shared__ u4_t lds[kWavesN][kBufN];
+    __shared__ int next_tile;
     const int tid = threadIdx.x;
-    s_cbh[tid] = a.cb_hi[tid];
-    if constexpr (CB_LO) {
-        s_cbl[2 * tid] = a.cb_lo[2 * tid];
-        s_cbl[2 * tid + 1] = a.cb_lo[2 * tid + 1];
+    for (int j = tid; j < kVqK; j += kWavesN * 64) {
+        const u4_t c = a.cb_hi[j];
+        s_cbA[2 * j] = u4_t{c.x, c.y, c.x, c.y};
+        s_cbA[2 * j + 1] = u4_t{c.z, c.w, c.z, c.w};
+        if constexpr (CB_LO) {
+            s_cbl[2 * j] = a.cb_lo[2 * j];
+            s_cbl[2 * j + 1] = a.cb_lo[2 * j + 1];
+        }
+        s_cb[2 * j] = reinterpret_cast<const f4_t *>(a.cb)[2 * j];
+        s_cb[2 * j + 1] = reinterpret_cast<const f4_t *>(a.cb)[2 * j + 1];
+        s_bias[j] = a.bias[j];
     }
-    s_cb[2 * tid] = reinterpret_cast<const f4_t *>(a.cb)[2 * tid];
-    s_cb[2 * tid + 1] = reinterpret_cast<const f4_t *>(a.cb)[2 * tid + 1];
-    s_bias[tid] = a.bias[tid];
+    if (tid == 0) next_tile = kWavesN;
     __syncthreads();
 
     const int lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     u4_t *L = lds[wv];
-    u4_t *Llo = zlo[wv];
-    const int half = lane >> 5, col = lane & 31;
-
-    // Each lane loads its own token's row straight into registers; the next
-    // tile's rows are requested before the current tile's search, which hides
-    // their latency (the LDS buffers then only hold the z rows).
-    const int64_t stride = (int64_t)gridDim.x * 4;
-    int64_t tile = (int64_t)blockIdx.x * 4 + wv;
-    u4_t xr[16];
-    auto load_rows = [&](int64_t t) {
-        const int64_t hq = t / tiles_per_h;
-        const int64_t tq = (t - hq * tiles_per_h) * kTile;
-        const int nq = (int)min((int64_t)kTile, T - tq);
-        const u4_t *src = a.x + (hq * T + tq + min(lane, nq - 1)) * 16;  // rows past a tail: last valid row
-#pragma unroll
-        for (int c = 0; c < 16; ++c) xr[c] = __builtin_nontemporal_load(src + c);
+    const int v = lane & 31, h = lane >> 5;
+    const bool upper = h != 0;
+    const int64_t G = gridDim.x;
+    int64_t tile = blockIdx.x + wv * G;
+    if (tile >= n_tiles) return;  // wave-uniform
+    auto issue = [&](int64_t t, int slot) {
+        int64_t tph = tiles_per_h;
+        asm volatile("" : "+s"(tph));
+        const int64_t hq = t / tph;
+        const int64_t tq = (t - hq * tph) * kTileN;
+        const int nq = (int)min((int64_t)kTileN, T - tq);
+        nsn_tile_to_lds(a.x + (hq * T + tq) * 16, nq, o + hq * kD, L, L + kRowsN + 32 * slot, lane);
     };
-    if (tile < n_tiles) load_rows(tile);
-    for (; tile < n_tiles; tile += stride) {
-        const int64_t hh = tile / tiles_per_h;
-        const int64_t t0 = (tile - hh * tiles_per_h) * kTile;
-        const int nv = (int)min((int64_t)kTile, T - t0);
-        const int h = (int)hh;
+    uint32_t w[32];
+    int ord = 0;  // ordinal of the current tile among this wave's: its means are in slot ord % 2
+    issue(tile, 0);
+    int64_t next = blockIdx.x + nsn_take_rows(L, lane, w, &next_tile) * G;
+    if (next < n_tiles) issue(next, 1);
+    for (;;) {
+        int64_t tph = tiles_per_h;
+        asm volatile("" : "+s"(tph));
+        const int64_t hh = tile / tph;
+        const int64_t t0 = (tile - hh * tph) * kTileN;
+        const int nv = (int)min((int64_t)kTileN, T - t0);
         const int64_t v0 = hh * T + t0;
-        uint32_t w[64];
-#pragma unroll
-        for (int c = 0; c < 16; ++c) {
-            w[4 * c + 0] = xr[c].x;
-            w[4 * c + 1] = xr[c].y;
-            w[4 * c + 2] = xr[c].z;
-            w[4 * c + 3] = xr[c].w;
-        }
 
-        const float ss = norm2_f16(w);
+        // ||x||^2: this half's chain, then (half 0) + (half 1) as norm2_f16
+        float ss = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 32; ++k) {
+            const h2_t p = __builtin_bit_cast(h2_t, w[k]);
+            ss = __builtin_amdgcn_fdot2(p, p, ss, false);
+        }
+        {
+            float p = ss, q = ss;
+            swap_halves(p, q);
+            ss = p + q;
+        }
         const float nx = __builtin_sqrtf(ss);
         const float inv = ss > 0.0f ? kSqrtD / nx : 0.0f;
-        const float *oh = o + __builtin_amdgcn_readfirstlane(h) * kD;
-        float y[128];
-        float nb2 = 0.0f;
+        // this half's 64 means (the slot the copy of the next tile does not write)
+        const f4_t *oL = reinterpret_cast<const f4_t *>(L + kRowsN + 32 * (ord & 1)) + 16 * h;
+        float y[64];
         {
             // a_t is rounded as in the stats pass before o is subtracted, so
             // a single token (o = a_t) gives b = 0 exactly
 #pragma clang fp contract(off)
 #pragma unroll
-            for (int k = 0; k < 64; ++k) {
-                const h2_t p = __builtin_bit_cast(h2_t, w[k]);
-                y[2 * k] = (float)p.x * inv - oh[2 * k];
-                y[2 * k + 1] = (float)p.y * inv - oh[2 * k + 1];
+            for (int k = 0; k < 16; ++k) {
+                const f4_t ov = oL[k];
+                const h2_t p0 = __builtin_bit_cast(h2_t, w[2 * k]), p1 = __builtin_bit_cast(h2_t, w[2 * k + 1]);
+                y[4 * k] = (float)p0.x * inv - ov.x;
+                y[4 * k + 1] = (float)p0.y * inv - ov.y;
+                y[4 * k + 2] = (float)p1.x * inv - ov.z;
+                y[4 * k + 3] = (float)p1.y * inv - ov.w;
             }
         }
+        float nb2 = 0.0f;
 #pragma unroll
-        for (int k = 0; k < 128; ++k) nb2 = fmaf(y[k], y[k], nb2);
+        for (int k = 0; k < 64; ++k) nb2 = fmaf(y[k], y[k], nb2);
+        {
+            float p = nb2, q = nb2;
+            swap_halves(p, q);
+            nb2 = p + q;
+        }
 #pragma unroll
-        for (int st = 1; st < 128; st <<= 1) {
+        for (int st = 1; st < 64; st <<= 1) {
 #pragma unroll
-            for (int i = 0; i < 128; i += 2 * st) {
+            for (int i = 0; i < 64; i += 2 * st) {
 #pragma unroll
                 for (int j = i; j < i + st; ++j) {
                     const float p0 = y[j], p1 = y[j + st];
@@ -287,128 +411,146 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 }
             }
         }
+        // stride-64 stage: register p = 8t + k (k < 4) with q = p + 4
+#pragma unroll
+        for (int p = 0; p < 64; ++p) {
+            if ((p & 4) != 0) continue;
+            float x0 = y[p], x1 = y[p + 4];
+            swap_halves(x0, x1);
+            y[p] = x0 + x1;
+            y[p + 4] = x0 - x1;
+        }
         const float nb = __builtin_sqrtf(nb2);
         const float invb = nb2 > 0.0f ? 1.0f / nb : 0.0f;
-        // z = H b / ||b||, staged as fp16 hi / lo rows
+        // z = H b / ||b||: this half's four dims of each sub-vector as exact
+        // fp16 hi + lo
+        u2_t zh[16], zl[16];
 #pragma unroll
-        for (int c = 0; c < 16; ++c) {
-            h8_t hv, lv;
+        for (int s = 0; s < 16; ++s) {
+            const int base = 8 * (s & 7) + 4 * (s >> 3);
+            h4_t hv, lv;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
+            for (int j = 0; j < 4; ++j) {
                 _Float16 lo;
-                hv[j] = split_f16(y[8 * c + j] * invb, lo);
+                hv[j] = split_f16(y[base + j] * invb, lo);
                 lv[j] = lo;
             }
-            L[swz(lane, c)] = __builtin_bit_cast(u4_t, hv);
-            Llo[swz(lane, c)] = __builtin_bit_cast(u4_t, lv);
+            zh[s] = __builtin_bit_cast(u2_t, hv);
+            zl[s] = __builtin_bit_cast(u2_t, lv);
+            // opaque: the resolve below must convert from these packed
+            // registers, not keep unpacked copies live through the search
+            asm volatile("" : "+v"(zh[s]), "+v"(zl[s]));
         }
-        wait_lgkm();
-        __builtin_amdgcn_wave_barrier();
-        if (tile + stride < n_tiles) load_rows(tile + stride);
 
-        uint32_t code[4] = {0u, 0u, 0u, 0u};  // codes of token `lane` (sub-vector s in byte s)
+        float bm[16];
+        int bg[16];
+#pragma unroll
+        for (int s = 0; s < 16; ++s) {
+            bm[s] = -INFINITY;
+            bg[s] = 0;
+        }
 #pragma unroll 1
-        for (int tb = 0; tb < 2; ++tb) {
-            const int row = 32 * tb + col;  // token of this lane's column
-            const u4_t *Lz = half ? Llo : L;  // B of the x16 pass: z_hi (k < 8) or z_lo (k >= 8)
-            float bm[16];
-            int bg[16];
+        for (int mb = 0; mb < 8; ++mb) {
+            const int ent = 32 * mb + v;  // codeword row of this lane's A operand
+            const h8_t A16 = __builtin_bit_cast(h8_t, s_cbA[2 * ent + h]);
+            h4_t A8 = {};
+            if constexpr (CB_LO) A8 = __builtin_bit_cast(h4_t, s_cbl[2 * ent + h]);
+            // accumulator rows of this lane: codeword 32 mb + 8 (r/4) + 4 h + r%4
+            f16v_t bias;
 #pragma unroll
-            for (int s = 0; s < 16; ++s) {
-                bm[s] = -INFINITY;
-                bg[s] = 0;
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const f4_t bq = reinterpret_cast<const f4_t *>(s_bias)[(32 * mb + 8 * r4 + 4 * h) >> 2];
+                bias[4 * r4] = bq.x;
+                bias[4 * r4 + 1] = bq.y;
+                bias[4 * r4 + 2] = bq.z;
+                bias[4 * r4 + 3] = bq.w;
             }
-#pragma unroll 1
-            for (int mb = 0; mb < 8; ++mb) {
-                const int ent = 32 * mb + col;  // codeword row of this lane's A operand
-                const h8_t A16 = __builtin_bit_cast(h8_t, s_cbh[ent]);
-                h4_t A8 = {};
-                if constexpr (CB_LO) A8 = __builtin_bit_cast(h4_t, s_cbl[2 * ent + half]);
-                // accumulator rows of this lane: codeword 32 mb + 8 (r/4) + 4 half + r%4
-                f16v_t bias;
+            // four sub-vectors at a time in independent accumulators, so that
+            // the matrix cores run while earlier results are scanned
 #pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4) {
-                    const f4_t bq = reinterpret_cast<const f4_t *>(s_bias)[(32 * mb + 8 * r4 + 4 * half) >> 2];
-                    bias[4 * r4] = bq.x;
-                    bias[4 * r4 + 1] = bq.y;
-                    bias[4 * r4 + 2] = bq.z;
-                    bias[4 * r4 + 3] = bq.w;
+            for (int s4 = 0; s4 < 16; s4 += 4) {
+                f16v_t acc[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const u2_t zhs = zh[s4 + u], zls = zl[s4 + u];
+                    const h8_t B16 = __builtin_bit_cast(h8_t, u4_t{zhs.x, zhs.y, zls.x, zls.y});
+                    acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A16, B16, bias, 0, 0, 0);
                 }
-                // four sub-vectors at a time in independent accumulators, so
-                // that the matrix cores run while earlier results are scanned
+                if constexpr (CB_LO) {
 #pragma unroll
-                for (int s4 = 0; s4 < 16; s4 += 4) {
-                    f16v_t acc[4];
+                    for (int u = 0; u < 4; ++u)
+                        acc[u] = __builtin_amdgcn_mfma_f32_32x32x8f16(A8, __builtin_bit_cast(h4_t, zh[s4 + u]),
+                                                                      acc[u], 0, 0, 0);
+                }
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const h8_t B16 = __builtin_bit_cast(h8_t, Lz[swz(row, s4 + u)]);
-                        acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A16, B16, bias, 0, 0, 0);
-                    }
-                    if constexpr (CB_LO) {
+                for (int u = 0; u < 4; ++u) {
+                    const int s = s4 + u;
 #pragma unroll
-                        for (int u = 0; u < 4; ++u) {
-                            const h4_t B8 =
-                                __builtin_bit_cast(h4_t, reinterpret_cast<const u2_t *>(L + swz(row, s4 + u))[half]);
-                            acc[u] = __builtin_amdgcn_mfma_f32_32x32x8f16(A8, B8, acc[u], 0, 0, 0);
-                        }
-                    }
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const int s = s4 + u;
-#pragma unroll
-                        for (int r4 = 0; r4 < 4; ++r4) {
-                            const float m = max4(acc[u][4 * r4], acc[u][4 * r4 + 1], acc[u][4 * r4 + 2], acc[u][4 * r4 + 3]);
-                            const bool better = m > bm[s];
-                            bm[s] = better ? m : bm[s];
-                            bg[s] = better ? 4 * mb + r4 : bg[s];
-                        }
+                    for (int r4 = 0; r4 < 4; ++r4) {
+                        const float m = max4(acc[u][4 * r4], acc[u][4 * r4 + 1], acc[u][4 * r4 + 2], acc[u][4 * r4 + 3]);
+                        const bool better = m > bm[s];
+                        bm[s] = better ? m : bm[s];
+                        bg[s] = better ? 4 * mb + r4 : bg[s];
                     }
                 }
-            }
-            // resolve the best group of each sub-vector in fp32, then merge with
-            // the lane holding the other half of every codeword block
-#pragma unroll
-            for (int s = 0; s < 16; ++s) {
-                const h8_t zh = __builtin_bit_cast(h8_t, L[swz(row, s)]);
-                const h8_t zl = __builtin_bit_cast(h8_t, Llo[swz(row, s)]);
-                float z[8];
-#pragma unroll
-                for (int t = 0; t < 8; ++t) z[t] = (float)zh[t] + (float)zl[t];
-                const int g = bg[s];
-                const int j0 = 32 * (g >> 2) + 8 * (g & 3) + 4 * half;
-                float best = -INFINITY;
-                int bi = j0;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int j = j0 + r;
-                    const f4_t c0 = s_cb[2 * j], c1 = s_cb[2 * j + 1];
-                    float sc = s_bias[j];
-                    sc = fmaf(z[0], c0.x, sc);
-                    sc = fmaf(z[1], c0.y, sc);
-                    sc = fmaf(z[2], c0.z, sc);
-                    sc = fmaf(z[3], c0.w, sc);
-                    sc = fmaf(z[4], c1.x, sc);
-                    sc = fmaf(z[5], c1.y, sc);
-                    sc = fmaf(z[6], c1.z, sc);
-                    sc = fmaf(z[7], c1.w, sc);
-                    const bool better = sc > best;  // increasing index: strict > keeps the lowest
-                    best = better ? sc : best;
-                    bi = better ? j : bi;
-                }
-                const float ob = __shfl_xor(best, 32);
-                const int oi = __shfl_xor(bi, 32);
-                const int win = (ob > best || (ob == best && oi < bi)) ? oi : bi;
-                if (half == tb) code[s >> 2] |= (uint32_t)win << (8 * (s & 3));
             }
         }
-        if (lane < nv) {
-            const int64_t v = v0 + lane;
-            u4_t cv = {code[0], code[1], code[2], code[3]};
-            a.codes[v] = cv;
-            a.s1[v] = nx / kSqrtD;
-            a.s2[v] = nb / kSqrtD;
+        // resolve the best group of each sub-vector in fp32, then merge with
+        // the other half (which searched the other 16 codewords of each block)
+        uint32_t code[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int s = 0; s < 16; ++s) {
+            const h4_t zhs = __builtin_bit_cast(h4_t, zh[s]), zls = __builtin_bit_cast(h4_t, zl[s]);
+            float zo[4], zp[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) zo[t] = (float)zhs[t] + (float)zls[t];  // dims 4h + t
+#pragma unroll
+            for (int t = 0; t < 4; ++t) zp[t] = other_half(zo[t], upper);        // dims 4(1-h) + t
+            const int g = bg[s];
+            const int j0 = 32 * (g >> 2) + 8 * (g & 3) + 4 * h;
+            float best = -INFINITY;
+            int bi = j0;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int j = j0 + r;
+                const f4_t co = s_cb[2 * j + h], cp = s_cb[2 * j + 1 - h];
+                float sc = s_bias[j];
+                sc = fmaf(zo[0], co.x, sc);
+                sc = fmaf(zo[1], co.y, sc);
+                sc = fmaf(zo[2], co.z, sc);
+                sc = fmaf(zo[3], co.w, sc);
+                sc = fmaf(zp[0], cp.x, sc);
+                sc = fmaf(zp[1], cp.y, sc);
+                sc = fmaf(zp[2], cp.z, sc);
+                sc = fmaf(zp[3], cp.w, sc);
+                const bool better = sc > best;  // increasing index: strict > keeps the lowest
+                best = better ? sc : best;
+                bi = better ? j : bi;
+            }
+            const float ob = other_half(best, upper);
+            const int oi = other_half_i(bi, upper);
+            const int win = (ob > best || (ob == best && oi < bi)) ? oi : bi;
+            code[s >> 2] |= (uint32_t)win << (8 * (s & 3));
         }
-        __builtin_amdgcn_wave_barrier();
+        // The next tile's rows, then the copy of the tile after it, then this
+        // tile's stores.  The rows are read only now: held through the search
+        // they would not fit in the registers.
+        const bool has_next = next < n_tiles;
+        int64_t after = n_tiles;
+        if (has_next) {
+            after = blockIdx.x + nsn_take_rows(L, lane, w, &next_tile) * G;
+            if (after < n_tiles) issue(after, ord & 1);  // the slot of this tile, no longer read
+        }
+        if (!upper && v < nv) {  // lanes of tokens past a ragged tail searched stale rows
+            const int64_t t = v0 + v;
+            a.codes[t] = u4_t{code[0], code[1], code[2], code[3]};
+            a.s1[t] = nx / kSqrtD;
+            a.s2[t] = nb / kSqrtD;
+        }
+        if (!has_next) break;
+        tile = next;
+        next = after;
+        ++ord;
     }
 }
 
@@ -437,16 +579,17 @@ hipError_t launch_nsn_vq(const kvq_ctx *ctx, const void *x, int64_t H, int64_t T
     a.codes = (u4_t *)codes;
     a.s1 = s1;
     a.s2 = s2;
-    const int64_t tiles_per_h = (T + kTile - 1) / kTile;
+    const int64_t tiles_per_h = (T + kTileN - 1) / kTileN;
     const int64_t n_tiles = tiles_per_h * H;
-    int64_t blocks = (n_tiles + 3) / 4;
+    // one workgroup per CU, each with at least one tile
+    int64_t blocks = n_tiles;
     if (blocks > ctx->n_cu) blocks = ctx->n_cu;
     if (ctx->vq_exact_f16)
-        hipLaunchKernelGGL(k_nsn_vq<false>, dim3((unsigned)blocks), dim3(256), 0, s, a, (const float *)o, T, (int)H,
-                           tiles_per_h, n_tiles);
+        hipLaunchKernelGGL(k_nsn_vq<false>, dim3((unsigned)blocks), dim3(kWavesN * 64), 0, s, a, (const float *)o, T,
+                           (int)H, tiles_per_h, n_tiles);
     else
-        hipLaunchKernelGGL(k_nsn_vq<true>, dim3((unsigned)blocks), dim3(256), 0, s, a, (const float *)o, T, (int)H,
-                           tiles_per_h, n_tiles);
+        hipLaunchKernelGGL(k_nsn_vq<true>, dim3((unsigned)blocks), dim3(kWavesN * 64), 0, s, a, (const float *)o, T,
+                           (int)H, tiles_per_h, n_tiles);
     return hipGetLastError();
 }
 
