@@ -188,7 +188,13 @@ kvq_status kvq_create(const kvq_config *cfg, kvq_ctx **out)
             if ((float)lo != 0.0f) exact = false;
         }
         c->S_exact_f16 = exact;
-        if (st == KVQ_OK) st = upload(&c->d_S, cfg->qjl_S, n);
+        // fp32 S transposed for the query projection of the score kernels
+        float *st_t = st == KVQ_OK ? (float *)std::malloc(n * sizeof(float)) : nullptr;
+        if (st == KVQ_OK && !st_t) st = KVQ_E_NOMEM;
+        for (int i = 0; st == KVQ_OK && i < kvq::kD; ++i)
+            for (int j = 0; j < kvq::kD; ++j) st_t[i * kvq::kD + j] = cfg->qjl_S[j * kvq::kD + i];
+        if (st == KVQ_OK) st = upload(&c->d_S, st_t, n);
+        std::free(st_t);
         if (st == KVQ_OK) st = upload(&c->d_S16, s16, 2 * n);
         std::free(s16);
     }

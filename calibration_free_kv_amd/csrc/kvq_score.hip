@@ -124,38 +124,10 @@ __device__ __forceinline__ void stage_centroids(const Codebook &cb, float *ctab)
 }
 
 // Sum of the table entries of one record for the G heads (the G entries of a
-// (field, value) pair are read with one 16- or 8-byte LDS load).
-template <int BITS, int G>
-__device__ __forceinline__ void score_record(const uint32_t *Wd, const float *lut, float *acc)
-{
-    using FD = Fields<BITS>;
-#pragma unroll
-    for (int h = 0; h < G; ++h) acc[h] = 0.0f;
-#pragma unroll
-    for (int f = 0; f < FD::NF; ++f) {
-        const int e = f * FD::E + (int)field<BITS>(Wd, f);
-        if constexpr (G % 4 == 0) {
-#pragma unroll
-            for (int h4 = 0; h4 < G / 4; ++h4) {
-                const f4_t x = reinterpret_cast<const f4_t *>(lut)[e * (G / 4) + h4];
-                acc[4 * h4] += x.x;
-                acc[4 * h4 + 1] += x.y;
-                acc[4 * h4 + 2] += x.z;
-                acc[4 * h4 + 3] += x.w;
-            }
-        } else if constexpr (G == 2) {
-            const f2_t x = reinterpret_cast<const f2_t *>(lut)[e];
-            acc[0] += x.x;
-            acc[1] += x.y;
-        } else {
-            acc[0] += lut[e];
-        }
-    }
-}
-
-// score_record in groups of 8 fields: the scheduler may not move address
-// computations or reads across groups, so at most 8 entries are in flight
-// (all 64 at once would not fit in the registers of a wave).
+// (field, value) pair are read with one 16- or 8-byte LDS load), in groups of
+// 8 fields: the scheduler may not move address computations or reads across
+// groups, so at most 8 entries are in flight (all 64 at once would not fit
+// in the registers of a wave).
 template <int BITS, int G>
 __device__ __forceinline__ void score_record_grouped(const uint32_t *Wd, const float *lut, float *acc)
 {
@@ -206,11 +178,16 @@ __device__ __forceinline__ void load_record(const uint8_t *codes, int64_t v, uin
 // QJL: + rho gamma sqrt(pi/2)/m sum_j (2 sgn_j - 1) p_h[j], p_h = S q'_h / sqrt(d),
 // read through a second table over the 32 nibbles of the 128 sign bits.
 // ---------------------------------------------------------------------------
+// One block of 16 waves per (batch, KV head, token range), about one block per
+// CU: the prologue (tables, and for QJL the projection of the G queries) is
+// built by 1024 threads and amortised over a long range.
+constexpr int kLgThreads = 1024;
+
 template <int BITS, int G, bool QJL>
-__global__ __launch_bounds__(kThreads) void k_logits(
+__global__ __launch_bounds__(kLgThreads) void k_logits(
     const half_t *__restrict__ q, const uint8_t *__restrict__ codes, const float *__restrict__ norms,
     const uint32_t *__restrict__ qjl_signs, const float *__restrict__ qjl_gamma,
-    const float *__restrict__ signs, const float *__restrict__ S, Codebook cb,
+    const float *__restrict__ signs, const float *__restrict__ St, Codebook cb,
     float *__restrict__ logits, int64_t T, int H, int Hq, int64_t tokens_per_block,
     int64_t blocks_per_bh)
 {
@@ -231,16 +208,20 @@ __global__ __launch_bounds__(kThreads) void k_logits(
     rotate_queries<G>(q, signs, b, g, Hq, qr);
     build_tables<BITS, G>(qr, ctab, lut);
     if constexpr (QJL) {
+        // p_h[j] = sum_i S[j][i] q'_h[i] / sqrt(d): thread (h, j) walks row i of
+        // S^T, so that the 128 threads of a head read 512 contiguous bytes per
+        // step; the steps are unrolled to keep many loads in flight
         const float inv_sqrt_d = 0.08838834764831845f;
-        for (int idx = threadIdx.x; idx < G * kD; idx += kThreads) {
+        for (int idx = threadIdx.x; idx < G * kD; idx += kLgThreads) {
             const int h = idx >> 7, j = idx & (kD - 1);
             float s = 0.0f;
-            for (int i = 0; i < kD; ++i) s += S[j * kD + i] * qr[h * kD + i];
+#pragma unroll 16
+            for (int i = 0; i < kD; ++i) s = fmaf(St[i * kD + j], qr[h * kD + i], s);
             pq[idx] = s * inv_sqrt_d;
         }
         __syncthreads();
         const float coef = 1.2533141373155003f / kD;  // sqrt(pi/2) / m
-        for (int idx = threadIdx.x; idx < 32 * 16 * G; idx += kThreads) {
+        for (int idx = threadIdx.x; idx < 32 * 16 * G; idx += kLgThreads) {
             const int h = idx % G, e = (idx / G) & 15, f = idx / (16 * G);
             float v = 0.0f;
 #pragma unroll
@@ -252,26 +233,45 @@ __global__ __launch_bounds__(kThreads) void k_logits(
 
     const int64_t t_begin = part * tokens_per_block;
     const int64_t t_end = min(T, t_begin + tokens_per_block);
-    for (int64_t t = t_begin + threadIdx.x; t < t_end; t += kThreads) {
-        const int64_t v = bh * T + t;
-        uint32_t Wd[FD::W + 1];
-        load_record<BITS>(codes, v, Wd);
-        float acc[G];
-        score_record<BITS, G>(Wd, lut, acc);
-        const float rho = norms[v];
+    // Register prefetch: a thread loads its next token's records before it
+    // scores the current one.  The loads are unconditional (indexes past the
+    // range re-read its last token), so the compiler's wait before the scoring
+    // counts exactly the prefetch loads issued after them.
+    uint32_t Wn[FD::W + 1];
+    float rn = 0.0f, gn = 0.0f;
+    u4_t sn = {};
+    auto fetch = [&](int64_t t) {
+        const int64_t v = bh * T + min(t, t_end - 1);
+        load_record<BITS>(codes, v, Wn);
+        rn = norms[v];
         if constexpr (QJL) {
-            const u4_t sg = reinterpret_cast<const u4_t *>(qjl_signs)[v];
+            sn = reinterpret_cast<const u4_t *>(qjl_signs)[v];
+            gn = qjl_gamma[v];
+        }
+    };
+    int64_t t = t_begin + threadIdx.x;
+    fetch(t);
+    for (; t < t_end; t += kLgThreads) {
+        uint32_t Wd[FD::W + 1];
+#pragma unroll
+        for (int k = 0; k <= FD::W; ++k) Wd[k] = Wn[k];
+        const float rho = rn, gm = gn;
+        const u4_t sg = sn;
+        fetch(t + kLgThreads);
+        float acc[G];
+        score_record_grouped<BITS, G>(Wd, lut, acc);
+        if constexpr (QJL) {
             const uint32_t sw[4] = {sg.x, sg.y, sg.z, sg.w};
             float qa[G];
 #pragma unroll
             for (int h = 0; h < G; ++h) qa[h] = 0.0f;
 #pragma unroll
             for (int f = 0; f < 32; ++f) {
+                if (f % 8 == 0) __builtin_amdgcn_sched_barrier(0);  // at most 8 entries in flight
                 const float *e = slut + (f * 16 + (int)((sw[f >> 3] >> (4 * (f & 7))) & 15u)) * G;
 #pragma unroll
                 for (int h = 0; h < G; ++h) qa[h] += e[h];
             }
-            const float gm = qjl_gamma[v];
 #pragma unroll
             for (int h = 0; h < G; ++h) acc[h] = fmaf(gm, qa[h], acc[h]);
         }
@@ -742,10 +742,10 @@ hipError_t run_logits(const kvq_ctx *ctx, const void *q, int64_t B, int64_t Hq, 
 {
     using FD = Fields<BITS>;
     const int64_t bhs = B * ctx->H;
-    // enough blocks to fill the chip, but at least 1024 tokens per block to
-    // amortise the table build
+    // about one block per CU, and at least 1024 tokens per block to amortise
+    // the prologue
     int64_t per = (T + 1023) / 1024;
-    const int64_t want = (2048 + bhs - 1) / bhs;
+    const int64_t want = ((int64_t)ctx->n_cu + bhs - 1) / bhs;
     if (per > want) per = want;
     if (per < 1) per = 1;
     const int64_t tpb = (T + per - 1) / per;
@@ -757,7 +757,7 @@ hipError_t run_logits(const kvq_ctx *ctx, const void *q, int64_t B, int64_t Hq, 
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
         attr_set = true;
     }
-    hipLaunchKernelGGL((k_logits<BITS, G, QJL>), dim3((unsigned)(bhs * blocks_per_bh)), dim3(kThreads), shm,
+    hipLaunchKernelGGL((k_logits<BITS, G, QJL>), dim3((unsigned)(bhs * blocks_per_bh)), dim3(kLgThreads), shm,
                        s, (const half_t *)q, codes, norms, (const uint32_t *)qjl_signs, qjl_gamma,
                        ctx->d_signs, ctx->d_S, ctx->cb, logits, T, ctx->H, (int)Hq, tpb, blocks_per_bh);
     return hipGetLastError();
