@@ -107,6 +107,15 @@ def test_nsn_vq_full_size_sampled():
     print(compare(x, cb, g, t_sel=t_sel, o_ref=o_ref))
 
 
+def test_nsn_vq_multi_tile_all_tokens():
+    """Every token of 8 heads x 20000: about 5000 tiles of 32 tokens for 2048
+    waves, so most waves encode several tiles, some of them across a head
+    boundary (each tile carries its head's channel means)."""
+    x = synth.make("nsn_vq", T=20000)["x"]
+    cb = codebook()
+    print(compare(x, cb, run(x, cb)))
+
+
 def test_nsn_vq_deterministic():
     x = synth.make("nsn_vq", T=3000)["x"]
     cb = codebook()
