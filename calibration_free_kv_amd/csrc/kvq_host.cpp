@@ -80,7 +80,18 @@ void free_ctx(kvq_ctx *c)
     (void)hipFree(c->d_vq);
     (void)hipFree(c->d_vq16);
     (void)hipFree(c->d_vqbias);
+    std::free(c->h_signs);
     delete c;
+}
+
+// SplitMix64 (Steele, Lea and Flood 2014): output n (counting from 0) of the
+// generator seeded with `seed`.
+uint64_t splitmix64(uint64_t seed, uint64_t n)
+{
+    uint64_t z = seed + (n + 1) * 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
 }
 
 template <class T>
@@ -124,10 +135,9 @@ kvq_status kvq_create(const kvq_config *cfg, kvq_ctx **out)
     const int H = cfg->n_kv_heads;
     if (mode != KVQ_MODE_NSN_VQ) {
         if (cfg->bits < 1 || cfg->bits > 4) return KVQ_E_INVAL;
-        if (!cfg->signs_k || !cfg->signs_v) return KVQ_E_INVAL;
         for (int i = 0; i < H * kvq::kD; ++i) {
-            if (cfg->signs_k[i] != 1 && cfg->signs_k[i] != -1) return KVQ_E_INVAL;
-            if (cfg->signs_v[i] != 1 && cfg->signs_v[i] != -1) return KVQ_E_INVAL;
+            if (cfg->signs_k && cfg->signs_k[i] != 1 && cfg->signs_k[i] != -1) return KVQ_E_INVAL;
+            if (cfg->signs_v && cfg->signs_v[i] != 1 && cfg->signs_v[i] != -1) return KVQ_E_INVAL;
         }
     }
     if (mode == KVQ_MODE_MSE_QJL && !cfg->qjl_S) return KVQ_E_INVAL;
@@ -156,12 +166,16 @@ kvq_status kvq_create(const kvq_config *cfg, kvq_ctx **out)
         const size_t n = (size_t)H * kvq::kD;
         uint32_t *mask = (uint32_t *)std::calloc(2 * n / 2, sizeof(uint32_t));
         float *sg = (float *)std::malloc(2 * n * sizeof(float));
-        if (!mask || !sg) st = KVQ_E_NOMEM;
+        c->h_signs = (int8_t *)std::malloc(2 * n);
+        if (!mask || !sg || !c->h_signs) st = KVQ_E_NOMEM;
         for (int kind = 0; st == KVQ_OK && kind < 2; ++kind) {
             const int8_t *src = kind ? cfg->signs_v : cfg->signs_k;
+            int8_t *dst = c->h_signs + kind * n;
+            for (size_t i = 0; i < n; ++i)
+                dst[i] = src ? src[i] : ((splitmix64(cfg->seed, ((uint64_t)kind << 32) + i) >> 63) ? -1 : 1);
             for (size_t i = 0; i < n; ++i) {
-                sg[kind * n + i] = (float)src[i];
-                if (src[i] < 0) mask[(kind * n + i) / 2] |= (i & 1) ? 0x80000000u : 0x8000u;
+                sg[kind * n + i] = (float)dst[i];
+                if (dst[i] < 0) mask[(kind * n + i) / 2] |= (i & 1) ? 0x80000000u : 0x8000u;
             }
         }
         if (st == KVQ_OK) st = upload(&c->d_sgnmask, mask, n);
@@ -240,12 +254,17 @@ kvq_status kvq_destroy(kvq_ctx *ctx)
     return KVQ_OK;
 }
 
-kvq_status kvq_get_tables(const kvq_ctx *ctx, float *centroids, float *thresholds)
+kvq_status kvq_get_tables(const kvq_ctx *ctx, float *centroids, float *thresholds, int8_t *signs_k,
+                          int8_t *signs_v)
 {
     if (!ctx) return KVQ_E_INVAL;
+    if ((signs_k || signs_v) && !ctx->h_signs) return KVQ_E_INVAL;
     const int L = 1 << ctx->bits;
+    const size_t n = (size_t)ctx->H * kvq::kD;
     if (centroids) std::memcpy(centroids, ctx->cb.c, L * sizeof(float));
     if (thresholds) std::memcpy(thresholds, ctx->cb.t, (L - 1) * sizeof(float));
+    if (signs_k) std::memcpy(signs_k, ctx->h_signs, n);
+    if (signs_v) std::memcpy(signs_v, ctx->h_signs + n, n);
     return KVQ_OK;
 }
 

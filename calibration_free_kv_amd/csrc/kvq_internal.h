@@ -31,6 +31,7 @@ struct kvq_ctx {
     uint32_t *d_sgnmask;  // [2][H][64]: fp16-pair sign masks of D_K, D_V
     uint32_t *d_sgnmask_h;  // same, masks of coordinates 64..127 also flipping every sign
     float *d_signs;       // [2][H][128]: D_K, D_V as +-1.0f
+    int8_t *h_signs;      // host copy [2][H][128] of D_K, D_V (MSE modes)
     float *d_S;           // [128][128] QJL projection transposed, d_S[i][j] = S[j][i] (MSE_QJL)
     _Float16 *d_S16;      // [2][128][128] fp16 hi and lo parts of S (MSE_QJL)
     bool S_exact_f16;     // S_lo == 0

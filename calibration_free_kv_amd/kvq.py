@@ -37,7 +37,7 @@ class KvqError(RuntimeError):
 class kvq_config(C.Structure):
     _fields_ = [
         ("d", C.c_int32), ("bits", C.c_int32), ("mode", C.c_int32), ("n_kv_heads", C.c_int32),
-        ("signs_k", C.POINTER(C.c_int8)), ("signs_v", C.POINTER(C.c_int8)),
+        ("seed", C.c_uint64), ("signs_k", C.POINTER(C.c_int8)), ("signs_v", C.POINTER(C.c_int8)),
         ("qjl_S", C.POINTER(C.c_float)), ("vq_codebook", C.POINTER(C.c_float)),
         ("device", C.c_int32),
     ]
@@ -57,7 +57,7 @@ def lib():
         vp, i64, i32, sz = C.c_void_p, C.c_int64, C.c_int32, C.c_size_t
         L.kvq_create.argtypes = [C.POINTER(kvq_config), C.POINTER(vp)]
         L.kvq_destroy.argtypes = [vp]
-        L.kvq_get_tables.argtypes = [vp, vp, vp]
+        L.kvq_get_tables.argtypes = [vp, vp, vp, vp, vp]
         L.kvq_codebook.argtypes = [i32, vp, vp]
         L.kvq_code_bytes_per_vec.argtypes = [vp]
         L.kvq_code_bytes_per_vec.restype = i64
@@ -117,13 +117,15 @@ def _dev_tensor(t, dtype, name):
 class Context:
     """A libkvq context (kvq_create/kvq_destroy) holding the b-bit tables, the
     random-sign diagonals of K and V per KV head, the QJL projection and the
-    NSN codebook, resident on one GPU."""
+    NSN codebook, resident on one GPU.  A diagonal left as None is generated
+    by the library from `seed` (SplitMix64, as kvq.h specifies)."""
 
     def __init__(self, n_kv_heads: int, bits: int = 3, signs_k=None, signs_v=None, mode: int = KVQ_MODE_MSE,
-                 qjl_S=None, vq_codebook=None, device: int = 0):
+                 qjl_S=None, vq_codebook=None, device: int = 0, seed: int = 0):
         self.n_kv_heads, self.bits, self.mode, self.device = n_kv_heads, bits, mode, device
         cfg = kvq_config()
         cfg.d, cfg.bits, cfg.mode, cfg.n_kv_heads, cfg.device = D, bits, mode, n_kv_heads, device
+        cfg.seed = seed
         keep = []
 
         def arr(a, dt, cty):
@@ -160,9 +162,17 @@ class Context:
         L = 1 << self.bits
         c = np.zeros(L, np.float32)
         t = np.zeros(L - 1, np.float32)
-        _check(lib().kvq_get_tables(self.handle, c.ctypes.data_as(C.c_void_p), t.ctypes.data_as(C.c_void_p)),
-               "kvq_get_tables")
+        _check(lib().kvq_get_tables(self.handle, c.ctypes.data_as(C.c_void_p), t.ctypes.data_as(C.c_void_p),
+                                    None, None), "kvq_get_tables")
         return c, t
+
+    def signs(self):
+        """The int8 +-1 diagonals (signs_k, signs_v) [H_kv, 128] the context uses."""
+        sk = np.zeros((self.n_kv_heads, D), np.int8)
+        sv = np.zeros((self.n_kv_heads, D), np.int8)
+        _check(lib().kvq_get_tables(self.handle, None, None, sk.ctypes.data_as(C.c_void_p),
+                                    sv.ctypes.data_as(C.c_void_p)), "kvq_get_tables")
+        return sk, sv
 
     def code_bytes(self) -> int:
         return int(lib().kvq_code_bytes_per_vec(self.handle))

@@ -69,14 +69,28 @@ typedef enum {
 enum { KVQ_MODE_MSE = 0, KVQ_MODE_MSE_QJL = 1, KVQ_MODE_NSN_VQ = 2 };
 enum { KVQ_KIND_K = 0, KVQ_KIND_V = 1 };
 
-/* Configuration of a context.  Host arrays are copied by kvq_create. */
+/* Configuration of a context.  Host arrays are copied by kvq_create.
+ *
+ * The random-sign diagonal D of the rotation ([PQ] sec. 2, randomized
+ * Hadamard transform: a random +-1 diagonal before H) is chosen per tensor
+ * (K, V) and per KV head.  In the MSE modes a non-NULL signs_k / signs_v gives
+ * it explicitly; a NULL one is generated from `seed` with SplitMix64 (Steele,
+ * Lea and Flood, "Fast splittable pseudorandom number generators", 2014):
+ * output n of the generator is mix64(seed + (n + 1) * 0x9E3779B97F4A7C15)
+ * with mix64(z) = z' ^ (z' >> 31), z' the result of
+ * z ^= z >> 30; z *= 0xBF58476D1CE4E5B9; z ^= z >> 27; z *= 0x94D049BB133111EB
+ * (all arithmetic mod 2^64), and coordinate i of head h of tensor kind
+ * (KVQ_KIND_K = 0, KVQ_KIND_V = 1) takes sign -1 when the top bit of output
+ * n = kind * 2^32 + h * d + i is set, else +1.  kvq_get_tables returns the
+ * signs a context uses. */
 typedef struct {
     int32_t d;                 /* head dimension; must be 128                         */
     int32_t bits;              /* MSE code width b in {1,2,3,4} (MSE, MSE_QJL modes)  */
     int32_t mode;              /* KVQ_MODE_*                                          */
     int32_t n_kv_heads;        /* H_kv >= 1                                           */
-    const int8_t *signs_k;     /* host [n_kv_heads, d], entries +1/-1: D of K  (MSE*) */
-    const int8_t *signs_v;     /* host [n_kv_heads, d], entries +1/-1: D of V  (MSE*) */
+    uint64_t seed;             /* seed of D where signs_k or signs_v is NULL         */
+    const int8_t *signs_k;     /* host [n_kv_heads, d], entries +1/-1: D of K, or NULL */
+    const int8_t *signs_v;     /* host [n_kv_heads, d], entries +1/-1: D of V, or NULL */
     const float *qjl_S;        /* host [d, d] row-major Gaussian projection (MSE_QJL) */
     const float *vq_codebook;  /* host [256, 8] fp32 codebook (NSN_VQ)                */
     int32_t device;            /* HIP device ordinal                                  */
@@ -95,9 +109,14 @@ kvq_status kvq_create(const kvq_config *cfg, kvq_ctx **out);
  * The caller must not destroy a context while its work is in flight. */
 kvq_status kvq_destroy(kvq_ctx *ctx);
 
-/* Copy the context's fp32 tables to host memory: centroids [2^b],
- * thresholds [2^b - 1] (either pointer may be NULL). */
-kvq_status kvq_get_tables(const kvq_ctx *ctx, float *centroids, float *thresholds);
+/* Copy the context's tables to host memory: the fp32 Lloyd-Max centroids
+ * [2^b] and thresholds [2^b - 1] ([PQ] sec. 2), and the int8 +-1 diagonals
+ * of D for K and V, [n_kv_heads, d] each ([PQ] sec. 2, randomized Hadamard
+ * transform), whether given or generated from the seed.  Any output pointer
+ * may be NULL.  Errors: KVQ_E_INVAL for a NULL context, or a sign output in
+ * the NSN_VQ mode (which has no D). */
+kvq_status kvq_get_tables(const kvq_ctx *ctx, float *centroids, float *thresholds, int8_t *signs_k,
+                          int8_t *signs_v);
 
 /* The fp32 tables of a bit width without a context or a device: centroids
  * [2^b] and thresholds [2^b - 1] of the N(0,1) Lloyd-Max quantiser, exactly

@@ -3,7 +3,8 @@
 Only the tests, the smoke check and the benchmark's CPU-baseline leg use this
 package.  It wraps ``kvq_oracle.c`` (plain C, IEEE double) through ctypes and
 shares no code with the GPU library.  See the header of ``kvq_oracle.c`` for the
-page sections each routine follows.
+page sections each routine follows.  The seeded sign generator (SplitMix64) is
+written here in Python integers.
 
 Array conventions: fp16 inputs are widened exactly to float64 here; codes are
 packed LSB-first per vector (coordinate i in bits [b*i, b*i+b)).
@@ -132,6 +133,33 @@ def fwht(x):
     y = _f64(x).copy()
     lib().kvqo_fwht(_p(y, _D), y.shape[0])
     return y
+
+
+# --------------------------------------------------------------------------- random signs
+_M64 = (1 << 64) - 1
+
+
+def splitmix64(seed: int, n: int) -> int:
+    """Output n (from 0) of SplitMix64 seeded with `seed` (Steele, Lea and Flood,
+    "Fast splittable pseudorandom number generators", OOPSLA 2014): the state
+    after n + 1 steps of the golden-gamma increment, passed through the
+    variant-13 64-bit finaliser.  Python integers, reduced mod 2^64 by hand."""
+    z = (seed + (n + 1) * 0x9E3779B97F4A7C15) & _M64
+    z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & _M64
+    z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & _M64
+    return z ^ (z >> 31)
+
+
+def seeded_signs(seed: int, H: int, kind: int, d: int = 128):
+    """Random-sign diagonal D ("PolarQuant", Methodology: the randomized
+    Hadamard transform draws a random +-1 diagonal) of tensor `kind` (0 = K,
+    1 = V) for H KV heads, drawn from a seed: coordinate i of head h is -1
+    when the top bit of SplitMix64 output kind*2^32 + h*d + i is set."""
+    out = np.empty((H, d), np.int8)
+    for h in range(H):
+        for i in range(d):
+            out[h, i] = -1 if splitmix64(seed, (kind << 32) + h * d + i) >> 63 else 1
+    return out
 
 
 # --------------------------------------------------------------------------- packing

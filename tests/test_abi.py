@@ -78,7 +78,7 @@ def test_null_context_calls():
     L = kvq.lib()
     assert L.kvq_destroy(None) == kvq.KVQ_OK
     assert L.kvq_code_bytes_per_vec(None) == 0
-    assert L.kvq_get_tables(None, None, None) == kvq.KVQ_E_INVAL
+    assert L.kvq_get_tables(None, None, None, None, None) == kvq.KVQ_E_INVAL
     assert L.kvq_quantize(None, 0, None, 1, 1, 1, None, None, None, None, None) == kvq.KVQ_E_INVAL
     assert L.kvq_logits(None, None, 1, 1, 1, None, None, None, None, None, None) == kvq.KVQ_E_INVAL
     assert L.kvq_attn_decode(None, None, 1, 1, 1, None, None, None, None, 0.0, None, None, 0, None) == kvq.KVQ_E_INVAL

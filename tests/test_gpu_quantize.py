@@ -111,3 +111,25 @@ def test_quantize_kv_fused_equals_separate(bits):
     for a, b in ((ko, ks), (vo, vs)):
         assert torch.equal(a["codes"], b["codes"]) and torch.equal(a["norms"], b["norms"])
     check_codes(inp["v"], inp["signs_v"], bits, to_np(vo["codes"]), to_np(vo["norms"]), label="fused V")
+
+
+@pytest.mark.parametrize("seed", [0, 0xDEADBEEFCAFEF00D])
+def test_seeded_signs_match_oracle(seed):
+    """A context given a seed instead of sign arrays draws D_K and D_V with
+    SplitMix64; the library's draw equals the oracle's own generator, and the
+    codes of K and V follow that D."""
+    import oracle as O
+
+    inp = synth.make("l8b32k", T=300)
+    H = inp["k"].shape[1]
+    ctx = kvq.Context(H, 3, None, None, seed=seed)
+    sk, sv = ctx.signs()
+    ok, ov = O.seeded_signs(seed, H, 0), O.seeded_signs(seed, H, 1)
+    assert np.array_equal(sk, ok) and np.array_equal(sv, ov)
+    for kind, x, signs in ((kvq.KVQ_KIND_K, inp["k"], ok), (kvq.KVQ_KIND_V, inp["v"], ov)):
+        out = ctx.quantize(kind, torch.from_numpy(x).cuda())
+        check_codes(x, signs, 3, to_np(out["codes"]), to_np(out["norms"]), label="seeded")
+    # explicit arrays are returned as given
+    ctx2 = kvq.Context(H, 3, inp["signs_k"], None, seed=seed)
+    sk2, sv2 = ctx2.signs()
+    assert np.array_equal(sk2, inp["signs_k"]) and np.array_equal(sv2, ov)
