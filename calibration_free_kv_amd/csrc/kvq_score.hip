@@ -281,46 +281,73 @@ __global__ __launch_bounds__(kLgThreads) void k_logits(
 }
 
 // ---------------------------------------------------------------------------
-// kvq_attn_decode: split-K flash decoding.  Block (b, g, split) owns a token
-// range of one (batch, KV head).  After the shared prologue (rotated queries,
-// K field tables) every wave works alone on 64-token tiles of the range:
-//  K  lane = token: logit from the field tables, scaled by rho_K and by
-//     sm_scale*log2(e); wave max / sum give a running (m, l) per head
-//     (base-2 exponentials);
-//  V  lane = 8 consecutive coordinates (an octet) and one of four token
-//     phases: the weights p_h,t rho_V,t and the staged V records are read
-//     from the wave's LDS and accumulated in the rotated domain,
-//     acc_h[i] += p rho_V c[idx_t,i].
-// The block's waves merge once at the end; the block writes (m, l, acc) for
-// its G heads and the last block of a (b, g) to finish (arrival counter)
+// kvq_attn_decode: split-K flash decoding on the matrix cores.  Block
+// (b, g, split) owns a token range of one (batch, KV head); each of its
+// waves works alone on 64-token tiles of the range, and both contractions of
+// a tile are 16x16x32 fp16 matrix products with fp32 accumulation:
+//  K  logits^T = Q' K^T, contracted over the 128 coordinates.  Q' holds the
+//     rotated, power-of-two-scaled query of each head split into an fp16
+//     high part and an fp16 low part (two rows per head), and K^T the fp16
+//     high and low parts of the key centroids, read from a table indexed by
+//     the codes of two adjacent coordinates; the two products give the logit
+//     to about 2^-22 relative.
+//  V  acc = P' V, contracted over tokens.  P' holds the fp16 high and low
+//     parts (two rows per head) of the weights 2^(s + log2 rho_V - mv) with
+//     mv the running maximum of that exponent; V the centroid high and low
+//     parts of one code each (the two parts sit at adjacent positions of the
+//     contraction, against two copies of the weight).  Dividing out rho_V in
+//     the exponent keeps every weight in [0, 1], so no fp16 operand can
+//     overflow whatever the norms are.
+// The running softmax state per head is (m, l) over 2^s and mv over the
+// numerator; a wave converts its accumulator to the 2^(s - m) scale once at
+// the end.  The waves of a block merge in LDS; the block writes (m, l, acc)
+// for its G heads and the last block of a (b, g) to finish (arrival counter)
 // merges the splits and applies the inverse rotation once:
 // out_h = D_V .* H acc / (d l).
+//
+// Lane roles in a tile (lane = 16 kg + n):
+//  logits  B operand: token 16 rg + n (rg = 0..3), coordinates 32 kg .. 32 kg
+//          + 31, which are BITS consecutive dwords of the record, loaded
+//          straight from memory; result rows 4 kg, 4 kg + 1 are head kg.
+//  weights head kg, tokens 16 rg + n.
+//  values  B operand: coordinates 8 n .. 8 n + 7 (one per product nb) of
+//          tokens 16 kq + 4 kg .. + 3, from the wave's V records staged in
+//          LDS transposed (dword w of token t at [w][t]); accumulator nb of
+//          the lane holds rows 4 kg, 4 kg + 1 (head kg) of coordinate 8 n + nb.
 // ---------------------------------------------------------------------------
 constexpr int kDecWaves = 16;
 constexpr int kDecThreads = kDecWaves * 64;
 
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef uint32_t u2_t __attribute__((ext_vector_type(2)));
+
+// Dynamic LDS of the decode kernel (the centroid tables are static arrays,
+// whose addresses fold into the offsets of the LDS instructions).
 template <int BITS, int G>
 struct DecSmem {
-    using FD = Fields<BITS>;
-    // staged V record stride in dwords: at least one word past the record
-    // (the funnel shift of the last octet reads it), 16 when that suffices
-    static constexpr int RW = FD::W + 1 <= 16 ? 16 : FD::W + 1;
-    // the field tables come first: with a constant base, every field's part
-    // of an entry address fits the 16-bit offset of an LDS instruction
-    static constexpr int lut = 0;                                 // [NF][E][G]
-    static constexpr int c2 = lut + FD::NF * FD::E * G;           // [2^(2b)][2] centroid pairs
-    static constexpr int vbuf = c2 + 2 * (1 << (2 * BITS));       // [waves][64][RW] V records
-    static constexpr int wbuf = vbuf + kDecWaves * 64 * RW;       // [waves][64][G] weights
-    static constexpr int qr = wbuf + kDecWaves * 64 * G;          // [G][128] rotated queries
-    static constexpr int wm = qr + G * kD;                        // [waves][G] wave maxima
-    static constexpr int wl = wm + kDecWaves * G;                 // [waves][G] wave sums
-    static constexpr int ctab = wl + kDecWaves * G;               // [16] centroids
-    static constexpr int flag = ctab + 16;                        // [1] last-arrival flag
-    static constexpr int total = flag + 4;
-    // end-of-block reuse of vbuf..wbuf: per-wave accumulators, split merge
-    static_assert(qr - vbuf >= kDecWaves * G * kD, "wave merge buffer does not fit");
-    static_assert(qr - vbuf >= 2 * kMaxSplits * G, "split merge buffer does not fit");
-    static_assert(FD::NF * FD::E * G * 4 <= 65536, "field offsets must fit an LDS immediate");
+    static constexpr int W = 4 * BITS;             // dwords per record
+    static constexpr int NP = 1 << (2 * BITS);     // codes of a coordinate pair
+    static constexpr int QS = 136;                 // halves per query row (padded as below)
+    static constexpr int ctab = 0;                 // [16] fp32 centroids
+    static constexpr int qh = ctab + 16;           // [2G + 1][QS] fp16 query rows: high, low parts; zeros
+    static constexpr int qf = qh + (2 * G + 1) * QS / 2;  // [G] logit factor of each head
+    static constexpr int wm = qf + 4;              // [waves][G] wave maxima
+    static constexpr int wl = wm + kDecWaves * G;  // [waves][G] wave sums
+    static constexpr int flag = wl + kDecWaves * G;  // [1] last-arrival flag, [1] published query heads
+    // per-wave staging, from `stage` on: V records transposed [W + 1][VS]
+    // (the last row is only ever read as the unused upper bits of a funnel
+    // shift), then the weight operand [16 rows][PS] fp16.  The padded row
+    // strides (4 banks, resp. 2 banks, past a multiple of the bank count) put
+    // the rows that the lanes of one read group fetch in distinct banks.
+    static constexpr int VS = 68;                  // dwords per transposed V row
+    static constexpr int PS = 68;                  // halves per weight row
+    static constexpr int PT = VS * (W + 1);
+    static constexpr int STG = PT + 16 * PS / 2;
+    static constexpr int stage = (flag + 4 + 63) / 64 * 64;
+    static constexpr int total = stage + kDecWaves * STG;
+    // end-of-block reuse of the staging area: per-wave accumulators, split merge
+    static_assert(kDecWaves * STG >= kDecWaves * G * kD, "wave merge buffer does not fit");
+    static_assert(kDecWaves * STG >= kMaxSplits * G, "split merge buffer does not fit");
 };
 
 // Cross-row exchanges on the VALU (gfx950 lane swaps): with the same value in
@@ -339,19 +366,30 @@ __device__ __forceinline__ float2 swap32(float x)
     return float2{__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1])};
 }
 
-// Wave-wide max / sum, result in every lane: four DPP steps inside each row
-// of 16 lanes, then the exchanges across rows and halves.
+// Reductions inside each row of 16 lanes (four DPP steps), and over the wave
+// (then the exchanges across rows and halves); result in every lane.
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x)
 {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
 }
-__device__ __forceinline__ float wave_max(float x)
+__device__ __forceinline__ float row_max(float x)
 {
     x = fmaxf(x, dpp<0xB1>(x));   // quad_perm [1,0,3,2]
     x = fmaxf(x, dpp<0x4E>(x));   // quad_perm [2,3,0,1]
     x = fmaxf(x, dpp<0x141>(x));  // row_half_mirror
-    x = fmaxf(x, dpp<0x140>(x));  // row_mirror
+    return fmaxf(x, dpp<0x140>(x));  // row_mirror
+}
+__device__ __forceinline__ float row_sum(float x)
+{
+    x += dpp<0xB1>(x);
+    x += dpp<0x4E>(x);
+    x += dpp<0x141>(x);
+    return x + dpp<0x140>(x);
+}
+__device__ __forceinline__ float wave_max(float x)
+{
+    x = row_max(x);
     float2 p = swap16(x);
     x = fmaxf(p.x, p.y);
     p = swap32(x);
@@ -359,19 +397,21 @@ __device__ __forceinline__ float wave_max(float x)
 }
 __device__ __forceinline__ float wave_sum(float x)
 {
-    x += dpp<0xB1>(x);
-    x += dpp<0x4E>(x);
-    x += dpp<0x141>(x);
-    x += dpp<0x140>(x);
+    x = row_sum(x);
     float2 p = swap16(x);
     x = p.x + p.y;
     p = swap32(x);
     return p.x + p.y;
 }
-// A value that is the same in every lane, moved to a scalar register.
-__device__ __forceinline__ float uniform(float x)
+// o[r] = x of lane 16 r + (l & 15), for r = 0..3: row r broadcast to every row.
+__device__ __forceinline__ void row_broadcast(float x, float (&o)[4])
 {
-    return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
+    const float2 h = swap32(x);   // rows (0, 1, 0, 1) and (2, 3, 2, 3)
+    const float2 a = swap16(h.x), c = swap16(h.y);
+    o[0] = a.x;
+    o[1] = a.y;
+    o[2] = c.x;
+    o[3] = c.y;
 }
 // LDS written by some lanes of a wave is read by other lanes of the same wave.
 __device__ __forceinline__ void wave_lds_sync()
@@ -381,39 +421,81 @@ __device__ __forceinline__ void wave_lds_sync()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// One V step of a lane: the octet of token tt's staged record (bits of 8
-// coordinates, as four fields of two), its four centroid pairs, the G weights
-// of the token, 8 G multiply-adds.
-template <int BITS, int G>
-__device__ __forceinline__ void v_step(const uint32_t *rec, const float *wrow, const float *c2, int owd, int osh,
-                                       float (&acc)[G][8])
+// NB bits at bit offset O (compile time) of a window of consecutive dwords.
+template <int O, int NB, int N>
+__device__ __forceinline__ uint32_t window_bits(const uint32_t (&w)[N])
 {
-    constexpr uint32_t fmask = (1u << (2 * BITS)) - 1u;
-    const uint32_t bits = __builtin_amdgcn_alignbit(rec[owd + 1], rec[owd], (uint32_t)osh);
-    f2_t cp[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) cp[k] = reinterpret_cast<const f2_t *>(c2)[(bits >> (2 * BITS * k)) & fmask];
-    float wv[G];
-    if constexpr (G % 4 == 0) {
-#pragma unroll
-        for (int h4 = 0; h4 < G / 4; ++h4) {
-            const f4_t x = reinterpret_cast<const f4_t *>(wrow)[h4];
-            wv[4 * h4] = x.x;
-            wv[4 * h4 + 1] = x.y;
-            wv[4 * h4 + 2] = x.z;
-            wv[4 * h4 + 3] = x.w;
-        }
+    constexpr int wd = O >> 5, sh = O & 31;
+    static_assert(wd < N, "field outside the window");
+    if constexpr (sh + NB <= 32) {
+        return (w[wd] >> sh) & ((1u << NB) - 1u);
     } else {
-#pragma unroll
-        for (int h = 0; h < G; ++h) wv[h] = wrow[h];
+        static_assert(wd + 1 < N, "field outside the window");
+        return __builtin_amdgcn_alignbit(w[wd + 1], w[wd], (uint32_t)sh) & ((1u << NB) - 1u);
     }
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            acc[h][2 * k] = fmaf(wv[h], cp[k].x, acc[h][2 * k]);
-            acc[h][2 * k + 1] = fmaf(wv[h], cp[k].y, acc[h][2 * k + 1]);
-        }
+}
+
+// fp16 high part of x (round to nearest) and the fp16 rounding of the rest.
+__device__ __forceinline__ void split_f16(float x, _Float16 &hi, _Float16 &lo)
+{
+    hi = (_Float16)x;
+    lo = (_Float16)(x - (float)hi);
+}
+__device__ __forceinline__ uint32_t pack_h2(_Float16 a, _Float16 b)
+{
+    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+// B operands of the logits for coordinates 32 kg + 8 CB .. + 7 of one token:
+// the four coordinate pairs of the lane's window, high and low parts.
+template <int BITS, int CB>
+__device__ __forceinline__ void key_operands(const uint32_t (&win)[BITS], const uint32_t *khi, const uint32_t *klo,
+                                             u4_t &bh, u4_t &bl)
+{
+    constexpr uint32_t NB = 2 * BITS;
+    const uint32_t e0 = window_bits<8 * BITS * CB + 0 * NB, NB>(win);
+    const uint32_t e1 = window_bits<8 * BITS * CB + 1 * NB, NB>(win);
+    const uint32_t e2 = window_bits<8 * BITS * CB + 2 * NB, NB>(win);
+    const uint32_t e3 = window_bits<8 * BITS * CB + 3 * NB, NB>(win);
+    bh = u4_t{khi[e0], khi[e1], khi[e2], khi[e3]};
+    bl = u4_t{klo[e0], klo[e1], klo[e2], klo[e3]};
+}
+
+// Logit partial sums of one 16-token row group (tokens 16 rg + n) over the
+// 128 coordinates: eight products, the operands of each block looked up
+// while the previous block's products run.
+template <int BITS>
+__device__ __forceinline__ f4_t logit_group(const uint32_t (&win)[BITS], const uint32_t *khi, const uint32_t *klo,
+                                            const h8_t (&aq)[4])
+{
+    f4_t d = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    u4_t h0, l0, h1, l1;
+    key_operands<BITS, 0>(win, khi, klo, h0, l0);
+    key_operands<BITS, 1>(win, khi, klo, h1, l1);
+    __builtin_amdgcn_sched_barrier(0);
+    d = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[0], __builtin_bit_cast(h8_t, h0), d, 0, 0, 0);
+    d = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[0], __builtin_bit_cast(h8_t, l0), d, 0, 0, 0);
+    key_operands<BITS, 2>(win, khi, klo, h0, l0);
+    __builtin_amdgcn_sched_barrier(0);
+    d = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[1], __builtin_bit_cast(h8_t, h1), d, 0, 0, 0);
+    d = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[1], __builtin_bit_cast(h8_t, l1), d, 0, 0, 0);
+    key_operands<BITS, 3>(win, khi, klo, h1, l1);
+    __builtin_amdgcn_sched_barrier(0);
+    d = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[2], __builtin_bit_cast(h8_t, h0), d, 0, 0, 0);
+    d = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[2], __builtin_bit_cast(h8_t, l0), d, 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    d = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[3], __builtin_bit_cast(h8_t, h1), d, 0, 0, 0);
+    d = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[3], __builtin_bit_cast(h8_t, l1), d, 0, 0, 0);
+    return d;
+}
+
+// B operand of the values for coordinate 8 n + NB of the lane's four tokens.
+template <int BITS, int NB>
+__device__ __forceinline__ u4_t value_operand(const uint32_t (&oc)[4], const uint32_t *vtab)
+{
+    constexpr uint32_t cm = (1u << BITS) - 1u;
+    return u4_t{vtab[(oc[0] >> (BITS * NB)) & cm], vtab[(oc[1] >> (BITS * NB)) & cm],
+                vtab[(oc[2] >> (BITS * NB)) & cm], vtab[(oc[3] >> (BITS * NB)) & cm]};
 }
 
 template <int BITS, int G>
@@ -424,219 +506,276 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
     float *__restrict__ part, unsigned *__restrict__ counters, int64_t T, int H, int Hq,
     int n_split, int64_t chunk)
 {
-    using FD = Fields<BITS>;
+    static_assert(G == 1 || G == 2 || G == 4, "two rows per head in one 16-row operand");
     using SM = DecSmem<BITS, G>;
-    constexpr int RW = SM::RW;
+    constexpr int W = SM::W;
+    constexpr uint32_t cm = (1u << BITS) - 1u;
     extern __shared__ __align__(16) float smem[];
-    float *qr = smem + SM::qr;
-    float *lut = smem + SM::lut;
-    float *c2 = smem + SM::c2;
+    // centroid tables, fp16 high part in the low half of a dword and low part
+    // in the high half where one code is looked up; for a coordinate pair,
+    // the high (khi) and low (klo) parts of both centroids.  klo lies 1040
+    // bytes past khi: no paired LDS read can reach both at one address
+    // (which would return a high and a low part in adjacent registers, to be
+    // moved apart again for the two products).
+    __shared__ uint32_t ktab[260 + SM::NP], vtab[1 << BITS];
+    static_assert(SM::NP <= 260, "pair table overlaps");
+    uint32_t *khi = ktab, *klo = ktab + 260;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    uint32_t *vbuf = reinterpret_cast<uint32_t *>(smem + SM::vbuf) + wv * 64 * RW;
-    float *wbuf = smem + SM::wbuf + wv * 64 * G;
+    const int kg = lane >> 4, n = lane & 15;
+    uint32_t *stg = reinterpret_cast<uint32_t *>(smem + SM::stage) + wv * SM::STG;
+    _Float16 *pT = reinterpret_cast<_Float16 *>(stg + SM::PT);
     const int64_t bh = blockIdx.x / n_split;
     const int split = (int)(blockIdx.x - bh * n_split);
     const int64_t b = bh / H;
     const int g = (int)(bh - b * H);
 
-    // V lane roles: coordinate octet co (coordinates 8co .. 8co+7) and token
-    // phase ph (tokens ph, ph+4, ...): the 8b bits of an octet come from one
-    // funnel shift of two record dwords, its four centroid pairs from four
-    // 8-byte LDS reads.
-    const int co = lane & 15, ph = lane >> 4;
-    constexpr int OB = 8 * BITS;  // bits of an octet
-    const int obit = OB * co, owd = obit >> 5, osh = obit & 31;
-
-    float m_run[G], l_run[G], acc[G][8];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-        m_run[h] = -INFINITY;
-        l_run[h] = 0.0f;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) acc[h][k] = 0.0f;
-    }
-
     const int64_t t_begin = (int64_t)split * chunk;
     const int64_t t_end = min(T, t_begin + chunk);
-    // The query loads go out first: memory operations complete in issue order,
-    // so loads issued after the records would make the prologue wait for them.
+    // The prologue holds no block barrier once loads are in flight: a barrier
+    // would hold every wave until the last one had issued its record loads,
+    // i.e. until the memory system had accepted the whole block's tiles.
+    // Wave h < G rotates query head h and publishes it in LDS with a count;
+    // the other waves issue their loads and then wait for the count.  The
+    // count is cleared behind the one barrier at the start, when no memory
+    // operation is outstanding yet.
+    unsigned *ready = reinterpret_cast<unsigned *>(smem + SM::flag) + 1;
+    if (tid == 0) *ready = 0u;
+    __syncthreads();
+    // The query loads go out first (memory operations complete in issue
+    // order): lane l holds coordinates 2l, 2l+1 of head wv.
     uint32_t qv = 0u;
     f2_t qs = f2_t{0.0f, 0.0f};
     if (wv < G) {
         qv = reinterpret_cast<const uint32_t *>(q + ((int64_t)b * Hq + (int64_t)g * G + wv) * kD)[lane];
         qs = reinterpret_cast<const f2_t *>(signs_k + g * kD)[lane];
     }
+    // the centroids too: indexed at run time, they are read from memory
+    const float cen = cb.c[lane & 15];
     // The records of the wave's next tile are held in registers: loaded before
-    // the prologue for the first tile, and right after the current tile's
-    // records have been consumed for the others.
-    uint32_t Kw[FD::W + 1], Vw[FD::W];
+    // the prologue for the first tile; for the others, the keys once the
+    // current logits are formed and the values once the current value
+    // products are issued, so that only one of the two is in flight during
+    // each phase.  Every lane loads (tokens past the end re-read the last one
+    // of the range), so the loads carry no lane-dependent branch.  Keys: the
+    // lane's window (BITS dwords) of the records of tokens 16 rg + n, and
+    // rho_K of token `lane`; values and rho_V: token `lane`.
+    uint32_t Kw[4][BITS], Vw[W];
     float rk = 0.0f, rv = 0.0f;
-    // Every lane loads (tokens past the end re-read the last one of the
-    // range), so the loads carry no lane-dependent branch and the compiler's
-    // wait for the query values counts exactly the loads issued after them.
     // Addresses: a wave-uniform 64-bit base for the tile plus a 32-bit lane
-    // offset (scalar-base loads; one VGPR of address per load).
-    auto fetch = [&](int64_t t0) {
+    // offset (scalar-base loads).
+    auto fetch_k = [&](int64_t t0) {
         t0 = min(t0, t_end - 1);  // a wave without a tile loads the range's last token
         const int64_t v0 = bh * T + t0;
-        const uint32_t l = (uint32_t)min((int64_t)lane, t_end - 1 - t0);  // >= 0
-        const uint32_t off = l * (16u * BITS);  // bytes
-        const char *ks = reinterpret_cast<const char *>(kc) + v0 * (16 * BITS) + off;
-        const char *vs = reinterpret_cast<const char *>(vc) + v0 * (16 * BITS) + off;
+        const uint32_t last = (uint32_t)min((int64_t)63, t_end - 1 - t0);  // last valid token of the tile
+        const uint32_t l = min((uint32_t)lane, last);
+        const char *kb = reinterpret_cast<const char *>(kc) + v0 * (16 * BITS);
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+            const uint32_t t = min((uint32_t)(16 * rg + n), last);
+            const uint32_t *src = reinterpret_cast<const uint32_t *>(kb + (t * (16u * BITS) + 4u * BITS * kg));
+#pragma unroll
+            for (int i = 0; i < BITS; ++i) Kw[rg][i] = src[i];
+        }
+        rk = *reinterpret_cast<const float *>(reinterpret_cast<const char *>(kn + v0) + 4 * l);
+    };
+    auto fetch_v = [&](int64_t t0) {
+        t0 = min(t0, t_end - 1);
+        const int64_t v0 = bh * T + t0;
+        const uint32_t l = min((uint32_t)lane, (uint32_t)min((int64_t)63, t_end - 1 - t0));
+        const u4_t *vs = reinterpret_cast<const u4_t *>(reinterpret_cast<const char *>(vc) + v0 * (16 * BITS) +
+                                                          l * (16u * BITS));
 #pragma unroll
         for (int k = 0; k < BITS; ++k) {
-            const u4_t x = reinterpret_cast<const u4_t *>(ks)[k], y = reinterpret_cast<const u4_t *>(vs)[k];
-            Kw[4 * k] = x.x;
-            Kw[4 * k + 1] = x.y;
-            Kw[4 * k + 2] = x.z;
-            Kw[4 * k + 3] = x.w;
+            const u4_t y = vs[k];
             Vw[4 * k] = y.x;
             Vw[4 * k + 1] = y.y;
             Vw[4 * k + 2] = y.z;
             Vw[4 * k + 3] = y.w;
         }
-        Kw[4 * BITS] = 0u;  // guard word for fields that end on the last dword
-        rk = *reinterpret_cast<const float *>(reinterpret_cast<const char *>(kn + v0) + 4 * l);
         rv = *reinterpret_cast<const float *>(reinterpret_cast<const char *>(vn + v0) + 4 * l);
     };
     constexpr int64_t kStride = (int64_t)kDecWaves * 64;
-    // the centroids too: indexed at run time, they are read from memory
-    float cen = 0.0f;
-    if (tid < 16) cen = cb.c[tid];
     __builtin_amdgcn_sched_barrier(0);  // keep the prologue's loads ahead of the records
-    fetch(t_begin + (int64_t)wv * 64);
+    fetch_k(t_begin + (int64_t)wv * 64);
+    fetch_v(t_begin + (int64_t)wv * 64);
+
     float *ctab = smem + SM::ctab;
-    if (tid < 16) ctab[tid] = cen;
-    if (wv < G) {  // one wave per head: qr[h] = H (D_K .* q_h)
+    float *qf = smem + SM::qf;
+    _Float16 *qh = reinterpret_cast<_Float16 *>(smem + SM::qh);
+    // centroid tables: every wave writes the same values and reads back its own
+    if (lane < 16) ctab[lane] = cen;
+    // rows of the weight operand that no head writes stay zero
+    for (int i = lane; i < 8 * SM::PS; i += 64) stg[SM::PT + i] = 0u;
+    if (wv == 0) reinterpret_cast<uint32_t *>(qh + 2 * G * SM::QS)[lane] = 0u;  // the zero query row
+    wave_lds_sync();
+    for (int e = lane; e < SM::NP; e += 64) {
+        _Float16 ha, la, hb, lb;
+        split_f16(ctab[e & cm], ha, la);
+        split_f16(ctab[e >> BITS], hb, lb);
+        khi[e] = pack_h2(ha, hb);
+        klo[e] = pack_h2(la, lb);
+    }
+    if (lane < (1 << BITS)) {
+        _Float16 h, l;
+        split_f16(ctab[lane], h, l);
+        vtab[lane] = pack_h2(h, l);
+    }
+    if (wv < G) {
+        // q'_h = H (D_K .* q_h), scaled by a power of two that puts its
+        // largest entry in [2^14, 2^15): inside the fp16 range, with full
+        // precision for the high and low parts (rows 2h and 2h + 1 of qh).
+        // The logit factor undoes the scale.
         float x0 = (float)__builtin_bit_cast(h2_t, qv).x * qs.x;
         float x1 = (float)__builtin_bit_cast(h2_t, qv).y * qs.y;
         wave_fwht(x0, x1, lane);
-        reinterpret_cast<f2_t *>(qr + wv * kD)[lane] = f2_t{x0, x1};
+        const float amax = wave_max(fmaxf(__builtin_fabsf(x0), __builtin_fabsf(x1)));
+        const int e = amax > 0.0f ? __builtin_amdgcn_frexp_expf(amax) : 0;
+        const float sc = __builtin_ldexpf(1.0f, 15 - e);
+        _Float16 h0, l0, h1, l1;
+        split_f16(x0 * sc, h0, l0);
+        split_f16(x1 * sc, h1, l1);
+        reinterpret_cast<uint32_t *>(qh + (2 * wv) * SM::QS)[lane] = pack_h2(h0, h1);
+        reinterpret_cast<uint32_t *>(qh + (2 * wv + 1) * SM::QS)[lane] = pack_h2(l0, l1);
+        if (lane == 0) qf[wv] = scale_log2 / ((float)kD * sc);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        if (lane == 0) __hip_atomic_fetch_add(ready, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
-    __syncthreads();
-    constexpr uint32_t cm = (1u << BITS) - 1u;
-    for (int e = tid; e < (1 << (2 * BITS)); e += kDecThreads) {
-        c2[2 * e] = ctab[e & cm];
-        c2[2 * e + 1] = ctab[(e >> BITS) & cm];
+    // wait until the G heads are published (the zero row was written by wave
+    // 0 before its own count, or is this wave's own write)
+    while (__hip_atomic_load(ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < (unsigned)G)
+        __builtin_amdgcn_s_sleep(1);
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    // A operand of the logits: row n is part (n & 3) of head n >> 2 (0: high,
+    // 1: low, 2 and 3: zero), coordinates 32 kg + 8 cb + j.
+    h8_t aq[4];
+    {
+        const int ah = n >> 2, ap = n & 3;
+        const int row = ah < G && ap < 2 ? 2 * ah + ap : 2 * G;
+        const h8_t *src = reinterpret_cast<const h8_t *>(qh + row * SM::QS + 32 * kg);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) aq[c] = src[c];
     }
-    build_tables<BITS, G>(qr, ctab, lut);
-    __syncthreads();
+    const float fq = kg < G ? qf[kg] : 0.0f;
 
-    const uint32_t *vrow = vbuf + ph * RW;  // this lane's token phase in the staged records
-    const float *wrow = wbuf + ph * G;
+    float m_run = -INFINITY, l_run = 0.0f, mv_run = -INFINITY;
+    f4_t acc[8];
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) acc[nb] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    const int obit = 8 * BITS * n, ow = obit >> 5, osh = obit & 31;
+
     for (int64_t t0 = t_begin + (int64_t)wv * 64; t0 < t_end; t0 += kStride) {
         const int nt = (int)min((int64_t)64, t_end - t0);
-        const bool valid = lane < nt;
-        float s[G];
-        const float rvc = rv;
-        // lanes past the end hold a copy of the last record: staged (never
-        // read) and scored (then discarded)
-        if constexpr (RW % 4 == 0) {  // 16-byte aligned rows
+        const bool more = t0 + kStride < t_end;
+        // logits of tokens 16 rg + n for head kg (rows 4 kg, 4 kg + 1)
+        float s[4];
 #pragma unroll
-            for (int k = 0; k < FD::W / 4; ++k)
-                reinterpret_cast<u4_t *>(vbuf + lane * RW)[k] = u4_t{Vw[4 * k], Vw[4 * k + 1], Vw[4 * k + 2], Vw[4 * k + 3]};
-        } else {
-#pragma unroll
-            for (int k = 0; k < FD::W; ++k) vbuf[lane * RW + k] = Vw[k];
+        for (int rg = 0; rg < 4; ++rg) {
+            const f4_t d = logit_group<BITS>(Kw[rg], khi, klo, aq);
+            s[rg] = d[0] + d[1];
         }
-        score_record_grouped<BITS, G>(Kw, lut, s);
-        const float rs = rk * scale_log2;
+        float rkb[4], lvb[4];
+        row_broadcast(rk, rkb);
+        row_broadcast(__builtin_amdgcn_logf(rv), lvb);  // log2 rho_V; -inf for a zero vector
+        if (more) fetch_k(t0 + kStride);  // this tile's keys are consumed
+        // stage the V records transposed: dword w of token `lane` at [w][lane]
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-            s[h] = valid ? s[h] * rs : -INFINITY;
-            // the sums are formed here, not sunk past the loads below (which
-            // would keep all 64 table entries live in registers meanwhile)
-            asm volatile("" : : "v"(s[h]));
+        for (int w = 0; w < W; ++w) stg[SM::VS * w + lane] = Vw[w];
+        // online softmax of head kg over the 16 lanes of its row
+        float sv[4], mt = -INFINITY, mvt = -INFINITY;
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+            s[rg] = 16 * rg + n < nt ? s[rg] * (fq * rkb[rg]) : -INFINITY;
+            sv[rg] = s[rg] + lvb[rg];
+            mt = fmaxf(mt, s[rg]);
+            mvt = fmaxf(mvt, sv[rg]);
         }
-        if (t0 + kStride < t_end) fetch(t0 + kStride);  // this tile's records are consumed
-        // m, l and the rescale factor are the same in every lane: kept in
-        // scalar registers
-        float alpha[G];
+        const float mn = fmaxf(m_run, row_max(mt));  // finite: token 0 of the tile is valid
+        const float mvn = fmaxf(mv_run, row_max(mvt));
+        const float mvs = mvn == -INFINITY ? 0.0f : mvn;  // all numerators zero so far
+        const float alpha = __builtin_amdgcn_exp2f(m_run - mn);    // 0 on the first tile
+        const float beta = __builtin_amdgcn_exp2f(mv_run - mvs);
+        float ps = 0.0f;
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-            const float mn = uniform(fmaxf(m_run[h], wave_max(s[h])));
-            alpha[h] = uniform(__builtin_amdgcn_exp2f(m_run[h] - mn));  // 0 on the first tile (m_run = -inf)
-            m_run[h] = mn;
-            const float p = valid ? __builtin_amdgcn_exp2f(s[h] - mn) : 0.0f;
-            l_run[h] = uniform(l_run[h] * alpha[h] + wave_sum(p));
-            s[h] = p * rvc;
-#pragma unroll
-            for (int k = 0; k < 8; ++k) acc[h][k] *= alpha[h];
+        for (int rg = 0; rg < 4; ++rg) {
+            ps += __builtin_amdgcn_exp2f(s[rg] - mn);
+            const float pv = __builtin_amdgcn_exp2f(sv[rg] - mvs);  // in [0, 1]
+            _Float16 hi, lo;
+            split_f16(pv, hi, lo);
+            pT[(4 * kg) * SM::PS + 16 * rg + n] = hi;
+            pT[(4 * kg + 1) * SM::PS + 16 * rg + n] = lo;
         }
-        if constexpr (G % 4 == 0) {
+        l_run = l_run * alpha + row_sum(ps);
+        m_run = mn;
+        mv_run = mvn;
 #pragma unroll
-            for (int h4 = 0; h4 < G / 4; ++h4)
-                reinterpret_cast<f4_t *>(wbuf + lane * G)[h4] = f4_t{s[4 * h4], s[4 * h4 + 1], s[4 * h4 + 2], s[4 * h4 + 3]};
-        } else {
-#pragma unroll
-            for (int h = 0; h < G; ++h) wbuf[lane * G + h] = s[h];
+        for (int nb = 0; nb < 8; ++nb) {
+            acc[nb][0] *= beta;
+            acc[nb][1] *= beta;
         }
         wave_lds_sync();
-        if (nt == 64) {  // full tile: 16 steps with constant LDS offsets
+        // values: acc += P' V over the tile's four 16-token groups
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                // at most two steps' loads in flight: hoisting all sixteen
-                // would need far more registers than a wave has
-                __builtin_amdgcn_sched_barrier(0);
-                v_step<BITS, G>(vrow + 4 * j * RW, wrow + 4 * j * G, c2, owd, osh, acc);
+        for (int kq = 0; kq < 4; ++kq) {
+            const int tb = 16 * kq + 4 * kg;
+            const u2_t pp = *reinterpret_cast<const u2_t *>(pT + n * SM::PS + tb);
+            const u4_t a = u4_t{__builtin_amdgcn_perm(pp.x, pp.x, 0x01000100u), __builtin_amdgcn_perm(pp.x, pp.x, 0x03020302u),
+                                __builtin_amdgcn_perm(pp.y, pp.y, 0x01000100u), __builtin_amdgcn_perm(pp.y, pp.y, 0x03020302u)};
+            const u4_t x = *reinterpret_cast<const u4_t *>(stg + SM::VS * ow + tb);
+            uint32_t oc[4];
+            if constexpr (BITS == 3) {  // octets straddle dwords
+                const u4_t y = *reinterpret_cast<const u4_t *>(stg + SM::VS * (ow + 1) + tb);
+                oc[0] = __builtin_amdgcn_alignbit(y.x, x.x, (uint32_t)osh);
+                oc[1] = __builtin_amdgcn_alignbit(y.y, x.y, (uint32_t)osh);
+                oc[2] = __builtin_amdgcn_alignbit(y.z, x.z, (uint32_t)osh);
+                oc[3] = __builtin_amdgcn_alignbit(y.w, x.w, (uint32_t)osh);
+            } else {
+                oc[0] = x.x >> osh;
+                oc[1] = x.y >> osh;
+                oc[2] = x.z >> osh;
+                oc[3] = x.w >> osh;
             }
-        } else {
-            for (int tt = ph; tt < nt; tt += 4) v_step<BITS, G>(vbuf + tt * RW, wbuf + tt * G, c2, owd, osh, acc);
+            // each product's operand is looked up while the previous one runs
+            const h8_t ah = __builtin_bit_cast(h8_t, a);
+            u4_t b0 = value_operand<BITS, 0>(oc, vtab), b1;
+#define KVQ_VSTEP(NB, CUR, NXT)                                                              \
+    if constexpr (NB < 7) NXT = value_operand<BITS, (NB < 7 ? NB + 1 : 7)>(oc, vtab);       \
+    __builtin_amdgcn_sched_barrier(0);                                                        \
+    acc[NB] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, __builtin_bit_cast(h8_t, CUR), acc[NB], 0, 0, 0);
+            KVQ_VSTEP(0, b0, b1)
+            KVQ_VSTEP(1, b1, b0)
+            KVQ_VSTEP(2, b0, b1)
+            KVQ_VSTEP(3, b1, b0)
+            KVQ_VSTEP(4, b0, b1)
+            KVQ_VSTEP(5, b1, b0)
+            KVQ_VSTEP(6, b0, b1)
+            KVQ_VSTEP(7, b1, b0)
+#undef KVQ_VSTEP
         }
-        wave_lds_sync();  // vbuf / wbuf are rewritten by the next tile
+        if (more) fetch_v(t0 + kStride);
+        wave_lds_sync();  // the staging area is rewritten by the next tile
     }
 
-    // Sum the four token phases (lanes l, l^16, l^32, l^48 hold partial sums
-    // of the same coordinates) with lane swaps: one swap and one add per
-    // register and level.  Afterwards register r of red[] holds in row k
-    // (lanes 16k .. 16k+15, coordinate octet co) the total of accumulator
-    // 4r + k, accumulator a = 8h + j being coordinate 8co + j of head h.
-    constexpr int NA = 8 * G;
-    float red[NA / 4];
-    {
-        float s1[NA / 2];
-#pragma unroll
-        for (int i = 0; i < NA / 2; ++i) {  // level 1: pairs (2i, 2i+1) across halves
-            const float a = acc[(2 * i) / 8][(2 * i) % 8], c = acc[(2 * i + 1) / 8][(2 * i + 1) % 8];
-            const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, a),
-                                                            __builtin_bit_cast(unsigned, c), false, false);
-            // lanes 0-31: a's halves summed; lanes 32-63: c's
-            s1[i] = __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
-        }
-#pragma unroll
-        for (int i = 0; i < NA / 4; ++i) {  // level 2: pairs (2i, 2i+1) across rows
-            const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, s1[2 * i]),
-                                                            __builtin_bit_cast(unsigned, s1[2 * i + 1]), false, false);
-            red[i] = __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
-        }
-    }
-
-    // Block merge of the waves: M = max_w m_w, acc = sum_w 2^(m_w - M) acc_w, same for l.
-    float *wacc = smem + SM::vbuf;  // reuse: [waves][G][128]
+    // Block merge of the waves: the wave's accumulator in the 2^(s - m)
+    // scale, then M = max_w m_w, acc = sum_w 2^(m_w - M) acc_w, same for l.
+    float *wacc = smem + SM::stage;  // reuse: [waves][G][128]
     float *wm = smem + SM::wm;
     float *wl = smem + SM::wl;
-    __syncthreads();  // all waves done with vbuf / wbuf
-    {
-        // level-1 result i holds accumulator 2i (lanes 0-31) and 2i+1 (lanes
-        // 32-63); level 2 combined level-1 results 2i (rows 0, 2 -> rows 0, 2)
-        // and 2i+1 (rows 1, 3): row k of red[i] is accumulator
-        // {4i, 4i+2, 4i+1, 4i+3}[k]
-        const int k = ph;
-        const int sel = (k == 0) ? 0 : (k == 1) ? 2 : (k == 2) ? 1 : 3;
+    const float fv = mv_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mv_run - m_run);
+    __syncthreads();  // all waves done with their staging areas
+    if (kg < G) {
+        float r[8];
 #pragma unroll
-        for (int i = 0; i < NA / 4; ++i) {
-            const int a = 4 * i + sel, h = a >> 3, j = a & 7;
-            wacc[(wv * G + h) * kD + 8 * co + j] = red[i];
+        for (int nb = 0; nb < 8; ++nb) r[nb] = (acc[nb][0] + acc[nb][1]) * fv;
+        f4_t *dst = reinterpret_cast<f4_t *>(wacc + (wv * G + kg) * kD + 8 * n);
+        dst[0] = f4_t{r[0], r[1], r[2], r[3]};
+        dst[1] = f4_t{r[4], r[5], r[6], r[7]};
+        if (n == 0) {
+            wm[wv * G + kg] = m_run;
+            wl[wv * G + kg] = l_run;
         }
     }
-    if (lane == 0)
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            wm[wv * G + h] = m_run[h];
-            wl[wv * G + h] = l_run[h];
-        }
     __syncthreads();
     float *my = part + ((bh * n_split + split) * G) * (kD + 2);
     for (int idx = tid; idx < G * kD; idx += kDecThreads) {
@@ -682,7 +821,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
     // f_s = 2^(m_s - M) / (d L) with M = max_s m_s, L = sum_s l_s 2^(m_s - M);
     // lane l accumulates coordinates 2l, 2l+1 over the splits, then the
     // inverse rotation out = D_V .* H (sum_s f_s acc_s) in the same wave.
-    float *fw = smem + SM::vbuf;  // reuse: [G][n_split] merge weights
+    float *fw = smem + SM::stage;  // reuse: [G][n_split] merge weights
     const float *all = part + (bh * n_split) * G * (kD + 2);
     const int64_t sst = (int64_t)G * (kD + 2);  // split stride
     constexpr int kPerLane = kMaxSplits / 64;
