@@ -347,7 +347,7 @@ struct DecSmem {
     static constexpr int total = stage + kDecWaves * STG;
     // end-of-block reuse of the staging area: per-wave accumulators, split merge
     static_assert(kDecWaves * STG >= kDecWaves * G * kD, "wave merge buffer does not fit");
-    static_assert(kDecWaves * STG >= kMaxSplits * G, "split merge buffer does not fit");
+    static_assert(kDecWaves * STG >= kDecWaves * (kMaxSplits + kD), "split merge buffers do not fit");
 };
 
 // Cross-row exchanges on the VALU (gfx950 lane swaps): with the same value in
@@ -538,13 +538,10 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
     // i.e. until the memory system had accepted the whole block's tiles.
     // Wave h < G rotates query head h and publishes it in LDS with a count;
     // the other waves issue their loads and then wait for the count.  The
-    // count is cleared behind the one barrier at the start, when no memory
-    // operation is outstanding yet.
+    // count is cleared behind the one barrier at the start, which also puts
+    // the block's query loads ahead of all of its record loads (lane l loads
+    // coordinates 2l, 2l+1 of head wv).
     unsigned *ready = reinterpret_cast<unsigned *>(smem + SM::flag) + 1;
-    if (tid == 0) *ready = 0u;
-    __syncthreads();
-    // The query loads go out first (memory operations complete in issue
-    // order): lane l holds coordinates 2l, 2l+1 of head wv.
     uint32_t qv = 0u;
     f2_t qs = f2_t{0.0f, 0.0f};
     if (wv < G) {
@@ -553,6 +550,8 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
     }
     // the centroids too: indexed at run time, they are read from memory
     const float cen = cb.c[lane & 15];
+    if (tid == 0) *ready = 0u;
+    __syncthreads();
     // The records of the wave's next tile are held in registers: loaded before
     // the prologue for the first tile; for the others, the keys once the
     // current logits are formed and the values once the current value
@@ -777,6 +776,13 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
         }
     }
     __syncthreads();
+    // The split partials are written and read with device-scope (coherent,
+    // written-through) accesses, so handing them over needs no cache
+    // write-back or invalidation: once a wave's stores are complete
+    // (vmcnt(0)) they are visible to every compute unit, the barrier orders
+    // the arrival count after all of them, and the merging block reads them
+    // at device scope after seeing the count.
+    auto st_dev = [](float *p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
     float *my = part + ((bh * n_split + split) * G) * (kD + 2);
     for (int idx = tid; idx < G * kD; idx += kDecThreads) {
         const int h = idx >> 7, i = idx & (kD - 1);
@@ -790,50 +796,51 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
             A = fmaf(f, wacc[(w * G + h) * kD + i], A);
             L = fmaf(f, wl[w * G + h], L);
         }
-        my[h * (kD + 2) + 2 + i] = A;
+        st_dev(my + h * (kD + 2) + 2 + i, A);
         if (i == 0) {
-            my[h * (kD + 2)] = M;
-            my[h * (kD + 2) + 1] = L;
+            st_dev(my + h * (kD + 2), M);
+            st_dev(my + h * (kD + 2) + 1, L);
         }
     }
 
-    // Arrival: the last split of (b, g) merges.  Each wave waits for its own
-    // partial stores, the barrier joins the waves, and one device-scope release by thread 0 then
-    // publishes them (the L2 write-back it implies is a whole-cache operation,
-    // so one per block suffices) before the counter is incremented.  The last
-    // block performs one device-scope acquire (L2 invalidate) before reading
-    // the other blocks' partials.
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's stores have reached L2
+    // Arrival: the last split of (b, g) to finish merges.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's partial stores are complete
     __syncthreads();
     unsigned &last = *reinterpret_cast<unsigned *>(smem + SM::flag);
-    if (wv == 0) {  // wave-uniform: cache write-back / invalidate act per wave
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    if (wv == 0) {
         unsigned prev = 0;
-        if (lane == 0) prev = atomicAdd(counters + bh, 1u);
+        if (lane == 0) prev = __hip_atomic_fetch_add(counters + bh, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const unsigned is_last = __builtin_amdgcn_readfirstlane(prev) == (unsigned)(n_split - 1);
-        if (is_last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         if (lane == 0) last = is_last;
     }
     __syncthreads();
     if (!last) return;
 
-    // Merge of the splits, one wave per head (the other waves are done):
-    // f_s = 2^(m_s - M) / (d L) with M = max_s m_s, L = sum_s l_s 2^(m_s - M);
-    // lane l accumulates coordinates 2l, 2l+1 over the splits, then the
-    // inverse rotation out = D_V .* H (sum_s f_s acc_s) in the same wave.
-    float *fw = smem + SM::stage;  // reuse: [G][n_split] merge weights
-    const float *all = part + (bh * n_split) * G * (kD + 2);
-    const int64_t sst = (int64_t)G * (kD + 2);  // split stride
+    // Merge of the splits: f_s = 2^(m_s - M) / (d L) with M = max_s m_s,
+    // L = sum_s l_s 2^(m_s - M), acc = sum_s f_s acc_s, then the inverse
+    // rotation out = D_V .* H acc.  The kDecWaves / G waves of head h = w % G
+    // each take every (kDecWaves / G)-th split (lane l: coordinates 2l, 2l+1)
+    // and one of them sums their partial sums and rotates.
+    auto ld_dev = [](const float *p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+    auto ld_dev2 = [](const float *p) {  // two floats at an 8-byte aligned address
+        return __builtin_bit_cast(f2_t, __hip_atomic_load(reinterpret_cast<const uint64_t *>(p), __ATOMIC_RELAXED,
+                                                          __HIP_MEMORY_SCOPE_AGENT));
+    };
+    constexpr int WPH = kDecWaves / G;                   // waves per head
     constexpr int kPerLane = kMaxSplits / 64;
-    for (int h = wv; h < G; h += kDecWaves) {
-        const float *ah = all + h * (kD + 2);
+    const int mh = wv % G, mj = wv / G;
+    float *fh = smem + SM::stage + wv * kMaxSplits;       // reuse: this wave's merge weights [n_split]
+    float *pacc = smem + SM::stage + kDecWaves * kMaxSplits;  // [waves][128] partial sums
+    const float *ah = part + (bh * n_split) * G * (kD + 2) + mh * (kD + 2);
+    const int64_t sst = (int64_t)G * (kD + 2);  // split stride
+    {
         float mv[kPerLane], lv[kPerLane];
         float M = -INFINITY;
 #pragma unroll
         for (int k = 0; k < kPerLane; ++k) {
             const int sp = lane + 64 * k;
-            mv[k] = sp < n_split ? ah[sp * sst] : -INFINITY;
-            lv[k] = sp < n_split ? ah[sp * sst + 1] : 0.0f;
+            mv[k] = sp < n_split ? ld_dev(ah + sp * sst) : -INFINITY;
+            lv[k] = sp < n_split ? ld_dev(ah + sp * sst + 1) : 0.0f;
             M = fmaxf(M, mv[k]);
         }
         M = wave_max(M);
@@ -842,7 +849,6 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
         for (int k = 0; k < kPerLane; ++k) L = fmaf(lv[k], __builtin_amdgcn_exp2f(mv[k] - M), L);
         L = wave_sum(L);
         const float inv = 1.0f / (L * kD);
-        float *fh = fw + h * n_split;
 #pragma unroll
         for (int k = 0; k < kPerLane; ++k) {
             const int sp = lane + 64 * k;
@@ -851,27 +857,39 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
         wave_lds_sync();
         const float *col = ah + 2 + 2 * lane;
         float a0 = 0.0f, a1 = 0.0f;
-        int sp = 0;
-        for (; sp + 16 <= n_split; sp += 16) {  // 16 independent loads in flight
-            f2_t v[16];
+        int sp = mj;
+        for (; sp + 7 * WPH < n_split; sp += 8 * WPH) {  // 8 independent loads in flight
+            f2_t v[8];
 #pragma unroll
-            for (int u = 0; u < 16; ++u) v[u] = *reinterpret_cast<const f2_t *>(col + (sp + u) * sst);
+            for (int u = 0; u < 8; ++u) v[u] = ld_dev2(col + (sp + u * WPH) * sst);
 #pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                a0 = fmaf(fh[sp + u], v[u].x, a0);
-                a1 = fmaf(fh[sp + u], v[u].y, a1);
+            for (int u = 0; u < 8; ++u) {
+                a0 = fmaf(fh[sp + u * WPH], v[u].x, a0);
+                a1 = fmaf(fh[sp + u * WPH], v[u].y, a1);
             }
         }
-        for (; sp < n_split; ++sp) {
-            const f2_t v = *reinterpret_cast<const f2_t *>(col + sp * sst);
+        for (; sp < n_split; sp += WPH) {
+            const f2_t v = ld_dev2(col + sp * sst);
             a0 = fmaf(fh[sp], v.x, a0);
             a1 = fmaf(fh[sp], v.y, a1);
         }
+        reinterpret_cast<f2_t *>(pacc + wv * kD)[lane] = f2_t{a0, a1};
+    }
+    __syncthreads();
+    if (mj == 0) {
+        float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+        for (int j = 0; j < WPH; ++j) {
+            const f2_t v = reinterpret_cast<const f2_t *>(pacc + (j * G + mh) * kD)[lane];
+            a0 += v.x;
+            a1 += v.y;
+        }
         wave_fwht(a0, a1, lane);
         const f2_t sv = reinterpret_cast<const f2_t *>(signs_v + g * kD)[lane];
-        reinterpret_cast<f2_t *>(out + ((b * Hq) + (int64_t)g * G + h) * kD)[lane] = f2_t{a0 * sv.x, a1 * sv.y};
+        reinterpret_cast<f2_t *>(out + ((b * Hq) + (int64_t)g * G + mh) * kD)[lane] = f2_t{a0 * sv.x, a1 * sv.y};
     }
-    if (tid == 0) counters[bh] = 0u;  // leave the counter ready for the next call
+    if (tid == 0)  // leave the counter ready for the next call
+        __hip_atomic_store(counters + bh, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int BITS, int G, bool QJL>
