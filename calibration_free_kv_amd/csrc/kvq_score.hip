@@ -4,14 +4,16 @@
 // inner products) and one decode step of attention over the quantised cache
 // ("PolarQuant", Technical summary sec. 2 for the dequantisation).
 //
-// Both kernels start with the same prologue per (batch, KV head): the G query
-// heads of the group are rotated once in LDS, q' = H (D_K .* q), and turned
-// into lookup tables over fields of the packed key record.  A field holds the
-// codes of F consecutive coordinates (F = 2 for b <= 3, F = 1 for b = 4), and
-// entry e of field f of head h is sum_k q'_h[F f + k] c[code_k(e)] / d.  A
-// key's logit is then rho times the sum of one table entry per field, which
-// replaces 128 multiply-adds per head with 128/F LDS reads that serve all G
-// heads at once (the G entries of one (field, value) pair are contiguous).
+// Both kernels rotate the G query heads of a (batch, KV head) group once,
+// q' = H (D_K .* q).  The logits kernel turns them into lookup tables over
+// fields of the packed key record.  A field holds the codes of F consecutive
+// coordinates (F = 2 for b <= 3, F = 1 for b = 4), and entry e of field f of
+// head h is sum_k q'_h[F f + k] c[code_k(e)] / d.  A key's logit is then rho
+// times the sum of one table entry per field, which replaces 128
+// multiply-adds per head with 128/F LDS reads that serve all G heads at once
+// (the G entries of one (field, value) pair are contiguous).  The decode
+// kernel instead runs its two contractions (logits over coordinates, values
+// over tokens) on the matrix cores; see its own description below.
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -548,8 +550,6 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
         qv = reinterpret_cast<const uint32_t *>(q + ((int64_t)b * Hq + (int64_t)g * G + wv) * kD)[lane];
         qs = reinterpret_cast<const f2_t *>(signs_k + g * kD)[lane];
     }
-    // the centroids too: indexed at run time, they are read from memory
-    const float cen = cb.c[lane & 15];
     if (tid == 0) *ready = 0u;
     __syncthreads();
     // The records of the wave's next tile are held in registers: loaded before
@@ -603,8 +603,12 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
     float *ctab = smem + SM::ctab;
     float *qf = smem + SM::qf;
     _Float16 *qh = reinterpret_cast<_Float16 *>(smem + SM::qh);
-    // centroid tables: every wave writes the same values and reads back its own
-    if (lane < 16) ctab[lane] = cen;
+    // centroid tables: every wave writes the same values and reads back its
+    // own (the centroids are kernel arguments at constant offsets: scalar loads)
+    if (lane == 0) {
+#pragma unroll
+        for (int k = 0; k < (1 << BITS); ++k) ctab[k] = cb.c[k];
+    }
     // rows of the weight operand that no head writes stay zero
     for (int i = lane; i < 8 * SM::PS; i += 64) stg[SM::PT + i] = 0u;
     if (wv == 0) reinterpret_cast<uint32_t *>(qh + 2 * G * SM::QS)[lane] = 0u;  // the zero query row
