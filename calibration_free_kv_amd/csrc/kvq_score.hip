@@ -564,25 +564,28 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
     float rk = 0.0f, rv = 0.0f;
     // Addresses: a wave-uniform 64-bit base for the tile plus a 32-bit lane
     // offset (scalar-base loads).
-    auto fetch_k = [&](int64_t t0) {
-        t0 = min(t0, t_end - 1);  // a wave without a tile loads the range's last token
+    // t0 < t_end; `last` = min(63, t_end - 1 - t0), the tile's last valid
+    // token (32-bit scalar arithmetic: the scalar unit has no 64-bit compare).
+    auto tile_last = [&](int64_t t0) { return (uint32_t)min((int)(t_end - t0) - 1, 63); };
+    auto fetch_k = [&](int64_t t0, uint32_t last) {
         const int64_t v0 = bh * T + t0;
-        const uint32_t last = (uint32_t)min((int64_t)63, t_end - 1 - t0);  // last valid token of the tile
         const uint32_t l = min((uint32_t)lane, last);
         const char *kb = reinterpret_cast<const char *>(kc) + v0 * (16 * BITS);
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
             const uint32_t t = min((uint32_t)(16 * rg + n), last);
-            const uint32_t *src = reinterpret_cast<const uint32_t *>(kb + (t * (16u * BITS) + 4u * BITS * kg));
+            // opaque, so that the lane part stays out of the (scalar) base
+            uint32_t off = t * (16u * BITS) + 4u * BITS * kg;
+            asm volatile("" : "+v"(off));
+            const uint32_t *src = reinterpret_cast<const uint32_t *>(kb + off);
 #pragma unroll
             for (int i = 0; i < BITS; ++i) Kw[rg][i] = src[i];
         }
         rk = *reinterpret_cast<const float *>(reinterpret_cast<const char *>(kn + v0) + 4 * l);
     };
-    auto fetch_v = [&](int64_t t0) {
-        t0 = min(t0, t_end - 1);
+    auto fetch_v = [&](int64_t t0, uint32_t last) {
         const int64_t v0 = bh * T + t0;
-        const uint32_t l = min((uint32_t)lane, (uint32_t)min((int64_t)63, t_end - 1 - t0));
+        const uint32_t l = min((uint32_t)lane, last);
         const u4_t *vs = reinterpret_cast<const u4_t *>(reinterpret_cast<const char *>(vc) + v0 * (16 * BITS) +
                                                           l * (16u * BITS));
 #pragma unroll
@@ -597,8 +600,12 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
     };
     constexpr int64_t kStride = (int64_t)kDecWaves * 64;
     __builtin_amdgcn_sched_barrier(0);  // keep the prologue's loads ahead of the records
-    fetch_k(t_begin + (int64_t)wv * 64);
-    fetch_v(t_begin + (int64_t)wv * 64);
+    {
+        // a wave without a tile loads the range's last token
+        const int64_t t0 = t_begin + min(wv * 64, (int)(t_end - t_begin) - 1);
+        fetch_k(t0, tile_last(t0));
+        fetch_v(t0, tile_last(t0));
+    }
 
     float *ctab = smem + SM::ctab;
     float *qf = smem + SM::qf;
@@ -668,9 +675,16 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
     for (int nb = 0; nb < 8; ++nb) acc[nb] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
     const int obit = 8 * BITS * n, ow = obit >> 5, osh = obit & 31;
 
-    for (int64_t t0 = t_begin + (int64_t)wv * 64; t0 < t_end; t0 += kStride) {
-        const int nt = (int)min((int64_t)64, t_end - t0);
-        const bool more = t0 + kStride < t_end;
+    // token positions relative to the range start, in 32-bit scalar registers
+    const int span = (int)(t_end - t_begin);
+    for (int rel = wv * 64; rel < span; rel += (int)kStride) {
+        const int nt = min(64, span - rel);
+        const bool more = rel + (int)kStride < span;
+        // start of the next tile, opaque so that the whole of it stays in the
+        // scalar base of the loads rather than in the lane offsets
+        int64_t tn = t_begin + rel + kStride;
+        asm volatile("" : "+s"(tn));
+        const uint32_t lastn = (uint32_t)min(span - rel - (int)kStride - 1, 63);
         // logits of tokens 16 rg + n for head kg (rows 4 kg, 4 kg + 1)
         float s[4];
 #pragma unroll
@@ -681,7 +695,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
         float rkb[4], lvb[4];
         row_broadcast(rk, rkb);
         row_broadcast(__builtin_amdgcn_logf(rv), lvb);  // log2 rho_V; -inf for a zero vector
-        if (more) fetch_k(t0 + kStride);  // this tile's keys are consumed
+        if (more) fetch_k(tn, lastn);  // this tile's keys are consumed
         // stage the V records transposed: dword w of token `lane` at [w][lane]
 #pragma unroll
         for (int w = 0; w < W; ++w) stg[SM::VS * w + lane] = Vw[w];
@@ -756,7 +770,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
             KVQ_VSTEP(7, b1, b0)
 #undef KVQ_VSTEP
         }
-        if (more) fetch_v(t0 + kStride);
+        if (more) fetch_v(tn, lastn);
         wave_lds_sync();  // the staging area is rewritten by the next tile
     }
 
