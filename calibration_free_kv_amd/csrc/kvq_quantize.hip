@@ -317,6 +317,7 @@ __global__ __launch_bounds__(kWavesQ * 64) __attribute__((amdgpu_waves_per_eu(4,
     issue(tile);
     int64_t next = blockIdx.x + take_rows<0>(L, lane, w, &next_tile) * G;
     if (next < total) issue(next);
+    int64_t pending = total;  // a drawn tile whose copy is not yet issued
     for (;;) {
         const int kt = tile >= n_tiles;
         const TileGeom g = geom<kTileH>(tile - kt * n_tiles, T, H, tiles_per_bh);
@@ -354,6 +355,13 @@ __global__ __launch_bounds__(kWavesQ * 64) __attribute__((amdgpu_waves_per_eu(4,
         for (int i = 0; i < 64; i += 8) pair_fmac8(y + i, cross);
         // Both lanes form the same sum (fp32 addition commutes).
         ss += pair_swap(ss);
+        // The copy of the tile after next goes out here, half an encode
+        // before its wait: issued a whole encode ahead, the copies of all
+        // waves kept about twice the data in flight that the memory system
+        // needs to stay busy, and every request waited correspondingly longer
+        // in its queues (which shows at the start and at the end of the grid).
+        if (pending < total) issue(pending);
+        pending = total;
 
         const float rho = __builtin_sqrtf(ss);
         const float r = rho > 0.0f ? rho : 1.0f;  // zero vector: y = 0 -> index L/2 - 1
@@ -396,7 +404,7 @@ __global__ __launch_bounds__(kWavesQ * 64) __attribute__((amdgpu_waves_per_eu(4,
         int64_t after = total;
         if (has_next) {
             after = blockIdx.x + take_rows<0>(L, lane, w, &next_tile) * G;
-            if (after < total) issue(after);
+            pending = after;
         }
         if ((lane >> 1) < g.nv) {  // lanes past a ragged tail encoded stale rows
             // the lanes of the tile write 64 * 8 BITS contiguous bytes
