@@ -12,7 +12,9 @@ set s + 2, written two steps earlier, so they are not served from that cache.
 value = (K and V vectors quantised + keys scored) per second of the whole step.
 roofline = the dominant kernel (kvq_quantize_kv): algorithmic bytes per launch
 (fp16 input, packed codes, fp32 norms) / mean launch duration from HIP events
-recorded on the stream the kernels run on.  traffic = HBM bytes per launch
+recorded on the stream the kernels run on, in a second pass of as many steps
+right after the timed ones (events between the kernels would otherwise sit
+inside the timed steps).  traffic = HBM bytes per launch
 from the committed rocprofv3 counter record for the same kernel source, or
 null when the kernel source has changed since the counters were taken.
 
@@ -194,15 +196,22 @@ def main_step(torch, kvq, synth, args, dev, timer):
     for s in range(args.warmup):
         step(s)
     torch.cuda.synchronize()
-    evs = [[E() for _ in range(3)] for _ in range(args.steps)]
+    # The K timed steps carry no events of their own (each event is a command
+    # in the stream that separates the kernels).  A second pass of K steps,
+    # right after, brackets every launch with events on the launching stream
+    # for the per-kernel durations of the roofline.
     t_start, t_end = E(), E()
     torch.cuda.synchronize()
     t_start.record(stream)
     for s in range(args.steps):
-        step(args.warmup + s, evs[s])
+        step(args.warmup + s)
     t_end.record(stream)
     torch.cuda.synchronize()
     ms_step = t_start.elapsed_time(t_end) / args.steps
+    evs = [[E() for _ in range(3)] for _ in range(args.steps)]
+    for s in range(args.steps):
+        step(args.warmup + args.steps + s, evs[s])
+    torch.cuda.synchronize()
     q_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     d_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
 

@@ -317,6 +317,7 @@ __global__ __launch_bounds__(kWavesQ * 64) __attribute__((amdgpu_waves_per_eu(4,
     issue(tile);
     int64_t next = blockIdx.x + take_rows<0>(L, lane, w, &next_tile) * G;
     if (next < total) issue(next);
+    constexpr bool kMidIssue = BITS <= 3;
     int64_t pending = total;  // a drawn tile whose copy is not yet issued
     for (;;) {
         const int kt = tile >= n_tiles;
@@ -360,8 +361,12 @@ __global__ __launch_bounds__(kWavesQ * 64) __attribute__((amdgpu_waves_per_eu(4,
         // waves kept about twice the data in flight that the memory system
         // needs to stay busy, and every request waited correspondingly longer
         // in its queues (which shows at the start and at the end of the grid).
-        if (pending < total) issue(pending);
-        pending = total;
+        // At b = 4 the register held for it over the transform costs spills,
+        // and the copy goes out right after the row reads instead.
+        if constexpr (kMidIssue) {
+            if (pending < total) issue(pending);
+            pending = total;
+        }
 
         const float rho = __builtin_sqrtf(ss);
         const float r = rho > 0.0f ? rho : 1.0f;  // zero vector: y = 0 -> index L/2 - 1
@@ -404,7 +409,10 @@ __global__ __launch_bounds__(kWavesQ * 64) __attribute__((amdgpu_waves_per_eu(4,
         int64_t after = total;
         if (has_next) {
             after = blockIdx.x + take_rows<0>(L, lane, w, &next_tile) * G;
-            pending = after;
+            if constexpr (kMidIssue)
+                pending = after;
+            else if (after < total)
+                issue(after);
         }
         if ((lane >> 1) < g.nv) {  // lanes past a ragged tail encoded stale rows
             // the lanes of the tile write 64 * 8 BITS contiguous bytes
