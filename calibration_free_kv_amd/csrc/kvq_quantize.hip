@@ -128,19 +128,47 @@ struct TileGeom {
     int h;       // KV head
 };
 
+// floor(n / d) for 0 <= n < 2^31 and 1 <= d < 2^31 as (umulhi(n, m) + n) >> l,
+// with l = ceil(log2 d) and m = ceil(2^(32+l) / d) - 2^32 (Granlund and
+// Montgomery, "Division by invariant integers using multiplication", 1994):
+// a few scalar instructions instead of a 64-bit division sequence.
+struct FastDiv {
+    uint32_t m, l;
+};
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) { return (__umulhi(n, f.m) + n) >> f.l; }
+
+// Tile index -> (batch, head) row block: tiles_per_bh tiles of TILE vectors
+// per (batch, head), T vectors each, H heads.
+struct TileMap {
+    int64_t T;
+    uint32_t tiles_per_bh, H;
+    FastDiv by_tiles, by_H;
+};
+
+// Host side: the map of a launch.
+FastDiv make_fastdiv(uint32_t d)
+{
+    uint32_t l = 0;
+    while ((1ull << l) < d) ++l;
+    const uint64_t m = ((1ull << (32 + l)) - 1) / d + 1;  // ceil(2^(32+l) / d), l <= 31
+    return FastDiv{(uint32_t)(m - (1ull << 32)), l};
+}
+
+TileMap make_map(int64_t T, int H, int64_t tiles_per_bh)
+{
+    return TileMap{T, (uint32_t)tiles_per_bh, (uint32_t)H, make_fastdiv((uint32_t)tiles_per_bh),
+                   make_fastdiv((uint32_t)H)};
+}
+
 template <int TILE = kTile>
-__device__ __forceinline__ TileGeom geom(int64_t tile, int64_t T, int H, int64_t tiles_per_bh)
+__device__ __forceinline__ TileGeom geom(uint32_t tile, const TileMap &mp)
 {
     TileGeom g;
-    // opaque divisors: the compiler would otherwise hoist their float
-    // conversions (for the division) out of the persistent loop and spill them,
-    // and every reload would wait for all outstanding memory operations
-    asm volatile("" : "+s"(tiles_per_bh), "+s"(H));
-    const int64_t bh = tile / tiles_per_bh;
-    const int64_t t0 = (tile - bh * tiles_per_bh) * TILE;
-    g.v0 = bh * T + t0;
-    g.nv = (int)min((int64_t)TILE, T - t0);
-    g.h = (int)(bh % H);
+    const uint32_t bh = fdiv(tile, mp.by_tiles);
+    const uint32_t t0 = (tile - bh * mp.tiles_per_bh) * TILE;
+    g.v0 = (int64_t)bh * mp.T + t0;
+    g.nv = (int)min((int64_t)TILE, mp.T - t0);
+    g.h = (int)(bh - fdiv(bh, mp.by_H) * mp.H);
     return g;
 }
 
@@ -290,7 +318,7 @@ struct QArgs {
 // cross-lane butterfly stage (lower lane: a - (-b), upper lane: -b + a).
 template <int BITS>
 __global__ __launch_bounds__(kWavesQ * 64) __attribute__((amdgpu_waves_per_eu(4, 4))) void k_quantize(
-    QArgs a, const uint32_t *__restrict__ sgnh, HalfThresholds ht, int64_t T, int H, int64_t tiles_per_bh,
+    QArgs a, const uint32_t *__restrict__ sgnh, HalfThresholds ht, TileMap mp,
     int64_t n_tiles, int n_tensors)
 {
     __shared__ u4_t lds[kWavesQ][kBufH];  // 132 KiB
@@ -308,8 +336,8 @@ __global__ __launch_bounds__(kWavesQ * 64) __attribute__((amdgpu_waves_per_eu(4,
     if (tile >= total) return;  // wave-uniform
     auto issue = [&](int64_t t) {
         const int k = t >= n_tiles;
-        const TileGeom gg = geom<kTileH>(t - k * n_tiles, T, H, tiles_per_bh);
-        tile_to_lds(a.x[k] + gg.v0 * 16, gg.nv, sgnh + (a.kind[k] * H + gg.h) * 64, L, lane);
+        const TileGeom gg = geom<kTileH>((uint32_t)(t - k * n_tiles), mp);
+        tile_to_lds(a.x[k] + gg.v0 * 16, gg.nv, sgnh + (a.kind[k] * (int)mp.H + gg.h) * 64, L, lane);
     };
     // cross-lane stage: lower lane a - (-b) = a + b, upper lane -b + a = a - b
     const float cross = (lane & 1) ? 1.0f : -1.0f;
@@ -321,7 +349,7 @@ __global__ __launch_bounds__(kWavesQ * 64) __attribute__((amdgpu_waves_per_eu(4,
     int64_t pending = total;  // a drawn tile whose copy is not yet issued
     for (;;) {
         const int kt = tile >= n_tiles;
-        const TileGeom g = geom<kTileH>(tile - kt * n_tiles, T, H, tiles_per_bh);
+        const TileGeom g = geom<kTileH>((uint32_t)(tile - kt * n_tiles), mp);
 
         // ||x||^2 of the half row with fp16 products (exact in fp32)
         // accumulated in fp32; D is already applied (signs do not change it).
@@ -664,7 +692,7 @@ constexpr int kWavesJ = 12;  // waves per workgroup of the QJL kernel
 
 template <int BITS, bool S_LO>
 __global__ __launch_bounds__(kWavesJ * 64) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_quantize_qjl(
-    QjlArgs a, const uint32_t *__restrict__ sgn, HalfThresholds ht, int64_t T, int H, int64_t tiles_per_bh,
+    QjlArgs a, const uint32_t *__restrict__ sgn, HalfThresholds ht, TileMap mp,
     int64_t n_tiles)
 {
     __shared__ u4_t Ss[kD * 16];              // S_hi, row n chunk c at slot n*16 + (c ^ (n & 15))
@@ -680,7 +708,7 @@ __global__ __launch_bounds__(kWavesJ * 64) __attribute__((amdgpu_waves_per_eu(3,
     int64_t tile = blockIdx.x + wv * G;
     if (tile >= n_tiles) return;  // wave-uniform
     auto issue = [&](int64_t t) {
-        const TileGeom gg = geom<kTileH>(t, T, H, tiles_per_bh);
+        const TileGeom gg = geom<kTileH>((uint32_t)(t), mp);
         qjl_tile_to_lds(a.x + gg.v0 * 16, gg.nv, sgn + gg.h * 64, L, lane);
     };
     const int v = lane & 31, h = lane >> 5;
@@ -692,7 +720,7 @@ __global__ __launch_bounds__(kWavesJ * 64) __attribute__((amdgpu_waves_per_eu(3,
     int64_t next = blockIdx.x + qjl_take_rows(L, lane, w, &next_tile) * G;
     if (next < n_tiles) issue(next);
     for (;;) {
-        const TileGeom g = geom<kTileH>(tile, T, H, tiles_per_bh);
+        const TileGeom g = geom<kTileH>((uint32_t)(tile), mp);
         float ss = 0.0f;
 #pragma unroll
         for (int k = 0; k < 32; ++k) {
@@ -842,12 +870,14 @@ hipError_t run_qjl(const kvq_ctx *ctx, const void *x, int64_t B, int64_t T, uint
     // one workgroup per CU, each with at least one tile
     int64_t blocks = n_tiles;
     if (blocks > (int64_t)ctx->n_cu) blocks = ctx->n_cu;
+    if (n_tiles >= (int64_t)1 << 31) return hipErrorInvalidValue;  // 32-bit tile indices
+    const TileMap mp = make_map(T, ctx->H, tiles_per_bh);
     if (a.S_lo)
         hipLaunchKernelGGL((k_quantize_qjl<BITS, true>), dim3((unsigned)blocks), dim3(kWavesJ * 64), 0, s, a,
-                           (const uint32_t *)ctx->d_sgnmask, ht, T, ctx->H, tiles_per_bh, n_tiles);
+                           (const uint32_t *)ctx->d_sgnmask, ht, mp, n_tiles);
     else
         hipLaunchKernelGGL((k_quantize_qjl<BITS, false>), dim3((unsigned)blocks), dim3(kWavesJ * 64), 0, s, a,
-                           (const uint32_t *)ctx->d_sgnmask, ht, T, ctx->H, tiles_per_bh, n_tiles);
+                           (const uint32_t *)ctx->d_sgnmask, ht, mp, n_tiles);
     return hipGetLastError();
 }
 
@@ -862,8 +892,10 @@ hipError_t run(const kvq_ctx *ctx, const QArgs &a, int n_tensors, int64_t B, int
     // one workgroup per CU, each with at least one tile
     int64_t blocks = n_tiles * n_tensors;
     if (blocks > (int64_t)ctx->n_cu) blocks = ctx->n_cu;
+    if (n_tiles * n_tensors >= (int64_t)1 << 31) return hipErrorInvalidValue;  // 32-bit tile indices
     hipLaunchKernelGGL(k_quantize<BITS>, dim3((unsigned)blocks), dim3(kWavesQ * 64), 0, s, a,
-                       (const uint32_t *)ctx->d_sgnmask_h, ht, T, ctx->H, tiles_per_bh, n_tiles, n_tensors);
+                       (const uint32_t *)ctx->d_sgnmask_h, ht, make_map(T, ctx->H, tiles_per_bh), n_tiles,
+                       n_tensors);
     return hipGetLastError();
 }
 
