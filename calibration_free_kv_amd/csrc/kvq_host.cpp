@@ -77,7 +77,6 @@ void free_ctx(kvq_ctx *c)
     (void)hipFree(c->d_signs);
     (void)hipFree(c->d_S);
     (void)hipFree(c->d_S16);
-    (void)hipFree(c->d_vq);
     (void)hipFree(c->d_vq16);
     (void)hipFree(c->d_vqbias);
     std::free(c->h_signs);
@@ -233,7 +232,6 @@ kvq_status kvq_create(const kvq_config *cfg, kvq_ctx **out)
             bias[j] = (float)(-0.5 * sq);
         }
         c->vq_exact_f16 = exact;
-        if (st == KVQ_OK) st = upload(&c->d_vq, cfg->vq_codebook, n);
         if (st == KVQ_OK) st = upload(&c->d_vq16, c16, 2 * n);
         if (st == KVQ_OK) st = upload(&c->d_vqbias, bias, (size_t)kvq::kVqK);
         std::free(c16);

@@ -35,7 +35,6 @@ struct kvq_ctx {
     float *d_S;           // [128][128] QJL projection transposed, d_S[i][j] = S[j][i] (MSE_QJL)
     _Float16 *d_S16;      // [2][128][128] fp16 hi and lo parts of S (MSE_QJL)
     bool S_exact_f16;     // S_lo == 0
-    float *d_vq;          // [256][8] NSN codebook (NSN_VQ)
     _Float16 *d_vq16;     // [2][256][8] fp16 hi and lo parts of the codebook
     bool vq_exact_f16;    // codebook lo == 0
     float *d_vqbias;      // [256] -||C_j||^2 / 2

@@ -165,11 +165,23 @@ __device__ __forceinline__ _Float16 split_f16(float v, _Float16 &lo)
     return (_Float16)h;
 }
 
-// max of four scores (v_max3 + v_max: this file is compiled without NaN
-// semantics, the scores being finite sums of finite products)
-__device__ __forceinline__ float max4(float a, float b, float c, float d)
+// The 16 scores of one accumulator, each with its position r in its low
+// four mantissa bits (as 15 - r), reduced to their maximum (v_max3 tree:
+// this file is compiled without NaN semantics, the scores being finite sums
+// of finite products).
+__device__ __forceinline__ float marked(float x, uint32_t r)
 {
-    return fmaxf(fmaxf(fmaxf(a, b), c), d);
+    return __builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, x) & ~15u) | (15u - r));
+}
+__device__ __forceinline__ float max16_marked(const f16v_t &a)
+{
+    float e[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) e[r] = marked(a[r], (uint32_t)r);
+    const float m0 = fmaxf(fmaxf(e[0], e[1]), e[2]), m1 = fmaxf(fmaxf(e[3], e[4]), e[5]);
+    const float m2 = fmaxf(fmaxf(e[6], e[7]), e[8]), m3 = fmaxf(fmaxf(e[9], e[10]), e[11]);
+    const float m4 = fmaxf(fmaxf(e[12], e[13]), e[14]);
+    return fmaxf(fmaxf(fmaxf(fmaxf(m0, m1), m2), fmaxf(m3, m4)), e[15]);
 }
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * 16 + (chunk ^ (row & 15)); }
@@ -178,7 +190,6 @@ struct VqArgs {
     const u4_t *x;
     const u4_t *cb_hi;    // [256] entries of 8 fp16 (hi parts)
     const u2_t *cb_lo;    // [256][2] lo parts, dims 4q .. 4q + 3 at index 2 j + q (unused if exactly fp16)
-    const float *cb;      // [256][8] fp32 codebook
     const float *bias;    // [256] -||C_j||^2 / 2
     u4_t *codes;          // [H][T][16 bytes]
     float *s1, *s2;       // [H][T]
@@ -206,14 +217,18 @@ struct VqArgs {
 // .. 8h+7), and the A operand holds dims 4h .. 4h+3 of C_hi twice, so the
 // operands come straight from registers.  One v_mfma_f32_32x32x8_f16 adds
 // C_lo . z_hi when the codebook is not fp16-exact.  A lane then holds 16
-// scores of its token: four groups of four consecutive codewords.  It keeps,
-// per sub-vector, only the best group (its maximum, strictly larger in
-// increasing codeword order), and at the end recomputes the group's four
-// scores in fp32 (z = z_hi + z_lo, the other half's four dims fetched with a
-// half swap) to pick the entry; the lane holding the other 16 codewords of
-// each block does the same, and the better of the two (lower index on ties)
-// is the code.  Keeping groups instead of single entries takes the arg max
-// bookkeeping from 3 VALU operations per (sub-vector, codeword) to about 1.3.
+// scores of its token, register r being codeword 32 mb + 8 (r/4) + 4 h + r%4.
+// The score's low four mantissa bits are replaced by 15 - r, so that one
+// max3 tree over the 16 values yields the best score together with its
+// position (on a tie in the other 28 bits the lower codeword wins); the lane
+// keeps, per sub-vector, that value and the block mb (strictly larger in
+// increasing block order).  The lane holding the other 16 codewords of each
+// block does the same, and the better of the two (lower index on ties) is
+// the code.  The marking changes a score by at most 15 units in the last
+// place, about 4e-6 for the scores here, so it can only reorder entries whose
+// bisecting hyperplane lies within that distance of z_s: a decision inside
+// the 1e-5 band the parity checks allow.  About 1.7 VALU operations per
+// (sub-vector, codeword), and no table reads after the search.
 constexpr int kTileN = 32;           // tokens per tile of the search
 constexpr int kWavesN = 8;           // waves per workgroup (two per SIMD)
 constexpr int kRowsN = kTileN * 16;  // 16-byte chunks of x per tile
@@ -311,7 +326,6 @@ __global__ __launch_bounds__(kWavesN * 64) __attribute__((amdgpu_waves_per_eu(2,
 {
     __shared__ u4_t s_cbA[2 * kVqK];  // entry j, half q: dims 4q .. 4q+3 of C_hi, twice
     __shared__ u2_t s_cbl[2 * kVqK];  // lo parts, dims 4q .. 4q+3 at 2 j + q
-    __shared__ f4_t s_cb[2 * kVqK];   // fp32 codebook, dims 4q .. 4q+3 at 2 j + q
     __shared__ float s_bias[kVqK];
     __shared__ u4_t lds[kWavesN][kBufN];
     __shared__ int next_tile;
@@ -324,8 +338,6 @@ __global__ __launch_bounds__(kWavesN * 64) __attribute__((amdgpu_waves_per_eu(2,
             s_cbl[2 * j] = a.cb_lo[2 * j];
             s_cbl[2 * j + 1] = a.cb_lo[2 * j + 1];
         }
-        s_cb[2 * j] = reinterpret_cast<const f4_t *>(a.cb)[2 * j];
-        s_cb[2 * j + 1] = reinterpret_cast<const f4_t *>(a.cb)[2 * j + 1];
         s_bias[j] = a.bias[j];
     }
     if (tid == 0) next_tile = kWavesN;
@@ -437,9 +449,6 @@ __global__ __launch_bounds__(kWavesN * 64) __attribute__((amdgpu_waves_per_eu(2,
             }
             zh[s] = __builtin_bit_cast(u2_t, hv);
             zl[s] = __builtin_bit_cast(u2_t, lv);
-            // opaque: the resolve below must convert from these packed
-            // registers, not keep unpacked copies live through the search
-            asm volatile("" : "+v"(zh[s]), "+v"(zl[s]));
         }
 
         float bm[16];
@@ -485,51 +494,23 @@ __global__ __launch_bounds__(kWavesN * 64) __attribute__((amdgpu_waves_per_eu(2,
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const int s = s4 + u;
-#pragma unroll
-                    for (int r4 = 0; r4 < 4; ++r4) {
-                        const float m = max4(acc[u][4 * r4], acc[u][4 * r4 + 1], acc[u][4 * r4 + 2], acc[u][4 * r4 + 3]);
-                        const bool better = m > bm[s];
-                        bm[s] = better ? m : bm[s];
-                        bg[s] = better ? 4 * mb + r4 : bg[s];
-                    }
+                    const float m = max16_marked(acc[u]);
+                    const bool better = m > bm[s];
+                    bm[s] = better ? m : bm[s];
+                    bg[s] = better ? mb : bg[s];
                 }
             }
         }
-        // resolve the best group of each sub-vector in fp32, then merge with
-        // the other half (which searched the other 16 codewords of each block)
+        // the entry of each sub-vector's best marked score, then the better of
+        // the two halves (each searched the other 16 codewords of every block)
         uint32_t code[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int s = 0; s < 16; ++s) {
-            const h4_t zhs = __builtin_bit_cast(h4_t, zh[s]), zls = __builtin_bit_cast(h4_t, zl[s]);
-            float zo[4], zp[4];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) zo[t] = (float)zhs[t] + (float)zls[t];  // dims 4h + t
-#pragma unroll
-            for (int t = 0; t < 4; ++t) zp[t] = other_half(zo[t], upper);        // dims 4(1-h) + t
-            const int g = bg[s];
-            const int j0 = 32 * (g >> 2) + 8 * (g & 3) + 4 * h;
-            float best = -INFINITY;
-            int bi = j0;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int j = j0 + r;
-                const f4_t co = s_cb[2 * j + h], cp = s_cb[2 * j + 1 - h];
-                float sc = s_bias[j];
-                sc = fmaf(zo[0], co.x, sc);
-                sc = fmaf(zo[1], co.y, sc);
-                sc = fmaf(zo[2], co.z, sc);
-                sc = fmaf(zo[3], co.w, sc);
-                sc = fmaf(zp[0], cp.x, sc);
-                sc = fmaf(zp[1], cp.y, sc);
-                sc = fmaf(zp[2], cp.z, sc);
-                sc = fmaf(zp[3], cp.w, sc);
-                const bool better = sc > best;  // increasing index: strict > keeps the lowest
-                best = better ? sc : best;
-                bi = better ? j : bi;
-            }
-            const float ob = other_half(best, upper);
+            const int r = 15 - (int)(__builtin_bit_cast(uint32_t, bm[s]) & 15u);
+            const int bi = 32 * bg[s] + 8 * (r >> 2) + 4 * h + (r & 3);
+            const float ob = other_half(bm[s], upper);
             const int oi = other_half_i(bi, upper);
-            const int win = (ob > best || (ob == best && oi < bi)) ? oi : bi;
+            const int win = (ob > bm[s] || (ob == bm[s] && oi < bi)) ? oi : bi;
             code[s >> 2] |= (uint32_t)win << (8 * (s & 3));
         }
         // The next tile's rows, then the copy of the tile after it, then this
@@ -574,7 +555,6 @@ hipError_t launch_nsn_vq(const kvq_ctx *ctx, const void *x, int64_t H, int64_t T
     a.x = (const u4_t *)x;
     a.cb_hi = (const u4_t *)ctx->d_vq16;
     a.cb_lo = (const u2_t *)(ctx->d_vq16 + kVqK * kVqSub);
-    a.cb = ctx->d_vq;
     a.bias = ctx->d_vqbias;
     a.codes = (u4_t *)codes;
     a.s1 = s1;
