@@ -30,23 +30,25 @@ typedef float f16v_t __attribute__((ext_vector_type(16)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kTile = 64;
-constexpr int kChunk = 1024;  // tokens per stats block
+constexpr int kChunk = 2048;  // tokens per stats block
 constexpr float kSqrtD = 11.313708498984761f;
 
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 __device__ __forceinline__ void wait_lgkm() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 // Skewed direct-to-LDS tile copy (chunk c of vector v lands in slot (c + v) % 16).
+// Always 16 copy instructions with every lane active (rows past nv re-read
+// the last row), so that a wait can count them.
 __device__ __forceinline__ void tile_to_lds(const u4_t *src, int nv, u4_t *L, int lane)
 {
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
         const int v = 4 * j + (lane >> 4);
         const int c = ((lane & 15) - v) & 15;
-        if (v < nv)
-            __builtin_amdgcn_global_load_lds(
-                (const __attribute__((address_space(1))) void *)(src + v * 16 + c),
-                (__attribute__((address_space(3))) void *)(L + j * 64), 16, 0, 0);
+        const int row = v < nv ? v : nv - 1;
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void *)(src + row * 16 + c),
+            (__attribute__((address_space(3))) void *)(L + j * 64), 16, 0, 0);
     }
 }
 
@@ -78,45 +80,67 @@ __device__ __forceinline__ float norm2_f16(const uint32_t *w)
 }
 
 // (1) partial sums over token chunks of a_t = sqrt(d) x_t / ||x_t||.
-// Block (h, chunk), 4 waves; lane = token for the norms, then lane = channel
-// pair for the sums (rows read back from the staged tile).
-__global__ __launch_bounds__(256) void k_nsn_stats(const u4_t *__restrict__ x, float *__restrict__ part,
-                                                    int64_t T, int n_chunks)
+// Block (h, chunk), kStatWaves waves with one 16 KiB tile buffer each.  A wave
+// waits for its tile, reads it into registers twice (lane = token: the whole
+// row for the norm; lane = channel pair: dword `lane` of every row), sends the
+// copy of its next tile into the freed buffer, and only then does the
+// arithmetic, so its next copy is in flight meanwhile.  Rows past the end of
+// the chunk hold a copy of the last row and get the factor 0.
+constexpr int kStatWaves = 8;
+__global__ __launch_bounds__(64 * kStatWaves) void k_nsn_stats(const u4_t *__restrict__ x,
+                                                               float *__restrict__ part, int64_t T, int n_chunks)
 {
-    __shared__ u4_t lds[4][kTile * 16];
-    __shared__ float red[4][kD];
+    __shared__ u4_t lds[kStatWaves][kTile * 16];  // 128 KiB
+    __shared__ float red[kStatWaves][kD];
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int h = blockIdx.x / n_chunks, chunk = blockIdx.x % n_chunks;
     const int64_t c0 = (int64_t)chunk * kChunk, c1 = min(T, c0 + kChunk);
+    const u4_t *xh = x + (int64_t)h * T * 16;
     u4_t *L = lds[wv];
+    const uint32_t *Ld = (const uint32_t *)L;
+    // dword `lane` of row t sits at 64 t + 4 ((lane / 4 + t) mod 16) + lane mod 4
+    int cofs[16];
+#pragma unroll
+    for (int b = 0; b < 16; ++b)
+        cofs[b] = 4 * (((lane >> 2) + b) & 15) + (lane & 3);
     float acc0 = 0.0f, acc1 = 0.0f;
-    for (int64_t t0 = c0 + (int64_t)wv * kTile; t0 < c1; t0 += 4 * kTile) {
+    int64_t t0 = c0 + (int64_t)wv * kTile;
+    if (t0 < c1)
+        tile_to_lds(xh + t0 * 16, (int)min((int64_t)kTile, c1 - t0), L, lane);
+    for (; t0 < c1; t0 += kStatWaves * kTile) {
         const int nv = (int)min((int64_t)kTile, c1 - t0);
-        tile_to_lds(x + ((int64_t)h * T + t0) * 16, nv, L, lane);
         wait_vm();
-        uint32_t w[64];
+        uint32_t w[64], col[kTile];
         read_row(L, lane, w);
+#pragma unroll
+        for (int t = 0; t < kTile; ++t)
+            col[t] = Ld[64 * t + cofs[t & 15]];
+        wait_lgkm();
+        __builtin_amdgcn_wave_barrier();
+        const int64_t tn = t0 + kStatWaves * kTile;
+        if (tn < c1)
+            tile_to_lds(xh + tn * 16, (int)min((int64_t)kTile, c1 - tn), L, lane);
         const float ss = norm2_f16(w);
         const float inv = (lane < nv && ss > 0.0f) ? kSqrtD / __builtin_sqrtf(ss) : 0.0f;
-        // lane = channel pair (2 lane, 2 lane + 1): dword `lane` of every row
-        for (int t = 0; t < nv; ++t) {
+#pragma unroll
+        for (int t = 0; t < kTile; ++t) {
             const float it = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, inv), t));
-            const u4_t v = L[t * 16 + (((lane >> 2) + t) & 15)];
-            const uint32_t d = (lane & 3) == 0 ? v.x : (lane & 3) == 1 ? v.y : (lane & 3) == 2 ? v.z : v.w;
-            const h2_t p = __builtin_bit_cast(h2_t, d);
+            const h2_t p = __builtin_bit_cast(h2_t, col[t]);
             acc0 = fmaf((float)p.x, it, acc0);
             acc1 = fmaf((float)p.y, it, acc1);
         }
-        wait_lgkm();
-        __builtin_amdgcn_wave_barrier();
     }
     red[wv][2 * lane] = acc0;
     red[wv][2 * lane + 1] = acc1;
     __syncthreads();
     if (threadIdx.x < kD) {
         const int i = threadIdx.x;
-        part[((int64_t)h * n_chunks + chunk) * kD + i] = (red[0][i] + red[1][i]) + (red[2][i] + red[3][i]);
+        float s = 0.0f;
+#pragma unroll
+        for (int k = 0; k < kStatWaves; ++k)
+            s += red[k][i];
+        part[((int64_t)h * n_chunks + chunk) * kD + i] = s;
     }
 }
 
@@ -548,7 +572,7 @@ hipError_t launch_nsn_vq(const kvq_ctx *ctx, const void *x, int64_t H, int64_t T
 {
     const int n_chunks = (int)((T + kChunk - 1) / kChunk);
     float *part = (float *)ws;
-    hipLaunchKernelGGL(k_nsn_stats, dim3((unsigned)(H * n_chunks)), dim3(256), 0, s, (const u4_t *)x, part, T,
+    hipLaunchKernelGGL(k_nsn_stats, dim3((unsigned)(H * n_chunks)), dim3(64 * kStatWaves), 0, s, (const u4_t *)x, part, T,
                        n_chunks);
     hipLaunchKernelGGL(k_nsn_mean, dim3((unsigned)H), dim3(kD * kMeanGroups), 0, s, part, o, T, n_chunks);
     VqArgs a{};
