@@ -130,3 +130,32 @@ def kmeans_init(seed: int, n: int, K: int = 256):
 def random_tensor(seed: int, shape, scale: float = 1.0, dtype=np.float16):
     rng = np.random.Generator(np.random.PCG64(seed))
     return (rng.standard_normal(shape) * scale).astype(dtype)
+
+
+def random_codes(seed: int, lead, bits: int, qjl_m: int = 0):
+    """Stand-in encoded keys for scoring at full size (no quantizer involved):
+    uniform packed code bytes [*lead, 16*bits], norms exp(N(3.4, 0.25^2)) (the
+    spread of ||x|| for the lognormal-scaled 128-vectors above), and with
+    qjl_m > 0 uniform sign bytes [*lead, qjl_m/8] and gamma ~ U(0.2, 0.5)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    lead = tuple(lead)
+    out = dict(codes=rng.integers(0, 256, size=lead + (16 * bits,), dtype=np.uint8),
+               norms=np.exp(rng.normal(3.4, 0.25, size=lead)).astype(np.float32))
+    if qjl_m:
+        out["qjl_signs"] = rng.integers(0, 256, size=lead + (qjl_m // 8,), dtype=np.uint8)
+        out["qjl_gamma"] = rng.uniform(0.2, 0.5, size=lead).astype(np.float32)
+    return out
+
+
+def random_nsn_codes(seed: int, lead, d: int = D, sub: int = 8, o_scale: float = 0.5):
+    """Stand-in NSN-VQ encoded vectors (no quantizer involved): entry indices
+    uniform over 256 [*lead, d/sub] u8, s1 = exp(N(1, 0.25^2)), s2 ~ U(0.6, 1.0)
+    (both fp32 [*lead]), and channel means o ~ N(0, o_scale^2) fp32
+    [*lead[:-1], d] (one per head; larger than zero-mean data gives, so that
+    the mean term is exercised)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    lead = tuple(lead)
+    return dict(codes=rng.integers(0, 256, size=lead + (d // sub,), dtype=np.uint8),
+                s1=np.exp(rng.normal(1.0, 0.25, size=lead)).astype(np.float32),
+                s2=rng.uniform(0.6, 1.0, size=lead).astype(np.float32),
+                o=(rng.standard_normal(lead[:-1] + (d,)) * o_scale).astype(np.float32))

@@ -1,9 +1,12 @@
 """GPU parity of the QJL residual path (kvq_quantize in MSE_QJL mode and
 kvq_logits with the QJL term) against the CPU oracle.
 
-Sign bits are compared on the GPU's own MSE codes (the oracle recomputes the
-residual from its double-precision rotation and the GPU's indices): exact
-except bits whose projection lies within 1e-5 * gamma of zero."""
+Sign bits and gamma are compared on every vector whose GPU indices equal the
+oracle's (all but the rare vectors with a flagged boundary flip, whose
+residual is a different vector; those are counted): exact except bits whose
+projection lies within 1e-5 * gamma of zero.  The logit tests score codes
+written by the oracle (small cases) or drawn by the seeded generator (full
+size); no GPU output feeds the oracle."""
 import numpy as np
 import pytest
 import torch
@@ -29,20 +32,46 @@ def check_qjl(inp, bits, S, o, where=None):
         bb, hh, tt = [a.ravel() for a in np.meshgrid(np.arange(B), np.arange(H), np.arange(T), indexing="ij")]
     else:
         bb, hh, tt = where
-    mism = 0
+    mism = skipped = 0
     for h in np.unique(hh):
         sel = hh == h
         xs = x[bb[sel], h, tt[sel]][None, None]
         ref = O.quantize(xs, inp["signs_k"][h:h + 1], bits, want_y=True)
-        gi = unpack_np(o["codes"][bb[sel], h, tt[sel]], bits)[None, None]
-        q = O.qjl(ref["y"], gi, S, bits)
-        np.testing.assert_allclose(o["qjl_gamma"][bb[sel], h, tt[sel]], q["gamma"][0, 0], rtol=1e-5, atol=1e-7)
-        gs = np.unpackbits(o["qjl_signs"][bb[sel], h, tt[sel]], axis=-1, bitorder="little")
-        rs = np.unpackbits(q["signs"][0, 0], axis=-1, bitorder="little")
-        bad = (gs != rs) & (q["flags"][0, 0] == 0)
+        q = O.qjl(ref["y"], ref["idx"], S, bits)
+        same = (unpack_np(o["codes"][bb[sel], h, tt[sel]], bits) == ref["idx"][0, 0]).all(-1)
+        skipped += int((~same).sum())
+        np.testing.assert_allclose(o["qjl_gamma"][bb[sel], h, tt[sel]][same], q["gamma"][0, 0][same],
+                                   rtol=1e-5, atol=1e-7)
+        gs = np.unpackbits(o["qjl_signs"][bb[sel], h, tt[sel]], axis=-1, bitorder="little")[same]
+        rs = np.unpackbits(q["signs"][0, 0], axis=-1, bitorder="little")[same]
+        bad = (gs != rs) & (q["flags"][0, 0][same] == 0)
         assert not bad.any(), "%d sign bits differ outside the 1e-5*gamma band" % int(bad.sum())
         mism += int((gs != rs).sum())
-    return mism
+    assert skipped <= max(2, len(hh) // 100), skipped
+    return mism, skipped
+
+
+def oracle_qjl_codes(inp, bits):
+    """Codes, fp32 norms, sign bits and fp32 gamma of every key, from the oracle."""
+    r = O.quantize(inp["k"], inp["signs_k"], bits, want_y=True)
+    q = O.qjl(r["y"], r["idx"], inp["S"], bits)
+    return dict(codes=r["codes"], norms=r["norms"].astype(np.float32), qjl_signs=q["signs"],
+                qjl_gamma=q["gamma"].astype(np.float32))
+
+
+def check_qjl_logits(inp, ctx, c, t=None):
+    g = {k: torch.from_numpy(np.ascontiguousarray(v)).cuda() for k, v in c.items()}
+    lg = to_np(ctx.logits(torch.from_numpy(inp["q"]).cuda(), g["codes"], g["norms"], g["qjl_signs"],
+                          g["qjl_gamma"]))
+    sub = (lambda a: a) if t is None else (lambda a: a[:, :, t])
+    ref = O.logits(inp["q"], sub(c["codes"]), sub(c["norms"]).astype(np.float64), inp["signs_k"], 2,
+                   qjl_signs=sub(c["qjl_signs"]), gamma=sub(c["qjl_gamma"]).astype(np.float64), S=inp["S"])
+    G = inp["Hq"] // inp["Hkv"]
+    scale = np.linalg.norm(inp["q"].astype(np.float64), axis=-1)[..., None] * np.repeat(sub(c["norms"]), G, axis=1)
+    err = np.abs(sub(lg) - ref) / np.maximum(scale, 1e-30)
+    assert err.max() <= 1e-3
+    assert err.max() <= 1e-5, err.max()
+    return err.max()
 
 
 @pytest.mark.parametrize("bits", [1, 2, 3, 4])
@@ -82,26 +111,15 @@ def test_qjl_zero_vector():
 @pytest.mark.parametrize("T", [1000, 4097])
 def test_qjl_logits(T):
     inp = synth.make("long128k_qjl", T=T)
-    ctx, o, out = run_qjl(inp, 2, inp["S"])
-    q = torch.from_numpy(inp["q"]).cuda()
-    lg = to_np(ctx.logits(q, out["codes"], out["norms"], out["qjl_signs"], out["qjl_gamma"]))
-    ref = O.logits(inp["q"], o["codes"], o["norms"].astype(np.float64), inp["signs_k"], 2,
-                   qjl_signs=o["qjl_signs"], gamma=o["qjl_gamma"].astype(np.float64), S=inp["S"])
-    G = inp["Hq"] // inp["Hkv"]
-    scale = np.linalg.norm(inp["q"].astype(np.float64), axis=-1)[..., None] * np.repeat(o["norms"], G, axis=1)
-    err = np.abs(lg - ref) / np.maximum(scale, 1e-30)
-    assert err.max() <= 1e-3
-    assert err.max() <= 1e-5, err.max()
+    ctx = kvq.Context(inp["Hkv"], 2, inp["signs_k"], inp["signs_v"], mode=kvq.KVQ_MODE_MSE_QJL, qjl_S=inp["S"])
+    print("max rel err", check_qjl_logits(inp, ctx, oracle_qjl_codes(inp, 2)))
 
 
 def test_qjl_logits_full_size_sampled():
+    """All 8 x 131072 keys as drawn by the seeded generator (uniform codes and
+    sign bits, lognormal norms and gamma); the oracle scores 2048 of them."""
     inp = synth.make("long128k_qjl")
-    ctx, o, out = run_qjl(inp, 2, inp["S"])
-    q = torch.from_numpy(inp["q"]).cuda()
-    lg = to_np(ctx.logits(q, out["codes"], out["norms"], out["qjl_signs"], out["qjl_gamma"]))
+    c = synth.random_codes(11, (1, inp["Hkv"], inp["T"]), 2, qjl_m=128)
+    ctx = kvq.Context(inp["Hkv"], 2, inp["signs_k"], inp["signs_v"], mode=kvq.KVQ_MODE_MSE_QJL, qjl_S=inp["S"])
     t = np.random.default_rng(9).integers(0, inp["T"], 2048)
-    ref = O.logits(inp["q"], o["codes"][:, :, t], o["norms"][:, :, t].astype(np.float64), inp["signs_k"], 2,
-                   qjl_signs=o["qjl_signs"][:, :, t], gamma=o["qjl_gamma"][:, :, t].astype(np.float64), S=inp["S"])
-    G = inp["Hq"] // inp["Hkv"]
-    scale = np.linalg.norm(inp["q"].astype(np.float64), axis=-1)[..., None] * np.repeat(o["norms"][:, :, t], G, axis=1)
-    assert (np.abs(lg[:, :, t] - ref) / scale).max() <= 1e-5
+    print("max rel err", check_qjl_logits(inp, ctx, c, t=t))

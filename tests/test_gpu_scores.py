@@ -1,7 +1,8 @@
 """GPU parity of kvq_logits and kvq_attn_decode against the CPU oracle.
 
-Both sides score the SAME packed codes (the GPU's), so decision-boundary
-flips in quantisation cannot leak into these tolerances: logits within
+Both sides score the SAME packed codes and fp32 norms, written by the
+oracle's quantizer (the GPU consumes them), so decision-boundary flips in
+quantisation cannot leak into these tolerances: logits within
 1e-3 * ||q|| ||k||, attention outputs within 2e-3 max-abs."""
 import numpy as np
 import pytest
@@ -14,11 +15,18 @@ from tests.gpu_util import needs_gpu, to_np
 pytestmark = [pytest.mark.gpu, needs_gpu]
 
 
+def oracle_codes(x, signs, bits):
+    """Packed codes and fp32 norms from the oracle's quantizer, on the GPU."""
+    r = O.quantize(x, signs, bits)
+    return dict(codes=torch.from_numpy(r["codes"]).cuda(),
+                norms=torch.from_numpy(r["norms"].astype(np.float32)).cuda())
+
+
 def quantized(name, bits, T=None, B=None):
     inp = synth.make(name, T=T, B=B)
     ctx = kvq.Context(inp["Hkv"], bits, inp["signs_k"], inp["signs_v"])
-    k = ctx.quantize(0, torch.from_numpy(inp["k"]).cuda())
-    v = ctx.quantize(1, torch.from_numpy(inp["v"]).cuda()) if "v" in inp else None
+    k = oracle_codes(inp["k"], inp["signs_k"], bits)
+    v = oracle_codes(inp["v"], inp["signs_v"], bits) if "v" in inp else None
     return inp, ctx, k, v
 
 
