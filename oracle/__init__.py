@@ -75,6 +75,10 @@ def _setup(L):
     L.kvqo_nsn_vq.argtypes = [C.c_int, C.c_int, C.c_int, i64, i64, _D, _D, C.c_double, _U8, _D,
                               _D, _D, _D, _U8, _D]
     L.kvqo_nsn_reconstruct.argtypes = [C.c_int, _D, C.c_double, C.c_double, _D, _D]
+    L.kvqo_nsn_logits.argtypes = [C.c_int, C.c_int, C.c_int, i64, i64, i64, i64, _D, _U8, _D, _D, _D,
+                                  _D, _D]
+    L.kvqo_nsn_attention.argtypes = [C.c_int, C.c_int, i64, i64, i64, i64, _D, _U8, _D, _D, _D, _U8,
+                                     _D, _D, _D, _D, C.c_double, _D]
     L.kvqo_kmeans.argtypes = [i64, C.c_int, C.c_int, _D, _I64, C.c_int, _D, _D]
     L.kvqo_kmeans.restype = C.c_int
 
@@ -322,6 +326,42 @@ def nsn_reconstruct(zq, s1, s2, o):
     d = zq.shape[0]
     out = np.zeros(d)
     lib().kvqo_nsn_reconstruct(d, _p(zq, _D), float(s1), float(s2), _p(o, _D), _p(out, _D))
+    return out
+
+
+def nsn_logits(q, codes, s1, s2, o, codebook, route: int = 1):
+    """q [B,Hq,d]; codes [B,Hkv,T,d/sub] u8; s1, s2 [B,Hkv,T]; o [B,Hkv,d];
+    codebook [K,sub] -> logits [B,Hq,T] (route 1: reconstruct then dot;
+    route 2: rotated query against the entries)."""
+    q = _f64(q)
+    B, Hq, d = q.shape
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    _, Hkv, T, _ = codes.shape
+    cb = _f64(codebook)
+    out = np.zeros((B, Hq, T))
+    _chk(lib().kvqo_nsn_logits(route, d, cb.shape[1], B, Hq, Hkv, T, _p(q, _D), _p(codes, _U8),
+                               _p(_f64(s1), _D), _p(_f64(s2), _D), _p(_f64(o), _D), _p(cb, _D),
+                               _p(out, _D)))
+    return out
+
+
+def nsn_attention(q, kc, ks1, ks2, ko, vc, vs1, vs2, vo, codebook, sm_scale: float | None = None):
+    """Decode attention over NSN-VQ keys and values (layouts as nsn_logits)
+    -> out [B,Hq,d]."""
+    q = _f64(q)
+    B, Hq, d = q.shape
+    kc = np.ascontiguousarray(kc, dtype=np.uint8)
+    vc = np.ascontiguousarray(vc, dtype=np.uint8)
+    _, Hkv, T, _ = kc.shape
+    cb = _f64(codebook)
+    if sm_scale is None:
+        sm_scale = 1.0 / np.sqrt(d)
+    out = np.zeros((B, Hq, d))
+    args = [_f64(a) for a in (ks1, ks2, ko, vs1, vs2, vo)]
+    _chk(lib().kvqo_nsn_attention(d, cb.shape[1], B, Hq, Hkv, T, _p(q, _D), _p(kc, _U8),
+                                  _p(args[0], _D), _p(args[1], _D), _p(args[2], _D), _p(vc, _U8),
+                                  _p(args[3], _D), _p(args[4], _D), _p(args[5], _D), _p(cb, _D),
+                                  float(sm_scale), _p(out, _D)))
     return out
 
 

@@ -568,6 +568,121 @@ ORC_API void kvqo_nsn_reconstruct(int d, const double *zq, double s1, double s2,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Attention over NSN-VQ codes (NSNQuant, "Detalhes de Implementacao": the    */
+/* score uses the byproducts s1, s2, o inside the attention kernels).  The    */
+/* reconstruction inverts Metodologia 1-2: x_hat = s1 (s2 H zq / sqrt(d) + o), */
+/* zq the 16 codebook entries the codes name, in sub-vector order.            */
+/* codes [B, Hkv, T, d/sub]; s1, s2 [B, Hkv, T]; o [B, Hkv, d]; q [B, Hq, d]; */
+/* KV head of query head h = h / (Hq / Hkv).                                   */
+/* ------------------------------------------------------------------------ */
+
+static void nsn_entries(int d, int sub, const uint8_t *code, const double *cb, double *zq)
+{
+    for (int s = 0; s < d / sub; ++s)
+        for (int k = 0; k < sub; ++k) zq[s * sub + k] = cb[(int)code[s] * sub + k];
+}
+
+/* route 1: <q, x_hat> with x_hat reconstructed.  route 2: the query is
+ * rotated once, q' = H q / sqrt(d), and
+ *   logit = s1 (s2 sum_s <q'_s, C[code_s]> + <q, o>),
+ * which is route 1 with H symmetric moved onto q. */
+ORC_API int kvqo_nsn_logits(int route, int d, int sub, int64_t B, int64_t Hq, int64_t Hkv, int64_t T,
+                            const double *q, const uint8_t *codes, const double *s1, const double *s2,
+                            const double *o, const double *cb, double *logits)
+{
+    if (Hkv <= 0 || Hq % Hkv || d % sub) return -1;
+    const int64_t G = Hq / Hkv;
+    const int ns = d / sub;
+    double *zq = (double *)malloc(sizeof(double) * d);
+    double *xh = (double *)malloc(sizeof(double) * d);
+    double *qr = (double *)malloc(sizeof(double) * d);
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t h = 0; h < Hq; ++h) {
+            const int64_t g = h / G;
+            const double *qh = q + (b * Hq + h) * d;
+            const double *og = o + (b * Hkv + g) * d;
+            double qo = 0.0;
+            for (int i = 0; i < d; ++i) qo += qh[i] * og[i];
+            for (int i = 0; i < d; ++i) qr[i] = qh[i];
+            kvqo_fwht(qr, d);
+            for (int i = 0; i < d; ++i) qr[i] /= sqrt((double)d);
+            for (int64_t t = 0; t < T; ++t) {
+                const int64_t v = (b * Hkv + g) * T + t;
+                double acc = 0.0;
+                if (route == 1) {
+                    nsn_entries(d, sub, codes + v * ns, cb, zq);
+                    kvqo_nsn_reconstruct(d, zq, s1[v], s2[v], og, xh);
+                    for (int i = 0; i < d; ++i) acc += qh[i] * xh[i];
+                } else {
+                    for (int sidx = 0; sidx < ns; ++sidx) {
+                        const double *c = cb + (int)codes[v * ns + sidx] * sub;
+                        for (int k = 0; k < sub; ++k) acc += qr[sidx * sub + k] * c[k];
+                    }
+                    acc = s1[v] * (s2[v] * acc + qo);
+                }
+                logits[(b * Hq + h) * T + t] = acc;
+            }
+        }
+    free(zq);
+    free(xh);
+    free(qr);
+    return 0;
+}
+
+/* Decode attention by definition: reconstruct every key and value, logits
+ * <q, k_hat> times sm_scale, softmax in two passes (maximum, exponentials),
+ * out = sum_t w_t v_hat_t / sum_t w_t. */
+ORC_API int kvqo_nsn_attention(int d, int sub, int64_t B, int64_t Hq, int64_t Hkv, int64_t T,
+                               const double *q, const uint8_t *kc, const double *ks1, const double *ks2,
+                               const double *ko, const uint8_t *vc, const double *vs1, const double *vs2,
+                               const double *vo, const double *cb, double sm_scale, double *out)
+{
+    if (Hkv <= 0 || Hq % Hkv || T <= 0 || d % sub) return -1;
+    const int64_t G = Hq / Hkv;
+    const int ns = d / sub;
+    double *K = (double *)malloc(sizeof(double) * T * d);
+    double *V = (double *)malloc(sizeof(double) * T * d);
+    double *zq = (double *)malloc(sizeof(double) * d);
+    double *w = (double *)malloc(sizeof(double) * T);
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t g = 0; g < Hkv; ++g) {
+            const int64_t bg = b * Hkv + g;
+            for (int64_t t = 0; t < T; ++t) {
+                const int64_t v = bg * T + t;
+                nsn_entries(d, sub, kc + v * ns, cb, zq);
+                kvqo_nsn_reconstruct(d, zq, ks1[v], ks2[v], ko + bg * d, K + t * d);
+                nsn_entries(d, sub, vc + v * ns, cb, zq);
+                kvqo_nsn_reconstruct(d, zq, vs1[v], vs2[v], vo + bg * d, V + t * d);
+            }
+            for (int64_t hh = 0; hh < G; ++hh) {
+                const double *qh = q + (b * Hq + g * G + hh) * d;
+                double mx = -INFINITY;
+                for (int64_t t = 0; t < T; ++t) {
+                    double a = 0.0;
+                    for (int i = 0; i < d; ++i) a += qh[i] * K[t * d + i];
+                    w[t] = sm_scale * a;
+                    if (w[t] > mx) mx = w[t];
+                }
+                double l = 0.0;
+                for (int64_t t = 0; t < T; ++t) {
+                    w[t] = exp(w[t] - mx);
+                    l += w[t];
+                }
+                double *oh = out + (b * Hq + g * G + hh) * d;
+                for (int i = 0; i < d; ++i) oh[i] = 0.0;
+                for (int64_t t = 0; t < T; ++t)
+                    for (int i = 0; i < d; ++i) oh[i] += w[t] * V[t * d + i];
+                for (int i = 0; i < d; ++i) oh[i] /= l;
+            }
+        }
+    free(K);
+    free(V);
+    free(zq);
+    free(w);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* k-means (Lloyd's algorithm) for the NSN vector codebook, on synthetic      */
 /* N(0, I) samples (NSNQuant, Metodologia 3).  samples [n, dim]; init [K]     */
 /* distinct sample indices; stops when no assignment changes or after         */
