@@ -77,6 +77,7 @@ void free_ctx(kvq_ctx *c)
     (void)hipFree(c->d_signs);
     (void)hipFree(c->d_S);
     (void)hipFree(c->d_S16);
+    (void)hipFree(c->d_vq);
     (void)hipFree(c->d_vq16);
     (void)hipFree(c->d_vqbias);
     std::free(c->h_signs);
@@ -232,6 +233,7 @@ kvq_status kvq_create(const kvq_config *cfg, kvq_ctx **out)
             bias[j] = (float)(-0.5 * sq);
         }
         c->vq_exact_f16 = exact;
+        if (st == KVQ_OK) st = upload(&c->d_vq, cfg->vq_codebook, n);
         if (st == KVQ_OK) st = upload(&c->d_vq16, c16, 2 * n);
         if (st == KVQ_OK) st = upload(&c->d_vqbias, bias, (size_t)kvq::kVqK);
         std::free(c16);
@@ -394,7 +396,7 @@ kvq_status kvq_nsn_vq_quantize(kvq_ctx *ctx, const void *x_f16, int64_t H, int64
 {
     if (!ctx || ctx->mode != KVQ_MODE_NSN_VQ) return KVQ_E_INVAL;
     if (H < 1 || T < 1 || T > (int64_t(1) << 31) || H > (int64_t(1) << 20)) return KVQ_E_INVAL;
-    if (H * ((T + 1023) / 1024) > INT32_MAX) return KVQ_E_INVAL;  // one stats block per 1024 tokens
+    if (H * ((T + 2047) / 2048) > INT32_MAX) return KVQ_E_INVAL;  // one stats block per 2048 tokens
     if (!x_f16 || !codes || !s1 || !s2 || !o || !ws) return KVQ_E_INVAL;
     if (!aligned(x_f16, 16) || !aligned(codes, 16) || !aligned(s1, 4) || !aligned(s2, 4) ||
         !aligned(o, 4) || !aligned(ws, 256))
@@ -403,6 +405,79 @@ kvq_status kvq_nsn_vq_quantize(kvq_ctx *ctx, const void *x_f16, int64_t H, int64
     DeviceGuard g(ctx->device);
     if (!g.ok) return KVQ_E_DEVICE;
     return launch_status(kvq::launch_nsn_vq(ctx, x_f16, H, T, codes, s1, s2, o, ws, (hipStream_t)stream));
+}
+
+
+namespace {
+bool nsn_group_ok(const kvq_ctx *ctx, int64_t H_q)
+{
+    if (H_q < 1 || H_q % ctx->H) return false;
+    const int64_t G = H_q / ctx->H;
+    return G == 1 || G == 2 || G == 4 || G == 8;
+}
+}  // namespace
+
+kvq_status kvq_nsn_logits(kvq_ctx *ctx, const void *q_f16, int64_t B, int64_t H_q, int64_t T,
+                          const uint8_t *codes, const float *s1, const float *s2, const float *o, float *logits,
+                          void *stream)
+{
+    if (!ctx || ctx->mode != KVQ_MODE_NSN_VQ) return KVQ_E_INVAL;
+    if (B < 0 || T < 0 || !nsn_group_ok(ctx, H_q)) return KVQ_E_INVAL;
+    if (B == 0 || T == 0) return KVQ_OK;
+    if (!q_f16 || !codes || !s1 || !s2 || !o || !logits) return KVQ_E_INVAL;
+    if (!aligned(q_f16, 16) || !aligned(codes, 16) || !aligned(s1, 4) || !aligned(s2, 4) || !aligned(o, 16) ||
+        !aligned(logits, 4))
+        return KVQ_E_INVAL;
+    if (T > (int64_t(1) << 31) || B * ctx->H > 65535) return KVQ_E_INVAL;
+    DeviceGuard g(ctx->device);
+    if (!g.ok) return KVQ_E_DEVICE;
+    return launch_status(
+        kvq::launch_nsn_logits(ctx, q_f16, B, H_q, T, codes, s1, s2, o, logits, (hipStream_t)stream));
+}
+
+size_t kvq_nsn_attn_decode_ws_bytes(const kvq_ctx *ctx, int64_t B, int64_t H_q, int64_t T)
+{
+    if (!ctx || B < 1 || T < 1 || H_q < 1) return 0;
+    return kvq::nsn_decode_ws_bytes(B, H_q, T);
+}
+
+kvq_status kvq_nsn_attn_decode_splits(kvq_ctx *ctx, const void *q_f16, int64_t B, int64_t H_q, int64_t T,
+                                      const uint8_t *k_codes, const float *k_s1, const float *k_s2,
+                                      const float *k_o, const uint8_t *v_codes, const float *v_s1,
+                                      const float *v_s2, const float *v_o, float sm_scale, float *out, void *ws,
+                                      size_t ws_bytes, int32_t n_split, void *stream)
+{
+    if (!ctx || ctx->mode != KVQ_MODE_NSN_VQ) return KVQ_E_INVAL;
+    if (B < 0 || T < 1 || !nsn_group_ok(ctx, H_q)) return KVQ_E_INVAL;
+    if (n_split < 0 || !std::isfinite(sm_scale) || sm_scale < 0.f) return KVQ_E_INVAL;
+    if (B == 0) return KVQ_OK;
+    if (!q_f16 || !k_codes || !k_s1 || !k_s2 || !k_o || !v_codes || !v_s1 || !v_s2 || !v_o || !out || !ws)
+        return KVQ_E_INVAL;
+    if (!aligned(q_f16, 16) || !aligned(k_codes, 16) || !aligned(v_codes, 16) || !aligned(k_s1, 4) ||
+        !aligned(k_s2, 4) || !aligned(v_s1, 4) || !aligned(v_s2, 4) || !aligned(k_o, 16) || !aligned(v_o, 16) ||
+        !aligned(out, 16) || !aligned(ws, 256))
+        return KVQ_E_INVAL;
+    if (T > (int64_t(1) << 31) || B * ctx->H > 65535) return KVQ_E_INVAL;
+    if (ws_bytes < kvq::nsn_decode_ws_bytes(B, H_q, T)) return KVQ_E_WORKSPACE;
+    const int64_t max_split = kvq::decode_max_splits(T);
+    int ns = n_split == 0 ? kvq::nsn_decode_auto_splits(ctx, B, T) : n_split;
+    if (ns > max_split) ns = (int)max_split;
+    if (ns < 1) ns = 1;
+    if (sm_scale == 0.f) sm_scale = 1.0f / std::sqrt((float)kvq::kD);
+    DeviceGuard g(ctx->device);
+    if (!g.ok) return KVQ_E_DEVICE;
+    const kvq::NsnKV kv{k_codes, k_s1, k_s2, k_o, v_codes, v_s1, v_s2, v_o};
+    return launch_status(
+        kvq::launch_nsn_decode(ctx, q_f16, B, H_q, T, kv, sm_scale, out, ws, ns, (hipStream_t)stream));
+}
+
+kvq_status kvq_nsn_attn_decode(kvq_ctx *ctx, const void *q_f16, int64_t B, int64_t H_q, int64_t T,
+                               const uint8_t *k_codes, const float *k_s1, const float *k_s2, const float *k_o,
+                               const uint8_t *v_codes, const float *v_s1, const float *v_s2, const float *v_o,
+                               float sm_scale, float *out, void *ws, size_t ws_bytes, void *stream)
+{
+    return kvq_nsn_attn_decode_splits(ctx, q_f16, B, H_q, T, k_codes, k_s1, k_s2, k_o, v_codes, v_s1, v_s2, v_o,
+                                      sm_scale, out, ws, ws_bytes, 0, stream);
 }
 
 }  // extern "C"

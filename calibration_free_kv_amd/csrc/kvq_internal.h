@@ -35,6 +35,7 @@ struct kvq_ctx {
     float *d_S;           // [128][128] QJL projection transposed, d_S[i][j] = S[j][i] (MSE_QJL)
     _Float16 *d_S16;      // [2][128][128] fp16 hi and lo parts of S (MSE_QJL)
     bool S_exact_f16;     // S_lo == 0
+    float *d_vq;          // [256][8] fp32 codebook (NSN_VQ scoring)
     _Float16 *d_vq16;     // [2][256][8] fp16 hi and lo parts of the codebook
     bool vq_exact_f16;    // codebook lo == 0
     float *d_vqbias;      // [256] -||C_j||^2 / 2
@@ -71,5 +72,23 @@ size_t nsn_ws_bytes(int64_t H, int64_t T);
 
 hipError_t launch_nsn_vq(const kvq_ctx *ctx, const void *x, int64_t H, int64_t T, uint8_t *codes,
                          float *s1, float *s2, float *o, void *ws, hipStream_t s);
+
+// NSN-VQ encoded keys and values of one decode call (outputs of kvq_nsn_vq_quantize).
+struct NsnKV {
+    const uint8_t *kc;
+    const float *ks1, *ks2, *ko;
+    const uint8_t *vc;
+    const float *vs1, *vs2, *vo;
+};
+
+hipError_t launch_nsn_logits(const kvq_ctx *ctx, const void *q, int64_t B, int64_t Hq, int64_t T,
+                             const uint8_t *codes, const float *s1, const float *s2, const float *o, float *logits,
+                             hipStream_t s);
+
+int64_t nsn_decode_chunk(int64_t T, int n_split);
+int nsn_decode_auto_splits(const kvq_ctx *ctx, int64_t B, int64_t T);
+size_t nsn_decode_ws_bytes(int64_t B, int64_t Hq, int64_t T);
+hipError_t launch_nsn_decode(const kvq_ctx *ctx, const void *q, int64_t B, int64_t Hq, int64_t T, const NsnKV &kv,
+                             float sm_scale, float *out, void *ws, int n_split, hipStream_t s);
 
 }  // namespace kvq

@@ -15,6 +15,7 @@
 // kernel instead runs its two contractions (logits over coordinates, values
 // over tokens) on the matrix cores; see its own description below.
 #include "kvq_internal.h"
+#include "kvq_wave.h"
 
 namespace kvq {
 namespace {
@@ -50,22 +51,6 @@ __device__ __forceinline__ uint32_t field(const uint32_t *Wd, int f)
     return v & ((1u << nb) - 1u);
 }
 
-// One Walsh-Hadamard transform of 128 values held two per lane (lane l holds
-// coordinates 2l and 2l+1): the first stage inside the lane, the other six
-// across lanes with shuffles.
-__device__ __forceinline__ void wave_fwht(float &x0, float &x1, int lane)
-{
-    const float a = x0 + x1;
-    x1 = x0 - x1;
-    x0 = a;
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) {
-        const float p0 = __shfl_xor(x0, m), p1 = __shfl_xor(x1, m);
-        const bool up = (lane & m) != 0;
-        x0 = up ? p0 - x0 : x0 + p0;
-        x1 = up ? p1 - x1 : x1 + p1;
-    }
-}
 
 // Prologue shared by the score kernels: qr[G][128] <- H (D .* q_h) for the G
 // query heads of KV head g of batch b, one wave per head.  Ends with a barrier.
@@ -352,59 +337,6 @@ struct DecSmem {
     static_assert(kDecWaves * STG >= kDecWaves * (kMaxSplits + kD), "split merge buffers do not fit");
 };
 
-// Cross-row exchanges on the VALU (gfx950 lane swaps): with the same value in
-// both operands, the swap of odd and even rows yields lane l ^ 16 in one
-// result and lane l in the other, and likewise for halves (l ^ 32).
-__device__ __forceinline__ float2 swap16(float x)
-{
-    const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x),
-                                                    false, false);
-    return float2{__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1])};
-}
-__device__ __forceinline__ float2 swap32(float x)
-{
-    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x),
-                                                    false, false);
-    return float2{__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1])};
-}
-
-// Reductions inside each row of 16 lanes (four DPP steps), and over the wave
-// (then the exchanges across rows and halves); result in every lane.
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x)
-{
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
-}
-__device__ __forceinline__ float row_max(float x)
-{
-    x = fmaxf(x, dpp<0xB1>(x));   // quad_perm [1,0,3,2]
-    x = fmaxf(x, dpp<0x4E>(x));   // quad_perm [2,3,0,1]
-    x = fmaxf(x, dpp<0x141>(x));  // row_half_mirror
-    return fmaxf(x, dpp<0x140>(x));  // row_mirror
-}
-__device__ __forceinline__ float row_sum(float x)
-{
-    x += dpp<0xB1>(x);
-    x += dpp<0x4E>(x);
-    x += dpp<0x141>(x);
-    return x + dpp<0x140>(x);
-}
-__device__ __forceinline__ float wave_max(float x)
-{
-    x = row_max(x);
-    float2 p = swap16(x);
-    x = fmaxf(p.x, p.y);
-    p = swap32(x);
-    return fmaxf(p.x, p.y);
-}
-__device__ __forceinline__ float wave_sum(float x)
-{
-    x = row_sum(x);
-    float2 p = swap16(x);
-    x = p.x + p.y;
-    p = swap32(x);
-    return p.x + p.y;
-}
 // o[r] = x of lane 16 r + (l & 15), for r = 0..3: row r broadcast to every row.
 __device__ __forceinline__ void row_broadcast(float x, float (&o)[4])
 {
@@ -414,13 +346,6 @@ __device__ __forceinline__ void row_broadcast(float x, float (&o)[4])
     o[1] = a.y;
     o[2] = c.x;
     o[3] = c.y;
-}
-// LDS written by some lanes of a wave is read by other lanes of the same wave.
-__device__ __forceinline__ void wave_lds_sync()
-{
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 // NB bits at bit offset O (compile time) of a window of consecutive dwords.

@@ -24,7 +24,8 @@ D = 128
 EXPORTS = [
     "kvq_create", "kvq_destroy", "kvq_get_tables", "kvq_codebook", "kvq_code_bytes_per_vec", "kvq_strerror",
     "kvq_quantize", "kvq_quantize_kv", "kvq_logits", "kvq_attn_decode_ws_bytes", "kvq_attn_decode",
-    "kvq_attn_decode_splits", "kvq_nsn_vq_ws_bytes", "kvq_nsn_vq_quantize",
+    "kvq_attn_decode_splits", "kvq_nsn_vq_ws_bytes", "kvq_nsn_vq_quantize", "kvq_nsn_logits",
+    "kvq_nsn_attn_decode_ws_bytes", "kvq_nsn_attn_decode", "kvq_nsn_attn_decode_splits",
 ]
 
 
@@ -74,6 +75,13 @@ def lib():
         L.kvq_nsn_vq_ws_bytes.argtypes = [vp, i64, i64]
         L.kvq_nsn_vq_ws_bytes.restype = sz
         L.kvq_nsn_vq_quantize.argtypes = [vp, vp, i64, i64, vp, vp, vp, vp, vp, sz, vp]
+        L.kvq_nsn_logits.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, vp, vp, vp]
+        L.kvq_nsn_attn_decode_ws_bytes.argtypes = [vp, i64, i64, i64]
+        L.kvq_nsn_attn_decode_ws_bytes.restype = sz
+        L.kvq_nsn_attn_decode.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, C.c_float, vp,
+                                          vp, sz, vp]
+        L.kvq_nsn_attn_decode_splits.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp,
+                                                 C.c_float, vp, vp, sz, i32, vp]
         _lib = L
     return _lib
 
@@ -245,6 +253,33 @@ class Context:
         kvq_nsn_vq_quantize(self, x, H, T, out["codes"], out["s1"], out["s2"], out["o"], ws)
         return out
 
+    def nsn_logits(self, q, codes, s1, s2, o, out=None):
+        """q [B,Hq,128] fp16; codes [B,Hkv,T,16] u8; s1, s2 [B,Hkv,T]; o [B,Hkv,128] -> [B,Hq,T]."""
+        _dev_tensor(q, torch.float16, "q")
+        B, Hq, _ = q.shape
+        T = codes.shape[2]
+        if out is None:
+            out = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+        kvq_nsn_logits(self, q, B, Hq, T, codes, s1, s2, o, out)
+        return out
+
+    def nsn_decode_ws(self, B, Hq, T):
+        n = int(lib().kvq_nsn_attn_decode_ws_bytes(self.handle, B, Hq, T))
+        return torch.empty(n, dtype=torch.uint8, device=self.dev)
+
+    def nsn_attn_decode(self, q, k, v, sm_scale: float = 0.0, ws=None, out=None, n_split: int = 0):
+        """k, v: dicts of codes, s1, s2, o as nsn_logits takes them -> out [B,Hq,128] fp32."""
+        _dev_tensor(q, torch.float16, "q")
+        B, Hq, _ = q.shape
+        T = k["codes"].shape[2]
+        if ws is None:
+            ws = self.nsn_decode_ws(B, Hq, T)
+        if out is None:
+            out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+        kvq_nsn_attn_decode_splits(self, q, B, Hq, T, k["codes"], k["s1"], k["s2"], k["o"], v["codes"], v["s1"],
+                                   v["s2"], v["o"], sm_scale, out, ws, n_split)
+        return out
+
 
 # ---------------------------------------------------------------------- C-ABI mirrors
 def kvq_quantize(ctx: Context, kind, x, B, H_kv, T, codes, norms, qjl_signs=None, qjl_gamma=None):
@@ -286,3 +321,27 @@ def kvq_nsn_vq_quantize(ctx: Context, x, H, T, codes, s1, s2, o, ws):
     _check(lib().kvq_nsn_vq_quantize(ctx.handle, _ptr(x), H, T, _ptr(codes), _ptr(s1), _ptr(s2), _ptr(o),
                                      _ptr(ws), ws.numel() * ws.element_size(), _stream(x.device)),
            "kvq_nsn_vq_quantize")
+
+
+def _nsn_inputs(codes, s1, s2, o, tag):
+    _dev_tensor(codes, torch.uint8, tag + "codes")
+    for t, n in ((s1, "s1"), (s2, "s2"), (o, "o")):
+        _dev_tensor(t, torch.float32, tag + n)
+
+
+def kvq_nsn_logits(ctx: Context, q, B, H_q, T, codes, s1, s2, o, logits):
+    _nsn_inputs(codes, s1, s2, o, "")
+    _dev_tensor(logits, torch.float32, "logits")
+    _check(lib().kvq_nsn_logits(ctx.handle, _ptr(q), B, H_q, T, _ptr(codes), _ptr(s1), _ptr(s2), _ptr(o),
+                                _ptr(logits), _stream(q.device)), "kvq_nsn_logits")
+
+
+def kvq_nsn_attn_decode_splits(ctx: Context, q, B, H_q, T, kc, ks1, ks2, ko, vc, vs1, vs2, vo, sm_scale, out, ws,
+                               n_split):
+    _nsn_inputs(kc, ks1, ks2, ko, "k_")
+    _nsn_inputs(vc, vs1, vs2, vo, "v_")
+    _dev_tensor(out, torch.float32, "out")
+    _check(lib().kvq_nsn_attn_decode_splits(ctx.handle, _ptr(q), B, H_q, T, _ptr(kc), _ptr(ks1), _ptr(ks2),
+                                            _ptr(ko), _ptr(vc), _ptr(vs1), _ptr(vs2), _ptr(vo), float(sm_scale),
+                                            _ptr(out), _ptr(ws), ws.numel() * ws.element_size(), int(n_split),
+                                            _stream(q.device)), "kvq_nsn_attn_decode")

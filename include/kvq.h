@@ -219,6 +219,54 @@ kvq_status kvq_nsn_vq_quantize(kvq_ctx *ctx, const void *x_f16, int64_t H, int64
                                uint8_t *codes, float *s1, float *s2, float *o, void *ws,
                                size_t ws_bytes, void *stream);
 
+/* Attention logits from NSN-VQ codes ([NSN] Detalhes de Implementacao: the
+ * score takes the byproducts s1, s2, o directly).  A key reconstructs as
+ * x_hat = s1 (s2 H zq / sqrt(d) + o), zq the 16 codebook entries its codes
+ * name (the inverse of [NSN] Metodologia 1-2), so with q' = H q / sqrt(d)
+ *   logits[b,h,t] = s1_t (s2_t sum_s <q'_s, C[code_t,s]> + <q_h, o_g>),
+ *   g = h / (H_q / H_kv), H_kv = the context's n_kv_heads.
+ *   q_f16    [B, H_q, d] fp16; H_q / H_kv in {1, 2, 4, 8}
+ *   codes    [B, H_kv, T, 16] bytes; s1, s2 [B, H_kv, T] fp32; o [B, H_kv, d]
+ *            fp32 (16-byte aligned): kvq_nsn_vq_quantize's outputs with its
+ *            heads = the B * H_kv (batch, KV head) pairs
+ *   logits   out [B, H_q, T] fp32 (raw inner products, no softmax scale)
+ * Requires a context in KVQ_MODE_NSN_VQ (its codebook is the one used).
+ * B * H_kv <= 65535.  B == 0 or T == 0 is a no-op. */
+kvq_status kvq_nsn_logits(kvq_ctx *ctx, const void *q_f16, int64_t B, int64_t H_q, int64_t T,
+                          const uint8_t *codes, const float *s1, const float *s2, const float *o,
+                          float *logits, void *stream);
+
+/* Workspace bytes kvq_nsn_attn_decode needs for these sizes (per-split partial
+ * sums). */
+size_t kvq_nsn_attn_decode_ws_bytes(const kvq_ctx *ctx, int64_t B, int64_t H_q, int64_t T);
+
+/* One decode step of attention over NSN-VQ encoded keys and values: logits as
+ * in kvq_nsn_logits, softmax with scale sm_scale (0 means 1/sqrt(d)), and
+ *   out[b,h] = sum_t softmax_t x_hat^V_t
+ *            = (H (sum_t w_t s1_t s2_t zq_t) / sqrt(d) + (sum_t w_t s1_t) o_V) / sum_t w_t.
+ *   k_*, v_*  kvq_nsn_vq_quantize's outputs for K and V (layouts as in
+ *             kvq_nsn_logits)
+ *   out       [B, H_q, d] fp32
+ *   ws        device workspace of at least kvq_nsn_attn_decode_ws_bytes()
+ *             bytes, 256-byte aligned; no initialisation needed.  Calls that
+ *             share a workspace must be ordered on one stream.
+ * T must be >= 1.  Errors: KVQ_E_WORKSPACE if ws_bytes is too small. */
+kvq_status kvq_nsn_attn_decode(kvq_ctx *ctx, const void *q_f16, int64_t B, int64_t H_q, int64_t T,
+                               const uint8_t *k_codes, const float *k_s1, const float *k_s2,
+                               const float *k_o, const uint8_t *v_codes, const float *v_s1,
+                               const float *v_s2, const float *v_o, float sm_scale, float *out,
+                               void *ws, size_t ws_bytes, void *stream);
+
+/* As kvq_nsn_attn_decode with an explicit number of token splits per (batch,
+ * KV head) (0 = automatic); the result does not depend on it beyond fp32
+ * rounding.  n_split is clamped to [1, min(512, ceil(T / 64))]. */
+kvq_status kvq_nsn_attn_decode_splits(kvq_ctx *ctx, const void *q_f16, int64_t B, int64_t H_q,
+                                      int64_t T, const uint8_t *k_codes, const float *k_s1,
+                                      const float *k_s2, const float *k_o, const uint8_t *v_codes,
+                                      const float *v_s1, const float *v_s2, const float *v_o,
+                                      float sm_scale, float *out, void *ws, size_t ws_bytes,
+                                      int32_t n_split, void *stream);
+
 #ifdef __cplusplus
 }
 #endif
