@@ -36,7 +36,7 @@ constexpr float kInvSqrtD = 0.08838834764831845f;
 constexpr float kLog2e = 1.4426950408889634f;
 
 template <int G>
-struct NsnSmem {
+struct alignas(16) NsnSmem {
     static constexpr int TAB = kNS * kVqK * G;           // floats of the table
     float tab[TAB];
     float cb[kVqK * kVqSub];                             // fp32 codebook
@@ -91,20 +91,21 @@ __device__ void nsn_tables(const half_t *__restrict__ q, const float *__restrict
     __syncthreads();
 }
 
-// sum_s T[s][code_s] for the G heads, in sub-vector order.
+// sum_s T[s][code_s] for the G heads, in sub-vector order.  The G values of
+// an entry are read as one vector (16-byte aligned for G >= 4).
 template <int G>
 __device__ __forceinline__ void nsn_key_sum(const u4_t code, const float *tab, float (&acc)[G])
 {
-#pragma unroll
-    for (int h = 0; h < G; ++h) acc[h] = 0.0f;
+    typedef float fg_t __attribute__((ext_vector_type(G)));
+    fg_t sum = 0.0f;
 #pragma unroll
     for (int s = 0; s < kNS; ++s) {
         const uint32_t w = s < 4 ? code.x : s < 8 ? code.y : s < 12 ? code.z : code.w;
         const uint32_t j = (w >> (8 * (s & 3))) & 0xFFu;
-        const float *e = tab + (s * kVqK + j) * G;
-#pragma unroll
-        for (int h = 0; h < G; ++h) acc[h] += e[h];
+        sum += *reinterpret_cast<const fg_t *>(tab + (s * kVqK + j) * G);
     }
+#pragma unroll
+    for (int h = 0; h < G; ++h) acc[h] = sum[h];
 }
 
 // logits[b, g G + h, t] = s1_t (s2_t sum_s T_h[s][code_t,s] + <q_h, o>).
@@ -115,19 +116,33 @@ __global__ __launch_bounds__(kThreadsN) void k_nsn_logits(const half_t *__restri
                                                           const float *__restrict__ o, const float *__restrict__ cb,
                                                           float *__restrict__ logits, int64_t Hkv, int64_t T)
 {
+    constexpr int NT = kLogitChunk / kThreadsN;  // tokens per thread
     __shared__ NsnSmem<G> sm;
     const int64_t bg = blockIdx.y, b = bg / Hkv, g = bg % Hkv;
     const int64_t Hq = Hkv * G, qbase = b * Hq + g * G;
-    nsn_tables<G, kThreadsN>(q, o, cb, bg, qbase, sm);
     const int64_t c0 = (int64_t)blockIdx.x * kLogitChunk, c1 = min(T, c0 + kLogitChunk);
-    for (int64_t t = c0 + threadIdx.x; t < c1; t += kThreadsN) {
-        const int64_t v = bg * T + t;
-        const u4_t code = codes[v];
-        const float a = s1[v], c = s2[v];
-        float acc[G];
-        nsn_key_sum<G>(code, sm.tab, acc);
+    // the keys' loads go out before the prologue (a token past the end
+    // re-reads the chunk's first one and is not stored)
+    u4_t code[NT];
+    float a[NT], c[NT];
 #pragma unroll
-        for (int h = 0; h < G; ++h) logits[(qbase + h) * T + t] = a * fmaf(c, acc[h], sm.qo[h]);
+    for (int i = 0; i < NT; ++i) {
+        const int64_t t = c0 + threadIdx.x + i * kThreadsN;
+        const int64_t v = bg * T + (t < c1 ? t : c0);
+        code[i] = codes[v];
+        a[i] = s1[v];
+        c[i] = s2[v];
+    }
+    nsn_tables<G, kThreadsN>(q, o, cb, bg, qbase, sm);
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+        const int64_t t = c0 + threadIdx.x + i * kThreadsN;
+        float acc[G];
+        nsn_key_sum<G>(code[i], sm.tab, acc);
+        if (t < c1) {
+#pragma unroll
+            for (int h = 0; h < G; ++h) logits[(qbase + h) * T + t] = a[i] * fmaf(c[i], acc[h], sm.qo[h]);
+        }
     }
 }
 
@@ -145,6 +160,17 @@ struct DecodeSmem {
     u4_t vcode[dec_waves<G>()][64];
     float wts[dec_waves<G>()][64][G];
 };
+// One lane's token of a decode tile: K and V codes and byproducts.
+struct TileIn {
+    u4_t kcode, vcode;
+    float a, c, e1, e2;  // s1_K, s2_K, s1_V, s2_V
+};
+__device__ __forceinline__ TileIn load_tile(const u4_t *kc, const float *ks1, const float *ks2, const u4_t *vc,
+                                            const float *vs1, const float *vs2, int64_t base, int64_t t)
+{
+    const int64_t v = base + t;
+    return TileIn{kc[v], vc[v], ks1[v], ks2[v], vs1[v], vs2[v]};
+}
 constexpr int kPartStride = kD + 4;  // floats per (split, head) partial: acc[128], M, L, WO, pad
 
 template <int G>
@@ -161,8 +187,12 @@ __global__ __launch_bounds__(64 * dec_waves<G>()) void k_nsn_part(const half_t *
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t bg = blockIdx.y, b = bg / Hkv, g = bg % Hkv;
     const int64_t qbase = b * Hkv * G + g * G;
-    nsn_tables<G, 64 * NW>(q, ko, cb, bg, qbase, sm.t);
     const int64_t c0 = (int64_t)blockIdx.x * chunk, c1 = min(T, c0 + chunk);
+    // The first tile's loads go out before the prologue, every later tile's
+    // before the current one is processed.
+    int64_t t0 = c0 + 64 * wv;
+    TileIn cur = load_tile(kc, ks1, ks2, vc, vs1, vs2, bg * T, t0 + lane < c1 ? t0 + lane : t0);
+    nsn_tables<G, 64 * NW>(q, ko, cb, bg, qbase, sm.t);
 
     float m[G], l[G], wo[G], acc[G][2];
 #pragma unroll
@@ -174,34 +204,35 @@ __global__ __launch_bounds__(64 * dec_waves<G>()) void k_nsn_part(const half_t *
     const uint8_t *vcb = reinterpret_cast<const uint8_t *>(sm.vcode[wv]) + vs;
     const float *cbk = sm.t.cb + vk;
 
-    for (int64_t t0 = c0 + 64 * wv; t0 < c1; t0 += 64 * NW) {
-        const int64_t t = t0 + lane;
-        const bool valid = t < c1;
-        const int64_t v = bg * T + (valid ? t : t0);
-        const u4_t kcode = kc[v], vcode = vc[v];
-        const float a = ks1[v], c = ks2[v], e1 = vs1[v], e2 = vs2[v];
+    for (; t0 < c1; t0 += 64 * NW) {
+        const bool valid = t0 + lane < c1;
+        const int64_t tn = t0 + 64 * NW;
+        TileIn nxt = cur;
+        if (tn < c1) nxt = load_tile(kc, ks1, ks2, vc, vs1, vs2, bg * T, tn + lane < c1 ? tn + lane : tn);
         float ks[G];
-        nsn_key_sum<G>(kcode, sm.t.tab, ks);
+        nsn_key_sum<G>(cur.kcode, sm.t.tab, ks);
         float w[G];
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-            const float lg = valid ? a * fmaf(c, ks[h], sm.t.qo[h]) * scale2 : -__builtin_inff();
+            const float lg = valid ? cur.a * fmaf(cur.c, ks[h], sm.t.qo[h]) * scale2 : -__builtin_inff();
             const float mn = fmaxf(m[h], wave_max(lg));
             const float alpha = __builtin_amdgcn_exp2f(m[h] - mn);
             const float p = __builtin_amdgcn_exp2f(lg - mn);
             m[h] = mn;
             l[h] = fmaf(l[h], alpha, p);
-            wo[h] = fmaf(wo[h], alpha, p * e1);
+            wo[h] = fmaf(wo[h], alpha, p * cur.e1);
             acc[h][0] *= alpha;
             acc[h][1] *= alpha;
-            w[h] = p * e1 * e2;
+            w[h] = p * cur.e1 * cur.e2;
         }
-        sm.vcode[wv][lane] = vcode;
+        sm.vcode[wv][lane] = cur.vcode;
 #pragma unroll
         for (int h = 0; h < G; ++h) sm.wts[wv][lane][h] = w[h];
         wave_lds_sync();
-        const int nv = (int)min((int64_t)64, c1 - t0);
-        for (int i = 0; i < nv; ++i) {
+        // all 64 tokens: past the end the weights are 0 and the staged index
+        // is that of the tile's first token
+#pragma unroll
+        for (int i = 0; i < 64; ++i) {
             const uint32_t j = vcb[16 * i];
             const f2_t ce = *reinterpret_cast<const f2_t *>(cbk + j * kVqSub);
 #pragma unroll
@@ -212,6 +243,7 @@ __global__ __launch_bounds__(64 * dec_waves<G>()) void k_nsn_part(const half_t *
             }
         }
         wave_lds_sync();
+        cur = nxt;
     }
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -270,8 +302,10 @@ __global__ __launch_bounds__(64 * G) void k_nsn_merge(const float *__restrict__ 
     const int64_t bg = blockIdx.x, b = bg / Hkv, g = bg % Hkv;
     const float *p0 = part + (bg * n_split * G + h) * kPartStride;
     float M = -__builtin_inff();
+#pragma unroll 8
     for (int s = 0; s < n_split; ++s) M = fmaxf(M, p0[(int64_t)s * G * kPartStride + kD]);
     float x0 = 0.0f, x1 = 0.0f, L = 0.0f, WO = 0.0f;
+#pragma unroll 8
     for (int s = 0; s < n_split; ++s) {
         const float *p = p0 + (int64_t)s * G * kPartStride;
         const float f = __builtin_amdgcn_exp2f(p[kD] - M);
