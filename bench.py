@@ -108,6 +108,35 @@ class Timer:
         return float(ms.mean()), float(np.percentile(ms, 10)), float(np.percentile(ms, 90))
 
 
+def run_graph(timer, launch, reps, per_graph=10, check=None):
+    """Mean duration of back-to-back launches replayed from a HIP graph (no
+    host launch cost in the timed region): per_graph launches are captured
+    once; each timed replay is bracketed by events.  check(), if given,
+    compares the replayed result with an eager one."""
+    torch = timer.torch
+    for i in range(3):
+        launch(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(per_graph):
+            launch(i)
+    for _ in range(2):
+        g.replay()
+        torch.cuda.synchronize()
+        if check is not None:
+            check()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for i in range(reps):
+        ev[i][0].record(timer.stream)
+        g.replay()
+        ev[i][1].record(timer.stream)
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in ev]) / per_graph
+    del g
+    return float(ms.mean()), float(np.percentile(ms, 10)), float(np.percentile(ms, 90))
+
+
 def row(ms, p10, p90, nbytes=None, flops=None, **extra):
     r = {"ms": ms, "p10_ms": p10, "p90_ms": p90}
     if nbytes is not None:
@@ -402,7 +431,51 @@ def rows(torch, kvq, synth, dev, timer, reps, oracle_rates):
                                 unit="vectors", note="three launches (stats, mean, search); x is read twice; "
                                 "flops = exhaustive distances 16 x 256 x 8 x 2 per vector")
     oracle_rates["nsn_vq_8x65536"] = oracle_rate(lambda: O.nsn_vq(inp["x"][:1, :1024], cb), 1024)
-    del xsn, x0, ctx
+    del xsn, x0
+
+    # NSN-VQ scoring from codes: logits and one decode step, 8 KV heads x 65536
+    # keys, 32 query heads; stand-in encoded K and V from the seeded generator
+    Hq = 32
+    n = H * T
+    per_set = n * 2 * (16 + 8)
+    ns = rng_sets(per_set)
+    dv = lambda e: {k: torch.from_numpy(v).to(dev) for k, v in e.items()}  # noqa: E731
+    kv = [(dv(synth.random_nsn_codes(40 + 2 * i, (1, H, T))), dv(synth.random_nsn_codes(41 + 2 * i, (1, H, T))))
+          for i in range(ns)]
+    qn = torch.from_numpy(synth.random_tensor(42, (1, Hq, D))).to(dev)
+    lgo = torch.empty((1, Hq, T), dtype=torch.float32, device=dev)
+    dout = torch.empty((1, Hq, D), dtype=torch.float32, device=dev)
+    wsd = ctx.nsn_decode_ws(1, Hq, T)
+
+    def nlg(i):
+        ctx.nsn_logits(qn, **kv[i % ns][0], out=lgo)
+
+    def ndec(i):
+        ctx.nsn_attn_decode(qn, kv[i % ns][0], kv[i % ns][1], ws=wsd, out=dout)
+
+    def same(fn, res):
+        def check():
+            got = res.clone()
+            fn(0)
+            torch.cuda.synchronize()
+            assert torch.equal(got, res), "graph replay differs from the eager launch"
+        return check
+    last = ns - 1
+    out["nsn_logits_8x65536_g4"] = row(*run_graph(timer, nlg, reps, ns, check=same(lambda i: nlg(last), lgo)),
+                                       nbytes=n * (16 + 8 + 4 * Hq // H), units_per_launch=n, unit="keys",
+                                       buffer_sets=ns, note="graph replay; 16 table lookups per key serve 4 heads")
+    out["nsn_attn_decode_8x65536_g4"] = row(*run_graph(timer, ndec, reps, ns, check=same(lambda i: ndec(last), dout)),
+                                            nbytes=n * 2 * (16 + 8), units_per_launch=n, unit="keys",
+                                            buffer_sets=ns, note="graph replay; two launches (splits, merge)")
+    e = synth.random_nsn_codes(40, (1, H, 1024))
+    f = synth.random_nsn_codes(41, (1, H, 1024))
+    qh = synth.random_tensor(42, (1, Hq, D))
+    oracle_rates["nsn_logits_8x65536_g4"] = oracle_rate(
+        lambda: O.nsn_logits(qh, e["codes"], e["s1"], e["s2"], e["o"], cb), H * 1024)
+    oracle_rates["nsn_attn_decode_8x65536_g4"] = oracle_rate(
+        lambda: O.nsn_attention(qh, e["codes"], e["s1"], e["s2"], e["o"], f["codes"], f["s1"], f["s2"], f["o"], cb),
+        H * 1024)
+    del kv, ctx
     torch.cuda.empty_cache()
     return out
 
