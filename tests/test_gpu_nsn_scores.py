@@ -138,6 +138,19 @@ def test_nsn_decode_zero_query_is_mean_value():
     np.testing.assert_allclose(decode(ctx_for(2), q, k, v), decode_ref(q, k, v), atol=2e-3)
 
 
+@pytest.mark.parametrize("G", [4, 8])
+def test_nsn_decode_zero_values(G):
+    """Value vectors with s1 = 0 (zero vectors) weigh in the softmax but add
+    nothing; in one KV head every value is zero."""
+    k, v = oracle_encoded(26, 1, 2, 700), oracle_encoded(27, 1, 2, 700)
+    v["s1"][0, 0, ::2] = 0.0
+    v["s1"][0, 1, :] = 0.0
+    q = query(28, 1, 2 * G)
+    got, want = decode(ctx_for(2), q, k, v), decode_ref(q, k, v)
+    assert np.abs(got - want).max() <= 2e-3
+    np.testing.assert_allclose(got[0, G:], want[0, G:], atol=1e-6)  # mean term only
+
+
 def test_nsn_score_validation():
     k = on_gpu(oracle_encoded(24, 1, 2, 100))
     q = torch.from_numpy(query(25, 1, 8)).cuda()
