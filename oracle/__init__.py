@@ -71,6 +71,8 @@ def _setup(L):
                               _F, _U8, _D, _D, C.c_int, _D]
     L.kvqo_attention.argtypes = [C.c_int, C.c_int, i64, i64, i64, i64, _D, _U8, _D, _U8, _D,
                                  _I8, _I8, _F, C.c_double, _D]
+    L.kvqo_attention_stream.argtypes = [C.c_int, C.c_int, i64, i64, i64, i64, i64, _D, _U8, _D, _U8, _D, _D,
+                                        _D, _I8, _I8, _F, C.c_double, _D]
     L.kvqo_qjl.argtypes = [C.c_int, C.c_int, i64, _D, _I32, _F, _D, C.c_double, _U8, _D, _U8]
     L.kvqo_nsn_vq.argtypes = [C.c_int, C.c_int, C.c_int, i64, i64, _D, _D, C.c_double, _U8, _D,
                               _D, _D, _D, _U8, _D]
@@ -276,6 +278,30 @@ def attention(q, kc, kn, vc, vn, signs_k, signs_v, bits: int, sm_scale: float | 
     _chk(lib().kvqo_attention(d, bits, B, Hq, Hkv, T, _p(q, _D), _p(kc, _U8), _p(kn, _D),
                               _p(vc, _U8), _p(vn, _D), _p(sk, _I8), _p(sv, _I8), _p(c, _F),
                               float(sm_scale), _p(out, _D)))
+    return out
+
+
+def attention_stream(q, kc, kn, vc, vn, k_tail, v_tail, signs_k, signs_v, bits: int,
+                     sm_scale: float | None = None):
+    """Attention over T quantised tokens (codes [B,Hkv,T,rec], norms [B,Hkv,T])
+    followed by R full-precision ones (k_tail, v_tail [B,Hkv,R,d]) -> [B,Hq,d]."""
+    q = _f64(q)
+    B, Hq, d = q.shape
+    kt, vt = _f64(k_tail), _f64(v_tail)
+    Hkv, R = kt.shape[1], kt.shape[2]
+    kc = np.ascontiguousarray(kc, dtype=np.uint8).reshape(B, Hkv, -1, d * bits // 8)
+    vc = np.ascontiguousarray(vc, dtype=np.uint8).reshape(B, Hkv, -1, d * bits // 8)
+    T = kc.shape[2]
+    kn, vn = _f64(kn), _f64(vn)
+    c, _ = tables_f32(bits)
+    if sm_scale is None:
+        sm_scale = 1.0 / np.sqrt(d)
+    out = np.zeros((B, Hq, d))
+    _chk(lib().kvqo_attention_stream(d, bits, B, Hq, Hkv, T, R, _p(q, _D), _p(kc, _U8), _p(kn, _D), _p(vc, _U8),
+                                     _p(vn, _D), _p(kt, _D), _p(vt, _D),
+                                     _p(np.ascontiguousarray(signs_k, dtype=np.int8), _I8),
+                                     _p(np.ascontiguousarray(signs_v, dtype=np.int8), _I8), _p(c, _F),
+                                     float(sm_scale), _p(out, _D)))
     return out
 
 

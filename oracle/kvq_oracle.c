@@ -432,6 +432,66 @@ ORC_API int kvqo_attention(int d, int bits, int64_t B, int64_t Hq, int64_t Hkv, 
 }
 
 /* ------------------------------------------------------------------------ */
+/* Decode attention over a cache split into a quantised part and a full-     */
+/* precision residual (NSNQuant, "Detalhes de Implementacao": following KIVI, */
+/* the residual is quantised and appended when it fills).  Token order: the  */
+/* T quantised tokens, then the R residual ones (kt, vt [B, Hkv, R, d]);     */
+/* keys and values are the dequantised prefix followed by the residual rows, */
+/* then the same two-pass softmax as kvqo_attention over all T + R tokens.   */
+/* ------------------------------------------------------------------------ */
+
+ORC_API int kvqo_attention_stream(int d, int bits, int64_t B, int64_t Hq, int64_t Hkv, int64_t T, int64_t R,
+                                  const double *q, const uint8_t *kc, const double *kn, const uint8_t *vc,
+                                  const double *vn, const double *kt, const double *vt,
+                                  const int8_t *signs_k, const int8_t *signs_v, const float *c32,
+                                  double sm_scale, double *out)
+{
+    if (Hkv <= 0 || Hq % Hkv || T < 0 || R < 0 || T + R <= 0) return -1;
+    const int64_t G = Hq / Hkv, N = T + R;
+    const int rec = d * bits / 8;
+    double *K = (double *)malloc(sizeof(double) * N * d);
+    double *V = (double *)malloc(sizeof(double) * N * d);
+    double *s = (double *)malloc(sizeof(double) * N);
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t g = 0; g < Hkv; ++g) {
+            for (int64_t t = 0; t < T; ++t) {
+                const int64_t v = (b * Hkv + g) * T + t;
+                kvqo_dequant(d, bits, kc + v * rec, kn[v], signs_k + g * d, c32, K + t * d);
+                kvqo_dequant(d, bits, vc + v * rec, vn[v], signs_v + g * d, c32, V + t * d);
+            }
+            for (int64_t t = 0; t < R; ++t)
+                for (int i = 0; i < d; ++i) {
+                    K[(T + t) * d + i] = kt[((b * Hkv + g) * R + t) * d + i];
+                    V[(T + t) * d + i] = vt[((b * Hkv + g) * R + t) * d + i];
+                }
+            for (int64_t hh = 0; hh < G; ++hh) {
+                const double *qh = q + (b * Hq + g * G + hh) * d;
+                double mx = -INFINITY;
+                for (int64_t t = 0; t < N; ++t) {
+                    double a = 0.0;
+                    for (int i = 0; i < d; ++i) a += qh[i] * K[t * d + i];
+                    s[t] = sm_scale * a;
+                    if (s[t] > mx) mx = s[t];
+                }
+                double l = 0.0;
+                for (int64_t t = 0; t < N; ++t) {
+                    s[t] = exp(s[t] - mx);
+                    l += s[t];
+                }
+                double *o = out + (b * Hq + g * G + hh) * d;
+                for (int i = 0; i < d; ++i) o[i] = 0.0;
+                for (int64_t t = 0; t < N; ++t)
+                    for (int i = 0; i < d; ++i) o[i] += s[t] * V[t * d + i];
+                for (int i = 0; i < d; ++i) o[i] /= l;
+            }
+        }
+    free(K);
+    free(V);
+    free(s);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* QJL 1-bit residual (TurboQuant, Stage 2).  Reading: the residual lives in  */
 /* the orthonormal rotated space, r = (y - c[idx]) / sqrt(d); gamma = ||r||;  */
 /* z = S r with S [m, d] of N(0,1) entries; sign bit sgn_j = [z_j >= 0].      */
