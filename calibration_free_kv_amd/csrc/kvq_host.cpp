@@ -2,6 +2,7 @@
 // argument validation and kernel launches behind the C ABI of kvq.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
@@ -407,6 +408,72 @@ kvq_status kvq_nsn_vq_quantize(kvq_ctx *ctx, const void *x_f16, int64_t H, int64
     return launch_status(kvq::launch_nsn_vq(ctx, x_f16, H, T, codes, s1, s2, o, ws, (hipStream_t)stream));
 }
 
+
+size_t kvq_attn_decode_stream_ws_bytes(const kvq_ctx *ctx, int64_t B, int64_t H_q, int64_t T_cap)
+{
+    if (!ctx || B < 1 || T_cap < 0 || H_q < 1) return 0;
+    const int64_t bhs = B * ctx->H;
+    const int64_t slots = (T_cap > 0 ? kvq::decode_max_splits(T_cap) : 0) + 1;  // splits + the window's slot
+    return ((bhs * sizeof(unsigned) + 255) / 256) * 256 + (size_t)(B * H_q) * (size_t)slots * (kvq::kD + 2) * 4;
+}
+
+kvq_status kvq_attn_decode_stream(kvq_ctx *ctx, const void *q_f16, int64_t B, int64_t H_q, int64_t T,
+                                  int64_t T_cap, const uint8_t *k_codes, const float *k_norms,
+                                  const uint8_t *v_codes, const float *v_norms, int64_t R, int64_t R_cap,
+                                  const void *k_tail_f16, const void *v_tail_f16, float sm_scale, float *out,
+                                  void *ws, size_t ws_bytes, void *stream)
+{
+    if (!ctx || ctx->mode != KVQ_MODE_MSE) return KVQ_E_INVAL;
+    if (B < 0 || H_q < 1 || H_q % ctx->H) return KVQ_E_INVAL;
+    const int64_t G = H_q / ctx->H;
+    if (G != 1 && G != 2 && G != 4) return KVQ_E_INVAL;
+    if (T < 0 || T > T_cap || R < 0 || R > R_cap || T + R < 1) return KVQ_E_INVAL;
+    if (!std::isfinite(sm_scale) || sm_scale < 0.f) return KVQ_E_INVAL;
+    if (B == 0) return KVQ_OK;
+    if (!q_f16 || !out || !ws) return KVQ_E_INVAL;
+    if (T > 0 && (!k_codes || !k_norms || !v_codes || !v_norms)) return KVQ_E_INVAL;
+    if (R > 0 && (!k_tail_f16 || !v_tail_f16)) return KVQ_E_INVAL;
+    if (!aligned(q_f16, 16) || !aligned(out, 16) || !aligned(ws, 256)) return KVQ_E_INVAL;
+    if (T > 0 && (!aligned(k_codes, 16) || !aligned(v_codes, 16) || !aligned(k_norms, 4) || !aligned(v_norms, 4)))
+        return KVQ_E_INVAL;
+    if (R > 0 && (!aligned(k_tail_f16, 16) || !aligned(v_tail_f16, 16))) return KVQ_E_INVAL;
+    if (T_cap > (int64_t(1) << 31) || R_cap > (int64_t(1) << 31) || B * ctx->H > (int64_t(1) << 31))
+        return KVQ_E_INVAL;
+    if (ws_bytes < kvq_attn_decode_stream_ws_bytes(ctx, B, H_q, T_cap)) return KVQ_E_WORKSPACE;
+    int ns = 1;
+    if (T > 0) {
+        ns = kvq::decode_auto_splits(B, ctx->H, T);
+        const int64_t cap = std::min<int64_t>(kvq::decode_max_splits(T), kvq::kMaxSplits - 1);
+        if (ns > cap) ns = (int)cap;
+        if (ns < 1) ns = 1;
+    }
+    if (sm_scale == 0.f) sm_scale = 1.0f / std::sqrt((float)kvq::kD);
+    DeviceGuard g(ctx->device);
+    if (!g.ok) return KVQ_E_DEVICE;
+    const kvq::DecodeTail tail{k_tail_f16, v_tail_f16, R, R_cap};
+    return launch_status(kvq::launch_decode_stream(ctx, q_f16, B, H_q, T, T_cap, k_codes, k_norms, v_codes, v_norms,
+                                                   R > 0 ? &tail : nullptr, sm_scale, out, ws, ns,
+                                                   (hipStream_t)stream));
+}
+
+kvq_status kvq_flush(kvq_ctx *ctx, const void *k_tail_f16, const void *v_tail_f16, int64_t B, int64_t H_kv, int64_t R,
+                     int64_t R_cap, uint8_t *k_codes, float *k_norms, uint8_t *v_codes, float *v_norms, int64_t T0,
+                     int64_t T_cap, void *stream)
+{
+    if (!ctx || ctx->mode != KVQ_MODE_MSE) return KVQ_E_INVAL;
+    if (B < 0 || H_kv != ctx->H || R < 0 || R > R_cap || T0 < 0 || T0 + R > T_cap) return KVQ_E_INVAL;
+    if (B == 0 || R == 0) return KVQ_OK;
+    if (!k_tail_f16 || !v_tail_f16 || !k_codes || !k_norms || !v_codes || !v_norms) return KVQ_E_INVAL;
+    if (!aligned(k_tail_f16, 16) || !aligned(v_tail_f16, 16) || !aligned(k_codes, 16) || !aligned(v_codes, 16) ||
+        !aligned(k_norms, 4) || !aligned(v_norms, 4))
+        return KVQ_E_INVAL;
+    if (T_cap > (int64_t(1) << 31) || R_cap > (int64_t(1) << 31) || 2 * B * H_kv * R > (int64_t(1) << 32))
+        return KVQ_E_INVAL;
+    DeviceGuard g(ctx->device);
+    if (!g.ok) return KVQ_E_DEVICE;
+    return launch_status(kvq::launch_flush(ctx, k_tail_f16, v_tail_f16, B, R, R_cap, k_codes, k_norms, v_codes,
+                                           v_norms, T0, T_cap, (hipStream_t)stream));
+}
 
 namespace {
 bool nsn_group_ok(const kvq_ctx *ctx, int64_t H_q)

@@ -68,6 +68,25 @@ hipError_t launch_decode(const kvq_ctx *ctx, const void *q, int64_t B, int64_t H
                          const uint8_t *kc, const float *kn, const uint8_t *vc, const float *vn,
                          float sm_scale, float *out, void *ws, int n_split, hipStream_t s);
 
+// Residual window of a streaming cache: R full-precision tokens per (batch, KV
+// head) in fp16 arrays [B, H_kv, R_cap, 128].
+struct DecodeTail {
+    const void *k, *v;
+    int64_t R, R_cap;
+};
+// Decode over T quantised tokens (arrays of ldt tokens per (batch, KV head))
+// followed by the residual window (tail may be null; T may be 0 with a tail).
+hipError_t launch_decode_stream(const kvq_ctx *ctx, const void *q, int64_t B, int64_t Hq, int64_t T, int64_t ldt,
+                                const uint8_t *kc, const float *kn, const uint8_t *vc, const float *vn,
+                                const DecodeTail *tail, float sm_scale, float *out, void *ws, int n_split,
+                                hipStream_t s);
+
+// Quantise the first R tokens of K and V residual windows ([B, H_kv, R_cap,
+// 128] fp16) into positions T0 .. T0 + R - 1 of packed arrays of T_cap tokens
+// per (batch, KV head).
+hipError_t launch_flush(const kvq_ctx *ctx, const void *kt, const void *vt, int64_t B, int64_t R, int64_t R_cap,
+                        uint8_t *kc, float *kn, uint8_t *vc, float *vn, int64_t T0, int64_t T_cap, hipStream_t s);
+
 size_t nsn_ws_bytes(int64_t H, int64_t T);
 
 hipError_t launch_nsn_vq(const kvq_ctx *ctx, const void *x, int64_t H, int64_t T, uint8_t *codes,

@@ -430,9 +430,12 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
     const half_t *__restrict__ q, const uint8_t *__restrict__ kc, const float *__restrict__ kn,
     const uint8_t *__restrict__ vc, const float *__restrict__ vn, const float *__restrict__ signs_k,
     const float *__restrict__ signs_v, Codebook cb, float scale_log2, float *__restrict__ out,
-    float *__restrict__ part, unsigned *__restrict__ counters, int64_t T, int H, int Hq,
-    int n_split, int64_t chunk)
+    float *__restrict__ part, unsigned *__restrict__ counters, int64_t T, int64_t ldt, int H, int Hq,
+    int n_split, int n_part, int64_t chunk)
 {
+    // T valid tokens of each (b, g) in arrays of ldt tokens per (b, g); the
+    // partials of (b, g) occupy n_part slots (n_split blocks, plus one slot
+    // written beforehand by the residual-window kernel when n_part > n_split)
     static_assert(G == 1 || G == 2 || G == 4, "two rows per head in one 16-row operand");
     using SM = DecSmem<BITS, G>;
     constexpr int W = SM::W;
@@ -493,7 +496,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
     // token (32-bit scalar arithmetic: the scalar unit has no 64-bit compare).
     auto tile_last = [&](int64_t t0) { return (uint32_t)min((int)(t_end - t0) - 1, 63); };
     auto fetch_k = [&](int64_t t0, uint32_t last) {
-        const int64_t v0 = bh * T + t0;
+        const int64_t v0 = bh * ldt + t0;
         const uint32_t l = min((uint32_t)lane, last);
         const char *kb = reinterpret_cast<const char *>(kc) + v0 * (16 * BITS);
 #pragma unroll
@@ -509,7 +512,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
         rk = *reinterpret_cast<const float *>(reinterpret_cast<const char *>(kn + v0) + 4 * l);
     };
     auto fetch_v = [&](int64_t t0, uint32_t last) {
-        const int64_t v0 = bh * T + t0;
+        const int64_t v0 = bh * ldt + t0;
         const uint32_t l = min((uint32_t)lane, last);
         const u4_t *vs = reinterpret_cast<const u4_t *>(reinterpret_cast<const char *>(vc) + v0 * (16 * BITS) +
                                                           l * (16u * BITS));
@@ -726,7 +729,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
     // the arrival count after all of them, and the merging block reads them
     // at device scope after seeing the count.
     auto st_dev = [](float *p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
-    float *my = part + ((bh * n_split + split) * G) * (kD + 2);
+    float *my = part + ((bh * n_part + split) * G) * (kD + 2);
     for (int idx = tid; idx < G * kD; idx += kDecThreads) {
         const int h = idx >> 7, i = idx & (kD - 1);
         float M = -INFINITY;
@@ -774,7 +777,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
     const int mh = wv % G, mj = wv / G;
     float *fh = smem + SM::stage + wv * kMaxSplits;       // reuse: this wave's merge weights [n_split]
     float *pacc = smem + SM::stage + kDecWaves * kMaxSplits;  // [waves][128] partial sums
-    const float *ah = part + (bh * n_split) * G * (kD + 2) + mh * (kD + 2);
+    const float *ah = part + (bh * n_part) * G * (kD + 2) + mh * (kD + 2);
     const int64_t sst = (int64_t)G * (kD + 2);  // split stride
     {
         float mv[kPerLane], lv[kPerLane];
@@ -782,8 +785,8 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
 #pragma unroll
         for (int k = 0; k < kPerLane; ++k) {
             const int sp = lane + 64 * k;
-            mv[k] = sp < n_split ? ld_dev(ah + sp * sst) : -INFINITY;
-            lv[k] = sp < n_split ? ld_dev(ah + sp * sst + 1) : 0.0f;
+            mv[k] = sp < n_part ? ld_dev(ah + sp * sst) : -INFINITY;
+            lv[k] = sp < n_part ? ld_dev(ah + sp * sst + 1) : 0.0f;
             M = fmaxf(M, mv[k]);
         }
         M = wave_max(M);
@@ -795,13 +798,13 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
 #pragma unroll
         for (int k = 0; k < kPerLane; ++k) {
             const int sp = lane + 64 * k;
-            if (sp < n_split) fh[sp] = __builtin_amdgcn_exp2f(mv[k] - M) * inv;
+            if (sp < n_part) fh[sp] = __builtin_amdgcn_exp2f(mv[k] - M) * inv;
         }
         wave_lds_sync();
         const float *col = ah + 2 + 2 * lane;
         float a0 = 0.0f, a1 = 0.0f;
         int sp = mj;
-        for (; sp + 7 * WPH < n_split; sp += 8 * WPH) {  // 8 independent loads in flight
+        for (; sp + 7 * WPH < n_part; sp += 8 * WPH) {  // 8 independent loads in flight
             f2_t v[8];
 #pragma unroll
             for (int u = 0; u < 8; ++u) v[u] = ld_dev2(col + (sp + u * WPH) * sst);
@@ -811,7 +814,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
                 a1 = fmaf(fh[sp + u * WPH], v[u].y, a1);
             }
         }
-        for (; sp < n_split; sp += WPH) {
+        for (; sp < n_part; sp += WPH) {
             const f2_t v = ld_dev2(col + sp * sst);
             a0 = fmaf(fh[sp], v.x, a0);
             a1 = fmaf(fh[sp], v.y, a1);
@@ -863,17 +866,110 @@ hipError_t run_logits(const kvq_ctx *ctx, const void *q, int64_t B, int64_t Hq, 
     return hipGetLastError();
 }
 
+// Residual window of a streaming cache: the partial (m, l, acc) of its R
+// full-precision tokens for the G query heads of (b, g), in the convention of
+// the decode partials (base-2 scores s = scale_log2 <q, k>, acc in the
+// rotated domain: H (D_V .* sum_t 2^(s_t - m) v_t)), written to slot n_split
+// of the (b, g) partials; with no quantised tokens (direct) it writes the
+// output itself, sum_t 2^(s_t - m) v_t / l.  One wave per query head; per
+// 64-token chunk the lanes score one token each (the query from LDS), then
+// act as coordinate pairs (2 lane, 2 lane + 1) summing the values.
+template <int G>
+__global__ __launch_bounds__(64 * G) void k_tail(const half_t *__restrict__ q, const half_t *__restrict__ kt,
+                                                 const half_t *__restrict__ vt, const float *__restrict__ signs_v,
+                                                 float scale_log2, float *__restrict__ part, float *__restrict__ out,
+                                                 int64_t R, int64_t R_cap, int H, int Hq, int n_part, int n_split,
+                                                 bool direct)
+{
+    __shared__ __align__(16) float qf[G][kD];
+    const int lane = threadIdx.x & 63, h = threadIdx.x >> 6;
+    const int64_t bh = blockIdx.x, b = bh / H;
+    const int g = (int)(bh - b * H);
+    const int64_t qrow = b * Hq + (int64_t)g * G + h;
+    {
+        const h2_t pr = reinterpret_cast<const h2_t *>(q + qrow * kD)[lane];
+        reinterpret_cast<f2_t *>(qf[h])[lane] = f2_t{(float)pr.x, (float)pr.y};
+    }
+    wave_lds_sync();
+    const half_t *kb = kt + bh * R_cap * kD, *vb = vt + bh * R_cap * kD;
+    float m = -INFINITY, l = 0.0f, a0 = 0.0f, a1 = 0.0f;
+    for (int64_t c = 0; c < R; c += 64) {
+        const int64_t t = c + lane;
+        float sc = -INFINITY;
+        if (t < R) {
+            const h8_t *kr = reinterpret_cast<const h8_t *>(kb + t * kD);
+            float acc = 0.0f;
+#pragma unroll
+            for (int i = 0; i < kD / 8; ++i) {
+                const h8_t kv = kr[i];
+                const f4_t q0 = reinterpret_cast<const f4_t *>(qf[h])[2 * i];
+                const f4_t q1 = reinterpret_cast<const f4_t *>(qf[h])[2 * i + 1];
+                acc = fmaf(q0.x, (float)kv[0], acc);
+                acc = fmaf(q0.y, (float)kv[1], acc);
+                acc = fmaf(q0.z, (float)kv[2], acc);
+                acc = fmaf(q0.w, (float)kv[3], acc);
+                acc = fmaf(q1.x, (float)kv[4], acc);
+                acc = fmaf(q1.y, (float)kv[5], acc);
+                acc = fmaf(q1.z, (float)kv[6], acc);
+                acc = fmaf(q1.w, (float)kv[7], acc);
+            }
+            sc = acc * scale_log2;
+        }
+        const float mn = fmaxf(m, wave_max(sc));
+        const float al = __builtin_amdgcn_exp2f(m - mn);
+        const float p = __builtin_amdgcn_exp2f(sc - mn);
+        m = mn;
+        l = fmaf(l, al, p);
+        a0 *= al;
+        a1 *= al;
+        const int nv = (int)min((int64_t)64, R - c);
+        for (int j = 0; j < nv; ++j) {
+            const float pj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, p), j));
+            const h2_t v2 = reinterpret_cast<const h2_t *>(vb + (c + j) * kD)[lane];
+            a0 = fmaf(pj, (float)v2.x, a0);
+            a1 = fmaf(pj, (float)v2.y, a1);
+        }
+    }
+    l = wave_sum(l);
+    if (direct) {
+        const float inv = 1.0f / l;
+        reinterpret_cast<f2_t *>(out + qrow * kD)[lane] = f2_t{a0 * inv, a1 * inv};
+        return;
+    }
+    const f2_t sv = reinterpret_cast<const f2_t *>(signs_v + g * kD)[lane];
+    float x0 = a0 * sv.x, x1 = a1 * sv.y;
+    wave_fwht(x0, x1, lane);
+    float *dst = part + ((bh * n_part + n_split) * G + h) * (kD + 2);
+    reinterpret_cast<f2_t *>(dst + 2)[lane] = f2_t{x0, x1};
+    if (lane == 0) {
+        dst[0] = m;
+        dst[1] = l;
+    }
+}
+
 template <int BITS, int G>
-hipError_t run_decode(const kvq_ctx *ctx, const void *q, int64_t B, int64_t Hq, int64_t T,
-                      const uint8_t *kc, const float *kn, const uint8_t *vc, const float *vn,
+hipError_t run_decode(const kvq_ctx *ctx, const void *q, int64_t B, int64_t Hq, int64_t T, int64_t ldt,
+                      const uint8_t *kc, const float *kn, const uint8_t *vc, const float *vn, const DecodeTail *tail,
                       float sm_scale, float *out, void *ws, int n_split, hipStream_t s)
 {
     using SM = DecSmem<BITS, G>;
     const int64_t bhs = B * ctx->H;
-    const int64_t chunk = (T + n_split - 1) / n_split;
-    n_split = (int)((T + chunk - 1) / chunk);  // no empty split
+    const float scale_log2 = sm_scale * 1.4426950408889634f;
     unsigned *counters = (unsigned *)ws;
     float *part = (float *)((char *)ws + ((bhs * sizeof(unsigned) + 255) / 256) * 256);
+    int n_part = 0;
+    int64_t chunk = 0;
+    if (T > 0) {
+        chunk = (T + n_split - 1) / n_split;
+        n_split = (int)((T + chunk - 1) / chunk);  // no empty split
+        n_part = n_split + (tail ? 1 : 0);
+    }
+    if (tail) {
+        hipLaunchKernelGGL((k_tail<G>), dim3((unsigned)bhs), dim3(64 * G), 0, s, (const half_t *)q,
+                           (const half_t *)tail->k, (const half_t *)tail->v, ctx->d_signs + ctx->H * kD, scale_log2,
+                           part, out, tail->R, tail->R_cap, ctx->H, (int)Hq, n_part, n_split, T == 0);
+        if (T == 0) return hipGetLastError();
+    }
     const size_t shm = sizeof(float) * SM::total;
     static bool attr_set = false;
     if (!attr_set) {
@@ -883,8 +979,7 @@ hipError_t run_decode(const kvq_ctx *ctx, const void *q, int64_t B, int64_t Hq, 
     }
     hipLaunchKernelGGL((k_decode<BITS, G>), dim3((unsigned)(bhs * n_split)), dim3(kDecThreads), shm, s,
                        (const half_t *)q, kc, kn, vc, vn, ctx->d_signs, ctx->d_signs + ctx->H * kD, ctx->cb,
-                       sm_scale * 1.4426950408889634f, out, part, counters, T, ctx->H, (int)Hq, n_split,
-                       chunk);
+                       scale_log2, out, part, counters, T, ldt, ctx->H, (int)Hq, n_split, n_part, chunk);
     return hipGetLastError();
 }
 
@@ -908,14 +1003,14 @@ hipError_t dispatch_logits(const kvq_ctx *ctx, int G, bool qjl, const void *q, i
 }
 
 template <int BITS>
-hipError_t dispatch_decode(const kvq_ctx *ctx, int G, const void *q, int64_t B, int64_t Hq, int64_t T,
+hipError_t dispatch_decode(const kvq_ctx *ctx, int G, const void *q, int64_t B, int64_t Hq, int64_t T, int64_t ldt,
                            const uint8_t *kc, const float *kn, const uint8_t *vc, const float *vn,
-                           float sm, float *out, void *ws, int ns, hipStream_t s)
+                           const DecodeTail *tail, float sm, float *out, void *ws, int ns, hipStream_t s)
 {
     switch (G) {
-    case 1: return run_decode<BITS, 1>(ctx, q, B, Hq, T, kc, kn, vc, vn, sm, out, ws, ns, s);
-    case 2: return run_decode<BITS, 2>(ctx, q, B, Hq, T, kc, kn, vc, vn, sm, out, ws, ns, s);
-    case 4: return run_decode<BITS, 4>(ctx, q, B, Hq, T, kc, kn, vc, vn, sm, out, ws, ns, s);
+    case 1: return run_decode<BITS, 1>(ctx, q, B, Hq, T, ldt, kc, kn, vc, vn, tail, sm, out, ws, ns, s);
+    case 2: return run_decode<BITS, 2>(ctx, q, B, Hq, T, ldt, kc, kn, vc, vn, tail, sm, out, ws, ns, s);
+    case 4: return run_decode<BITS, 4>(ctx, q, B, Hq, T, ldt, kc, kn, vc, vn, tail, sm, out, ws, ns, s);
     }
     return hipErrorNotSupported;
 }
@@ -959,12 +1054,20 @@ hipError_t launch_decode(const kvq_ctx *ctx, const void *q, int64_t B, int64_t H
                          const uint8_t *kc, const float *kn, const uint8_t *vc, const float *vn,
                          float sm_scale, float *out, void *ws, int n_split, hipStream_t s)
 {
+    return launch_decode_stream(ctx, q, B, Hq, T, T, kc, kn, vc, vn, nullptr, sm_scale, out, ws, n_split, s);
+}
+
+hipError_t launch_decode_stream(const kvq_ctx *ctx, const void *q, int64_t B, int64_t Hq, int64_t T, int64_t ldt,
+                                const uint8_t *kc, const float *kn, const uint8_t *vc, const float *vn,
+                                const DecodeTail *tail, float sm_scale, float *out, void *ws, int n_split,
+                                hipStream_t s)
+{
     const int G = (int)(Hq / ctx->H);
     switch (ctx->bits) {
-    case 1: return dispatch_decode<1>(ctx, G, q, B, Hq, T, kc, kn, vc, vn, sm_scale, out, ws, n_split, s);
-    case 2: return dispatch_decode<2>(ctx, G, q, B, Hq, T, kc, kn, vc, vn, sm_scale, out, ws, n_split, s);
-    case 3: return dispatch_decode<3>(ctx, G, q, B, Hq, T, kc, kn, vc, vn, sm_scale, out, ws, n_split, s);
-    case 4: return dispatch_decode<4>(ctx, G, q, B, Hq, T, kc, kn, vc, vn, sm_scale, out, ws, n_split, s);
+    case 1: return dispatch_decode<1>(ctx, G, q, B, Hq, T, ldt, kc, kn, vc, vn, tail, sm_scale, out, ws, n_split, s);
+    case 2: return dispatch_decode<2>(ctx, G, q, B, Hq, T, ldt, kc, kn, vc, vn, tail, sm_scale, out, ws, n_split, s);
+    case 3: return dispatch_decode<3>(ctx, G, q, B, Hq, T, ldt, kc, kn, vc, vn, tail, sm_scale, out, ws, n_split, s);
+    case 4: return dispatch_decode<4>(ctx, G, q, B, Hq, T, ldt, kc, kn, vc, vn, tail, sm_scale, out, ws, n_split, s);
     }
     return hipErrorInvalidValue;
 }

@@ -26,6 +26,7 @@ EXPORTS = [
     "kvq_quantize", "kvq_quantize_kv", "kvq_logits", "kvq_attn_decode_ws_bytes", "kvq_attn_decode",
     "kvq_attn_decode_splits", "kvq_nsn_vq_ws_bytes", "kvq_nsn_vq_quantize", "kvq_nsn_logits",
     "kvq_nsn_attn_decode_ws_bytes", "kvq_nsn_attn_decode", "kvq_nsn_attn_decode_splits",
+    "kvq_attn_decode_stream_ws_bytes", "kvq_attn_decode_stream", "kvq_flush",
 ]
 
 
@@ -75,6 +76,11 @@ def lib():
         L.kvq_nsn_vq_ws_bytes.argtypes = [vp, i64, i64]
         L.kvq_nsn_vq_ws_bytes.restype = sz
         L.kvq_nsn_vq_quantize.argtypes = [vp, vp, i64, i64, vp, vp, vp, vp, vp, sz, vp]
+        L.kvq_attn_decode_stream_ws_bytes.argtypes = [vp, i64, i64, i64]
+        L.kvq_attn_decode_stream_ws_bytes.restype = sz
+        L.kvq_attn_decode_stream.argtypes = [vp, vp, i64, i64, i64, i64, vp, vp, vp, vp, i64, i64, vp, vp,
+                                             C.c_float, vp, vp, sz, vp]
+        L.kvq_flush.argtypes = [vp, vp, vp, i64, i64, i64, i64, vp, vp, vp, vp, i64, i64, vp]
         L.kvq_nsn_logits.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, vp, vp, vp]
         L.kvq_nsn_attn_decode_ws_bytes.argtypes = [vp, i64, i64, i64]
         L.kvq_nsn_attn_decode_ws_bytes.restype = sz
@@ -253,6 +259,30 @@ class Context:
         kvq_nsn_vq_quantize(self, x, H, T, out["codes"], out["s1"], out["s2"], out["o"], ws)
         return out
 
+    def stream_ws(self, B, Hq, T_cap):
+        n = int(lib().kvq_attn_decode_stream_ws_bytes(self.handle, B, Hq, T_cap))
+        return torch.zeros(n, dtype=torch.uint8, device=self.dev)
+
+    def attn_decode_stream(self, q, k_codes, k_norms, v_codes, v_norms, T, k_tail, v_tail, R, sm_scale: float = 0.0,
+                           ws=None, out=None):
+        """Decode over the first T tokens of packed arrays [B,Hkv,T_cap,...] followed by
+        the first R tokens of fp16 windows [B,Hkv,R_cap,128]."""
+        _dev_tensor(q, torch.float16, "q")
+        B, Hq, _ = q.shape
+        T_cap, R_cap = k_codes.shape[2], k_tail.shape[2]
+        if ws is None:
+            ws = self.stream_ws(B, Hq, T_cap)
+        if out is None:
+            out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+        kvq_attn_decode_stream(self, q, B, Hq, T, T_cap, k_codes, k_norms, v_codes, v_norms, R, R_cap, k_tail,
+                               v_tail, sm_scale, out, ws)
+        return out
+
+    def flush(self, k_tail, v_tail, R, k_codes, k_norms, v_codes, v_norms, T0):
+        """Quantise the first R window tokens into positions T0.. of the packed arrays."""
+        B, Hkv, R_cap, _ = k_tail.shape
+        kvq_flush(self, k_tail, v_tail, B, Hkv, R, R_cap, k_codes, k_norms, v_codes, v_norms, T0, k_codes.shape[2])
+
     def nsn_logits(self, q, codes, s1, s2, o, out=None):
         """q [B,Hq,128] fp16; codes [B,Hkv,T,16] u8; s1, s2 [B,Hkv,T]; o [B,Hkv,128] -> [B,Hq,T]."""
         _dev_tensor(q, torch.float16, "q")
@@ -345,3 +375,24 @@ def kvq_nsn_attn_decode_splits(ctx: Context, q, B, H_q, T, kc, ks1, ks2, ko, vc,
                                             _ptr(ko), _ptr(vc), _ptr(vs1), _ptr(vs2), _ptr(vo), float(sm_scale),
                                             _ptr(out), _ptr(ws), ws.numel() * ws.element_size(), int(n_split),
                                             _stream(q.device)), "kvq_nsn_attn_decode")
+
+
+def kvq_attn_decode_stream(ctx: Context, q, B, H_q, T, T_cap, k_codes, k_norms, v_codes, v_norms, R, R_cap, k_tail,
+                           v_tail, sm_scale, out, ws):
+    for t, dt, n in ((k_codes, torch.uint8, "k_codes"), (v_codes, torch.uint8, "v_codes"),
+                     (k_norms, torch.float32, "k_norms"), (v_norms, torch.float32, "v_norms"),
+                     (k_tail, torch.float16, "k_tail"), (v_tail, torch.float16, "v_tail"), (out, torch.float32, "out")):
+        _dev_tensor(t, dt, n)
+    _check(lib().kvq_attn_decode_stream(ctx.handle, _ptr(q), B, H_q, T, T_cap, _ptr(k_codes), _ptr(k_norms),
+                                        _ptr(v_codes), _ptr(v_norms), R, R_cap, _ptr(k_tail), _ptr(v_tail),
+                                        float(sm_scale), _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
+                                        _stream(q.device)), "kvq_attn_decode_stream")
+
+
+def kvq_flush(ctx: Context, k_tail, v_tail, B, H_kv, R, R_cap, k_codes, k_norms, v_codes, v_norms, T0, T_cap):
+    for t, dt, n in ((k_codes, torch.uint8, "k_codes"), (v_codes, torch.uint8, "v_codes"),
+                     (k_norms, torch.float32, "k_norms"), (v_norms, torch.float32, "v_norms"),
+                     (k_tail, torch.float16, "k_tail"), (v_tail, torch.float16, "v_tail")):
+        _dev_tensor(t, dt, n)
+    _check(lib().kvq_flush(ctx.handle, _ptr(k_tail), _ptr(v_tail), B, H_kv, R, R_cap, _ptr(k_codes), _ptr(k_norms),
+                           _ptr(v_codes), _ptr(v_norms), T0, T_cap, _stream(k_tail.device)), "kvq_flush")

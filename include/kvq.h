@@ -219,6 +219,42 @@ kvq_status kvq_nsn_vq_quantize(kvq_ctx *ctx, const void *x_f16, int64_t H, int64
                                uint8_t *codes, float *s1, float *s2, float *o, void *ws,
                                size_t ws_bytes, void *stream);
 
+/* Streaming cache ([NSN] Detalhes de Implementacao: following KIVI, the KV
+ * cache is a quantised part plus a full-precision residual window that is
+ * quantised and appended when it fills).  Per (batch, KV head) the packed
+ * arrays hold T_cap tokens ([B, H_kv, T_cap, 16 b] codes, [B, H_kv, T_cap]
+ * norms) of which the first T are valid, and the window arrays hold R_cap
+ * fp16 tokens ([B, H_kv, R_cap, d]) of which the first R are valid.
+ *
+ * Workspace bytes kvq_attn_decode_stream needs for caches of T_cap tokens. */
+size_t kvq_attn_decode_stream_ws_bytes(const kvq_ctx *ctx, int64_t B, int64_t H_q, int64_t T_cap);
+
+/* One decode step over such a cache (MSE mode): attention of each query over
+ * the T quantised tokens followed by the R window tokens, one softmax over
+ * all T + R (scale sm_scale, 0 means 1/sqrt(d)); the quantised tokens are
+ * scored and dequantised as in kvq_attn_decode, the window tokens used as
+ * they are.  H_q / H_kv in {1, 2, 4}; 0 <= T <= T_cap, 0 <= R <= R_cap,
+ * T + R >= 1 (either part may be empty; its pointers may then be NULL).
+ *   out  [B, H_q, d] fp32
+ *   ws   at least kvq_attn_decode_stream_ws_bytes() bytes, 256-byte aligned,
+ *        its counter words zero before the first call (every completed call
+ *        leaves them zero); calls sharing it must be ordered on one stream.
+ * Errors: KVQ_E_WORKSPACE if ws_bytes is too small. */
+kvq_status kvq_attn_decode_stream(kvq_ctx *ctx, const void *q_f16, int64_t B, int64_t H_q, int64_t T,
+                                  int64_t T_cap, const uint8_t *k_codes, const float *k_norms,
+                                  const uint8_t *v_codes, const float *v_norms, int64_t R, int64_t R_cap,
+                                  const void *k_tail_f16, const void *v_tail_f16, float sm_scale,
+                                  float *out, void *ws, size_t ws_bytes, void *stream);
+
+/* Flush of the window: the first R tokens of the K and V windows of every
+ * (batch, KV head) are quantised exactly as kvq_quantize quantises a vector
+ * and written to positions T0 .. T0 + R - 1 of the packed arrays (layouts as
+ * above, H_kv = the context's n_kv_heads; MSE mode).  Other positions are not
+ * touched.  Requires T0 + R <= T_cap.  R == 0 or B == 0 is a no-op. */
+kvq_status kvq_flush(kvq_ctx *ctx, const void *k_tail_f16, const void *v_tail_f16, int64_t B, int64_t H_kv,
+                     int64_t R, int64_t R_cap, uint8_t *k_codes, float *k_norms, uint8_t *v_codes,
+                     float *v_norms, int64_t T0, int64_t T_cap, void *stream);
+
 /* Attention logits from NSN-VQ codes ([NSN] Detalhes de Implementacao: the
  * score takes the byproducts s1, s2, o directly).  A key reconstructs as
  * x_hat = s1 (s2 H zq / sqrt(d) + o), zq the 16 codebook entries its codes
