@@ -476,6 +476,44 @@ def rows(torch, kvq, synth, dev, timer, reps, oracle_rates):
         lambda: O.nsn_attention(qh, e["codes"], e["s1"], e["s2"], e["o"], f["codes"], f["s1"], f["s2"], f["o"], cb),
         H * 1024)
     del kv, ctx
+
+    # streaming cache: decode over 32704 packed tokens (of 32768 slots) plus a
+    # 64-token fp16 window, and the flush of a 64-token window (b = 3, 8 KV
+    # heads, 32 query heads); stand-in packed codes from the seeded generator
+    inp = synth.make("l8b32k", T=1)
+    Hkv, Hq, T_cap, T_s, R_cap, R_s = 8, 32, 32768, 32704, 128, 64
+    ctx = kvq.Context(Hkv, 3, inp["signs_k"], inp["signs_v"], device=dev.index)
+    n = Hkv * T_s
+    ns = rng_sets(n * 2 * rec_bytes(3))
+    dv = lambda e: {k: torch.from_numpy(v).to(dev) for k, v in e.items()}  # noqa: E731
+    k0, v0 = dv(synth.random_codes(60, (1, Hkv, T_cap), 3)), dv(synth.random_codes(61, (1, Hkv, T_cap), 3))
+    kt0 = torch.from_numpy(synth.random_tensor(90, (1, Hkv, R_cap, D))).to(dev)
+    vt0 = torch.from_numpy(synth.random_tensor(91, (1, Hkv, R_cap, D))).to(dev)
+    cl = lambda e: {k: v.clone() for k, v in e.items()}  # noqa: E731
+    pk = [(cl(k0), cl(v0)) for _ in range(ns)]
+    win = [(kt0.clone(), vt0.clone()) for _ in range(ns)]
+    qs = torch.from_numpy(synth.random_tensor(43, (1, Hq, D))).to(dev)
+    sout = torch.empty((1, Hq, D), dtype=torch.float32, device=dev)
+    sws = ctx.stream_ws(1, Hq, T_cap)
+
+    def sdec(i):
+        k, v = pk[i % ns]
+        kt, vt = win[i % ns]
+        ctx.attn_decode_stream(qs, k["codes"], k["norms"], v["codes"], v["norms"], T_s, kt, vt, R_s, ws=sws, out=sout)
+
+    def sflush(i):
+        k, v = pk[i % ns]
+        kt, vt = win[i % ns]
+        ctx.flush(kt, vt, R_s, k["codes"], k["norms"], v["codes"], v["norms"], T_s)
+    last = ns - 1
+    out["attn_decode_stream_l8b32k_b3"] = row(
+        *run_graph(timer, sdec, reps, ns, check=same(lambda i: sdec(last), sout)),
+        nbytes=n * 2 * rec_bytes(3) + Hkv * R_s * 2 * 2 * D, units_per_launch=n + Hkv * R_s, unit="keys",
+        buffer_sets=ns, note="graph replay; 32704 packed + 64 fp16 window tokens per KV head; two launches")
+    out["flush_window64_b3"] = row(*run_graph(timer, sflush, reps, ns), nbytes=quant_bytes(2 * Hkv * R_s, 3),
+                                   units_per_launch=2 * Hkv * R_s, unit="vectors", buffer_sets=ns,
+                                   note="graph replay; latency-bound (1024 vectors)")
+    del pk, win, ctx
     torch.cuda.empty_cache()
     return out
 

@@ -922,12 +922,21 @@ __global__ __launch_bounds__(64 * G) void k_tail(const half_t *__restrict__ q, c
         l = fmaf(l, al, p);
         a0 *= al;
         a1 *= al;
+        // values in groups of 16 tokens with all 16 loads in flight (tokens
+        // past the end re-read the chunk's first one, with weight 0)
         const int nv = (int)min((int64_t)64, R - c);
-        for (int j = 0; j < nv; ++j) {
-            const float pj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, p), j));
-            const h2_t v2 = reinterpret_cast<const h2_t *>(vb + (c + j) * kD)[lane];
-            a0 = fmaf(pj, (float)v2.x, a0);
-            a1 = fmaf(pj, (float)v2.y, a1);
+        for (int j0 = 0; j0 < nv; j0 += 16) {
+            h2_t v2[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+                v2[u] = reinterpret_cast<const h2_t *>(vb + (c + (j0 + u < nv ? j0 + u : 0)) * kD)[lane];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const float pj =
+                    __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, p), j0 + u));
+                a0 = fmaf(pj, (float)v2[u].x, a0);
+                a1 = fmaf(pj, (float)v2[u].y, a1);
+            }
         }
     }
     l = wave_sum(l);
