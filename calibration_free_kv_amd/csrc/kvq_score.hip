@@ -873,7 +873,9 @@ hipError_t run_logits(const kvq_ctx *ctx, const void *q, int64_t B, int64_t Hq, 
 // of the (b, g) partials; with no quantised tokens (direct) it writes the
 // output itself, sum_t 2^(s_t - m) v_t / l.  One wave per query head; per
 // 64-token chunk the lanes score one token each (the query from LDS), then
-// act as coordinate pairs (2 lane, 2 lane + 1) summing the values.
+// act as coordinate pairs (2 lane, 2 lane + 1) summing the values.  A chunk's
+// key rows and value pairs are loaded in one go (the first chunk's before
+// the query is staged).
 template <int G>
 __global__ __launch_bounds__(64 * G) void k_tail(const half_t *__restrict__ q, const half_t *__restrict__ kt,
                                                  const half_t *__restrict__ vt, const float *__restrict__ signs_v,
@@ -886,35 +888,44 @@ __global__ __launch_bounds__(64 * G) void k_tail(const half_t *__restrict__ q, c
     const int64_t bh = blockIdx.x, b = bh / H;
     const int g = (int)(bh - b * H);
     const int64_t qrow = b * Hq + (int64_t)g * G + h;
+    const half_t *kb = kt + bh * R_cap * kD, *vb = vt + bh * R_cap * kD;
+    // one 64-token chunk: the lane's key row and the chunk's value pairs are
+    // loaded together with the query, so the three loads overlap
+    h8_t krow[kD / 8];
+    h2_t vrow[64];
+    auto load_chunk = [&](int64_t c) {
+        const int64_t t = c + lane < R ? c + lane : c;
+#pragma unroll
+        for (int i = 0; i < kD / 8; ++i) krow[i] = reinterpret_cast<const h8_t *>(kb + t * kD)[i];
+#pragma unroll
+        for (int u = 0; u < 64; ++u)
+            vrow[u] = reinterpret_cast<const h2_t *>(vb + (c + u < R ? c + u : c) * kD)[lane];
+    };
+    load_chunk(0);
     {
         const h2_t pr = reinterpret_cast<const h2_t *>(q + qrow * kD)[lane];
         reinterpret_cast<f2_t *>(qf[h])[lane] = f2_t{(float)pr.x, (float)pr.y};
     }
     wave_lds_sync();
-    const half_t *kb = kt + bh * R_cap * kD, *vb = vt + bh * R_cap * kD;
     float m = -INFINITY, l = 0.0f, a0 = 0.0f, a1 = 0.0f;
     for (int64_t c = 0; c < R; c += 64) {
-        const int64_t t = c + lane;
-        float sc = -INFINITY;
-        if (t < R) {
-            const h8_t *kr = reinterpret_cast<const h8_t *>(kb + t * kD);
-            float acc = 0.0f;
+        if (c > 0) load_chunk(c);
+        float acc = 0.0f;
 #pragma unroll
-            for (int i = 0; i < kD / 8; ++i) {
-                const h8_t kv = kr[i];
-                const f4_t q0 = reinterpret_cast<const f4_t *>(qf[h])[2 * i];
-                const f4_t q1 = reinterpret_cast<const f4_t *>(qf[h])[2 * i + 1];
-                acc = fmaf(q0.x, (float)kv[0], acc);
-                acc = fmaf(q0.y, (float)kv[1], acc);
-                acc = fmaf(q0.z, (float)kv[2], acc);
-                acc = fmaf(q0.w, (float)kv[3], acc);
-                acc = fmaf(q1.x, (float)kv[4], acc);
-                acc = fmaf(q1.y, (float)kv[5], acc);
-                acc = fmaf(q1.z, (float)kv[6], acc);
-                acc = fmaf(q1.w, (float)kv[7], acc);
-            }
-            sc = acc * scale_log2;
+        for (int i = 0; i < kD / 8; ++i) {
+            const h8_t kv = krow[i];
+            const f4_t q0 = reinterpret_cast<const f4_t *>(qf[h])[2 * i];
+            const f4_t q1 = reinterpret_cast<const f4_t *>(qf[h])[2 * i + 1];
+            acc = fmaf(q0.x, (float)kv[0], acc);
+            acc = fmaf(q0.y, (float)kv[1], acc);
+            acc = fmaf(q0.z, (float)kv[2], acc);
+            acc = fmaf(q0.w, (float)kv[3], acc);
+            acc = fmaf(q1.x, (float)kv[4], acc);
+            acc = fmaf(q1.y, (float)kv[5], acc);
+            acc = fmaf(q1.z, (float)kv[6], acc);
+            acc = fmaf(q1.w, (float)kv[7], acc);
         }
+        const float sc = c + lane < R ? acc * scale_log2 : -INFINITY;
         const float mn = fmaxf(m, wave_max(sc));
         const float al = __builtin_amdgcn_exp2f(m - mn);
         const float p = __builtin_amdgcn_exp2f(sc - mn);
@@ -922,21 +933,12 @@ __global__ __launch_bounds__(64 * G) void k_tail(const half_t *__restrict__ q, c
         l = fmaf(l, al, p);
         a0 *= al;
         a1 *= al;
-        // values in groups of 16 tokens with all 16 loads in flight (tokens
-        // past the end re-read the chunk's first one, with weight 0)
-        const int nv = (int)min((int64_t)64, R - c);
-        for (int j0 = 0; j0 < nv; j0 += 16) {
-            h2_t v2[16];
+        // tokens past the end re-read the chunk's first one, with weight 0
 #pragma unroll
-            for (int u = 0; u < 16; ++u)
-                v2[u] = reinterpret_cast<const h2_t *>(vb + (c + (j0 + u < nv ? j0 + u : 0)) * kD)[lane];
-#pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                const float pj =
-                    __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, p), j0 + u));
-                a0 = fmaf(pj, (float)v2[u].x, a0);
-                a1 = fmaf(pj, (float)v2[u].y, a1);
-            }
+        for (int u = 0; u < 64; ++u) {
+            const float pj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, p), u));
+            a0 = fmaf(pj, (float)vrow[u].x, a0);
+            a1 = fmaf(pj, (float)vrow[u].y, a1);
         }
     }
     l = wave_sum(l);
