@@ -58,6 +58,12 @@ def _setup(L):
     L.kvqo_gauss_mse.argtypes = [C.c_int, _D, _D]
     L.kvqo_gauss_mse.restype = C.c_double
     L.kvqo_tables_f32.argtypes = [C.c_int, _F, _F]
+    L.kvqo_beta_mass.argtypes = [C.c_int, C.c_double, C.c_double]
+    L.kvqo_beta_mass.restype = C.c_double
+    L.kvqo_lloyd_max_beta.argtypes = [C.c_int, C.c_int, C.c_int, C.c_double, _D, C.POINTER(C.c_int)]
+    L.kvqo_beta_mse.argtypes = [C.c_int, C.c_int, _D, _D]
+    L.kvqo_beta_mse.restype = C.c_double
+    L.kvqo_tables_f32_beta.argtypes = [C.c_int, C.c_int, _F, _F]
     L.kvqo_hadamard_entry.argtypes = [C.c_int, C.c_int]
     L.kvqo_hadamard_dense.argtypes = [_D, _D, C.c_int]
     L.kvqo_fwht.argtypes = [_D, C.c_int]
@@ -111,6 +117,33 @@ def lloyd_max(bits: int, init=None, max_iter: int = 1_000_000, tol: float = 1e-1
 
 def gauss_mse(bits: int, c, t) -> float:
     return lib().kvqo_gauss_mse(bits, _p(_f64(c), _D), _p(_f64(t), _D))
+
+
+def beta_mass(d: int, a: float, b: float) -> float:
+    """int_a^b (1 - y^2/d)^((d-3)/2) dy (unnormalised law of sqrt(d) u_i)."""
+    return lib().kvqo_beta_mass(d, a, b)
+
+
+def lloyd_max_beta(bits: int, d: int = 128, max_iter: int = 1_000_000, tol: float = 1e-13):
+    """Lloyd-Max centroids for the coordinate law of a uniform unit vector in
+    R^d scaled by sqrt(d); returns (centroids, iterations)."""
+    c = np.zeros(1 << bits)
+    it = C.c_int(0)
+    _chk(lib().kvqo_lloyd_max_beta(bits, d, max_iter, tol, _p(c, _D), C.byref(it)))
+    return c, it.value
+
+
+def beta_mse(bits: int, c, t, d: int = 128) -> float:
+    return lib().kvqo_beta_mse(bits, d, _p(_f64(c), _D), _p(_f64(t), _D))
+
+
+def tables_f32_beta(bits: int, d: int = 128):
+    """Canonical fp32 centroids and thresholds of the exact-d law."""
+    L = 1 << bits
+    c = np.zeros(L, np.float32)
+    t = np.zeros(L - 1, np.float32)
+    _chk(lib().kvqo_tables_f32_beta(bits, d, _p(c, _F), _p(t, _F)))
+    return c, t
 
 
 def tables_f32(bits: int):

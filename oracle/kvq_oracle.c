@@ -131,6 +131,161 @@ ORC_API int kvqo_tables_f32(int bits, float *c32, float *t32)
 }
 
 /* ------------------------------------------------------------------------ */
+/* Lloyd-Max for the exact coordinate law at dimension d ("O Que E           */
+/* TurboQuant?", Como Funciona, Estagio 1: after the rotation each coordinate */
+/* of the unit vector follows Beta((d-1)/2, (d-1)/2) on [-1, 1]; the Lloyd-Max */
+/* quantiser is optimised for that law).  With the coordinates scaled by      */
+/* sqrt(d) to unit variance, the density on [-sqrt d, sqrt d] is proportional */
+/* to g(y) = (1 - y^2/d)^((d-3)/2).  Cell integrals:                          */
+/*   m0(a, b) = int_a^b g: F(b) - F(a), F tabulated on a grid of step 1/512   */
+/*              by 8-point Gauss-Legendre per step, plus Gauss-Legendre over  */
+/*              the partial step;                                             */
+/*   m1(a, b) = int_a^b y g = d/(d-1) [G(a) - G(b)], G(y) = (1 - y^2/d)^((d-1)/2). */
+/* ------------------------------------------------------------------------ */
+
+static const double kGLx[4] = {0.1834346424956498, 0.5255324099163290, 0.7966664774136267, 0.9602898564975363};
+static const double kGLw[4] = {0.3626837833783620, 0.3137066458778873, 0.2223810344533745, 0.1012285362903763};
+
+typedef struct {
+    int d;
+    double r, h;   /* support radius sqrt(d), grid step */
+    int n;         /* grid points */
+    double *F;     /* F[i] = int_{-r}^{-r + i h} g */
+} beta_law;
+
+static double beta_g(const beta_law *B, double y)
+{
+    const double u = 1.0 - y * y / B->d;
+    return u <= 0.0 ? 0.0 : pow(u, 0.5 * (B->d - 3));
+}
+
+static double beta_gl(const beta_law *B, double a, double b)
+{
+    const double m = 0.5 * (a + b), hw = 0.5 * (b - a);
+    double s = 0.0;
+    for (int k = 0; k < 4; ++k) s += kGLw[k] * (beta_g(B, m - hw * kGLx[k]) + beta_g(B, m + hw * kGLx[k]));
+    return s * hw;
+}
+
+static int beta_init(beta_law *B, int d)
+{
+    B->d = d;
+    B->r = sqrt((double)d);
+    B->h = 1.0 / 512.0;
+    B->n = (int)ceil(2.0 * B->r / B->h) + 1;
+    B->F = (double *)malloc(sizeof(double) * B->n);
+    if (!B->F) return -1;
+    B->F[0] = 0.0;
+    for (int i = 1; i < B->n; ++i) {
+        const double a = -B->r + (i - 1) * B->h;
+        double b = a + B->h;
+        if (b > B->r) b = B->r;
+        B->F[i] = B->F[i - 1] + beta_gl(B, a, b);
+    }
+    return 0;
+}
+
+static double beta_F(const beta_law *B, double y)
+{
+    if (y <= -B->r) return 0.0;
+    if (y >= B->r) y = B->r;
+    int i = (int)floor((y + B->r) / B->h);
+    if (i >= B->n - 1) i = B->n - 2;
+    const double y0 = -B->r + i * B->h;
+    return B->F[i] + beta_gl(B, y0, y);
+}
+
+static double beta_G(const beta_law *B, double y)
+{
+    const double u = 1.0 - y * y / B->d;
+    return u <= 0.0 ? 0.0 : pow(u, 0.5 * (B->d - 1));
+}
+
+/* Total mass Z = int g over the support, also in closed form:
+ * sqrt(d) B(1/2, (d-1)/2) (exposed for the tests). */
+ORC_API double kvqo_beta_mass(int d, double a, double b)
+{
+    beta_law B;
+    if (d < 4 || beta_init(&B, d)) return -1.0;
+    const double m = beta_F(&B, b) - beta_F(&B, a);
+    free(B.F);
+    return m;
+}
+
+/* Centroids c[2^bits] (fp64) of the Lloyd-Max quantiser for the law above;
+ * start from uniform levels on [-2.5, 2.5], iterate until max |dc| < tol. */
+ORC_API int kvqo_lloyd_max_beta(int bits, int d, int max_iter, double tol, double *c_out, int *iters_out)
+{
+    if (bits < 1 || bits > 8 || d < 4) return -1;
+    beta_law B;
+    if (beta_init(&B, d)) return -1;
+    const int L = 1 << bits;
+    double c[256], t[257];
+    for (int j = 0; j < L; ++j) c[j] = -2.5 + 5.0 * (j + 0.5) / L;
+    const double k1 = (double)d / (d - 1);
+    int it = 0;
+    for (; it < max_iter; ++it) {
+        t[0] = -B.r;
+        t[L] = B.r;
+        for (int j = 1; j < L; ++j) t[j] = 0.5 * (c[j - 1] + c[j]);
+        double delta = 0.0;
+        for (int j = 0; j < L; ++j) {
+            const double m0 = beta_F(&B, t[j + 1]) - beta_F(&B, t[j]);
+            const double m1 = k1 * (beta_G(&B, t[j]) - beta_G(&B, t[j + 1]));
+            const double cn = m1 / m0;
+            if (fabs(cn - c[j]) > delta) delta = fabs(cn - c[j]);
+            c[j] = cn;
+        }
+        if (delta < tol) { ++it; break; }
+    }
+    memcpy(c_out, c, sizeof(double) * L);
+    if (iters_out) *iters_out = it;
+    free(B.F);
+    return 0;
+}
+
+/* Mean squared error of quantiser (c, t) under the law, per coordinate:
+ * sum_j int_{t_{j-1}}^{t_j} (y - c_j)^2 g / Z, with int y^2 g by Gauss-Legendre. */
+ORC_API double kvqo_beta_mse(int bits, int d, const double *c, const double *t)
+{
+    beta_law B;
+    if (beta_init(&B, d)) return -1.0;
+    const int L = 1 << bits;
+    const double Z = B.F[B.n - 1];
+    double mse = 0.0;
+    for (int j = 0; j < L; ++j) {
+        const double a = j == 0 ? -B.r : t[j - 1], b = j == L - 1 ? B.r : t[j];
+        /* int (y - c)^2 g over [a, b], panel by panel */
+        const int np = (int)ceil((b - a) / B.h) + 1;
+        const double hp = (b - a) / np;
+        double s = 0.0;
+        for (int p = 0; p < np; ++p) {
+            const double pa = a + p * hp, m = pa + 0.5 * hp, hw = 0.5 * hp;
+            for (int k = 0; k < 4; ++k) {
+                const double y0 = m - hw * kGLx[k], y1 = m + hw * kGLx[k];
+                s += kGLw[k] * hw * ((y0 - c[j]) * (y0 - c[j]) * beta_g(&B, y0) + (y1 - c[j]) * (y1 - c[j]) * beta_g(&B, y1));
+            }
+        }
+        mse += s;
+    }
+    free(B.F);
+    return mse / Z;
+}
+
+/* Canonical fp32 tables of the law, rounded as kvqo_tables_f32 rounds. */
+ORC_API int kvqo_tables_f32_beta(int bits, int d, float *c32, float *t32)
+{
+    const int L = 1 << bits;
+    double c[256];
+    int rc = kvqo_lloyd_max_beta(bits, d, 1000000, 1e-13, c, NULL);
+    if (rc) return rc;
+    for (int j = 0; j < L; ++j) c32[j] = (float)c[j];
+    for (int j = 0; j + 1 < L; ++j)
+        t32[j] = (float)(((double)c32[j] + (double)c32[j + 1]) * 0.5);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Walsh-Hadamard                                                             */
 /* ------------------------------------------------------------------------ */
 
