@@ -1,4 +1,5 @@
-// libkvq host side: context lifetime, the Gaussian Lloyd-Max table builder,
+// libkvq host side: context lifetime, the Lloyd-Max table builders (N(0,1) and
+// the exact law at d = 128),
 // argument validation and kernel launches behind the C ABI of kvq.h.
 #include <hip/hip_runtime.h>
 
@@ -52,6 +53,101 @@ void build_codebook(int bits, kvq::Codebook *cb)
     }
     // Stored thresholds: fp32 midpoints of adjacent fp32 centroids.
     for (int j = 0; j + 1 < L; ++j) cb->t[j] = (float)(((double)cb->c[j] + (double)cb->c[j + 1]) * 0.5);
+}
+
+// ---------------------------------------------------------------------------
+// Lloyd-Max quantiser for the exact coordinate law at dimension d
+// ("TurboQuant", Como Funciona, Estagio 1: after the rotation a coordinate of
+// the unit vector follows Beta((d-1)/2, (d-1)/2) on [-1, 1]; the quantiser is
+// optimised for that law).  Scaled by sqrt(d) (unit variance) the density is
+// proportional to g(y) = (1 - y^2/d)^((d-3)/2) on [-sqrt d, sqrt d].  As for
+// the Gaussian only the positive levels are iterated; the cell integrals of g
+// and y g come from cumulative Simpson sums from 0 on a grid of step 1/2048,
+// plus one Simpson step over the partial interval.
+// ---------------------------------------------------------------------------
+struct BetaHalf {
+    int d;
+    double r, h;
+    int n;
+    double *m0, *m1;  // int_0^{i h} g, int_0^{i h} y g
+    double g(double y) const
+    {
+        const double u = 1.0 - y * y / d;
+        return u <= 0.0 ? 0.0 : std::pow(u, 0.5 * (d - 3));
+    }
+    void simpson(double a, double b, double &s0, double &s1) const
+    {
+        const double m = 0.5 * (a + b), ga = g(a), gm = g(m), gb = g(b), w = (b - a) / 6.0;
+        s0 = w * (ga + 4.0 * gm + gb);
+        s1 = w * (a * ga + 4.0 * m * gm + b * gb);
+    }
+    bool init(int dim)
+    {
+        d = dim;
+        r = std::sqrt((double)d);
+        h = 1.0 / 2048.0;
+        n = (int)std::ceil(r / h) + 1;
+        m0 = (double *)std::malloc(sizeof(double) * n);
+        m1 = (double *)std::malloc(sizeof(double) * n);
+        if (!m0 || !m1) return false;
+        m0[0] = m1[0] = 0.0;
+        for (int i = 1; i < n; ++i) {
+            double s0, s1;
+            simpson((i - 1) * h, std::fmin(i * h, r), s0, s1);
+            m0[i] = m0[i - 1] + s0;
+            m1[i] = m1[i - 1] + s1;
+        }
+        return true;
+    }
+    void at(double y, double &a0, double &a1) const  // int_0^y of g and y g
+    {
+        y = std::fmin(y, r);
+        int i = (int)(y / h);
+        if (i > n - 1) i = n - 1;
+        double s0 = 0.0, s1 = 0.0;
+        if (y > i * h) simpson(i * h, y, s0, s1);
+        a0 = m0[i] + s0;
+        a1 = m1[i] + s1;
+    }
+    ~BetaHalf()
+    {
+        std::free(m0);
+        std::free(m1);
+    }
+};
+
+bool build_codebook_beta(int bits, int d, kvq::Codebook *cb)
+{
+    BetaHalf B{};
+    if (!B.init(d)) return false;
+    const int L = 1 << bits, half = L / 2;
+    double m[8];
+    for (int k = 0; k < half; ++k) m[k] = 3.0 * (k + 0.5) / half;
+    for (int it = 0; it < 200000; ++it) {
+        double tau[9];
+        tau[0] = 0.0;
+        for (int k = 1; k < half; ++k) tau[k] = 0.5 * (m[k - 1] + m[k]);
+        tau[half] = B.r;
+        double change = 0.0, lo0, lo1, hi0, hi1;
+        B.at(tau[0], lo0, lo1);
+        for (int k = 0; k < half; ++k) {
+            B.at(tau[k + 1], hi0, hi1);
+            const double nm = (hi1 - lo1) / (hi0 - lo0);
+            change = std::fmax(change, std::fabs(nm - m[k]));
+            m[k] = nm;
+            lo0 = hi0;
+            lo1 = hi1;
+        }
+        if (change <= 1e-15) break;
+    }
+    std::memset(cb, 0, sizeof(*cb));
+    cb->bits = bits;
+    for (int k = 0; k < half; ++k) {
+        cb->c[half + k] = (float)m[k];
+        cb->c[half - 1 - k] = -(float)m[k];
+    }
+    for (int j = 0; j + 1 < L; ++j) cb->t[j] = (float)(((double)cb->c[j] + (double)cb->c[j + 1]) * 0.5);
+    return true;
 }
 
 struct DeviceGuard {
@@ -143,6 +239,8 @@ kvq_status kvq_create(const kvq_config *cfg, kvq_ctx **out)
     }
     if (mode == KVQ_MODE_MSE_QJL && !cfg->qjl_S) return KVQ_E_INVAL;
     if (mode == KVQ_MODE_NSN_VQ && !cfg->vq_codebook) return KVQ_E_INVAL;
+    if (cfg->codebook != KVQ_CODEBOOK_GAUSS && cfg->codebook != KVQ_CODEBOOK_BETA) return KVQ_E_INVAL;
+    if (cfg->codebook == KVQ_CODEBOOK_BETA && mode == KVQ_MODE_NSN_VQ) return KVQ_E_INVAL;
 
     int ndev = 0;
     if (hipGetDeviceCount(&ndev) != hipSuccess || cfg->device < 0 || cfg->device >= ndev)
@@ -160,7 +258,14 @@ kvq_status kvq_create(const kvq_config *cfg, kvq_ctx **out)
     if (hipDeviceGetAttribute(&c->n_cu, hipDeviceAttributeMultiprocessorCount, cfg->device) != hipSuccess ||
         c->n_cu < 1)
         c->n_cu = 256;
-    build_codebook(c->bits, &c->cb);
+    if (cfg->codebook == KVQ_CODEBOOK_BETA) {
+        if (!build_codebook_beta(c->bits, kvq::kD, &c->cb)) {
+            free_ctx(c);
+            return KVQ_E_NOMEM;
+        }
+    } else {
+        build_codebook(c->bits, &c->cb);
+    }
 
     kvq_status st = KVQ_OK;
     if (mode != KVQ_MODE_NSN_VQ) {

@@ -68,6 +68,11 @@ typedef enum {
 
 enum { KVQ_MODE_MSE = 0, KVQ_MODE_MSE_QJL = 1, KVQ_MODE_NSN_VQ = 2 };
 enum { KVQ_KIND_K = 0, KVQ_KIND_V = 1 };
+/* Scalar codebook of the MSE modes: Lloyd-Max for N(0,1) ([PQ] sec. 2), or
+ * Lloyd-Max for the exact law of a rotated unit vector's coordinate at
+ * d = 128, Beta((d-1)/2, (d-1)/2) on [-1, 1] scaled by sqrt(d) ([TQ] Como
+ * Funciona, Estagio 1). */
+enum { KVQ_CODEBOOK_GAUSS = 0, KVQ_CODEBOOK_BETA = 1 };
 
 /* Configuration of a context.  Host arrays are copied by kvq_create.
  *
@@ -94,6 +99,7 @@ typedef struct {
     const float *qjl_S;        /* host [d, d] row-major Gaussian projection (MSE_QJL) */
     const float *vq_codebook;  /* host [256, 8] fp32 codebook (NSN_VQ)                */
     int32_t device;            /* HIP device ordinal                                  */
+    int32_t codebook;          /* KVQ_CODEBOOK_* (MSE modes; 0 = N(0,1))              */
 } kvq_config;
 
 /* Create a context: validates the configuration, builds the b-bit N(0,1)

@@ -119,6 +119,14 @@ def gauss_mse(bits: int, c, t) -> float:
     return lib().kvqo_gauss_mse(bits, _p(_f64(c), _D), _p(_f64(t), _D))
 
 
+def _tables(bits: int, codebook: str):
+    if codebook == "gauss":
+        return tables_f32(bits)
+    if codebook == "beta":
+        return tables_f32_beta(bits)
+    raise ValueError(codebook)
+
+
 def beta_mass(d: int, a: float, b: float) -> float:
     """int_a^b (1 - y^2/d)^((d-3)/2) dy (unnormalised law of sqrt(d) u_i)."""
     return lib().kvqo_beta_mass(d, a, b)
@@ -239,7 +247,7 @@ def scalar_quantize(y, bits: int):
 
 
 # --------------------------------------------------------------------------- quantize
-def quantize(x, signs, bits: int, band: float = BAND, want_y: bool = False):
+def quantize(x, signs, bits: int, band: float = BAND, want_y: bool = False, codebook: str = "gauss"):
     """x [B,H,T,d] (any float dtype; fp16 widened exactly); signs [H,d] (+-1).
 
     Returns dict(codes [B,H,T,d*b/8] u8, norms [B,H,T] f64, idx [B,H,T,d],
@@ -248,7 +256,7 @@ def quantize(x, signs, bits: int, band: float = BAND, want_y: bool = False):
     B, H, T, d = x.shape
     signs = np.ascontiguousarray(signs, dtype=np.int8)
     assert signs.shape == (H, d)
-    _, t = tables_f32(bits)
+    _, t = _tables(bits, codebook)
     codes = np.zeros((B, H, T, d * bits // 8), np.uint8)
     norms = np.zeros((B, H, T))
     idx = np.zeros((B, H, T, d), np.int32)
@@ -273,7 +281,7 @@ def dequant(rec, rho, signs_row, bits: int, d: int = 128):
 
 
 def logits(q, codes, norms, signs, bits: int, route: int = 1, qjl_signs=None, gamma=None,
-           S=None):
+           S=None, codebook: str = "gauss"):
     """q [B,Hq,d]; codes [B,Hkv,T,rec]; norms [B,Hkv,T]; signs [Hkv,d] -> [B,Hq,T]."""
     q = _f64(q)
     B, Hq, d = q.shape
@@ -281,7 +289,7 @@ def logits(q, codes, norms, signs, bits: int, route: int = 1, qjl_signs=None, ga
     _, Hkv, T, _ = codes.shape
     norms = _f64(norms)
     signs = np.ascontiguousarray(signs, dtype=np.int8)
-    c, _ = tables_f32(bits)
+    c, _ = _tables(bits, codebook)
     out = np.zeros((B, Hq, T))
     m = 0
     if qjl_signs is not None:
@@ -295,7 +303,8 @@ def logits(q, codes, norms, signs, bits: int, route: int = 1, qjl_signs=None, ga
     return out
 
 
-def attention(q, kc, kn, vc, vn, signs_k, signs_v, bits: int, sm_scale: float | None = None):
+def attention(q, kc, kn, vc, vn, signs_k, signs_v, bits: int, sm_scale: float | None = None,
+              codebook: str = "gauss"):
     q = _f64(q)
     B, Hq, d = q.shape
     kc = np.ascontiguousarray(kc, dtype=np.uint8)
@@ -304,7 +313,7 @@ def attention(q, kc, kn, vc, vn, signs_k, signs_v, bits: int, sm_scale: float | 
     kn, vn = _f64(kn), _f64(vn)
     sk = np.ascontiguousarray(signs_k, dtype=np.int8)
     sv = np.ascontiguousarray(signs_v, dtype=np.int8)
-    c, _ = tables_f32(bits)
+    c, _ = _tables(bits, codebook)
     if sm_scale is None:
         sm_scale = 1.0 / np.sqrt(d)
     out = np.zeros((B, Hq, d))
