@@ -301,19 +301,47 @@ __global__ __launch_bounds__(64 * G) void k_nsn_merge(const float *__restrict__ 
     const int lane = threadIdx.x & 63, h = threadIdx.x >> 6;
     const int64_t bg = blockIdx.x, b = bg / Hkv, g = bg % Hkv;
     const float *p0 = part + (bg * n_split * G + h) * kPartStride;
+    const int64_t sst = (int64_t)G * kPartStride;  // split stride
+    // split headers (M, L, WO) one split per lane, all loads in flight
+    __shared__ float fw[G][kMaxSplits];
+    constexpr int kPer = kMaxSplits / 64;
+    float mv[kPer], lv[kPer], ov_[kPer];
     float M = -__builtin_inff();
-#pragma unroll 8
-    for (int s = 0; s < n_split; ++s) M = fmaxf(M, p0[(int64_t)s * G * kPartStride + kD]);
-    float x0 = 0.0f, x1 = 0.0f, L = 0.0f, WO = 0.0f;
-#pragma unroll 8
-    for (int s = 0; s < n_split; ++s) {
-        const float *p = p0 + (int64_t)s * G * kPartStride;
-        const float f = __builtin_amdgcn_exp2f(p[kD] - M);
-        const f2_t a = reinterpret_cast<const f2_t *>(p)[lane];
-        x0 = fmaf(f, a.x, x0);
-        x1 = fmaf(f, a.y, x1);
-        L = fmaf(f, p[kD + 1], L);
-        WO = fmaf(f, p[kD + 2], WO);
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const int sp = lane + 64 * k;
+        const bool in = sp < n_split;
+        mv[k] = in ? p0[sp * sst + kD] : -__builtin_inff();
+        lv[k] = in ? p0[sp * sst + kD + 1] : 0.0f;
+        ov_[k] = in ? p0[sp * sst + kD + 2] : 0.0f;
+        M = fmaxf(M, mv[k]);
+    }
+    M = wave_max(M);
+    float L = 0.0f, WO = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const int sp = lane + 64 * k;
+        const float f = __builtin_amdgcn_exp2f(mv[k] - M);  // 0 past the last split
+        L = fmaf(f, lv[k], L);
+        WO = fmaf(f, ov_[k], WO);
+        if (sp < n_split) fw[h][sp] = f;
+    }
+    L = wave_sum(L);
+    WO = wave_sum(WO);
+    wave_lds_sync();
+    // accumulators: 16 splits' loads in flight at a time
+    float x0 = 0.0f, x1 = 0.0f;
+    for (int s0 = 0; s0 < n_split; s0 += 16) {
+        f2_t a[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+            a[u] = s0 + u < n_split ? reinterpret_cast<const f2_t *>(p0 + (s0 + u) * sst)[lane] : f2_t{0.0f, 0.0f};
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const float f = s0 + u < n_split ? fw[h][s0 + u] : 0.0f;
+            x0 = fmaf(f, a[u].x, x0);
+            x1 = fmaf(f, a[u].y, x1);
+        }
     }
     wave_fwht(x0, x1, lane);
     const f2_t ov = reinterpret_cast<const f2_t *>(vo + bg * kD)[lane];
