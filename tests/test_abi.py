@@ -69,6 +69,9 @@ def test_create_validation():
     assert L.kvq_create(C.byref(cfg), C.byref(h)) == kvq.KVQ_E_INVAL
     cfg, keep = _cfg(mode=2)  # NSN mode needs a codebook
     assert L.kvq_create(C.byref(cfg), C.byref(h)) == kvq.KVQ_E_INVAL
+    for bad in (dict(codebook=2), dict(codebook=-1)):  # not a KVQ_CODEBOOK_*
+        cfg, keep = _cfg(**bad)
+        assert L.kvq_create(C.byref(cfg), C.byref(h)) == kvq.KVQ_E_INVAL, bad
     cfg, keep = _cfg(device=999)  # no such device (no device at all on a CPU host)
     assert L.kvq_create(C.byref(cfg), C.byref(h)) == kvq.KVQ_E_DEVICE
     assert not h.value
@@ -85,5 +88,13 @@ def test_null_context_calls():
     assert L.kvq_attn_decode_ws_bytes(None, 1, 1, 1) == 0
     assert L.kvq_nsn_vq_ws_bytes(None, 1, 1) == 0
     assert L.kvq_nsn_vq_quantize(None, None, 1, 1, None, None, None, None, None, 0, None) == kvq.KVQ_E_INVAL
+    assert L.kvq_nsn_logits(None, None, 1, 4, 1, None, None, None, None, None, None) == kvq.KVQ_E_INVAL
+    assert L.kvq_nsn_attn_decode_ws_bytes(None, 1, 4, 1) == 0
+    assert L.kvq_nsn_attn_decode(None, None, 1, 4, 1, None, None, None, None, None, None, None, None, 0.0, None,
+                                 None, 0, None) == kvq.KVQ_E_INVAL
+    assert L.kvq_attn_decode_stream_ws_bytes(None, 1, 4, 1) == 0
+    assert L.kvq_attn_decode_stream(None, None, 1, 4, 1, 1, None, None, None, None, 0, 0, None, None, 0.0, None,
+                                    None, 0, None) == kvq.KVQ_E_INVAL
+    assert L.kvq_flush(None, None, None, 1, 1, 1, 1, None, None, None, None, 0, 1, None) == kvq.KVQ_E_INVAL
     for s in range(6):
         assert kvq.strerror(s)
