@@ -159,3 +159,11 @@ def random_nsn_codes(seed: int, lead, d: int = D, sub: int = 8, o_scale: float =
                 s1=np.exp(rng.normal(1.0, 0.25, size=lead)).astype(np.float32),
                 s2=rng.uniform(0.6, 1.0, size=lead).astype(np.float32),
                 o=(rng.standard_normal(lead[:-1] + (d,)) * o_scale).astype(np.float32))
+
+
+def random_orthogonal(seed: int, d: int = D):
+    """A Haar-random orthogonal d x d matrix (float64): QR of a seeded N(0,1)
+    matrix with the signs of R's diagonal moved into Q."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q, r = np.linalg.qr(rng.standard_normal((d, d)))
+    return q * np.sign(np.diag(r))[None, :]

@@ -79,6 +79,12 @@ def _setup(L):
                                  _I8, _I8, _F, C.c_double, _D]
     L.kvqo_attention_stream.argtypes = [C.c_int, C.c_int, i64, i64, i64, i64, i64, _D, _U8, _D, _U8, _D, _D,
                                         _D, _I8, _I8, _F, C.c_double, _D]
+    L.kvqo_quantize_dense.argtypes = [C.c_int, C.c_int, i64, i64, i64, _D, _D, _F, C.c_double, _U8, _D, _D, _I32,
+                                      _U8]
+    L.kvqo_dequant_dense.argtypes = [C.c_int, C.c_int, _U8, C.c_double, _D, _F, _D]
+    L.kvqo_logits_dense.argtypes = [C.c_int, C.c_int, C.c_int, i64, i64, i64, i64, _D, _U8, _D, _D, _F, _D]
+    L.kvqo_attention_dense.argtypes = [C.c_int, C.c_int, i64, i64, i64, i64, _D, _U8, _D, _U8, _D, _D, _F,
+                                       C.c_double, _D]
     L.kvqo_qjl.argtypes = [C.c_int, C.c_int, i64, _D, _I32, _F, _D, C.c_double, _U8, _D, _U8]
     L.kvqo_nsn_vq.argtypes = [C.c_int, C.c_int, C.c_int, i64, i64, _D, _D, C.c_double, _U8, _D,
                               _D, _D, _D, _U8, _D]
@@ -344,6 +350,60 @@ def attention_stream(q, kc, kn, vc, vn, k_tail, v_tail, signs_k, signs_v, bits: 
                                      _p(np.ascontiguousarray(signs_k, dtype=np.int8), _I8),
                                      _p(np.ascontiguousarray(signs_v, dtype=np.int8), _I8), _p(c, _F),
                                      float(sm_scale), _p(out, _D)))
+    return out
+
+
+def quantize_dense(x, Q, bits: int, band: float = BAND, want_y: bool = False, codebook: str = "gauss"):
+    """As quantize, with the dense rotation y = sqrt(d) Q x / ||x|| (Q [d,d] orthogonal)."""
+    x = _f64(x)
+    B, H, T, d = x.shape
+    Q = _f64(Q)
+    _, t = _tables(bits, codebook)
+    codes = np.zeros((B, H, T, d * bits // 8), np.uint8)
+    norms = np.zeros((B, H, T))
+    idx = np.zeros((B, H, T, d), np.int32)
+    flags = np.zeros((B, H, T, d), np.uint8)
+    y = np.zeros((B, H, T, d)) if want_y else None
+    _chk(lib().kvqo_quantize_dense(d, bits, B, H, T, _p(x, _D), _p(Q, _D), _p(t, _F), band, _p(codes, _U8),
+                                   _p(norms, _D), _p(y, _D), _p(idx, _I32), _p(flags, _U8)))
+    out = dict(codes=codes, norms=norms, idx=idx, flags=flags)
+    if want_y:
+        out["y"] = y
+    return out
+
+
+def dequant_dense(rec, rho, Q, bits: int, d: int = 128, codebook: str = "gauss"):
+    c, _ = _tables(bits, codebook)
+    out = np.zeros(d)
+    lib().kvqo_dequant_dense(d, bits, _p(np.ascontiguousarray(rec, dtype=np.uint8), _U8), float(rho), _p(_f64(Q), _D),
+                             _p(c, _F), _p(out, _D))
+    return out
+
+
+def logits_dense(q, codes, norms, Q, bits: int, route: int = 1, codebook: str = "gauss"):
+    q = _f64(q)
+    B, Hq, d = q.shape
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    _, Hkv, T, _ = codes.shape
+    c, _ = _tables(bits, codebook)
+    out = np.zeros((B, Hq, T))
+    _chk(lib().kvqo_logits_dense(route, d, bits, B, Hq, Hkv, T, _p(q, _D), _p(codes, _U8), _p(_f64(norms), _D),
+                                 _p(_f64(Q), _D), _p(c, _F), _p(out, _D)))
+    return out
+
+
+def attention_dense(q, kc, kn, vc, vn, Q, bits: int, sm_scale: float | None = None, codebook: str = "gauss"):
+    q = _f64(q)
+    B, Hq, d = q.shape
+    kc = np.ascontiguousarray(kc, dtype=np.uint8)
+    vc = np.ascontiguousarray(vc, dtype=np.uint8)
+    _, Hkv, T, _ = kc.shape
+    c, _ = _tables(bits, codebook)
+    if sm_scale is None:
+        sm_scale = 1.0 / np.sqrt(d)
+    out = np.zeros((B, Hq, d))
+    _chk(lib().kvqo_attention_dense(d, bits, B, Hq, Hkv, T, _p(q, _D), _p(kc, _U8), _p(_f64(kn), _D), _p(vc, _U8),
+                                    _p(_f64(vn), _D), _p(_f64(Q), _D), _p(c, _F), float(sm_scale), _p(out, _D)))
     return out
 
 

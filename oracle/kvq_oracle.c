@@ -587,6 +587,154 @@ ORC_API int kvqo_attention(int d, int bits, int64_t B, int64_t Hq, int64_t Hkv, 
 }
 
 /* ------------------------------------------------------------------------ */
+/* Dense rotation ("O Que E TurboQuant?", Como Funciona, Estagio 1: a random  */
+/* orthogonal transformation independent of the data, from the QR            */
+/* decomposition of a Gaussian matrix).  Q [d, d] row-major orthogonal, the   */
+/* same for every head and for K and V.  Scaled like the Hadamard path so     */
+/* that the coordinates have unit variance:                                   */
+/*   y = sqrt(d) Q (x / rho);  k_hat = rho Q^T c[idx] / sqrt(d);              */
+/*   <q, k_hat> = rho / d * <sqrt(d) Q q, c[idx]>.                            */
+/* ------------------------------------------------------------------------ */
+
+static void matvec(const double *Q, const double *x, double *y, int d, int transpose)
+{
+    for (int i = 0; i < d; ++i) {
+        double s = 0.0;
+        for (int j = 0; j < d; ++j) s += (transpose ? Q[(int64_t)j * d + i] : Q[(int64_t)i * d + j]) * x[j];
+        y[i] = s;
+    }
+}
+
+ORC_API int kvqo_quantize_dense(int d, int bits, int64_t B, int64_t H, int64_t T, const double *x,
+                                const double *Q, const float *t32, double band, uint8_t *codes, double *norms,
+                                double *y_out, int32_t *idx_out, uint8_t *flags)
+{
+    if (d <= 0 || d > 1024 || bits < 1 || bits > 8) return -1;
+    const int L = 1 << bits;
+    const int rec = d * bits / 8;
+    double t[255];
+    for (int j = 0; j + 1 < L; ++j) t[j] = t32[j];
+    double *u = (double *)malloc(sizeof(double) * d);
+    double *y = (double *)malloc(sizeof(double) * d);
+    int32_t *idx = (int32_t *)malloc(sizeof(int32_t) * d);
+    for (int64_t v = 0; v < B * H * T; ++v) {
+        const double *xv = x + v * d;
+        double ss = 0.0;
+        for (int i = 0; i < d; ++i) ss += xv[i] * xv[i];
+        const double rho = sqrt(ss);
+        for (int i = 0; i < d; ++i) u[i] = rho > 0.0 ? xv[i] / rho : 0.0;
+        matvec(Q, u, y, d, 0);
+        for (int i = 0; i < d; ++i) {
+            y[i] *= sqrt((double)d);
+            int f = 0;
+            idx[i] = bucket(y[i], t, L, band, &f);
+            if (flags) flags[v * d + i] = (uint8_t)f;
+            if (y_out) y_out[v * d + i] = y[i];
+            if (idx_out) idx_out[v * d + i] = idx[i];
+        }
+        norms[v] = rho;
+        kvqo_pack(idx, d, bits, codes + v * rec);
+    }
+    free(u);
+    free(y);
+    free(idx);
+    return 0;
+}
+
+ORC_API void kvqo_dequant_dense(int d, int bits, const uint8_t *rec, double rho, const double *Q,
+                                const float *c32, double *out)
+{
+    int32_t idx[1024];
+    double c[1024];
+    kvqo_unpack(rec, d, bits, idx);
+    for (int i = 0; i < d; ++i) c[i] = c32[idx[i]];
+    matvec(Q, c, out, d, 1);
+    for (int i = 0; i < d; ++i) out[i] *= rho / sqrt((double)d);
+}
+
+/* route 0: dequantise, then <q, k_hat>; route 1: rotated query q' = sqrt(d) Q q. */
+ORC_API int kvqo_logits_dense(int route, int d, int bits, int64_t B, int64_t Hq, int64_t Hkv, int64_t T,
+                              const double *q, const uint8_t *codes, const double *norms, const double *Q,
+                              const float *c32, double *logits)
+{
+    if (Hkv <= 0 || Hq % Hkv || d > 1024) return -1;
+    const int64_t G = Hq / Hkv;
+    const int rec = d * bits / 8;
+    double *kh = (double *)malloc(sizeof(double) * d);
+    double *qr = (double *)malloc(sizeof(double) * d);
+    int32_t idx[1024];
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t h = 0; h < Hq; ++h) {
+            const int64_t g = h / G;
+            const double *qh = q + (b * Hq + h) * d;
+            matvec(Q, qh, qr, d, 0);
+            for (int i = 0; i < d; ++i) qr[i] *= sqrt((double)d);
+            for (int64_t t = 0; t < T; ++t) {
+                const int64_t v = (b * Hkv + g) * T + t;
+                double acc = 0.0;
+                if (route == 0) {
+                    kvqo_dequant_dense(d, bits, codes + v * rec, norms[v], Q, c32, kh);
+                    for (int i = 0; i < d; ++i) acc += qh[i] * kh[i];
+                } else {
+                    kvqo_unpack(codes + v * rec, d, bits, idx);
+                    for (int i = 0; i < d; ++i) acc += qr[i] * c32[idx[i]];
+                    acc *= norms[v] / d;
+                }
+                logits[(b * Hq + h) * T + t] = acc;
+            }
+        }
+    free(kh);
+    free(qr);
+    return 0;
+}
+
+/* Decode attention with the dense rotation: as kvqo_attention, keys and
+ * values dequantised with Q^T. */
+ORC_API int kvqo_attention_dense(int d, int bits, int64_t B, int64_t Hq, int64_t Hkv, int64_t T, const double *q,
+                                 const uint8_t *kc, const double *kn, const uint8_t *vc, const double *vn,
+                                 const double *Q, const float *c32, double sm_scale, double *out)
+{
+    if (Hkv <= 0 || Hq % Hkv || T <= 0 || d > 1024) return -1;
+    const int64_t G = Hq / Hkv;
+    const int rec = d * bits / 8;
+    double *K = (double *)malloc(sizeof(double) * T * d);
+    double *V = (double *)malloc(sizeof(double) * T * d);
+    double *s = (double *)malloc(sizeof(double) * T);
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t g = 0; g < Hkv; ++g) {
+            for (int64_t t = 0; t < T; ++t) {
+                const int64_t v = (b * Hkv + g) * T + t;
+                kvqo_dequant_dense(d, bits, kc + v * rec, kn[v], Q, c32, K + t * d);
+                kvqo_dequant_dense(d, bits, vc + v * rec, vn[v], Q, c32, V + t * d);
+            }
+            for (int64_t hh = 0; hh < G; ++hh) {
+                const double *qh = q + (b * Hq + g * G + hh) * d;
+                double mx = -INFINITY;
+                for (int64_t t = 0; t < T; ++t) {
+                    double a = 0.0;
+                    for (int i = 0; i < d; ++i) a += qh[i] * K[t * d + i];
+                    s[t] = sm_scale * a;
+                    if (s[t] > mx) mx = s[t];
+                }
+                double l = 0.0;
+                for (int64_t t = 0; t < T; ++t) {
+                    s[t] = exp(s[t] - mx);
+                    l += s[t];
+                }
+                double *o = out + (b * Hq + g * G + hh) * d;
+                for (int i = 0; i < d; ++i) o[i] = 0.0;
+                for (int64_t t = 0; t < T; ++t)
+                    for (int i = 0; i < d; ++i) o[i] += s[t] * V[t * d + i];
+                for (int i = 0; i < d; ++i) o[i] /= l;
+            }
+        }
+    free(K);
+    free(V);
+    free(s);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Decode attention over a cache split into a quantised part and a full-     */
 /* precision residual (NSNQuant, "Detalhes de Implementacao": following KIVI, */
 /* the residual is quantised and appended when it fills).  Token order: the  */
