@@ -326,6 +326,30 @@ def rows(torch, kvq, synth, dev, timer, reps, oracle_rates):
     oracle_rates["attn_decode_l8b32k_b3"] = oracle_rate(
         lambda: O.attention(inp["q"], rq["codes"], rq["norms"], rv["codes"], rv["norms"], inp["signs_k"],
                             inp["signs_v"], 3), B * Hkv * 2048)
+    # dense rotation (one Haar-random Q for every head), 3 bits
+    ctx = kvq.Context(Hkv, 3, device=dev.index, rot_Q=synth.random_orthogonal(44).astype(np.float32))
+    ns = rng_sets(decode_bytes(n, 3))
+    cs = [[torch.empty((B, Hkv, T, 48), dtype=torch.uint8, device=dev),
+           torch.empty((B, Hkv, T), dtype=torch.float32, device=dev),
+           torch.empty((B, Hkv, T, 48), dtype=torch.uint8, device=dev),
+           torch.empty((B, Hkv, T), dtype=torch.float32, device=dev)] for _ in range(ns)]
+
+    def quantd(i):
+        k, v = xs[i % len(xs)]
+        c = cs[i % ns]
+        kvq.kvq_quantize_kv(ctx, k, v, B, Hkv, T, c[0], c[1], c[2], c[3])
+    # the rotation on the matrix cores: 128 x 128 products, high and low parts of Q
+    out["quantize_kv_dense_l8b32k_b3"] = row(*timer.run(quantd, reps, 4 + ns), nbytes=quant_bytes(2 * n, 3),
+                                             flops=2 * n * 2 * 2 * D * D, units_per_launch=2 * n, unit="vectors")
+    outb = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    ws = ctx.decode_ws(B, Hq, T)
+
+    def decd(i):
+        c = cs[i % ns]
+        kvq.kvq_attn_decode(ctx, q, B, Hq, T, c[0], c[1], c[2], c[3], 0.0, outb, ws)
+    out["attn_decode_dense_l8b32k_b3"] = row(*timer.run(decd, reps, 5), nbytes=decode_bytes(n, 3),
+                                             units_per_launch=n, unit="keys", buffer_sets=ns)
+    del cs, ctx
     del xs, k0, v0
     torch.cuda.empty_cache()
 

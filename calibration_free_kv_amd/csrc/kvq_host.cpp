@@ -175,6 +175,9 @@ void free_ctx(kvq_ctx *c)
     (void)hipFree(c->d_S);
     (void)hipFree(c->d_S16);
     (void)hipFree(c->d_vq);
+    (void)hipFree(c->d_Q);
+    (void)hipFree(c->d_Qt);
+    (void)hipFree(c->d_Q16);
     (void)hipFree(c->d_vq16);
     (void)hipFree(c->d_vqbias);
     std::free(c->h_signs);
@@ -241,6 +244,13 @@ kvq_status kvq_create(const kvq_config *cfg, kvq_ctx **out)
     if (mode == KVQ_MODE_NSN_VQ && !cfg->vq_codebook) return KVQ_E_INVAL;
     if (cfg->codebook != KVQ_CODEBOOK_GAUSS && cfg->codebook != KVQ_CODEBOOK_BETA) return KVQ_E_INVAL;
     if (cfg->codebook == KVQ_CODEBOOK_BETA && mode == KVQ_MODE_NSN_VQ) return KVQ_E_INVAL;
+    if (cfg->rotation != KVQ_ROTATION_HADAMARD && cfg->rotation != KVQ_ROTATION_DENSE) return KVQ_E_INVAL;
+    if (cfg->rotation == KVQ_ROTATION_DENSE) {
+        if (mode != KVQ_MODE_MSE) return KVQ_E_UNSUPPORTED;
+        if (!cfg->rot_Q) return KVQ_E_INVAL;
+        for (int i = 0; i < kvq::kD * kvq::kD; ++i)
+            if (!std::isfinite(cfg->rot_Q[i]) || std::fabs(cfg->rot_Q[i]) > 1.0f) return KVQ_E_INVAL;
+    }
 
     int ndev = 0;
     if (hipGetDeviceCount(&ndev) != hipSuccess || cfg->device < 0 || cfg->device >= ndev)
@@ -253,6 +263,7 @@ kvq_status kvq_create(const kvq_config *cfg, kvq_ctx **out)
     c->d = cfg->d;
     c->bits = mode == KVQ_MODE_NSN_VQ ? 1 : cfg->bits;
     c->mode = mode;
+    c->rotation = cfg->rotation;
     c->H = H;
     c->device = cfg->device;
     if (hipDeviceGetAttribute(&c->n_cu, hipDeviceAttributeMultiprocessorCount, cfg->device) != hipSuccess ||
@@ -344,6 +355,25 @@ kvq_status kvq_create(const kvq_config *cfg, kvq_ctx **out)
         if (st == KVQ_OK) st = upload(&c->d_vqbias, bias, (size_t)kvq::kVqK);
         std::free(c16);
     }
+    if (st == KVQ_OK && cfg->rotation == KVQ_ROTATION_DENSE) {
+        const size_t n = (size_t)kvq::kD * kvq::kD;
+        float *qt = (float *)std::malloc(n * sizeof(float));
+        _Float16 *q16 = (_Float16 *)std::malloc(2 * n * sizeof(_Float16));
+        if (!qt || !q16) st = KVQ_E_NOMEM;
+        for (int i = 0; st == KVQ_OK && i < kvq::kD; ++i)
+            for (int j = 0; j < kvq::kD; ++j) {
+                const float v = cfg->rot_Q[i * kvq::kD + j];
+                qt[j * kvq::kD + i] = v;
+                const _Float16 hi = (_Float16)v;
+                q16[i * kvq::kD + j] = hi;
+                q16[n + i * kvq::kD + j] = (_Float16)(v - (float)hi);
+            }
+        if (st == KVQ_OK) st = upload(&c->d_Q, cfg->rot_Q, n);
+        if (st == KVQ_OK) st = upload(&c->d_Qt, qt, n);
+        if (st == KVQ_OK) st = upload(&c->d_Q16, q16, 2 * n);
+        std::free(qt);
+        std::free(q16);
+    }
     if (st != KVQ_OK) {
         free_ctx(c);
         return st;
@@ -406,6 +436,9 @@ kvq_status kvq_quantize(kvq_ctx *ctx, int32_t kind, const void *x_f16, int64_t B
     if (B * H_kv > (int64_t(1) << 40) || T > (int64_t(1) << 31)) return KVQ_E_INVAL;
     DeviceGuard g(ctx->device);
     if (!g.ok) return KVQ_E_DEVICE;
+    if (ctx->rotation == KVQ_ROTATION_DENSE)
+        return launch_status(kvq::launch_quantize_dense(ctx, x_f16, nullptr, B * H_kv * T, codes, norms, nullptr,
+                                                        nullptr, (hipStream_t)stream));
     return launch_status(kvq::launch_quantize(ctx, kind, x_f16, B, T, codes, norms, qjl_signs,
                                               qjl_gamma, (hipStream_t)stream));
 }
@@ -424,6 +457,9 @@ kvq_status kvq_quantize_kv(kvq_ctx *ctx, const void *k_f16, const void *v_f16, i
     if (B * H_kv > (int64_t(1) << 40) || T > (int64_t(1) << 31)) return KVQ_E_INVAL;
     DeviceGuard g(ctx->device);
     if (!g.ok) return KVQ_E_DEVICE;
+    if (ctx->rotation == KVQ_ROTATION_DENSE)
+        return launch_status(kvq::launch_quantize_dense(ctx, k_f16, v_f16, B * H_kv * T, k_codes, k_norms,
+                                                        v_codes, v_norms, (hipStream_t)stream));
     return launch_status(kvq::launch_quantize_kv(ctx, k_f16, v_f16, B, T, k_codes, k_norms, v_codes, v_norms,
                                                  (hipStream_t)stream));
 }
@@ -529,6 +565,7 @@ kvq_status kvq_attn_decode_stream(kvq_ctx *ctx, const void *q_f16, int64_t B, in
                                   void *ws, size_t ws_bytes, void *stream)
 {
     if (!ctx || ctx->mode != KVQ_MODE_MSE) return KVQ_E_INVAL;
+    if (ctx->rotation != KVQ_ROTATION_HADAMARD) return KVQ_E_UNSUPPORTED;
     if (B < 0 || H_q < 1 || H_q % ctx->H) return KVQ_E_INVAL;
     const int64_t G = H_q / ctx->H;
     if (G != 1 && G != 2 && G != 4) return KVQ_E_INVAL;
@@ -566,6 +603,7 @@ kvq_status kvq_flush(kvq_ctx *ctx, const void *k_tail_f16, const void *v_tail_f1
                      int64_t T_cap, void *stream)
 {
     if (!ctx || ctx->mode != KVQ_MODE_MSE) return KVQ_E_INVAL;
+    if (ctx->rotation != KVQ_ROTATION_HADAMARD) return KVQ_E_UNSUPPORTED;
     if (B < 0 || H_kv != ctx->H || R < 0 || R > R_cap || T0 < 0 || T0 + R > T_cap) return KVQ_E_INVAL;
     if (B == 0 || R == 0) return KVQ_OK;
     if (!k_tail_f16 || !v_tail_f16 || !k_codes || !k_norms || !v_codes || !v_norms) return KVQ_E_INVAL;

@@ -36,6 +36,10 @@ struct kvq_ctx {
     _Float16 *d_S16;      // [2][128][128] fp16 hi and lo parts of S (MSE_QJL)
     bool S_exact_f16;     // S_lo == 0
     float *d_vq;          // [256][8] fp32 codebook (NSN_VQ scoring)
+    int rotation;         // KVQ_ROTATION_*
+    float *d_Q;           // [128][128] dense rotation Q, row-major (KVQ_ROTATION_DENSE)
+    float *d_Qt;          // its transpose
+    _Float16 *d_Q16;      // [2][128][128] fp16 high and low parts of Q
     _Float16 *d_vq16;     // [2][256][8] fp16 hi and lo parts of the codebook
     bool vq_exact_f16;    // codebook lo == 0
     float *d_vqbias;      // [256] -||C_j||^2 / 2
@@ -67,6 +71,11 @@ int decode_auto_splits(int64_t B, int64_t Hkv, int64_t T);
 hipError_t launch_decode(const kvq_ctx *ctx, const void *q, int64_t B, int64_t Hq, int64_t T,
                          const uint8_t *kc, const float *kn, const uint8_t *vc, const float *vn,
                          float sm_scale, float *out, void *ws, int n_split, hipStream_t s);
+
+// Quantise with the dense rotation: N vectors of the list xk (and N of xv
+// when xv is not null) into ck/nk (cv/nv).
+hipError_t launch_quantize_dense(const kvq_ctx *ctx, const void *xk, const void *xv, int64_t N, uint8_t *ck,
+                                 float *nk, uint8_t *cv, float *nv, hipStream_t s);
 
 // Residual window of a streaming cache: R full-precision tokens per (batch, KV
 // head) in fp16 arrays [B, H_kv, R_cap, 128].

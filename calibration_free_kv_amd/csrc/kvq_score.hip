@@ -53,20 +53,32 @@ __device__ __forceinline__ uint32_t field(const uint32_t *Wd, int f)
 
 
 // Prologue shared by the score kernels: qr[G][128] <- H (D .* q_h) for the G
-// query heads of KV head g of batch b, one wave per head.  Ends with a barrier.
+// query heads of KV head g of batch b, one wave per head; with a dense
+// rotation Q (not null) instead qr <- sqrt(d) Q q_h.  Ends with a barrier.
 template <int G>
 __device__ void rotate_queries(const half_t *__restrict__ q, const float *__restrict__ signs,
-                               int64_t b, int g, int Hq, float *qr)
+                               int64_t b, int g, int Hq, float *qr, const float *__restrict__ Qm)
 {
     const int lane = threadIdx.x & 63;
     const int wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
     for (int h = wv; h < G; h += nw) {
         const uint32_t pr =
             reinterpret_cast<const uint32_t *>(q + ((int64_t)b * Hq + (int64_t)g * G + h) * kD)[lane];
-        const f2_t sg = reinterpret_cast<const f2_t *>(signs + g * kD)[lane];
-        float x0 = (float)__builtin_bit_cast(h2_t, pr).x * sg.x;
-        float x1 = (float)__builtin_bit_cast(h2_t, pr).y * sg.y;
-        wave_fwht(x0, x1, lane);
+        float x0 = (float)__builtin_bit_cast(h2_t, pr).x;
+        float x1 = (float)__builtin_bit_cast(h2_t, pr).y;
+        if (Qm) {
+            reinterpret_cast<f2_t *>(qr + h * kD)[lane] = f2_t{x0, x1};
+            wave_lds_sync();
+            gemv_rows2(Qm, qr + h * kD, lane, x0, x1);
+            wave_lds_sync();
+            x0 *= 11.313708498984761f;
+            x1 *= 11.313708498984761f;
+        } else {
+            const f2_t sg = reinterpret_cast<const f2_t *>(signs + g * kD)[lane];
+            x0 *= sg.x;
+            x1 *= sg.y;
+            wave_fwht(x0, x1, lane);
+        }
         reinterpret_cast<f2_t *>(qr + h * kD)[lane] = f2_t{x0, x1};
     }
     __syncthreads();
@@ -176,7 +188,7 @@ __global__ __launch_bounds__(kLgThreads) void k_logits(
     const uint32_t *__restrict__ qjl_signs, const float *__restrict__ qjl_gamma,
     const float *__restrict__ signs, const float *__restrict__ St, Codebook cb,
     float *__restrict__ logits, int64_t T, int H, int Hq, int64_t tokens_per_block,
-    int64_t blocks_per_bh)
+    int64_t blocks_per_bh, const float *__restrict__ Qm)
 {
     using FD = Fields<BITS>;
     extern __shared__ __align__(16) float smem[];
@@ -192,7 +204,7 @@ __global__ __launch_bounds__(kLgThreads) void k_logits(
     const int g = (int)(bh - b * H);
 
     stage_centroids(cb, ctab);
-    rotate_queries<G>(q, signs, b, g, Hq, qr);
+    rotate_queries<G>(q, signs, b, g, Hq, qr, Qm);
     build_tables<BITS, G>(qr, ctab, lut);
     if constexpr (QJL) {
         // p_h[j] = sum_i S[j][i] q'_h[i] / sqrt(d): thread (h, j) walks row i of
@@ -431,8 +443,11 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
     const uint8_t *__restrict__ vc, const float *__restrict__ vn, const float *__restrict__ signs_k,
     const float *__restrict__ signs_v, Codebook cb, float scale_log2, float *__restrict__ out,
     float *__restrict__ part, unsigned *__restrict__ counters, int64_t T, int64_t ldt, int H, int Hq,
-    int n_split, int n_part, int64_t chunk)
+    int n_split, int n_part, int64_t chunk, const float *__restrict__ Qm, const float *__restrict__ Qtm)
 {
+    // Qm, Qtm (dense rotation and its transpose, or null): the query is
+    // rotated as sqrt(d) Q q and the output as sqrt(d) Q^T acc instead of
+    // with the randomized Hadamard transform.
     // T valid tokens of each (b, g) in arrays of ldt tokens per (b, g); the
     // partials of (b, g) occupy n_part slots (n_split blocks, plus one slot
     // written beforehand by the residual-window kernel when n_part > n_split)
@@ -565,9 +580,21 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
         // largest entry in [2^14, 2^15): inside the fp16 range, with full
         // precision for the high and low parts (rows 2h and 2h + 1 of qh).
         // The logit factor undoes the scale.
-        float x0 = (float)__builtin_bit_cast(h2_t, qv).x * qs.x;
-        float x1 = (float)__builtin_bit_cast(h2_t, qv).y * qs.y;
-        wave_fwht(x0, x1, lane);
+        float x0 = (float)__builtin_bit_cast(h2_t, qv).x;
+        float x1 = (float)__builtin_bit_cast(h2_t, qv).y;
+        if (Qm) {  // this wave's staging area holds q while it is rotated
+            float *qtmp = reinterpret_cast<float *>(stg);
+            reinterpret_cast<f2_t *>(qtmp)[lane] = f2_t{x0, x1};
+            wave_lds_sync();
+            gemv_rows2(Qm, qtmp, lane, x0, x1);
+            wave_lds_sync();
+            x0 *= 11.313708498984761f;
+            x1 *= 11.313708498984761f;
+        } else {
+            x0 *= qs.x;
+            x1 *= qs.y;
+            wave_fwht(x0, x1, lane);
+        }
         const float amax = wave_max(fmaxf(__builtin_fabsf(x0), __builtin_fabsf(x1)));
         const int e = amax > 0.0f ? __builtin_amdgcn_frexp_expf(amax) : 0;
         const float sc = __builtin_ldexpf(1.0f, 15 - e);
@@ -830,9 +857,17 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
             a0 += v.x;
             a1 += v.y;
         }
-        wave_fwht(a0, a1, lane);
-        const f2_t sv = reinterpret_cast<const f2_t *>(signs_v + g * kD)[lane];
-        reinterpret_cast<f2_t *>(out + ((b * Hq) + (int64_t)g * G + mh) * kD)[lane] = f2_t{a0 * sv.x, a1 * sv.y};
+        if (Qtm) {  // out = sqrt(d) Q^T acc, with acc in this wave's partial-sum slot
+            reinterpret_cast<f2_t *>(pacc + wv * kD)[lane] = f2_t{a0, a1};
+            wave_lds_sync();
+            gemv_rows2(Qtm, pacc + wv * kD, lane, a0, a1);
+            reinterpret_cast<f2_t *>(out + ((b * Hq) + (int64_t)g * G + mh) * kD)[lane] =
+                f2_t{a0 * 11.313708498984761f, a1 * 11.313708498984761f};
+        } else {
+            wave_fwht(a0, a1, lane);
+            const f2_t sv = reinterpret_cast<const f2_t *>(signs_v + g * kD)[lane];
+            reinterpret_cast<f2_t *>(out + ((b * Hq) + (int64_t)g * G + mh) * kD)[lane] = f2_t{a0 * sv.x, a1 * sv.y};
+        }
     }
     if (tid == 0)  // leave the counter ready for the next call
         __hip_atomic_store(counters + bh, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -862,7 +897,8 @@ hipError_t run_logits(const kvq_ctx *ctx, const void *q, int64_t B, int64_t Hq, 
     }
     hipLaunchKernelGGL((k_logits<BITS, G, QJL>), dim3((unsigned)(bhs * blocks_per_bh)), dim3(kLgThreads), shm,
                        s, (const half_t *)q, codes, norms, (const uint32_t *)qjl_signs, qjl_gamma,
-                       ctx->d_signs, ctx->d_S, ctx->cb, logits, T, ctx->H, (int)Hq, tpb, blocks_per_bh);
+                       ctx->d_signs, ctx->d_S, ctx->cb, logits, T, ctx->H, (int)Hq, tpb, blocks_per_bh,
+                       ctx->rotation == KVQ_ROTATION_DENSE ? ctx->d_Q : nullptr);
     return hipGetLastError();
 }
 
@@ -990,7 +1026,9 @@ hipError_t run_decode(const kvq_ctx *ctx, const void *q, int64_t B, int64_t Hq, 
     }
     hipLaunchKernelGGL((k_decode<BITS, G>), dim3((unsigned)(bhs * n_split)), dim3(kDecThreads), shm, s,
                        (const half_t *)q, kc, kn, vc, vn, ctx->d_signs, ctx->d_signs + ctx->H * kD, ctx->cb,
-                       scale_log2, out, part, counters, T, ldt, ctx->H, (int)Hq, n_split, n_part, chunk);
+                       scale_log2, out, part, counters, T, ldt, ctx->H, (int)Hq, n_split, n_part, chunk,
+                       ctx->rotation == KVQ_ROTATION_DENSE ? ctx->d_Q : nullptr,
+                       ctx->rotation == KVQ_ROTATION_DENSE ? ctx->d_Qt : nullptr);
     return hipGetLastError();
 }
 

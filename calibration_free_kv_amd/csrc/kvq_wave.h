@@ -86,5 +86,41 @@ __device__ __forceinline__ void wave_lds_sync()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// o0 = sum_j M[2 lane][j] v[j], o1 = sum_j M[2 lane + 1][j] v[j]: a 128 x 128
+// row-major fp32 matrix in global memory times a 128-vector in LDS (16-byte
+// aligned), eight row pieces of each row in flight at a time.
+__device__ __forceinline__ void gemv_rows2(const float *__restrict__ M, const float *v, int lane, float &o0,
+                                           float &o1)
+{
+    typedef float f4v __attribute__((ext_vector_type(4)));
+    const f4v *r0 = reinterpret_cast<const f4v *>(M + 256 * lane);
+    const f4v *r1 = r0 + 32;
+    const f4v *x = reinterpret_cast<const f4v *>(v);
+    float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+    for (int c0 = 0; c0 < 32; c0 += 8) {
+        f4v m0[8], m1[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            m0[u] = r0[c0 + u];
+            m1[u] = r1[c0 + u];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const f4v xv = x[c0 + u];
+            a0 = fmaf(m0[u].x, xv.x, a0);
+            a0 = fmaf(m0[u].y, xv.y, a0);
+            a0 = fmaf(m0[u].z, xv.z, a0);
+            a0 = fmaf(m0[u].w, xv.w, a0);
+            a1 = fmaf(m1[u].x, xv.x, a1);
+            a1 = fmaf(m1[u].y, xv.y, a1);
+            a1 = fmaf(m1[u].z, xv.z, a1);
+            a1 = fmaf(m1[u].w, xv.w, a1);
+        }
+    }
+    o0 = a0;
+    o1 = a1;
+}
+
 }  // namespace
 }  // namespace kvq

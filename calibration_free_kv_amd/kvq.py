@@ -20,6 +20,7 @@ KVQ_OK, KVQ_E_INVAL, KVQ_E_UNSUPPORTED, KVQ_E_DEVICE, KVQ_E_NOMEM, KVQ_E_WORKSPA
 KVQ_MODE_MSE, KVQ_MODE_MSE_QJL, KVQ_MODE_NSN_VQ = 0, 1, 2
 KVQ_KIND_K, KVQ_KIND_V = 0, 1
 KVQ_CODEBOOK_GAUSS, KVQ_CODEBOOK_BETA = 0, 1
+KVQ_ROTATION_HADAMARD, KVQ_ROTATION_DENSE = 0, 1
 D = 128
 
 EXPORTS = [
@@ -42,7 +43,8 @@ class kvq_config(C.Structure):
         ("d", C.c_int32), ("bits", C.c_int32), ("mode", C.c_int32), ("n_kv_heads", C.c_int32),
         ("seed", C.c_uint64), ("signs_k", C.POINTER(C.c_int8)), ("signs_v", C.POINTER(C.c_int8)),
         ("qjl_S", C.POINTER(C.c_float)), ("vq_codebook", C.POINTER(C.c_float)),
-        ("device", C.c_int32), ("codebook", C.c_int32),
+        ("device", C.c_int32), ("codebook", C.c_int32), ("rotation", C.c_int32),
+        ("rot_Q", C.POINTER(C.c_float)),
     ]
 
 
@@ -136,7 +138,8 @@ class Context:
     by the library from `seed` (SplitMix64, as kvq.h specifies)."""
 
     def __init__(self, n_kv_heads: int, bits: int = 3, signs_k=None, signs_v=None, mode: int = KVQ_MODE_MSE,
-                 qjl_S=None, vq_codebook=None, device: int = 0, seed: int = 0, codebook: int = KVQ_CODEBOOK_GAUSS):
+                 qjl_S=None, vq_codebook=None, device: int = 0, seed: int = 0, codebook: int = KVQ_CODEBOOK_GAUSS,
+                 rot_Q=None):
         self.n_kv_heads, self.bits, self.mode, self.device = n_kv_heads, bits, mode, device
         cfg = kvq_config()
         cfg.d, cfg.bits, cfg.mode, cfg.n_kv_heads, cfg.device = D, bits, mode, n_kv_heads, device
@@ -154,6 +157,8 @@ class Context:
         cfg.signs_v = arr(signs_v, np.int8, C.c_int8)
         cfg.qjl_S = arr(qjl_S, np.float32, C.c_float)
         cfg.vq_codebook = arr(vq_codebook, np.float32, C.c_float)
+        cfg.rotation = KVQ_ROTATION_DENSE if rot_Q is not None else KVQ_ROTATION_HADAMARD
+        cfg.rot_Q = arr(rot_Q, np.float32, C.c_float)
         h = C.c_void_p()
         _check(lib().kvq_create(C.byref(cfg), C.byref(h)), "kvq_create")
         self.handle = h

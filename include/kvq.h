@@ -73,6 +73,12 @@ enum { KVQ_KIND_K = 0, KVQ_KIND_V = 1 };
  * d = 128, Beta((d-1)/2, (d-1)/2) on [-1, 1] scaled by sqrt(d) ([TQ] Como
  * Funciona, Estagio 1). */
 enum { KVQ_CODEBOOK_GAUSS = 0, KVQ_CODEBOOK_BETA = 1 };
+/* Rotation of the MSE modes: the randomized Hadamard transform y = H (D .* u)
+ * ([PQ] sec. 2; [NSN] sec. 2), or a dense orthogonal Q given by the caller,
+ * y = sqrt(d) Q u ([TQ] Como Funciona, Estagio 1: QR of a Gaussian matrix),
+ * the same Q for K, V and every head (KVQ_MODE_MSE only; not with the
+ * streaming-cache calls). */
+enum { KVQ_ROTATION_HADAMARD = 0, KVQ_ROTATION_DENSE = 1 };
 
 /* Configuration of a context.  Host arrays are copied by kvq_create.
  *
@@ -100,6 +106,8 @@ typedef struct {
     const float *vq_codebook;  /* host [256, 8] fp32 codebook (NSN_VQ)                */
     int32_t device;            /* HIP device ordinal                                  */
     int32_t codebook;          /* KVQ_CODEBOOK_* (MSE modes; 0 = N(0,1))              */
+    int32_t rotation;          /* KVQ_ROTATION_* (0 = randomized Hadamard)            */
+    const float *rot_Q;        /* host [d, d] row-major orthogonal Q (ROTATION_DENSE)  */
 } kvq_config;
 
 /* Create a context: validates the configuration, builds the b-bit N(0,1)

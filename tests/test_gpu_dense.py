@@ -1,0 +1,169 @@
+"""GPU parity of the dense-rotation mode (a caller-given orthogonal Q in place
+of the randomized Hadamard transform) against the CPU oracle.
+
+The orthogonal matrices are seeded Haar draws (QR of a Gaussian matrix),
+rounded to fp32 once; the library and the oracle receive the same fp32
+entries.  Quantisation: exact indices except coordinates within 1e-5 of a
+threshold (the oracle's flags), norms to 1e-5.  Scoring reads the oracle's
+codes: logits within 1e-5 ||q|| ||k||, attention outputs within 2e-3."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from calibration_free_kv_amd import kvq, synth
+from tests.gpu_util import needs_gpu, to_np, unpack_np
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+
+
+def rot(seed):
+    return synth.random_orthogonal(seed).astype(np.float32)
+
+
+def check_dense_codes(x, Q, bits, codes, norms, codebook="gauss"):
+    ref = O.quantize_dense(x, Q.astype(np.float64), bits, codebook=codebook)
+    gi = unpack_np(to_np(codes), bits)
+    bad = (gi != ref["idx"]) & (ref["flags"] == 0)
+    assert not bad.any(), int(bad.sum())
+    np.testing.assert_allclose(to_np(norms), ref["norms"], rtol=1e-5, atol=1e-30)
+    return int(((gi != ref["idx"])).sum()), int(ref["flags"].sum())
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_quantize_dense_ragged(bits):
+    """2 x 8 x 777 vectors: 194 full groups of 64 and a ragged one."""
+    inp = synth.make("l8b32k", T=777, B=2)
+    Q = rot(30 + bits)
+    ctx = kvq.Context(8, bits, rot_Q=Q)
+    x = inp["k"].copy()
+    x[1, 5, 776] = 0  # a zero vector: every coordinate at 0
+    r = ctx.quantize(kvq.KVQ_KIND_K, torch.from_numpy(x).cuda())
+    print("bits=%d (mismatches, flagged) = %s" % (bits, check_dense_codes(x, Q, bits, r["codes"], r["norms"])))
+    assert to_np(r["norms"])[1, 5, 776] == 0
+
+
+@pytest.mark.parametrize("T", [1, 63, 1000])
+def test_quantize_kv_dense_and_beta_codebook(T):
+    inp = synth.make("l8b32k", T=T)
+    Q = rot(40)
+    for cb, name in ((kvq.KVQ_CODEBOOK_GAUSS, "gauss"), (kvq.KVQ_CODEBOOK_BETA, "beta")):
+        ctx = kvq.Context(8, 3, rot_Q=Q, codebook=cb)
+        ko, vo = ctx.quantize_kv(torch.from_numpy(inp["k"]).cuda(), torch.from_numpy(inp["v"]).cuda())
+        check_dense_codes(inp["k"], Q, 3, ko["codes"], ko["norms"], codebook=name)
+        check_dense_codes(inp["v"], Q, 3, vo["codes"], vo["norms"], codebook=name)
+
+
+def test_quantize_dense_full_size_sampled():
+    """The full l8b32k cache (8 x 32768 keys): 4096 sampled vectors checked."""
+    inp = synth.make("l8b32k")
+    Q = rot(41)
+    ctx = kvq.Context(8, 3, rot_Q=Q)
+    r = ctx.quantize(kvq.KVQ_KIND_K, torch.from_numpy(inp["k"]).cuda())
+    t = np.sort(np.random.default_rng(42).choice(inp["k"].shape[2], 512, replace=False))
+    check_dense_codes(inp["k"][:, :, t], Q, 3, r["codes"][:, :, torch.from_numpy(t).cuda()],
+                      r["norms"][:, :, torch.from_numpy(t).cuda()])
+
+
+def oracle_dense_codes(x, Q, bits):
+    r = O.quantize_dense(x, Q.astype(np.float64), bits)
+    return r["codes"], r["norms"].astype(np.float32)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_logits_dense(bits):
+    inp = synth.make("l8b32k", T=777, B=2)
+    Q = rot(50)
+    kc, kn = oracle_dense_codes(inp["k"], Q, bits)
+    ctx = kvq.Context(8, bits, rot_Q=Q)
+    lg = to_np(ctx.logits(torch.from_numpy(inp["q"]).cuda(), torch.from_numpy(kc).cuda(),
+                          torch.from_numpy(kn).cuda()))
+    ref = O.logits_dense(inp["q"], kc, kn.astype(np.float64), Q.astype(np.float64), bits)
+    scale = np.linalg.norm(inp["q"].astype(np.float64), axis=-1)[..., None] * np.repeat(kn.astype(np.float64), 4,
+                                                                                       axis=1)
+    err = np.abs(lg - ref) / np.maximum(scale, 1e-30)
+    print("bits=%d max rel err %.3g" % (bits, err.max()))
+    assert err.max() <= 1e-5
+
+
+def decode_case(bits, T, B=1, Hkv=8, Hq=32, seed=60, n_split=0):
+    inp = synth.make("l8b32k", T=T, B=B)
+    Q = rot(seed)
+    k, v = inp["k"][:, :Hkv], inp["v"][:, :Hkv]
+    q = inp["q"][:, :Hq]
+    kc, kn = oracle_dense_codes(k, Q, bits)
+    vc, vn = oracle_dense_codes(v, Q, bits)
+    ctx = kvq.Context(Hkv, bits, rot_Q=Q)
+    g = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    out = to_np(ctx.attn_decode(g(q), g(kc), g(kn), g(vc), g(vn), n_split=n_split))
+    ref = O.attention_dense(q, kc, kn.astype(np.float64), vc, vn.astype(np.float64), Q.astype(np.float64), bits)
+    return np.abs(out - ref).max()
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("T", [1, 50, 3001])
+def test_decode_dense(bits, T):
+    err = decode_case(bits, T)
+    print("bits=%d T=%d max abs err %.3g" % (bits, T, err))
+    assert err <= 2e-3
+
+
+@pytest.mark.parametrize("G", [1, 2])
+def test_decode_dense_groups_batch_splits(G):
+    for n_split in (0, 1, 5):
+        assert decode_case(3, 2000, B=2, Hkv=4, Hq=4 * G, seed=61, n_split=n_split) <= 2e-3
+
+
+def test_decode_dense_full_size():
+    """8 KV heads x 32768 tokens, 32 query heads, every output checked."""
+    err = decode_case(3, None, seed=62)
+    print("full size max abs err %.3g" % err)
+    assert err <= 2e-3
+
+
+def test_hadamard_matrix_as_dense_rotation_matches_hadamard_path():
+    """Q = H diag(D) / sqrt(d) makes the dense mode the Hadamard mode: the
+    same codes (away from thresholds) and the same logits and outputs."""
+    inp = synth.make("l8b32k", T=1500)
+    Hm = O.hadamard_matrix(128).astype(np.float64)
+    out = {}
+    for dense in (False, True):
+        # one Q serves all heads, so use the same signs for every head and both kinds
+        s = np.repeat(inp["signs_k"][:1], 8, axis=0)
+        Q = (Hm * s[0][None, :].astype(np.float64) / np.sqrt(128)).astype(np.float32)
+        ctx = kvq.Context(8, 3, s, s, rot_Q=Q if dense else None)
+        ko, vo = ctx.quantize_kv(torch.from_numpy(inp["k"]).cuda(), torch.from_numpy(inp["v"]).cuda())
+        q = torch.from_numpy(inp["q"]).cuda()
+        out[dense] = dict(k=unpack_np(to_np(ko["codes"]), 3), kn=to_np(ko["norms"]),
+                          lg=to_np(ctx.logits(q, ko["codes"], ko["norms"])),
+                          o=to_np(ctx.attn_decode(q, ko["codes"], ko["norms"], vo["codes"], vo["norms"])))
+    a, b = out[False], out[True]
+    assert np.mean(a["k"] != b["k"]) < 1e-4
+    np.testing.assert_allclose(b["kn"], a["kn"], rtol=1e-6)
+    same = np.all(a["k"] == b["k"], axis=-1)  # keys whose codes agree
+    scale = np.linalg.norm(inp["q"].astype(np.float64), axis=-1)[..., None] * np.repeat(a["kn"], 4, axis=1)
+    diff = np.abs(a["lg"] - b["lg"]) / scale
+    assert diff[np.repeat(same, 4, axis=1)].max() <= 1e-5
+
+
+def test_dense_validation():
+    Q = rot(70)
+    with pytest.raises(kvq.KvqError) as e:  # dense rotation needs the MSE mode
+        kvq.Context(2, 3, mode=kvq.KVQ_MODE_MSE_QJL, qjl_S=np.eye(128, dtype=np.float32), rot_Q=Q)
+    assert e.value.status == kvq.KVQ_E_UNSUPPORTED
+    bad = Q.copy()
+    bad[3, 4] = np.nan
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.Context(2, 3, rot_Q=bad)
+    assert e.value.status == kvq.KVQ_E_INVAL
+    ctx = kvq.Context(2, 3, rot_Q=Q)
+    kc = torch.zeros((1, 2, 64, 48), dtype=torch.uint8, device="cuda")
+    kn = torch.ones((1, 2, 64), dtype=torch.float32, device="cuda")
+    kt = torch.zeros((1, 2, 16, 128), dtype=torch.float16, device="cuda")
+    q = torch.zeros((1, 8, 128), dtype=torch.float16, device="cuda")
+    with pytest.raises(kvq.KvqError) as e:  # the streaming cache is Hadamard-only
+        ctx.attn_decode_stream(q, kc, kn, kc, kn, 10, kt, kt, 4)
+    assert e.value.status == kvq.KVQ_E_UNSUPPORTED
+    with pytest.raises(kvq.KvqError) as e:
+        ctx.flush(kt, kt, 4, kc, kn, kc, kn, 0)
+    assert e.value.status == kvq.KVQ_E_UNSUPPORTED
