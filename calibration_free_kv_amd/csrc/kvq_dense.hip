@@ -15,7 +15,11 @@
 // rows one read touches fall in distinct banks).  The norm comes from the A
 // registers; the scaled outputs are bucketed with the antisymmetric binary
 // search over the positive thresholds, staged in LDS as bytes, and packed
-// with lane = vector.
+// with lane = vector.  A lane's D registers hold, for one vector, the outputs
+// m, m + 16, ..., m + 112: the stage keeps a row in that order (byte 8 m + j
+// holds output 16 j + m), so that they leave as one 8-byte write, and the
+// packing loop, whose positions are all compile-time, reads them back in the
+// same order.  Eight waves share one copy of Q (two per SIMD).
 #include "kvq_internal.h"
 #include "kvq_wave.h"
 
@@ -26,7 +30,7 @@ typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kDenseWaves = 4;
+constexpr int kDenseWaves = 8;
 constexpr int kQRow = kD + 8;   // padded row of Q in LDS, in halves
 constexpr int kSRow = kD + 16;  // padded row of the index stage, in bytes (36 dwords: a 16-lane
                                 // read of 16-byte pieces of 16 rows touches 64 distinct banks)
@@ -95,8 +99,12 @@ __global__ __launch_bounds__(64 * kDenseWaves) void k_quantize_dense(
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 A[sg][ks] = *reinterpret_cast<const h8_t *>(src + 32 * ks + 8 * kg);
-#pragma unroll
-                for (int j = 0; j < 8; ++j) s = fmaf((float)A[sg][ks][j], (float)A[sg][ks][j], s);
+                // squares of fp16 values are exact in fp32; pairs summed by the packed dot product
+                const h8_t a = A[sg][ks];
+                s = __builtin_amdgcn_fdot2(__builtin_shufflevector(a, a, 0, 1), __builtin_shufflevector(a, a, 0, 1), s, false);
+                s = __builtin_amdgcn_fdot2(__builtin_shufflevector(a, a, 2, 3), __builtin_shufflevector(a, a, 2, 3), s, false);
+                s = __builtin_amdgcn_fdot2(__builtin_shufflevector(a, a, 4, 5), __builtin_shufflevector(a, a, 4, 5), s, false);
+                s = __builtin_amdgcn_fdot2(__builtin_shufflevector(a, a, 6, 7), __builtin_shufflevector(a, a, 6, 7), s, false);
             }
             ss[sg] = s;
         }
@@ -135,17 +143,19 @@ __global__ __launch_bounds__(64 * kDenseWaves) void k_quantize_dense(
             }
         }
         wave_lds_sync();  // the scales are in LDS
-        // D[sg][nb][r]: vector 16 sg + 4 kg + r, output 16 nb + m16
+        // D[sg][nb][r]: vector 16 sg + 4 kg + r, output 16 nb + m16 -> stage byte 8 m16 + nb
 #pragma unroll
         for (int sg = 0; sg < 4; ++sg) {
             const f4_t s4 = *reinterpret_cast<const f4_t *>(&scl[wv][16 * sg + 4 * kg]);
 #pragma unroll
-            for (int nb = 0; nb < 8; ++nb) {
+            for (int r = 0; r < 4; ++r) {
+                uint32_t w0 = 0u, w1 = 0u;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const uint32_t ix = bucket_idx<BITS>(D[sg][nb][r] * s4[r], P);
-                    stage[wv][(16 * sg + 4 * kg + r) * kSRow + 16 * nb + m16] = (uint8_t)ix;
+                for (int nb = 0; nb < 4; ++nb) {
+                    w0 |= bucket_idx<BITS>(D[sg][nb][r] * s4[r], P) << (8 * nb);
+                    w1 |= bucket_idx<BITS>(D[sg][nb + 4][r] * s4[r], P) << (8 * nb);
                 }
+                *reinterpret_cast<uint2 *>(&stage[wv][(16 * sg + 4 * kg + r) * kSRow + 8 * m16]) = uint2{w0, w1};
             }
         }
         wave_lds_sync();
@@ -161,7 +171,8 @@ __global__ __launch_bounds__(64 * kDenseWaves) void k_quantize_dense(
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     const uint32_t ix = (b16[e >> 2] >> (8 * (e & 3))) & 0xFFu;
-                    const int i = 16 * c + e, p = BITS * i, w = p >> 5, sh = p & 31;
+                    const int pos = 16 * c + e, i = 16 * (pos & 7) + (pos >> 3);  // output index
+                    const int p = BITS * i, w = p >> 5, sh = p & 31;
                     W[w] |= ix << sh;
                     if (sh + BITS > 32) W[w + 1] |= ix >> (32 - sh);
                 }
@@ -187,7 +198,7 @@ hipError_t dense_b(const kvq_ctx *ctx, const void *xk, const void *xv, int64_t N
     const int64_t total = xv ? 2 * N : N;
     const int64_t n_groups = (total + 63) / 64;
     int64_t blocks = (n_groups + kDenseWaves - 1) / kDenseWaves;
-    const int64_t cap = 2 * (int64_t)ctx->n_cu;
+    const int64_t cap = ctx->n_cu;  // one block fits a CU's LDS: persistent blocks
     if (blocks > cap) blocks = cap;
     // with no V list the index space ends at N
     hipLaunchKernelGGL(k_quantize_dense<BITS>, dim3((unsigned)blocks), dim3(64 * kDenseWaves), 0, s,

@@ -54,31 +54,32 @@ __device__ __forceinline__ uint32_t field(const uint32_t *Wd, int f)
 
 // Prologue shared by the score kernels: qr[G][128] <- H (D .* q_h) for the G
 // query heads of KV head g of batch b, one wave per head; with a dense
-// rotation Q (not null) instead qr <- sqrt(d) Q q_h.  Ends with a barrier.
-template <int G>
+// rotation Q (not null) instead qr <- sqrt(d) Q q_h by the whole block of NT
+// threads, with (NT / 128) G 128 floats of LDS at `scratch`.  Ends with a
+// barrier.
+template <int G, int NT>
 __device__ void rotate_queries(const half_t *__restrict__ q, const float *__restrict__ signs,
-                               int64_t b, int g, int Hq, float *qr, const float *__restrict__ Qm)
+                               int64_t b, int g, int Hq, float *qr, const float *__restrict__ Qm, float *scratch)
 {
-    const int lane = threadIdx.x & 63;
-    const int wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    for (int h = wv; h < G; h += nw) {
-        const uint32_t pr =
-            reinterpret_cast<const uint32_t *>(q + ((int64_t)b * Hq + (int64_t)g * G + h) * kD)[lane];
+    const int tid = threadIdx.x;
+    const half_t *qb = q + ((int64_t)b * Hq + (int64_t)g * G) * kD;
+    if (Qm) {  // uniform
+        for (int i = tid; i < G * kD; i += NT) qr[i] = (float)qb[i];
+        __syncthreads();
+        const float y = block_gemv<G, NT>(Qm, qr, scratch, tid);  // every read of qr precedes its barrier
+        if (tid < G * kD) qr[tid] = y * 11.313708498984761f;
+        __syncthreads();
+        return;
+    }
+    const int lane = tid & 63, wv = tid >> 6;
+    for (int h = wv; h < G; h += NT / 64) {
+        const uint32_t pr = reinterpret_cast<const uint32_t *>(qb + h * kD)[lane];
         float x0 = (float)__builtin_bit_cast(h2_t, pr).x;
         float x1 = (float)__builtin_bit_cast(h2_t, pr).y;
-        if (Qm) {
-            reinterpret_cast<f2_t *>(qr + h * kD)[lane] = f2_t{x0, x1};
-            wave_lds_sync();
-            gemv_rows2(Qm, qr + h * kD, lane, x0, x1);
-            wave_lds_sync();
-            x0 *= 11.313708498984761f;
-            x1 *= 11.313708498984761f;
-        } else {
-            const f2_t sg = reinterpret_cast<const f2_t *>(signs + g * kD)[lane];
-            x0 *= sg.x;
-            x1 *= sg.y;
-            wave_fwht(x0, x1, lane);
-        }
+        const f2_t sg = reinterpret_cast<const f2_t *>(signs + g * kD)[lane];
+        x0 *= sg.x;
+        x1 *= sg.y;
+        wave_fwht(x0, x1, lane);
         reinterpret_cast<f2_t *>(qr + h * kD)[lane] = f2_t{x0, x1};
     }
     __syncthreads();
@@ -194,7 +195,9 @@ __global__ __launch_bounds__(kLgThreads) void k_logits(
     extern __shared__ __align__(16) float smem[];
     float *qr = smem;                       // [G][128]
     float *lut = qr + G * kD;               // [NF][E][G]
-    float *slut = lut + FD::NF * FD::E * G; // [32][16][G] (QJL)
+    // the tables' area also holds the dense rotation's partial sums
+    constexpr int LA = FD::NF * FD::E > kLgThreads ? FD::NF * FD::E : kLgThreads;
+    float *slut = lut + LA * G;             // [32][16][G] (QJL)
     float *pq = slut + (QJL ? 32 * 16 * G : 0);  // [G][128] (QJL)
     float *ctab = pq + (QJL ? G * kD : 0);       // [16] centroids
 
@@ -204,7 +207,7 @@ __global__ __launch_bounds__(kLgThreads) void k_logits(
     const int g = (int)(bh - b * H);
 
     stage_centroids(cb, ctab);
-    rotate_queries<G>(q, signs, b, g, Hq, qr, Qm);
+    rotate_queries<G, kLgThreads>(q, signs, b, g, Hq, qr, Qm, lut);
     build_tables<BITS, G>(qr, ctab, lut);
     if constexpr (QJL) {
         // p_h[j] = sum_i S[j][i] q'_h[i] / sqrt(d): thread (h, j) walks row i of
@@ -347,6 +350,8 @@ struct DecSmem {
     // end-of-block reuse of the staging area: per-wave accumulators, split merge
     static_assert(kDecWaves * STG >= kDecWaves * G * kD, "wave merge buffer does not fit");
     static_assert(kDecWaves * STG >= kDecWaves * (kMaxSplits + kD), "split merge buffers do not fit");
+    static_assert(kDecWaves * STG >= kDecWaves * kMaxSplits + (1 + kDecThreads / kD) * G * kD,
+                  "dense output rotation buffers do not fit");
 };
 
 // o[r] = x of lane 16 r + (l & 15), for r = 0..3: row r broadcast to every row.
@@ -443,11 +448,11 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
     const uint8_t *__restrict__ vc, const float *__restrict__ vn, const float *__restrict__ signs_k,
     const float *__restrict__ signs_v, Codebook cb, float scale_log2, float *__restrict__ out,
     float *__restrict__ part, unsigned *__restrict__ counters, int64_t T, int64_t ldt, int H, int Hq,
-    int n_split, int n_part, int64_t chunk, const float *__restrict__ Qm, const float *__restrict__ Qtm)
+    int n_split, int n_part, int64_t chunk, const float *__restrict__ qrot, const float *__restrict__ Qtm)
 {
-    // Qm, Qtm (dense rotation and its transpose, or null): the query is
-    // rotated as sqrt(d) Q q and the output as sqrt(d) Q^T acc instead of
-    // with the randomized Hadamard transform.
+    // qrot, Qtm (dense rotation, or null): the rotated queries sqrt(d) Q q,
+    // [B Hq][128] fp32 computed beforehand, and Q^T; the output is rotated
+    // back as sqrt(d) Q^T acc instead of with the randomized Hadamard transform.
     // T valid tokens of each (b, g) in arrays of ldt tokens per (b, g); the
     // partials of (b, g) occupy n_part slots (n_split blocks, plus one slot
     // written beforehand by the residual-window kernel when n_part > n_split)
@@ -582,14 +587,10 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
         // The logit factor undoes the scale.
         float x0 = (float)__builtin_bit_cast(h2_t, qv).x;
         float x1 = (float)__builtin_bit_cast(h2_t, qv).y;
-        if (Qm) {  // this wave's staging area holds q while it is rotated
-            float *qtmp = reinterpret_cast<float *>(stg);
-            reinterpret_cast<f2_t *>(qtmp)[lane] = f2_t{x0, x1};
-            wave_lds_sync();
-            gemv_rows2(Qm, qtmp, lane, x0, x1);
-            wave_lds_sync();
-            x0 *= 11.313708498984761f;
-            x1 *= 11.313708498984761f;
+        if (qrot) {
+            const f2_t r = reinterpret_cast<const f2_t *>(qrot + ((int64_t)b * Hq + (int64_t)g * G + wv) * kD)[lane];
+            x0 = r.x;
+            x1 = r.y;
         } else {
             x0 *= qs.x;
             x1 *= qs.y;
@@ -857,17 +858,18 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
             a0 += v.x;
             a1 += v.y;
         }
-        if (Qtm) {  // out = sqrt(d) Q^T acc, with acc in this wave's partial-sum slot
+        if (Qtm) {  // acc of head mh into slot mh (wave mh = this wave), rotated below
             reinterpret_cast<f2_t *>(pacc + wv * kD)[lane] = f2_t{a0, a1};
-            wave_lds_sync();
-            gemv_rows2(Qtm, pacc + wv * kD, lane, a0, a1);
-            reinterpret_cast<f2_t *>(out + ((b * Hq) + (int64_t)g * G + mh) * kD)[lane] =
-                f2_t{a0 * 11.313708498984761f, a1 * 11.313708498984761f};
         } else {
             wave_fwht(a0, a1, lane);
             const f2_t sv = reinterpret_cast<const f2_t *>(signs_v + g * kD)[lane];
             reinterpret_cast<f2_t *>(out + ((b * Hq) + (int64_t)g * G + mh) * kD)[lane] = f2_t{a0 * sv.x, a1 * sv.y};
         }
+    }
+    if (Qtm) {  // out = sqrt(d) Q^T acc for the G heads, by the whole block
+        __syncthreads();
+        const float y = block_gemv<G, kDecThreads>(Qtm, pacc, pacc + G * kD, tid);
+        if (tid < G * kD) out[((b * Hq) + (int64_t)g * G + (tid >> 7)) * kD + (tid & 127)] = y * 11.313708498984761f;
     }
     if (tid == 0)  // leave the counter ready for the next call
         __hip_atomic_store(counters + bh, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -888,7 +890,8 @@ hipError_t run_logits(const kvq_ctx *ctx, const void *q, int64_t B, int64_t Hq, 
     if (per < 1) per = 1;
     const int64_t tpb = (T + per - 1) / per;
     const int64_t blocks_per_bh = (T + tpb - 1) / tpb;
-    const size_t shm = sizeof(float) * (G * kD + FD::NF * FD::E * G + (QJL ? 32 * 16 * G + G * kD : 0) + 16);
+    constexpr int LA = FD::NF * FD::E > kLgThreads ? FD::NF * FD::E : kLgThreads;  // tables or rotation sums
+    const size_t shm = sizeof(float) * (G * kD + LA * G + (QJL ? 32 * 16 * G + G * kD : 0) + 16);
     static bool attr_set = false;
     if (!attr_set) {
         (void)hipFuncSetAttribute((const void *)k_logits<BITS, G, QJL>,
@@ -994,6 +997,29 @@ __global__ __launch_bounds__(64 * G) void k_tail(const half_t *__restrict__ q, c
     }
 }
 
+constexpr int kRotWaves = 8, kRotHeads = 4;
+
+// Rotated queries of the dense rotation, sqrt(d) Q q for each of `heads`
+// fp16 query vectors, kRotHeads per block (Q read once per block, every
+// thread's share of it in flight at once).
+__global__ __launch_bounds__(64 * kRotWaves) void k_rotate_dense(const half_t *__restrict__ q,
+                                                                 const float *__restrict__ Qm,
+                                                                 float *__restrict__ qrot, int64_t heads)
+{
+    __shared__ __align__(16) float qv[kRotHeads][kD];
+    __shared__ __align__(16) float part[64 * kRotWaves / kD][kRotHeads][kD];
+    const int tid = threadIdx.x;
+    const int64_t h0 = (int64_t)blockIdx.x * kRotHeads;
+    for (int i = tid; i < kRotHeads * kD; i += 64 * kRotWaves) {
+        const int64_t h = h0 + i / kD;
+        qv[i / kD][i % kD] = h < heads ? (float)q[h * kD + i % kD] : 0.0f;
+    }
+    __syncthreads();
+    const float y = block_gemv<kRotHeads, 64 * kRotWaves>(Qm, &qv[0][0], &part[0][0][0], tid);
+    const int64_t h = h0 + tid / kD;
+    if (tid < kRotHeads * kD && h < heads) qrot[h * kD + tid % kD] = y * 11.313708498984761f;
+}
+
 template <int BITS, int G>
 hipError_t run_decode(const kvq_ctx *ctx, const void *q, int64_t B, int64_t Hq, int64_t T, int64_t ldt,
                       const uint8_t *kc, const float *kn, const uint8_t *vc, const float *vn, const DecodeTail *tail,
@@ -1024,11 +1050,18 @@ hipError_t run_decode(const kvq_ctx *ctx, const void *q, int64_t B, int64_t Hq, 
                                   (int)shm);
         attr_set = true;
     }
+    const bool dense = ctx->rotation == KVQ_ROTATION_DENSE;
+    float *qrot = nullptr;
+    if (dense) {  // after the partials (sized for the most splits T allows)
+        qrot = part + (size_t)(B * Hq) * (size_t)decode_max_splits(T) * (kD + 2);
+        const int64_t heads = B * Hq;
+        hipLaunchKernelGGL(k_rotate_dense, dim3((unsigned)((heads + kRotHeads - 1) / kRotHeads)),
+                           dim3(64 * kRotWaves), 0, s, (const half_t *)q, ctx->d_Q, qrot, heads);
+    }
     hipLaunchKernelGGL((k_decode<BITS, G>), dim3((unsigned)(bhs * n_split)), dim3(kDecThreads), shm, s,
                        (const half_t *)q, kc, kn, vc, vn, ctx->d_signs, ctx->d_signs + ctx->H * kD, ctx->cb,
-                       scale_log2, out, part, counters, T, ldt, ctx->H, (int)Hq, n_split, n_part, chunk,
-                       ctx->rotation == KVQ_ROTATION_DENSE ? ctx->d_Q : nullptr,
-                       ctx->rotation == KVQ_ROTATION_DENSE ? ctx->d_Qt : nullptr);
+                       scale_log2, out, part, counters, T, ldt, ctx->H, (int)Hq, n_split, n_part, chunk, qrot,
+                       dense ? ctx->d_Qt : nullptr);
     return hipGetLastError();
 }
 
@@ -1085,8 +1118,9 @@ size_t decode_ws_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t T)
 {
     const int64_t bhs = B * Hkv;
     const int64_t max_split = decode_max_splits(T);
+    // counters, partials, then the rotated queries of the dense rotation
     return ((bhs * sizeof(unsigned) + 255) / 256) * 256 +
-           (size_t)(B * Hq) * (size_t)max_split * (kD + 2) * sizeof(float);
+           (size_t)(B * Hq) * (size_t)max_split * (kD + 2) * sizeof(float) + (size_t)(B * Hq) * kD * sizeof(float);
 }
 
 int decode_auto_splits(int64_t B, int64_t Hkv, int64_t T)

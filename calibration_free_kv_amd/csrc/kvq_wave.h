@@ -86,40 +86,46 @@ __device__ __forceinline__ void wave_lds_sync()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// o0 = sum_j M[2 lane][j] v[j], o1 = sum_j M[2 lane + 1][j] v[j]: a 128 x 128
-// row-major fp32 matrix in global memory times a 128-vector in LDS (16-byte
-// aligned), eight row pieces of each row in flight at a time.
-__device__ __forceinline__ void gemv_rows2(const float *__restrict__ M, const float *v, int lane, float &o0,
-                                           float &o1)
+// y[h][r] = sum_c M[r][c] x[h][c] for NH vectors x (LDS, [NH][128]) and a
+// 128 x 128 row-major fp32 matrix M in global memory, by all NT threads of
+// the block: thread t takes row t % 128 and the 128 / (NT / 128) columns of
+// slice t / 128, all of its part of M in flight at once (the block reads M
+// once); partial sums go to part[NT / 128][NH][128] in LDS.  Every thread
+// of the block must call it; it returns y[t / 128][t % 128] to threads
+// t < 128 NH.  `part` may be reused after a further barrier.
+template <int NH, int NT>
+__device__ __forceinline__ float block_gemv(const float *__restrict__ M, const float *x, float *part, int tid)
 {
     typedef float f4v __attribute__((ext_vector_type(4)));
-    const f4v *r0 = reinterpret_cast<const f4v *>(M + 256 * lane);
-    const f4v *r1 = r0 + 32;
-    const f4v *x = reinterpret_cast<const f4v *>(v);
-    float a0 = 0.0f, a1 = 0.0f;
+    constexpr int P = NT / 128, CW = 128 / P;
+    static_assert(NT % 128 == 0 && CW % 4 == 0, "whole rows and f4 pieces");
+    const int r = tid & 127, sl = tid >> 7;
+    const f4v *m = reinterpret_cast<const f4v *>(M + r * 128 + sl * CW);
+    f4v mv[CW / 4];
 #pragma unroll
-    for (int c0 = 0; c0 < 32; c0 += 8) {
-        f4v m0[8], m1[8];
+    for (int u = 0; u < CW / 4; ++u) mv[u] = m[u];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            m0[u] = r0[c0 + u];
-            m1[u] = r1[c0 + u];
+    for (int h = 0; h < NH; ++h) {
+        const f4v *xv = reinterpret_cast<const f4v *>(x + h * 128 + sl * CW);
+        float a = 0.0f;
+#pragma unroll
+        for (int u = 0; u < CW / 4; ++u) {
+            const f4v xx = xv[u];
+            a = fmaf(mv[u].x, xx.x, a);
+            a = fmaf(mv[u].y, xx.y, a);
+            a = fmaf(mv[u].z, xx.z, a);
+            a = fmaf(mv[u].w, xx.w, a);
         }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const f4v xv = x[c0 + u];
-            a0 = fmaf(m0[u].x, xv.x, a0);
-            a0 = fmaf(m0[u].y, xv.y, a0);
-            a0 = fmaf(m0[u].z, xv.z, a0);
-            a0 = fmaf(m0[u].w, xv.w, a0);
-            a1 = fmaf(m1[u].x, xv.x, a1);
-            a1 = fmaf(m1[u].y, xv.y, a1);
-            a1 = fmaf(m1[u].z, xv.z, a1);
-            a1 = fmaf(m1[u].w, xv.w, a1);
-        }
+        part[(sl * NH + h) * 128 + r] = a;
     }
-    o0 = a0;
-    o1 = a1;
+    __syncthreads();
+    float y = 0.0f;
+    if (tid < NH * 128) {
+        const int h = tid >> 7;
+#pragma unroll
+        for (int k = 0; k < P; ++k) y += part[(k * NH + h) * 128 + r];
+    }
+    return y;
 }
 
 }  // namespace
