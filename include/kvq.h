@@ -110,13 +110,16 @@ typedef struct {
     const float *rot_Q;        /* host [d, d] row-major orthogonal Q (ROTATION_DENSE)  */
 } kvq_config;
 
-/* Create a context: validates the configuration, builds the b-bit N(0,1)
- * Lloyd-Max tables ([PQ] sec. 2, [TQ] Como Implementar: codebooks
- * precomputed per bit width) and uploads them with D, S and the codebook to
- * the device.  *out receives the context (NULL on failure).
+/* Create a context: validates the configuration, builds the b-bit Lloyd-Max
+ * tables ([PQ] sec. 2, [TQ] Como Implementar: codebooks precomputed per bit
+ * width; N(0,1) or the exact-d law) and uploads them with D, S, the VQ
+ * codebook and the dense rotation Q (with its transpose and fp16 high/low
+ * parts) to the device.  *out receives the context (NULL on failure).
  * Errors: KVQ_E_INVAL (NULL pointers, d != 128, bits outside 1..4, a sign
- * entry not +-1, missing table for the mode), KVQ_E_DEVICE (no such device),
- * KVQ_E_NOMEM. */
+ * entry not +-1, missing table for the mode, unknown codebook or rotation,
+ * rot_Q NULL or with an entry not finite or above 1 in magnitude),
+ * KVQ_E_UNSUPPORTED (dense rotation outside KVQ_MODE_MSE), KVQ_E_DEVICE (no
+ * such device), KVQ_E_NOMEM. */
 kvq_status kvq_create(const kvq_config *cfg, kvq_ctx **out);
 
 /* Release a context and its device tables.  NULL is accepted (no-op).
@@ -253,7 +256,8 @@ size_t kvq_attn_decode_stream_ws_bytes(const kvq_ctx *ctx, int64_t B, int64_t H_
  *   ws   at least kvq_attn_decode_stream_ws_bytes() bytes, 256-byte aligned,
  *        its counter words zero before the first call (every completed call
  *        leaves them zero); calls sharing it must be ordered on one stream.
- * Errors: KVQ_E_WORKSPACE if ws_bytes is too small. */
+ * Errors: KVQ_E_WORKSPACE if ws_bytes is too small; KVQ_E_UNSUPPORTED for a
+ * context with the dense rotation. */
 kvq_status kvq_attn_decode_stream(kvq_ctx *ctx, const void *q_f16, int64_t B, int64_t H_q, int64_t T,
                                   int64_t T_cap, const uint8_t *k_codes, const float *k_norms,
                                   const uint8_t *v_codes, const float *v_norms, int64_t R, int64_t R_cap,
@@ -264,7 +268,8 @@ kvq_status kvq_attn_decode_stream(kvq_ctx *ctx, const void *q_f16, int64_t B, in
  * (batch, KV head) are quantised exactly as kvq_quantize quantises a vector
  * and written to positions T0 .. T0 + R - 1 of the packed arrays (layouts as
  * above, H_kv = the context's n_kv_heads; MSE mode).  Other positions are not
- * touched.  Requires T0 + R <= T_cap.  R == 0 or B == 0 is a no-op. */
+ * touched.  Requires T0 + R <= T_cap.  R == 0 or B == 0 is a no-op.
+ * Errors: KVQ_E_INVAL (sizes), KVQ_E_UNSUPPORTED (dense rotation). */
 kvq_status kvq_flush(kvq_ctx *ctx, const void *k_tail_f16, const void *v_tail_f16, int64_t B, int64_t H_kv,
                      int64_t R, int64_t R_cap, uint8_t *k_codes, float *k_norms, uint8_t *v_codes,
                      float *v_norms, int64_t T0, int64_t T_cap, void *stream);
