@@ -64,9 +64,11 @@ __device__ void rotate_queries(const half_t *__restrict__ q, const float *__rest
     const int tid = threadIdx.x;
     const half_t *qb = q + ((int64_t)b * Hq + (int64_t)g * G) * kD;
     if (Qm) {  // uniform
+        GemvSlice<NT> qs;
+        gemv_load<NT>(Qm, tid, qs);  // in flight while q is staged
         for (int i = tid; i < G * kD; i += NT) qr[i] = (float)qb[i];
         __syncthreads();
-        const float y = block_gemv<G, NT>(Qm, qr, scratch, tid);  // every read of qr precedes its barrier
+        const float y = block_gemv<G, NT>(qs, qr, scratch, tid);  // every read of qr precedes its barrier
         if (tid < G * kD) qr[tid] = y * 11.313708498984761f;
         __syncthreads();
         return;
@@ -789,6 +791,8 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
     }
     __syncthreads();
     if (!last) return;
+    GemvSlice<kDecThreads> qts;  // dense rotation: Q^T's slices in flight during the merge
+    if (Qtm) gemv_load<kDecThreads>(Qtm, tid, qts);
 
     // Merge of the splits: f_s = 2^(m_s - M) / (d L) with M = max_s m_s,
     // L = sum_s l_s 2^(m_s - M), acc = sum_s f_s acc_s, then the inverse
@@ -868,7 +872,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
     }
     if (Qtm) {  // out = sqrt(d) Q^T acc for the G heads, by the whole block
         __syncthreads();
-        const float y = block_gemv<G, kDecThreads>(Qtm, pacc, pacc + G * kD, tid);
+        const float y = block_gemv<G, kDecThreads>(qts, pacc, pacc + G * kD, tid);
         if (tid < G * kD) out[((b * Hq) + (int64_t)g * G + (tid >> 7)) * kD + (tid & 127)] = y * 11.313708498984761f;
     }
     if (tid == 0)  // leave the counter ready for the next call
@@ -1010,12 +1014,14 @@ __global__ __launch_bounds__(64 * kRotWaves) void k_rotate_dense(const half_t *_
     __shared__ __align__(16) float part[64 * kRotWaves / kD][kRotHeads][kD];
     const int tid = threadIdx.x;
     const int64_t h0 = (int64_t)blockIdx.x * kRotHeads;
+    GemvSlice<64 * kRotWaves> qs;
+    gemv_load<64 * kRotWaves>(Qm, tid, qs);  // in flight while the queries are staged
     for (int i = tid; i < kRotHeads * kD; i += 64 * kRotWaves) {
         const int64_t h = h0 + i / kD;
         qv[i / kD][i % kD] = h < heads ? (float)q[h * kD + i % kD] : 0.0f;
     }
     __syncthreads();
-    const float y = block_gemv<kRotHeads, 64 * kRotWaves>(Qm, &qv[0][0], &part[0][0][0], tid);
+    const float y = block_gemv<kRotHeads, 64 * kRotWaves>(qs, &qv[0][0], &part[0][0][0], tid);
     const int64_t h = h0 + tid / kD;
     if (tid < kRotHeads * kD && h < heads) qrot[h * kD + tid % kD] = y * 11.313708498984761f;
 }

@@ -86,35 +86,48 @@ __device__ __forceinline__ void wave_lds_sync()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// y[h][r] = sum_c M[r][c] x[h][c] for NH vectors x (LDS, [NH][128]) and a
-// 128 x 128 row-major fp32 matrix M in global memory, by all NT threads of
-// the block: thread t takes row t % 128 and the 128 / (NT / 128) columns of
-// slice t / 128, all of its part of M in flight at once (the block reads M
-// once); partial sums go to part[NT / 128][NH][128] in LDS.  Every thread
-// of the block must call it; it returns y[t / 128][t % 128] to threads
-// t < 128 NH.  `part` may be reused after a further barrier.
-template <int NH, int NT>
-__device__ __forceinline__ float block_gemv(const float *__restrict__ M, const float *x, float *part, int tid)
-{
+// Block-wide y[h][r] = sum_c M[r][c] x[h][c] for NH vectors x (LDS,
+// [NH][128]) and a 128 x 128 row-major fp32 matrix M in global memory, by
+// all NT threads of the block: thread t takes row t % 128 and the
+// 128 / (NT / 128) columns of slice t / 128.  gemv_load issues the thread's
+// part of M (all of it in flight at once, the block reading M once), so
+// that it can overlap other work; block_gemv then forms the partial sums in
+// part[NT / 128][NH][128] (LDS) and, after a barrier that every thread of
+// the block must reach, returns y[t / 128][t % 128] to threads t < 128 NH.
+// `part` may be reused after a further barrier.
+template <int NT>
+struct GemvSlice {
     typedef float f4v __attribute__((ext_vector_type(4)));
-    constexpr int P = NT / 128, CW = 128 / P;
+    static constexpr int P = NT / 128, CW = 128 / P;
     static_assert(NT % 128 == 0 && CW % 4 == 0, "whole rows and f4 pieces");
-    const int r = tid & 127, sl = tid >> 7;
-    const f4v *m = reinterpret_cast<const f4v *>(M + r * 128 + sl * CW);
-    f4v mv[CW / 4];
+    f4v m[CW / 4];
+};
+
+template <int NT>
+__device__ __forceinline__ void gemv_load(const float *__restrict__ M, int tid, GemvSlice<NT> &g)
+{
+    using S = GemvSlice<NT>;
+    const typename S::f4v *m = reinterpret_cast<const typename S::f4v *>(M + (tid & 127) * 128 + (tid >> 7) * S::CW);
 #pragma unroll
-    for (int u = 0; u < CW / 4; ++u) mv[u] = m[u];
+    for (int u = 0; u < S::CW / 4; ++u) g.m[u] = m[u];
+}
+
+template <int NH, int NT>
+__device__ __forceinline__ float block_gemv(const GemvSlice<NT> &g, const float *x, float *part, int tid)
+{
+    using S = GemvSlice<NT>;
+    const int r = tid & 127, sl = tid >> 7;
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
-        const f4v *xv = reinterpret_cast<const f4v *>(x + h * 128 + sl * CW);
+        const typename S::f4v *xv = reinterpret_cast<const typename S::f4v *>(x + h * 128 + sl * S::CW);
         float a = 0.0f;
 #pragma unroll
-        for (int u = 0; u < CW / 4; ++u) {
-            const f4v xx = xv[u];
-            a = fmaf(mv[u].x, xx.x, a);
-            a = fmaf(mv[u].y, xx.y, a);
-            a = fmaf(mv[u].z, xx.z, a);
-            a = fmaf(mv[u].w, xx.w, a);
+        for (int u = 0; u < S::CW / 4; ++u) {
+            const typename S::f4v xx = xv[u];
+            a = fmaf(g.m[u].x, xx.x, a);
+            a = fmaf(g.m[u].y, xx.y, a);
+            a = fmaf(g.m[u].z, xx.z, a);
+            a = fmaf(g.m[u].w, xx.w, a);
         }
         part[(sl * NH + h) * 128 + r] = a;
     }
@@ -123,7 +136,7 @@ __device__ __forceinline__ float block_gemv(const float *__restrict__ M, const f
     if (tid < NH * 128) {
         const int h = tid >> 7;
 #pragma unroll
-        for (int k = 0; k < P; ++k) y += part[(k * NH + h) * 128 + r];
+        for (int k = 0; k < S::P; ++k) y += part[(k * NH + h) * 128 + r];
     }
     return y;
 }
