@@ -7,19 +7,20 @@
 // of a call form one list.
 //
 // The rotation is a dense contraction and runs on the matrix cores:
-// v_mfma_f32_16x16x32_f16 with A = 16 vectors x 32 inputs (the fp16 inputs
-// themselves, exact) and B = 32 inputs x 16 outputs of Q, as its fp16 high
-// and low parts (two products, so Q enters to about 2^-22), fp32
-// accumulation.  A wave takes 64 vectors at a time (four A tiles share every
-// B tile read from LDS, where Q's rows are padded to 272 bytes so that the 16
-// rows one read touches fall in distinct banks).  The norm comes from the A
-// registers; the scaled outputs are bucketed with the antisymmetric binary
-// search over the positive thresholds, staged in LDS as bytes, and packed
-// with lane = vector.  A lane's D registers hold, for one vector, the outputs
-// m, m + 16, ..., m + 112: the stage keeps a row in that order (byte 8 m + j
-// holds output 16 j + m), so that they leave as one 8-byte write, and the
-// packing loop, whose positions are all compile-time, reads them back in the
-// same order.  Eight waves share one copy of Q (two per SIMD).
+// v_mfma_f32_16x16x32_f16 with A = 16 rows of Q (as its fp16 high and low
+// parts: two products, so Q enters to about 2^-22) and B = 32 inputs x 16
+// vectors (the fp16 inputs themselves, exact), fp32 accumulation.  A wave
+// takes 64 vectors at a time (four B tiles share every A tile read from
+// LDS, where Q's rows are padded to 272 bytes so that the 16 rows one read
+// touches fall in distinct banks).  Q's rows sit in LDS in an order chosen
+// so that the accumulator registers of a lane hold 8 consecutive output
+// coordinates of one vector, 32 j + 8 kg .. + 7 for j = 0..3 (kg = lane / 16):
+// their indices form one 8 b-bit piece of the record, assembled in registers
+// and written to the vector's LDS row at byte b (4 j + kg).  The norm comes
+// from the B registers (packed fp16 dot products and two lane swaps) and is
+// folded into the thresholds (t rho / sqrt(d) against Q x); the bucket is the
+// antisymmetric binary search over the positive thresholds.  Records leave
+// with lane = vector as 16-byte stores.  Eight waves share one copy of Q.
 #include "kvq_internal.h"
 #include "kvq_wave.h"
 
@@ -32,8 +33,6 @@ typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kDenseWaves = 8;
 constexpr int kQRow = kD + 8;   // padded row of Q in LDS, in halves
-constexpr int kSRow = kD + 16;  // padded row of the index stage, in bytes (36 dwords: a 16-lane
-                                // read of 16-byte pieces of 16 rows touches 64 distinct banks)
 
 struct PosThresholds {
     float p[8];  // t_{L/2} .. t_{L-2}: the positive thresholds of the antisymmetric table
@@ -44,21 +43,21 @@ struct PosThresholds {
 // (an exact tie at a negative threshold lands one cell up; such a coordinate
 // lies inside any decision band).
 template <int BITS>
-__device__ __forceinline__ uint32_t bucket_idx(float y, const PosThresholds &P)
+__device__ __forceinline__ uint32_t bucket_idx(float y, const float *p)
 {
     constexpr uint32_t half = 1u << (BITS - 1);
     const float a = __builtin_fabsf(y);
     uint32_t h = 0;
     if constexpr (BITS == 2) {
-        h = a > P.p[0];
+        h = a > p[0];
     } else if constexpr (BITS == 3) {
-        const bool c1 = a > P.p[1];
-        const bool c2 = a > (c1 ? P.p[2] : P.p[0]);
+        const bool c1 = a > p[1];
+        const bool c2 = a > (c1 ? p[2] : p[0]);
         h = 2u * c1 + c2;
     } else if constexpr (BITS == 4) {
-        const bool c1 = a > P.p[3];
-        const bool c2 = a > (c1 ? P.p[5] : P.p[1]);
-        const bool c3 = a > (c1 ? (c2 ? P.p[6] : P.p[4]) : (c2 ? P.p[2] : P.p[0]));
+        const bool c1 = a > p[3];
+        const bool c2 = a > (c1 ? p[5] : p[1]);
+        const bool c3 = a > (c1 ? (c2 ? p[6] : p[4]) : (c2 ? p[2] : p[0]));
         h = 4u * c1 + 2u * c2 + c3;
     }
     return y > 0.0f ? half + h : half - 1u - h;
@@ -71,58 +70,67 @@ __global__ __launch_bounds__(64 * kDenseWaves) void k_quantize_dense(
     float *__restrict__ nv, int64_t N, int64_t Ntot, int64_t n_groups)
 {
     constexpr int RW = 4 * BITS;  // dwords per record
-    __shared__ __align__(16) _Float16 qs[2][kD * kQRow];  // Q high, low parts; row = output
-    __shared__ __align__(16) uint8_t stage[kDenseWaves][64 * kSRow];
-    __shared__ __align__(16) float scl[kDenseWaves][64];
+    constexpr int SR = RW + 1;    // stage row stride in dwords (odd: a dword read of 64 rows is conflict-free)
+    constexpr int NP = (1 << (BITS - 1)) - 1;  // positive thresholds
+    __shared__ __align__(16) _Float16 qs[2][kD * kQRow];  // Q high, low parts, rows permuted
+    __shared__ __align__(16) uint32_t stage[kDenseWaves][64 * SR];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    // Q parts into LDS: 2 x 128 rows x 16 chunks of 8 halves
+    // LDS row 16 nb + a holds Q row 32 (nb / 2) + 8 (a / 4) + 4 (nb % 2) + a % 4:
+    // accumulator r of tile nb in lane group kg is then output 32 (nb / 2) + 8 kg + 4 (nb % 2) + r
     for (int i = tid; i < 2 * kD * 16; i += 64 * kDenseWaves) {
         const int part = i >> 11, row = (i >> 4) & (kD - 1), ch = i & 15;
-        *reinterpret_cast<u4_t *>(&qs[part][row * kQRow + 8 * ch]) = q16[i];
+        const int nb = row >> 4, a = row & 15;
+        const int src = 32 * (nb >> 1) + 8 * (a >> 2) + 4 * (nb & 1) + (a & 3);
+        *reinterpret_cast<u4_t *>(&qs[part][row * kQRow + 8 * ch]) = q16[(part * kD + src) * 16 + ch];
     }
     __syncthreads();
     const int m16 = lane & 15, kg = lane >> 4;
-    const float kSqrtD = 11.313708498984761f;
-    for (int64_t grp = (int64_t)blockIdx.x * kDenseWaves + wv; grp < n_groups;
-         grp += (int64_t)gridDim.x * kDenseWaves) {
-        // vectors 64 grp .. 64 grp + 63 of the list: K (0 .. N-1), then V (N .. Ntot-1)
-        const int64_t g0 = 64 * grp;
-        h8_t A[4][4];
-        float ss[4];
+    const float kInvSqrtD = 0.08838834764831845f;
+    uint8_t *srow_base = reinterpret_cast<uint8_t *>(&stage[wv][0]);
+    // vectors 64 grp .. 64 grp + 63 of the list: K (0 .. N-1), then V (N .. Ntot-1);
+    // vector 16 sg + m16 of a group is column m16 of B tile sg
+    h8_t X[4][4];
+    auto load_x = [&](int64_t grp) {
 #pragma unroll
         for (int sg = 0; sg < 4; ++sg) {
-            int64_t v = g0 + 16 * sg + m16;
+            int64_t v = 64 * grp + 16 * sg + m16;
             if (v >= Ntot) v = Ntot - 1;
             const _Float16 *src = v < N ? xk + v * kD : xv + (v - N) * kD;
-            float s = 0.0f;
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                A[sg][ks] = *reinterpret_cast<const h8_t *>(src + 32 * ks + 8 * kg);
-                // squares of fp16 values are exact in fp32; pairs summed by the packed dot product
-                const h8_t a = A[sg][ks];
-                s = __builtin_amdgcn_fdot2(__builtin_shufflevector(a, a, 0, 1), __builtin_shufflevector(a, a, 0, 1), s, false);
-                s = __builtin_amdgcn_fdot2(__builtin_shufflevector(a, a, 2, 3), __builtin_shufflevector(a, a, 2, 3), s, false);
-                s = __builtin_amdgcn_fdot2(__builtin_shufflevector(a, a, 4, 5), __builtin_shufflevector(a, a, 4, 5), s, false);
-                s = __builtin_amdgcn_fdot2(__builtin_shufflevector(a, a, 6, 7), __builtin_shufflevector(a, a, 6, 7), s, false);
-            }
-            ss[sg] = s;
+            for (int ks = 0; ks < 4; ++ks) X[sg][ks] = *reinterpret_cast<const h8_t *>(src + 32 * ks + 8 * kg);
         }
-        // norms: the four lanes of a vector (kg = 0..3) hold a quarter each
+    };
+    const int64_t gstride = (int64_t)gridDim.x * kDenseWaves;
+    int64_t grp = (int64_t)blockIdx.x * kDenseWaves + wv;
+    if (grp < n_groups) load_x(grp);
+    for (; grp < n_groups; grp += gstride) {
+        const int64_t g0 = 64 * grp;
+        float ps[4][NP > 0 ? NP : 1];  // thresholds scaled by rho / sqrt(d), per vector
 #pragma unroll
         for (int sg = 0; sg < 4; ++sg) {
-            float2 p = swap16(ss[sg]);
+            float ss = 0.0f;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                // squares of fp16 values are exact in fp32; pairs summed by the packed dot product
+                const h8_t a = X[sg][ks];
+                ss = __builtin_amdgcn_fdot2(__builtin_shufflevector(a, a, 0, 1), __builtin_shufflevector(a, a, 0, 1), ss, false);
+                ss = __builtin_amdgcn_fdot2(__builtin_shufflevector(a, a, 2, 3), __builtin_shufflevector(a, a, 2, 3), ss, false);
+                ss = __builtin_amdgcn_fdot2(__builtin_shufflevector(a, a, 4, 5), __builtin_shufflevector(a, a, 4, 5), ss, false);
+                ss = __builtin_amdgcn_fdot2(__builtin_shufflevector(a, a, 6, 7), __builtin_shufflevector(a, a, 6, 7), ss, false);
+            }
+            // the four lanes of a vector (kg = 0..3) hold a quarter each
+            float2 p = swap16(ss);
             const float s1 = p.x + p.y;
             p = swap32(s1);
-            const float tot = p.x + p.y;
-            const float rho = __builtin_sqrtf(tot);
-            const int64_t v = g0 + 16 * sg + m16;
-            if (kg == 0) {
-                scl[wv][16 * sg + m16] = rho > 0.0f ? kSqrtD / rho : 0.0f;
-                if (v < Ntot) (v < N ? nk[v] : nv[v - N]) = rho;
-            }
+            const float rho = __builtin_sqrtf(p.x + p.y);
+            const float sc = rho * kInvSqrtD;
+#pragma unroll
+            for (int k = 0; k < NP; ++k) ps[sg][k] = P.p[k] * sc;
+            const int64_t vn = g0 + 16 * sg + m16;
+            if (kg == 0 && vn < Ntot) (vn < N ? nk[vn] : nv[vn - N]) = rho;
         }
-        // y' = Q x for the 64 vectors, 16 outputs (nb) at a time
+        // Q x for the 64 vectors, 16 (permuted) outputs per tile nb
         f4_t D[4][8];
 #pragma unroll
         for (int sg = 0; sg < 4; ++sg)
@@ -133,50 +141,48 @@ __global__ __launch_bounds__(64 * kDenseWaves) void k_quantize_dense(
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 const int off = (16 * nb + m16) * kQRow + 32 * ks + 8 * kg;
-                const h8_t bh = *reinterpret_cast<const h8_t *>(&qs[0][off]);
-                const h8_t bl = *reinterpret_cast<const h8_t *>(&qs[1][off]);
+                const h8_t ah = *reinterpret_cast<const h8_t *>(&qs[0][off]);
+                const h8_t al = *reinterpret_cast<const h8_t *>(&qs[1][off]);
 #pragma unroll
                 for (int sg = 0; sg < 4; ++sg) {
-                    D[sg][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[sg][ks], bh, D[sg][nb], 0, 0, 0);
-                    D[sg][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[sg][ks], bl, D[sg][nb], 0, 0, 0);
+                    D[sg][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, X[sg][ks], D[sg][nb], 0, 0, 0);
+                    D[sg][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, X[sg][ks], D[sg][nb], 0, 0, 0);
                 }
             }
         }
-        wave_lds_sync();  // the scales are in LDS
-        // D[sg][nb][r]: vector 16 sg + 4 kg + r, output 16 nb + m16 -> stage byte 8 m16 + nb
+        // the inputs are consumed: the next group's loads overlap the bucketing below
+        if (grp + gstride < n_groups) load_x(grp + gstride);
+        // indices of outputs 32 j + 8 kg + u (u = 4 (nb % 2) + r, nb = 2 j + nb % 2) -> bits b u of piece j
 #pragma unroll
         for (int sg = 0; sg < 4; ++sg) {
-            const f4_t s4 = *reinterpret_cast<const f4_t *>(&scl[wv][16 * sg + 4 * kg]);
+            uint8_t *row = srow_base + (16 * sg + m16) * (4 * SR);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                uint32_t w0 = 0u, w1 = 0u;
+            for (int j = 0; j < 4; ++j) {
+                uint32_t pc = 0u;
 #pragma unroll
-                for (int nb = 0; nb < 4; ++nb) {
-                    w0 |= bucket_idx<BITS>(D[sg][nb][r] * s4[r], P) << (8 * nb);
-                    w1 |= bucket_idx<BITS>(D[sg][nb + 4][r] * s4[r], P) << (8 * nb);
+                for (int u = 0; u < 8; ++u)
+                    pc |= bucket_idx<BITS>(D[sg][2 * j + (u >> 2)][u & 3], ps[sg]) << (BITS * u);
+                const int off = BITS * (4 * j + kg);  // byte offset of the piece in the record
+                if constexpr (BITS == 4) {
+                    *reinterpret_cast<uint32_t *>(row + off) = pc;
+                } else if constexpr (BITS == 2) {
+                    *reinterpret_cast<uint16_t *>(row + off) = (uint16_t)pc;
+                } else if constexpr (BITS == 1) {
+                    row[off] = (uint8_t)pc;
+                } else {
+                    row[off] = (uint8_t)pc;
+                    row[off + 1] = (uint8_t)(pc >> 8);
+                    row[off + 2] = (uint8_t)(pc >> 16);
                 }
-                *reinterpret_cast<uint2 *>(&stage[wv][(16 * sg + 4 * kg + r) * kSRow + 8 * m16]) = uint2{w0, w1};
             }
         }
         wave_lds_sync();
-        // pack: lane = vector 64 grp + lane
+        // lane = vector 64 grp + lane
         {
-            const u4_t *row = reinterpret_cast<const u4_t *>(&stage[wv][lane * kSRow]);
+            const uint32_t *row = &stage[wv][lane * SR];
             uint32_t W[RW];
 #pragma unroll
-            for (int w = 0; w < RW; ++w) W[w] = 0u;
-#pragma unroll
-            for (int c = 0; c < kD / 16; ++c) {
-                const u4_t b16 = row[c];
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const uint32_t ix = (b16[e >> 2] >> (8 * (e & 3))) & 0xFFu;
-                    const int pos = 16 * c + e, i = 16 * (pos & 7) + (pos >> 3);  // output index
-                    const int p = BITS * i, w = p >> 5, sh = p & 31;
-                    W[w] |= ix << sh;
-                    if (sh + BITS > 32) W[w + 1] |= ix >> (32 - sh);
-                }
-            }
+            for (int w = 0; w < RW; ++w) W[w] = row[w];
             const int64_t v = g0 + lane;
             if (v < Ntot) {
                 u4_t *dst = reinterpret_cast<u4_t *>(v < N ? ck + v * RW : cv + (v - N) * RW);
