@@ -250,6 +250,14 @@ kvq_status kvq_create(const kvq_config *cfg, kvq_ctx **out)
         if (!cfg->rot_Q) return KVQ_E_INVAL;
         for (int i = 0; i < kvq::kD * kvq::kD; ++i)
             if (!std::isfinite(cfg->rot_Q[i]) || std::fabs(cfg->rot_Q[i]) > 1.0f) return KVQ_E_INVAL;
+        // orthogonal to within 1e-3: max |Q Q^T - I| over all entries, in double
+        const float *Q = cfg->rot_Q;
+        for (int i = 0; i < kvq::kD; ++i)
+            for (int j = i; j < kvq::kD; ++j) {
+                double dot = 0.0;
+                for (int k = 0; k < kvq::kD; ++k) dot += (double)Q[i * kvq::kD + k] * (double)Q[j * kvq::kD + k];
+                if (std::fabs(dot - (i == j ? 1.0 : 0.0)) > 1e-3) return KVQ_E_INVAL;
+            }
     }
 
     int ndev = 0;

@@ -117,7 +117,8 @@ typedef struct {
  * parts) to the device.  *out receives the context (NULL on failure).
  * Errors: KVQ_E_INVAL (NULL pointers, d != 128, bits outside 1..4, a sign
  * entry not +-1, missing table for the mode, unknown codebook or rotation,
- * rot_Q NULL or with an entry not finite or above 1 in magnitude),
+ * rot_Q NULL, with an entry not finite or above 1 in magnitude, or not
+ * orthogonal to within 1e-3 in every entry of Q Q^T - I),
  * KVQ_E_UNSUPPORTED (dense rotation outside KVQ_MODE_MSE), KVQ_E_DEVICE (no
  * such device), KVQ_E_NOMEM. */
 kvq_status kvq_create(const kvq_config *cfg, kvq_ctx **out);

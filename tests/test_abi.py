@@ -72,6 +72,30 @@ def test_create_validation():
     for bad in (dict(codebook=2), dict(codebook=-1)):  # not a KVQ_CODEBOOK_*
         cfg, keep = _cfg(**bad)
         assert L.kvq_create(C.byref(cfg), C.byref(h)) == kvq.KVQ_E_INVAL, bad
+    # dense rotation: the configuration is checked before any device is touched,
+    # so a valid one reaches the device check
+    eye = np.eye(128, dtype=np.float32)
+    qp = lambda a: a.ctypes.data_as(C.POINTER(C.c_float))  # noqa: E731
+    cfg, keep = _cfg(rotation=1, rot_Q=qp(eye), device=999)
+    assert L.kvq_create(C.byref(cfg), C.byref(h)) == kvq.KVQ_E_DEVICE
+    half = 0.5 * eye  # entries in range, not orthogonal
+    nan = eye.copy()
+    nan[3, 4] = np.nan
+    big = eye.copy()
+    big[0, 0] = 1.5
+    near = eye.copy()
+    near[5, 6] = 2e-3  # Q Q^T off by 2e-3 in two entries
+    for Q in (half, nan, big, near):
+        cfg, keep = _cfg(rotation=1, rot_Q=qp(Q), device=999)
+        assert L.kvq_create(C.byref(cfg), C.byref(h)) == kvq.KVQ_E_INVAL
+    cfg, keep = _cfg(rotation=1, device=999)  # no Q
+    assert L.kvq_create(C.byref(cfg), C.byref(h)) == kvq.KVQ_E_INVAL
+    cfg, keep = _cfg(rotation=2, rot_Q=qp(eye), device=999)  # not a KVQ_ROTATION_*
+    assert L.kvq_create(C.byref(cfg), C.byref(h)) == kvq.KVQ_E_INVAL
+    S = np.zeros((128, 128), np.float32)
+    cfg, keep = _cfg(mode=1, qjl_S=qp(S), rotation=1, rot_Q=qp(eye), device=999)  # dense is MSE-only
+    assert L.kvq_create(C.byref(cfg), C.byref(h)) == kvq.KVQ_E_UNSUPPORTED
+    assert not h.value
     cfg, keep = _cfg(device=999)  # no such device (no device at all on a CPU host)
     assert L.kvq_create(C.byref(cfg), C.byref(h)) == kvq.KVQ_E_DEVICE
     assert not h.value
