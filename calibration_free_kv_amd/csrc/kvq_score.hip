@@ -1001,7 +1001,7 @@ __global__ __launch_bounds__(64 * G) void k_tail(const half_t *__restrict__ q, c
     }
 }
 
-constexpr int kRotWaves = 8, kRotHeads = 4;
+constexpr int kRotWaves = 8, kRotHeads = 1;
 
 // Rotated queries of the dense rotation, sqrt(d) Q q for each of `heads`
 // fp16 query vectors, kRotHeads per block (Q read once per block, every
