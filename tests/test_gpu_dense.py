@@ -167,3 +167,18 @@ def test_dense_validation():
     with pytest.raises(kvq.KvqError) as e:
         ctx.flush(kt, kt, 4, kc, kn, kc, kn, 0)
     assert e.value.status == kvq.KVQ_E_UNSUPPORTED
+
+
+def test_quantize_kv_dense_equals_two_calls_and_is_deterministic():
+    """One K+V launch gives the bits of two single-list calls (the same
+    per-vector arithmetic), and repeated calls give the same bits."""
+    inp = synth.make("l8b32k", T=333, B=2)
+    ctx = kvq.Context(8, 3, rot_Q=rot(80))
+    k, v = torch.from_numpy(inp["k"]).cuda(), torch.from_numpy(inp["v"]).cuda()
+    ko, vo = ctx.quantize_kv(k, v)
+    k1 = ctx.quantize(kvq.KVQ_KIND_K, k)
+    v1 = ctx.quantize(kvq.KVQ_KIND_V, v)
+    ko2, _ = ctx.quantize_kv(k, v)
+    for a, b in ((ko, k1), (vo, v1), (ko, ko2)):
+        assert torch.equal(a["codes"], b["codes"])
+        assert torch.equal(a["norms"], b["norms"])
