@@ -14,6 +14,8 @@
 // (the G entries of one (field, value) pair are contiguous).  The decode
 // kernel instead runs its two contractions (logits over coordinates, values
 // over tokens) on the matrix cores; see its own description below.
+#include <atomic>
+
 #include "kvq_internal.h"
 #include "kvq_wave.h"
 
@@ -879,6 +881,23 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
         __hip_atomic_store(counters + bh, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Large dynamic LDS must be allowed per kernel and device, once: a bit per
+// device (the current one) records that it was done.  Concurrent first calls
+// may both set it, which is harmless.
+inline bool need_attr(const std::atomic<uint64_t> &mask)
+{
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    return dev >= 64 || !(mask.load(std::memory_order_acquire) & (1ull << dev));
+}
+
+inline void mark_attr(std::atomic<uint64_t> &mask)
+{
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    if (dev < 64) mask.fetch_or(1ull << dev, std::memory_order_release);
+}
+
 template <int BITS, int G, bool QJL>
 hipError_t run_logits(const kvq_ctx *ctx, const void *q, int64_t B, int64_t Hq, int64_t T,
                       const uint8_t *codes, const float *norms, const uint8_t *qjl_signs,
@@ -896,11 +915,11 @@ hipError_t run_logits(const kvq_ctx *ctx, const void *q, int64_t B, int64_t Hq, 
     const int64_t blocks_per_bh = (T + tpb - 1) / tpb;
     constexpr int LA = FD::NF * FD::E > kLgThreads ? FD::NF * FD::E : kLgThreads;  // tables or rotation sums
     const size_t shm = sizeof(float) * (G * kD + LA * G + (QJL ? 32 * 16 * G + G * kD : 0) + 16);
-    static bool attr_set = false;
-    if (!attr_set) {
+    static std::atomic<uint64_t> attr_set{0};  // one bit per device that has the attribute
+    if (need_attr(attr_set)) {
         (void)hipFuncSetAttribute((const void *)k_logits<BITS, G, QJL>,
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
-        attr_set = true;
+        mark_attr(attr_set);
     }
     hipLaunchKernelGGL((k_logits<BITS, G, QJL>), dim3((unsigned)(bhs * blocks_per_bh)), dim3(kLgThreads), shm,
                        s, (const half_t *)q, codes, norms, (const uint32_t *)qjl_signs, qjl_gamma,
@@ -1050,11 +1069,11 @@ hipError_t run_decode(const kvq_ctx *ctx, const void *q, int64_t B, int64_t Hq, 
         if (T == 0) return hipGetLastError();
     }
     const size_t shm = sizeof(float) * SM::total;
-    static bool attr_set = false;
-    if (!attr_set) {
+    static std::atomic<uint64_t> attr_set{0};  // one bit per device that has the attribute
+    if (need_attr(attr_set)) {
         (void)hipFuncSetAttribute((const void *)k_decode<BITS, G>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                   (int)shm);
-        attr_set = true;
+        mark_attr(attr_set);
     }
     const bool dense = ctx->rotation == KVQ_ROTATION_DENSE;
     float *qrot = nullptr;
