@@ -207,6 +207,10 @@ kvq_status upload(T **dst, const T *src, size_t n)
 
 kvq_status launch_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_E_DEVICE; }
 
+// Query heads per KV head that the kernels are built for.
+bool logits_group_built(int64_t G) { return G == 1 || G == 2 || G == 4 || G == 8; }
+bool decode_group_built(int64_t G) { return G == 1 || G == 2 || G == 4; }
+
 }  // namespace
 
 extern "C" {
@@ -477,7 +481,8 @@ kvq_status kvq_logits(kvq_ctx *ctx, const void *q_f16, int64_t B, int64_t H_q, i
                       const float *qjl_gamma, float *logits, void *stream)
 {
     if (!ctx || ctx->mode == KVQ_MODE_NSN_VQ) return KVQ_E_INVAL;
-    if (B < 0 || T < 0 || H_q < 1 || H_q % ctx->H || H_q / ctx->H > kvq::kMaxGroup) return KVQ_E_INVAL;
+    if (B < 0 || T < 0 || H_q < 1 || H_q % ctx->H) return KVQ_E_INVAL;
+    if (!logits_group_built(H_q / ctx->H)) return KVQ_E_UNSUPPORTED;
     const bool want_qjl = ctx->mode == KVQ_MODE_MSE_QJL;
     if (want_qjl != (qjl_signs != nullptr) || want_qjl != (qjl_gamma != nullptr)) return KVQ_E_INVAL;
     if (B == 0 || T == 0) return KVQ_OK;
@@ -505,7 +510,8 @@ kvq_status kvq_attn_decode_splits(kvq_ctx *ctx, const void *q_f16, int64_t B, in
                                   void *stream)
 {
     if (!ctx || ctx->mode != KVQ_MODE_MSE) return KVQ_E_INVAL;
-    if (B < 0 || T < 1 || H_q < 1 || H_q % ctx->H || H_q / ctx->H > kvq::kMaxGroup) return KVQ_E_INVAL;
+    if (B < 0 || T < 1 || H_q < 1 || H_q % ctx->H) return KVQ_E_INVAL;
+    if (!decode_group_built(H_q / ctx->H)) return KVQ_E_UNSUPPORTED;
     if (n_split < 0 || !std::isfinite(sm_scale) || sm_scale < 0.f) return KVQ_E_INVAL;
     if (B == 0) return KVQ_OK;
     if (!q_f16 || !k_codes || !k_norms || !v_codes || !v_norms || !out || !ws) return KVQ_E_INVAL;

@@ -178,7 +178,9 @@ kvq_status kvq_quantize_kv(kvq_ctx *ctx, const void *k_f16, const void *v_f16, i
  *   logits[b,h,t] = rho_t / d * sum_i q'_i c[idx_t,i]
  *                 (+ rho_t gamma_t sqrt(pi/2)/d * sum_j (2 sgn_t,j - 1) (S q')_j / sqrt(d)
  *                    in MSE_QJL mode)
- *   q_f16       [B, H_q, d] fp16 queries; H_q a multiple of H_kv, H_q/H_kv <= 8
+ *   q_f16       [B, H_q, d] fp16 queries; H_q a multiple of H_kv (else
+ *               KVQ_E_INVAL) with H_q/H_kv in {1, 2, 4, 8} (other ratios:
+ *               KVQ_E_UNSUPPORTED)
  *   codes, norms, qjl_signs, qjl_gamma   the K outputs of kvq_quantize
  *               (qjl_* required in MSE_QJL mode, NULL otherwise)
  *   logits      out [B, H_q, T] fp32 (raw inner products, no softmax scale) */
@@ -195,7 +197,9 @@ size_t kvq_attn_decode_ws_bytes(const kvq_ctx *ctx, int64_t B, int64_t H_q, int6
  * 1/sqrt(d)), and the V codes dequantised and accumulated:
  *   out[b,h] = sum_t softmax_t * v_hat_t,  v_hat = rho_V D_V .* (H c[idx_V]) / d
  * ([PQ] sec. 2 dequantisation; [NSN] Resultados: decode is memory-bound).
- *   q_f16       [B, H_q, d] fp16
+ *   q_f16       [B, H_q, d] fp16; H_q a multiple of H_kv (else KVQ_E_INVAL)
+ *               with H_q/H_kv in {1, 2, 4} (other ratios, e.g. 8 query heads
+ *               per KV head: KVQ_E_UNSUPPORTED)
  *   k_codes/k_norms, v_codes/v_norms   outputs of kvq_quantize for K and V
  *   out         [B, H_q, d] fp32
  *   ws          device workspace of at least kvq_attn_decode_ws_bytes() bytes.

@@ -129,3 +129,24 @@ def test_decode_split_request_is_clamped():
     ref = to_np(ctx.attn_decode(q, k["codes"], k["norms"], v["codes"], v["norms"]))
     big = to_np(ctx.attn_decode(q, k["codes"], k["norms"], v["codes"], v["norms"], n_split=100000))
     np.testing.assert_allclose(big, ref, rtol=1e-4, atol=1e-5)
+
+
+def test_group_sizes_without_kernels_are_rejected_on_the_host():
+    """Decode is built for 1, 2 and 4 query heads per KV head, logits for 1, 2,
+    4 and 8: other divisible ratios are KVQ_E_UNSUPPORTED (nothing launched),
+    a ratio that does not divide is KVQ_E_INVAL."""
+    inp, ctx, k, v = quantized("l8b32k", 3, T=100)
+    args = (k["codes"], k["norms"], v["codes"], v["norms"])
+    for hq, status in ((24, kvq.KVQ_E_UNSUPPORTED), (64, kvq.KVQ_E_UNSUPPORTED), (12, kvq.KVQ_E_INVAL)):
+        q = torch.zeros((1, hq, 128), dtype=torch.float16, device="cuda")
+        with pytest.raises(kvq.KvqError) as e:
+            ctx.attn_decode(q, *args)
+        assert e.value.status == status, hq
+    for hq, status in ((24, kvq.KVQ_E_UNSUPPORTED), (40, kvq.KVQ_E_UNSUPPORTED), (12, kvq.KVQ_E_INVAL)):
+        q = torch.zeros((1, hq, 128), dtype=torch.float16, device="cuda")
+        with pytest.raises(kvq.KvqError) as e:
+            ctx.logits(q, k["codes"], k["norms"])
+        assert e.value.status == status, hq
+    q8 = torch.from_numpy(np.repeat(inp["q"], 2, axis=1)).cuda()  # 64 query heads: 8 per KV head
+    lg = to_np(ctx.logits(q8, k["codes"], k["norms"]))
+    np.testing.assert_array_equal(lg[:, 0::2], lg[:, 1::2])
