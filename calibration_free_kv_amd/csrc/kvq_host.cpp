@@ -269,6 +269,8 @@ kvq_status kvq_create(const kvq_config *cfg, kvq_ctx **out)
         return KVQ_E_DEVICE;
     DeviceGuard g(cfg->device);
     if (!g.ok) return KVQ_E_DEVICE;
+    // scratch of kvq_attn_decode_noalloc on this device (once per device)
+    if (kvq::noalloc_setup(cfg->device) != hipSuccess) return KVQ_E_DEVICE;
 
     kvq_ctx *c = new (std::nothrow) kvq_ctx();
     if (!c) return KVQ_E_NOMEM;
@@ -538,6 +540,33 @@ kvq_status kvq_attn_decode(kvq_ctx *ctx, const void *q_f16, int64_t B, int64_t H
 {
     return kvq_attn_decode_splits(ctx, q_f16, B, H_q, T, k_codes, k_norms, v_codes, v_norms, sm_scale,
                                   out, ws, ws_bytes, 0, stream);
+}
+
+kvq_status kvq_attn_decode_noalloc(kvq_ctx *ctx, const void *q_f16, int64_t B, int64_t H_q, int64_t T,
+                                   const uint8_t *k_codes, const float *k_norms, const uint8_t *v_codes,
+                                   const float *v_norms, float sm_scale, float *out, void *stream)
+{
+    if (!ctx || ctx->mode != KVQ_MODE_MSE) return KVQ_E_INVAL;
+    if (B < 0 || T < 1 || H_q < 1 || H_q % ctx->H) return KVQ_E_INVAL;
+    if (!decode_group_built(H_q / ctx->H)) return KVQ_E_UNSUPPORTED;
+    if (!std::isfinite(sm_scale) || sm_scale < 0.f) return KVQ_E_INVAL;
+    if (B == 0) return KVQ_OK;
+    if (!q_f16 || !k_codes || !k_norms || !v_codes || !v_norms || !out) return KVQ_E_INVAL;
+    if (!aligned(q_f16, 16) || !aligned(k_codes, 16) || !aligned(v_codes, 16) || !aligned(k_norms, 4) ||
+        !aligned(v_norms, 4) || !aligned(out, 16))
+        return KVQ_E_INVAL;
+    if (T > (int64_t(1) << 31) || B * H_q > (int64_t(1) << 31)) return KVQ_E_INVAL;
+    const bool dense = ctx->rotation == KVQ_ROTATION_DENSE;
+    // the split count kvq_attn_decode would take, lowered until the scratch holds it
+    int64_t ns = std::min<int64_t>(kvq::decode_auto_splits(B, ctx->H, T), kvq::decode_max_splits(T));
+    if (ns < 1) ns = 1;
+    while (ns > 1 && kvq::noalloc_decode_bytes(B, H_q, ctx->H, (int)ns, dense) > kvq::kNoAllocScratchBytes) --ns;
+    if (kvq::noalloc_decode_bytes(B, H_q, ctx->H, (int)ns, dense) > kvq::kNoAllocScratchBytes) return KVQ_E_WORKSPACE;
+    if (sm_scale == 0.f) sm_scale = 1.0f / std::sqrt((float)kvq::kD);
+    DeviceGuard g(ctx->device);
+    if (!g.ok) return KVQ_E_DEVICE;
+    return launch_status(kvq::launch_decode_noalloc(ctx, q_f16, B, H_q, T, k_codes, k_norms, v_codes, v_norms,
+                                                    sm_scale, out, (int)ns, (hipStream_t)stream));
 }
 
 size_t kvq_nsn_vq_ws_bytes(const kvq_ctx *ctx, int64_t H, int64_t T)

@@ -14,6 +14,8 @@ constexpr int kD = 128;       // head dimension
 constexpr int kVqSub = 8;     // NSN sub-vector length
 constexpr int kVqK = 256;     // NSN codebook entries
 constexpr int kMaxGroup = 8;  // query heads per KV head supported by the score kernels
+// Device scratch of the no-allocation decode entry point, per device.
+constexpr size_t kNoAllocScratchBytes = size_t(KVQ_NOALLOC_SCRATCH_BYTES);
 
 // Scalar codebook of one bit width, passed to kernels by value.
 struct Codebook {
@@ -71,6 +73,17 @@ int decode_auto_splits(int64_t B, int64_t Hkv, int64_t T);
 hipError_t launch_decode(const kvq_ctx *ctx, const void *q, int64_t B, int64_t Hq, int64_t T,
                          const uint8_t *kc, const float *kn, const uint8_t *vc, const float *vn,
                          float sm_scale, float *out, void *ws, int n_split, hipStream_t s);
+
+// No-allocation decode: bytes of the scratch layout (counters, n_split
+// partial slots per (batch, query head), rotated queries if dense); the
+// one-time per-device set-up (address of the scratch array, counters
+// cleared), called by kvq_create with the device current; and the decode
+// launch on that scratch.
+size_t noalloc_decode_bytes(int64_t B, int64_t Hq, int64_t Hkv, int n_split, bool dense);
+hipError_t noalloc_setup(int device);
+hipError_t launch_decode_noalloc(const kvq_ctx *ctx, const void *q, int64_t B, int64_t Hq, int64_t T,
+                                 const uint8_t *kc, const float *kn, const uint8_t *vc, const float *vn,
+                                 float sm_scale, float *out, int n_split, hipStream_t s);
 
 // Quantise with the dense rotation: N vectors of the list xk (and N of xv
 // when xv is not null) into ck/nk (cv/nv).

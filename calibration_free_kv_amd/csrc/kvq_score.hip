@@ -15,9 +15,18 @@
 // kernel instead runs its two contractions (logits over coordinates, values
 // over tokens) on the matrix cores; see its own description below.
 #include <atomic>
+#include <mutex>
 
 #include "kvq_internal.h"
 #include "kvq_wave.h"
+
+// Device memory of the decode entry point that allocates nothing
+// (kvq_attn_decode_noalloc): arrival counters, split partials and, with the
+// dense rotation, the rotated queries, laid out as in a caller's decode
+// workspace.  Each device holds its own copy until the process ends.  Host
+// code never passes this name to a kernel: it is a host-side stand-in, and
+// the device address comes from hipGetSymbolAddress (kvq::noalloc_setup).
+static __device__ __align__(256) unsigned char scratch[kvq::kNoAllocScratchBytes];
 
 namespace kvq {
 namespace {
@@ -57,11 +66,11 @@ __device__ __forceinline__ uint32_t field(const uint32_t *Wd, int f)
 // Prologue shared by the score kernels: qr[G][128] <- H (D .* q_h) for the G
 // query heads of KV head g of batch b, one wave per head; with a dense
 // rotation Q (not null) instead qr <- sqrt(d) Q q_h by the whole block of NT
-// threads, with (NT / 128) G 128 floats of LDS at `scratch`.  Ends with a
+// threads, with (NT / 128) G 128 floats of LDS at `red`.  Ends with a
 // barrier.
 template <int G, int NT>
 __device__ void rotate_queries(const half_t *__restrict__ q, const float *__restrict__ signs,
-                               int64_t b, int g, int Hq, float *qr, const float *__restrict__ Qm, float *scratch)
+                               int64_t b, int g, int Hq, float *qr, const float *__restrict__ Qm, float *red)
 {
     const int tid = threadIdx.x;
     const half_t *qb = q + ((int64_t)b * Hq + (int64_t)g * G) * kD;
@@ -70,7 +79,7 @@ __device__ void rotate_queries(const half_t *__restrict__ q, const float *__rest
         gemv_load<NT>(Qm, tid, qs);  // in flight while q is staged
         for (int i = tid; i < G * kD; i += NT) qr[i] = (float)qb[i];
         __syncthreads();
-        const float y = block_gemv<G, NT>(qs, qr, scratch, tid);  // every read of qr precedes its barrier
+        const float y = block_gemv<G, NT>(qs, qr, red, tid);  // every read of qr precedes its barrier
         if (tid < G * kD) qr[tid] = y * 11.313708498984761f;
         __syncthreads();
         return;
@@ -1045,10 +1054,12 @@ __global__ __launch_bounds__(64 * kRotWaves) void k_rotate_dense(const half_t *_
     if (tid < kRotHeads * kD && h < heads) qrot[h * kD + tid % kD] = y * 11.313708498984761f;
 }
 
+// ws: arrival counters, then the split partials of `slots` slots per (batch,
+// query head), then (dense rotation) the rotated queries.
 template <int BITS, int G>
 hipError_t run_decode(const kvq_ctx *ctx, const void *q, int64_t B, int64_t Hq, int64_t T, int64_t ldt,
                       const uint8_t *kc, const float *kn, const uint8_t *vc, const float *vn, const DecodeTail *tail,
-                      float sm_scale, float *out, void *ws, int n_split, hipStream_t s)
+                      float sm_scale, float *out, void *ws, int n_split, int64_t slots, hipStream_t s)
 {
     using SM = DecSmem<BITS, G>;
     const int64_t bhs = B * ctx->H;
@@ -1077,8 +1088,8 @@ hipError_t run_decode(const kvq_ctx *ctx, const void *q, int64_t B, int64_t Hq, 
     }
     const bool dense = ctx->rotation == KVQ_ROTATION_DENSE;
     float *qrot = nullptr;
-    if (dense) {  // after the partials (sized for the most splits T allows)
-        qrot = part + (size_t)(B * Hq) * (size_t)decode_max_splits(T) * (kD + 2);
+    if (dense) {  // after the partials
+        qrot = part + (size_t)(B * Hq) * (size_t)slots * (kD + 2);
         const int64_t heads = B * Hq;
         hipLaunchKernelGGL(k_rotate_dense, dim3((unsigned)((heads + kRotHeads - 1) / kRotHeads)),
                            dim3(64 * kRotWaves), 0, s, (const half_t *)q, ctx->d_Q, qrot, heads);
@@ -1112,15 +1123,27 @@ hipError_t dispatch_logits(const kvq_ctx *ctx, int G, bool qjl, const void *q, i
 template <int BITS>
 hipError_t dispatch_decode(const kvq_ctx *ctx, int G, const void *q, int64_t B, int64_t Hq, int64_t T, int64_t ldt,
                            const uint8_t *kc, const float *kn, const uint8_t *vc, const float *vn,
-                           const DecodeTail *tail, float sm, float *out, void *ws, int ns, hipStream_t s)
+                           const DecodeTail *tail, float sm, float *out, void *ws, int ns, int64_t slots,
+                           hipStream_t s)
 {
     switch (G) {
-    case 1: return run_decode<BITS, 1>(ctx, q, B, Hq, T, ldt, kc, kn, vc, vn, tail, sm, out, ws, ns, s);
-    case 2: return run_decode<BITS, 2>(ctx, q, B, Hq, T, ldt, kc, kn, vc, vn, tail, sm, out, ws, ns, s);
-    case 4: return run_decode<BITS, 4>(ctx, q, B, Hq, T, ldt, kc, kn, vc, vn, tail, sm, out, ws, ns, s);
+    case 1: return run_decode<BITS, 1>(ctx, q, B, Hq, T, ldt, kc, kn, vc, vn, tail, sm, out, ws, ns, slots, s);
+    case 2: return run_decode<BITS, 2>(ctx, q, B, Hq, T, ldt, kc, kn, vc, vn, tail, sm, out, ws, ns, slots, s);
+    case 4: return run_decode<BITS, 4>(ctx, q, B, Hq, T, ldt, kc, kn, vc, vn, tail, sm, out, ws, ns, slots, s);
     }
     return hipErrorNotSupported;
 }
+
+__global__ void k_zero_u32(uint32_t *p, int64_t n)
+{
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = 0u;
+}
+
+// Device addresses of `scratch`, one per device, found once.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices];
 
 }  // namespace
 
@@ -1158,11 +1181,28 @@ int decode_auto_splits(int64_t B, int64_t Hkv, int64_t T)
     return (int)(ns < 1 ? 1 : ns);
 }
 
+namespace {
+hipError_t decode_bits(const kvq_ctx *ctx, const void *q, int64_t B, int64_t Hq, int64_t T, int64_t ldt,
+                       const uint8_t *kc, const float *kn, const uint8_t *vc, const float *vn, const DecodeTail *tail,
+                       float sm, float *out, void *ws, int ns, int64_t slots, hipStream_t s)
+{
+    const int G = (int)(Hq / ctx->H);
+    switch (ctx->bits) {
+    case 1: return dispatch_decode<1>(ctx, G, q, B, Hq, T, ldt, kc, kn, vc, vn, tail, sm, out, ws, ns, slots, s);
+    case 2: return dispatch_decode<2>(ctx, G, q, B, Hq, T, ldt, kc, kn, vc, vn, tail, sm, out, ws, ns, slots, s);
+    case 3: return dispatch_decode<3>(ctx, G, q, B, Hq, T, ldt, kc, kn, vc, vn, tail, sm, out, ws, ns, slots, s);
+    case 4: return dispatch_decode<4>(ctx, G, q, B, Hq, T, ldt, kc, kn, vc, vn, tail, sm, out, ws, ns, slots, s);
+    }
+    return hipErrorInvalidValue;
+}
+}  // namespace
+
 hipError_t launch_decode(const kvq_ctx *ctx, const void *q, int64_t B, int64_t Hq, int64_t T,
                          const uint8_t *kc, const float *kn, const uint8_t *vc, const float *vn,
                          float sm_scale, float *out, void *ws, int n_split, hipStream_t s)
 {
-    return launch_decode_stream(ctx, q, B, Hq, T, T, kc, kn, vc, vn, nullptr, sm_scale, out, ws, n_split, s);
+    return decode_bits(ctx, q, B, Hq, T, T, kc, kn, vc, vn, nullptr, sm_scale, out, ws, n_split,
+                       decode_max_splits(T), s);
 }
 
 hipError_t launch_decode_stream(const kvq_ctx *ctx, const void *q, int64_t B, int64_t Hq, int64_t T, int64_t ldt,
@@ -1170,14 +1210,48 @@ hipError_t launch_decode_stream(const kvq_ctx *ctx, const void *q, int64_t B, in
                                 const DecodeTail *tail, float sm_scale, float *out, void *ws, int n_split,
                                 hipStream_t s)
 {
-    const int G = (int)(Hq / ctx->H);
-    switch (ctx->bits) {
-    case 1: return dispatch_decode<1>(ctx, G, q, B, Hq, T, ldt, kc, kn, vc, vn, tail, sm_scale, out, ws, n_split, s);
-    case 2: return dispatch_decode<2>(ctx, G, q, B, Hq, T, ldt, kc, kn, vc, vn, tail, sm_scale, out, ws, n_split, s);
-    case 3: return dispatch_decode<3>(ctx, G, q, B, Hq, T, ldt, kc, kn, vc, vn, tail, sm_scale, out, ws, n_split, s);
-    case 4: return dispatch_decode<4>(ctx, G, q, B, Hq, T, ldt, kc, kn, vc, vn, tail, sm_scale, out, ws, n_split, s);
+    // no dense rotation here, so nothing follows the partials
+    return decode_bits(ctx, q, B, Hq, T, ldt, kc, kn, vc, vn, tail, sm_scale, out, ws, n_split, 0, s);
+}
+
+size_t noalloc_decode_bytes(int64_t B, int64_t Hq, int64_t Hkv, int n_split, bool dense)
+{
+    const int64_t bhs = B * Hkv;
+    return ((bhs * sizeof(unsigned) + 255) / 256) * 256 +
+           (size_t)(B * Hq) * (size_t)n_split * (kD + 2) * sizeof(float) +
+           (dense ? (size_t)(B * Hq) * kD * sizeof(float) : 0);
+}
+
+hipError_t noalloc_setup(int device)
+{
+    if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch[device]) return hipSuccess;
+    void *p = nullptr;
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    // the arrival counters start at zero (every completed call leaves them so)
+    hipLaunchKernelGGL(k_zero_u32, dim3(256), dim3(256), 0, nullptr, (uint32_t *)p,
+                       (int64_t)(kNoAllocScratchBytes / sizeof(uint32_t)));
+    e = hipGetLastError();
+    if (e == hipSuccess) e = hipStreamSynchronize(nullptr);
+    if (e != hipSuccess) return e;
+    g_scratch[device] = p;
+    return hipSuccess;
+}
+
+hipError_t launch_decode_noalloc(const kvq_ctx *ctx, const void *q, int64_t B, int64_t Hq, int64_t T,
+                                 const uint8_t *kc, const float *kn, const uint8_t *vc, const float *vn,
+                                 float sm_scale, float *out, int n_split, hipStream_t s)
+{
+    void *p = nullptr;
+    {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        if (ctx->device >= 0 && ctx->device < kMaxDevices) p = g_scratch[ctx->device];
     }
-    return hipErrorInvalidValue;
+    if (!p) return hipErrorNotInitialized;  // kvq_create sets it up
+    return decode_bits(ctx, q, B, Hq, T, T, kc, kn, vc, vn, nullptr, sm_scale, out, p, n_split, n_split, s);
 }
 
 }  // namespace kvq

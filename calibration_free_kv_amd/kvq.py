@@ -28,7 +28,7 @@ EXPORTS = [
     "kvq_quantize", "kvq_quantize_kv", "kvq_logits", "kvq_attn_decode_ws_bytes", "kvq_attn_decode",
     "kvq_attn_decode_splits", "kvq_nsn_vq_ws_bytes", "kvq_nsn_vq_quantize", "kvq_nsn_logits",
     "kvq_nsn_attn_decode_ws_bytes", "kvq_nsn_attn_decode", "kvq_nsn_attn_decode_splits",
-    "kvq_attn_decode_stream_ws_bytes", "kvq_attn_decode_stream", "kvq_flush",
+    "kvq_attn_decode_stream_ws_bytes", "kvq_attn_decode_stream", "kvq_flush", "kvq_attn_decode_noalloc",
 ]
 
 
@@ -76,6 +76,7 @@ def lib():
         L.kvq_attn_decode.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, vp, C.c_float, vp, vp, sz, vp]
         L.kvq_attn_decode_splits.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, vp, C.c_float, vp, vp,
                                              sz, i32, vp]
+        L.kvq_attn_decode_noalloc.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, vp, C.c_float, vp, vp]
         L.kvq_nsn_vq_ws_bytes.argtypes = [vp, i64, i64]
         L.kvq_nsn_vq_ws_bytes.restype = sz
         L.kvq_nsn_vq_quantize.argtypes = [vp, vp, i64, i64, vp, vp, vp, vp, vp, sz, vp]
@@ -251,6 +252,16 @@ class Context:
                                n_split)
         return out
 
+    def attn_decode_noalloc(self, q, k_codes, k_norms, v_codes, v_norms, sm_scale: float = 0.0, out=None):
+        """As attn_decode, on the library's fixed per-device scratch (no workspace)."""
+        _dev_tensor(q, torch.float16, "q")
+        B, Hq, _ = q.shape
+        T = k_codes.shape[2]
+        if out is None:
+            out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+        kvq_attn_decode_noalloc(self, q, B, Hq, T, k_codes, k_norms, v_codes, v_norms, sm_scale, out)
+        return out
+
     def nsn_vq_quantize(self, x, out=None, ws=None):
         _dev_tensor(x, torch.float16, "x")
         H, T, _ = x.shape
@@ -351,6 +362,13 @@ def kvq_attn_decode_splits(ctx: Context, q, B, H_q, T, k_codes, k_norms, v_codes
                                         _ptr(v_codes), _ptr(v_norms), float(sm_scale), _ptr(out), _ptr(ws),
                                         ws.numel() * ws.element_size(), int(n_split), _stream(q.device)),
            "kvq_attn_decode")
+
+
+def kvq_attn_decode_noalloc(ctx: Context, q, B, H_q, T, k_codes, k_norms, v_codes, v_norms, sm_scale, out):
+    _dev_tensor(out, torch.float32, "out")
+    _check(lib().kvq_attn_decode_noalloc(ctx.handle, _ptr(q), B, H_q, T, _ptr(k_codes), _ptr(k_norms),
+                                         _ptr(v_codes), _ptr(v_norms), float(sm_scale), _ptr(out),
+                                         _stream(q.device)), "kvq_attn_decode_noalloc")
 
 
 def kvq_nsn_vq_quantize(ctx: Context, x, H, T, codes, s1, s2, o, ws):

@@ -222,6 +222,34 @@ kvq_status kvq_attn_decode_splits(kvq_ctx *ctx, const void *q_f16, int64_t B, in
                                   float *out, void *ws, size_t ws_bytes, int32_t n_split,
                                   void *stream);
 
+/* Bytes of device scratch the library keeps per device for
+ * kvq_attn_decode_noalloc (held from the first kvq_create on that device
+ * until the process ends). */
+#define KVQ_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+
+/* kvq_attn_decode for callers that cannot allocate device memory or pass a
+ * workspace: code being captured into a HIP graph, tight serving loops,
+ * harnesses that forbid allocation.  It takes no workspace; its split
+ * partials and arrival counters live in a fixed scratch array of
+ * KVQ_NOALLOC_SCRATCH_BYTES on the context's device, shared by every call on
+ * that device (set up, counters cleared, by kvq_create).  The call allocates
+ * nothing and makes no synchronising call.  Arguments, layouts and results
+ * are those of kvq_attn_decode (equal to it up to fp32 rounding of a
+ * different split count).
+ * Limit: the scratch must hold ceil(4 B H_kv / 256) * 256 bytes of counters,
+ * plus 520 bytes per (batch, query head) and token split, plus (dense
+ * rotation) 512 bytes per (batch, query head).  The split count of
+ * kvq_attn_decode is lowered until that fits; if even one split does not
+ * (B * H_q above about 16000, about 8000 with the dense rotation) the call
+ * returns KVQ_E_WORKSPACE and launches nothing.
+ * Concurrency: all calls on one device share the scratch, which keeps the
+ * last call's contents, so calls that may overlap in time on one device (on
+ * different streams, or from different host threads) race and give wrong
+ * results; order them on one stream.  Other errors as kvq_attn_decode. */
+kvq_status kvq_attn_decode_noalloc(kvq_ctx *ctx, const void *q_f16, int64_t B, int64_t H_q, int64_t T,
+                                   const uint8_t *k_codes, const float *k_norms, const uint8_t *v_codes,
+                                   const float *v_norms, float sm_scale, float *out, void *stream);
+
 /* Workspace bytes kvq_nsn_vq_quantize needs for H heads of T tokens. */
 size_t kvq_nsn_vq_ws_bytes(const kvq_ctx *ctx, int64_t H, int64_t T);
 
