@@ -9,7 +9,7 @@ import torch
 
 import oracle as O
 from calibration_free_kv_amd import kvq, synth
-from tests.gpu_util import needs_gpu, to_np, unpack_np
+from tests.gpu_util import bound_mismatches, boundary_mismatches, needs_gpu, to_np, unpack_np
 
 pytestmark = [pytest.mark.gpu, needs_gpu]
 
@@ -38,12 +38,12 @@ def test_quantize_beta(bits):
 
 
 def check_codes_beta(x, signs, bits, codes, norms):
-    ref = O.quantize(x, signs, bits, codebook="beta")
+    ref = O.quantize(x, signs, bits, codebook="beta", want_y=True)
     gi = unpack_np(codes, bits)
-    bad = (gi != ref["idx"]) & (ref["flags"] == 0)
-    assert not bad.any(), int(bad.sum())
+    m, f = boundary_mismatches(gi, ref, O.tables_f32_beta(bits)[1], "beta")
+    bound_mismatches(m, f, "beta")
     np.testing.assert_allclose(norms, ref["norms"], rtol=1e-5, atol=1e-30)
-    return dict(mismatch_at_boundary=int((gi != ref["idx"]).sum()), flagged=int(ref["flags"].sum()))
+    return dict(mismatch_at_boundary=m, flagged=f)
 
 
 @pytest.mark.parametrize("bits", [2, 3])

@@ -12,7 +12,7 @@ import torch
 
 import oracle as O
 from calibration_free_kv_amd import kvq, synth
-from tests.gpu_util import needs_gpu, to_np, unpack_np
+from tests.gpu_util import bound_mismatches, boundary_mismatches, needs_gpu, to_np, unpack_np
 
 pytestmark = [pytest.mark.gpu, needs_gpu]
 
@@ -22,12 +22,13 @@ def rot(seed):
 
 
 def check_dense_codes(x, Q, bits, codes, norms, codebook="gauss"):
-    ref = O.quantize_dense(x, Q.astype(np.float64), bits, codebook=codebook)
+    ref = O.quantize_dense(x, Q.astype(np.float64), bits, codebook=codebook, want_y=True)
     gi = unpack_np(to_np(codes), bits)
-    bad = (gi != ref["idx"]) & (ref["flags"] == 0)
-    assert not bad.any(), int(bad.sum())
+    _, t = O.tables_f32_beta(bits) if codebook == "beta" else O.tables_f32(bits)
+    m, f = boundary_mismatches(gi, ref, t, "dense")
+    bound_mismatches(m, f, "dense")
     np.testing.assert_allclose(to_np(norms), ref["norms"], rtol=1e-5, atol=1e-30)
-    return int(((gi != ref["idx"])).sum()), int(ref["flags"].sum())
+    return m, f
 
 
 @pytest.mark.parametrize("bits", [1, 2, 3, 4])

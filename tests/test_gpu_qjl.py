@@ -1,10 +1,11 @@
 """GPU parity of the QJL residual path (kvq_quantize in MSE_QJL mode and
 kvq_logits with the QJL term) against the CPU oracle.
 
-Sign bits and gamma are compared on every vector whose GPU indices equal the
-oracle's (all but the rare vectors with a flagged boundary flip, whose
-residual is a different vector; those are counted): exact except bits whose
-projection lies within 1e-5 * gamma of zero.  The logit tests score codes
+Sign bits and gamma are compared on every vector: exact except bits whose
+projection lies within 1e-5 * gamma of zero.  A vector whose GPU indices
+differ from the oracle's at flagged coordinates (an admissible code: each
+such coordinate in the neighbouring cell across a threshold within 1e-5) is
+compared with the oracle's QJL residual of that admissible code.  The logit tests score codes
 written by the oracle (small cases) or drawn by the seeded generator (full
 size); no GPU output feeds the oracle."""
 import numpy as np
@@ -25,30 +26,65 @@ def run_qjl(inp, bits, S):
     return ctx, {n: to_np(t) for n, t in out.items()}, out
 
 
+def admissible_qjl(y, idx, flags, S, bits, gi):
+    """The oracle's QJL results for every admissible code vector of one key:
+    each flagged coordinate (within 1e-5 of a threshold) in its own cell or in
+    the neighbouring cell across that threshold.  Returns the alternative
+    whose indices equal the GPU's `gi` (the GPU's choice among them)."""
+    _, t = O.tables_f32(bits)
+    fpos = np.flatnonzero(flags)
+    assert len(fpos) <= 8, "too many flagged coordinates in one key"
+    alts = []
+    for mask in range(1 << len(fpos)):
+        alt = idx.copy()
+        for k, i in enumerate(fpos):
+            if mask >> k & 1:
+                # the other side of the threshold y[i] is near
+                j = int(np.argmin(np.abs(y[i] - t.astype(np.float64))))
+                alt[i] = j if idx[i] == j + 1 else j + 1
+        alts.append(alt)
+    for alt in alts:
+        if np.array_equal(alt, gi):
+            return O.qjl(y[None], alt[None], S, bits)
+    raise AssertionError("GPU indices are not an admissible code of the key")
+
+
 def check_qjl(inp, bits, S, o, where=None):
+    """Sign bits and gamma of every key: exact (gamma to 1e-5) except bits
+    whose projection lies within 1e-5 * gamma of zero.  A key whose GPU
+    indices differ from the oracle's at flagged coordinates is compared with
+    the oracle's QJL of those indices (its residual is a different vector)."""
     x = inp["k"]
     B, H, T, _ = x.shape
     if where is None:
         bb, hh, tt = [a.ravel() for a in np.meshgrid(np.arange(B), np.arange(H), np.arange(T), indexing="ij")]
     else:
         bb, hh, tt = where
-    mism = skipped = 0
+    mism = flipped = flagged = 0
     for h in np.unique(hh):
         sel = hh == h
         xs = x[bb[sel], h, tt[sel]][None, None]
         ref = O.quantize(xs, inp["signs_k"][h:h + 1], bits, want_y=True)
         q = O.qjl(ref["y"], ref["idx"], S, bits)
-        same = (unpack_np(o["codes"][bb[sel], h, tt[sel]], bits) == ref["idx"][0, 0]).all(-1)
-        skipped += int((~same).sum())
-        np.testing.assert_allclose(o["qjl_gamma"][bb[sel], h, tt[sel]][same], q["gamma"][0, 0][same],
-                                   rtol=1e-5, atol=1e-7)
-        gs = np.unpackbits(o["qjl_signs"][bb[sel], h, tt[sel]], axis=-1, bitorder="little")[same]
-        rs = np.unpackbits(q["signs"][0, 0], axis=-1, bitorder="little")[same]
-        bad = (gs != rs) & (q["flags"][0, 0][same] == 0)
+        gi = unpack_np(o["codes"][bb[sel], h, tt[sel]], bits)
+        g_gamma = o["qjl_gamma"][bb[sel], h, tt[sel]]
+        g_bits = np.unpackbits(o["qjl_signs"][bb[sel], h, tt[sel]], axis=-1, bitorder="little")
+        r_gamma = q["gamma"][0, 0].copy()
+        r_bits = np.unpackbits(q["signs"][0, 0], axis=-1, bitorder="little")
+        r_flags = q["flags"][0, 0].copy()
+        for v in np.flatnonzero(~(gi == ref["idx"][0, 0]).all(-1)):
+            alt = admissible_qjl(ref["y"][0, 0, v], ref["idx"][0, 0, v], ref["flags"][0, 0, v], S, bits, gi[v])
+            r_gamma[v] = alt["gamma"][0]
+            r_bits[v] = np.unpackbits(alt["signs"][0], bitorder="little")
+            r_flags[v] = alt["flags"][0]
+            flipped += 1
+        np.testing.assert_allclose(g_gamma, r_gamma, rtol=1e-5, atol=1e-7)
+        bad = (g_bits != r_bits) & (r_flags == 0)
         assert not bad.any(), "%d sign bits differ outside the 1e-5*gamma band" % int(bad.sum())
-        mism += int((gs != rs).sum())
-    assert skipped <= max(2, len(hh) // 100), skipped
-    return mism, skipped
+        mism += int((g_bits != r_bits).sum())
+        flagged += int(r_flags.sum())
+    assert mism <= flagged // 2 + 2, (mism, flagged)
+    return mism, flipped
 
 
 def oracle_qjl_codes(inp, bits):

@@ -13,7 +13,7 @@ import torch
 
 import oracle as O
 from calibration_free_kv_amd import kvq, synth
-from tests.gpu_util import needs_gpu, to_np, unpack_np
+from tests.gpu_util import bound_mismatches, boundary_mismatches, needs_gpu, to_np, unpack_np
 
 pytestmark = [pytest.mark.gpu, needs_gpu]
 
@@ -108,10 +108,10 @@ def test_flush_matches_oracle_and_touches_nothing_else(bits):
     got = {k: to_np(v) for k, v in g.items()}
     sel = slice(T0, T0 + R)
     for name, x, signs, c0, n0 in (("k", kt, inp["signs_k"], kc0, kn0), ("v", vt, inp["signs_v"], vc0, vn0)):
-        ref = O.quantize(x[:, :, :R], signs, bits)
+        ref = O.quantize(x[:, :, :R], signs, bits, want_y=True)
         gi = unpack_np(got[name + "c"][:, :, sel], bits)
-        bad = (gi != ref["idx"]) & (ref["flags"] == 0)
-        assert not bad.any(), (name, int(bad.sum()))
+        m, f = boundary_mismatches(gi, ref, O.tables_f32(bits)[1], "flush " + name)
+        bound_mismatches(m, f, "flush " + name)
         np.testing.assert_allclose(got[name + "n"][:, :, sel], ref["norms"], rtol=1e-5, atol=1e-30)
         keep = np.ones(T_cap, bool)
         keep[sel] = False
