@@ -763,12 +763,13 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
         }
     }
     __syncthreads();
-    // The split partials are written and read with device-scope (coherent,
-    // written-through) accesses, so handing them over needs no cache
-    // write-back or invalidation: once a wave's stores are complete
-    // (vmcnt(0)) they are visible to every compute unit, the barrier orders
-    // the arrival count after all of them, and the merging block reads them
-    // at device scope after seeing the count.
+    // Hand-over of the split partials to the last block of (b, g): every
+    // thread's partial stores happen before the block barrier, the barrier
+    // before wave 0's arrival count, which releases them at device scope;
+    // the count's read in the last block is followed by a device-scope
+    // acquire fence, and that block's other waves follow it through a
+    // barrier.  The partials themselves are device-scope stores and loads
+    // (written through to the coherence point).
     auto st_dev = [](float *p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
     float *my = part + ((bh * n_part + split) * G) * (kD + 2);
     for (int idx = tid; idx < G * kD; idx += kDecThreads) {
@@ -796,8 +797,11 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
     unsigned &last = *reinterpret_cast<unsigned *>(smem + SM::flag);
     if (wv == 0) {
         unsigned prev = 0;
-        if (lane == 0) prev = __hip_atomic_fetch_add(counters + bh, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (lane == 0) prev = __hip_atomic_fetch_add(counters + bh, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
         const unsigned is_last = __builtin_amdgcn_readfirstlane(prev) == (unsigned)(n_split - 1);
+        // only the last block acquires (a device-scope acquire invalidates
+        // the caches, which would cost every other block its cached records)
+        if (is_last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         if (lane == 0) last = is_last;
     }
     __syncthreads();
