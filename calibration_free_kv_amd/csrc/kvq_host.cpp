@@ -217,7 +217,10 @@ extern "C" {
 
 const char *kvq_strerror(kvq_status s)
 {
-    switch (s) {
+    // a C caller may pass any int: read it as an int, not as the enum type
+    int v;
+    std::memcpy(&v, &s, sizeof v);
+    switch (v) {
     case KVQ_OK: return "ok";
     case KVQ_E_INVAL: return "invalid argument";
     case KVQ_E_UNSUPPORTED: return "unsupported configuration";

@@ -14,6 +14,8 @@ constexpr int kD = 128;       // head dimension
 constexpr int kVqSub = 8;     // NSN sub-vector length
 constexpr int kVqK = 256;     // NSN codebook entries
 constexpr int kMaxGroup = 8;  // query heads per KV head supported by the score kernels
+constexpr int kNsnChunk = 2048;            // tokens per NSN statistics block
+constexpr int kNsnPartStride = kD + 4;     // floats per NSN decode partial: acc[128], M, L, WO, pad
 // Device scratch of the no-allocation decode entry point, per device.
 constexpr size_t kNoAllocScratchBytes = size_t(KVQ_NOALLOC_SCRATCH_BYTES);
 

@@ -1,0 +1,68 @@
+// Workspace layouts and split counts of the libkvq kernels: plain host
+// arithmetic, kept apart from the kernels so that the host side of the
+// library (validation, tables, layouts) also builds and runs without a GPU.
+#include "kvq_internal.h"
+
+namespace kvq {
+
+// Decode: arrival counters [B H_kv] (rounded up to 256 bytes), split partials
+// [B H_q][max splits][2 + 128] fp32, then the dense rotation's rotated
+// queries [B H_q][128] fp32.
+size_t decode_ws_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t T)
+{
+    const int64_t bhs = B * Hkv;
+    const int64_t max_split = decode_max_splits(T);
+    return ((bhs * sizeof(unsigned) + 255) / 256) * 256 +
+           (size_t)(B * Hq) * (size_t)max_split * (kD + 2) * sizeof(float) + (size_t)(B * Hq) * kD * sizeof(float);
+}
+
+int decode_auto_splits(int64_t B, int64_t Hkv, int64_t T)
+{
+    // about one block (16 waves) per compute unit, and at least 1024 tokens per block
+    const int64_t bhs = B * Hkv;
+    int64_t ns = (256 + bhs - 1) / bhs;
+    const int64_t cap = (T + 1023) / 1024;
+    if (ns > cap) ns = cap;
+    return (int)(ns < 1 ? 1 : ns);
+}
+
+// The same layout with exactly n_split partial slots per (batch, query head).
+size_t noalloc_decode_bytes(int64_t B, int64_t Hq, int64_t Hkv, int n_split, bool dense)
+{
+    const int64_t bhs = B * Hkv;
+    return ((bhs * sizeof(unsigned) + 255) / 256) * 256 +
+           (size_t)(B * Hq) * (size_t)n_split * (kD + 2) * sizeof(float) +
+           (dense ? (size_t)(B * Hq) * kD * sizeof(float) : 0);
+}
+
+// NSN statistics: channel sums per (head, 2048-token chunk), fp32 [H][chunks][128].
+size_t nsn_ws_bytes(int64_t H, int64_t T)
+{
+    const int64_t n_chunks = (T + kNsnChunk - 1) / kNsnChunk;
+    return (size_t)H * n_chunks * kD * sizeof(float);
+}
+
+// NSN-VQ decode: tokens per split (a multiple of the 64-token tile), the
+// automatic split count (about one block per compute unit), and the partials
+// [B H_q][max splits][kNsnPartStride] fp32.
+int64_t nsn_decode_chunk(int64_t T, int n_split)
+{
+    const int64_t per = (T + n_split - 1) / n_split;
+    return (per + 63) / 64 * 64;
+}
+
+int nsn_decode_auto_splits(const kvq_ctx *ctx, int64_t B, int64_t T)
+{
+    const int64_t groups = B * ctx->H;
+    int64_t ns = (ctx->n_cu + groups - 1) / groups;
+    const int64_t cap = decode_max_splits(T);
+    if (ns > cap) ns = cap;
+    return ns < 1 ? 1 : (int)ns;
+}
+
+size_t nsn_decode_ws_bytes(int64_t B, int64_t Hq, int64_t T)
+{
+    return (size_t)B * Hq * decode_max_splits(T) * kNsnPartStride * sizeof(float);
+}
+
+}  // namespace kvq

@@ -30,7 +30,7 @@ typedef float f16v_t __attribute__((ext_vector_type(16)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kTile = 64;
-constexpr int kChunk = 2048;  // tokens per stats block
+constexpr int kChunk = kNsnChunk;  // tokens per stats block
 constexpr float kSqrtD = 11.313708498984761f;
 
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
@@ -560,12 +560,6 @@ __global__ __launch_bounds__(kWavesN * 64) __attribute__((amdgpu_waves_per_eu(2,
 }
 
 }  // namespace
-
-size_t nsn_ws_bytes(int64_t H, int64_t T)
-{
-    const int64_t n_chunks = (T + kChunk - 1) / kChunk;
-    return (size_t)H * n_chunks * kD * sizeof(float);
-}
 
 hipError_t launch_nsn_vq(const kvq_ctx *ctx, const void *x, int64_t H, int64_t T, uint8_t *codes, float *s1,
                          float *s2, float *o, void *ws, hipStream_t s)

@@ -171,7 +171,7 @@ __device__ __forceinline__ TileIn load_tile(const u4_t *kc, const float *ks1, co
     const int64_t v = base + t;
     return TileIn{kc[v], vc[v], ks1[v], ks2[v], vs1[v], vs2[v]};
 }
-constexpr int kPartStride = kD + 4;  // floats per (split, head) partial: acc[128], M, L, WO, pad
+constexpr int kPartStride = kNsnPartStride;  // floats per (split, head) partial: acc[128], M, L, WO, pad
 
 template <int G>
 __global__ __launch_bounds__(64 * dec_waves<G>()) void k_nsn_part(const half_t *__restrict__ q, const u4_t *__restrict__ kc,
@@ -376,26 +376,6 @@ hipError_t decode_g(const kvq_ctx *ctx, const void *q, int64_t B, int64_t T, con
 }
 
 }  // namespace
-
-int64_t nsn_decode_chunk(int64_t T, int n_split)
-{
-    const int64_t per = (T + n_split - 1) / n_split;
-    return (per + 63) / 64 * 64;
-}
-
-int nsn_decode_auto_splits(const kvq_ctx *ctx, int64_t B, int64_t T)
-{
-    const int64_t groups = B * ctx->H;
-    int64_t ns = (ctx->n_cu + groups - 1) / groups;
-    const int64_t cap = decode_max_splits(T);
-    if (ns > cap) ns = cap;
-    return ns < 1 ? 1 : (int)ns;
-}
-
-size_t nsn_decode_ws_bytes(int64_t B, int64_t Hq, int64_t T)
-{
-    return (size_t)B * Hq * decode_max_splits(T) * kPartStride * sizeof(float);
-}
 
 hipError_t launch_nsn_logits(const kvq_ctx *ctx, const void *q, int64_t B, int64_t Hq, int64_t T,
                              const uint8_t *codes, const float *s1, const float *s2, const float *o, float *logits,

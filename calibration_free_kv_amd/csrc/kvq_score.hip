@@ -1166,25 +1166,6 @@ hipError_t launch_logits(const kvq_ctx *ctx, const void *q, int64_t B, int64_t H
     return hipErrorInvalidValue;
 }
 
-size_t decode_ws_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t T)
-{
-    const int64_t bhs = B * Hkv;
-    const int64_t max_split = decode_max_splits(T);
-    // counters, partials, then the rotated queries of the dense rotation
-    return ((bhs * sizeof(unsigned) + 255) / 256) * 256 +
-           (size_t)(B * Hq) * (size_t)max_split * (kD + 2) * sizeof(float) + (size_t)(B * Hq) * kD * sizeof(float);
-}
-
-int decode_auto_splits(int64_t B, int64_t Hkv, int64_t T)
-{
-    // about one block (16 waves) per compute unit, and at least 1024 tokens per block
-    const int64_t bhs = B * Hkv;
-    int64_t ns = (256 + bhs - 1) / bhs;
-    const int64_t cap = (T + 1023) / 1024;
-    if (ns > cap) ns = cap;
-    return (int)(ns < 1 ? 1 : ns);
-}
-
 namespace {
 hipError_t decode_bits(const kvq_ctx *ctx, const void *q, int64_t B, int64_t Hq, int64_t T, int64_t ldt,
                        const uint8_t *kc, const float *kn, const uint8_t *vc, const float *vn, const DecodeTail *tail,
@@ -1216,14 +1197,6 @@ hipError_t launch_decode_stream(const kvq_ctx *ctx, const void *q, int64_t B, in
 {
     // no dense rotation here, so nothing follows the partials
     return decode_bits(ctx, q, B, Hq, T, ldt, kc, kn, vc, vn, tail, sm_scale, out, ws, n_split, 0, s);
-}
-
-size_t noalloc_decode_bytes(int64_t B, int64_t Hq, int64_t Hkv, int n_split, bool dense)
-{
-    const int64_t bhs = B * Hkv;
-    return ((bhs * sizeof(unsigned) + 255) / 256) * 256 +
-           (size_t)(B * Hq) * (size_t)n_split * (kD + 2) * sizeof(float) +
-           (dense ? (size_t)(B * Hq) * kD * sizeof(float) : 0);
 }
 
 hipError_t noalloc_setup(int device)

@@ -1,0 +1,219 @@
+// Drives libkvq's C ABI on a fake device (HIP calls and kernel launches
+// stubbed), for a build with the address and undefined-behaviour sanitizers:
+// context creation for every mode and option, the table builders, and the
+// host validation of every entry point.  Prints "host ok".
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#include "kvq.h"
+#include "stub_record.h"
+
+#define CHECK(e)                                                                    \
+    do {                                                                            \
+        if (!(e)) {                                                                 \
+            std::fprintf(stderr, "check failed: %s (line %d)\n", #e, __LINE__);    \
+            return 1;                                                               \
+        }                                                                           \
+    } while (0)
+
+namespace {
+// A fake device buffer: 256-byte aligned host memory (never dereferenced by
+// the stubbed launches).
+struct Buf {
+    void *p;
+    explicit Buf(size_t n) : p(std::aligned_alloc(256, (n + 255) / 256 * 256 + 256)) {}
+    ~Buf() { std::free(p); }
+    template <class T> T *as(size_t byte_off = 0) { return reinterpret_cast<T *>(static_cast<char *>(p) + byte_off); }
+};
+
+kvq_config base(int bits, int mode, int H)
+{
+    kvq_config c;
+    std::memset(&c, 0, sizeof(c));
+    c.d = 128;
+    c.bits = bits;
+    c.mode = mode;
+    c.n_kv_heads = H;
+    c.seed = 1234;
+    return c;
+}
+}  // namespace
+
+int main()
+{
+    // tables without a context
+    for (int b = 1; b <= 4; ++b) {
+        float c[16], t[16];
+        CHECK(kvq_codebook(b, c, t) == KVQ_OK);
+        const int L = 1 << b;
+        for (int j = 0; j < L; ++j) CHECK(c[j] == -c[L - 1 - j]);
+        for (int j = 0; j + 1 < L; ++j) CHECK(c[j] < t[j] && t[j] < c[j + 1]);
+    }
+    float cc[16], tt[16];
+    CHECK(kvq_codebook(0, cc, tt) == KVQ_E_INVAL && kvq_codebook(5, cc, tt) == KVQ_E_INVAL);
+    CHECK(kvq_codebook(3, nullptr, tt) == KVQ_E_INVAL);
+    CHECK(std::strlen(kvq_strerror((kvq_status)99)) > 0);
+
+    const int H = 4;
+    std::vector<float> S(128 * 128), Q(128 * 128, 0.f), Qbad(128 * 128, 0.f), cb(256 * 8);
+    unsigned s = 7;
+    auto rnd = [&]() { s = s * 1664525u + 1013904223u; return ((s >> 8) & 0xFFFF) / 65536.0f - 0.5f; };
+    for (auto &v : S) v = rnd() * 4;
+    for (auto &v : cb) v = rnd() * 3;
+    for (int i = 0; i < 128; ++i) Q[i * 128 + i] = 1.f;
+    Qbad = Q;
+    Qbad[5] = 0.5f;
+    std::vector<int8_t> sg(H * 128, 1), sgbad(H * 128, 1);
+    sgbad[77] = 0;
+
+    // creation: valid and invalid configurations
+    kvq_ctx *ctx = nullptr;
+    CHECK(kvq_create(nullptr, &ctx) == KVQ_E_INVAL);
+    kvq_config c = base(3, KVQ_MODE_MSE, H);
+    c.d = 64;
+    CHECK(kvq_create(&c, &ctx) == KVQ_E_INVAL && ctx == nullptr);
+    c = base(5, KVQ_MODE_MSE, H);
+    CHECK(kvq_create(&c, &ctx) == KVQ_E_INVAL);
+    c = base(3, KVQ_MODE_MSE, H);
+    c.signs_k = sgbad.data();
+    CHECK(kvq_create(&c, &ctx) == KVQ_E_INVAL);
+    c = base(3, KVQ_MODE_MSE_QJL, H);
+    CHECK(kvq_create(&c, &ctx) == KVQ_E_INVAL);  // no S
+    c = base(3, KVQ_MODE_MSE, H);
+    c.rotation = KVQ_ROTATION_DENSE;
+    c.rot_Q = Qbad.data();
+    CHECK(kvq_create(&c, &ctx) == KVQ_E_INVAL);  // not orthogonal
+    c = base(3, KVQ_MODE_MSE_QJL, H);
+    c.qjl_S = S.data();
+    c.rotation = KVQ_ROTATION_DENSE;
+    c.rot_Q = Q.data();
+    kvq_status st = kvq_create(&c, &ctx);
+    CHECK(st == KVQ_E_UNSUPPORTED || st == KVQ_OK);
+    if (st == KVQ_OK) kvq_destroy(ctx);
+
+    std::vector<kvq_ctx *> all;
+    for (int b = 1; b <= 4; ++b)
+        for (int cbk = 0; cbk < 2; ++cbk) {
+            c = base(b, KVQ_MODE_MSE, H);
+            c.codebook = cbk;
+            if (b == 2) c.signs_k = sg.data();
+            CHECK(kvq_create(&c, &ctx) == KVQ_OK);
+            all.push_back(ctx);
+            float ct[16], tt2[16];
+            std::vector<int8_t> sk(H * 128), sv(H * 128);
+            CHECK(kvq_get_tables(ctx, ct, tt2, sk.data(), sv.data()) == KVQ_OK);
+            for (int i = 0; i < H * 128; ++i) CHECK((sk[i] == 1 || sk[i] == -1) && (sv[i] == 1 || sv[i] == -1));
+            CHECK(kvq_code_bytes_per_vec(ctx) == 16 * b);
+        }
+    kvq_ctx *mse = all[4];  // 3 bits, N(0,1) tables
+    c = base(2, KVQ_MODE_MSE_QJL, H);
+    c.qjl_S = S.data();
+    kvq_ctx *qjl = nullptr;
+    CHECK(kvq_create(&c, &qjl) == KVQ_OK);
+    c = base(1, KVQ_MODE_NSN_VQ, H);
+    c.vq_codebook = cb.data();
+    kvq_ctx *nsn = nullptr;
+    CHECK(kvq_create(&c, &nsn) == KVQ_OK);
+    CHECK(kvq_get_tables(nsn, nullptr, nullptr, sg.data(), nullptr) == KVQ_E_INVAL);
+    c = base(3, KVQ_MODE_MSE, H);
+    c.rotation = KVQ_ROTATION_DENSE;
+    c.rot_Q = Q.data();
+    kvq_ctx *dense = nullptr;
+    CHECK(kvq_create(&c, &dense) == KVQ_OK);
+
+    // quantize
+    const int64_t B = 2, T = 1000, Hq = 4 * H;
+    Buf x(B * H * T * 256), codes(B * H * T * 64), norms(B * H * T * 4), q(B * 8 * H * 256), out(B * 8 * H * 512);
+    Buf lg(B * 8 * H * T * 4), signs(B * H * T * 16), gamma(B * H * T * 4);
+    void *st0 = nullptr;
+    CHECK(kvq_quantize(mse, 2, x.p, B, H, T, codes.as<uint8_t>(), norms.as<float>(), nullptr, nullptr, st0) == KVQ_E_INVAL);
+    CHECK(kvq_quantize(mse, 0, x.p, B, H + 1, T, codes.as<uint8_t>(), norms.as<float>(), nullptr, nullptr, st0) == KVQ_E_INVAL);
+    CHECK(kvq_quantize(mse, 0, x.as<char>(2), B, H, T, codes.as<uint8_t>(), norms.as<float>(), nullptr, nullptr, st0) == KVQ_E_INVAL);
+    const int calls0 = g_last.calls;
+    CHECK(kvq_quantize(mse, 0, x.p, 0, H, T, codes.as<uint8_t>(), norms.as<float>(), nullptr, nullptr, st0) == KVQ_OK);
+    CHECK(g_last.calls == calls0);  // empty call: nothing launched
+    CHECK(kvq_quantize(mse, 1, x.p, B, H, T, codes.as<uint8_t>(), norms.as<float>(), nullptr, nullptr, st0) == KVQ_OK);
+    CHECK(std::strcmp(g_last.what, "quantize") == 0 && g_last.a == 1 && g_last.c == T);
+    CHECK(kvq_quantize(qjl, 0, x.p, B, H, T, codes.as<uint8_t>(), norms.as<float>(), nullptr, nullptr, st0) == KVQ_E_INVAL);
+    CHECK(kvq_quantize(qjl, 0, x.p, B, H, T, codes.as<uint8_t>(), norms.as<float>(), signs.as<uint8_t>(), gamma.as<float>(), st0) == KVQ_OK);
+    CHECK(kvq_quantize(qjl, 1, x.p, B, H, T, codes.as<uint8_t>(), norms.as<float>(), signs.as<uint8_t>(), gamma.as<float>(), st0) == KVQ_E_INVAL);
+    CHECK(kvq_quantize(dense, 0, x.p, B, H, T, codes.as<uint8_t>(), norms.as<float>(), nullptr, nullptr, st0) == KVQ_OK);
+    CHECK(std::strcmp(g_last.what, "quantize_dense") == 0 && g_last.a == B * H * T);
+    CHECK(kvq_quantize_kv(mse, x.p, x.p, B, H, T, codes.as<uint8_t>(), norms.as<float>(), codes.as<uint8_t>(), norms.as<float>(), st0) == KVQ_OK);
+    CHECK(kvq_quantize_kv(qjl, x.p, x.p, B, H, T, codes.as<uint8_t>(), norms.as<float>(), codes.as<uint8_t>(), norms.as<float>(), st0) == KVQ_E_INVAL);
+
+    // logits: group sizes 1, 2, 4, 8 are built; 3 is not; 6 heads do not divide
+    for (int G : {1, 2, 4, 8})
+        CHECK(kvq_logits(mse, q.p, B, H * G, T, codes.as<uint8_t>(), norms.as<float>(), nullptr, nullptr, lg.as<float>(), st0) == KVQ_OK);
+    CHECK(kvq_logits(mse, q.p, B, H * 3, T, codes.as<uint8_t>(), norms.as<float>(), nullptr, nullptr, lg.as<float>(), st0) == KVQ_E_UNSUPPORTED);
+    CHECK(kvq_logits(mse, q.p, B, 6, T, codes.as<uint8_t>(), norms.as<float>(), nullptr, nullptr, lg.as<float>(), st0) == KVQ_E_INVAL);
+    CHECK(kvq_logits(qjl, q.p, B, Hq, T, codes.as<uint8_t>(), norms.as<float>(), nullptr, nullptr, lg.as<float>(), st0) == KVQ_E_INVAL);
+    CHECK(kvq_logits(qjl, q.p, B, Hq, T, codes.as<uint8_t>(), norms.as<float>(), signs.as<uint8_t>(), gamma.as<float>(), lg.as<float>(), st0) == KVQ_OK);
+
+    // decode: workspace sizes, split clamping, group sizes
+    const size_t wsb = kvq_attn_decode_ws_bytes(mse, B, Hq, T);
+    CHECK(wsb > 0 && kvq_attn_decode_ws_bytes(nullptr, B, Hq, T) == 0);
+    Buf ws(wsb);
+    CHECK(kvq_attn_decode(mse, q.p, B, Hq, T, codes.as<uint8_t>(), norms.as<float>(), codes.as<uint8_t>(), norms.as<float>(), 0.f, out.as<float>(), ws.p, wsb - 1, st0) == KVQ_E_WORKSPACE);
+    CHECK(kvq_attn_decode(mse, q.p, B, Hq, T, codes.as<uint8_t>(), norms.as<float>(), codes.as<uint8_t>(), norms.as<float>(), 0.f, out.as<float>(), ws.as<char>(16), wsb, st0) == KVQ_E_INVAL);
+    CHECK(kvq_attn_decode(mse, q.p, B, Hq, T, codes.as<uint8_t>(), norms.as<float>(), codes.as<uint8_t>(), norms.as<float>(), -1.f, out.as<float>(), ws.p, wsb, st0) == KVQ_E_INVAL);
+    CHECK(kvq_attn_decode(mse, q.p, B, Hq, T, codes.as<uint8_t>(), norms.as<float>(), codes.as<uint8_t>(), norms.as<float>(), 0.f, out.as<float>(), ws.p, wsb, st0) == KVQ_OK);
+    CHECK(std::strcmp(g_last.what, "decode") == 0 && g_last.n_split >= 1 && g_last.n_split <= (T + 63) / 64);
+    CHECK(kvq_attn_decode_splits(mse, q.p, B, Hq, T, codes.as<uint8_t>(), norms.as<float>(), codes.as<uint8_t>(), norms.as<float>(), 0.f, out.as<float>(), ws.p, wsb, 1000000, st0) == KVQ_OK);
+    CHECK(g_last.n_split == (T + 63) / 64);
+    CHECK(kvq_attn_decode(mse, q.p, B, H * 8, T, codes.as<uint8_t>(), norms.as<float>(), codes.as<uint8_t>(), norms.as<float>(), 0.f, out.as<float>(), ws.p, wsb, st0) == KVQ_E_UNSUPPORTED);
+    CHECK(kvq_attn_decode(mse, q.p, B, Hq, 0, codes.as<uint8_t>(), norms.as<float>(), codes.as<uint8_t>(), norms.as<float>(), 0.f, out.as<float>(), ws.p, wsb, st0) == KVQ_E_INVAL);
+    CHECK(kvq_attn_decode(qjl, q.p, B, Hq, T, codes.as<uint8_t>(), norms.as<float>(), codes.as<uint8_t>(), norms.as<float>(), 0.f, out.as<float>(), ws.p, wsb, st0) == KVQ_E_INVAL);
+
+    // no-allocation decode: split count lowered to fit the fixed scratch, then rejected
+    CHECK(kvq_attn_decode_noalloc(mse, q.p, B, Hq, T, codes.as<uint8_t>(), norms.as<float>(), codes.as<uint8_t>(), norms.as<float>(), 0.f, out.as<float>(), st0) == KVQ_OK);
+    CHECK(std::strcmp(g_last.what, "decode_noalloc") == 0 && g_last.n_split >= 1);
+    {
+        const int64_t Bb = 900;  // 900 x 16 query heads at one split: 7.5 MB of partials, fits
+        Buf qb(Bb * Hq * 256), ob(Bb * Hq * 512);
+        st = kvq_attn_decode_noalloc(mse, qb.p, Bb, Hq, 100000, codes.as<uint8_t>(), norms.as<float>(), codes.as<uint8_t>(), norms.as<float>(), 0.f, ob.as<float>(), st0);
+        CHECK(st == KVQ_OK);
+        const size_t need = ((Bb * H * 4 + 255) / 256) * 256 + (size_t)Bb * Hq * g_last.n_split * 520;
+        CHECK(need <= KVQ_NOALLOC_SCRATCH_BYTES);
+        CHECK(g_last.n_split >= 1);
+    }
+    {
+        const int64_t Bb = 1100;  // 17600 query heads: not even one split fits
+        Buf qb(Bb * Hq * 256), ob(Bb * Hq * 512);
+        CHECK(kvq_attn_decode_noalloc(mse, qb.p, Bb, Hq, 10, codes.as<uint8_t>(), norms.as<float>(), codes.as<uint8_t>(), norms.as<float>(), 0.f, ob.as<float>(), st0) == KVQ_E_WORKSPACE);
+    }
+
+    // streaming cache
+    const int64_t Tcap = T + 100, R = 40, Rcap = 64;
+    const size_t sws = kvq_attn_decode_stream_ws_bytes(mse, B, Hq, Tcap);
+    Buf sw(sws), tail(B * H * Rcap * 256);
+    CHECK(kvq_attn_decode_stream(mse, q.p, B, Hq, T, Tcap, codes.as<uint8_t>(), norms.as<float>(), codes.as<uint8_t>(), norms.as<float>(), R, Rcap, tail.p, tail.p, 0.f, out.as<float>(), sw.p, sws, st0) == KVQ_OK);
+    CHECK(kvq_attn_decode_stream(mse, q.p, B, Hq, Tcap + 1, Tcap, codes.as<uint8_t>(), norms.as<float>(), codes.as<uint8_t>(), norms.as<float>(), R, Rcap, tail.p, tail.p, 0.f, out.as<float>(), sw.p, sws, st0) == KVQ_E_INVAL);
+    CHECK(kvq_attn_decode_stream(mse, q.p, B, Hq, 0, Tcap, nullptr, nullptr, nullptr, nullptr, 0, Rcap, tail.p, tail.p, 0.f, out.as<float>(), sw.p, sws, st0) == KVQ_E_INVAL);
+    CHECK(kvq_attn_decode_stream(dense, q.p, B, Hq, T, Tcap, codes.as<uint8_t>(), norms.as<float>(), codes.as<uint8_t>(), norms.as<float>(), R, Rcap, tail.p, tail.p, 0.f, out.as<float>(), sw.p, sws, st0) == KVQ_E_UNSUPPORTED);
+    CHECK(kvq_flush(mse, tail.p, tail.p, B, H, R, Rcap, codes.as<uint8_t>(), norms.as<float>(), codes.as<uint8_t>(), norms.as<float>(), T, Tcap, st0) == KVQ_OK);
+    CHECK(kvq_flush(mse, tail.p, tail.p, B, H, R, Rcap, codes.as<uint8_t>(), norms.as<float>(), codes.as<uint8_t>(), norms.as<float>(), Tcap - R + 1, Tcap, st0) == KVQ_E_INVAL);
+
+    // NSN-VQ
+    const size_t nws = kvq_nsn_vq_ws_bytes(nsn, H, T);
+    Buf nw(nws), o(H * 512), s1(H * T * 4);
+    CHECK(kvq_nsn_vq_quantize(nsn, x.p, H, T, codes.as<uint8_t>(), s1.as<float>(), s1.as<float>(), o.as<float>(), nw.p, nws - 4, st0) == KVQ_E_WORKSPACE);
+    CHECK(kvq_nsn_vq_quantize(nsn, x.p, H, T, codes.as<uint8_t>(), s1.as<float>(), s1.as<float>(), o.as<float>(), nw.p, nws, st0) == KVQ_OK);
+    CHECK(kvq_nsn_vq_quantize(mse, x.p, H, T, codes.as<uint8_t>(), s1.as<float>(), s1.as<float>(), o.as<float>(), nw.p, nws, st0) == KVQ_E_INVAL);
+    CHECK(kvq_nsn_logits(nsn, q.p, 1, H * 3, T, codes.as<uint8_t>(), s1.as<float>(), s1.as<float>(), o.as<float>(), lg.as<float>(), st0) == KVQ_E_INVAL);
+    CHECK(kvq_nsn_logits(nsn, q.p, 1, H * 8, T, codes.as<uint8_t>(), s1.as<float>(), s1.as<float>(), o.as<float>(), lg.as<float>(), st0) == KVQ_OK);
+    const size_t ndw = kvq_nsn_attn_decode_ws_bytes(nsn, 1, Hq, T);
+    Buf nd(ndw);
+    CHECK(kvq_nsn_attn_decode(nsn, q.p, 1, Hq, T, codes.as<uint8_t>(), s1.as<float>(), s1.as<float>(), o.as<float>(), codes.as<uint8_t>(), s1.as<float>(), s1.as<float>(), o.as<float>(), 0.f, out.as<float>(), nd.p, ndw, st0) == KVQ_OK);
+    CHECK(g_last.n_split >= 1 && g_last.n_split <= (T + 63) / 64);
+    CHECK(kvq_nsn_attn_decode(nsn, q.p, 1, Hq, T, codes.as<uint8_t>(), s1.as<float>(), s1.as<float>(), o.as<float>(), codes.as<uint8_t>(), s1.as<float>(), s1.as<float>(), o.as<float>(), 0.f, out.as<float>(), nd.p, ndw - 1, st0) == KVQ_E_WORKSPACE);
+
+    for (kvq_ctx *p : all) CHECK(kvq_destroy(p) == KVQ_OK);
+    CHECK(kvq_destroy(qjl) == KVQ_OK && kvq_destroy(nsn) == KVQ_OK && kvq_destroy(dense) == KVQ_OK);
+    CHECK(kvq_destroy(nullptr) == KVQ_OK);
+    std::printf("host ok\n");
+    return 0;
+}
