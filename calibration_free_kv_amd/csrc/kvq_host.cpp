@@ -170,7 +170,6 @@ void free_ctx(kvq_ctx *c)
 {
     if (!c) return;
     (void)hipFree(c->d_sgnmask);
-    (void)hipFree(c->d_sgnmask_h);
     (void)hipFree(c->d_signs);
     (void)hipFree(c->d_S);
     (void)hipFree(c->d_S16);
@@ -313,10 +312,6 @@ kvq_status kvq_create(const kvq_config *cfg, kvq_ctx **out)
             }
         }
         if (st == KVQ_OK) st = upload(&c->d_sgnmask, mask, n);
-        // dwords 32..63 of each head cover coordinates 64..127
-        for (size_t i = 0; st == KVQ_OK && i < n; ++i)
-            if (i % 64 >= 32) mask[i] ^= 0x80008000u;
-        if (st == KVQ_OK) st = upload(&c->d_sgnmask_h, mask, n);
         if (st == KVQ_OK) st = upload(&c->d_signs, sg, 2 * n);
         std::free(mask);
         std::free(sg);

@@ -33,7 +33,6 @@ struct kvq_ctx {
     int n_cu;             // compute units of the device
     kvq::Codebook cb;
     uint32_t *d_sgnmask;  // [2][H][64]: fp16-pair sign masks of D_K, D_V
-    uint32_t *d_sgnmask_h;  // same, masks of coordinates 64..127 also flipping every sign
     float *d_signs;       // [2][H][128]: D_K, D_V as +-1.0f
     int8_t *h_signs;      // host copy [2][H][128] of D_K, D_V (MSE modes)
     float *d_S;           // [128][128] QJL projection transposed, d_S[i][j] = S[j][i] (MSE_QJL)

@@ -173,55 +173,44 @@ __device__ __forceinline__ TileGeom geom(uint32_t tile, const TileMap &mp)
 }
 
 // LDS image of one wave tile: 32 rows of 16 chunks (16 bytes = 8 coordinates
-// each), then the 64 sign-mask dwords of the tile's head.  Half h of row v
-// (chunks 8h .. 8h+7) sits in slots [16 v + 8 h, 16 v + 8 h + 8), chunk
-// 8h + k at slot 16 v + 8 h + (k ^ m) with m = (v mod 8) ^ 4h.  At each of its
-// eight reads, lane 2v + h asks for slot k ^ m of its half row; over any 8 (or
-// 16) consecutive lanes these fall into distinct 16-byte bank groups, so the
-// half-row reads are free of bank conflicts.
+// each), then the 64 sign-mask dwords of the tile's head.  Chunk c of row v
+// sits in slot 16 v + (c ^ (v mod 16)).  The matrix-core operand read of step
+// s (below) asks lane v + 32 g for chunk 2 s + g of row v: over any 16
+// consecutive lanes these slots fall into 16 distinct 16-byte bank groups, so
+// the reads are free of bank conflicts.
 constexpr int kRowsH = kTileH * 16;   // 16-byte chunks of rows per tile
 constexpr int kBufH = kRowsH + 16;    // + 256 bytes of sign masks
 
 // Direct global -> LDS copy of one tile and its head's sign masks (no VGPR
-// staging).  Row-copy instruction j writes slots [64 j, 64 j + 64) of the
-// buffer, lane l at slot 64 j + l: vector v = 4 j + l/16, slot q = l % 16 of
-// its row, i.e. half h = q/8 and chunk 8h + ((q mod 8) ^ m).  Each such
-// instruction reads one contiguous KiB (four whole rows).  The chunk depends
-// on j only through j mod 2, so the address is a wave-uniform base plus one
-// of two per-lane offsets.  A ninth instruction copies the 64 mask dwords.
+// staging).  Row-copy instruction j writes slots [64 j, 64 j + 64), lane l at
+// slot 64 j + l: row v = 4 j + l/16 and chunk (l mod 16) ^ (v mod 16).  Each
+// instruction reads one contiguous KiB (four whole rows); the chunk depends on
+// j only through j mod 4, so the address is a wave-uniform base plus one of
+// four per-lane offsets.  A ninth instruction copies the 64 mask dwords.
 // Every call issues exactly 9 load instructions with all lanes active (waits
 // count them); rows past a ragged tail re-read the last valid row, and are
 // never stored.
-__device__ __forceinline__ int half_chunk(int v, int q)
-{
-    const int h = q >> 3;
-    return 8 * h + ((q & 7) ^ ((v & 7) ^ (4 * h)));
-}
-
 __device__ __forceinline__ void tile_to_lds(const u4_t *src, int nv, const uint32_t *msk, u4_t *L, int lane)
 {
     // lane is made opaque so that the offsets are recomputed here (a few
     // VALU ops) rather than hoisted out of the persistent loop and spilled
     asm volatile("" : "+v"(lane));
+    const int r = lane >> 4, q = lane & 15;
     if (nv == kTileH) {
-        uint32_t off[2];
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            const int v = 4 * p + (lane >> 4);
-            off[p] = (uint32_t)((lane >> 4) * 16 + half_chunk(v, lane & 15));
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t off = (uint32_t)(16 * r + (q ^ ((4 * j + r) & 15)));
             __builtin_amdgcn_global_load_lds(
-                (const __attribute__((address_space(1))) void *)(src + 64 * j + off[j & 1]),
+                (const __attribute__((address_space(1))) void *)(src + 64 * j + off),
                 (__attribute__((address_space(3))) void *)(L + j * 64), 16, 0, 0);
+        }
     } else {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const int v = 4 * j + (lane >> 4);
+            const int v = 4 * j + r;
             const int row = v < nv ? v : nv - 1;
             __builtin_amdgcn_global_load_lds(
-                (const __attribute__((address_space(1))) void *)(src + row * 16 + half_chunk(v, lane & 15)),
+                (const __attribute__((address_space(1))) void *)(src + row * 16 + (q ^ (v & 15))),
                 (__attribute__((address_space(3))) void *)(L + j * 64), 16, 0, 0);
         }
     }
@@ -229,30 +218,31 @@ __device__ __forceinline__ void tile_to_lds(const u4_t *src, int nv, const uint3
                                      (__attribute__((address_space(3))) void *)(L + kRowsH), 4, 0, 0);
 }
 
-// Wait for the wave's tile copy, read half row h of vector v into w (lane
-// 2v + h) and apply the signs of D.  Also draws the wave's next ticket from
-// the workgroup's LDS counter: the atomic goes out with the row reads, after
-// the copy has landed (the compiler makes any LDS access wait for all copies
-// into LDS that are still in flight).
+// Wait for the wave's tile copy and read the operand of the transform: lane
+// v + 32 g takes chunks 2 s + g (coordinates 16 s + 8 g .. + 7) of row v for
+// s = 0..7 into w[4 s .. 4 s + 3], with the signs of D applied.  Also draws
+// the wave's next ticket from the workgroup's LDS counter: the atomic goes out
+// with the row reads, after the copy has landed (the compiler makes any LDS
+// access wait for all copies into LDS that are still in flight).
 template <int N>
 __device__ __forceinline__ int take_rows(const u4_t *L, int lane, uint32_t *w, int *counter)
 {
     // the row reads stay after the preceding arithmetic: moved up into it
-    // they would hold 32 more VGPRs live through the transform
+    // they would hold 32 more VGPRs live through the encode
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("" : "+v"(lane));  // addresses recomputed per tile, not hoisted and spilled
     wait_vm_n<N>();
-    const int v = lane >> 1, h = lane & 1;
-    const int b = 16 * v + 8 * h + ((v & 7) ^ (4 * h));  // slot of chunk k: b ^ k
-    const u4_t *M = L + kRowsH + 8 * h;
+    const int v = lane & 31, g = lane >> 5;
+    const int b = 16 * v + (g ^ (v & 15));  // slot of step s: b ^ 2 s
+    const u4_t *M = L + kRowsH + g;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        const u4_t x = L[b ^ k];
-        const u4_t m = M[k];
-        w[4 * k + 0] = x.x ^ m.x;
-        w[4 * k + 1] = x.y ^ m.y;
-        w[4 * k + 2] = x.z ^ m.z;
-        w[4 * k + 3] = x.w ^ m.w;
+    for (int s = 0; s < 8; ++s) {
+        const u4_t x = L[b ^ (2 * s)];
+        const u4_t m = M[2 * s];
+        w[4 * s + 0] = x.x ^ m.x;
+        w[4 * s + 1] = x.y ^ m.y;
+        w[4 * s + 2] = x.z ^ m.z;
+        w[4 * s + 3] = x.w ^ m.w;
     }
     int t = 0;
     if (lane == 0) t = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -261,33 +251,41 @@ __device__ __forceinline__ int take_rows(const u4_t *L, int lane, uint32_t *w, i
     return __builtin_amdgcn_readfirstlane(t);
 }
 
-// The value of x in the other lane of the pair (lanes 2v, 2v + 1).
-__device__ __forceinline__ float pair_swap(float x)
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef float f16_t __attribute__((ext_vector_type(16)));
+
+// Swap of lanes 32..63 of x with lanes 0..31 of y (gfx950): returns
+// (x', y') with x' = [x_lo | y_lo] and y' = [x_hi | y_hi].
+__device__ __forceinline__ void swap_halves(float &x, float &y)
 {
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, y),
+                                                    false, false);
+    x = __builtin_bit_cast(float, (unsigned)r[0]);
+    y = __builtin_bit_cast(float, (unsigned)r[1]);
 }
 
-// y[i] += c * (y[i] of the other lane of the pair), i = 0..7, as one
-// v_fmac_f32 with a DPP source each (the compiler keeps the lane swap as a
-// separate move).  Every read of y[i] in the block happens before any lane
-// writes it, and each instruction reads a register no earlier instruction of
-// the block wrote; the leading s_nop 4 provides the wait states a DPP source
-// needs after a VALU write of that register (2) or a write of EXEC (5) by the
-// code before the block.
-__device__ __forceinline__ void pair_fmac8(float *y, float c)
+// A operand of the transform (v_mfma_f32_32x32x16_f16, rows = 32 outputs,
+// k = 16 inputs): block (mb, s) of the Sylvester matrix, rows 32 mb + r,
+// columns 16 s + k.  With r = 16 r1 + r0, s = 2 s1 + s0, its entries are
+// (-1)^popcount(mb & s1) (-1)^(r1 s0) H16[r0][k], so every block is one of
+// two fixed fragments F_s0 up to the sign (-1)^popcount(mb & s1), which is
+// applied to the other operand instead.  Lane l holds row l mod 32 and
+// k = 8 (l / 32) .. + 7 as fp16 +-1.
+__device__ __forceinline__ h8_t hadamard_fragment(int lane, int s0)
 {
-    asm volatile(
-        "s_nop 4\n\t"
-        "v_fmac_f32_dpp %0, %0, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %1, %1, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %2, %2, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %3, %3, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %4, %4, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %5, %5, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %6, %6, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %7, %7, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf"
-        : "+v"(y[0]), "+v"(y[1]), "+v"(y[2]), "+v"(y[3]), "+v"(y[4]), "+v"(y[5]), "+v"(y[6]), "+v"(y[7])
-        : "v"(c));
+    const int r = lane & 31, r0 = r & 15, r1 = r >> 4, k0 = 8 * (lane >> 5);
+    uint32_t d[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        uint32_t v = 0;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int neg = (__builtin_popcount(r0 & (k0 + 2 * p + e)) + r1 * s0) & 1;
+            v |= (neg ? 0xBC00u : 0x3C00u) << (16 * e);
+        }
+        d[p] = v;
+    }
+    return __builtin_bit_cast(h8_t, u4_t{d[0], d[1], d[2], d[3]});
 }
 
 // One workgroup of 16 waves per CU (four per SIMD) owns every G-th tile (G =
@@ -312,13 +310,21 @@ struct QArgs {
     int kind[2];  // K (0) or V (1): selects the random signs of each tensor
 };
 
-// sgnh: sign masks [2][H][64] of D_K and D_V as fp16-pair XOR masks, with the
-// masks of coordinates 64..127 also flipping every sign: the upper lane of a
-// pair transforms -x[64..127], which lets one FMA form both outputs of the
-// cross-lane butterfly stage (lower lane: a - (-b), upper lane: -b + a).
+// The rotation y = H (D .* x) of the tile's 32 vectors is one 128 x 128 x 32
+// product on the matrix cores: 32 v_mfma_f32_32x32x16_f16 with the fp16
+// inputs (signs of D applied) as the B operand, columns = vectors, and the
+// +-1 Hadamard blocks as A.  Products of fp16 values and +-1 are exact and
+// are summed in fp32, as accurate as the butterfly network in fp32 registers.
+// Output block mb (coordinates 32 mb .. + 31) leaves lane v + 32 g with
+// coordinates 32 mb + 8 q + 4 g + e (q, e = 0..3) of vector v in register
+// 4 q + e; one lane swap per register pair of blocks (0, 2) and (1, 3) gives
+// lane v + 32 h all coordinates [64 h, 64 h + 64) of vector v, local
+// coordinate 32 a + 8 q + 4 f + e in block a + 2 f, register 4 q + e.
+//
+// sgn: sign masks [2][H][64] of D_K and D_V as fp16-pair XOR masks.
 template <int BITS>
 __global__ __launch_bounds__(kWavesQ * 64) __attribute__((amdgpu_waves_per_eu(4, 4))) void k_quantize(
-    QArgs a, const uint32_t *__restrict__ sgnh, HalfThresholds ht, TileMap mp,
+    QArgs a, const uint32_t *__restrict__ sgn, HalfThresholds ht, TileMap mp,
     int64_t n_tiles, int n_tensors)
 {
     __shared__ u4_t lds[kWavesQ][kBufH];  // 132 KiB
@@ -337,10 +343,9 @@ __global__ __launch_bounds__(kWavesQ * 64) __attribute__((amdgpu_waves_per_eu(4,
     auto issue = [&](int64_t t) {
         const int k = t >= n_tiles;
         const TileGeom gg = geom<kTileH>((uint32_t)(t - k * n_tiles), mp);
-        tile_to_lds(a.x[k] + gg.v0 * 16, gg.nv, sgnh + (a.kind[k] * (int)mp.H + gg.h) * 64, L, lane);
+        tile_to_lds(a.x[k] + gg.v0 * 16, gg.nv, sgn + (a.kind[k] * (int)mp.H + gg.h) * 64, L, lane);
     };
-    // cross-lane stage: lower lane a - (-b) = a + b, upper lane -b + a = a - b
-    const float cross = (lane & 1) ? 1.0f : -1.0f;
+    const h8_t F0 = hadamard_fragment(lane, 0), F1 = hadamard_fragment(lane, 1);
     uint32_t w[32];
     issue(tile);
     int64_t next = blockIdx.x + take_rows<0>(L, lane, w, &next_tile) * G;
@@ -351,56 +356,64 @@ __global__ __launch_bounds__(kWavesQ * 64) __attribute__((amdgpu_waves_per_eu(4,
         const int kt = tile >= n_tiles;
         const TileGeom g = geom<kTileH>((uint32_t)(tile - kt * n_tiles), mp);
 
-        // ||x||^2 of the half row with fp16 products (exact in fp32)
-        // accumulated in fp32; D is already applied (signs do not change it).
+        // ||x||^2 of the lane's 64 coordinates with fp16 products (exact in
+        // fp32) accumulated in fp32; D is already applied (signs do not change it).
         float ss = 0.0f;
 #pragma unroll
         for (int k = 0; k < 32; ++k) {
             const h2_t p = __builtin_bit_cast(h2_t, w[k]);
             ss = __builtin_amdgcn_fdot2(p, p, ss, false);
         }
-        // First butterfly stage fused with the fp16 -> fp32 widening, then the
-        // other in-lane stages (strides 2 .. 32).
-        float y[64];
+        // y = H (D .* x): block mb accumulates sign(mb, s1) F_s0 . B_s over
+        // the eight steps s, the sign applied to B (fp16 sign bits).
+        f16_t acc[4] = {};
 #pragma unroll
-        for (int k = 0; k < 32; ++k) {
-            y[2 * k] = pair_sum(w[k]);
-            y[2 * k + 1] = pair_diff(w[k]);
-        }
+        for (int s = 0; s < 8; ++s) {
+            const u4_t bp = u4_t{w[4 * s], w[4 * s + 1], w[4 * s + 2], w[4 * s + 3]};
+            const u4_t bn = bp ^ 0x80008000u;
+            const h8_t F = (s & 1) ? F1 : F0;
 #pragma unroll
-        for (int s = 2; s < 64; s <<= 1) {
-#pragma unroll
-            for (int i = 0; i < 64; i += 2 * s) {
-#pragma unroll
-                for (int j = i; j < i + s; ++j) {
-                    const float p = y[j], q = y[j + s];
-                    y[j] = p + q;
-                    y[j + s] = p - q;
-                }
+            for (int mb = 0; mb < 4; ++mb) {
+                const bool neg = __builtin_popcount(mb & (s >> 1)) & 1;
+                acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(F, __builtin_bit_cast(h8_t, neg ? bn : bp),
+                                                                 acc[mb], 0, 0, 0);
             }
         }
-        // Stride-64 stage across the lane pair.
-#pragma unroll
-        for (int i = 0; i < 64; i += 8) pair_fmac8(y + i, cross);
-        // Both lanes form the same sum (fp32 addition commutes).
-        ss += pair_swap(ss);
+        // Both lanes of a vector form the same sum (fp32 addition commutes).
+        {
+            float o = ss, p = ss;
+            swap_halves(o, p);  // o: lanes 32..63 now hold lanes 0..31; p: lanes 0..31 hold 32..63
+            ss = (lane < 32 ? p : o) + ss;
+        }
         // The copy of the tile after next goes out here, half an encode
         // before its wait: issued a whole encode ahead, the copies of all
         // waves kept about twice the data in flight that the memory system
         // needs to stay busy, and every request waited correspondingly longer
         // in its queues (which shows at the start and at the end of the grid).
-        // At b = 4 the register held for it over the transform costs spills,
-        // and the copy goes out right after the row reads instead.
+        // At b = 4 the register held for it costs spills, and the copy goes
+        // out right after the row reads instead.
         if constexpr (kMidIssue) {
             if (pending < total) issue(pending);
             pending = total;
         }
+        // lane v + 32 h: coordinates [64 h, 64 h + 64) of vector v
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float x0 = acc[0][r], x2 = acc[2][r];
+            swap_halves(x0, x2);
+            acc[0][r] = x0;
+            acc[2][r] = x2;
+            float x1 = acc[1][r], x3 = acc[3][r];
+            swap_halves(x1, x3);
+            acc[1][r] = x1;
+            acc[3][r] = x3;
+        }
 
         const float rho = __builtin_sqrtf(ss);
-        const float r = rho > 0.0f ? rho : 1.0f;  // zero vector: y = 0 -> index L/2 - 1
+        const float rr = rho > 0.0f ? rho : 1.0f;  // zero vector: y = 0 -> index L/2 - 1
         float P[8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) P[k] = ht.p[k] * r;
+        for (int k = 0; k < 8; ++k) P[k] = ht.p[k] * rr;
 
         // Emit this lane's 64 BITS-bit indices (bits [64 BITS h, 64 BITS (h+1))
         // of the vector's LSB-first stream) from the last bit backwards: local
@@ -410,8 +423,10 @@ __global__ __launch_bounds__(kWavesQ * 64) __attribute__((amdgpu_waves_per_eu(4,
         for (int k = 0; k < 2 * BITS; ++k) out[k] = 0u;
 #pragma unroll
         for (int i = 63; i >= 0; --i) {
+            // local coordinate i = 32 a + 8 q + 4 f + e: block a + 2 f, register 4 q + e
+            const float yi = acc[(i >> 5) + 2 * ((i >> 2) & 1)][4 * ((i >> 3) & 3) + (i & 3)];
             uint64_t M[BITS];
-            index_bits<BITS>(y[i], P, M);
+            index_bits<BITS>(yi, P, M);
             const int lo = (BITS * i) >> 5, hi = (BITS * i + BITS - 1) >> 5;
             if constexpr (BITS == 1) {
                 out[lo] = append_bit(out[lo], M[0]);
@@ -442,12 +457,13 @@ __global__ __launch_bounds__(kWavesQ * 64) __attribute__((amdgpu_waves_per_eu(4,
             else if (after < total)
                 issue(after);
         }
-        if ((lane >> 1) < g.nv) {  // lanes past a ragged tail encoded stale rows
-            // the lanes of the tile write 64 * 8 BITS contiguous bytes
-            uint2 *dst = (uint2 *)(a.codes[kt] + g.v0 * BITS) + lane * BITS;
+        const int v = lane & 31, h = lane >> 5;
+        if (v < g.nv) {  // lanes past a ragged tail encoded stale rows
+            // the lanes of the tile write its 32 records (half h of record v)
+            uint2 *dst = (uint2 *)(a.codes[kt] + g.v0 * BITS) + (2 * v + h) * BITS;
 #pragma unroll
             for (int q = 0; q < BITS; ++q) dst[q] = make_uint2(out[2 * q], out[2 * q + 1]);
-            if (!(lane & 1)) a.norms[kt][g.v0 + (lane >> 1)] = rho;
+            if (h == 0) a.norms[kt][g.v0 + v] = rho;
         }
         if (!has_next) break;
         tile = next;
@@ -475,9 +491,7 @@ __global__ __launch_bounds__(kWavesQ * 64) __attribute__((amdgpu_waves_per_eu(4,
 // into sign bits with wave ballots; each key's 16-bit chunks are gathered on
 // the scalar unit and written into its own lane with v_writelane.
 // ---------------------------------------------------------------------------
-typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
-typedef float f16_t __attribute__((ext_vector_type(16)));
 
 struct QjlArgs {
     const u4_t *x;
@@ -623,16 +637,6 @@ __device__ __forceinline__ int qjl_take_rows(const u4_t *L, int lane, uint32_t *
     wait_lgkm();
     __builtin_amdgcn_wave_barrier();
     return __builtin_amdgcn_readfirstlane(t);
-}
-
-// Swap of lanes 32..63 of x with lanes 0..31 of y (gfx950): returns
-// (x', y') with x' = [x_lo | y_lo] and y' = [x_hi | y_hi].
-__device__ __forceinline__ void swap_halves(float &x, float &y)
-{
-    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, y),
-                                                    false, false);
-    x = __builtin_bit_cast(float, (unsigned)r[0]);
-    y = __builtin_bit_cast(float, (unsigned)r[1]);
 }
 
 // Append the BITS-bit indices of 32 coordinates y[0..31] (LSB-first stream of
@@ -894,7 +898,7 @@ hipError_t run(const kvq_ctx *ctx, const QArgs &a, int n_tensors, int64_t B, int
     if (blocks > (int64_t)ctx->n_cu) blocks = ctx->n_cu;
     if (n_tiles * n_tensors >= (int64_t)1 << 31) return hipErrorInvalidValue;  // 32-bit tile indices
     hipLaunchKernelGGL(k_quantize<BITS>, dim3((unsigned)blocks), dim3(kWavesQ * 64), 0, s, a,
-                       (const uint32_t *)ctx->d_sgnmask_h, ht, make_map(T, ctx->H, tiles_per_bh), n_tiles,
+                       (const uint32_t *)ctx->d_sgnmask, ht, make_map(T, ctx->H, tiles_per_bh), n_tiles,
                        n_tensors);
     return hipGetLastError();
 }
