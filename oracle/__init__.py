@@ -87,7 +87,7 @@ def _setup(L):
                                        C.c_double, _D]
     L.kvqo_qjl.argtypes = [C.c_int, C.c_int, i64, _D, _I32, _F, _D, C.c_double, _U8, _D, _U8]
     L.kvqo_nsn_vq.argtypes = [C.c_int, C.c_int, C.c_int, i64, i64, _D, _D, C.c_double, _U8, _D,
-                              _D, _D, _D, _U8, _D]
+                              _D, _D, _D, _U8, _D, C.c_int]
     L.kvqo_nsn_reconstruct.argtypes = [C.c_int, _D, C.c_double, C.c_double, _D, _D]
     L.kvqo_nsn_logits.argtypes = [C.c_int, C.c_int, C.c_int, i64, i64, i64, i64, _D, _U8, _D, _D, _D,
                                   _D, _D]
@@ -426,9 +426,10 @@ def qjl(y, idx, S, bits: int, band: float = BAND):
                 flags=fl.reshape(lead + (m,)))
 
 
-def nsn_vq(x, codebook, band: float = BAND, want_z: bool = False, o_given=None):
+def nsn_vq(x, codebook, band: float = BAND, want_z: bool = False, o_given=None, adaptive: bool = False):
     """x [H,T,d]; codebook [K, sub] -> dict(codes [H,T,d/sub], s1, s2 [H,T], o [H,d], flags).
-    o_given [H,d]: use this mean instead of the mean of the T tokens passed."""
+    o_given [H,d]: use this mean instead of the mean of the T tokens passed.
+    adaptive: s2 carries the adaptive scale alpha = ||z||^2 / <z, zq>."""
     x = _f64(x)
     H, T, d = x.shape
     cb = _f64(codebook)
@@ -441,7 +442,8 @@ def nsn_vq(x, codebook, band: float = BAND, want_z: bool = False, o_given=None):
     fl = np.zeros((H, T, d // sub), np.uint8)
     og = None if o_given is None else _f64(o_given)
     _chk(lib().kvqo_nsn_vq(d, sub, K, H, T, _p(x, _D), _p(cb, _D), band, _p(codes, _U8),
-                           _p(s1, _D), _p(s2, _D), _p(o, _D), _p(z, _D), _p(fl, _U8), _p(og, _D)))
+                           _p(s1, _D), _p(s2, _D), _p(o, _D), _p(z, _D), _p(fl, _U8), _p(og, _D),
+                           int(adaptive)))
     out = dict(codes=codes, s1=s1, s2=s2, o=o, flags=fl)
     if want_z:
         out["z"] = z

@@ -844,12 +844,18 @@ ORC_API int kvqo_qjl(int d, int m, int64_t n, const double *y, const int32_t *id
 /* a_t = 0; s2_t = 0 gives xt_t = 0.                                          */
 /* o_given: NULL, or a mean [H, d] to use instead of the mean of these T      */
 /* tokens (to encode a sample of a longer sequence).                         */
+/* adaptive: 1 for the adaptive scale (NSNQuant, Metodologia sec. 3, "Ajuste  */
+/* de Escala": the quantised vector is scaled so that its component along    */
+/* the original is preserved): zq = the selected entries, alpha =            */
+/* ||z||^2 / <z, zq> (1 when <z, zq> <= 0), and the returned s2 is           */
+/* alpha * s2, so that s1 (s2 H zq / sqrt(d) + o) reconstructs with the       */
+/* scaled zq and every other use of the byproducts is unchanged.            */
 /* ------------------------------------------------------------------------ */
 
 ORC_API int kvqo_nsn_vq(int d, int sub, int K, int64_t H, int64_t T, const double *x,
                         const double *codebook, double band, uint8_t *codes, double *s1,
                         double *s2, double *o, double *z_out, uint8_t *flags,
-                        const double *o_given)
+                        const double *o_given, int adaptive)
 {
     if (d % sub || T <= 0) return -1;
     const int nsub = d / sub;
@@ -911,6 +917,17 @@ ORC_API int kvqo_nsn_vq(int d, int sub, int K, int64_t H, int64_t T, const doubl
                     }
                     flags[(h * T + t) * nsub + s] = (uint8_t)(mind < band);
                 }
+            }
+            if (adaptive) {
+                double zz = 0.0, zq = 0.0;
+                for (int s = 0; s < nsub; ++s) {
+                    const int c = codes[(h * T + t) * nsub + s];
+                    for (int k = 0; k < sub; ++k) {
+                        zz += z[s * sub + k] * z[s * sub + k];
+                        zq += z[s * sub + k] * codebook[c * sub + k];
+                    }
+                }
+                if (zq > 0.0) s2[h * T + t] *= zz / zq;
             }
         }
     }

@@ -51,7 +51,7 @@ int kvqo_qjl(int d, int m, int64_t n, const double *y, const int32_t *idx, const
              double band, uint8_t *sgn, double *gamma, uint8_t *flags);
 int kvqo_nsn_vq(int d, int sub, int K, int64_t H, int64_t T, const double *x, const double *codebook, double band,
                 uint8_t *codes, double *s1, double *s2, double *o, double *z_out, uint8_t *flags,
-                const double *o_given);
+                const double *o_given, int adaptive);
 void kvqo_nsn_reconstruct(int d, const double *zq, double s1, double s2, const double *o, double *x_hat);
 int kvqo_nsn_logits(int route, int d, int sub, int64_t B, int64_t Hq, int64_t Hkv, int64_t T, const double *q,
                     const uint8_t *codes, const double *s1, const double *s2, const double *o, const double *cb,
@@ -158,8 +158,9 @@ int main(void)
     uint8_t *codes = zalloc((size_t)nv * (d / sub)), *fl = zalloc((size_t)nv * (d / sub));
     double *s1 = zalloc(sizeof(double) * nv), *s2 = zalloc(sizeof(double) * nv), *o = zalloc(sizeof(double) * B * H * d);
     double *z = zalloc(sizeof(double) * nv * d);
-    CHECK(kvqo_nsn_vq(d, sub, K, B * H, T, x, cbk, 1e-5, codes, s1, s2, o, z, fl, NULL) == 0);
-    CHECK(kvqo_nsn_vq(d, sub, K, B * H, T, x, cbk, 1e-5, codes, s1, s2, o, NULL, NULL, o) == 0);
+    CHECK(kvqo_nsn_vq(d, sub, K, B * H, T, x, cbk, 1e-5, codes, s1, s2, o, z, fl, NULL, 0) == 0);
+    CHECK(kvqo_nsn_vq(d, sub, K, B * H, T, x, cbk, 1e-5, codes, s1, s2, o, z, fl, NULL, 1) == 0);
+    CHECK(kvqo_nsn_vq(d, sub, K, B * H, T, x, cbk, 1e-5, codes, s1, s2, o, NULL, NULL, o, 1) == 0);
     double xh[128];
     kvqo_nsn_reconstruct(d, z, s1[0], s2[0], o, xh);
     double *lg = zalloc(sizeof(double) * B * Hq * T), *att = zalloc(sizeof(double) * B * Hq * d);
