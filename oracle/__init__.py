@@ -95,6 +95,8 @@ def _setup(L):
                                      _D, _D, _D, _D, C.c_double, _D]
     L.kvqo_kmeans.argtypes = [i64, C.c_int, C.c_int, _D, _I64, C.c_int, _D, _D]
     L.kvqo_kmeans.restype = C.c_int
+    L.kvqo_cosine_refine.argtypes = [i64, C.c_int, C.c_int, _D, _D, C.c_int, _D]
+    L.kvqo_cosine_refine.restype = C.c_int
 
 
 def _p(a, ty):
@@ -506,3 +508,14 @@ def kmeans(samples, init_idx, max_iter: int = 100):
     it = lib().kvqo_kmeans(n, dim, K, _p(s, _D), _p(init_idx, _I64), max_iter, _p(cb, _D),
                            _p(dist, _D))
     return cb, dist[:it], it
+
+
+def cosine_refine(samples, codebook, passes: int = 10):
+    """Cosine refinement of a codebook; returns (codebook, mean cosine per pass)."""
+    s = _f64(samples)
+    n, dim = s.shape
+    cb = _f64(codebook).copy()
+    mc = np.zeros(passes)
+    it = lib().kvqo_cosine_refine(n, dim, cb.shape[0], _p(s, _D), _p(cb, _D), passes, _p(mc, _D))
+    return cb, mc[:it]
+

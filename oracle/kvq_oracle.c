@@ -1127,3 +1127,89 @@ ORC_API int kvqo_kmeans(int64_t n, int dim, int K, const double *samples, const 
     free(cnt);
     return it;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Cosine refinement of a codebook (NSNQuant, Metodologia sec. 3: the k-means */
+/* codebook on standard-normal samples is refined to minimise the cosine     */
+/* distance between the vectors and their quantised versions).  Reading:     */
+/* each pass assigns every sample to its nearest entry (squared Euclidean    */
+/* distance, lowest index on ties: the quantiser in use), then moves each     */
+/* entry to the direction u = sum over its cell of x / ||x|| (the direction  */
+/* that maximises the cell's summed cosine similarity), with the length that */
+/* is least-squares optimal along u, mean over the cell of <x, u>.  Entries  */
+/* with an empty cell, or a zero direction sum, are kept.  mean_cos[i] is the */
+/* mean cosine similarity of the samples with their entries at the           */
+/* assignment of pass i (zero samples count as 1).  Returns the passes run.  */
+/* ------------------------------------------------------------------------ */
+
+ORC_API int kvqo_cosine_refine(int64_t n, int dim, int K, const double *samples, double *codebook, int passes,
+                               double *mean_cos)
+{
+    int32_t *asg = (int32_t *)malloc(sizeof(int32_t) * n);
+    double *usum = (double *)malloc(sizeof(double) * K * dim);
+    double *proj = (double *)malloc(sizeof(double) * K);
+    int64_t *cnt = (int64_t *)malloc(sizeof(int64_t) * K);
+    int it = 0;
+    for (; it < passes; ++it) {
+        double cs = 0.0;
+        for (int64_t i = 0; i < n; ++i) {
+            const double *x = samples + i * dim;
+            int best = 0;
+            double bd = INFINITY;
+            for (int j = 0; j < K; ++j) {
+                double dd = 0.0;
+                for (int k = 0; k < dim; ++k) {
+                    const double e = x[k] - codebook[j * dim + k];
+                    dd += e * e;
+                }
+                if (dd < bd) { bd = dd; best = j; }
+            }
+            asg[i] = best;
+            double xx = 0.0, cc = 0.0, xc = 0.0;
+            for (int k = 0; k < dim; ++k) {
+                xx += x[k] * x[k];
+                cc += codebook[best * dim + k] * codebook[best * dim + k];
+                xc += x[k] * codebook[best * dim + k];
+            }
+            cs += (xx > 0.0 && cc > 0.0) ? xc / sqrt(xx * cc) : 1.0;
+        }
+        if (mean_cos) mean_cos[it] = cs / (double)n;
+        memset(usum, 0, sizeof(double) * K * dim);
+        memset(cnt, 0, sizeof(int64_t) * K);
+        for (int64_t i = 0; i < n; ++i) {
+            const double *x = samples + i * dim;
+            double xx = 0.0;
+            for (int k = 0; k < dim; ++k) xx += x[k] * x[k];
+            if (xx <= 0.0) continue;
+            const double inv = 1.0 / sqrt(xx);
+            ++cnt[asg[i]];
+            for (int k = 0; k < dim; ++k) usum[asg[i] * dim + k] += x[k] * inv;
+        }
+        for (int j = 0; j < K; ++j) {
+            double uu = 0.0;
+            for (int k = 0; k < dim; ++k) uu += usum[j * dim + k] * usum[j * dim + k];
+            if (cnt[j] == 0 || uu <= 0.0) { proj[j] = -1.0; continue; }
+            const double inv = 1.0 / sqrt(uu);
+            for (int k = 0; k < dim; ++k) usum[j * dim + k] *= inv; /* unit direction */
+            proj[j] = 0.0;
+        }
+        for (int64_t i = 0; i < n; ++i) {
+            const int j = asg[i];
+            if (proj[j] < 0.0) continue;
+            double xu = 0.0;
+            for (int k = 0; k < dim; ++k) xu += samples[i * dim + k] * usum[j * dim + k];
+            proj[j] += xu;
+        }
+        for (int j = 0; j < K; ++j) {
+            if (proj[j] < 0.0) continue;
+            const double len = proj[j] / (double)cnt[j];
+            for (int k = 0; k < dim; ++k) codebook[j * dim + k] = len * usum[j * dim + k];
+        }
+    }
+    free(asg);
+    free(usum);
+    free(proj);
+    free(cnt);
+    return it;
+}
+

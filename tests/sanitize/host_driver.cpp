@@ -83,6 +83,16 @@ int main()
     c = base(3, KVQ_MODE_MSE_QJL, H);
     CHECK(kvq_create(&c, &ctx) == KVQ_E_INVAL);  // no S
     c = base(3, KVQ_MODE_MSE, H);
+    c.nsn_options = KVQ_NSN_ADAPTIVE_SCALE;  // an NSN option outside the NSN mode
+    CHECK(kvq_create(&c, &ctx) == KVQ_E_INVAL);
+    c = base(1, KVQ_MODE_NSN_VQ, H);
+    c.vq_codebook = cb.data();
+    c.nsn_options = 0x40;  // unknown option bit
+    CHECK(kvq_create(&c, &ctx) == KVQ_E_INVAL);
+    c.nsn_options = KVQ_NSN_ADAPTIVE_SCALE;
+    CHECK(kvq_create(&c, &ctx) == KVQ_OK);
+    CHECK(kvq_destroy(ctx) == KVQ_OK);
+    c = base(3, KVQ_MODE_MSE, H);
     c.rotation = KVQ_ROTATION_DENSE;
     c.rot_Q = Qbad.data();
     CHECK(kvq_create(&c, &ctx) == KVQ_E_INVAL);  // not orthogonal

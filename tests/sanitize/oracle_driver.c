@@ -62,6 +62,8 @@ int kvqo_nsn_attention(int d, int sub, int64_t B, int64_t Hq, int64_t Hkv, int64
                        double *out);
 int kvqo_kmeans(int64_t n, int dim, int K, const double *samples, const int64_t *init, int max_iter,
                 double *codebook, double *distortion);
+int kvqo_cosine_refine(int64_t n, int dim, int K, const double *samples, double *codebook, int passes,
+                       double *mean_cos);
 
 static uint64_t rs = 88172645463325252ull;
 static double urand(void)
@@ -174,6 +176,7 @@ int main(void)
     for (int64_t i = 0; i < ns * sub; ++i) smp[i] = nrand();
     for (int i = 0; i < 16; ++i) init[i] = i * 7;
     CHECK(kvqo_kmeans(ns, sub, 16, smp, init, 10, kcb, dist) > 0);
+    CHECK(kvqo_cosine_refine(ns, sub, 16, smp, kcb, 5, dist) == 5);
     free(cbk); free(codes); free(fl); free(s1); free(s2); free(o); free(z); free(lg); free(att); free(smp); free(kcb);
     free(x); free(v); free(sg); free(q); free(S); free(Q);
     printf("oracle ok\n");

@@ -16,8 +16,11 @@ pytestmark = [pytest.mark.gpu, needs_gpu]
 GOLDEN_CB = os.path.join(os.path.dirname(__file__), "golden", "vq_codebook_256x8.txt")
 
 
-def codebook():
-    return np.loadtxt(GOLDEN_CB, dtype=np.float32).reshape(256, 8)
+GOLDEN_CB_COS = os.path.join(os.path.dirname(__file__), "golden", "vq_codebook_256x8_cos.txt")
+
+
+def codebook(path=GOLDEN_CB):
+    return np.loadtxt(path, dtype=np.float32).reshape(256, 8)
 
 
 def run(x, cb):
@@ -129,3 +132,58 @@ def test_nsn_vq_deterministic():
     a, b = run(x, cb), run(x, cb)
     for k in a:
         assert np.array_equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("fp16_exact", [False, True])
+@pytest.mark.parametrize("T", [63, 2049])
+def test_nsn_vq_adaptive_scale(T, fp16_exact):
+    """KVQ_NSN_ADAPTIVE_SCALE: same codes, s2 carries alpha = ||z||^2 / <z, zq>
+    (compared with the oracle's to 1e-5 relative)."""
+    x = synth.make("nsn_vq", T=T)["x"]
+    cb = codebook()
+    if fp16_exact:
+        cb = cb.astype(np.float16).astype(np.float32)
+    ctx = kvq.Context(x.shape[0], 1, mode=kvq.KVQ_MODE_NSN_VQ, vq_codebook=cb,
+                      nsn_options=kvq.KVQ_NSN_ADAPTIVE_SCALE)
+    g = {k: to_np(v) for k, v in ctx.nsn_vq_quantize(torch.from_numpy(x).cuda()).items()}
+    ref = O.nsn_vq(x, cb, want_z=True, adaptive=True)
+    same = g["codes"] == ref["codes"]
+    assert same.all() or (~same <= (ref["flags"] == 1)).all()
+    tok = same.all(-1)  # a boundary flip changes the token's alpha: compare the others
+    np.testing.assert_allclose(g["s2"][tok], ref["s2"][tok], rtol=1e-5, atol=1e-6)
+    np.testing.assert_allclose(g["s1"], ref["s1"], rtol=1e-5, atol=1e-6)
+    plain = O.nsn_vq(x, cb)
+    assert np.mean(g["s2"] / plain["s2"]) > 1.0
+
+
+def test_nsn_vq_adaptive_full_size_sampled():
+    x = synth.make("nsn_vq")["x"]
+    cb = codebook()
+    ctx = kvq.Context(8, 1, mode=kvq.KVQ_MODE_NSN_VQ, vq_codebook=cb, nsn_options=kvq.KVQ_NSN_ADAPTIVE_SCALE)
+    g = {k: to_np(v) for k, v in ctx.nsn_vq_quantize(torch.from_numpy(x).cuda()).items()}
+    a = x.astype(np.float64)
+    nx = np.linalg.norm(a, axis=-1, keepdims=True)
+    o_ref = (np.sqrt(128) * a / np.where(nx > 0, nx, 1)).mean(axis=1)
+    t_sel = np.random.default_rng(2).choice(x.shape[1], 256, replace=False)
+    ref = O.nsn_vq(x[:, t_sel], cb, o_given=o_ref, adaptive=True)
+    tok = (g["codes"][:, t_sel] == ref["codes"]).all(-1)
+    assert tok.mean() > 0.99
+    np.testing.assert_allclose(g["s2"][:, t_sel][tok], ref["s2"][tok], rtol=1e-5, atol=1e-6)
+
+
+@pytest.mark.parametrize("adaptive", [False, True])
+def test_nsn_vq_cosine_refined_codebook(adaptive):
+    """The cosine-refined codebook fixture is an input like any other: codes
+    and byproducts against the oracle with it (all tokens of 8 x 3000)."""
+    x = synth.make("nsn_vq", T=3000)["x"]
+    cb = codebook(GOLDEN_CB_COS)
+    ctx = kvq.Context(8, 1, mode=kvq.KVQ_MODE_NSN_VQ, vq_codebook=cb,
+                      nsn_options=kvq.KVQ_NSN_ADAPTIVE_SCALE if adaptive else 0)
+    g = {k: to_np(v) for k, v in ctx.nsn_vq_quantize(torch.from_numpy(x).cuda()).items()}
+    if not adaptive:
+        print(compare(x, cb, g))
+    else:
+        ref = O.nsn_vq(x, cb, adaptive=True)
+        tok = (g["codes"] == ref["codes"]).all(-1)
+        assert tok.mean() > 0.99
+        np.testing.assert_allclose(g["s2"][tok], ref["s2"][tok], rtol=1e-5, atol=1e-6)
