@@ -251,6 +251,8 @@ kvq_status kvq_create(const kvq_config *cfg, kvq_ctx **out)
     if (cfg->codebook != KVQ_CODEBOOK_GAUSS && cfg->codebook != KVQ_CODEBOOK_BETA) return KVQ_E_INVAL;
     if (cfg->codebook == KVQ_CODEBOOK_BETA && mode == KVQ_MODE_NSN_VQ) return KVQ_E_INVAL;
     if (cfg->rotation != KVQ_ROTATION_HADAMARD && cfg->rotation != KVQ_ROTATION_DENSE) return KVQ_E_INVAL;
+    if (cfg->nsn_options & ~KVQ_NSN_ADAPTIVE_SCALE) return KVQ_E_INVAL;
+    if (cfg->nsn_options && mode != KVQ_MODE_NSN_VQ) return KVQ_E_INVAL;
     if (cfg->rotation == KVQ_ROTATION_DENSE) {
         if (mode != KVQ_MODE_MSE) return KVQ_E_UNSUPPORTED;
         if (!cfg->rot_Q) return KVQ_E_INVAL;
@@ -280,6 +282,7 @@ kvq_status kvq_create(const kvq_config *cfg, kvq_ctx **out)
     c->bits = mode == KVQ_MODE_NSN_VQ ? 1 : cfg->bits;
     c->mode = mode;
     c->rotation = cfg->rotation;
+    c->nsn_options = cfg->nsn_options;
     c->H = H;
     c->device = cfg->device;
     if (hipDeviceGetAttribute(&c->n_cu, hipDeviceAttributeMultiprocessorCount, cfg->device) != hipSuccess ||

@@ -40,6 +40,7 @@ struct kvq_ctx {
     bool S_exact_f16;     // S_lo == 0
     float *d_vq;          // [256][8] fp32 codebook (NSN_VQ scoring)
     int rotation;         // KVQ_ROTATION_*
+    int nsn_options;      // KVQ_NSN_* bits (NSN_VQ)
     float *d_Q;           // [128][128] dense rotation Q, row-major (KVQ_ROTATION_DENSE)
     float *d_Qt;          // its transpose
     _Float16 *d_Q16;      // [2][128][128] fp16 high and low parts of Q

@@ -343,7 +343,13 @@ __device__ __forceinline__ int other_half_i(int x, bool upper)
     return __builtin_bit_cast(int, other_half(__builtin_bit_cast(float, x), upper));
 }
 
-template <bool CB_LO>
+// ADAPT: the adaptive scale (NSNQuant, Metodologia sec. 3, "Ajuste de
+// Escala"): s2 is stored as alpha s2 with alpha = ||z||^2 / <z, zq> = d /
+// <z, zq> (zq the selected entries; alpha = 1 when <z, zq> <= 0), so that the
+// reconstruction s1 (s2 H zq / sqrt(d) + o) preserves the component of the
+// token along itself.  <z, zq> is summed from the exact fp16 hi + lo parts of
+// z and of the entries once the codes are known.
+template <bool CB_LO, bool ADAPT>
 // o: channel means [H][128]
 __global__ __launch_bounds__(kWavesN * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_nsn_vq(
     VqArgs a, const float *__restrict__ o, int64_t T, int H, int64_t tiles_per_h, int64_t n_tiles)
@@ -528,6 +534,7 @@ __global__ __launch_bounds__(kWavesN * 64) __attribute__((amdgpu_waves_per_eu(2,
         // the entry of each sub-vector's best marked score, then the better of
         // the two halves (each searched the other 16 codewords of every block)
         uint32_t code[4] = {0u, 0u, 0u, 0u};
+        float dot = 0.0f;  // <z, zq> of this half's dims (adaptive scale)
 #pragma unroll
         for (int s = 0; s < 16; ++s) {
             const int r = 15 - (int)(__builtin_bit_cast(uint32_t, bm[s]) & 15u);
@@ -536,6 +543,32 @@ __global__ __launch_bounds__(kWavesN * 64) __attribute__((amdgpu_waves_per_eu(2,
             const int oi = other_half_i(bi, upper);
             const int win = (ob > bm[s] || (ob == bm[s] && oi < bi)) ? oi : bi;
             code[s >> 2] |= (uint32_t)win << (8 * (s & 3));
+            if constexpr (ADAPT) {
+                // (z_hi + z_lo) . (c_hi + c_lo) over dims 4h .. 4h+3 as packed
+                // fp16 dot products (exact products, fp32 sums)
+                const u4_t ch = s_cbA[2 * win + h];  // dims 4h .. 4h+3 of the entry (twice)
+                const u2_t zhs = zh[s], zls = zl[s];
+#pragma unroll
+                for (int p = 0; p < 2; ++p) {
+                    const h2_t c2 = __builtin_bit_cast(h2_t, p ? ch.y : ch.x);
+                    dot = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, p ? zhs.y : zhs.x), c2, dot, false);
+                    dot = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, p ? zls.y : zls.x), c2, dot, false);
+                }
+                if constexpr (CB_LO) {
+                    const u2_t cl = s_cbl[2 * win + h];
+#pragma unroll
+                    for (int p = 0; p < 2; ++p) {
+                        const h2_t c2 = __builtin_bit_cast(h2_t, p ? cl.y : cl.x);
+                        dot = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, p ? zhs.y : zhs.x), c2, dot, false);
+                        dot = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, p ? zls.y : zls.x), c2, dot, false);
+                    }
+                }
+            }
+        }
+        float s2v = nb / kSqrtD;
+        if constexpr (ADAPT) {
+            dot += other_half(dot, upper);
+            if (dot > 0.0f) s2v *= (float)kD / dot;
         }
         // The next tile's rows, then the copy of the tile after it, then this
         // tile's stores.  The rows are read only now: held through the search
@@ -550,7 +583,7 @@ __global__ __launch_bounds__(kWavesN * 64) __attribute__((amdgpu_waves_per_eu(2,
             const int64_t t = v0 + v;
             a.codes[t] = u4_t{code[0], code[1], code[2], code[3]};
             a.s1[t] = nx / kSqrtD;
-            a.s2[t] = nb / kSqrtD;
+            a.s2[t] = s2v;
         }
         if (!has_next) break;
         tile = next;
@@ -582,12 +615,16 @@ hipError_t launch_nsn_vq(const kvq_ctx *ctx, const void *x, int64_t H, int64_t T
     // one workgroup per CU, each with at least one tile
     int64_t blocks = n_tiles;
     if (blocks > ctx->n_cu) blocks = ctx->n_cu;
-    if (ctx->vq_exact_f16)
-        hipLaunchKernelGGL(k_nsn_vq<false>, dim3((unsigned)blocks), dim3(kWavesN * 64), 0, s, a, (const float *)o, T,
-                           (int)H, tiles_per_h, n_tiles);
-    else
-        hipLaunchKernelGGL(k_nsn_vq<true>, dim3((unsigned)blocks), dim3(kWavesN * 64), 0, s, a, (const float *)o, T,
-                           (int)H, tiles_per_h, n_tiles);
+    const bool adapt = (ctx->nsn_options & KVQ_NSN_ADAPTIVE_SCALE) != 0;
+#define KVQ_NSN_LAUNCH(LO, AD)                                                                                     \
+    hipLaunchKernelGGL((k_nsn_vq<LO, AD>), dim3((unsigned)blocks), dim3(kWavesN * 64), 0, s, a, (const float *)o, T, \
+                       (int)H, tiles_per_h, n_tiles)
+    if (ctx->vq_exact_f16) {
+        if (adapt) KVQ_NSN_LAUNCH(false, true); else KVQ_NSN_LAUNCH(false, false);
+    } else {
+        if (adapt) KVQ_NSN_LAUNCH(true, true); else KVQ_NSN_LAUNCH(true, false);
+    }
+#undef KVQ_NSN_LAUNCH
     return hipGetLastError();
 }
 

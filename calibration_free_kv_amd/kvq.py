@@ -21,6 +21,7 @@ KVQ_MODE_MSE, KVQ_MODE_MSE_QJL, KVQ_MODE_NSN_VQ = 0, 1, 2
 KVQ_KIND_K, KVQ_KIND_V = 0, 1
 KVQ_CODEBOOK_GAUSS, KVQ_CODEBOOK_BETA = 0, 1
 KVQ_ROTATION_HADAMARD, KVQ_ROTATION_DENSE = 0, 1
+KVQ_NSN_ADAPTIVE_SCALE = 1
 D = 128
 
 EXPORTS = [
@@ -44,7 +45,7 @@ class kvq_config(C.Structure):
         ("seed", C.c_uint64), ("signs_k", C.POINTER(C.c_int8)), ("signs_v", C.POINTER(C.c_int8)),
         ("qjl_S", C.POINTER(C.c_float)), ("vq_codebook", C.POINTER(C.c_float)),
         ("device", C.c_int32), ("codebook", C.c_int32), ("rotation", C.c_int32),
-        ("rot_Q", C.POINTER(C.c_float)),
+        ("rot_Q", C.POINTER(C.c_float)), ("nsn_options", C.c_int32),
     ]
 
 
@@ -140,7 +141,7 @@ class Context:
 
     def __init__(self, n_kv_heads: int, bits: int = 3, signs_k=None, signs_v=None, mode: int = KVQ_MODE_MSE,
                  qjl_S=None, vq_codebook=None, device: int = 0, seed: int = 0, codebook: int = KVQ_CODEBOOK_GAUSS,
-                 rot_Q=None):
+                 rot_Q=None, nsn_options: int = 0):
         self.n_kv_heads, self.bits, self.mode, self.device = n_kv_heads, bits, mode, device
         cfg = kvq_config()
         cfg.d, cfg.bits, cfg.mode, cfg.n_kv_heads, cfg.device = D, bits, mode, n_kv_heads, device
@@ -160,6 +161,7 @@ class Context:
         cfg.vq_codebook = arr(vq_codebook, np.float32, C.c_float)
         cfg.rotation = KVQ_ROTATION_DENSE if rot_Q is not None else KVQ_ROTATION_HADAMARD
         cfg.rot_Q = arr(rot_Q, np.float32, C.c_float)
+        cfg.nsn_options = nsn_options
         h = C.c_void_p()
         _check(lib().kvq_create(C.byref(cfg), C.byref(h)), "kvq_create")
         self.handle = h

@@ -79,6 +79,13 @@ enum { KVQ_CODEBOOK_GAUSS = 0, KVQ_CODEBOOK_BETA = 1 };
  * the same Q for K, V and every head (KVQ_MODE_MSE only; not with the
  * streaming-cache calls). */
 enum { KVQ_ROTATION_HADAMARD = 0, KVQ_ROTATION_DENSE = 1 };
+/* Options of the NSN_VQ mode (bits of kvq_config.nsn_options).
+ * KVQ_NSN_ADAPTIVE_SCALE ([NSN] Metodologia sec. 3, adaptive scale): the
+ * selected entries zq of a token are scaled by alpha = ||z||^2 / <z, zq>
+ * (1 when <z, zq> <= 0), which keeps the component of the reconstruction
+ * along the token exact; alpha is folded into the stored s2 (s2 <- alpha s2),
+ * so the scoring calls use it unchanged. */
+enum { KVQ_NSN_ADAPTIVE_SCALE = 1 };
 
 /* Configuration of a context.  Host arrays are copied by kvq_create.
  *
@@ -108,6 +115,7 @@ typedef struct {
     int32_t codebook;          /* KVQ_CODEBOOK_* (MSE modes; 0 = N(0,1))              */
     int32_t rotation;          /* KVQ_ROTATION_* (0 = randomized Hadamard)            */
     const float *rot_Q;        /* host [d, d] row-major orthogonal Q (ROTATION_DENSE)  */
+    int32_t nsn_options;       /* KVQ_NSN_* bits (NSN_VQ mode; 0 = none)              */
 } kvq_config;
 
 /* Create a context: validates the configuration, builds the b-bit Lloyd-Max
