@@ -82,7 +82,8 @@ def _setup(L):
     L.kvqo_quantize_dense.argtypes = [C.c_int, C.c_int, i64, i64, i64, _D, _D, _F, C.c_double, _U8, _D, _D, _I32,
                                       _U8]
     L.kvqo_dequant_dense.argtypes = [C.c_int, C.c_int, _U8, C.c_double, _D, _F, _D]
-    L.kvqo_logits_dense.argtypes = [C.c_int, C.c_int, C.c_int, i64, i64, i64, i64, _D, _U8, _D, _D, _F, _D]
+    L.kvqo_logits_dense.argtypes = [C.c_int, C.c_int, C.c_int, i64, i64, i64, i64, _D, _U8, _D, _D, _F, _U8, _D,
+                                    _D, C.c_int, _D]
     L.kvqo_attention_dense.argtypes = [C.c_int, C.c_int, i64, i64, i64, i64, _D, _U8, _D, _U8, _D, _D, _F,
                                        C.c_double, _D]
     L.kvqo_qjl.argtypes = [C.c_int, C.c_int, i64, _D, _I32, _F, _D, C.c_double, _U8, _D, _U8]
@@ -382,15 +383,25 @@ def dequant_dense(rec, rho, Q, bits: int, d: int = 128, codebook: str = "gauss")
     return out
 
 
-def logits_dense(q, codes, norms, Q, bits: int, route: int = 1, codebook: str = "gauss"):
+def logits_dense(q, codes, norms, Q, bits: int, route: int = 1, codebook: str = "gauss", qjl_signs=None,
+                 gamma=None, S=None):
+    """As logits with the dense rotation Q; with qjl_signs/gamma/S, plus the
+    QJL term of the residual in the rotated space."""
     q = _f64(q)
     B, Hq, d = q.shape
     codes = np.ascontiguousarray(codes, dtype=np.uint8)
     _, Hkv, T, _ = codes.shape
     c, _ = _tables(bits, codebook)
     out = np.zeros((B, Hq, T))
+    m = 0
+    if qjl_signs is not None:
+        qjl_signs = np.ascontiguousarray(qjl_signs, dtype=np.uint8)
+        gamma = _f64(gamma)
+        S = _f64(S)
+        m = S.shape[0]
     _chk(lib().kvqo_logits_dense(route, d, bits, B, Hq, Hkv, T, _p(q, _D), _p(codes, _U8), _p(_f64(norms), _D),
-                                 _p(_f64(Q), _D), _p(c, _F), _p(out, _D)))
+                                 _p(_f64(Q), _D), _p(c, _F), _p(qjl_signs, _U8), _p(gamma, _D), _p(S, _D), m,
+                                 _p(out, _D)))
     return out
 
 

@@ -653,15 +653,27 @@ ORC_API void kvqo_dequant_dense(int d, int bits, const uint8_t *rec, double rho,
 }
 
 /* route 0: dequantise, then <q, k_hat>; route 1: rotated query q' = sqrt(d) Q q. */
+/* With QJL signs (qjl_signs, gamma, S [m, d] not NULL; TurboQuant, Como     */
+/* Funciona, Estagio 1 + Estagio 2: the dense rotation, then the 1-bit sign   */
+/* residual): the residual r = (y - c[idx]) / sqrt(d) lives in the rotated    */
+/* space, u - u_hat = Q^T r, and its estimate is                              */
+/* r_hat = gamma sqrt(pi/2) / m S^T sgn, so                                   */
+/*  route 0: k_hat = rho Q^T (c[idx] / sqrt(d) + r_hat), then <q, k_hat>;     */
+/*  route 1: rho <q', c[idx]> / d + rho gamma sqrt(pi/2)/m sum_j sgn_j         */
+/*           (S q')_j / sqrt(d) with q' = sqrt(d) Q q.                         */
 ORC_API int kvqo_logits_dense(int route, int d, int bits, int64_t B, int64_t Hq, int64_t Hkv, int64_t T,
                               const double *q, const uint8_t *codes, const double *norms, const double *Q,
-                              const float *c32, double *logits)
+                              const float *c32, const uint8_t *qjl_signs, const double *gamma, const double *S,
+                              int m, double *logits)
 {
     if (Hkv <= 0 || Hq % Hkv || d > 1024) return -1;
     const int64_t G = Hq / Hkv;
     const int rec = d * bits / 8;
     double *kh = (double *)malloc(sizeof(double) * d);
     double *qr = (double *)malloc(sizeof(double) * d);
+    double *rh = (double *)malloc(sizeof(double) * d);
+    double *rq = (double *)malloc(sizeof(double) * d);
+    double *pq = (double *)malloc(sizeof(double) * (m > 0 ? m : 1));
     int32_t idx[1024];
     for (int64_t b = 0; b < B; ++b)
         for (int64_t h = 0; h < Hq; ++h) {
@@ -669,22 +681,48 @@ ORC_API int kvqo_logits_dense(int route, int d, int bits, int64_t B, int64_t Hq,
             const double *qh = q + (b * Hq + h) * d;
             matvec(Q, qh, qr, d, 0);
             for (int i = 0; i < d; ++i) qr[i] *= sqrt((double)d);
+            if (qjl_signs)
+                for (int j = 0; j < m; ++j) {
+                    double s = 0.0;
+                    for (int i = 0; i < d; ++i) s += S[(int64_t)j * d + i] * qr[i];
+                    pq[j] = s / sqrt((double)d);
+                }
             for (int64_t t = 0; t < T; ++t) {
                 const int64_t v = (b * Hkv + g) * T + t;
                 double acc = 0.0;
                 if (route == 0) {
                     kvqo_dequant_dense(d, bits, codes + v * rec, norms[v], Q, c32, kh);
+                    if (qjl_signs) {
+                        const uint8_t *sv = qjl_signs + v * (m / 8);
+                        const double coef = gamma[v] * sqrt(M_PI / 2.0) / m;
+                        for (int i = 0; i < d; ++i) rh[i] = 0.0;
+                        for (int j = 0; j < m; ++j) {
+                            const double sg = ((sv[j / 8] >> (j % 8)) & 1) ? 1.0 : -1.0;
+                            for (int i = 0; i < d; ++i) rh[i] += coef * sg * S[(int64_t)j * d + i];
+                        }
+                        matvec(Q, rh, rq, d, 1);
+                        for (int i = 0; i < d; ++i) kh[i] += norms[v] * rq[i];
+                    }
                     for (int i = 0; i < d; ++i) acc += qh[i] * kh[i];
                 } else {
                     kvqo_unpack(codes + v * rec, d, bits, idx);
                     for (int i = 0; i < d; ++i) acc += qr[i] * c32[idx[i]];
                     acc *= norms[v] / d;
+                    if (qjl_signs) {
+                        const uint8_t *sv = qjl_signs + v * (m / 8);
+                        double s = 0.0;
+                        for (int j = 0; j < m; ++j) s += (((sv[j / 8] >> (j % 8)) & 1) ? 1.0 : -1.0) * pq[j];
+                        acc += norms[v] * gamma[v] * sqrt(M_PI / 2.0) / m * s;
+                    }
                 }
                 logits[(b * Hq + h) * T + t] = acc;
             }
         }
     free(kh);
     free(qr);
+    free(rh);
+    free(rq);
+    free(pq);
     return 0;
 }
 

@@ -39,7 +39,8 @@ int kvqo_quantize_dense(int d, int bits, int64_t B, int64_t H, int64_t T, const 
 void kvqo_dequant_dense(int d, int bits, const uint8_t *rec, double rho, const double *Q, const float *c32,
                         double *out);
 int kvqo_logits_dense(int route, int d, int bits, int64_t B, int64_t Hq, int64_t Hkv, int64_t T, const double *q,
-                      const uint8_t *codes, const double *norms, const double *Q, const float *c32, double *logits);
+                      const uint8_t *codes, const double *norms, const double *Q, const float *c32,
+                      const uint8_t *qjl_signs, const double *gamma, const double *S, int m, double *logits);
 int kvqo_attention_dense(int d, int bits, int64_t B, int64_t Hq, int64_t Hkv, int64_t T, const double *q,
                          const uint8_t *kc, const double *kn, const uint8_t *vc, const double *vn, const double *Q,
                          const float *c32, double sm_scale, double *out);
@@ -123,7 +124,8 @@ int main(void)
         for (int route = 1; route <= 2; ++route) {
             CHECK(kvqo_logits(route, d, bits, B, Hq, H, T, q, kc, kn, sg, c32, NULL, NULL, NULL, 0, lg) == 0);
             CHECK(kvqo_logits(route, d, bits, B, Hq, H, T, q, kc, kn, sg, c32, qs, gm, S, m, lg) == 0);
-            CHECK(kvqo_logits_dense(route, d, bits, B, Hq, H, T, q, kc, kn, Q, c32, lg) == 0);
+            CHECK(kvqo_logits_dense(route, d, bits, B, Hq, H, T, q, kc, kn, Q, c32, NULL, NULL, NULL, 0, lg) == 0);
+            CHECK(kvqo_logits_dense(route, d, bits, B, Hq, H, T, q, kc, kn, Q, c32, qs, gm, S, m, lg) == 0);
         }
         CHECK(kvqo_attention(d, bits, B, Hq, H, T, q, kc, kn, vc, vn, sg, sg, c32, 0.1, att) == 0);
         CHECK(kvqo_attention_dense(d, bits, B, Hq, H, T, q, kc, kn, vc, vn, Q, c32, 0.1, att) == 0);
