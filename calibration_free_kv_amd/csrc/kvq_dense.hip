@@ -194,6 +194,252 @@ __global__ __launch_bounds__(64 * kDenseWaves) void k_quantize_dense(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Dense rotation followed by the 1-bit QJL residual ("O Que E TurboQuant?",
+// Como Funciona, Estagio 1 + Estagio 2): the MSE codes of y = sqrt(d) Q x /
+// ||x|| as above, then in the rotated space the residual e = y - c[idx]
+// (r = e / sqrt(d), gamma = ||e|| / sqrt(d)) and the sign bits of its
+// Gaussian projection S e.  Keys only (one list of N vectors).
+//
+// A wave takes 64 keys and works through them 16 at a time (the B tile sg):
+// rotation of the 16 keys (the products of the MSE kernel), codes written to
+// the stage rows, e formed in place of the accumulators, then the projection
+// z = S e as 16x16x32 products: A = 16 rows of S (fp16, from LDS), B = e of
+// the 16 keys as exact fp16 high and low parts.  The rotation's accumulator
+// layout is already the B layout of the projection: lane (m16, kg) holds
+// e[32 j + 8 kg .. + 7] of key m16 in the registers of K step j.  The result
+// gives lane (m16, kg) outputs 16 ot + 4 kg + r of key m16; its sign bits are
+// gathered into the key's four 32-bit words with two lane exchanges.  With an
+// S that is not exactly fp16, a third pass adds e_hi . S_lo (S_lo from global
+// memory).
+template <int BITS>
+__device__ __forceinline__ float bucket_centroid(float a, float y, const float *p, const float *mag)
+{
+    // the centroid c[idx] of the antisymmetric table, by the comparisons of bucket_idx
+    float m = mag[0];
+    if constexpr (BITS == 2) {
+        m = a > p[0] ? mag[1] : mag[0];
+    } else if constexpr (BITS == 3) {
+        const bool c1 = a > p[1];
+        const bool c2 = a > (c1 ? p[2] : p[0]);
+        m = c1 ? (c2 ? mag[3] : mag[2]) : (c2 ? mag[1] : mag[0]);
+    } else if constexpr (BITS == 4) {
+        const bool c1 = a > p[3];
+        const bool c2 = a > (c1 ? p[5] : p[1]);
+        const bool c3 = a > (c1 ? (c2 ? p[6] : p[4]) : (c2 ? p[2] : p[0]));
+        const int h = 4 * c1 + 2 * c2 + c3;
+#pragma unroll
+        for (int k = 1; k < 8; ++k) m = h == k ? mag[k] : m;
+    }
+    return y > 0.0f ? m : -m;
+}
+
+// v = hi + lo with hi the 11 leading significant bits of v (exact in fp16 under
+// any rounding; values below the fp16 normal range go wholly to lo), lo = v - hi
+// exact in fp32 and rounded once to fp16.
+__device__ __forceinline__ _Float16 split_hi_lo(float v, _Float16 &lo)
+{
+    float h = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, v) & 0xFFFFE000u);
+    h = __builtin_fabsf(v) < 0x1p-14f ? 0.0f : h;
+    lo = (_Float16)(v - h);
+    return (_Float16)h;
+}
+
+struct DenseMags {
+    float m[8];  // positive centroids c_{L/2} .. c_{L-1}
+};
+
+template <int BITS, bool S_LO>
+__global__ __launch_bounds__(64 * kDenseWaves) void k_quantize_dense_qjl(
+    const _Float16 *__restrict__ xk, const u4_t *__restrict__ q16, const u4_t *__restrict__ s16,
+    PosThresholds P, DenseMags Mg, uint32_t *__restrict__ ck, float *__restrict__ nk, u4_t *__restrict__ sg_out,
+    float *__restrict__ gamma, int64_t N, int64_t n_groups)
+{
+    constexpr int RW = 4 * BITS;  // dwords per record
+    constexpr int SR = RW + 1;    // stage row stride in dwords
+    constexpr int NP = (1 << (BITS - 1)) - 1;
+    __shared__ __align__(16) _Float16 qs[2][kD * kQRow];  // Q high, low parts, rows permuted
+    __shared__ __align__(16) _Float16 ss_[kD * kQRow];    // S high part, rows in order
+    __shared__ __align__(16) uint32_t stage[kDenseWaves][64 * SR];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    for (int i = tid; i < 2 * kD * 16; i += 64 * kDenseWaves) {
+        const int part = i >> 11, row = (i >> 4) & (kD - 1), ch = i & 15;
+        const int nb = row >> 4, a = row & 15;
+        const int src = 32 * (nb >> 1) + 8 * (a >> 2) + 4 * (nb & 1) + (a & 3);
+        *reinterpret_cast<u4_t *>(&qs[part][row * kQRow + 8 * ch]) = q16[(part * kD + src) * 16 + ch];
+    }
+    for (int i = tid; i < kD * 16; i += 64 * kDenseWaves) {
+        const int row = i >> 4, ch = i & 15;
+        *reinterpret_cast<u4_t *>(&ss_[row * kQRow + 8 * ch]) = s16[row * 16 + ch];
+    }
+    __syncthreads();
+    const int m16 = lane & 15, kg = lane >> 4;
+    const float kInvSqrtD = 0.08838834764831845f;
+    uint8_t *srow_base = reinterpret_cast<uint8_t *>(&stage[wv][0]);
+    h8_t X[4][4];
+    auto load_x = [&](int64_t grp, int sg) {
+        int64_t v = 64 * grp + 16 * sg + m16;
+        if (v >= N) v = N - 1;
+        const _Float16 *src = xk + v * kD;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) X[sg][ks] = *reinterpret_cast<const h8_t *>(src + 32 * ks + 8 * kg);
+    };
+    const int64_t gstride = (int64_t)gridDim.x * kDenseWaves;
+    int64_t grp = (int64_t)blockIdx.x * kDenseWaves + wv;
+    if (grp < n_groups)
+#pragma unroll
+        for (int sg = 0; sg < 4; ++sg) load_x(grp, sg);
+    for (; grp < n_groups; grp += gstride) {
+        const int64_t g0 = 64 * grp;
+        const bool more = grp + gstride < n_groups;
+#pragma unroll
+        for (int sg = 0; sg < 4; ++sg) {
+            // one key tile at a time: no scheduling across tiles (their
+            // registers would be live together)
+            __builtin_amdgcn_sched_barrier(0);
+            // norm of key 16 sg + m16 (the four lanes kg hold a quarter each)
+            float ssum = 0.0f;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const h8_t a = X[sg][ks];
+                ssum = __builtin_amdgcn_fdot2(__builtin_shufflevector(a, a, 0, 1), __builtin_shufflevector(a, a, 0, 1), ssum, false);
+                ssum = __builtin_amdgcn_fdot2(__builtin_shufflevector(a, a, 2, 3), __builtin_shufflevector(a, a, 2, 3), ssum, false);
+                ssum = __builtin_amdgcn_fdot2(__builtin_shufflevector(a, a, 4, 5), __builtin_shufflevector(a, a, 4, 5), ssum, false);
+                ssum = __builtin_amdgcn_fdot2(__builtin_shufflevector(a, a, 6, 7), __builtin_shufflevector(a, a, 6, 7), ssum, false);
+            }
+            float2 pr = swap16(ssum);
+            const float s1 = pr.x + pr.y;
+            pr = swap32(s1);
+            const float rho = __builtin_sqrtf(pr.x + pr.y);
+            const float sc = rho * kInvSqrtD;
+            const float inv = rho > 0.0f ? 11.313708498984761f / rho : 0.0f;  // sqrt(d) / rho
+            float ps[NP > 0 ? NP : 1];
+#pragma unroll
+            for (int k = 0; k < NP; ++k) ps[k] = P.p[k] * sc;
+            const int64_t vn = g0 + 16 * sg + m16;
+            if (kg == 0 && vn < N) nk[vn] = rho;
+            // Q x of the 16 keys
+            f4_t D[8];
+#pragma unroll
+            for (int nb = 0; nb < 8; ++nb) D[nb] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int nb = 0; nb < 8; ++nb) {
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    const int off = (16 * nb + m16) * kQRow + 32 * ks + 8 * kg;
+                    const h8_t ah = *reinterpret_cast<const h8_t *>(&qs[0][off]);
+                    const h8_t al = *reinterpret_cast<const h8_t *>(&qs[1][off]);
+                    D[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, X[sg][ks], D[nb], 0, 0, 0);
+                    D[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, X[sg][ks], D[nb], 0, 0, 0);
+                }
+            }
+            if (more) load_x(grp + gstride, sg);  // this key tile's inputs are consumed
+            // codes (pieces of 8 consecutive outputs 32 j + 8 kg + u) and the
+            // residual e = y - c[idx] in place, split into exact fp16 parts
+            uint8_t *row = srow_base + (16 * sg + m16) * (4 * SR);
+            u4_t eh[4], el[4];
+            float e2 = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                uint32_t pc = 0u;
+                _Float16 hv[8], lv[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const float y = D[2 * j + (u >> 2)][u & 3];
+                    pc |= bucket_idx<BITS>(y, ps) << (BITS * u);
+                    const float e = y * inv - bucket_centroid<BITS>(__builtin_fabsf(y), y, ps, Mg.m);
+                    e2 = fmaf(e, e, e2);
+                    _Float16 lo;
+                    hv[u] = split_hi_lo(e, lo);
+                    lv[u] = lo;
+                }
+                eh[j] = __builtin_bit_cast(u4_t, h8_t{hv[0], hv[1], hv[2], hv[3], hv[4], hv[5], hv[6], hv[7]});
+                el[j] = __builtin_bit_cast(u4_t, h8_t{lv[0], lv[1], lv[2], lv[3], lv[4], lv[5], lv[6], lv[7]});
+                const int off = BITS * (4 * j + kg);
+                if constexpr (BITS == 4) {
+                    *reinterpret_cast<uint32_t *>(row + off) = pc;
+                } else if constexpr (BITS == 2) {
+                    *reinterpret_cast<uint16_t *>(row + off) = (uint16_t)pc;
+                } else if constexpr (BITS == 1) {
+                    row[off] = (uint8_t)pc;
+                } else {
+                    row[off] = (uint8_t)pc;
+                    row[off + 1] = (uint8_t)(pc >> 8);
+                    row[off + 2] = (uint8_t)(pc >> 16);
+                }
+            }
+            pr = swap16(e2);
+            const float e2a = pr.x + pr.y;
+            pr = swap32(e2a);
+            if (kg == 0 && vn < N) gamma[vn] = __builtin_sqrtf(pr.x + pr.y) * kInvSqrtD;
+            // z = S e: output tile ot (outputs 16 ot .. + 15), K steps j
+            uint32_t wsg[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int ot = 0; ot < 8; ++ot) {
+                f4_t z = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const h8_t sa = *reinterpret_cast<const h8_t *>(&ss_[(16 * ot + m16) * kQRow + 32 * j + 8 * kg]);
+                    z = __builtin_amdgcn_mfma_f32_16x16x32_f16(sa, __builtin_bit_cast(h8_t, eh[j]), z, 0, 0, 0);
+                    z = __builtin_amdgcn_mfma_f32_16x16x32_f16(sa, __builtin_bit_cast(h8_t, el[j]), z, 0, 0, 0);
+                    if constexpr (S_LO) {
+                        const h8_t sl = __builtin_bit_cast(h8_t, s16[(kD + 16 * ot + m16) * 16 + 4 * j + kg]);
+                        z = __builtin_amdgcn_mfma_f32_16x16x32_f16(sl, __builtin_bit_cast(h8_t, eh[j]), z, 0, 0, 0);
+                    }
+                }
+                // outputs 16 ot + 4 kg + r: bit 16 (ot & 1) + 4 kg + r of word ot / 2
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (z[r] >= 0.0f) wsg[ot >> 1] |= 1u << (16 * (ot & 1) + 4 * kg + r);
+            }
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                wsg[w] |= (uint32_t)__shfl_xor((int)wsg[w], 16);
+                wsg[w] |= (uint32_t)__shfl_xor((int)wsg[w], 32);
+            }
+            if (kg == 0 && vn < N) sg_out[vn] = u4_t{wsg[0], wsg[1], wsg[2], wsg[3]};
+        }
+        wave_lds_sync();
+        {
+            const uint32_t *row = &stage[wv][lane * SR];
+            uint32_t W[RW];
+#pragma unroll
+            for (int w = 0; w < RW; ++w) W[w] = row[w];
+            const int64_t v = g0 + lane;
+            if (v < N) {
+                u4_t *dst = reinterpret_cast<u4_t *>(ck + v * RW);
+#pragma unroll
+                for (int k = 0; k < BITS; ++k) dst[k] = u4_t{W[4 * k], W[4 * k + 1], W[4 * k + 2], W[4 * k + 3]};
+            }
+        }
+        wave_lds_sync();  // the stage is free for the next group
+    }
+}
+
+template <int BITS>
+hipError_t dense_qjl_b(const kvq_ctx *ctx, const void *xk, int64_t N, uint8_t *ck, float *nk, uint8_t *signs,
+                       float *gamma, hipStream_t s)
+{
+    constexpr int L = 1 << BITS;
+    PosThresholds P{};
+    for (int k = 0; k < L / 2 - 1; ++k) P.p[k] = ctx->cb.t[L / 2 + k];
+    DenseMags M{};
+    for (int k = 0; k < L / 2; ++k) M.m[k] = ctx->cb.c[L / 2 + k];
+    const int64_t n_groups = (N + 63) / 64;
+    int64_t blocks = (n_groups + kDenseWaves - 1) / kDenseWaves;
+    if (blocks > ctx->n_cu) blocks = ctx->n_cu;
+    if (ctx->S_exact_f16)
+        hipLaunchKernelGGL((k_quantize_dense_qjl<BITS, false>), dim3((unsigned)blocks), dim3(64 * kDenseWaves), 0, s,
+                           (const _Float16 *)xk, (const u4_t *)ctx->d_Q16, (const u4_t *)ctx->d_S16, P, M,
+                           (uint32_t *)ck, nk, (u4_t *)signs, gamma, N, n_groups);
+    else
+        hipLaunchKernelGGL((k_quantize_dense_qjl<BITS, true>), dim3((unsigned)blocks), dim3(64 * kDenseWaves), 0, s,
+                           (const _Float16 *)xk, (const u4_t *)ctx->d_Q16, (const u4_t *)ctx->d_S16, P, M,
+                           (uint32_t *)ck, nk, (u4_t *)signs, gamma, N, n_groups);
+    return hipGetLastError();
+}
+
 template <int BITS>
 hipError_t dense_b(const kvq_ctx *ctx, const void *xk, const void *xv, int64_t N, uint8_t *ck, float *nk,
                    uint8_t *cv, float *nv, hipStream_t s)
@@ -214,6 +460,18 @@ hipError_t dense_b(const kvq_ctx *ctx, const void *xk, const void *xv, int64_t N
 }
 
 }  // namespace
+
+hipError_t launch_quantize_dense_qjl(const kvq_ctx *ctx, const void *xk, int64_t N, uint8_t *ck, float *nk,
+                                     uint8_t *signs, float *gamma, hipStream_t s)
+{
+    switch (ctx->bits) {
+    case 1: return dense_qjl_b<1>(ctx, xk, N, ck, nk, signs, gamma, s);
+    case 2: return dense_qjl_b<2>(ctx, xk, N, ck, nk, signs, gamma, s);
+    case 3: return dense_qjl_b<3>(ctx, xk, N, ck, nk, signs, gamma, s);
+    case 4: return dense_qjl_b<4>(ctx, xk, N, ck, nk, signs, gamma, s);
+    }
+    return hipErrorInvalidValue;
+}
 
 hipError_t launch_quantize_dense(const kvq_ctx *ctx, const void *xk, const void *xv, int64_t N, uint8_t *ck,
                                  float *nk, uint8_t *cv, float *nv, hipStream_t s)

@@ -254,7 +254,7 @@ kvq_status kvq_create(const kvq_config *cfg, kvq_ctx **out)
     if (cfg->nsn_options & ~KVQ_NSN_ADAPTIVE_SCALE) return KVQ_E_INVAL;
     if (cfg->nsn_options && mode != KVQ_MODE_NSN_VQ) return KVQ_E_INVAL;
     if (cfg->rotation == KVQ_ROTATION_DENSE) {
-        if (mode != KVQ_MODE_MSE) return KVQ_E_UNSUPPORTED;
+        if (mode == KVQ_MODE_NSN_VQ) return KVQ_E_UNSUPPORTED;
         if (!cfg->rot_Q) return KVQ_E_INVAL;
         for (int i = 0; i < kvq::kD * kvq::kD; ++i)
             if (!std::isfinite(cfg->rot_Q[i]) || std::fabs(cfg->rot_Q[i]) > 1.0f) return KVQ_E_INVAL;
@@ -451,6 +451,9 @@ kvq_status kvq_quantize(kvq_ctx *ctx, int32_t kind, const void *x_f16, int64_t B
     if (B * H_kv > (int64_t(1) << 40) || T > (int64_t(1) << 31)) return KVQ_E_INVAL;
     DeviceGuard g(ctx->device);
     if (!g.ok) return KVQ_E_DEVICE;
+    if (ctx->rotation == KVQ_ROTATION_DENSE && want_qjl)
+        return launch_status(kvq::launch_quantize_dense_qjl(ctx, x_f16, B * H_kv * T, codes, norms, qjl_signs,
+                                                            qjl_gamma, (hipStream_t)stream));
     if (ctx->rotation == KVQ_ROTATION_DENSE)
         return launch_status(kvq::launch_quantize_dense(ctx, x_f16, nullptr, B * H_kv * T, codes, norms, nullptr,
                                                         nullptr, (hipStream_t)stream));

@@ -92,6 +92,11 @@ hipError_t launch_decode_noalloc(const kvq_ctx *ctx, const void *q, int64_t B, i
 hipError_t launch_quantize_dense(const kvq_ctx *ctx, const void *xk, const void *xv, int64_t N, uint8_t *ck,
                                  float *nk, uint8_t *cv, float *nv, hipStream_t s);
 
+// Dense rotation plus the QJL residual of N keys: codes, norms, sign bits
+// [N][16 bytes] and residual norms gamma.
+hipError_t launch_quantize_dense_qjl(const kvq_ctx *ctx, const void *xk, int64_t N, uint8_t *ck, float *nk,
+                                     uint8_t *signs, float *gamma, hipStream_t s);
+
 // Residual window of a streaming cache: R full-precision tokens per (batch, KV
 // head) in fp16 arrays [B, H_kv, R_cap, 128].
 struct DecodeTail {

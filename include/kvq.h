@@ -76,8 +76,9 @@ enum { KVQ_CODEBOOK_GAUSS = 0, KVQ_CODEBOOK_BETA = 1 };
 /* Rotation of the MSE modes: the randomized Hadamard transform y = H (D .* u)
  * ([PQ] sec. 2; [NSN] sec. 2), or a dense orthogonal Q given by the caller,
  * y = sqrt(d) Q u ([TQ] Como Funciona, Estagio 1: QR of a Gaussian matrix),
- * the same Q for K, V and every head (KVQ_MODE_MSE only; not with the
- * streaming-cache calls). */
+ * the same Q for K, V and every head (KVQ_MODE_MSE, and KVQ_MODE_MSE_QJL
+ * where the QJL residual lives in the rotated space: [TQ] Estagio 1 +
+ * Estagio 2; not with the NSN_VQ mode or the streaming-cache calls). */
 enum { KVQ_ROTATION_HADAMARD = 0, KVQ_ROTATION_DENSE = 1 };
 /* Options of the NSN_VQ mode (bits of kvq_config.nsn_options).
  * KVQ_NSN_ADAPTIVE_SCALE ([NSN] Metodologia sec. 3, adaptive scale): the
@@ -127,7 +128,7 @@ typedef struct {
  * entry not +-1, missing table for the mode, unknown codebook or rotation,
  * rot_Q NULL, with an entry not finite or above 1 in magnitude, or not
  * orthogonal to within 1e-3 in every entry of Q Q^T - I),
- * KVQ_E_UNSUPPORTED (dense rotation outside KVQ_MODE_MSE), KVQ_E_DEVICE (no
+ * KVQ_E_UNSUPPORTED (dense rotation in KVQ_MODE_NSN_VQ), KVQ_E_DEVICE (no
  * such device), KVQ_E_NOMEM. */
 kvq_status kvq_create(const kvq_config *cfg, kvq_ctx **out);
 

@@ -56,6 +56,9 @@ hipError_t launch_quantize_kv(const kvq_ctx *, const void *, const void *, int64
 hipError_t launch_quantize_dense(const kvq_ctx *, const void *, const void *, int64_t N, uint8_t *, float *, uint8_t *,
                                  float *, hipStream_t)
 { return rec("quantize_dense", N); }
+hipError_t launch_quantize_dense_qjl(const kvq_ctx *, const void *, int64_t N, uint8_t *, float *, uint8_t *, float *,
+                                     hipStream_t)
+{ return rec("quantize_dense_qjl", N); }
 hipError_t launch_logits(const kvq_ctx *, const void *, int64_t B, int64_t Hq, int64_t T, const uint8_t *,
                          const float *, const uint8_t *, const float *, float *, hipStream_t)
 { return rec("logits", B, Hq, T); }

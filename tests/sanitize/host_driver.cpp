@@ -100,9 +100,14 @@ int main()
     c.qjl_S = S.data();
     c.rotation = KVQ_ROTATION_DENSE;
     c.rot_Q = Q.data();
-    kvq_status st = kvq_create(&c, &ctx);
-    CHECK(st == KVQ_E_UNSUPPORTED || st == KVQ_OK);
-    if (st == KVQ_OK) kvq_destroy(ctx);
+    kvq_ctx *dqjl = nullptr;
+    kvq_status st = kvq_create(&c, &dqjl);
+    CHECK(st == KVQ_OK);
+    c = base(1, KVQ_MODE_NSN_VQ, H);
+    c.vq_codebook = cb.data();
+    c.rotation = KVQ_ROTATION_DENSE;
+    c.rot_Q = Q.data();
+    CHECK(kvq_create(&c, &ctx) == KVQ_E_UNSUPPORTED);
 
     std::vector<kvq_ctx *> all;
     for (int b = 1; b <= 4; ++b)
@@ -152,6 +157,10 @@ int main()
     CHECK(kvq_quantize(qjl, 1, x.p, B, H, T, codes.as<uint8_t>(), norms.as<float>(), signs.as<uint8_t>(), gamma.as<float>(), st0) == KVQ_E_INVAL);
     CHECK(kvq_quantize(dense, 0, x.p, B, H, T, codes.as<uint8_t>(), norms.as<float>(), nullptr, nullptr, st0) == KVQ_OK);
     CHECK(std::strcmp(g_last.what, "quantize_dense") == 0 && g_last.a == B * H * T);
+    CHECK(kvq_quantize(dqjl, 0, x.p, B, H, T, codes.as<uint8_t>(), norms.as<float>(), signs.as<uint8_t>(), gamma.as<float>(), st0) == KVQ_OK);
+    CHECK(std::strcmp(g_last.what, "quantize_dense_qjl") == 0 && g_last.a == B * H * T);
+    CHECK(kvq_quantize(dqjl, 1, x.p, B, H, T, codes.as<uint8_t>(), norms.as<float>(), nullptr, nullptr, st0) == KVQ_OK);
+    CHECK(std::strcmp(g_last.what, "quantize_dense") == 0);
     CHECK(kvq_quantize_kv(mse, x.p, x.p, B, H, T, codes.as<uint8_t>(), norms.as<float>(), codes.as<uint8_t>(), norms.as<float>(), st0) == KVQ_OK);
     CHECK(kvq_quantize_kv(qjl, x.p, x.p, B, H, T, codes.as<uint8_t>(), norms.as<float>(), codes.as<uint8_t>(), norms.as<float>(), st0) == KVQ_E_INVAL);
 
@@ -223,6 +232,7 @@ int main()
 
     for (kvq_ctx *p : all) CHECK(kvq_destroy(p) == KVQ_OK);
     CHECK(kvq_destroy(qjl) == KVQ_OK && kvq_destroy(nsn) == KVQ_OK && kvq_destroy(dense) == KVQ_OK);
+    CHECK(kvq_destroy(dqjl) == KVQ_OK);
     CHECK(kvq_destroy(nullptr) == KVQ_OK);
     std::printf("host ok\n");
     return 0;

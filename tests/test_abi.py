@@ -92,8 +92,8 @@ def test_create_validation():
     assert L.kvq_create(C.byref(cfg), C.byref(h)) == kvq.KVQ_E_INVAL
     cfg, keep = _cfg(rotation=2, rot_Q=qp(eye), device=999)  # not a KVQ_ROTATION_*
     assert L.kvq_create(C.byref(cfg), C.byref(h)) == kvq.KVQ_E_INVAL
-    S = np.zeros((128, 128), np.float32)
-    cfg, keep = _cfg(mode=1, qjl_S=qp(S), rotation=1, rot_Q=qp(eye), device=999)  # dense is MSE-only
+    cb = np.ones((256, 8), np.float32)
+    cfg, keep = _cfg(mode=2, vq_codebook=qp(cb), rotation=1, rot_Q=qp(eye), device=999)  # NSN keeps its transform
     assert L.kvq_create(C.byref(cfg), C.byref(h)) == kvq.KVQ_E_UNSUPPORTED
     assert not h.value
     cfg, keep = _cfg(device=999)  # no such device (no device at all on a CPU host)

@@ -149,8 +149,8 @@ def test_hadamard_matrix_as_dense_rotation_matches_hadamard_path():
 
 def test_dense_validation():
     Q = rot(70)
-    with pytest.raises(kvq.KvqError) as e:  # dense rotation needs the MSE mode
-        kvq.Context(2, 3, mode=kvq.KVQ_MODE_MSE_QJL, qjl_S=np.eye(128, dtype=np.float32), rot_Q=Q)
+    with pytest.raises(kvq.KvqError) as e:  # the NSN-VQ mode keeps its own transform
+        kvq.Context(2, 1, mode=kvq.KVQ_MODE_NSN_VQ, vq_codebook=np.ones((256, 8), np.float32), rot_Q=Q)
     assert e.value.status == kvq.KVQ_E_UNSUPPORTED
     bad = Q.copy()
     bad[3, 4] = np.nan
@@ -183,3 +183,97 @@ def test_quantize_kv_dense_equals_two_calls_and_is_deterministic():
     for a, b in ((ko, k1), (vo, v1), (ko, ko2)):
         assert torch.equal(a["codes"], b["codes"])
         assert torch.equal(a["norms"], b["norms"])
+
+
+# --------------------------------------------------------------------------- dense rotation + QJL residual
+def check_dense_qjl(x, Q, S, bits, g, where=None):
+    """Codes (valid at flagged coordinates), norms, and for every key the QJL
+    sign bits and gamma of the residual in the dense-rotated space, against
+    the oracle (a key whose codes flipped at a flagged coordinate is compared
+    with the oracle's QJL of that admissible code)."""
+    from tests.test_gpu_qjl import admissible_qjl
+    B, H, T, _ = x.shape
+    if where is None:
+        bb, hh, tt = [a.ravel() for a in np.meshgrid(np.arange(B), np.arange(H), np.arange(T), indexing="ij")]
+    else:
+        bb, hh, tt = where
+    xs = x[bb, hh, tt][None, None]
+    ref = O.quantize_dense(xs, Q.astype(np.float64), bits, want_y=True)
+    gi = unpack_np(g["codes"][bb, hh, tt], bits)[None, None]
+    m, f = boundary_mismatches(gi, ref, O.tables_f32(bits)[1], "dense qjl codes")
+    bound_mismatches(m, f, "dense qjl codes")
+    np.testing.assert_allclose(g["norms"][bb, hh, tt], ref["norms"][0, 0], rtol=1e-5, atol=1e-30)
+    S64 = S.astype(np.float64)
+    q = O.qjl(ref["y"], ref["idx"], S64, bits)
+    r_gamma, r_flags = q["gamma"][0, 0].copy(), q["flags"][0, 0].copy()
+    r_bits = np.unpackbits(q["signs"][0, 0], axis=-1, bitorder="little")
+    for v in np.flatnonzero(~(gi[0, 0] == ref["idx"][0, 0]).all(-1)):
+        alt = admissible_qjl(ref["y"][0, 0, v], ref["idx"][0, 0, v], ref["flags"][0, 0, v], S64, bits, gi[0, 0, v])
+        r_gamma[v] = alt["gamma"][0]
+        r_bits[v] = np.unpackbits(alt["signs"][0], bitorder="little")
+        r_flags[v] = alt["flags"][0]
+    np.testing.assert_allclose(g["qjl_gamma"][bb, hh, tt], r_gamma, rtol=1e-5, atol=1e-7)
+    g_bits = np.unpackbits(g["qjl_signs"][bb, hh, tt], axis=-1, bitorder="little")
+    bad = (g_bits != r_bits) & (r_flags == 0)
+    assert not bad.any(), "%d sign bits differ outside the 1e-5*gamma band" % int(bad.sum())
+    nm = int((g_bits != r_bits).sum())
+    assert nm <= int(r_flags.sum()) // 2 + 2, (nm, int(r_flags.sum()))
+    return m, nm
+
+
+def run_dense_qjl(x, Q, S, bits, signs_k, signs_v):
+    ctx = kvq.Context(x.shape[1], bits, signs_k, signs_v, mode=kvq.KVQ_MODE_MSE_QJL, qjl_S=S, rot_Q=Q)
+    out = ctx.quantize(kvq.KVQ_KIND_K, torch.from_numpy(x).cuda())
+    return ctx, {k: to_np(v) for k, v in out.items()}
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_dense_qjl_quantize_ragged(bits):
+    """2 x 8 x 333 keys (ragged groups of 64), a zero key."""
+    inp = synth.make("long128k_qjl", T=333, B=2)
+    x = inp["k"].copy()
+    x[1, 2, 7] = 0
+    Q = rot(80 + bits)
+    ctx, g = run_dense_qjl(x, Q, inp["S"], bits, inp["signs_k"], inp["signs_v"])
+    print("bits=%d (code mismatches, sign mismatches) = %s" % (bits, check_dense_qjl(x, Q, inp["S"], bits, g)))
+    assert g["norms"][1, 2, 7] == 0
+
+
+def test_dense_qjl_general_fp32_projection():
+    """An S that is not exactly fp16: the kernel adds the e_hi . S_lo pass."""
+    inp = synth.make("long128k_qjl", T=200)
+    S = np.random.default_rng(6).standard_normal((128, 128)).astype(np.float32)
+    Q = rot(85)
+    ctx, g = run_dense_qjl(inp["k"], Q, S, 2, inp["signs_k"], inp["signs_v"])
+    check_dense_qjl(inp["k"], Q, S, 2, g)
+
+
+def test_dense_qjl_full_size_sampled():
+    """The long-context keys (8 x 131072) with the dense rotation and the QJL
+    residual: 2048 sampled keys checked."""
+    inp = synth.make("long128k_qjl")
+    Q = rot(86)
+    ctx, g = run_dense_qjl(inp["k"], Q, inp["S"], 2, inp["signs_k"], inp["signs_v"])
+    rng = np.random.default_rng(4)
+    n = 2048
+    where = (np.zeros(n, int), rng.integers(0, 8, n), rng.integers(0, inp["T"], n))
+    print(check_dense_qjl(inp["k"], Q, inp["S"], 2, g, where=where))
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_dense_qjl_logits(bits):
+    """Logits with the QJL term in the rotated space, on the oracle's codes."""
+    inp = synth.make("long128k_qjl", T=900)
+    Q = rot(90 + bits)
+    S = inp["S"]
+    r = O.quantize_dense(inp["k"], Q.astype(np.float64), bits, want_y=True)
+    qj = O.qjl(r["y"], r["idx"], S.astype(np.float64), bits)
+    kn, gm = r["norms"].astype(np.float32), qj["gamma"].astype(np.float32)
+    ctx = kvq.Context(8, bits, mode=kvq.KVQ_MODE_MSE_QJL, qjl_S=S, rot_Q=Q)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    lg = to_np(ctx.logits(dev(inp["q"]), dev(r["codes"]), dev(kn), dev(qj["signs"]), dev(gm)))
+    ref = O.logits_dense(inp["q"], r["codes"], kn.astype(np.float64), Q.astype(np.float64), bits,
+                         qjl_signs=qj["signs"], gamma=gm.astype(np.float64), S=S.astype(np.float64))
+    scale = np.linalg.norm(inp["q"].astype(np.float64), axis=-1)[..., None] * np.repeat(kn.astype(np.float64), 4, axis=1)
+    err = (np.abs(lg - ref) / scale).max()
+    assert err <= 1e-5, err
