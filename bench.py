@@ -468,6 +468,27 @@ def rows(torch, kvq, synth, dev, timer, reps, oracle_rates):
         kvq.kvq_logits(ctx, q, B, Hq, T, c["codes"], c["norms"], c["qjl_signs"], c["qjl_gamma"], lo[i % 2])
     out["logits_qjl_long128k_b2"] = row(*timer.run(lg, reps, 5), nbytes=lb, units_per_launch=n * Hq,
                                         unit="logits", buffer_sets=ns)
+    # the same workload with the dense rotation (TurboQuant's Estagio 1 + 2)
+    Qd = synth.random_orthogonal(31).astype(np.float32)
+    ctxd = kvq.Context(Hkv, 2, inp["signs_k"], inp["signs_v"], mode=kvq.KVQ_MODE_MSE_QJL, qjl_S=inp["S"],
+                       rot_Q=Qd, device=dev.index)
+
+    def qjld(i):
+        c = cs[i % ns]
+        kvq.kvq_quantize(ctxd, kvq.KVQ_KIND_K, ks[i % 2], B, Hkv, T, c["codes"], c["norms"], c["qjl_signs"],
+                         c["qjl_gamma"])
+    out["quantize_qjl_dense_long128k_b2"] = row(*timer.run(qjld, reps, ns), nbytes=quant_bytes(n, 2, qjl=True),
+                                                flops=n * 2 * (2 * D * D + 2 * D * D), units_per_launch=n,
+                                                unit="vectors",
+                                                note="flops = rotation (Q as two fp16 parts) and projection "
+                                                     "(e as two fp16 parts), 2 d^2 each per part")
+
+    def lgd(i):
+        c = cs[i % ns]
+        kvq.kvq_logits(ctxd, q, B, Hq, T, c["codes"], c["norms"], c["qjl_signs"], c["qjl_gamma"], lo[i % 2])
+    out["logits_qjl_dense_long128k_b2"] = row(*timer.run(lgd, reps, 5), nbytes=lb, units_per_launch=n * Hq,
+                                              unit="logits", buffer_sets=ns)
+    del ctxd
     kk = inp["k"][:, :, :1024]
 
     def oracle_qjl():
@@ -510,7 +531,16 @@ def rows(torch, kvq, synth, dev, timer, reps, oracle_rates):
                                 unit="vectors", note="three launches (stats, mean, search); x is read twice; "
                                 "flops = exhaustive distances 16 x 256 x 8 x 2 per vector")
     oracle_rates["nsn_vq_8x65536"] = oracle_rate(lambda: O.nsn_vq(inp["x"][:1, :1024], cb), 1024)
-    del xsn, x0
+    # with the adaptive scale and the cosine-refined codebook
+    cbc = np.loadtxt(os.path.join(ROOT, "tests", "golden", "vq_codebook_256x8_cos.txt"),
+                     dtype=np.float32).reshape(256, 8)
+    ctxa = kvq.Context(H, 1, mode=kvq.KVQ_MODE_NSN_VQ, vq_codebook=cbc, nsn_options=kvq.KVQ_NSN_ADAPTIVE_SCALE,
+                       device=dev.index)
+    out["nsn_vq_adaptive_8x65536"] = row(*timer.run(lambda i: ctxa.nsn_vq_quantize(xsn[i % 4], out=o, ws=ws), reps, 4),
+                                         nbytes=nsn_bytes(H * T), flops=H * T * 16 * 256 * 8 * 2,
+                                         units_per_launch=H * T, unit="vectors",
+                                         note="adaptive scale folded into s2, cosine-refined codebook")
+    del xsn, x0, ctxa
 
     # NSN-VQ scoring from codes: logits and one decode step, 8 KV heads x 65536
     # keys, 32 query heads; stand-in encoded K and V from the seeded generator
