@@ -94,6 +94,8 @@ def _setup(L):
                                   _D, _D]
     L.kvqo_nsn_attention.argtypes = [C.c_int, C.c_int, i64, i64, i64, i64, _D, _U8, _D, _D, _D, _U8,
                                      _D, _D, _D, _D, C.c_double, _D]
+    L.kvqo_nsn_attention_stream.argtypes = [C.c_int, C.c_int, i64, i64, i64, i64, i64, i64, _D, _U8, _D, _D, _D,
+                                            _U8, _D, _D, _D, _D, _D, _D, C.c_double, _D]
     L.kvqo_kmeans.argtypes = [i64, C.c_int, C.c_int, _D, _I64, C.c_int, _D, _D]
     L.kvqo_kmeans.restype = C.c_int
     L.kvqo_cosine_refine.argtypes = [i64, C.c_int, C.c_int, _D, _D, C.c_int, _D]
@@ -505,6 +507,31 @@ def nsn_attention(q, kc, ks1, ks2, ko, vc, vs1, vs2, vo, codebook, sm_scale: flo
                                   _p(args[0], _D), _p(args[1], _D), _p(args[2], _D), _p(vc, _U8),
                                   _p(args[3], _D), _p(args[4], _D), _p(args[5], _D), _p(cb, _D),
                                   float(sm_scale), _p(out, _D)))
+    return out
+
+
+def nsn_attention_stream(q, kc, ks1, ks2, ko, vc, vs1, vs2, vo, k_tail, v_tail, codebook, Gs: int,
+                         sm_scale: float | None = None):
+    """Decode over an NSN-VQ streaming cache: T packed tokens (codes [B,Hkv,T,d/sub],
+    s1/s2 [B,Hkv,T]) encoded in groups of Gs tokens with per-group means
+    [B,Hkv,T/Gs,d], then R full-precision window tokens [B,Hkv,R,d] -> [B,Hq,d]."""
+    q = _f64(q)
+    B, Hq, d = q.shape
+    kt, vt = _f64(k_tail), _f64(v_tail)
+    Hkv, R = kt.shape[1], kt.shape[2]
+    cb = _f64(codebook)
+    sub = cb.shape[1]
+    kc = np.ascontiguousarray(kc, dtype=np.uint8).reshape(B, Hkv, -1, d // sub)
+    vc = np.ascontiguousarray(vc, dtype=np.uint8).reshape(B, Hkv, -1, d // sub)
+    T = kc.shape[2]
+    if sm_scale is None:
+        sm_scale = 1.0 / np.sqrt(d)
+    out = np.zeros((B, Hq, d))
+    args = [_f64(a) for a in (ks1, ks2, ko, vs1, vs2, vo)]
+    _chk(lib().kvqo_nsn_attention_stream(d, sub, B, Hq, Hkv, T, Gs, R, _p(q, _D), _p(kc, _U8), _p(args[0], _D),
+                                         _p(args[1], _D), _p(args[2], _D), _p(vc, _U8), _p(args[3], _D),
+                                         _p(args[4], _D), _p(args[5], _D), _p(kt, _D), _p(vt, _D), _p(cb, _D),
+                                         float(sm_scale), _p(out, _D)))
     return out
 
 

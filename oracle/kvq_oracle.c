@@ -1167,6 +1167,76 @@ ORC_API int kvqo_kmeans(int64_t n, int dim, int K, const double *samples, const 
 }
 
 /* ------------------------------------------------------------------------ */
+/* Decode attention over an NSN-VQ streaming cache (NSNQuant, Detalhes de     */
+/* Implementacao, Residuos: following KIVI the cache is a quantised part and  */
+/* a full-precision residual that is quantised and appended when it fills;   */
+/* read with Metodologia sec. 1, each flushed group of Gs tokens is encoded   */
+/* as one call, with its own channel mean).  Packed token t of (b, g) is      */
+/* reconstructed with the mean of its group t / Gs:                           */
+/*   x_hat_t = s1_t (s2_t H zq_t / sqrt(d) + o_{t / Gs}),                      */
+/* followed by the R window tokens as they are; one softmax over all T + R.  */
+/* kc, vc [B, Hkv, T, d/sub]; ks1.. [B, Hkv, T]; ko, vo [B, Hkv, T / Gs, d]    */
+/* (T a multiple of Gs; T = 0 allowed); kt, vt [B, Hkv, R, d].               */
+/* ------------------------------------------------------------------------ */
+
+ORC_API int kvqo_nsn_attention_stream(int d, int sub, int64_t B, int64_t Hq, int64_t Hkv, int64_t T, int64_t Gs,
+                                      int64_t R, const double *q, const uint8_t *kc, const double *ks1,
+                                      const double *ks2, const double *ko, const uint8_t *vc, const double *vs1,
+                                      const double *vs2, const double *vo, const double *kt, const double *vt,
+                                      const double *cb, double sm_scale, double *out)
+{
+    if (Hkv <= 0 || Hq % Hkv || T < 0 || R < 0 || T + R <= 0 || d % sub || Gs <= 0 || T % Gs) return -1;
+    const int64_t G = Hq / Hkv, N = T + R, ng = T / Gs;
+    const int ns = d / sub;
+    double *K = (double *)malloc(sizeof(double) * N * d);
+    double *V = (double *)malloc(sizeof(double) * N * d);
+    double *zq = (double *)malloc(sizeof(double) * d);
+    double *w = (double *)malloc(sizeof(double) * N);
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t g = 0; g < Hkv; ++g) {
+            const int64_t bg = b * Hkv + g;
+            for (int64_t t = 0; t < T; ++t) {
+                const int64_t v = bg * T + t;
+                const double *okg = ko + (bg * ng + t / Gs) * d, *ovg = vo + (bg * ng + t / Gs) * d;
+                nsn_entries(d, sub, kc + v * ns, cb, zq);
+                kvqo_nsn_reconstruct(d, zq, ks1[v], ks2[v], okg, K + t * d);
+                nsn_entries(d, sub, vc + v * ns, cb, zq);
+                kvqo_nsn_reconstruct(d, zq, vs1[v], vs2[v], ovg, V + t * d);
+            }
+            for (int64_t t = 0; t < R; ++t)
+                for (int i = 0; i < d; ++i) {
+                    K[(T + t) * d + i] = kt[(bg * R + t) * d + i];
+                    V[(T + t) * d + i] = vt[(bg * R + t) * d + i];
+                }
+            for (int64_t hh = 0; hh < G; ++hh) {
+                const double *qh = q + (b * Hq + g * G + hh) * d;
+                double mx = -INFINITY;
+                for (int64_t t = 0; t < N; ++t) {
+                    double a = 0.0;
+                    for (int i = 0; i < d; ++i) a += qh[i] * K[t * d + i];
+                    w[t] = sm_scale * a;
+                    if (w[t] > mx) mx = w[t];
+                }
+                double l = 0.0;
+                for (int64_t t = 0; t < N; ++t) {
+                    w[t] = exp(w[t] - mx);
+                    l += w[t];
+                }
+                double *oh = out + (b * Hq + g * G + hh) * d;
+                for (int i = 0; i < d; ++i) oh[i] = 0.0;
+                for (int64_t t = 0; t < N; ++t)
+                    for (int i = 0; i < d; ++i) oh[i] += w[t] * V[t * d + i];
+                for (int i = 0; i < d; ++i) oh[i] /= l;
+            }
+        }
+    free(K);
+    free(V);
+    free(zq);
+    free(w);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Cosine refinement of a codebook (NSNQuant, Metodologia sec. 3: the k-means */
 /* codebook on standard-normal samples is refined to minimise the cosine     */
 /* distance between the vectors and their quantised versions).  Reading:     */

@@ -61,6 +61,11 @@ int kvqo_nsn_attention(int d, int sub, int64_t B, int64_t Hq, int64_t Hkv, int64
                        const uint8_t *kc, const double *ks1, const double *ks2, const double *ko, const uint8_t *vc,
                        const double *vs1, const double *vs2, const double *vo, const double *cb, double sm_scale,
                        double *out);
+int kvqo_nsn_attention_stream(int d, int sub, int64_t B, int64_t Hq, int64_t Hkv, int64_t T, int64_t Gs, int64_t R,
+                              const double *q, const uint8_t *kc, const double *ks1, const double *ks2,
+                              const double *ko, const uint8_t *vc, const double *vs1, const double *vs2,
+                              const double *vo, const double *kt, const double *vt, const double *cb,
+                              double sm_scale, double *out);
 int kvqo_kmeans(int64_t n, int dim, int K, const double *samples, const int64_t *init, int max_iter,
                 double *codebook, double *distortion);
 int kvqo_cosine_refine(int64_t n, int dim, int K, const double *samples, double *codebook, int passes,
@@ -171,6 +176,15 @@ int main(void)
     for (int route = 1; route <= 2; ++route)
         CHECK(kvqo_nsn_logits(route, d, sub, B, Hq, H, T, q, codes, s1, s2, o, cbk, lg) == 0);
     CHECK(kvqo_nsn_attention(d, sub, B, Hq, H, T, q, codes, s1, s2, o, codes, s1, s2, o, cbk, 0.1, att) == 0);
+    {   /* one group of T tokens (the means o are per (b, g)), and a window of R */
+        double *kt2 = zalloc(sizeof(double) * B * H * 5 * d);
+        for (int i = 0; i < B * H * 5 * d; ++i) kt2[i] = nrand();
+        CHECK(kvqo_nsn_attention_stream(d, sub, B, Hq, H, T, T, 5, q, codes, s1, s2, o, codes, s1, s2, o, kt2, kt2,
+                                        cbk, 0.1, att) == 0);
+        CHECK(kvqo_nsn_attention_stream(d, sub, B, Hq, H, 0, 1, 5, q, codes, s1, s2, o, codes, s1, s2, o, kt2, kt2,
+                                        cbk, 0.1, att) == 0);
+        free(kt2);
+    }
     /* k-means on a few samples */
     const int64_t ns = 2000;
     double *smp = zalloc(sizeof(double) * ns * sub), *kcb = zalloc(sizeof(double) * 16 * sub), dist[10];
