@@ -728,6 +728,89 @@ kvq_status kvq_nsn_attn_decode_splits(kvq_ctx *ctx, const void *q_f16, int64_t B
         kvq::launch_nsn_decode(ctx, q_f16, B, H_q, T, kv, sm_scale, out, ws, ns, (hipStream_t)stream));
 }
 
+size_t kvq_nsn_flush_ws_bytes(const kvq_ctx *ctx, int64_t B, int64_t Gs)
+{
+    if (!ctx || B < 1 || Gs < 1) return 0;
+    return kvq::nsn_ws_bytes(B * ctx->H, Gs);
+}
+
+kvq_status kvq_nsn_flush(kvq_ctx *ctx, const void *k_tail_f16, const void *v_tail_f16, int64_t B, int64_t H_kv,
+                         int64_t Gs, int64_t R_cap, uint8_t *k_codes, float *k_s1, float *k_s2, float *k_o,
+                         uint8_t *v_codes, float *v_s1, float *v_s2, float *v_o, int64_t T0, int64_t T_cap, void *ws,
+                         size_t ws_bytes, void *stream)
+{
+    if (!ctx || ctx->mode != KVQ_MODE_NSN_VQ) return KVQ_E_INVAL;
+    if (B < 0 || H_kv != ctx->H || Gs < 64 || Gs % 64 || Gs > R_cap || T0 < 0 || T0 % Gs || T_cap % Gs ||
+        T0 + Gs > T_cap)
+        return KVQ_E_INVAL;
+    if (B == 0) return KVQ_OK;
+    if (!k_tail_f16 || !v_tail_f16 || !k_codes || !k_s1 || !k_s2 || !k_o || !v_codes || !v_s1 || !v_s2 || !v_o || !ws)
+        return KVQ_E_INVAL;
+    if (!aligned(k_tail_f16, 16) || !aligned(v_tail_f16, 16) || !aligned(k_codes, 16) || !aligned(v_codes, 16) ||
+        !aligned(k_s1, 4) || !aligned(k_s2, 4) || !aligned(v_s1, 4) || !aligned(v_s2, 4) || !aligned(k_o, 16) ||
+        !aligned(v_o, 16) || !aligned(ws, 256))
+        return KVQ_E_INVAL;
+    if (T_cap > (int64_t(1) << 31) || R_cap > (int64_t(1) << 31) || B * H_kv > (int64_t(1) << 20)) return KVQ_E_INVAL;
+    if (ws_bytes < kvq::nsn_ws_bytes(B * H_kv, Gs)) return KVQ_E_WORKSPACE;
+    DeviceGuard g(ctx->device);
+    if (!g.ok) return KVQ_E_DEVICE;
+    const int64_t H = B * H_kv, grp = T0 / Gs, ldo = (T_cap / Gs) * kvq::kD;
+    hipError_t e = kvq::launch_nsn_vq_strided(ctx, k_tail_f16, H, Gs, R_cap, k_codes + T0 * 16, k_s1 + T0, k_s2 + T0,
+                                              T_cap, k_o + grp * kvq::kD, ldo, ws, (hipStream_t)stream);
+    if (e == hipSuccess)
+        e = kvq::launch_nsn_vq_strided(ctx, v_tail_f16, H, Gs, R_cap, v_codes + T0 * 16, v_s1 + T0, v_s2 + T0, T_cap,
+                                       v_o + grp * kvq::kD, ldo, ws, (hipStream_t)stream);
+    return launch_status(e);
+}
+
+size_t kvq_nsn_attn_decode_stream_ws_bytes(const kvq_ctx *ctx, int64_t B, int64_t H_q, int64_t T_cap)
+{
+    if (!ctx || B < 1 || H_q < 1 || T_cap < 0) return 0;
+    return kvq::nsn_stream_ws_bytes(B, H_q, T_cap);
+}
+
+kvq_status kvq_nsn_attn_decode_stream(kvq_ctx *ctx, const void *q_f16, int64_t B, int64_t H_q, int64_t T,
+                                      int64_t T_cap, int64_t Gs, const uint8_t *k_codes, const float *k_s1,
+                                      const float *k_s2, const float *k_o, const uint8_t *v_codes, const float *v_s1,
+                                      const float *v_s2, const float *v_o, int64_t R, int64_t R_cap,
+                                      const void *k_tail_f16, const void *v_tail_f16, float sm_scale, float *out,
+                                      void *ws, size_t ws_bytes, int32_t n_split, void *stream)
+{
+    if (!ctx || ctx->mode != KVQ_MODE_NSN_VQ) return KVQ_E_INVAL;
+    if (B < 0 || H_q < 1 || H_q % ctx->H) return KVQ_E_INVAL;
+    const int64_t G = H_q / ctx->H;
+    if (G != 1 && G != 2 && G != 4) return KVQ_E_INVAL;
+    if (Gs < 64 || Gs % 64 || T < 0 || T > T_cap || T % Gs || T_cap % Gs) return KVQ_E_INVAL;
+    if (R < 0 || R > R_cap || T + R < 1 || n_split < 0) return KVQ_E_INVAL;
+    if (!std::isfinite(sm_scale) || sm_scale < 0.f) return KVQ_E_INVAL;
+    if (T_cap > (int64_t(1) << 31) || R_cap > (int64_t(1) << 31) || B * ctx->H > 65535) return KVQ_E_INVAL;
+    if (T > (int64_t)(kvq::kMaxSplits - 1) * kvq::kNsnMaxGroupsBlk * Gs) return KVQ_E_INVAL;
+    if (B == 0) return KVQ_OK;
+    if (!q_f16 || !out || !ws) return KVQ_E_INVAL;
+    if (T > 0 && (!k_codes || !k_s1 || !k_s2 || !k_o || !v_codes || !v_s1 || !v_s2 || !v_o)) return KVQ_E_INVAL;
+    if (R > 0 && (!k_tail_f16 || !v_tail_f16)) return KVQ_E_INVAL;
+    if (!aligned(q_f16, 16) || !aligned(out, 16) || !aligned(ws, 256)) return KVQ_E_INVAL;
+    if (T > 0 && (!aligned(k_codes, 16) || !aligned(v_codes, 16) || !aligned(k_s1, 4) || !aligned(k_s2, 4) ||
+                  !aligned(v_s1, 4) || !aligned(v_s2, 4) || !aligned(k_o, 16) || !aligned(v_o, 16)))
+        return KVQ_E_INVAL;
+    if (R > 0 && (!aligned(k_tail_f16, 16) || !aligned(v_tail_f16, 16))) return KVQ_E_INVAL;
+    if (ws_bytes < kvq::nsn_stream_ws_bytes(B, H_q, T_cap)) return KVQ_E_WORKSPACE;
+    int ns = 1;
+    if (T > 0) {
+        ns = n_split == 0 ? kvq::nsn_decode_auto_splits(ctx, B, T) : n_split;
+        const int64_t cap = std::min<int64_t>(T / 64, kvq::kMaxSplits - 1);
+        if (ns > cap) ns = (int)cap;
+        if (ns < 1) ns = 1;
+    }
+    if (sm_scale == 0.f) sm_scale = 1.0f / std::sqrt((float)kvq::kD);
+    DeviceGuard g(ctx->device);
+    if (!g.ok) return KVQ_E_DEVICE;
+    const kvq::NsnKV kv{k_codes, k_s1, k_s2, k_o, v_codes, v_s1, v_s2, v_o};
+    const kvq::NsnStream st{T_cap, Gs, k_tail_f16, v_tail_f16, R, R_cap};
+    return launch_status(kvq::launch_nsn_decode_stream(ctx, q_f16, B, H_q, T, kv, st, sm_scale, out, ws, ns,
+                                                       (hipStream_t)stream));
+}
+
 kvq_status kvq_nsn_attn_decode(kvq_ctx *ctx, const void *q_f16, int64_t B, int64_t H_q, int64_t T,
                                const uint8_t *k_codes, const float *k_s1, const float *k_s2, const float *k_o,
                                const uint8_t *v_codes, const float *v_s1, const float *v_s2, const float *v_o,

@@ -120,6 +120,10 @@ size_t nsn_ws_bytes(int64_t H, int64_t T);
 
 hipError_t launch_nsn_vq(const kvq_ctx *ctx, const void *x, int64_t H, int64_t T, uint8_t *codes,
                          float *s1, float *s2, float *o, void *ws, hipStream_t s);
+// The same over H heads of T tokens held ldx tokens apart (input), written
+// ldt tokens apart (codes, s1, s2) with the means ldo floats apart.
+hipError_t launch_nsn_vq_strided(const kvq_ctx *ctx, const void *x, int64_t H, int64_t T, int64_t ldx, uint8_t *codes,
+                                 float *s1, float *s2, int64_t ldt, float *o, int64_t ldo, void *ws, hipStream_t s);
 
 // NSN-VQ encoded keys and values of one decode call (outputs of kvq_nsn_vq_quantize).
 struct NsnKV {
@@ -138,5 +142,22 @@ int nsn_decode_auto_splits(const kvq_ctx *ctx, int64_t B, int64_t T);
 size_t nsn_decode_ws_bytes(int64_t B, int64_t Hq, int64_t T);
 hipError_t launch_nsn_decode(const kvq_ctx *ctx, const void *q, int64_t B, int64_t Hq, int64_t T, const NsnKV &kv,
                              float sm_scale, float *out, void *ws, int n_split, hipStream_t s);
+
+// Streaming NSN-VQ cache: packed rows of T_cap tokens flushed in groups of Gs
+// tokens, each group with its own K and V means ([B Hkv][T_cap / Gs][128]
+// fp32, in NsnKV's ko and vo), and a window of R (of R_cap) fp16 tokens.
+struct NsnStream {
+    int64_t T_cap, Gs;
+    const void *kt, *vt;
+    int64_t R, R_cap;
+};
+constexpr int kNsnMaxGroupsBlk = 32;  // flush groups one decode block covers at most
+// tokens per split: a multiple of Gs (itself a multiple of 64), at most
+// kNsnMaxGroupsBlk groups; 0 if T needs more than kMaxSplits - 1 such splits
+int64_t nsn_stream_chunk(int64_t T, int n_split, int64_t Gs);
+size_t nsn_stream_ws_bytes(int64_t B, int64_t Hq, int64_t T_cap);
+hipError_t launch_nsn_decode_stream(const kvq_ctx *ctx, const void *q, int64_t B, int64_t Hq, int64_t T,
+                                    const NsnKV &kv, const NsnStream &st, float sm_scale, float *out, void *ws,
+                                    int n_split, hipStream_t s);
 
 }  // namespace kvq

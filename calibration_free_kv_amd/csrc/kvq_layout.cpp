@@ -65,4 +65,23 @@ size_t nsn_decode_ws_bytes(int64_t B, int64_t Hq, int64_t T)
     return (size_t)B * Hq * decode_max_splits(T) * kNsnPartStride * sizeof(float);
 }
 
+// Streaming NSN-VQ decode: splits hold whole flush groups (Gs tokens, a
+// multiple of 64) and at most kNsnMaxGroupsBlk of them; one partial slot per
+// split (at most kMaxSplits - 1) plus the window's.
+int64_t nsn_stream_chunk(int64_t T, int n_split, int64_t Gs)
+{
+    const int64_t per = (T + n_split - 1) / n_split;
+    int64_t chunk = (per + Gs - 1) / Gs * Gs;
+    if (chunk > kNsnMaxGroupsBlk * Gs) chunk = kNsnMaxGroupsBlk * Gs;
+    if ((T + chunk - 1) / chunk > kMaxSplits - 1) return 0;
+    return chunk;
+}
+
+size_t nsn_stream_ws_bytes(int64_t B, int64_t Hq, int64_t T_cap)
+{
+    int64_t slots = (T_cap + 63) / 64;
+    if (slots > kMaxSplits - 1) slots = kMaxSplits - 1;
+    return (size_t)B * Hq * (slots + 1) * kNsnPartStride * sizeof(float);
+}
+
 }  // namespace kvq

@@ -88,7 +88,8 @@ __device__ __forceinline__ float norm2_f16(const uint32_t *w)
 // the chunk hold a copy of the last row and get the factor 0.
 constexpr int kStatWaves = 8;
 __global__ __launch_bounds__(64 * kStatWaves) void k_nsn_stats(const u4_t *__restrict__ x,
-                                                               float *__restrict__ part, int64_t T, int n_chunks)
+                                                               float *__restrict__ part, int64_t T, int n_chunks,
+                                                               int64_t ldx)
 {
     __shared__ u4_t lds[kStatWaves][kTile * 16];  // 128 KiB
     __shared__ float red[kStatWaves][kD];
@@ -96,7 +97,7 @@ __global__ __launch_bounds__(64 * kStatWaves) void k_nsn_stats(const u4_t *__res
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int h = blockIdx.x / n_chunks, chunk = blockIdx.x % n_chunks;
     const int64_t c0 = (int64_t)chunk * kChunk, c1 = min(T, c0 + kChunk);
-    const u4_t *xh = x + (int64_t)h * T * 16;
+    const u4_t *xh = x + (int64_t)h * ldx * 16;  // the head's tokens (ldx apart per head)
     u4_t *L = lds[wv];
     const uint32_t *Ld = (const uint32_t *)L;
     // dword `lane` of row t sits at 64 t + 4 ((lane / 4 + t) mod 16) + lane mod 4
@@ -149,7 +150,8 @@ __global__ __launch_bounds__(64 * kStatWaves) void k_nsn_stats(const u4_t *__res
 // then the 8 group sums are added in order.
 constexpr int kMeanGroups = 8;
 __global__ __launch_bounds__(kD * kMeanGroups) void k_nsn_mean(const float *__restrict__ part,
-                                                              float *__restrict__ o, int64_t T, int n_chunks)
+                                                              float *__restrict__ o, int64_t T, int n_chunks,
+                                                              int64_t ldo)
 {
     __shared__ float red[kMeanGroups][kD];
     const int h = blockIdx.x, i = threadIdx.x & (kD - 1), j = threadIdx.x >> 7;
@@ -170,7 +172,7 @@ __global__ __launch_bounds__(kD * kMeanGroups) void k_nsn_mean(const float *__re
         float t = 0.0f;
 #pragma unroll
         for (int g = 0; g < kMeanGroups; ++g) t += red[g][i];
-        o[h * kD + i] = t / (float)T;
+        o[h * ldo + i] = t / (float)T;
     }
 }
 
@@ -352,8 +354,11 @@ __device__ __forceinline__ int other_half_i(int x, bool upper)
 template <bool CB_LO, bool ADAPT>
 // o: channel means [H][128]
 __global__ __launch_bounds__(kWavesN * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_nsn_vq(
-    VqArgs a, const float *__restrict__ o, int64_t T, int H, int64_t tiles_per_h, int64_t n_tiles)
+    VqArgs a, const float *__restrict__ o, int64_t T, int H, int64_t tiles_per_h, int64_t n_tiles, int64_t ldx,
+    int64_t ldo, int64_t ldt)
 {
+    // ldx, ldt: tokens between heads in the input and in the outputs; ldo:
+    // floats between the heads' means
     __shared__ u4_t s_cbA[2 * kVqK];  // entry j, half q: dims 4q .. 4q+3 of C_hi, twice
     __shared__ u2_t s_cbl[2 * kVqK];  // lo parts, dims 4q .. 4q+3 at 2 j + q
     __shared__ float s_bias[kVqK];
@@ -387,7 +392,7 @@ __global__ __launch_bounds__(kWavesN * 64) __attribute__((amdgpu_waves_per_eu(2,
         const int64_t hq = t / tph;
         const int64_t tq = (t - hq * tph) * kTileN;
         const int nq = (int)min((int64_t)kTileN, T - tq);
-        nsn_tile_to_lds(a.x + (hq * T + tq) * 16, nq, o + hq * kD, L, L + kRowsN + 32 * slot, lane);
+        nsn_tile_to_lds(a.x + (hq * ldx + tq) * 16, nq, o + hq * ldo, L, L + kRowsN + 32 * slot, lane);
     };
     uint32_t w[32];
     int ord = 0;  // ordinal of the current tile among this wave's: its means are in slot ord % 2
@@ -400,7 +405,7 @@ __global__ __launch_bounds__(kWavesN * 64) __attribute__((amdgpu_waves_per_eu(2,
         const int64_t hh = tile / tph;
         const int64_t t0 = (tile - hh * tph) * kTileN;
         const int nv = (int)min((int64_t)kTileN, T - t0);
-        const int64_t v0 = hh * T + t0;
+        const int64_t v0 = hh * ldt + t0;
 
         // ||x||^2: this half's chain, then (half 0) + (half 1) as norm2_f16
         float ss = 0.0f;
@@ -597,11 +602,17 @@ __global__ __launch_bounds__(kWavesN * 64) __attribute__((amdgpu_waves_per_eu(2,
 hipError_t launch_nsn_vq(const kvq_ctx *ctx, const void *x, int64_t H, int64_t T, uint8_t *codes, float *s1,
                          float *s2, float *o, void *ws, hipStream_t s)
 {
+    return launch_nsn_vq_strided(ctx, x, H, T, T, codes, s1, s2, T, o, kD, ws, s);
+}
+
+hipError_t launch_nsn_vq_strided(const kvq_ctx *ctx, const void *x, int64_t H, int64_t T, int64_t ldx, uint8_t *codes,
+                                 float *s1, float *s2, int64_t ldt, float *o, int64_t ldo, void *ws, hipStream_t s)
+{
     const int n_chunks = (int)((T + kChunk - 1) / kChunk);
     float *part = (float *)ws;
     hipLaunchKernelGGL(k_nsn_stats, dim3((unsigned)(H * n_chunks)), dim3(64 * kStatWaves), 0, s, (const u4_t *)x, part, T,
-                       n_chunks);
-    hipLaunchKernelGGL(k_nsn_mean, dim3((unsigned)H), dim3(kD * kMeanGroups), 0, s, part, o, T, n_chunks);
+                       n_chunks, ldx);
+    hipLaunchKernelGGL(k_nsn_mean, dim3((unsigned)H), dim3(kD * kMeanGroups), 0, s, part, o, T, n_chunks, ldo);
     VqArgs a{};
     a.x = (const u4_t *)x;
     a.cb_hi = (const u4_t *)ctx->d_vq16;
@@ -618,7 +629,7 @@ hipError_t launch_nsn_vq(const kvq_ctx *ctx, const void *x, int64_t H, int64_t T
     const bool adapt = (ctx->nsn_options & KVQ_NSN_ADAPTIVE_SCALE) != 0;
 #define KVQ_NSN_LAUNCH(LO, AD)                                                                                     \
     hipLaunchKernelGGL((k_nsn_vq<LO, AD>), dim3((unsigned)blocks), dim3(kWavesN * 64), 0, s, a, (const float *)o, T, \
-                       (int)H, tiles_per_h, n_tiles)
+                       (int)H, tiles_per_h, n_tiles, ldx, ldo, ldt)
     if (ctx->vq_exact_f16) {
         if (adapt) KVQ_NSN_LAUNCH(false, true); else KVQ_NSN_LAUNCH(false, false);
     } else {

@@ -49,8 +49,8 @@ struct alignas(16) NsnSmem {
 // with a barrier.  Table entry (s, j, h) = sum_k q'_h[8 s + k] C_j[k], one
 // fp32 chain over k.
 template <int G, int NT>
-__device__ void nsn_tables(const half_t *__restrict__ q, const float *__restrict__ o, const float *__restrict__ cb,
-                           int64_t bg, int64_t qbase, NsnSmem<G> &sm)
+__device__ void nsn_tables(const half_t *__restrict__ q, const float *__restrict__ obg, const float *__restrict__ cb,
+                           int64_t qbase, NsnSmem<G> &sm)
 {
     static_assert(NT % kVqK == 0, "one thread per entry and sub-vector group");
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -58,7 +58,7 @@ __device__ void nsn_tables(const half_t *__restrict__ q, const float *__restrict
         reinterpret_cast<f4_t *>(sm.cb)[i] = reinterpret_cast<const f4_t *>(cb)[i];
     for (int h = wv; h < G; h += NT / 64) {
         const h2_t pr = reinterpret_cast<const h2_t *>(q + (qbase + h) * kD)[lane];
-        const f2_t ov = reinterpret_cast<const f2_t *>(o + bg * kD)[lane];
+        const f2_t ov = reinterpret_cast<const f2_t *>(obg)[lane];
         float x0 = (float)pr.x, x1 = (float)pr.y;
         const float qo = wave_sum(fmaf(x1, ov.y, x0 * ov.x));
         wave_fwht(x0, x1, lane);
@@ -133,7 +133,7 @@ __global__ __launch_bounds__(kThreadsN) void k_nsn_logits(const half_t *__restri
         a[i] = s1[v];
         c[i] = s2[v];
     }
-    nsn_tables<G, kThreadsN>(q, o, cb, bg, qbase, sm);
+    nsn_tables<G, kThreadsN>(q, o + bg * kD, cb, qbase, sm);
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
         const int64_t t = c0 + threadIdx.x + i * kThreadsN;
@@ -154,11 +154,19 @@ __global__ __launch_bounds__(kThreadsN) void k_nsn_logits(const half_t *__restri
 // all G heads and walks the tile's tokens, reading each token's entry index
 // and its weights p s1_V s2_V from LDS.  The waves then merge in LDS and the
 // block writes {acc[128], M, L, WO} per head to the workspace.
-template <int G>
+// Streaming cache (GROUPED): the packed tokens were flushed in groups of
+// gsize tokens, each with its own means; a block's range covers at most
+// kMaxGroupsBlk groups, whose K means enter the logits as <q, o^K_g> and whose
+// V means enter the value sums in the code domain as H o^V_g / sqrt(d) times
+// the tile's sum of p s1_V (a 64-token tile lies in one group).
+constexpr int kMaxGroupsBlk = kNsnMaxGroupsBlk;
+template <int G, bool GROUPED>
 struct DecodeSmem {
     NsnSmem<G> t;
     u4_t vcode[dec_waves<G>()][64];
     float wts[dec_waves<G>()][64][G];
+    float og[GROUPED ? kMaxGroupsBlk : 1][kD];  // H o^V_g / sqrt(d)
+    float qog[GROUPED ? kMaxGroupsBlk : 1][G];  // <q_h, o^K_g>
 };
 // One lane's token of a decode tile: K and V codes and byproducts.
 struct TileIn {
@@ -173,16 +181,23 @@ __device__ __forceinline__ TileIn load_tile(const u4_t *kc, const float *ks1, co
 }
 constexpr int kPartStride = kNsnPartStride;  // floats per (split, head) partial: acc[128], M, L, WO, pad
 
-template <int G>
+// ldt: tokens between (b, g) rows of the packed arrays; n_part: partial
+// slots per (b, g) (one more than the splits when a window partial follows);
+// GROUPED: ko, vo are per-group means [B Hkv][ngc][128] of groups of gsize
+// tokens (gsize and the range start multiples of 64 and of gsize), else the
+// per-(b, g) means [B Hkv][128].
+template <int G, bool GROUPED>
 __global__ __launch_bounds__(64 * dec_waves<G>()) void k_nsn_part(const half_t *__restrict__ q, const u4_t *__restrict__ kc,
                                                         const float *__restrict__ ks1, const float *__restrict__ ks2,
                                                         const float *__restrict__ ko, const u4_t *__restrict__ vc,
                                                         const float *__restrict__ vs1, const float *__restrict__ vs2,
                                                         const float *__restrict__ cb, float *__restrict__ part,
-                                                        int64_t Hkv, int64_t T, int64_t chunk, float scale2)
+                                                        int64_t Hkv, int64_t T, int64_t chunk, float scale2,
+                                                        int64_t ldt, int n_part, const float *__restrict__ vo,
+                                                        int64_t gsize, int64_t ngc)
 {
     constexpr int NW = dec_waves<G>();
-    __shared__ DecodeSmem<G> sm;
+    __shared__ DecodeSmem<G, GROUPED> sm;
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t bg = blockIdx.y, b = bg / Hkv, g = bg % Hkv;
@@ -191,8 +206,29 @@ __global__ __launch_bounds__(64 * dec_waves<G>()) void k_nsn_part(const half_t *
     // The first tile's loads go out before the prologue, every later tile's
     // before the current one is processed.
     int64_t t0 = c0 + 64 * wv;
-    TileIn cur = load_tile(kc, ks1, ks2, vc, vs1, vs2, bg * T, t0 + lane < c1 ? t0 + lane : t0);
-    nsn_tables<G, 64 * NW>(q, ko, cb, bg, qbase, sm.t);
+    TileIn cur = load_tile(kc, ks1, ks2, vc, vs1, vs2, bg * ldt, t0 + lane < c1 ? t0 + lane : t0);
+    const int64_t gfirst = GROUPED ? c0 / gsize : 0;
+    nsn_tables<G, 64 * NW>(q, GROUPED ? ko + (bg * ngc + gfirst) * kD : ko + bg * kD, cb, qbase, sm.t);
+    if constexpr (GROUPED) {
+        // the block's groups: rotated V means and <q_h, o^K_g> = <q'_h, H o^K_g / sqrt(d)>
+        const int ngb = (int)((c1 - c0 + gsize - 1) / gsize);
+        for (int gi = wv; gi < ngb; gi += NW) {
+            const int64_t row = (bg * ngc + gfirst + gi) * kD;
+            const f2_t ovv = reinterpret_cast<const f2_t *>(vo + row)[lane];
+            const f2_t okk = reinterpret_cast<const f2_t *>(ko + row)[lane];
+            float v0 = ovv.x, v1 = ovv.y, k0 = okk.x, k1 = okk.y;
+            wave_fwht(v0, v1, lane);
+            wave_fwht(k0, k1, lane);
+            reinterpret_cast<f2_t *>(sm.og[gi])[lane] = f2_t{v0 * kInvSqrtD, v1 * kInvSqrtD};
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                const f2_t qq = reinterpret_cast<const f2_t *>(sm.t.qs + h * kD)[lane];
+                const float d = wave_sum(fmaf(qq.x, k0 * kInvSqrtD, qq.y * (k1 * kInvSqrtD)));
+                if (lane == 0) sm.qog[gi][h] = d;
+            }
+        }
+        __syncthreads();
+    }
 
     float m[G], l[G], wo[G], acc[G][2];
 #pragma unroll
@@ -208,21 +244,30 @@ __global__ __launch_bounds__(64 * dec_waves<G>()) void k_nsn_part(const half_t *
         const bool valid = t0 + lane < c1;
         const int64_t tn = t0 + 64 * NW;
         TileIn nxt = cur;
-        if (tn < c1) nxt = load_tile(kc, ks1, ks2, vc, vs1, vs2, bg * T, tn + lane < c1 ? tn + lane : tn);
+        if (tn < c1) nxt = load_tile(kc, ks1, ks2, vc, vs1, vs2, bg * ldt, tn + lane < c1 ? tn + lane : tn);
         float ks[G];
         nsn_key_sum<G>(cur.kcode, sm.t.tab, ks);
         float w[G];
+        const int gi = GROUPED ? (int)((t0 - c0) / gsize) : 0;  // the tile's group (wave-uniform)
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-            const float lg = valid ? cur.a * fmaf(cur.c, ks[h], sm.t.qo[h]) * scale2 : -__builtin_inff();
+            const float qoh = GROUPED ? sm.qog[gi][h] : sm.t.qo[h];
+            const float lg = valid ? cur.a * fmaf(cur.c, ks[h], qoh) * scale2 : -__builtin_inff();
             const float mn = fmaxf(m[h], wave_max(lg));
             const float alpha = __builtin_amdgcn_exp2f(m[h] - mn);
             const float p = __builtin_amdgcn_exp2f(lg - mn);
             m[h] = mn;
             l[h] = fmaf(l[h], alpha, p);
-            wo[h] = fmaf(wo[h], alpha, p * cur.e1);
             acc[h][0] *= alpha;
             acc[h][1] *= alpha;
+            if constexpr (GROUPED) {
+                // the tile's sum of p s1_V times its group's rotated V mean
+                const float wt = wave_sum(p * cur.e1);
+                acc[h][0] = fmaf(wt, sm.og[gi][8 * vs + vk], acc[h][0]);
+                acc[h][1] = fmaf(wt, sm.og[gi][8 * vs + vk + 1], acc[h][1]);
+            } else {
+                wo[h] = fmaf(wo[h], alpha, p * cur.e1);
+            }
             w[h] = p * cur.e1 * cur.e2;
         }
         sm.vcode[wv][lane] = cur.vcode;
@@ -266,7 +311,7 @@ __global__ __launch_bounds__(64 * dec_waves<G>()) void k_nsn_part(const half_t *
         }
     }
     __syncthreads();
-    const int64_t split = blockIdx.x, n_split = gridDim.x;
+    const int64_t split = blockIdx.x;
     for (int i = threadIdx.x; i < G * kD; i += 64 * NW) {
         const int h = i / kD, dim = i % kD;
         float M = -__builtin_inff();
@@ -281,7 +326,7 @@ __global__ __launch_bounds__(64 * dec_waves<G>()) void k_nsn_part(const half_t *
             L = fmaf(f, p[kD + 1], L);
             WO = fmaf(f, p[kD + 2], WO);
         }
-        float *dst = part + ((bg * n_split + split) * G + h) * kPartStride;
+        float *dst = part + ((bg * n_part + split) * G + h) * kPartStride;
         dst[dim] = A;
         if (dim == 0) {
             dst[kD] = M;
@@ -292,8 +337,9 @@ __global__ __launch_bounds__(64 * dec_waves<G>()) void k_nsn_part(const half_t *
 }
 
 // Decode, part 2.  Block b * Hkv + g, one wave per head h (lane: dimensions
-// 2 lane, 2 lane + 1): merge of the splits, f_s = 2^(M_s - M), then
-// out = (H acc / sqrt(d) + WO o_V) / L.
+// 2 lane, 2 lane + 1): merge of the n_split partial slots, f_s = 2^(M_s - M),
+// then out = (H acc / sqrt(d) + WO o_V) / L (vo NULL: the V means are already
+// in acc, WO = 0).
 template <int G>
 __global__ __launch_bounds__(64 * G) void k_nsn_merge(const float *__restrict__ part, const float *__restrict__ vo,
                                                       float *__restrict__ out, int64_t Hkv, int n_split)
@@ -344,10 +390,45 @@ __global__ __launch_bounds__(64 * G) void k_nsn_merge(const float *__restrict__ 
         }
     }
     wave_fwht(x0, x1, lane);
-    const f2_t ov = reinterpret_cast<const f2_t *>(vo + bg * kD)[lane];
+    const f2_t ov = vo ? reinterpret_cast<const f2_t *>(vo + bg * kD)[lane] : f2_t{0.0f, 0.0f};
     const float inv = 1.0f / L;
     reinterpret_cast<f2_t *>(out + ((b * Hkv + g) * G + h) * kD)[lane] =
         f2_t{fmaf(x0, kInvSqrtD, WO * ov.x) * inv, fmaf(x1, kInvSqrtD, WO * ov.y) * inv};
+}
+
+// Window of a streaming cache: the partial of its R fp16 tokens for the G
+// query heads of (b, g) in the convention of k_nsn_part (base-2 scores,
+// acc = H (sum_t 2^(s_t - M) v_t) / sqrt(d) so that the merge's transform
+// returns the plain sum, WO = 0), written to slot `slot` of n_part; with no
+// packed tokens (direct) the output itself.  One wave per query head.
+template <int G>
+__global__ __launch_bounds__(64 * G) void k_nsn_tail(const half_t *__restrict__ q, const half_t *__restrict__ kt,
+                                                     const half_t *__restrict__ vt, float scale2,
+                                                     float *__restrict__ part, float *__restrict__ out, int64_t R,
+                                                     int64_t R_cap, int n_part, int slot, bool direct)
+{
+    __shared__ __align__(16) float qf[G][kD];
+    const int lane = threadIdx.x & 63, h = threadIdx.x >> 6;
+    const int64_t bg = blockIdx.x;
+    const int64_t qrow = bg * G + h;  // (b Hkv + g) G + h = b Hq + g G + h
+    const WindowPartial w = window_partial(qf[h], kt + bg * R_cap * kD, vt + bg * R_cap * kD, R, scale2, lane, [&] {
+        const h2_t pr = reinterpret_cast<const h2_t *>(q + qrow * kD)[lane];
+        reinterpret_cast<f2_t *>(qf[h])[lane] = f2_t{(float)pr.x, (float)pr.y};
+    });
+    if (direct) {
+        const float inv = 1.0f / w.l;
+        reinterpret_cast<f2_t *>(out + qrow * kD)[lane] = f2_t{w.a0 * inv, w.a1 * inv};
+        return;
+    }
+    float x0 = w.a0, x1 = w.a1;
+    wave_fwht(x0, x1, lane);
+    float *dst = part + ((bg * n_part + slot) * G + h) * kPartStride;
+    reinterpret_cast<f2_t *>(dst)[lane] = f2_t{x0 * kInvSqrtD, x1 * kInvSqrtD};
+    if (lane == 0) {
+        dst[kD] = w.m;
+        dst[kD + 1] = w.l;
+        dst[kD + 2] = 0.0f;
+    }
 }
 
 template <int G>
@@ -367,11 +448,44 @@ hipError_t decode_g(const kvq_ctx *ctx, const void *q, int64_t B, int64_t T, con
     const int64_t chunk = nsn_decode_chunk(T, n_split);
     const int ns = (int)((T + chunk - 1) / chunk);
     float *part = (float *)ws;
-    hipLaunchKernelGGL(k_nsn_part<G>, dim3((unsigned)ns, (unsigned)(B * ctx->H)), dim3(64 * dec_waves<G>()), 0, s,
-                       (const half_t *)q, (const u4_t *)kv.kc, kv.ks1, kv.ks2, kv.ko, (const u4_t *)kv.vc, kv.vs1,
-                       kv.vs2, ctx->d_vq, part, (int64_t)ctx->H, T, chunk, sm_scale * kLog2e);
+    hipLaunchKernelGGL((k_nsn_part<G, false>), dim3((unsigned)ns, (unsigned)(B * ctx->H)), dim3(64 * dec_waves<G>()),
+                       0, s, (const half_t *)q, (const u4_t *)kv.kc, kv.ks1, kv.ks2, kv.ko, (const u4_t *)kv.vc,
+                       kv.vs1, kv.vs2, ctx->d_vq, part, (int64_t)ctx->H, T, chunk, sm_scale * kLog2e, T, ns,
+                       (const float *)nullptr, (int64_t)0, (int64_t)0);
     hipLaunchKernelGGL(k_nsn_merge<G>, dim3((unsigned)(B * ctx->H)), dim3(64 * G), 0, s, part, kv.vo, out,
                        (int64_t)ctx->H, ns);
+    return hipGetLastError();
+}
+
+// Streaming cache: the window's partial (slot ns, or the output when T = 0),
+// the packed tokens' splits with per-group means, then the merge.
+template <int G>
+hipError_t decode_stream_g(const kvq_ctx *ctx, const void *q, int64_t B, int64_t T, const NsnKV &kv,
+                           const NsnStream &st, float sm_scale, float *out, void *ws, int n_split, hipStream_t s)
+{
+    static_assert(G <= 4, "the grouped decode block fits LDS for up to 4 query heads per KV head");
+    const float scale2 = sm_scale * kLog2e;
+    float *part = (float *)ws;
+    const int64_t bgs = B * ctx->H;
+    int ns = 0, n_part = 1;
+    int64_t chunk = 0;
+    if (T > 0) {
+        chunk = nsn_stream_chunk(T, n_split, st.Gs);
+        if (chunk == 0) return hipErrorInvalidValue;  // more splits than partial slots
+        ns = (int)((T + chunk - 1) / chunk);
+        n_part = ns + (st.R > 0 ? 1 : 0);
+    }
+    if (st.R > 0)
+        hipLaunchKernelGGL(k_nsn_tail<G>, dim3((unsigned)bgs), dim3(64 * G), 0, s, (const half_t *)q,
+                           (const half_t *)st.kt, (const half_t *)st.vt, scale2, part, out, st.R, st.R_cap, n_part,
+                           ns, T == 0);
+    if (T == 0) return hipGetLastError();
+    hipLaunchKernelGGL((k_nsn_part<G, true>), dim3((unsigned)ns, (unsigned)bgs), dim3(64 * dec_waves<G>()), 0, s,
+                       (const half_t *)q, (const u4_t *)kv.kc, kv.ks1, kv.ks2, kv.ko, (const u4_t *)kv.vc, kv.vs1,
+                       kv.vs2, ctx->d_vq, part, (int64_t)ctx->H, T, chunk, scale2, st.T_cap, n_part, kv.vo, st.Gs,
+                       st.T_cap / st.Gs);
+    hipLaunchKernelGGL(k_nsn_merge<G>, dim3((unsigned)bgs), dim3(64 * G), 0, s, part, (const float *)nullptr, out,
+                       (int64_t)ctx->H, n_part);
     return hipGetLastError();
 }
 
@@ -398,6 +512,18 @@ hipError_t launch_nsn_decode(const kvq_ctx *ctx, const void *q, int64_t B, int64
         case 2: return decode_g<2>(ctx, q, B, T, kv, sm_scale, out, ws, n_split, s);
         case 4: return decode_g<4>(ctx, q, B, T, kv, sm_scale, out, ws, n_split, s);
         case 8: return decode_g<8>(ctx, q, B, T, kv, sm_scale, out, ws, n_split, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_nsn_decode_stream(const kvq_ctx *ctx, const void *q, int64_t B, int64_t Hq, int64_t T,
+                                    const NsnKV &kv, const NsnStream &st, float sm_scale, float *out, void *ws,
+                                    int n_split, hipStream_t s)
+{
+    switch (Hq / ctx->H) {
+        case 1: return decode_stream_g<1>(ctx, q, B, T, kv, st, sm_scale, out, ws, n_split, s);
+        case 2: return decode_stream_g<2>(ctx, q, B, T, kv, st, sm_scale, out, ws, n_split, s);
+        case 4: return decode_stream_g<4>(ctx, q, B, T, kv, st, sm_scale, out, ws, n_split, s);
         default: return hipErrorInvalidValue;
     }
 }

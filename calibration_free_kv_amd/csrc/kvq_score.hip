@@ -946,11 +946,7 @@ hipError_t run_logits(const kvq_ctx *ctx, const void *q, int64_t B, int64_t Hq, 
 // the decode partials (base-2 scores s = scale_log2 <q, k>, acc in the
 // rotated domain: H (D_V .* sum_t 2^(s_t - m) v_t)), written to slot n_split
 // of the (b, g) partials; with no quantised tokens (direct) it writes the
-// output itself, sum_t 2^(s_t - m) v_t / l.  One wave per query head; per
-// 64-token chunk the lanes score one token each (the query from LDS), then
-// act as coordinate pairs (2 lane, 2 lane + 1) summing the values.  A chunk's
-// key rows and value pairs are loaded in one go (the first chunk's before
-// the query is staged).
+// output itself, sum_t 2^(s_t - m) v_t / l.  One wave per query head.
 template <int G>
 __global__ __launch_bounds__(64 * G) void k_tail(const half_t *__restrict__ q, const half_t *__restrict__ kt,
                                                  const half_t *__restrict__ vt, const float *__restrict__ signs_v,
@@ -963,73 +959,23 @@ __global__ __launch_bounds__(64 * G) void k_tail(const half_t *__restrict__ q, c
     const int64_t bh = blockIdx.x, b = bh / H;
     const int g = (int)(bh - b * H);
     const int64_t qrow = b * Hq + (int64_t)g * G + h;
-    const half_t *kb = kt + bh * R_cap * kD, *vb = vt + bh * R_cap * kD;
-    // one 64-token chunk: the lane's key row and the chunk's value pairs are
-    // loaded together with the query, so the three loads overlap
-    h8_t krow[kD / 8];
-    h2_t vrow[64];
-    auto load_chunk = [&](int64_t c) {
-        const int64_t t = c + lane < R ? c + lane : c;
-#pragma unroll
-        for (int i = 0; i < kD / 8; ++i) krow[i] = reinterpret_cast<const h8_t *>(kb + t * kD)[i];
-#pragma unroll
-        for (int u = 0; u < 64; ++u)
-            vrow[u] = reinterpret_cast<const h2_t *>(vb + (c + u < R ? c + u : c) * kD)[lane];
-    };
-    load_chunk(0);
-    {
+    const WindowPartial w = window_partial(qf[h], kt + bh * R_cap * kD, vt + bh * R_cap * kD, R, scale_log2, lane, [&] {
         const h2_t pr = reinterpret_cast<const h2_t *>(q + qrow * kD)[lane];
         reinterpret_cast<f2_t *>(qf[h])[lane] = f2_t{(float)pr.x, (float)pr.y};
-    }
-    wave_lds_sync();
-    float m = -INFINITY, l = 0.0f, a0 = 0.0f, a1 = 0.0f;
-    for (int64_t c = 0; c < R; c += 64) {
-        if (c > 0) load_chunk(c);
-        float acc = 0.0f;
-#pragma unroll
-        for (int i = 0; i < kD / 8; ++i) {
-            const h8_t kv = krow[i];
-            const f4_t q0 = reinterpret_cast<const f4_t *>(qf[h])[2 * i];
-            const f4_t q1 = reinterpret_cast<const f4_t *>(qf[h])[2 * i + 1];
-            acc = fmaf(q0.x, (float)kv[0], acc);
-            acc = fmaf(q0.y, (float)kv[1], acc);
-            acc = fmaf(q0.z, (float)kv[2], acc);
-            acc = fmaf(q0.w, (float)kv[3], acc);
-            acc = fmaf(q1.x, (float)kv[4], acc);
-            acc = fmaf(q1.y, (float)kv[5], acc);
-            acc = fmaf(q1.z, (float)kv[6], acc);
-            acc = fmaf(q1.w, (float)kv[7], acc);
-        }
-        const float sc = c + lane < R ? acc * scale_log2 : -INFINITY;
-        const float mn = fmaxf(m, wave_max(sc));
-        const float al = __builtin_amdgcn_exp2f(m - mn);
-        const float p = __builtin_amdgcn_exp2f(sc - mn);
-        m = mn;
-        l = fmaf(l, al, p);
-        a0 *= al;
-        a1 *= al;
-        // tokens past the end re-read the chunk's first one, with weight 0
-#pragma unroll
-        for (int u = 0; u < 64; ++u) {
-            const float pj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, p), u));
-            a0 = fmaf(pj, (float)vrow[u].x, a0);
-            a1 = fmaf(pj, (float)vrow[u].y, a1);
-        }
-    }
-    l = wave_sum(l);
+    });
     if (direct) {
-        const float inv = 1.0f / l;
-        reinterpret_cast<f2_t *>(out + qrow * kD)[lane] = f2_t{a0 * inv, a1 * inv};
+        const float inv = 1.0f / w.l;
+        reinterpret_cast<f2_t *>(out + qrow * kD)[lane] = f2_t{w.a0 * inv, w.a1 * inv};
         return;
     }
     const f2_t sv = reinterpret_cast<const f2_t *>(signs_v + g * kD)[lane];
-    float x0 = a0 * sv.x, x1 = a1 * sv.y;
+    float x0 = w.a0 * sv.x, x1 = w.a1 * sv.y;
     wave_fwht(x0, x1, lane);
     float *dst = part + ((bh * n_part + n_split) * G + h) * (kD + 2);
     reinterpret_cast<f2_t *>(dst + 2)[lane] = f2_t{x0, x1};
     if (lane == 0) {
-        dst[0] = m;
-        dst[1] = l;
+        dst[0] = w.m;
+        dst[1] = w.l;
     }
 }
 

@@ -141,5 +141,74 @@ __device__ __forceinline__ float block_gemv(const GemvSlice<NT> &g, const float 
     return y;
 }
 
+// Softmax partial of one query head over R full-precision tokens (fp16 rows
+// of 128 at kb, vb), by one wave.  Per 64-token chunk the lanes score one
+// token each against the fp32 query qf (LDS, staged by stage_query while
+// the first chunk's loads are in flight), then act as coordinate pairs
+// (2 lane, 2 lane + 1) summing the values.  Scores are base 2,
+// scale_log2 <q, k>; the result is the maximum m, the sum l of 2^(s_t - m)
+// (every lane) and the lane's pair of sum_t 2^(s_t - m) v_t.
+struct WindowPartial {
+    float m, l, a0, a1;
+};
+template <class StageQuery>
+__device__ __forceinline__ WindowPartial window_partial(const float *qf, const _Float16 *__restrict__ kb,
+                                                        const _Float16 *__restrict__ vb, int64_t R,
+                                                        float scale_log2, int lane, StageQuery stage_query)
+{
+    typedef _Float16 h8v __attribute__((ext_vector_type(8)));
+    typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+    typedef float f4v __attribute__((ext_vector_type(4)));
+    // one 64-token chunk: the lane's key row and the chunk's value pairs
+    h8v krow[128 / 8];
+    h2v vrow[64];
+    auto load_chunk = [&](int64_t c) {
+        const int64_t t = c + lane < R ? c + lane : c;
+#pragma unroll
+        for (int i = 0; i < 128 / 8; ++i) krow[i] = reinterpret_cast<const h8v *>(kb + t * 128)[i];
+#pragma unroll
+        for (int u = 0; u < 64; ++u)
+            vrow[u] = reinterpret_cast<const h2v *>(vb + (c + u < R ? c + u : c) * 128)[lane];
+    };
+    load_chunk(0);
+    stage_query();
+    wave_lds_sync();
+    float m = -__builtin_inff(), l = 0.0f, a0 = 0.0f, a1 = 0.0f;
+    for (int64_t c = 0; c < R; c += 64) {
+        if (c > 0) load_chunk(c);
+        float acc = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 128 / 8; ++i) {
+            const h8v kv = krow[i];
+            const f4v q0 = reinterpret_cast<const f4v *>(qf)[2 * i];
+            const f4v q1 = reinterpret_cast<const f4v *>(qf)[2 * i + 1];
+            acc = fmaf(q0.x, (float)kv[0], acc);
+            acc = fmaf(q0.y, (float)kv[1], acc);
+            acc = fmaf(q0.z, (float)kv[2], acc);
+            acc = fmaf(q0.w, (float)kv[3], acc);
+            acc = fmaf(q1.x, (float)kv[4], acc);
+            acc = fmaf(q1.y, (float)kv[5], acc);
+            acc = fmaf(q1.z, (float)kv[6], acc);
+            acc = fmaf(q1.w, (float)kv[7], acc);
+        }
+        const float sc = c + lane < R ? acc * scale_log2 : -__builtin_inff();
+        const float mn = fmaxf(m, wave_max(sc));
+        const float al = __builtin_amdgcn_exp2f(m - mn);
+        const float p = __builtin_amdgcn_exp2f(sc - mn);
+        m = mn;
+        l = fmaf(l, al, p);
+        a0 *= al;
+        a1 *= al;
+        // tokens past the end re-read the chunk's first one, with weight 0
+#pragma unroll
+        for (int u = 0; u < 64; ++u) {
+            const float pj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, p), u));
+            a0 = fmaf(pj, (float)vrow[u].x, a0);
+            a1 = fmaf(pj, (float)vrow[u].y, a1);
+        }
+    }
+    return WindowPartial{m, wave_sum(l), a0, a1};
+}
+
 }  // namespace
 }  // namespace kvq

@@ -30,6 +30,7 @@ EXPORTS = [
     "kvq_attn_decode_splits", "kvq_nsn_vq_ws_bytes", "kvq_nsn_vq_quantize", "kvq_nsn_logits",
     "kvq_nsn_attn_decode_ws_bytes", "kvq_nsn_attn_decode", "kvq_nsn_attn_decode_splits",
     "kvq_attn_decode_stream_ws_bytes", "kvq_attn_decode_stream", "kvq_flush", "kvq_attn_decode_noalloc",
+    "kvq_nsn_flush_ws_bytes", "kvq_nsn_flush", "kvq_nsn_attn_decode_stream_ws_bytes", "kvq_nsn_attn_decode_stream",
 ]
 
 
@@ -93,6 +94,14 @@ def lib():
                                           vp, sz, vp]
         L.kvq_nsn_attn_decode_splits.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp,
                                                  C.c_float, vp, vp, sz, i32, vp]
+        L.kvq_nsn_flush_ws_bytes.argtypes = [vp, i64, i64]
+        L.kvq_nsn_flush_ws_bytes.restype = sz
+        L.kvq_nsn_flush.argtypes = [vp, vp, vp, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, vp, sz,
+                                    vp]
+        L.kvq_nsn_attn_decode_stream_ws_bytes.argtypes = [vp, i64, i64, i64]
+        L.kvq_nsn_attn_decode_stream_ws_bytes.restype = sz
+        L.kvq_nsn_attn_decode_stream.argtypes = [vp, vp, i64, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp,
+                                                 i64, i64, vp, vp, C.c_float, vp, vp, sz, i32, vp]
         _lib = L
     return _lib
 
@@ -329,6 +338,47 @@ class Context:
                                    v["s2"], v["o"], sm_scale, out, ws, n_split)
         return out
 
+    def nsn_stream_alloc(self, B, T_cap, Gs):
+        """Packed arrays of a streaming NSN-VQ cache: codes [B,Hkv,T_cap,16], s1/s2
+        [B,Hkv,T_cap], means o [B,Hkv,T_cap/Gs,128], for K and V."""
+        dev, H = self.dev, self.n_kv_heads
+
+        def one():
+            return dict(codes=torch.zeros((B, H, T_cap, 16), dtype=torch.uint8, device=dev),
+                        s1=torch.zeros((B, H, T_cap), dtype=torch.float32, device=dev),
+                        s2=torch.zeros((B, H, T_cap), dtype=torch.float32, device=dev),
+                        o=torch.zeros((B, H, T_cap // Gs, D), dtype=torch.float32, device=dev))
+        return one(), one()
+
+    def nsn_flush(self, k_tail, v_tail, Gs, k, v, T0, ws=None):
+        """Encode the first Gs tokens of the fp16 windows [B,Hkv,R_cap,128] as flush
+        group T0 / Gs of the packed dicts k, v (layout of nsn_stream_alloc)."""
+        B, Hkv, R_cap, _ = k_tail.shape
+        if ws is None:
+            ws = torch.empty(int(lib().kvq_nsn_flush_ws_bytes(self.handle, B, Gs)), dtype=torch.uint8,
+                             device=k_tail.device)
+        kvq_nsn_flush(self, k_tail, v_tail, B, Hkv, Gs, R_cap, k["codes"], k["s1"], k["s2"], k["o"], v["codes"],
+                      v["s1"], v["s2"], v["o"], T0, k["codes"].shape[2], ws)
+
+    def nsn_stream_ws(self, B, Hq, T_cap):
+        n = int(lib().kvq_nsn_attn_decode_stream_ws_bytes(self.handle, B, Hq, T_cap))
+        return torch.empty(n, dtype=torch.uint8, device=self.dev)
+
+    def nsn_attn_decode_stream(self, q, k, v, T, Gs, k_tail, v_tail, R, sm_scale: float = 0.0, ws=None, out=None,
+                               n_split: int = 0):
+        """Decode over the first T packed tokens (dicts of nsn_stream_alloc) followed by the
+        first R tokens of the fp16 windows [B,Hkv,R_cap,128] -> out [B,Hq,128] fp32."""
+        _dev_tensor(q, torch.float16, "q")
+        B, Hq, _ = q.shape
+        T_cap, R_cap = k["codes"].shape[2], k_tail.shape[2]
+        if ws is None:
+            ws = self.nsn_stream_ws(B, Hq, T_cap)
+        if out is None:
+            out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+        kvq_nsn_attn_decode_stream(self, q, B, Hq, T, T_cap, Gs, k["codes"], k["s1"], k["s2"], k["o"], v["codes"],
+                                   v["s1"], v["s2"], v["o"], R, R_cap, k_tail, v_tail, sm_scale, out, ws, n_split)
+        return out
+
 
 # ---------------------------------------------------------------------- C-ABI mirrors
 def kvq_quantize(ctx: Context, kind, x, B, H_kv, T, codes, norms, qjl_signs=None, qjl_gamma=None):
@@ -422,3 +472,28 @@ def kvq_flush(ctx: Context, k_tail, v_tail, B, H_kv, R, R_cap, k_codes, k_norms,
         _dev_tensor(t, dt, n)
     _check(lib().kvq_flush(ctx.handle, _ptr(k_tail), _ptr(v_tail), B, H_kv, R, R_cap, _ptr(k_codes), _ptr(k_norms),
                            _ptr(v_codes), _ptr(v_norms), T0, T_cap, _stream(k_tail.device)), "kvq_flush")
+
+
+def kvq_nsn_flush(ctx: Context, k_tail, v_tail, B, H_kv, Gs, R_cap, kc, ks1, ks2, ko, vc, vs1, vs2, vo, T0, T_cap,
+                  ws):
+    _nsn_inputs(kc, ks1, ks2, ko, "k_")
+    _nsn_inputs(vc, vs1, vs2, vo, "v_")
+    _dev_tensor(k_tail, torch.float16, "k_tail")
+    _dev_tensor(v_tail, torch.float16, "v_tail")
+    _check(lib().kvq_nsn_flush(ctx.handle, _ptr(k_tail), _ptr(v_tail), B, H_kv, Gs, R_cap, _ptr(kc), _ptr(ks1),
+                               _ptr(ks2), _ptr(ko), _ptr(vc), _ptr(vs1), _ptr(vs2), _ptr(vo), T0, T_cap, _ptr(ws),
+                               ws.numel() * ws.element_size(), _stream(k_tail.device)), "kvq_nsn_flush")
+
+
+def kvq_nsn_attn_decode_stream(ctx: Context, q, B, H_q, T, T_cap, Gs, kc, ks1, ks2, ko, vc, vs1, vs2, vo, R, R_cap,
+                               k_tail, v_tail, sm_scale, out, ws, n_split=0):
+    _nsn_inputs(kc, ks1, ks2, ko, "k_")
+    _nsn_inputs(vc, vs1, vs2, vo, "v_")
+    _dev_tensor(k_tail, torch.float16, "k_tail")
+    _dev_tensor(v_tail, torch.float16, "v_tail")
+    _dev_tensor(out, torch.float32, "out")
+    _check(lib().kvq_nsn_attn_decode_stream(ctx.handle, _ptr(q), B, H_q, T, T_cap, Gs, _ptr(kc), _ptr(ks1),
+                                            _ptr(ks2), _ptr(ko), _ptr(vc), _ptr(vs1), _ptr(vs2), _ptr(vo), R, R_cap,
+                                            _ptr(k_tail), _ptr(v_tail), float(sm_scale), _ptr(out), _ptr(ws),
+                                            ws.numel() * ws.element_size(), int(n_split), _stream(q.device)),
+           "kvq_nsn_attn_decode_stream")

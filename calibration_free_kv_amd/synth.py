@@ -147,18 +147,20 @@ def random_codes(seed: int, lead, bits: int, qjl_m: int = 0):
     return out
 
 
-def random_nsn_codes(seed: int, lead, d: int = D, sub: int = 8, o_scale: float = 0.5):
+def random_nsn_codes(seed: int, lead, d: int = D, sub: int = 8, o_scale: float = 0.5, n_groups=None):
     """Stand-in NSN-VQ encoded vectors (no quantizer involved): entry indices
     uniform over 256 [*lead, d/sub] u8, s1 = exp(N(1, 0.25^2)), s2 ~ U(0.6, 1.0)
     (both fp32 [*lead]), and channel means o ~ N(0, o_scale^2) fp32
     [*lead[:-1], d] (one per head; larger than zero-mean data gives, so that
-    the mean term is exercised)."""
+    the mean term is exercised), or [*lead[:-1], n_groups, d] (one per flush
+    group of a streaming cache)."""
     rng = np.random.Generator(np.random.PCG64(seed))
     lead = tuple(lead)
+    og = () if n_groups is None else (int(n_groups),)
     return dict(codes=rng.integers(0, 256, size=lead + (d // sub,), dtype=np.uint8),
                 s1=np.exp(rng.normal(1.0, 0.25, size=lead)).astype(np.float32),
                 s2=rng.uniform(0.6, 1.0, size=lead).astype(np.float32),
-                o=(rng.standard_normal(lead[:-1] + (d,)) * o_scale).astype(np.float32))
+                o=(rng.standard_normal(lead[:-1] + og + (d,)) * o_scale).astype(np.float32))
 
 
 def random_orthogonal(seed: int, d: int = D):

@@ -364,6 +364,59 @@ kvq_status kvq_nsn_attn_decode_splits(kvq_ctx *ctx, const void *q_f16, int64_t B
                                       float sm_scale, float *out, void *ws, size_t ws_bytes,
                                       int32_t n_split, void *stream);
 
+/* Streaming NSN-VQ cache ([NSN] Detalhes de Implementacao: recent tokens
+ * stay in a full-precision window that is quantised when it fills, as in
+ * KIVI).  The pages do not say which tokens the channel mean o of
+ * [NSN] Metodologia 2 runs over in this setting; here every flush of Gs
+ * window tokens is encoded as one call of kvq_nsn_vq_quantize would encode
+ * them, with its own K and V means, so packed tokens never change once
+ * written.  Per (batch, KV head) the packed arrays hold T_cap tokens
+ * ([B, H_kv, T_cap, 16] codes, [B, H_kv, T_cap] s1 and s2 fp32) of which the
+ * first T are valid, the means [B, H_kv, T_cap / Gs, d] fp32 (mean g belongs
+ * to tokens g Gs .. g Gs + Gs - 1), and the windows [B, H_kv, R_cap, d] fp16
+ * of which the first R are valid.  Gs is a multiple of 64.
+ *
+ * Workspace bytes kvq_nsn_flush needs. */
+size_t kvq_nsn_flush_ws_bytes(const kvq_ctx *ctx, int64_t B, int64_t Gs);
+
+/* Flush: the first Gs tokens of the K and V windows of every (batch, KV
+ * head) are encoded as kvq_nsn_vq_quantize encodes Gs tokens of one head,
+ * and written to positions T0 .. T0 + Gs - 1 of the packed arrays and to
+ * mean T0 / Gs.  Other positions are not touched.  H_kv must be the
+ * context's n_kv_heads; Gs <= R_cap; T0 and T_cap multiples of Gs;
+ * T0 + Gs <= T_cap.  ws: kvq_nsn_flush_ws_bytes() bytes, 256-byte aligned,
+ * no initialisation needed.  B == 0 is a no-op.  Requires a context in
+ * KVQ_MODE_NSN_VQ.  Errors: KVQ_E_INVAL (sizes, alignment), KVQ_E_WORKSPACE. */
+kvq_status kvq_nsn_flush(kvq_ctx *ctx, const void *k_tail_f16, const void *v_tail_f16, int64_t B, int64_t H_kv,
+                         int64_t Gs, int64_t R_cap, uint8_t *k_codes, float *k_s1, float *k_s2, float *k_o,
+                         uint8_t *v_codes, float *v_s1, float *v_s2, float *v_o, int64_t T0, int64_t T_cap,
+                         void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace bytes kvq_nsn_attn_decode_stream needs for caches of T_cap tokens. */
+size_t kvq_nsn_attn_decode_stream_ws_bytes(const kvq_ctx *ctx, int64_t B, int64_t H_q, int64_t T_cap);
+
+/* One decode step over such a cache: one softmax (scale sm_scale, 0 means
+ * 1/sqrt(d)) over the T packed tokens, each reconstructed with the means of
+ * its flush group as x_hat = s1 (s2 H zq / sqrt(d) + o_g), followed by the
+ * R window tokens as they are.  H_q / H_kv in {1, 2, 4}; 0 <= T <= T_cap,
+ * T a multiple of Gs, 0 <= R <= R_cap, T + R >= 1 (an empty part's pointers
+ * may be NULL); T <= 511 * 32 * Gs.  n_split: token splits per (batch, KV
+ * head), 0 = automatic; a split holds whole flush groups, at most 32 of
+ * them, so the count used may differ; the result depends on it only through
+ * fp32 rounding.
+ *   out  [B, H_q, d] fp32
+ *   ws   at least kvq_nsn_attn_decode_stream_ws_bytes() bytes, 256-byte
+ *        aligned, no initialisation needed; calls sharing it must be ordered
+ *        on one stream.
+ * B * H_kv <= 65535.  Errors: KVQ_E_INVAL, KVQ_E_WORKSPACE. */
+kvq_status kvq_nsn_attn_decode_stream(kvq_ctx *ctx, const void *q_f16, int64_t B, int64_t H_q, int64_t T,
+                                      int64_t T_cap, int64_t Gs, const uint8_t *k_codes, const float *k_s1,
+                                      const float *k_s2, const float *k_o, const uint8_t *v_codes,
+                                      const float *v_s1, const float *v_s2, const float *v_o, int64_t R,
+                                      int64_t R_cap, const void *k_tail_f16, const void *v_tail_f16,
+                                      float sm_scale, float *out, void *ws, size_t ws_bytes, int32_t n_split,
+                                      void *stream);
+
 #ifdef __cplusplus
 }
 #endif

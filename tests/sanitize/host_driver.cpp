@@ -230,6 +230,50 @@ int main()
     CHECK(g_last.n_split >= 1 && g_last.n_split <= (T + 63) / 64);
     CHECK(kvq_nsn_attn_decode(nsn, q.p, 1, Hq, T, codes.as<uint8_t>(), s1.as<float>(), s1.as<float>(), o.as<float>(), codes.as<uint8_t>(), s1.as<float>(), s1.as<float>(), o.as<float>(), 0.f, out.as<float>(), nd.p, ndw - 1, st0) == KVQ_E_WORKSPACE);
 
+    // NSN-VQ streaming cache: flush groups of Gs tokens, decode over packed + window
+    {
+        const int64_t Gs = 128, Tc = 1024, Rc = 192, Tn = 512, Rn = 40;
+        Buf pc(B * H * Tc * 16), ps(B * H * Tc * 4), po(B * H * (Tc / Gs) * 512), win(B * H * Rc * 256);
+        const size_t fws = kvq_nsn_flush_ws_bytes(nsn, B, Gs);
+        CHECK(fws > 0 && kvq_nsn_flush_ws_bytes(nullptr, B, Gs) == 0);
+        Buf fw(fws);
+        auto flush = [&](kvq_ctx *cx, int64_t g, int64_t t0, int64_t tcap, size_t wsb) {
+            return kvq_nsn_flush(cx, win.p, win.p, B, H, g, Rc, pc.as<uint8_t>(), ps.as<float>(), ps.as<float>(),
+                                 po.as<float>(), pc.as<uint8_t>(), ps.as<float>(), ps.as<float>(), po.as<float>(), t0,
+                                 tcap, fw.p, wsb, st0);
+        };
+        CHECK(flush(nsn, Gs, 256, Tc, fws) == KVQ_OK);
+        CHECK(std::strcmp(g_last.what, "nsn_vq_strided") == 0 && g_last.a == B * H && g_last.b == Gs && g_last.c == Tc);
+        CHECK(flush(nsn, Gs, 100, Tc, fws) == KVQ_E_INVAL);       // T0 not a multiple of Gs
+        CHECK(flush(nsn, 96, 192, Tc, fws) == KVQ_E_INVAL);       // Gs not a multiple of 64
+        CHECK(flush(nsn, Gs, Tc, Tc, fws) == KVQ_E_INVAL);        // past the capacity
+        CHECK(flush(nsn, 256, 0, 1024, fws) == KVQ_E_INVAL);      // Gs > R_cap
+        CHECK(flush(nsn, Gs, 0, 1000, fws) == KVQ_E_INVAL);       // T_cap not a multiple of Gs
+        CHECK(flush(mse, Gs, 0, Tc, fws) == KVQ_E_INVAL);         // not an NSN context
+        CHECK(flush(nsn, Gs, 0, Tc, fws - 1) == KVQ_E_WORKSPACE);
+        const size_t dws = kvq_nsn_attn_decode_stream_ws_bytes(nsn, B, Hq, Tc);
+        CHECK(dws > 0);
+        Buf dw(dws);
+        auto dec = [&](int64_t hq, int64_t t, int64_t r, bool packed, size_t wsb, int32_t ns) {
+            return kvq_nsn_attn_decode_stream(
+                nsn, q.p, B, hq, t, Tc, Gs, packed ? pc.as<uint8_t>() : nullptr, packed ? ps.as<float>() : nullptr,
+                packed ? ps.as<float>() : nullptr, packed ? po.as<float>() : nullptr, packed ? pc.as<uint8_t>() : nullptr,
+                packed ? ps.as<float>() : nullptr, packed ? ps.as<float>() : nullptr, packed ? po.as<float>() : nullptr,
+                r, Rc, win.p, win.p, 0.f, out.as<float>(), dw.p, wsb, ns, st0);
+        };
+        CHECK(dec(Hq, Tn, Rn, true, dws, 0) == KVQ_OK);
+        CHECK(std::strcmp(g_last.what, "nsn_decode_stream") == 0 && g_last.n_split >= 1 && g_last.n_split <= Tn / 64);
+        CHECK(dec(Hq, Tn, Rn, true, dws, 1000) == KVQ_OK && g_last.n_split == Tn / 64);
+        CHECK(dec(Hq, 500, Rn, true, dws, 0) == KVQ_E_INVAL);     // T not a multiple of Gs
+        CHECK(dec(H * 8, Tn, Rn, true, dws, 0) == KVQ_E_INVAL);   // 8 query heads per KV head
+        CHECK(dec(Hq, 0, 0, true, dws, 0) == KVQ_E_INVAL);        // nothing to attend to
+        CHECK(dec(Hq, 0, Rn, false, dws, 0) == KVQ_OK);           // window only
+        CHECK(dec(Hq, Tn, 0, true, dws, 0) == KVQ_OK);            // packed only
+        CHECK(dec(Hq, Tn, Rn, false, dws, 0) == KVQ_E_INVAL);     // packed tokens without arrays
+        CHECK(dec(Hq, Tn, Rn, true, dws - 1, 0) == KVQ_E_WORKSPACE);
+        CHECK(dec(Hq, Tc + Gs, Rn, true, dws, 0) == KVQ_E_INVAL); // T > T_cap
+    }
+
     for (kvq_ctx *p : all) CHECK(kvq_destroy(p) == KVQ_OK);
     CHECK(kvq_destroy(qjl) == KVQ_OK && kvq_destroy(nsn) == KVQ_OK && kvq_destroy(dense) == KVQ_OK);
     CHECK(kvq_destroy(dqjl) == KVQ_OK);
