@@ -98,6 +98,7 @@ def _setup(L):
                                             _U8, _D, _D, _D, _D, _D, _D, C.c_double, _D]
     L.kvqo_kmeans.argtypes = [i64, C.c_int, C.c_int, _D, _I64, C.c_int, _D, _D]
     L.kvqo_kmeans.restype = C.c_int
+    L.kvqo_dq4.argtypes = [i64, _D, C.c_double, _U8, _D, _D, _U8]
     L.kvqo_cosine_refine.argtypes = [i64, C.c_int, C.c_int, _D, _D, C.c_int, _D]
     L.kvqo_cosine_refine.restype = C.c_int
 
@@ -463,6 +464,91 @@ def nsn_vq(x, codebook, band: float = BAND, want_z: bool = False, o_given=None, 
     if want_z:
         out["z"] = z
     return out
+
+
+BAND_DQ = 1e-4  # band of the 4-bit rounding decisions, in units of one step
+DQ_BLOCK = 32   # tokens per block of s1 double quantisation
+
+
+def dq4(v, band: float = BAND_DQ):
+    """4-bit min-max quantisation of one block v [n] -> (codes u8 [n], lo, step,
+    flags u8 [n]); the stored values are lo + codes * step."""
+    v = _f64(v).ravel()
+    code = np.zeros(v.shape[0], np.uint8)
+    fl = np.zeros(v.shape[0], np.uint8)
+    lo, step = C.c_double(), C.c_double()
+    _chk(lib().kvqo_dq4(v.shape[0], _p(v, _D), band, _p(code, _U8), C.byref(lo), C.byref(step), _p(fl, _U8)))
+    return code, lo.value, step.value, fl
+
+
+def pack_nibbles(codes):
+    """4-bit codes [..., n] -> bytes [..., ceil(n/2)]: code i in byte i // 2,
+    the low nibble for even i."""
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    n = c.shape[-1]
+    out = np.zeros(c.shape[:-1] + ((n + 1) // 2,), np.uint8)
+    for i in range(n):
+        out[..., i // 2] |= (c[..., i] & 15) << (4 * (i % 2))
+    return out
+
+
+def unpack_nibbles(packed, n: int):
+    p = np.ascontiguousarray(packed, dtype=np.uint8)
+    return np.stack([(p[..., i // 2] >> (4 * (i % 2))) & 15 for i in range(n)], axis=-1).astype(np.uint8)
+
+
+def nsn_mean(x):
+    """Per-head channel mean o of a_t = sqrt(d) x_t / ||x_t|| (0 for a zero
+    token) over the T tokens of x [H,T,d] (NSNQuant, Metodologia sec. 1)."""
+    x = _f64(x)
+    nx = np.linalg.norm(x, axis=-1, keepdims=True)
+    a = np.where(nx > 0, np.sqrt(x.shape[-1]) * x / np.where(nx > 0, nx, 1.0), 0.0)
+    return a.mean(axis=1)
+
+
+def nsn_vq_dq(x, codebook, band: float = BAND, band_dq: float = BAND_DQ, block: int = DQ_BLOCK,
+              want_z: bool = False, adaptive: bool = False, o_hat=None):
+    """NSN-VQ with the byproducts double-quantised to 4 bits (NSNQuant,
+    Metodologia sec. 3, "Double Quantization").  The steps in order: the mean o
+    of the T tokens, its 4-bit form o_hat (one block of d channels per head),
+    the shift and second normalisation with o_hat (so that x_hat = s1 (s2 H zq
+    / sqrt(d) + o_hat) undoes the encoding), the codes, then s1 in 4-bit blocks
+    of `block` tokens.  o_hat [H,d]: use this quantised mean instead (one of
+    the admissible alternatives at flagged channels).  Returns nsn_vq's dict
+    plus o_codes [H,d], o_lo, o_step [H], o_hat, o_flags, s1_codes [H,T],
+    s1_lo, s1_step [H,ceil(T/block)], s1_hat [H,T], s1_flags, and the packed
+    nibbles oq [H,d/2], s1q [H,ceil(T/2)]."""
+    x = _f64(x)
+    H, T, d = x.shape
+    o = nsn_mean(x)
+    oc = np.zeros((H, d), np.uint8)
+    ofl = np.zeros((H, d), np.uint8)
+    olo, ost = np.zeros(H), np.zeros(H)
+    for h in range(H):
+        oc[h], olo[h], ost[h], ofl[h] = dq4(o[h], band_dq)
+    if o_hat is None:
+        o_hat = olo[:, None] + oc * ost[:, None]
+    r = nsn_vq(x, codebook, band=band, want_z=want_z, o_given=o_hat, adaptive=adaptive)
+    nb = (T + block - 1) // block
+    sc = np.zeros((H, T), np.uint8)
+    sfl = np.zeros((H, T), np.uint8)
+    slo, sst = np.zeros((H, nb)), np.zeros((H, nb))
+    for h in range(H):
+        for b in range(nb):
+            sl = slice(b * block, min(T, (b + 1) * block))
+            sc[h, sl], slo[h, b], sst[h, b], sfl[h, sl] = dq4(r["s1"][h, sl], band_dq)
+    s1_hat = slo[:, np.arange(T) // block] + sc * sst[:, np.arange(T) // block]
+    r.update(o=o, o_codes=oc, o_lo=olo, o_step=ost, o_hat=o_hat, o_flags=ofl, s1_codes=sc, s1_lo=slo,
+             s1_step=sst, s1_hat=s1_hat, s1_flags=sfl, oq=pack_nibbles(oc), s1q=pack_nibbles(sc))
+    return r
+
+
+def dq_codebook(codebook, band: float = BAND_DQ):
+    """The codebook's entries in 4 bits, one block over all of them -> (codes
+    [K,sub], lo, step, flags, dequantised codebook [K,sub])."""
+    cb = _f64(codebook)
+    c, lo, step, fl = dq4(cb.ravel(), band)
+    return c.reshape(cb.shape), lo, step, fl.reshape(cb.shape), (lo + c * step).reshape(cb.shape)
 
 
 def nsn_reconstruct(zq, s1, s2, o):

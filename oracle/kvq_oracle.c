@@ -975,6 +975,44 @@ ORC_API int kvqo_nsn_vq(int d, int sub, int K, int64_t H, int64_t T, const doubl
     return 0;
 }
 
+/* ------------------------------------------------------------------------ */
+/* 4-bit double quantisation (NSNQuant, Metodologia sec. 3, "Double          */
+/* Quantization": the NSN parameters o and s1, and the codebook entries, are  */
+/* stored with 4 bits).  The page gives no scheme; the reading here is the    */
+/* plain uniform min-max quantiser of a block of n values:                    */
+/*   lo = min v,  step = (max v - lo) / 15,                                   */
+/*   code = floor((v - lo) / step + 1/2) in [0, 15]  (all 0 when step = 0),   */
+/*   stored value lo + code * step.                                           */
+/* flags: 1 when (v - lo) / step lies within `band` of a half-integer, where  */
+/* another precision may round the other way.                                */
+/* ------------------------------------------------------------------------ */
+ORC_API int kvqo_dq4(int64_t n, const double *v, double band, uint8_t *code, double *lo_out,
+                     double *step_out, uint8_t *flags)
+{
+    if (n <= 0) return -1;
+    double lo = v[0], hi = v[0];
+    for (int64_t i = 1; i < n; ++i) {
+        if (v[i] < lo) lo = v[i];
+        if (v[i] > hi) hi = v[i];
+    }
+    const double step = (hi - lo) / 15.0;
+    for (int64_t i = 0; i < n; ++i) {
+        int c = 0, f = 0;
+        if (step > 0.0) {
+            const double u = (v[i] - lo) / step;
+            c = (int)floor(u + 0.5);
+            if (c < 0) c = 0;
+            if (c > 15) c = 15;
+            f = fabs(u - floor(u) - 0.5) < band;
+        }
+        code[i] = (uint8_t)c;
+        if (flags) flags[i] = (uint8_t)f;
+    }
+    *lo_out = lo;
+    *step_out = step;
+    return 0;
+}
+
 /* Reconstruction from the NSN byproducts and a rotated vector zq [d]:        */
 /*   x_hat = s1 * (s2 * H zq / sqrt(d) + o)                                   */
 ORC_API void kvqo_nsn_reconstruct(int d, const double *zq, double s1, double s2,
