@@ -206,6 +206,25 @@ kvq_status upload(T **dst, const T *src, size_t n)
 
 kvq_status launch_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_E_DEVICE; }
 
+// The codebook's n values in 4 bits ([NSN] Metodologia sec. 3, double
+// quantisation): one block, lo = min, step = (max - lo) / 15, each value
+// replaced by lo + code step with code the nearest level; decided in double.
+void dq4_codebook(float *v, size_t n)
+{
+    double lo = v[0], hi = v[0];
+    for (size_t i = 1; i < n; ++i) {
+        lo = std::min(lo, (double)v[i]);
+        hi = std::max(hi, (double)v[i]);
+    }
+    const double step = (hi - lo) / 15.0;
+    if (!(step > 0.0)) return;
+    for (size_t i = 0; i < n; ++i) {
+        int c = (int)std::floor(((double)v[i] - lo) / step + 0.5);
+        c = std::min(15, std::max(0, c));
+        v[i] = (float)(lo + c * step);
+    }
+}
+
 // Query heads per KV head that the kernels are built for.
 bool logits_group_built(int64_t G) { return G == 1 || G == 2 || G == 4 || G == 8; }
 bool decode_group_built(int64_t G) { return G == 1 || G == 2 || G == 4; }
@@ -251,7 +270,7 @@ kvq_status kvq_create(const kvq_config *cfg, kvq_ctx **out)
     if (cfg->codebook != KVQ_CODEBOOK_GAUSS && cfg->codebook != KVQ_CODEBOOK_BETA) return KVQ_E_INVAL;
     if (cfg->codebook == KVQ_CODEBOOK_BETA && mode == KVQ_MODE_NSN_VQ) return KVQ_E_INVAL;
     if (cfg->rotation != KVQ_ROTATION_HADAMARD && cfg->rotation != KVQ_ROTATION_DENSE) return KVQ_E_INVAL;
-    if (cfg->nsn_options & ~KVQ_NSN_ADAPTIVE_SCALE) return KVQ_E_INVAL;
+    if (cfg->nsn_options & ~(KVQ_NSN_ADAPTIVE_SCALE | KVQ_NSN_DQ_CODEBOOK)) return KVQ_E_INVAL;
     if (cfg->nsn_options && mode != KVQ_MODE_NSN_VQ) return KVQ_E_INVAL;
     if (cfg->rotation == KVQ_ROTATION_DENSE) {
         if (mode == KVQ_MODE_NSN_VQ) return KVQ_E_UNSUPPORTED;
@@ -348,12 +367,18 @@ kvq_status kvq_create(const kvq_config *cfg, kvq_ctx **out)
         const size_t n = (size_t)kvq::kVqK * kvq::kVqSub;
         float bias[kvq::kVqK];
         _Float16 *c16 = (_Float16 *)std::malloc(2 * n * sizeof(_Float16));
-        if (!c16) st = KVQ_E_NOMEM;
+        float *cbv = (float *)std::malloc(n * sizeof(float));
+        if (!c16 || !cbv) st = KVQ_E_NOMEM;
+        for (size_t i = 0; st == KVQ_OK && i < n; ++i) {
+            cbv[i] = cfg->vq_codebook[i];
+            if (!std::isfinite(cbv[i])) st = KVQ_E_INVAL;
+        }
+        if (st == KVQ_OK && (cfg->nsn_options & KVQ_NSN_DQ_CODEBOOK)) dq4_codebook(cbv, n);
         bool exact = true;
         for (int j = 0; st == KVQ_OK && j < kvq::kVqK; ++j) {
             double sq = 0.0;
             for (int k = 0; k < kvq::kVqSub; ++k) {
-                const float v = cfg->vq_codebook[j * kvq::kVqSub + k];
+                const float v = cbv[j * kvq::kVqSub + k];
                 if (!std::isfinite(v) || std::fabs(v) > 60000.f) st = KVQ_E_INVAL;
                 sq += (double)v * v;
                 const _Float16 hi = (_Float16)v;
@@ -365,10 +390,11 @@ kvq_status kvq_create(const kvq_config *cfg, kvq_ctx **out)
             bias[j] = (float)(-0.5 * sq);
         }
         c->vq_exact_f16 = exact;
-        if (st == KVQ_OK) st = upload(&c->d_vq, cfg->vq_codebook, n);
+        if (st == KVQ_OK) st = upload(&c->d_vq, cbv, n);
         if (st == KVQ_OK) st = upload(&c->d_vq16, c16, 2 * n);
         if (st == KVQ_OK) st = upload(&c->d_vqbias, bias, (size_t)kvq::kVqK);
         std::free(c16);
+        std::free(cbv);
     }
     if (st == KVQ_OK && cfg->rotation == KVQ_ROTATION_DENSE) {
         const size_t n = (size_t)kvq::kD * kvq::kD;
@@ -724,6 +750,85 @@ kvq_status kvq_nsn_attn_decode_splits(kvq_ctx *ctx, const void *q_f16, int64_t B
     DeviceGuard g(ctx->device);
     if (!g.ok) return KVQ_E_DEVICE;
     const kvq::NsnKV kv{k_codes, k_s1, k_s2, k_o, v_codes, v_s1, v_s2, v_o};
+    return launch_status(
+        kvq::launch_nsn_decode(ctx, q_f16, B, H_q, T, kv, sm_scale, out, ws, ns, (hipStream_t)stream));
+}
+
+size_t kvq_nsn_vq_dq_ws_bytes(const kvq_ctx *ctx, int64_t H, int64_t T)
+{
+    if (!ctx || H < 1 || T < 1) return 0;
+    return kvq::nsn_dq_ws_bytes(H, T);
+}
+
+kvq_status kvq_nsn_vq_quantize_dq(kvq_ctx *ctx, const void *x_f16, int64_t H, int64_t T, uint8_t *codes,
+                                  uint8_t *s1q, float *s1p, float *s2, uint8_t *oq, float *op, void *ws,
+                                  size_t ws_bytes, void *stream)
+{
+    if (!ctx || ctx->mode != KVQ_MODE_NSN_VQ) return KVQ_E_INVAL;
+    if (H < 1 || T < 1 || T > (int64_t(1) << 31) || H > (int64_t(1) << 20)) return KVQ_E_INVAL;
+    if (H * ((T + 2047) / 2048) > INT32_MAX) return KVQ_E_INVAL;
+    if (!x_f16 || !codes || !s1q || !s1p || !s2 || !oq || !op || !ws) return KVQ_E_INVAL;
+    if (!aligned(x_f16, 16) || !aligned(codes, 16) || !aligned(s1p, 8) || !aligned(s2, 4) || !aligned(op, 8) ||
+        !aligned(ws, 256))
+        return KVQ_E_INVAL;
+    if (ws_bytes < kvq::nsn_dq_ws_bytes(H, T)) return KVQ_E_WORKSPACE;
+    DeviceGuard g(ctx->device);
+    if (!g.ok) return KVQ_E_DEVICE;
+    const kvq::NsnDq dq{s1q, s1p, oq, op};
+    return launch_status(kvq::launch_nsn_vq_dq(ctx, x_f16, H, T, codes, s2, dq, ws, (hipStream_t)stream));
+}
+
+namespace {
+bool dq_in_ok(const uint8_t *s1q, const float *s1p, const float *s2, const uint8_t *oq, const float *op)
+{
+    return s1q && s1p && s2 && oq && op && aligned(s1p, 8) && aligned(s2, 4) && aligned(op, 8);
+}
+}  // namespace
+
+kvq_status kvq_nsn_logits_dq(kvq_ctx *ctx, const void *q_f16, int64_t B, int64_t H_q, int64_t T,
+                             const uint8_t *codes, const uint8_t *s1q, const float *s1p, const float *s2,
+                             const uint8_t *oq, const float *op, float *logits, void *stream)
+{
+    if (!ctx || ctx->mode != KVQ_MODE_NSN_VQ) return KVQ_E_INVAL;
+    if (B < 0 || T < 0 || !nsn_group_ok(ctx, H_q)) return KVQ_E_INVAL;
+    if (B == 0 || T == 0) return KVQ_OK;
+    if (!q_f16 || !codes || !logits || !dq_in_ok(s1q, s1p, s2, oq, op)) return KVQ_E_INVAL;
+    if (!aligned(q_f16, 16) || !aligned(codes, 16) || !aligned(logits, 4)) return KVQ_E_INVAL;
+    if (T > (int64_t(1) << 31) || B * ctx->H > 65535) return KVQ_E_INVAL;
+    DeviceGuard g(ctx->device);
+    if (!g.ok) return KVQ_E_DEVICE;
+    const kvq::NsnDqIn dq{s1q, s1p, oq, op};
+    return launch_status(kvq::launch_nsn_logits_dq(ctx, q_f16, B, H_q, T, codes, dq, s2, logits, (hipStream_t)stream));
+}
+
+kvq_status kvq_nsn_attn_decode_dq(kvq_ctx *ctx, const void *q_f16, int64_t B, int64_t H_q, int64_t T,
+                                  const uint8_t *k_codes, const uint8_t *k_s1q, const float *k_s1p,
+                                  const float *k_s2, const uint8_t *k_oq, const float *k_op,
+                                  const uint8_t *v_codes, const uint8_t *v_s1q, const float *v_s1p,
+                                  const float *v_s2, const uint8_t *v_oq, const float *v_op, float sm_scale,
+                                  float *out, void *ws, size_t ws_bytes, int32_t n_split, void *stream)
+{
+    if (!ctx || ctx->mode != KVQ_MODE_NSN_VQ) return KVQ_E_INVAL;
+    if (B < 0 || T < 1 || !nsn_group_ok(ctx, H_q)) return KVQ_E_INVAL;
+    if (n_split < 0 || !std::isfinite(sm_scale) || sm_scale < 0.f) return KVQ_E_INVAL;
+    if (B == 0) return KVQ_OK;
+    if (!q_f16 || !k_codes || !v_codes || !out || !ws || !dq_in_ok(k_s1q, k_s1p, k_s2, k_oq, k_op) ||
+        !dq_in_ok(v_s1q, v_s1p, v_s2, v_oq, v_op))
+        return KVQ_E_INVAL;
+    if (!aligned(q_f16, 16) || !aligned(k_codes, 16) || !aligned(v_codes, 16) || !aligned(out, 16) ||
+        !aligned(ws, 256))
+        return KVQ_E_INVAL;
+    if (T > (int64_t(1) << 31) || B * ctx->H > 65535) return KVQ_E_INVAL;
+    if (ws_bytes < kvq::nsn_decode_ws_bytes(B, H_q, T)) return KVQ_E_WORKSPACE;
+    const int64_t max_split = kvq::decode_max_splits(T);
+    int ns = n_split == 0 ? kvq::nsn_decode_auto_splits(ctx, B, T) : n_split;
+    if (ns > max_split) ns = (int)max_split;
+    if (ns < 1) ns = 1;
+    if (sm_scale == 0.f) sm_scale = 1.0f / std::sqrt((float)kvq::kD);
+    DeviceGuard g(ctx->device);
+    if (!g.ok) return KVQ_E_DEVICE;
+    kvq::NsnKV kv{k_codes, nullptr, k_s2, nullptr, v_codes, nullptr, v_s2, nullptr, true,
+                  kvq::NsnDqIn{k_s1q, k_s1p, k_oq, k_op}, kvq::NsnDqIn{v_s1q, v_s1p, v_oq, v_op}};
     return launch_status(
         kvq::launch_nsn_decode(ctx, q_f16, B, H_q, T, kv, sm_scale, out, ws, ns, (hipStream_t)stream));
 }

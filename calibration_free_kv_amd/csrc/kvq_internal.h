@@ -125,17 +125,45 @@ hipError_t launch_nsn_vq(const kvq_ctx *ctx, const void *x, int64_t H, int64_t T
 hipError_t launch_nsn_vq_strided(const kvq_ctx *ctx, const void *x, int64_t H, int64_t T, int64_t ldx, uint8_t *codes,
                                  float *s1, float *s2, int64_t ldt, float *o, int64_t ldo, void *ws, hipStream_t s);
 
-// NSN-VQ encoded keys and values of one decode call (outputs of kvq_nsn_vq_quantize).
+// Double quantisation of the NSN byproducts: s1 as 4-bit codes with one
+// (lo, step) pair per block of kNsnDqBlock tokens, o as 4-bit codes with one
+// pair per head.
+constexpr int kNsnDqBlock = 32;
+struct NsnDq {
+    uint8_t *s1q;  // [H][ceil(T / 2)]
+    float *s1p;    // [H][ceil(T / 32)][2]
+    uint8_t *oq;   // [H][64]
+    float *op;     // [H][2]
+};
+size_t nsn_ws_bytes_aligned(int64_t H, int64_t T);  // nsn_ws_bytes rounded up to 256 bytes
+size_t nsn_dq_ws_bytes(int64_t H, int64_t T);       // + the dequantised means [H][128]
+hipError_t launch_nsn_vq_dq(const kvq_ctx *ctx, const void *x, int64_t H, int64_t T, uint8_t *codes, float *s2,
+                            const NsnDq &dq, void *ws, hipStream_t s);
+
+// NSN-VQ encoded keys and values of one decode call (outputs of
+// kvq_nsn_vq_quantize, or of kvq_nsn_vq_quantize_dq: then s1 and o are read
+// from the 4-bit forms in kdq / vdq and ks1, ko, vs1, vo are unused).
+struct NsnDqIn {
+    const uint8_t *s1q;
+    const float *s1p;
+    const uint8_t *oq;
+    const float *op;
+};
 struct NsnKV {
     const uint8_t *kc;
     const float *ks1, *ks2, *ko;
     const uint8_t *vc;
     const float *vs1, *vs2, *vo;
+    bool dq;
+    NsnDqIn kdq, vdq;
 };
 
 hipError_t launch_nsn_logits(const kvq_ctx *ctx, const void *q, int64_t B, int64_t Hq, int64_t T,
                              const uint8_t *codes, const float *s1, const float *s2, const float *o, float *logits,
                              hipStream_t s);
+hipError_t launch_nsn_logits_dq(const kvq_ctx *ctx, const void *q, int64_t B, int64_t Hq, int64_t T,
+                                const uint8_t *codes, const NsnDqIn &dq, const float *s2, float *logits,
+                                hipStream_t s);
 
 int64_t nsn_decode_chunk(int64_t T, int n_split);
 int nsn_decode_auto_splits(const kvq_ctx *ctx, int64_t B, int64_t T);

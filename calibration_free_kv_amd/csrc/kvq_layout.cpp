@@ -42,6 +42,11 @@ size_t nsn_ws_bytes(int64_t H, int64_t T)
     return (size_t)H * n_chunks * kD * sizeof(float);
 }
 
+size_t nsn_ws_bytes_aligned(int64_t H, int64_t T) { return (nsn_ws_bytes(H, T) + 255) / 256 * 256; }
+
+// Double quantisation: the dequantised means [H][128] fp32 after the sums.
+size_t nsn_dq_ws_bytes(int64_t H, int64_t T) { return nsn_ws_bytes_aligned(H, T) + (size_t)H * kD * sizeof(float); }
+
 // NSN-VQ decode: tokens per split (a multiple of the 64-token tile), the
 // automatic split count (about one block per compute unit), and the partials
 // [B H_q][max splits][kNsnPartStride] fp32.

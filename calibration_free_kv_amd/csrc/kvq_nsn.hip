@@ -148,10 +148,34 @@ __global__ __launch_bounds__(64 * kStatWaves) void k_nsn_stats(const u4_t *__res
 // (2) o[h][i] = sum over chunks / T, in a fixed order (deterministic): thread
 // group j (of 8) sums chunks j, j + 8, ... with its loads in flight together,
 // then the 8 group sums are added in order.
+// Double quantisation (oq non-NULL): the head's 128 means become 4-bit codes
+// over [lo, lo + 15 step] (lo = min, step = range / 15, nearest level), o
+// receives the dequantised means lo + code step that the search shifts by,
+// oq the codes (channel i in byte i / 2, low nibble for even i), op (lo, step).
 constexpr int kMeanGroups = 8;
+__device__ __forceinline__ float lanes_min(float x)
+{
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) x = fminf(x, __shfl_xor(x, m));
+    return x;
+}
+__device__ __forceinline__ float lanes_max(float x)
+{
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) x = fmaxf(x, __shfl_xor(x, m));
+    return x;
+}
+// 4-bit code of v in [lo, lo + 15 step]: the nearest level (0 when step = 0)
+__device__ __forceinline__ int dq4_code(float v, float lo, float step)
+{
+    if (!(step > 0.0f)) return 0;
+    const int c = (int)floorf((v - lo) / step + 0.5f);
+    return c < 0 ? 0 : c > 15 ? 15 : c;
+}
 __global__ __launch_bounds__(kD * kMeanGroups) void k_nsn_mean(const float *__restrict__ part,
                                                               float *__restrict__ o, int64_t T, int n_chunks,
-                                                              int64_t ldo)
+                                                              int64_t ldo, uint8_t *__restrict__ oq,
+                                                              float *__restrict__ op)
 {
     __shared__ float red[kMeanGroups][kD];
     const int h = blockIdx.x, i = threadIdx.x & (kD - 1), j = threadIdx.x >> 7;
@@ -168,11 +192,37 @@ __global__ __launch_bounds__(kD * kMeanGroups) void k_nsn_mean(const float *__re
     for (; c < n_chunks; c += kMeanGroups) s += ph[(int64_t)c * kD];
     red[j][i] = s;
     __syncthreads();
+    float ov = 0.0f;
     if (j == 0) {
         float t = 0.0f;
 #pragma unroll
         for (int g = 0; g < kMeanGroups; ++g) t += red[g][i];
-        o[h * ldo + i] = t / (float)T;
+        ov = t / (float)T;
+    }
+    if (!oq) {
+        if (j == 0) o[h * ldo + i] = ov;
+        return;
+    }
+    __shared__ float ext[2][2];  // per wave of the 128 channels: min, max
+    if (j == 0) {
+        const float a = lanes_min(ov), b = lanes_max(ov);
+        if ((i & 63) == 0) {
+            ext[i >> 6][0] = a;
+            ext[i >> 6][1] = b;
+        }
+    }
+    __syncthreads();
+    if (j == 0) {
+        const float lo = fminf(ext[0][0], ext[1][0]), hi = fmaxf(ext[0][1], ext[1][1]);
+        const float step = (hi - lo) / 15.0f;
+        const int c = dq4_code(ov, lo, step);
+        const int c_next = __shfl_xor(c, 1);
+        o[h * ldo + i] = fmaf((float)c, step, lo);
+        if (!(i & 1)) oq[h * (kD / 2) + i / 2] = (uint8_t)(c | (c_next << 4));
+        if (i == 0) {
+            op[2 * h] = lo;
+            op[2 * h + 1] = step;
+        }
     }
 }
 
@@ -218,7 +268,10 @@ struct VqArgs {
     const u2_t *cb_lo;    // [256][2] lo parts, dims 4q .. 4q + 3 at index 2 j + q (unused if exactly fp16)
     const float *bias;    // [256] -||C_j||^2 / 2
     u4_t *codes;          // [H][T][16 bytes]
-    float *s1, *s2;       // [H][T]
+    float *s1, *s2;       // [H][T] (s1 may be NULL with s1q)
+    uint8_t *s1q;         // double quantisation: [H][ldq] 4-bit s1 codes (token t in byte t / 2), or NULL
+    float *s1p;           // [H][nblk][2] (lo, step) per block of 32 tokens (one tile)
+    int64_t ldq, nblk;
 };
 
 // (3) per-token transform and nearest-entry search.  Tiles of 32 tokens of
@@ -258,6 +311,7 @@ struct VqArgs {
 constexpr int kTileN = 32;           // tokens per tile of the search
 constexpr int kWavesN = 8;           // waves per workgroup (two per SIMD)
 constexpr int kRowsN = kTileN * 16;  // 16-byte chunks of x per tile
+static_assert(kTileN == kNsnDqBlock, "a block of double-quantised s1 is one search tile");
 constexpr int kBufN = kRowsN + 64;   // + two slots of the head's 128 channel means
 
 // Rows of the tile: chunk c of row v at slot 16 v + ((c + v) mod 16), so the
@@ -584,11 +638,27 @@ __global__ __launch_bounds__(kWavesN * 64) __attribute__((amdgpu_waves_per_eu(2,
             after = blockIdx.x + nsn_take_rows(L, lane, w, &next_tile) * G;
             if (after < n_tiles) issue(after, ord & 1);  // the slot of this tile, no longer read
         }
+        const float s1v = nx / kSqrtD;
         if (!upper && v < nv) {  // lanes of tokens past a ragged tail searched stale rows
             const int64_t t = v0 + v;
             a.codes[t] = u4_t{code[0], code[1], code[2], code[3]};
-            a.s1[t] = nx / kSqrtD;
+            if (a.s1) a.s1[t] = s1v;
             a.s2[t] = s2v;
+        }
+        if (a.s1q) {
+            // s1 in 4 bits over the tile's tokens (both halves hold the same values)
+            const float lo = lanes_min(v < nv ? s1v : __builtin_inff());
+            const float hi = lanes_max(v < nv ? s1v : -__builtin_inff());
+            const float step = (hi - lo) / 15.0f;
+            const int c = dq4_code(s1v, lo, step);
+            const int c_pair = __shfl_xor(c, 1);  // every lane takes part in the exchange
+            const int c_next = v + 1 < nv ? c_pair : 0;
+            if (!upper && v < nv && !(v & 1)) a.s1q[hh * a.ldq + (t0 + v) / 2] = (uint8_t)(c | (c_next << 4));
+            if (lane == 0) {
+                float *pp = a.s1p + (hh * a.nblk + t0 / kTileN) * 2;
+                pp[0] = lo;
+                pp[1] = step;
+            }
         }
         if (!has_next) break;
         tile = next;
@@ -599,21 +669,49 @@ __global__ __launch_bounds__(kWavesN * 64) __attribute__((amdgpu_waves_per_eu(2,
 
 }  // namespace
 
+namespace {
+hipError_t nsn_vq_run(const kvq_ctx *ctx, const void *x, int64_t H, int64_t T, int64_t ldx, uint8_t *codes, float *s1,
+                      float *s2, int64_t ldt, float *o, int64_t ldo, const NsnDq *dq, void *ws, hipStream_t s);
+}  // namespace
+
 hipError_t launch_nsn_vq(const kvq_ctx *ctx, const void *x, int64_t H, int64_t T, uint8_t *codes, float *s1,
                          float *s2, float *o, void *ws, hipStream_t s)
 {
-    return launch_nsn_vq_strided(ctx, x, H, T, T, codes, s1, s2, T, o, kD, ws, s);
+    return nsn_vq_run(ctx, x, H, T, T, codes, s1, s2, T, o, kD, nullptr, ws, s);
 }
 
 hipError_t launch_nsn_vq_strided(const kvq_ctx *ctx, const void *x, int64_t H, int64_t T, int64_t ldx, uint8_t *codes,
                                  float *s1, float *s2, int64_t ldt, float *o, int64_t ldo, void *ws, hipStream_t s)
 {
+    return nsn_vq_run(ctx, x, H, T, ldx, codes, s1, s2, ldt, o, ldo, nullptr, ws, s);
+}
+
+// Double quantisation: the dequantised means live in the workspace after the
+// channel sums.
+hipError_t launch_nsn_vq_dq(const kvq_ctx *ctx, const void *x, int64_t H, int64_t T, uint8_t *codes, float *s2,
+                            const NsnDq &dq, void *ws, hipStream_t s)
+{
+    float *ohat = (float *)((char *)ws + nsn_ws_bytes_aligned(H, T));
+    return nsn_vq_run(ctx, x, H, T, T, codes, nullptr, s2, T, ohat, kD, &dq, ws, s);
+}
+
+namespace {
+hipError_t nsn_vq_run(const kvq_ctx *ctx, const void *x, int64_t H, int64_t T, int64_t ldx, uint8_t *codes, float *s1,
+                      float *s2, int64_t ldt, float *o, int64_t ldo, const NsnDq *dq, void *ws, hipStream_t s)
+{
     const int n_chunks = (int)((T + kChunk - 1) / kChunk);
     float *part = (float *)ws;
     hipLaunchKernelGGL(k_nsn_stats, dim3((unsigned)(H * n_chunks)), dim3(64 * kStatWaves), 0, s, (const u4_t *)x, part, T,
                        n_chunks, ldx);
-    hipLaunchKernelGGL(k_nsn_mean, dim3((unsigned)H), dim3(kD * kMeanGroups), 0, s, part, o, T, n_chunks, ldo);
+    hipLaunchKernelGGL(k_nsn_mean, dim3((unsigned)H), dim3(kD * kMeanGroups), 0, s, part, o, T, n_chunks, ldo,
+                       dq ? dq->oq : nullptr, dq ? dq->op : nullptr);
     VqArgs a{};
+    if (dq) {
+        a.s1q = dq->s1q;
+        a.s1p = dq->s1p;
+        a.ldq = (T + 1) / 2;
+        a.nblk = (T + kTileN - 1) / kTileN;
+    }
     a.x = (const u4_t *)x;
     a.cb_hi = (const u4_t *)ctx->d_vq16;
     a.cb_lo = (const u2_t *)(ctx->d_vq16 + kVqK * kVqSub);
@@ -638,5 +736,6 @@ hipError_t launch_nsn_vq_strided(const kvq_ctx *ctx, const void *x, int64_t H, i
 #undef KVQ_NSN_LAUNCH
     return hipGetLastError();
 }
+}  // namespace
 
 }  // namespace kvq

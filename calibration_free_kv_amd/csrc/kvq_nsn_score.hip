@@ -44,13 +44,39 @@ struct alignas(16) NsnSmem {
     float qo[G];                                         // <q, o>
 };
 
+// Double quantisation of the byproducts (the *_dq calls): s1 of token t of
+// row bg is its 4-bit code in the block of kNsnDqBlock tokens, lo + code
+// step with that block's (lo, step); the means are 4-bit codes with one
+// (lo, step) per row.
+__device__ __forceinline__ float dq_s1(const NsnDqIn &dq, int64_t bg, int64_t T, int64_t t)
+{
+    const int64_t ldq = (T + 1) / 2, nblk = (T + kNsnDqBlock - 1) / kNsnDqBlock;
+    const uint32_t byte = dq.s1q[bg * ldq + (t >> 1)];
+    const uint32_t c = (byte >> (4 * (uint32_t)(t & 1))) & 15u;
+    const f2_t p = reinterpret_cast<const f2_t *>(dq.s1p)[bg * nblk + t / kNsnDqBlock];
+    return fmaf((float)c, p.y, p.x);
+}
+// Means of channels 2 lane, 2 lane + 1: from the fp32 row `orow`, or (DQ)
+// from the 4-bit codes of row bg.
+template <bool DQ>
+__device__ __forceinline__ f2_t load_mean(const float *orow, const NsnDqIn &dq, int64_t bg, int lane)
+{
+    if constexpr (DQ) {
+        const uint32_t byte = dq.oq[bg * (kD / 2) + lane];
+        const f2_t p = reinterpret_cast<const f2_t *>(dq.op)[bg];
+        return f2_t{fmaf((float)(byte & 15u), p.y, p.x), fmaf((float)(byte >> 4), p.y, p.x)};
+    } else {
+        return reinterpret_cast<const f2_t *>(orow)[lane];
+    }
+}
+
 // Prologue of both kernels: codebook into LDS, q' and <q, o> for the G query
 // heads of KV head g of batch b (one wave per head), then the table.  Ends
 // with a barrier.  Table entry (s, j, h) = sum_k q'_h[8 s + k] C_j[k], one
 // fp32 chain over k.
-template <int G, int NT>
+template <int G, int NT, bool DQ = false>
 __device__ void nsn_tables(const half_t *__restrict__ q, const float *__restrict__ obg, const float *__restrict__ cb,
-                           int64_t qbase, NsnSmem<G> &sm)
+                           int64_t qbase, NsnSmem<G> &sm, const NsnDqIn &dq = NsnDqIn{}, int64_t bg = 0)
 {
     static_assert(NT % kVqK == 0, "one thread per entry and sub-vector group");
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -58,7 +84,7 @@ __device__ void nsn_tables(const half_t *__restrict__ q, const float *__restrict
         reinterpret_cast<f4_t *>(sm.cb)[i] = reinterpret_cast<const f4_t *>(cb)[i];
     for (int h = wv; h < G; h += NT / 64) {
         const h2_t pr = reinterpret_cast<const h2_t *>(q + (qbase + h) * kD)[lane];
-        const f2_t ov = reinterpret_cast<const f2_t *>(obg)[lane];
+        const f2_t ov = load_mean<DQ>(obg, dq, bg, lane);
         float x0 = (float)pr.x, x1 = (float)pr.y;
         const float qo = wave_sum(fmaf(x1, ov.y, x0 * ov.x));
         wave_fwht(x0, x1, lane);
@@ -110,11 +136,12 @@ __device__ __forceinline__ void nsn_key_sum(const u4_t code, const float *tab, f
 
 // logits[b, g G + h, t] = s1_t (s2_t sum_s T_h[s][code_t,s] + <q_h, o>).
 // Block (chunk of kLogitChunk tokens, b * Hkv + g); one thread per token.
-template <int G>
+template <int G, bool DQ>
 __global__ __launch_bounds__(kThreadsN) void k_nsn_logits(const half_t *__restrict__ q, const u4_t *__restrict__ codes,
                                                           const float *__restrict__ s1, const float *__restrict__ s2,
                                                           const float *__restrict__ o, const float *__restrict__ cb,
-                                                          float *__restrict__ logits, int64_t Hkv, int64_t T)
+                                                          float *__restrict__ logits, int64_t Hkv, int64_t T,
+                                                          NsnDqIn dq)
 {
     constexpr int NT = kLogitChunk / kThreadsN;  // tokens per thread
     __shared__ NsnSmem<G> sm;
@@ -128,12 +155,12 @@ __global__ __launch_bounds__(kThreadsN) void k_nsn_logits(const half_t *__restri
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
         const int64_t t = c0 + threadIdx.x + i * kThreadsN;
-        const int64_t v = bg * T + (t < c1 ? t : c0);
+        const int64_t tc = t < c1 ? t : c0, v = bg * T + tc;
         code[i] = codes[v];
-        a[i] = s1[v];
+        a[i] = DQ ? dq_s1(dq, bg, T, tc) : s1[v];
         c[i] = s2[v];
     }
-    nsn_tables<G, kThreadsN>(q, o + bg * kD, cb, qbase, sm);
+    nsn_tables<G, kThreadsN, DQ>(q, DQ ? nullptr : o + bg * kD, cb, qbase, sm, dq, bg);
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
         const int64_t t = c0 + threadIdx.x + i * kThreadsN;
@@ -179,6 +206,13 @@ __device__ __forceinline__ TileIn load_tile(const u4_t *kc, const float *ks1, co
     const int64_t v = base + t;
     return TileIn{kc[v], vc[v], ks1[v], ks2[v], vs1[v], vs2[v]};
 }
+// The same with s1 of K and V from their 4-bit forms (rows of T tokens).
+__device__ __forceinline__ TileIn load_tile_dq(const u4_t *kc, const NsnDqIn &kdq, const float *ks2, const u4_t *vc,
+                                               const NsnDqIn &vdq, const float *vs2, int64_t bg, int64_t T, int64_t t)
+{
+    const int64_t v = bg * T + t;
+    return TileIn{kc[v], vc[v], dq_s1(kdq, bg, T, t), ks2[v], dq_s1(vdq, bg, T, t), vs2[v]};
+}
 constexpr int kPartStride = kNsnPartStride;  // floats per (split, head) partial: acc[128], M, L, WO, pad
 
 // ldt: tokens between (b, g) rows of the packed arrays; n_part: partial
@@ -186,7 +220,8 @@ constexpr int kPartStride = kNsnPartStride;  // floats per (split, head) partial
 // GROUPED: ko, vo are per-group means [B Hkv][ngc][128] of groups of gsize
 // tokens (gsize and the range start multiples of 64 and of gsize), else the
 // per-(b, g) means [B Hkv][128].
-template <int G, bool GROUPED>
+// DQ: s1 and the K means from their 4-bit forms (kdq, vdq; rows of T tokens).
+template <int G, bool GROUPED, bool DQ>
 __global__ __launch_bounds__(64 * dec_waves<G>()) void k_nsn_part(const half_t *__restrict__ q, const u4_t *__restrict__ kc,
                                                         const float *__restrict__ ks1, const float *__restrict__ ks2,
                                                         const float *__restrict__ ko, const u4_t *__restrict__ vc,
@@ -194,8 +229,9 @@ __global__ __launch_bounds__(64 * dec_waves<G>()) void k_nsn_part(const half_t *
                                                         const float *__restrict__ cb, float *__restrict__ part,
                                                         int64_t Hkv, int64_t T, int64_t chunk, float scale2,
                                                         int64_t ldt, int n_part, const float *__restrict__ vo,
-                                                        int64_t gsize, int64_t ngc)
+                                                        int64_t gsize, int64_t ngc, NsnDqIn kdq, NsnDqIn vdq)
 {
+    static_assert(!(GROUPED && DQ), "the streaming cache keeps fp32 byproducts");
     constexpr int NW = dec_waves<G>();
     __shared__ DecodeSmem<G, GROUPED> sm;
     const int lane = threadIdx.x & 63;
@@ -204,11 +240,18 @@ __global__ __launch_bounds__(64 * dec_waves<G>()) void k_nsn_part(const half_t *
     const int64_t qbase = b * Hkv * G + g * G;
     const int64_t c0 = (int64_t)blockIdx.x * chunk, c1 = min(T, c0 + chunk);
     // The first tile's loads go out before the prologue, every later tile's
-    // before the current one is processed.
+    // before the current one is processed.  Lanes past the end of the range
+    // (and every lane of a wave the range gives no tile) load the range's
+    // first token, whose weight is then 0.
     int64_t t0 = c0 + 64 * wv;
-    TileIn cur = load_tile(kc, ks1, ks2, vc, vs1, vs2, bg * ldt, t0 + lane < c1 ? t0 + lane : t0);
+    auto fetch = [&](int64_t t) {
+        if constexpr (DQ) return load_tile_dq(kc, kdq, ks2, vc, vdq, vs2, bg, T, t);
+        else return load_tile(kc, ks1, ks2, vc, vs1, vs2, bg * ldt, t);
+    };
+    TileIn cur = fetch(t0 + lane < c1 ? t0 + lane : c0);
     const int64_t gfirst = GROUPED ? c0 / gsize : 0;
-    nsn_tables<G, 64 * NW>(q, GROUPED ? ko + (bg * ngc + gfirst) * kD : ko + bg * kD, cb, qbase, sm.t);
+    nsn_tables<G, 64 * NW, DQ>(q, DQ ? nullptr : GROUPED ? ko + (bg * ngc + gfirst) * kD : ko + bg * kD, cb, qbase,
+                               sm.t, kdq, bg);
     if constexpr (GROUPED) {
         // the block's groups: rotated V means and <q_h, o^K_g> = <q'_h, H o^K_g / sqrt(d)>
         const int ngb = (int)((c1 - c0 + gsize - 1) / gsize);
@@ -244,7 +287,7 @@ __global__ __launch_bounds__(64 * dec_waves<G>()) void k_nsn_part(const half_t *
         const bool valid = t0 + lane < c1;
         const int64_t tn = t0 + 64 * NW;
         TileIn nxt = cur;
-        if (tn < c1) nxt = load_tile(kc, ks1, ks2, vc, vs1, vs2, bg * ldt, tn + lane < c1 ? tn + lane : tn);
+        if (tn < c1) nxt = fetch(tn + lane < c1 ? tn + lane : c0);
         float ks[G];
         nsn_key_sum<G>(cur.kcode, sm.t.tab, ks);
         float w[G];
@@ -275,7 +318,7 @@ __global__ __launch_bounds__(64 * dec_waves<G>()) void k_nsn_part(const half_t *
         for (int h = 0; h < G; ++h) sm.wts[wv][lane][h] = w[h];
         wave_lds_sync();
         // all 64 tokens: past the end the weights are 0 and the staged index
-        // is that of the tile's first token
+        // is that of the range's first token
 #pragma unroll
         for (int i = 0; i < 64; ++i) {
             const uint32_t j = vcb[16 * i];
@@ -340,9 +383,9 @@ __global__ __launch_bounds__(64 * dec_waves<G>()) void k_nsn_part(const half_t *
 // 2 lane, 2 lane + 1): merge of the n_split partial slots, f_s = 2^(M_s - M),
 // then out = (H acc / sqrt(d) + WO o_V) / L (vo NULL: the V means are already
 // in acc, WO = 0).
-template <int G>
+template <int G, bool DQ>
 __global__ __launch_bounds__(64 * G) void k_nsn_merge(const float *__restrict__ part, const float *__restrict__ vo,
-                                                      float *__restrict__ out, int64_t Hkv, int n_split)
+                                                      float *__restrict__ out, int64_t Hkv, int n_split, NsnDqIn vdq)
 {
     const int lane = threadIdx.x & 63, h = threadIdx.x >> 6;
     const int64_t bg = blockIdx.x, b = bg / Hkv, g = bg % Hkv;
@@ -390,7 +433,8 @@ __global__ __launch_bounds__(64 * G) void k_nsn_merge(const float *__restrict__ 
         }
     }
     wave_fwht(x0, x1, lane);
-    const f2_t ov = vo ? reinterpret_cast<const f2_t *>(vo + bg * kD)[lane] : f2_t{0.0f, 0.0f};
+    const f2_t ov = DQ ? load_mean<true>(nullptr, vdq, bg, lane)
+                       : vo ? load_mean<false>(vo + bg * kD, vdq, bg, lane) : f2_t{0.0f, 0.0f};
     const float inv = 1.0f / L;
     reinterpret_cast<f2_t *>(out + ((b * Hkv + g) * G + h) * kD)[lane] =
         f2_t{fmaf(x0, kInvSqrtD, WO * ov.x) * inv, fmaf(x1, kInvSqrtD, WO * ov.y) * inv};
@@ -431,13 +475,13 @@ __global__ __launch_bounds__(64 * G) void k_nsn_tail(const half_t *__restrict__ 
     }
 }
 
-template <int G>
+template <int G, bool DQ>
 hipError_t logits_g(const kvq_ctx *ctx, const void *q, int64_t B, int64_t T, const uint8_t *codes, const float *s1,
-                    const float *s2, const float *o, float *logits, hipStream_t s)
+                    const float *s2, const float *o, float *logits, const NsnDqIn &dq, hipStream_t s)
 {
     const int64_t n_chunks = (T + kLogitChunk - 1) / kLogitChunk;
-    hipLaunchKernelGGL(k_nsn_logits<G>, dim3((unsigned)n_chunks, (unsigned)(B * ctx->H)), dim3(kThreadsN), 0, s,
-                       (const half_t *)q, (const u4_t *)codes, s1, s2, o, ctx->d_vq, logits, (int64_t)ctx->H, T);
+    hipLaunchKernelGGL((k_nsn_logits<G, DQ>), dim3((unsigned)n_chunks, (unsigned)(B * ctx->H)), dim3(kThreadsN), 0, s,
+                       (const half_t *)q, (const u4_t *)codes, s1, s2, o, ctx->d_vq, logits, (int64_t)ctx->H, T, dq);
     return hipGetLastError();
 }
 
@@ -448,12 +492,19 @@ hipError_t decode_g(const kvq_ctx *ctx, const void *q, int64_t B, int64_t T, con
     const int64_t chunk = nsn_decode_chunk(T, n_split);
     const int ns = (int)((T + chunk - 1) / chunk);
     float *part = (float *)ws;
-    hipLaunchKernelGGL((k_nsn_part<G, false>), dim3((unsigned)ns, (unsigned)(B * ctx->H)), dim3(64 * dec_waves<G>()),
-                       0, s, (const half_t *)q, (const u4_t *)kv.kc, kv.ks1, kv.ks2, kv.ko, (const u4_t *)kv.vc,
-                       kv.vs1, kv.vs2, ctx->d_vq, part, (int64_t)ctx->H, T, chunk, sm_scale * kLog2e, T, ns,
-                       (const float *)nullptr, (int64_t)0, (int64_t)0);
-    hipLaunchKernelGGL(k_nsn_merge<G>, dim3((unsigned)(B * ctx->H)), dim3(64 * G), 0, s, part, kv.vo, out,
-                       (int64_t)ctx->H, ns);
+#define KVQ_NSN_PART(DQ)                                                                                        \
+    hipLaunchKernelGGL((k_nsn_part<G, false, DQ>), dim3((unsigned)ns, (unsigned)(B * ctx->H)),                   \
+                       dim3(64 * dec_waves<G>()), 0, s, (const half_t *)q, (const u4_t *)kv.kc, kv.ks1, kv.ks2, kv.ko, \
+                       (const u4_t *)kv.vc, kv.vs1, kv.vs2, ctx->d_vq, part, (int64_t)ctx->H, T, chunk,           \
+                       sm_scale * kLog2e, T, ns, (const float *)nullptr, (int64_t)0, (int64_t)0, kv.kdq, kv.vdq);   \
+    hipLaunchKernelGGL((k_nsn_merge<G, DQ>), dim3((unsigned)(B * ctx->H)), dim3(64 * G), 0, s, part, kv.vo, out,  \
+                       (int64_t)ctx->H, ns, kv.vdq)
+    if (kv.dq) {
+        KVQ_NSN_PART(true);
+    } else {
+        KVQ_NSN_PART(false);
+    }
+#undef KVQ_NSN_PART
     return hipGetLastError();
 }
 
@@ -480,12 +531,12 @@ hipError_t decode_stream_g(const kvq_ctx *ctx, const void *q, int64_t B, int64_t
                            (const half_t *)st.kt, (const half_t *)st.vt, scale2, part, out, st.R, st.R_cap, n_part,
                            ns, T == 0);
     if (T == 0) return hipGetLastError();
-    hipLaunchKernelGGL((k_nsn_part<G, true>), dim3((unsigned)ns, (unsigned)bgs), dim3(64 * dec_waves<G>()), 0, s,
-                       (const half_t *)q, (const u4_t *)kv.kc, kv.ks1, kv.ks2, kv.ko, (const u4_t *)kv.vc, kv.vs1,
+    hipLaunchKernelGGL((k_nsn_part<G, true, false>), dim3((unsigned)ns, (unsigned)bgs), dim3(64 * dec_waves<G>()), 0,
+                       s, (const half_t *)q, (const u4_t *)kv.kc, kv.ks1, kv.ks2, kv.ko, (const u4_t *)kv.vc, kv.vs1,
                        kv.vs2, ctx->d_vq, part, (int64_t)ctx->H, T, chunk, scale2, st.T_cap, n_part, kv.vo, st.Gs,
-                       st.T_cap / st.Gs);
-    hipLaunchKernelGGL(k_nsn_merge<G>, dim3((unsigned)bgs), dim3(64 * G), 0, s, part, (const float *)nullptr, out,
-                       (int64_t)ctx->H, n_part);
+                       st.T_cap / st.Gs, NsnDqIn{}, NsnDqIn{});
+    hipLaunchKernelGGL((k_nsn_merge<G, false>), dim3((unsigned)bgs), dim3(64 * G), 0, s, part, (const float *)nullptr,
+                       out, (int64_t)ctx->H, n_part, NsnDqIn{});
     return hipGetLastError();
 }
 
@@ -495,11 +546,24 @@ hipError_t launch_nsn_logits(const kvq_ctx *ctx, const void *q, int64_t B, int64
                              const uint8_t *codes, const float *s1, const float *s2, const float *o, float *logits,
                              hipStream_t s)
 {
+    const NsnDqIn none{};
     switch (Hq / ctx->H) {
-        case 1: return logits_g<1>(ctx, q, B, T, codes, s1, s2, o, logits, s);
-        case 2: return logits_g<2>(ctx, q, B, T, codes, s1, s2, o, logits, s);
-        case 4: return logits_g<4>(ctx, q, B, T, codes, s1, s2, o, logits, s);
-        case 8: return logits_g<8>(ctx, q, B, T, codes, s1, s2, o, logits, s);
+        case 1: return logits_g<1, false>(ctx, q, B, T, codes, s1, s2, o, logits, none, s);
+        case 2: return logits_g<2, false>(ctx, q, B, T, codes, s1, s2, o, logits, none, s);
+        case 4: return logits_g<4, false>(ctx, q, B, T, codes, s1, s2, o, logits, none, s);
+        case 8: return logits_g<8, false>(ctx, q, B, T, codes, s1, s2, o, logits, none, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_nsn_logits_dq(const kvq_ctx *ctx, const void *q, int64_t B, int64_t Hq, int64_t T,
+                                const uint8_t *codes, const NsnDqIn &dq, const float *s2, float *logits, hipStream_t s)
+{
+    switch (Hq / ctx->H) {
+        case 1: return logits_g<1, true>(ctx, q, B, T, codes, nullptr, s2, nullptr, logits, dq, s);
+        case 2: return logits_g<2, true>(ctx, q, B, T, codes, nullptr, s2, nullptr, logits, dq, s);
+        case 4: return logits_g<4, true>(ctx, q, B, T, codes, nullptr, s2, nullptr, logits, dq, s);
+        case 8: return logits_g<8, true>(ctx, q, B, T, codes, nullptr, s2, nullptr, logits, dq, s);
         default: return hipErrorInvalidValue;
     }
 }

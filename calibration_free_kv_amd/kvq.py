@@ -22,6 +22,7 @@ KVQ_KIND_K, KVQ_KIND_V = 0, 1
 KVQ_CODEBOOK_GAUSS, KVQ_CODEBOOK_BETA = 0, 1
 KVQ_ROTATION_HADAMARD, KVQ_ROTATION_DENSE = 0, 1
 KVQ_NSN_ADAPTIVE_SCALE = 1
+KVQ_NSN_DQ_CODEBOOK = 2
 D = 128
 
 EXPORTS = [
@@ -31,6 +32,7 @@ EXPORTS = [
     "kvq_nsn_attn_decode_ws_bytes", "kvq_nsn_attn_decode", "kvq_nsn_attn_decode_splits",
     "kvq_attn_decode_stream_ws_bytes", "kvq_attn_decode_stream", "kvq_flush", "kvq_attn_decode_noalloc",
     "kvq_nsn_flush_ws_bytes", "kvq_nsn_flush", "kvq_nsn_attn_decode_stream_ws_bytes", "kvq_nsn_attn_decode_stream",
+    "kvq_nsn_vq_dq_ws_bytes", "kvq_nsn_vq_quantize_dq", "kvq_nsn_logits_dq", "kvq_nsn_attn_decode_dq",
 ]
 
 
@@ -102,6 +104,12 @@ def lib():
         L.kvq_nsn_attn_decode_stream_ws_bytes.restype = sz
         L.kvq_nsn_attn_decode_stream.argtypes = [vp, vp, i64, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp,
                                                  i64, i64, vp, vp, C.c_float, vp, vp, sz, i32, vp]
+        L.kvq_nsn_vq_dq_ws_bytes.argtypes = [vp, i64, i64]
+        L.kvq_nsn_vq_dq_ws_bytes.restype = sz
+        L.kvq_nsn_vq_quantize_dq.argtypes = [vp, vp, i64, i64, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.kvq_nsn_logits_dq.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.kvq_nsn_attn_decode_dq.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                             C.c_float, vp, vp, sz, i32, vp]
         _lib = L
     return _lib
 
@@ -338,6 +346,47 @@ class Context:
                                    v["s2"], v["o"], sm_scale, out, ws, n_split)
         return out
 
+    def nsn_vq_quantize_dq(self, x, out=None, ws=None):
+        """NSN-VQ with 4-bit s1 and means: x [H,T,128] fp16 -> dict(codes [H,T,16],
+        s1q [H,ceil(T/2)] u8, s1p [H,ceil(T/32),2], s2 [H,T], oq [H,64] u8, op [H,2])."""
+        _dev_tensor(x, torch.float16, "x")
+        H, T, _ = x.shape
+        dev = x.device
+        if ws is None:
+            ws = torch.empty(int(lib().kvq_nsn_vq_dq_ws_bytes(self.handle, H, T)), dtype=torch.uint8, device=dev)
+        if out is None:
+            out = dict(codes=torch.empty((H, T, 16), dtype=torch.uint8, device=dev),
+                       s1q=torch.empty((H, (T + 1) // 2), dtype=torch.uint8, device=dev),
+                       s1p=torch.empty((H, (T + 31) // 32, 2), dtype=torch.float32, device=dev),
+                       s2=torch.empty((H, T), dtype=torch.float32, device=dev),
+                       oq=torch.empty((H, D // 2), dtype=torch.uint8, device=dev),
+                       op=torch.empty((H, 2), dtype=torch.float32, device=dev))
+        kvq_nsn_vq_quantize_dq(self, x, H, T, out, ws)
+        return out
+
+    def nsn_logits_dq(self, q, e, out=None):
+        """q [B,Hq,128] fp16; e: dict as nsn_vq_quantize_dq returns it with heads
+        [B,Hkv] leading (codes [B,Hkv,T,16], s1q [B,Hkv,ceil(T/2)], ...) -> [B,Hq,T]."""
+        _dev_tensor(q, torch.float16, "q")
+        B, Hq, _ = q.shape
+        T = e["codes"].shape[2]
+        if out is None:
+            out = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+        kvq_nsn_logits_dq(self, q, B, Hq, T, e, out)
+        return out
+
+    def nsn_attn_decode_dq(self, q, k, v, sm_scale: float = 0.0, ws=None, out=None, n_split: int = 0):
+        """Decode over double-quantised keys and values (dicts as nsn_logits_dq takes)."""
+        _dev_tensor(q, torch.float16, "q")
+        B, Hq, _ = q.shape
+        T = k["codes"].shape[2]
+        if ws is None:
+            ws = self.nsn_decode_ws(B, Hq, T)
+        if out is None:
+            out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+        kvq_nsn_attn_decode_dq(self, q, B, Hq, T, k, v, sm_scale, out, ws, n_split)
+        return out
+
     def nsn_stream_alloc(self, B, T_cap, Gs):
         """Packed arrays of a streaming NSN-VQ cache: codes [B,Hkv,T_cap,16], s1/s2
         [B,Hkv,T_cap], means o [B,Hkv,T_cap/Gs,128], for K and V."""
@@ -497,3 +546,32 @@ def kvq_nsn_attn_decode_stream(ctx: Context, q, B, H_q, T, T_cap, Gs, kc, ks1, k
                                             _ptr(k_tail), _ptr(v_tail), float(sm_scale), _ptr(out), _ptr(ws),
                                             ws.numel() * ws.element_size(), int(n_split), _stream(q.device)),
            "kvq_nsn_attn_decode_stream")
+
+
+_DQ_KEYS = (("codes", torch.uint8), ("s1q", torch.uint8), ("s1p", torch.float32), ("s2", torch.float32),
+            ("oq", torch.uint8), ("op", torch.float32))
+
+
+def _dq_args(e, tag):
+    for n, dt in _DQ_KEYS:
+        _dev_tensor(e[n], dt, tag + n)
+    return [_ptr(e[n]) for n, _ in _DQ_KEYS]
+
+
+def kvq_nsn_vq_quantize_dq(ctx: Context, x, H, T, out, ws):
+    c, s1q, s1p, s2, oq, op = _dq_args(out, "")
+    _check(lib().kvq_nsn_vq_quantize_dq(ctx.handle, _ptr(x), H, T, c, s1q, s1p, s2, oq, op, _ptr(ws),
+                                        ws.numel() * ws.element_size(), _stream(x.device)), "kvq_nsn_vq_quantize_dq")
+
+
+def kvq_nsn_logits_dq(ctx: Context, q, B, H_q, T, e, logits):
+    _dev_tensor(logits, torch.float32, "logits")
+    _check(lib().kvq_nsn_logits_dq(ctx.handle, _ptr(q), B, H_q, T, *_dq_args(e, ""), _ptr(logits),
+                                   _stream(q.device)), "kvq_nsn_logits_dq")
+
+
+def kvq_nsn_attn_decode_dq(ctx: Context, q, B, H_q, T, k, v, sm_scale, out, ws, n_split=0):
+    _dev_tensor(out, torch.float32, "out")
+    _check(lib().kvq_nsn_attn_decode_dq(ctx.handle, _ptr(q), B, H_q, T, *_dq_args(k, "k_"), *_dq_args(v, "v_"),
+                                        float(sm_scale), _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
+                                        int(n_split), _stream(q.device)), "kvq_nsn_attn_decode_dq")

@@ -163,6 +163,28 @@ def random_nsn_codes(seed: int, lead, d: int = D, sub: int = 8, o_scale: float =
                 o=(rng.standard_normal(lead[:-1] + og + (d,)) * o_scale).astype(np.float32))
 
 
+def random_nsn_dq_codes(seed: int, lead, d: int = D, sub: int = 8, block: int = 32):
+    """Stand-in NSN-VQ encoded vectors with 4-bit byproducts (no quantizer
+    involved): entry indices uniform [*lead, d/sub] u8, s2 ~ U(0.6, 1.0) fp32
+    [*lead], s1 as uniform 4-bit codes packed two per byte [*lead[:-1],
+    ceil(T/2)] with per-block (lo, step) fp32 [*lead[:-1], ceil(T/block), 2],
+    lo = exp(N(0.8, 0.2^2)), step ~ U(0.02, 0.06), and the means as uniform
+    4-bit codes [*lead[:-1], d/2] with (lo, step) [*lead[:-1], 2], lo ~
+    U(-1.2, -0.8), step ~ U(0.1, 0.16)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    lead = tuple(lead)
+    T = lead[-1]
+    rows = lead[:-1]
+    nb = (T + block - 1) // block
+    s1p = np.stack([np.exp(rng.normal(0.8, 0.2, size=rows + (nb,))), rng.uniform(0.02, 0.06, size=rows + (nb,))],
+                   axis=-1).astype(np.float32)
+    op = np.stack([rng.uniform(-1.2, -0.8, size=rows), rng.uniform(0.1, 0.16, size=rows)], axis=-1).astype(np.float32)
+    return dict(codes=rng.integers(0, 256, size=lead + (d // sub,), dtype=np.uint8),
+                s1q=rng.integers(0, 256, size=rows + ((T + 1) // 2,), dtype=np.uint8), s1p=s1p,
+                s2=rng.uniform(0.6, 1.0, size=lead).astype(np.float32),
+                oq=rng.integers(0, 256, size=rows + (d // 2,), dtype=np.uint8), op=op)
+
+
 def random_orthogonal(seed: int, d: int = D):
     """A Haar-random orthogonal d x d matrix (float64): QR of a seeded N(0,1)
     matrix with the signs of R's diagonal moved into Q."""

@@ -86,7 +86,12 @@ enum { KVQ_ROTATION_HADAMARD = 0, KVQ_ROTATION_DENSE = 1 };
  * (1 when <z, zq> <= 0), which keeps the component of the reconstruction
  * along the token exact; alpha is folded into the stored s2 (s2 <- alpha s2),
  * so the scoring calls use it unchanged. */
-enum { KVQ_NSN_ADAPTIVE_SCALE = 1 };
+/* KVQ_NSN_DQ_CODEBOOK ([NSN] Metodologia sec. 3, double quantisation): the
+ * codebook's entries are stored with 4 bits: the 2048 values as one block,
+ * lo = min, step = (max - lo) / 15, each replaced by lo + c step with c the
+ * nearest of the 16 levels (decided in double precision at kvq_create); the
+ * context then encodes and scores with these values. */
+enum { KVQ_NSN_ADAPTIVE_SCALE = 1, KVQ_NSN_DQ_CODEBOOK = 2 };
 
 /* Configuration of a context.  Host arrays are copied by kvq_create.
  *
@@ -363,6 +368,49 @@ kvq_status kvq_nsn_attn_decode_splits(kvq_ctx *ctx, const void *q_f16, int64_t B
                                       const float *v_s1, const float *v_s2, const float *v_o,
                                       float sm_scale, float *out, void *ws, size_t ws_bytes,
                                       int32_t n_split, void *stream);
+
+/* Double quantisation of the NSN byproducts ([NSN] Metodologia sec. 3: the
+ * parameters o and s1 are stored with 4 bits).  The page gives no scheme;
+ * here a block of values v is stored as 4-bit codes c with one fp32 pair
+ * (lo, step): lo = min v, step = (max v - lo) / 15, c the nearest level of
+ * (v - lo) / step (0 when step = 0), value lo + c step.  Blocks: the 128
+ * means of a head; s1 in blocks of 32 consecutive tokens of a head (the last
+ * one shorter).  Packing: code i of a row in byte i / 2, low nibble for even
+ * i.  Per token 16 code bytes + 0.5 (s1) + 0.25 (block pair) + 4 (s2).
+ *
+ * Workspace bytes kvq_nsn_vq_quantize_dq needs. */
+size_t kvq_nsn_vq_dq_ws_bytes(const kvq_ctx *ctx, int64_t H, int64_t T);
+
+/* NSN-VQ as kvq_nsn_vq_quantize, with the double-quantised byproducts: the
+ * mean o of each head is quantised first and the shift b_t = a_t - o_hat
+ * uses the stored (dequantised) means, so that
+ * x_hat = s1_hat (s2 H zq / sqrt(d) + o_hat) inverts the encoding; s1 is
+ * quantised per block of 32 tokens.
+ *   codes  out [H, T, 16] bytes;  s2 out [H, T] fp32
+ *   s1q    out [H, ceil(T / 2)] bytes;  s1p out [H, ceil(T / 32), 2] fp32 (lo, step)
+ *   oq     out [H, 64] bytes;  op out [H, 2] fp32 (lo, step)
+ *   ws     kvq_nsn_vq_dq_ws_bytes() bytes, 256-byte aligned, no initialisation.
+ * s1p and op 8-byte aligned.  T >= 1.  Requires a context in KVQ_MODE_NSN_VQ. */
+kvq_status kvq_nsn_vq_quantize_dq(kvq_ctx *ctx, const void *x_f16, int64_t H, int64_t T, uint8_t *codes,
+                                  uint8_t *s1q, float *s1p, float *s2, uint8_t *oq, float *op, void *ws,
+                                  size_t ws_bytes, void *stream);
+
+/* kvq_nsn_logits over double-quantised byproducts (layouts of
+ * kvq_nsn_vq_quantize_dq with its heads = the B * H_kv pairs): s1 and o are
+ * read as lo + c step.  Other arguments and errors as kvq_nsn_logits. */
+kvq_status kvq_nsn_logits_dq(kvq_ctx *ctx, const void *q_f16, int64_t B, int64_t H_q, int64_t T,
+                             const uint8_t *codes, const uint8_t *s1q, const float *s1p, const float *s2,
+                             const uint8_t *oq, const float *op, float *logits, void *stream);
+
+/* kvq_nsn_attn_decode_splits over double-quantised keys and values (layouts
+ * of kvq_nsn_vq_quantize_dq); workspace kvq_nsn_attn_decode_ws_bytes().
+ * Other arguments and errors as kvq_nsn_attn_decode_splits. */
+kvq_status kvq_nsn_attn_decode_dq(kvq_ctx *ctx, const void *q_f16, int64_t B, int64_t H_q, int64_t T,
+                                  const uint8_t *k_codes, const uint8_t *k_s1q, const float *k_s1p,
+                                  const float *k_s2, const uint8_t *k_oq, const float *k_op,
+                                  const uint8_t *v_codes, const uint8_t *v_s1q, const float *v_s1p,
+                                  const float *v_s2, const uint8_t *v_oq, const float *v_op, float sm_scale,
+                                  float *out, void *ws, size_t ws_bytes, int32_t n_split, void *stream);
 
 /* Streaming NSN-VQ cache ([NSN] Detalhes de Implementacao: recent tokens
  * stay in a full-precision window that is quantised when it fills, as in

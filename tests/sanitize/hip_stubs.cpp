@@ -81,12 +81,18 @@ hipError_t launch_nsn_vq(const kvq_ctx *, const void *, int64_t H, int64_t T, ui
 hipError_t launch_nsn_logits(const kvq_ctx *, const void *, int64_t B, int64_t Hq, int64_t T, const uint8_t *,
                              const float *, const float *, const float *, float *, hipStream_t)
 { return rec("nsn_logits", B, Hq, T); }
-hipError_t launch_nsn_decode(const kvq_ctx *, const void *, int64_t B, int64_t Hq, int64_t T, const NsnKV &, float,
+hipError_t launch_nsn_decode(const kvq_ctx *, const void *, int64_t B, int64_t Hq, int64_t T, const NsnKV &kv, float,
                              float *, void *, int ns, hipStream_t)
-{ return rec("nsn_decode", B, Hq, T, ns); }
+{ return rec(kv.dq ? "nsn_decode_dq" : "nsn_decode", B, Hq, T, ns); }
 hipError_t launch_nsn_vq_strided(const kvq_ctx *, const void *, int64_t H, int64_t T, int64_t, uint8_t *, float *,
                                  float *, int64_t ldt, float *, int64_t, void *, hipStream_t)
 { return rec("nsn_vq_strided", H, T, ldt); }
+hipError_t launch_nsn_vq_dq(const kvq_ctx *, const void *, int64_t H, int64_t T, uint8_t *, float *, const NsnDq &,
+                            void *, hipStream_t)
+{ return rec("nsn_vq_dq", H, T); }
+hipError_t launch_nsn_logits_dq(const kvq_ctx *, const void *, int64_t B, int64_t Hq, int64_t T, const uint8_t *,
+                                const NsnDqIn &, const float *, float *, hipStream_t)
+{ return rec("nsn_logits_dq", B, Hq, T); }
 hipError_t launch_nsn_decode_stream(const kvq_ctx *, const void *, int64_t B, int64_t Hq, int64_t T, const NsnKV &,
                                     const NsnStream &, float, float *, void *, int ns, hipStream_t)
 { return rec("nsn_decode_stream", B, Hq, T, ns); }

@@ -230,6 +230,38 @@ int main()
     CHECK(g_last.n_split >= 1 && g_last.n_split <= (T + 63) / 64);
     CHECK(kvq_nsn_attn_decode(nsn, q.p, 1, Hq, T, codes.as<uint8_t>(), s1.as<float>(), s1.as<float>(), o.as<float>(), codes.as<uint8_t>(), s1.as<float>(), s1.as<float>(), o.as<float>(), 0.f, out.as<float>(), nd.p, ndw - 1, st0) == KVQ_E_WORKSPACE);
 
+    // NSN-VQ with double-quantised byproducts
+    {
+        const size_t qws = kvq_nsn_vq_dq_ws_bytes(nsn, H, T);
+        CHECK(qws > kvq_nsn_vq_ws_bytes(nsn, H, T));
+        Buf qw(qws), s1q(H * T), s1p(H * T * 8), s2(H * T * 4), oq(H * 64), op(H * 8);
+        CHECK(kvq_nsn_vq_quantize_dq(nsn, x.p, H, T, codes.as<uint8_t>(), s1q.as<uint8_t>(), s1p.as<float>(), s2.as<float>(), oq.as<uint8_t>(), op.as<float>(), qw.p, qws, st0) == KVQ_OK);
+        CHECK(std::strcmp(g_last.what, "nsn_vq_dq") == 0 && g_last.a == H && g_last.b == T);
+        CHECK(kvq_nsn_vq_quantize_dq(nsn, x.p, H, T, codes.as<uint8_t>(), s1q.as<uint8_t>(), s1p.as<float>(), s2.as<float>(), oq.as<uint8_t>(), op.as<float>(), qw.p, qws - 1, st0) == KVQ_E_WORKSPACE);
+        CHECK(kvq_nsn_vq_quantize_dq(nsn, x.p, H, T, codes.as<uint8_t>(), s1q.as<uint8_t>(), s1p.as<float>(4), s2.as<float>(), oq.as<uint8_t>(), op.as<float>(), qw.p, qws, st0) == KVQ_E_INVAL);
+        CHECK(kvq_nsn_vq_quantize_dq(mse, x.p, H, T, codes.as<uint8_t>(), s1q.as<uint8_t>(), s1p.as<float>(), s2.as<float>(), oq.as<uint8_t>(), op.as<float>(), qw.p, qws, st0) == KVQ_E_INVAL);
+        CHECK(kvq_nsn_logits_dq(nsn, q.p, 1, H * 8, T, codes.as<uint8_t>(), s1q.as<uint8_t>(), s1p.as<float>(), s2.as<float>(), oq.as<uint8_t>(), op.as<float>(), lg.as<float>(), st0) == KVQ_OK);
+        CHECK(std::strcmp(g_last.what, "nsn_logits_dq") == 0);
+        CHECK(kvq_nsn_logits_dq(nsn, q.p, 1, H * 8, T, codes.as<uint8_t>(), nullptr, s1p.as<float>(), s2.as<float>(), oq.as<uint8_t>(), op.as<float>(), lg.as<float>(), st0) == KVQ_E_INVAL);
+        const size_t ddw = kvq_nsn_attn_decode_ws_bytes(nsn, 1, Hq, T);
+        Buf dd(ddw);
+        CHECK(kvq_nsn_attn_decode_dq(nsn, q.p, 1, Hq, T, codes.as<uint8_t>(), s1q.as<uint8_t>(), s1p.as<float>(), s2.as<float>(), oq.as<uint8_t>(), op.as<float>(), codes.as<uint8_t>(), s1q.as<uint8_t>(), s1p.as<float>(), s2.as<float>(), oq.as<uint8_t>(), op.as<float>(), 0.f, out.as<float>(), dd.p, ddw, 0, st0) == KVQ_OK);
+        CHECK(std::strcmp(g_last.what, "nsn_decode_dq") == 0 && g_last.n_split >= 1);
+        CHECK(kvq_nsn_attn_decode_dq(nsn, q.p, 1, Hq, T, codes.as<uint8_t>(), s1q.as<uint8_t>(), s1p.as<float>(), s2.as<float>(), oq.as<uint8_t>(), op.as<float>(), codes.as<uint8_t>(), s1q.as<uint8_t>(), s1p.as<float>(), s2.as<float>(), oq.as<uint8_t>(), nullptr, 0.f, out.as<float>(), dd.p, ddw, 0, st0) == KVQ_E_INVAL);
+        CHECK(kvq_nsn_attn_decode_dq(nsn, q.p, 1, Hq, T, codes.as<uint8_t>(), s1q.as<uint8_t>(), s1p.as<float>(), s2.as<float>(), oq.as<uint8_t>(), op.as<float>(), codes.as<uint8_t>(), s1q.as<uint8_t>(), s1p.as<float>(), s2.as<float>(), oq.as<uint8_t>(), op.as<float>(), 0.f, out.as<float>(), dd.p, ddw - 1, 0, st0) == KVQ_E_WORKSPACE);
+    }
+    {
+        // the codebook option: accepted in the NSN mode only
+        kvq_config cd = base(1, KVQ_MODE_NSN_VQ, H);
+        cd.vq_codebook = cb.data();
+        cd.nsn_options = KVQ_NSN_DQ_CODEBOOK | KVQ_NSN_ADAPTIVE_SCALE;
+        kvq_ctx *cx = nullptr;
+        CHECK(kvq_create(&cd, &cx) == KVQ_OK && kvq_destroy(cx) == KVQ_OK);
+        cd = base(3, KVQ_MODE_MSE, H);
+        cd.nsn_options = KVQ_NSN_DQ_CODEBOOK;
+        CHECK(kvq_create(&cd, &cx) == KVQ_E_INVAL);
+    }
+
     // NSN-VQ streaming cache: flush groups of Gs tokens, decode over packed + window
     {
         const int64_t Gs = 128, Tc = 1024, Rc = 192, Tn = 512, Rn = 40;
