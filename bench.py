@@ -47,6 +47,7 @@ HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, GB/s
 FP16_MFMA_TFLOPS = 2500.0  # MI355X dense fp16 matrix peak
 D = 128
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "kvq_quantize_kv_l8b32k_b3_traffic.md")
+TRACE_RECORD = os.path.join(ROOT, "profiles", "kvq_step_l8b32k_b3_kernel_trace.md")
 QUANT_SRC = os.path.join(ROOT, "calibration_free_kv_amd", "csrc", "kvq_quantize.hip")
 
 
@@ -75,19 +76,25 @@ def source_sha(path):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()
 
 
-def read_traffic():
-    """Bytes per launch from the committed counter record, if it is current."""
+def read_record(path, key):
+    """A value of a committed rocprofv3 record, if the record is current (its
+    source_sha256 is that of the quantize kernel's source)."""
     try:
-        txt = open(TRAFFIC_RECORD).read()
+        txt = open(path).read()
     except OSError:
         return None
     m = dict(re.findall(r"^- (\w+): `?([^`\n]+)`?$", txt, re.M))
     if m.get("source_sha256") != source_sha(QUANT_SRC):
         return None
     try:
-        return float(m["traffic_bytes_per_launch"])
+        return float(m[key])
     except (KeyError, ValueError):
         return None
+
+
+def read_traffic():
+    """Bytes per launch from the committed counter record, if it is current."""
+    return read_record(TRAFFIC_RECORD, "traffic_bytes_per_launch")
 
 
 class Timer:
@@ -237,6 +244,18 @@ def cpu_baseline(inp, bits, budget_s=10.0):
             "single_thread_value": out[1][2], "cpu_model": cpu_model()}
 
 
+def trace_roofline(qb):
+    """The same roofline from the committed rocprofv3 kernel trace of this step
+    (kernel durations only, without the gaps between launches that the events
+    include), or None when the kernel source has changed since the trace."""
+    us = read_record(TRACE_RECORD, "quantize_avg_us")
+    if us is None:
+        return None
+    gbs = qb / (us * 1e-6) / 1e9
+    return {"ms_per_launch": us * 1e-3, "achieved": gbs, "frac": gbs / HBM_PEAK_GBS,
+            "source": "profiles/" + os.path.basename(TRACE_RECORD)}
+
+
 def main_step(torch, kvq, synth, args, dev, timer):
     bits = 3
     inp = synth.make("l8b32k")
@@ -321,7 +340,7 @@ def main_step(torch, kvq, synth, args, dev, timer):
                    "bits": bits, "tokens": T, "kv_heads": Hkv, "q_heads": Hq, "batch": B, "buffer_sets": nset},
         "roofline": {"bound": "hbm", "achieved": q_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": q_gbs / HBM_PEAK_GBS, "traffic": read_traffic(), "kernel": "kvq_quantize_kv",
-                     "bytes_per_launch": qb, "ms_per_launch": q_ms},
+                     "bytes_per_launch": qb, "ms_per_launch": q_ms, "trace": trace_roofline(qb)},
         "kernels": {
             "kvq_quantize_kv": {"ms": q_ms, "GB/s": q_gbs, "frac_hbm": q_gbs / HBM_PEAK_GBS,
                                 "vectors_per_s": 2 * n / (q_ms * 1e-3)},
@@ -584,7 +603,65 @@ def rows(torch, kvq, synth, dev, timer, reps, oracle_rates):
     oracle_rates["nsn_attn_decode_8x65536_g4"] = oracle_rate(
         lambda: O.nsn_attention(qh, e["codes"], e["s1"], e["s2"], e["o"], f["codes"], f["s1"], f["s2"], f["o"], cb),
         H * 1024)
-    del kv, ctx
+    del kv
+
+    # double-quantised byproducts (4-bit s1 per 32 tokens, 4-bit means): the
+    # encoder over 8 heads x 65536 tokens and decode from such codes
+    x0 = torch.from_numpy(inp["x"]).to(dev)
+    xsn = [x0] + [x0.clone() for _ in range(3)]
+    odq = ctx.nsn_vq_quantize_dq(x0)
+    wsq = torch.empty(int(kvq.lib().kvq_nsn_vq_dq_ws_bytes(ctx.handle, H, T)), dtype=torch.uint8, device=dev)
+    dq_meta = H * T * (0.5 + 8 / 32) + H * (64 + 8)  # s1 nibbles and block pairs, mean nibbles and pairs
+    out["nsn_vq_dq_8x65536"] = row(*timer.run(lambda i: ctx.nsn_vq_quantize_dq(xsn[i % 4], out=odq, ws=wsq), reps, 4),
+                                   nbytes=H * T * (2 * D + 16 + 4) + dq_meta, flops=H * T * 16 * 256 * 8 * 2,
+                                   units_per_launch=H * T, unit="vectors",
+                                   note="three launches; 4-bit s1 (32-token blocks) and means")
+    del xsn, x0
+    per_set = n * 2 * (16 + 4.75)
+    ns = rng_sets(per_set)
+    kvd = [(dv(synth.random_nsn_dq_codes(70 + 2 * i, (1, H, T))), dv(synth.random_nsn_dq_codes(71 + 2 * i, (1, H, T))))
+           for i in range(ns)]
+
+    def ndecq(i):
+        ctx.nsn_attn_decode_dq(qn, kvd[i % ns][0], kvd[i % ns][1], ws=wsd, out=dout)
+    last = ns - 1
+    out["nsn_attn_decode_dq_8x65536_g4"] = row(
+        *run_graph(timer, ndecq, reps, ns, check=same(lambda i: ndecq(last), dout)),
+        nbytes=n * 2 * (16 + 4.75), units_per_launch=n, unit="keys", buffer_sets=ns,
+        note="graph replay; s1 read as 4-bit codes with per-block pairs")
+    del kvd
+
+    # streaming NSN-VQ cache: 65408 packed tokens in flush groups of 128 (each
+    # with its own means) plus a 100-token fp16 window, 8 KV heads, 32 query
+    # heads; and the flush of one 128-token group of the window
+    Gs, T_cap, T_s, R_cap, R_s = 128, 65536, 65408, 128, 100
+    n = H * T_s
+    ns = rng_sets(n * 2 * (16 + 8))
+    kvs = [(dv(synth.random_nsn_codes(80 + 2 * i, (1, H, T_cap), n_groups=T_cap // Gs)),
+            dv(synth.random_nsn_codes(81 + 2 * i, (1, H, T_cap), n_groups=T_cap // Gs))) for i in range(ns)]
+    wins = [(torch.from_numpy(synth.random_tensor(84 + 2 * i, (1, H, R_cap, D))).to(dev),
+             torch.from_numpy(synth.random_tensor(85 + 2 * i, (1, H, R_cap, D))).to(dev)) for i in range(ns)]
+    wss = ctx.nsn_stream_ws(1, Hq, T_cap)
+    wsf = torch.empty(int(kvq.lib().kvq_nsn_flush_ws_bytes(ctx.handle, 1, Gs)), dtype=torch.uint8, device=dev)
+
+    def nsdec(i):
+        k, v = kvs[i % ns]
+        kt, vt = wins[i % ns]
+        ctx.nsn_attn_decode_stream(qn, k, v, T_s, Gs, kt, vt, R_s, ws=wss, out=dout)
+
+    def nsflush(i):
+        k, v = kvs[i % ns]
+        kt, vt = wins[i % ns]
+        ctx.nsn_flush(kt, vt, Gs, k, v, T_s, ws=wsf)
+    last = ns - 1
+    out["nsn_attn_decode_stream_8x65408_g4"] = row(
+        *run_graph(timer, nsdec, reps, ns, check=same(lambda i: nsdec(last), dout)),
+        nbytes=n * 2 * (16 + 8) + H * (T_s // Gs) * 2 * D * 4 + H * R_s * 2 * 2 * D, units_per_launch=n + H * R_s,
+        unit="keys", buffer_sets=ns, note="graph replay; per-group means; three launches (window, splits, merge)")
+    out["nsn_flush_group128"] = row(*run_graph(timer, nsflush, reps, ns), nbytes=2 * H * Gs * (2 * D + 24),
+                                    units_per_launch=2 * H * Gs, unit="vectors", buffer_sets=ns,
+                                    note="graph replay; K and V, three launches each; latency-bound (2048 vectors)")
+    del kvs, wins, ctx
 
     # streaming cache: decode over 32704 packed tokens (of 32768 slots) plus a
     # 64-token fp16 window, and the flush of a 64-token window (b = 3, 8 KV
