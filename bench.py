@@ -73,18 +73,23 @@ def nsn_bytes(n_vec):
 
 
 def source_sha(path):
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+    """sha256 of a source's code: comments and blank lines removed, so that a
+    record stays valid across edits of comments only."""
+    txt = open(path).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    lines = [re.sub(r"//.*$", "", ln).rstrip() for ln in txt.splitlines()]
+    return hashlib.sha256("\n".join(ln for ln in lines if ln.strip()).encode()).hexdigest()
 
 
 def read_record(path, key):
     """A value of a committed rocprofv3 record, if the record is current (its
-    source_sha256 is that of the quantize kernel's source)."""
+    code_sha256 is that of the quantize kernel's source code)."""
     try:
         txt = open(path).read()
     except OSError:
         return None
     m = dict(re.findall(r"^- (\w+): `?([^`\n]+)`?$", txt, re.M))
-    if m.get("source_sha256") != source_sha(QUANT_SRC):
+    if m.get("code_sha256") != source_sha(QUANT_SRC):
         return None
     try:
         return float(m[key])

@@ -4,18 +4,19 @@
 // Estagio 1).
 //
 // Mapping on gfx950: a wave quantises a tile of 32 consecutive vectors of one
-// (batch, KV head) with two lanes per vector: lane 2v + h holds coordinates
-// [64 h, 64 h + 64) of vector v, so a wave needs about 100 VGPRs and four
-// waves share each SIMD.  The tile (8 KiB of fp16) is copied from HBM straight
-// into LDS (each copy instruction reads one contiguous KiB) and read back as
-// half rows.  Six of the seven butterfly stages of the transform run inside
-// the lane; the stage that pairs coordinate i with i + 64 is one DPP lane swap
-// fused into an FMA.  The random signs D of the head travel with the tile and
-// are applied as an XOR on the fp16 sign bits; the norm is a chain of packed
-// fp16 dot products with fp32 accumulation, completed across the lane pair.
-// Instead of dividing the coordinates by the norm, the rotated coordinates of
-// x itself are compared with the thresholds scaled by ||x|| (same decisions up
-// to fp32 rounding, no per-coordinate multiply).
+// (batch, KV head) with two lanes per vector: after the transform lane v + 32 h
+// holds coordinates [64 h, 64 h + 64) of vector v, so a wave needs about 100
+// VGPRs and four waves share each SIMD.  The tile (8 KiB of fp16) is copied
+// from HBM straight into LDS (each copy instruction reads one contiguous KiB)
+// and read back in the operand layout of the matrix cores: the rotation of
+// the tile is one exact 128 x 128 x 32 product of the +-1 Hadamard matrix
+// with the fp16 inputs, summed in fp32.  The random signs D of the head
+// travel with the tile and are applied as an XOR on the fp16 sign bits; the
+// norm is a chain of packed fp16 dot products with fp32 accumulation,
+// completed across the lane pair.  Instead of dividing the coordinates by
+// the norm, the rotated coordinates of x itself are compared with the
+// thresholds scaled by ||x|| (same decisions up to fp32 rounding, no
+// per-coordinate multiply).
 #include "kvq_internal.h"
 
 #include <type_traits>
@@ -477,19 +478,9 @@ __global__ __launch_bounds__(kWavesQ * 64) __attribute__((amdgpu_waves_per_eu(4,
 // rotated space r = (y/rho - c[idx]) / sqrt(d), its norm gamma = ||r|| and
 // the 128 sign bits [(S r)_j >= 0] of its Gaussian projection.  Only the signs
 // are stored, and they do not depend on the positive factor 1/sqrt(d), so the
-// kernel projects e = y/rho - c[idx].
-//
-// The projection is a dense 64 x 128 x 128 contraction per tile and runs on
-// the matrix cores (v_mfma_f32_16x16x32_f16).  The sign decisions need the
-// product to about 1e-6 of ||e||, so e is split into fp16 hi + lo parts and
-// accumulated in fp32 over two passes (a third pass adds e_hi * S_lo when S
-// is not exactly representable in fp16).  e of the 64 keys is staged in LDS
-// as fp16 hi and lo rows (16-byte chunks XOR-swizzled by row so that the
-// operand reads are conflict-free) and read back in the operand layout: lane
-// l holds row l%16, k = 8 (l/16) .. +7.  The
-// 16 x 16 result blocks (lane l: rows 4 (l/16) .. +3, column l%16) are turned
-// into sign bits with wave ballots; each key's 16-bit chunks are gathered on
-// the scalar unit and written into its own lane with v_writelane.
+// kernel projects e = y/rho - c[idx].  The projection is a dense contraction
+// per tile and runs on the matrix cores with e split exactly into fp16 hi +
+// lo parts (details at k_quantize_qjl).
 // ---------------------------------------------------------------------------
 typedef float f4_t __attribute__((ext_vector_type(4)));
 
@@ -674,10 +665,11 @@ __device__ __forceinline__ void encode32(float *y, const float *P, const float *
 
 // Quantise with the 1-bit QJL residual, one workgroup of 12 waves per CU
 // (three per SIMD), tiles of 32 keys claimed as in k_quantize.
-//  - MSE part as in k_quantize, except that the stride-64 butterfly pairs
-//    lanes l and l ^ 32: one gfx950 half swap of registers (i, i + 32) and an
-//    add and a subtract give coordinates i, i + 64 (lanes 0-31) and 32 + i,
-//    96 + i (lanes 32-63).  So register r of half h holds coordinate
+//  - MSE part: the rotation is an in-register Walsh-Hadamard butterfly
+//    network (six stages inside the lane; the lane pair of a key holds its
+//    two halves), whose stride-64 stage pairs lanes l and l ^ 32: one gfx950
+//    half swap of registers (i, i + 32) and an add and a subtract give
+//    coordinates i, i + 64 (lanes 0-31) and 32 + i, 96 + i (lanes 32-63).  So register r of half h holds coordinate
 //    C(h, r) = 32 h + r for r < 32 and 64 + 32 h + (r - 32) for r >= 32, and
 //    each half packs two runs of 32 coordinates.
 //  - e = y / rho - c[idx] per coordinate (the factor 1/sqrt(d) of r does not
