@@ -26,11 +26,13 @@ def test_algorithmic_bytes():
 def test_traffic_record_tracks_the_kernel_source(tmp_path, monkeypatch):
     rec = tmp_path / "rec.md"
     src = tmp_path / "k.hip"
-    src.write_text("kernel v1")
+    src.write_text("// the kernel\nint kernel_v1;\n")
     sha = bench.source_sha(str(src))
-    rec.write_text("- source_sha256: `%s`\n- traffic_bytes_per_launch: `123`\n" % sha)
+    rec.write_text("- code_sha256: `%s`\n- traffic_bytes_per_launch: `123`\n" % sha)
     monkeypatch.setattr(bench, "TRAFFIC_RECORD", str(rec))
     monkeypatch.setattr(bench, "QUANT_SRC", str(src))
     assert bench.read_traffic() == 123.0
-    src.write_text("kernel v2")  # the kernel changed since the counters were taken
+    src.write_text("// the kernel, described anew\n\nint kernel_v1;  /* same code */\n")
+    assert bench.read_traffic() == 123.0  # comments and blank lines do not count
+    src.write_text("// the kernel\nint kernel_v2;\n")  # the code changed since the counters were taken
     assert bench.read_traffic() is None
