@@ -99,6 +99,14 @@ def _setup(L):
     L.kvqo_kmeans.argtypes = [i64, C.c_int, C.c_int, _D, _I64, C.c_int, _D, _D]
     L.kvqo_kmeans.restype = C.c_int
     L.kvqo_dq4.argtypes = [i64, _D, C.c_double, _U8, _D, _D, _U8]
+    L.kvqo_nsn_front.argtypes = [C.c_int, i64, i64, _D, _D, _D, _D, _D, _D]
+    L.kvqo_gskm.argtypes = [i64, C.c_int, C.c_int, _D, _I64, C.c_int, _D, _D]
+    L.kvqo_lloyd_1d.argtypes = [i64, _D, C.c_int, C.c_int, _D]
+    L.kvqo_gsrq_encode.argtypes = [i64, C.c_int, C.c_int, C.c_int, _D, _D, _D, _D, _D, C.c_double, _U8, _D, _U8]
+    L.kvqo_gsrq_logits.argtypes = [C.c_int, C.c_int, C.c_int, i64, i64, i64, i64, _D, _U8, _D, _D, _D, _D, _D, _D,
+                                   _D, _D]
+    L.kvqo_gsrq_attention.argtypes = [C.c_int, C.c_int, i64, i64, i64, i64, _D, _U8, _D, _D, _D, _U8, _D, _D, _D,
+                                      _D, _D, _D, _D, C.c_double, _D]
     L.kvqo_cosine_refine.argtypes = [i64, C.c_int, C.c_int, _D, _D, C.c_int, _D]
     L.kvqo_cosine_refine.restype = C.c_int
 
@@ -643,3 +651,128 @@ def cosine_refine(samples, codebook, passes: int = 10):
     it = lib().kvqo_cosine_refine(n, dim, cb.shape[0], _p(s, _D), _p(cb, _D), passes, _p(mc, _D))
     return cb, mc[:it]
 
+
+# ---------------------------------------------------------------- GSRQ
+GSRQ_M = 32  # sub-vector dimension of the GSRQ reading (4 sub-vectors per 128-dim vector)
+
+
+def nsn_front(x, o_given=None):
+    """NSN front end of x [H,T,d] -> dict(s1, s2 [H,T], o [H,d], z [H,T,d])."""
+    x = _f64(x)
+    H, T, d = x.shape
+    s1, s2 = np.zeros((H, T)), np.zeros((H, T))
+    o, z = np.zeros((H, d)), np.zeros((H, T, d))
+    og = None if o_given is None else _f64(o_given)
+    _chk(lib().kvqo_nsn_front(d, H, T, _p(x, _D), _p(og, _D), _p(s1, _D), _p(s2, _D), _p(o, _D), _p(z, _D)))
+    return dict(s1=s1, s2=s2, o=o, z=z)
+
+
+def gskm(samples, init_idx, passes: int = 20):
+    """Gain-shape k-means: (unit shapes [K, m], mean best projection per pass)."""
+    x = _f64(samples)
+    n, m = x.shape
+    init_idx = np.ascontiguousarray(init_idx, dtype=np.int64)
+    K = init_idx.shape[0]
+    shapes = np.zeros((K, m))
+    obj = np.zeros(passes)
+    it = lib().kvqo_gskm(n, m, K, _p(x, _D), _p(init_idx, _I64), passes, _p(shapes, _D), _p(obj, _D))
+    return shapes, obj[:it]
+
+
+def lloyd_1d(values, L: int, passes: int = 50):
+    v = _f64(values).ravel()
+    levels = np.zeros(L)
+    _chk(lib().kvqo_lloyd_1d(v.shape[0], _p(v, _D), L, passes, _p(levels, _D)))
+    return levels
+
+
+def gsrq_train(samples, inits, L: int = 16, passes: int = 20):
+    """Two GSRQ stages trained on samples [n, m]: per stage GSKM shapes (from
+    the initial sample indices inits[k], K of them), then the gain levels from
+    the best projections, then the residuals feed the next stage."""
+    x = _f64(samples)
+    out = {}
+    r = x.copy()
+    for k in (1, 2):
+        S, obj = gskm(r, inits[k - 1], passes)
+        p = r @ S.T
+        j = np.argmax(p, axis=1)
+        G = lloyd_1d(p[np.arange(r.shape[0]), j], L)
+        codes, zhat, _ = gsrq_encode_stage_only(r, S, G)
+        r = r - zhat
+        out["S%d" % k], out["G%d" % k], out["objective%d" % k] = S, G, obj
+    return out
+
+
+def gsrq_encode_stage_only(z, S, G):
+    """One stage (the second with zero gains) -> (codes, reproductions, flags)."""
+    zero = np.zeros_like(G)
+    return gsrq_encode(z, dict(S1=S, G1=G, S2=S, G2=zero))
+
+
+def gsrq_encode(z, tab, band: float = BAND):
+    """Sub-vectors z [n, m] -> (codes [n, 3] = (j1, j2, c1 | c2 << 4),
+    reproductions [n, m], flags [n])."""
+    z = _f64(z)
+    n, m = z.shape
+    S1, G1, S2, G2 = (_f64(tab[k]) for k in ("S1", "G1", "S2", "G2"))
+    codes = np.zeros((n, 3), np.uint8)
+    zhat = np.zeros((n, m))
+    fl = np.zeros(n, np.uint8)
+    _chk(lib().kvqo_gsrq_encode(n, m, S1.shape[0], G1.shape[0], _p(z, _D), _p(S1, _D), _p(G1, _D), _p(S2, _D),
+                                _p(G2, _D), band, _p(codes, _U8), _p(zhat, _D), _p(fl, _U8)))
+    return codes, zhat, fl
+
+
+def gsrq_records(codes, P: int):
+    """Per-sub-vector codes [..., P, 3] -> records [..., 3P]: the P stage-1
+    shapes, the P stage-2 shapes, the P gain bytes."""
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    return np.concatenate([c[..., 0], c[..., 1], c[..., 2]], axis=-1)
+
+
+def gsrq_vq(x, tab, band: float = BAND, o_given=None):
+    """GSRQ of x [H,T,d] on the NSN front end -> dict(codes [H,T,3P] records,
+    s1, s2 [H,T], o [H,d], z, zhat [H,T,d], flags [H,T,P])."""
+    f = nsn_front(x, o_given)
+    H, T, d = f["z"].shape
+    m = _f64(tab["S1"]).shape[1]
+    P = d // m
+    codes, zhat, fl = gsrq_encode(f["z"].reshape(-1, m), tab, band)
+    f.update(codes=gsrq_records(codes.reshape(H, T, P, 3), P), zhat=zhat.reshape(H, T, d), flags=fl.reshape(H, T, P))
+    return f
+
+
+def _gsrq_tabs(tab):
+    return [_f64(tab[k]) for k in ("S1", "G1", "S2", "G2")]
+
+
+def gsrq_logits(q, codes, s1, s2, o, tab, route: int = 2):
+    q = _f64(q)
+    B, Hq, d = q.shape
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    _, Hkv, T, _ = codes.shape
+    S1, G1, S2, G2 = _gsrq_tabs(tab)
+    out = np.zeros((B, Hq, T))
+    _chk(lib().kvqo_gsrq_logits(route, d, S1.shape[1], B, Hq, Hkv, T, _p(q, _D), _p(codes, _U8), _p(_f64(s1), _D),
+                                _p(_f64(s2), _D), _p(_f64(o), _D), _p(S1, _D), _p(G1, _D), _p(S2, _D), _p(G2, _D),
+                                _p(out, _D)))
+    return out
+
+
+def gsrq_attention(q, kc, ks1, ks2, ko, vc, vs1, vs2, vo, tab, sm_scale: float | None = None):
+    q = _f64(q)
+    B, Hq, d = q.shape
+    kc = np.ascontiguousarray(kc, dtype=np.uint8)
+    vc = np.ascontiguousarray(vc, dtype=np.uint8)
+    _, Hkv, T, _ = kc.shape
+    S1, G1, S2, G2 = _gsrq_tabs(tab)
+    if sm_scale is None:
+        sm_scale = 1.0 / np.sqrt(d)
+    out = np.zeros((B, Hq, d))
+    a = [_f64(t) for t in (ks1, ks2, ko, vs1, vs2, vo)]
+    _chk(lib().kvqo_gsrq_attention(d, S1.shape[1], B, Hq, Hkv, T, _p(q, _D), _p(kc, _U8), _p(a[0], _D),
+                                   _p(a[1], _D), _p(a[2], _D), _p(vc, _U8), _p(a[3], _D), _p(a[4], _D),
+                                   _p(a[5], _D), _p(S1, _D), _p(G1, _D), _p(S2, _D), _p(G2, _D), float(sm_scale),
+                                   _p(out, _D)))
+    return out

@@ -1359,3 +1359,316 @@ ORC_API int kvqo_cosine_refine(int64_t n, int dim, int K, const double *samples,
     return it;
 }
 
+/* ------------------------------------------------------------------------ */
+/* NSN front end alone (NSNQuant, Metodologia 1-2): the steps of kvqo_nsn_vq */
+/* up to the rotated vector z, without the codebook search.  x [H, T, d];    */
+/* s1, s2 [H, T]; o [H, d] (the mean of the T tokens, or o_given); z [H,T,d]. */
+/* ------------------------------------------------------------------------ */
+ORC_API int kvqo_nsn_front(int d, int64_t H, int64_t T, const double *x, const double *o_given, double *s1,
+                           double *s2, double *o, double *z)
+{
+    if (T <= 0) return -1;
+    const double sd = sqrt((double)d);
+    double *a = (double *)malloc(sizeof(double) * T * d);
+    for (int64_t h = 0; h < H; ++h) {
+        const double *xh = x + h * T * d;
+        double *oh = o + h * d;
+        for (int i = 0; i < d; ++i) oh[i] = 0.0;
+        for (int64_t t = 0; t < T; ++t) {
+            double ss = 0.0;
+            for (int i = 0; i < d; ++i) ss += xh[t * d + i] * xh[t * d + i];
+            const double nx = sqrt(ss);
+            s1[h * T + t] = nx / sd;
+            for (int i = 0; i < d; ++i) a[t * d + i] = nx > 0.0 ? sd * xh[t * d + i] / nx : 0.0;
+        }
+        for (int64_t t = 0; t < T; ++t)
+            for (int i = 0; i < d; ++i) oh[i] += a[t * d + i];
+        for (int i = 0; i < d; ++i) oh[i] = o_given ? o_given[h * d + i] : oh[i] / (double)T;
+        for (int64_t t = 0; t < T; ++t) {
+            double *zt = z + (h * T + t) * d;
+            double ss = 0.0;
+            for (int i = 0; i < d; ++i) {
+                zt[i] = a[t * d + i] - oh[i];
+                ss += zt[i] * zt[i];
+            }
+            const double nb = sqrt(ss);
+            s2[h * T + t] = nb / sd;
+            for (int i = 0; i < d; ++i) zt[i] = nb > 0.0 ? zt[i] / (nb / sd) : 0.0;
+            kvqo_fwht(zt, d);
+            for (int i = 0; i < d; ++i) zt[i] /= sd;
+        }
+    }
+    free(a);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Gain-shape residual quantisation ("GSRQ: Quantitzacio Residual de Forma-  */
+/* Guanys per a Cau KV de Menys d'1 Bit", q2bstudio): gain-shape k-means     */
+/* (GSKM) keeps the norm (gain) of the reproduction apart from its direction */
+/* (shape), so that the averaging of k-means does not shrink it; GSKM stages */
+/* inside a residual quantisation pipeline give GSRQ.  The page gives no     */
+/* dimensions, stage count or training recipe; the reading here:             */
+/*  - GSKM on n samples of dimension m: K unit shapes, initialised from K     */
+/*    given samples (normalised); a pass assigns every sample to the shape of */
+/*    largest projection <x, s_j> (lowest j on ties), then moves each shape   */
+/*    to the normalised sum of its samples (the unit vector with the largest  */
+/*    summed projection over the cell); a shape with no sample or a zero sum  */
+/*    is kept.  objective[it] = mean best projection at pass it's assignment. */
+/*  - gain levels: Lloyd's algorithm in one dimension on the best            */
+/*    projections (levels = cell means, thresholds = midpoints), started at   */
+/*    the (i + 1/2) / L quantiles.                                            */
+/*  - encoding of a sub-vector, stage k = 1, 2 on the running residual r      */
+/*    (r = z first): j = argmax_j <r, S_k[j]> (lowest j on ties),             */
+/*    p = <r, S_k[j]>, c = #{l : t_k[l] < p} (t_k the midpoints of the sorted */
+/*    levels G_k), r <- r - G_k[c] S_k[j]; the reproduction is z - r.        */
+/* ------------------------------------------------------------------------ */
+
+ORC_API int kvqo_gskm(int64_t n, int m, int K, const double *x, const int64_t *init, int passes, double *shapes,
+                      double *objective)
+{
+    int32_t *asg = (int32_t *)malloc(sizeof(int32_t) * n);
+    double *sum = (double *)malloc(sizeof(double) * K * m);
+    for (int j = 0; j < K; ++j) {
+        double ss = 0.0;
+        for (int k = 0; k < m; ++k) ss += x[init[j] * m + k] * x[init[j] * m + k];
+        const double inv = ss > 0.0 ? 1.0 / sqrt(ss) : 0.0;
+        for (int k = 0; k < m; ++k) shapes[j * m + k] = x[init[j] * m + k] * inv;
+    }
+    int it = 0;
+    for (; it < passes; ++it) {
+        double tot = 0.0;
+        for (int64_t i = 0; i < n; ++i) {
+            int best = 0;
+            double bp = -INFINITY;
+            for (int j = 0; j < K; ++j) {
+                double p = 0.0;
+                for (int k = 0; k < m; ++k) p += x[i * m + k] * shapes[j * m + k];
+                if (p > bp) { bp = p; best = j; }
+            }
+            asg[i] = best;
+            tot += bp;
+        }
+        if (objective) objective[it] = tot / (double)n;
+        memset(sum, 0, sizeof(double) * K * m);
+        for (int64_t i = 0; i < n; ++i)
+            for (int k = 0; k < m; ++k) sum[asg[i] * m + k] += x[i * m + k];
+        for (int j = 0; j < K; ++j) {
+            double ss = 0.0;
+            for (int k = 0; k < m; ++k) ss += sum[j * m + k] * sum[j * m + k];
+            if (ss <= 0.0) continue;
+            const double inv = 1.0 / sqrt(ss);
+            for (int k = 0; k < m; ++k) shapes[j * m + k] = sum[j * m + k] * inv;
+        }
+    }
+    free(asg);
+    free(sum);
+    return it;
+}
+
+static int cmp_double(const void *a, const void *b)
+{
+    const double x = *(const double *)a, y = *(const double *)b;
+    return x < y ? -1 : x > y ? 1 : 0;
+}
+
+/* Returns 0 (passes run as given). */
+ORC_API int kvqo_lloyd_1d(int64_t n, const double *v, int L, int passes, double *levels)
+{
+    if (n <= 0 || L <= 0) return -1;
+    double *sv = (double *)malloc(sizeof(double) * n);
+    double *sum = (double *)malloc(sizeof(double) * L);
+    int64_t *cnt = (int64_t *)malloc(sizeof(int64_t) * L);
+    memcpy(sv, v, sizeof(double) * n);
+    qsort(sv, (size_t)n, sizeof(double), cmp_double);
+    for (int l = 0; l < L; ++l) {
+        int64_t i = (int64_t)(((double)l + 0.5) / L * (double)n);
+        if (i >= n) i = n - 1;
+        levels[l] = sv[i];
+    }
+    int it = 0;
+    for (; it < passes; ++it) {
+        memset(sum, 0, sizeof(double) * L);
+        memset(cnt, 0, sizeof(int64_t) * L);
+        for (int64_t i = 0; i < n; ++i) {
+            int c = 0;
+            while (c < L - 1 && 0.5 * (levels[c] + levels[c + 1]) < sv[i]) ++c;
+            sum[c] += sv[i];
+            ++cnt[c];
+        }
+        for (int l = 0; l < L; ++l)
+            if (cnt[l] > 0) levels[l] = sum[l] / (double)cnt[l];
+    }
+    free(sv);
+    free(sum);
+    free(cnt);
+    return 0;
+}
+
+/* One stage on residual r [m]: the shape index, the gain index and flags   */
+/* (bit 0: best projection within band of the runner-up; bit 1: projection */
+/* within band of a gain threshold); r is updated.                          */
+static void gsrq_stage(int m, int K, int L, double *r, const double *S, const double *G, double band, int *j_out,
+                       int *c_out, int *flags)
+{
+    int best = 0;
+    double bp = -INFINITY, second = -INFINITY;
+    for (int j = 0; j < K; ++j) {
+        double p = 0.0;
+        for (int k = 0; k < m; ++k) p += r[k] * S[j * m + k];
+        if (p > bp) { second = bp; bp = p; best = j; }
+        else if (p > second) second = p;
+    }
+    int c = 0, f = 0;
+    for (int l = 0; l + 1 < L; ++l) {
+        const double t = 0.5 * (G[l] + G[l + 1]);
+        if (t < bp) ++c;
+        if (fabs(bp - t) < band) f |= 2;
+    }
+    if (bp - second < band) f |= 1;
+    for (int k = 0; k < m; ++k) r[k] -= G[c] * S[best * m + k];
+    *j_out = best;
+    *c_out = c;
+    *flags = f;
+}
+
+/* n sub-vectors z [n][m] -> codes [n][3] = (j1, j2, c1 | c2 << 4), the       */
+/* reproductions zhat [n][m] and flags [n] (stage-1 bits 0-1, stage-2 2-3).  */
+/* K <= 256 shapes and L <= 16 sorted levels per stage.                      */
+ORC_API int kvqo_gsrq_encode(int64_t n, int m, int K, int L, const double *z, const double *S1, const double *G1,
+                             const double *S2, const double *G2, double band, uint8_t *codes, double *zhat,
+                             uint8_t *flags)
+{
+    if (K > 256 || L > 16 || m > 256) return -1;
+    double r[256];
+    for (int64_t i = 0; i < n; ++i) {
+        for (int k = 0; k < m; ++k) r[k] = z[i * m + k];
+        int j1, c1, f1, j2, c2, f2;
+        gsrq_stage(m, K, L, r, S1, G1, band, &j1, &c1, &f1);
+        gsrq_stage(m, K, L, r, S2, G2, band, &j2, &c2, &f2);
+        codes[i * 3] = (uint8_t)j1;
+        codes[i * 3 + 1] = (uint8_t)j2;
+        codes[i * 3 + 2] = (uint8_t)(c1 | (c2 << 4));
+        if (zhat)
+            for (int k = 0; k < m; ++k) zhat[i * m + k] = z[i * m + k] - r[k];
+        if (flags) flags[i] = (uint8_t)(f1 | (f2 << 2));
+    }
+    return 0;
+}
+
+/* Reproduction of a whole vector from its record: P = d / m sub-vectors,    */
+/* record bytes [j1 of each sub-vector][j2 of each][c1 | c2 << 4 of each].    */
+static void gsrq_entries(int d, int m, const uint8_t *rec, const double *S1, const double *G1, const double *S2,
+                         const double *G2, double *zq)
+{
+    const int P = d / m;
+    for (int s = 0; s < P; ++s) {
+        const int j1 = rec[s], j2 = rec[P + s], c1 = rec[2 * P + s] & 15, c2 = rec[2 * P + s] >> 4;
+        for (int k = 0; k < m; ++k) zq[s * m + k] = G1[c1] * S1[j1 * m + k] + G2[c2] * S2[j2 * m + k];
+    }
+}
+
+/* Logits and decode attention over GSRQ records with the NSN byproducts      */
+/* (x_hat = s1 (s2 H zq / sqrt(d) + o), as for NSN-VQ).  route 1: reconstruct */
+/* then dot; route 2: q' = H q / sqrt(d) and                                  */
+/*   logit = s1 (s2 sum_s (G1[c1] <q'_s, S1[j1]> + G2[c2] <q'_s, S2[j2]>) + <q, o>). */
+ORC_API int kvqo_gsrq_logits(int route, int d, int m, int64_t B, int64_t Hq, int64_t Hkv, int64_t T,
+                             const double *q, const uint8_t *codes, const double *s1, const double *s2,
+                             const double *o, const double *S1, const double *G1, const double *S2,
+                             const double *G2, double *logits)
+{
+    if (Hkv <= 0 || Hq % Hkv || d % m) return -1;
+    const int64_t G = Hq / Hkv;
+    const int P = d / m, rb = 3 * P;
+    double *zq = (double *)malloc(sizeof(double) * d);
+    double *xh = (double *)malloc(sizeof(double) * d);
+    double *qr = (double *)malloc(sizeof(double) * d);
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t h = 0; h < Hq; ++h) {
+            const int64_t g = h / G;
+            const double *qh = q + (b * Hq + h) * d;
+            const double *og = o + (b * Hkv + g) * d;
+            double qo = 0.0;
+            for (int i = 0; i < d; ++i) qo += qh[i] * og[i];
+            for (int i = 0; i < d; ++i) qr[i] = qh[i];
+            kvqo_fwht(qr, d);
+            for (int i = 0; i < d; ++i) qr[i] /= sqrt((double)d);
+            for (int64_t t = 0; t < T; ++t) {
+                const int64_t v = (b * Hkv + g) * T + t;
+                const uint8_t *rec = codes + v * rb;
+                double acc = 0.0;
+                if (route == 1) {
+                    gsrq_entries(d, m, rec, S1, G1, S2, G2, zq);
+                    kvqo_nsn_reconstruct(d, zq, s1[v], s2[v], og, xh);
+                    for (int i = 0; i < d; ++i) acc += qh[i] * xh[i];
+                } else {
+                    for (int s = 0; s < P; ++s) {
+                        const int j1 = rec[s], j2 = rec[P + s], c1 = rec[2 * P + s] & 15, c2 = rec[2 * P + s] >> 4;
+                        double a1 = 0.0, a2 = 0.0;
+                        for (int k = 0; k < m; ++k) {
+                            a1 += qr[s * m + k] * S1[j1 * m + k];
+                            a2 += qr[s * m + k] * S2[j2 * m + k];
+                        }
+                        acc += G1[c1] * a1 + G2[c2] * a2;
+                    }
+                    acc = s1[v] * (s2[v] * acc + qo);
+                }
+                logits[(b * Hq + h) * T + t] = acc;
+            }
+        }
+    free(zq);
+    free(xh);
+    free(qr);
+    return 0;
+}
+
+ORC_API int kvqo_gsrq_attention(int d, int m, int64_t B, int64_t Hq, int64_t Hkv, int64_t T, const double *q,
+                                const uint8_t *kc, const double *ks1, const double *ks2, const double *ko,
+                                const uint8_t *vc, const double *vs1, const double *vs2, const double *vo,
+                                const double *S1, const double *G1, const double *S2, const double *G2,
+                                double sm_scale, double *out)
+{
+    if (Hkv <= 0 || Hq % Hkv || T <= 0 || d % m) return -1;
+    const int64_t G = Hq / Hkv;
+    const int rb = 3 * (d / m);
+    double *K = (double *)malloc(sizeof(double) * T * d);
+    double *V = (double *)malloc(sizeof(double) * T * d);
+    double *zq = (double *)malloc(sizeof(double) * d);
+    double *w = (double *)malloc(sizeof(double) * T);
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t g = 0; g < Hkv; ++g) {
+            const int64_t bg = b * Hkv + g;
+            for (int64_t t = 0; t < T; ++t) {
+                const int64_t v = bg * T + t;
+                gsrq_entries(d, m, kc + v * rb, S1, G1, S2, G2, zq);
+                kvqo_nsn_reconstruct(d, zq, ks1[v], ks2[v], ko + bg * d, K + t * d);
+                gsrq_entries(d, m, vc + v * rb, S1, G1, S2, G2, zq);
+                kvqo_nsn_reconstruct(d, zq, vs1[v], vs2[v], vo + bg * d, V + t * d);
+            }
+            for (int64_t hh = 0; hh < G; ++hh) {
+                const double *qh = q + (b * Hq + g * G + hh) * d;
+                double mx = -INFINITY;
+                for (int64_t t = 0; t < T; ++t) {
+                    double a = 0.0;
+                    for (int i = 0; i < d; ++i) a += qh[i] * K[t * d + i];
+                    w[t] = sm_scale * a;
+                    if (w[t] > mx) mx = w[t];
+                }
+                double l = 0.0;
+                for (int64_t t = 0; t < T; ++t) {
+                    w[t] = exp(w[t] - mx);
+                    l += w[t];
+                }
+                double *oh = out + (b * Hq + g * G + hh) * d;
+                for (int i = 0; i < d; ++i) oh[i] = 0.0;
+                for (int64_t t = 0; t < T; ++t)
+                    for (int i = 0; i < d; ++i) oh[i] += w[t] * V[t * d + i];
+                for (int i = 0; i < d; ++i) oh[i] /= l;
+            }
+        }
+    free(K);
+    free(V);
+    free(zq);
+    free(w);
+    return 0;
+}
