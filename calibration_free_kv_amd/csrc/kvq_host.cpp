@@ -179,6 +179,7 @@ void free_ctx(kvq_ctx *c)
     (void)hipFree(c->d_Q16);
     (void)hipFree(c->d_vq16);
     (void)hipFree(c->d_vqbias);
+    (void)hipFree(c->d_gsrq);
     std::free(c->h_signs);
     delete c;
 }
@@ -206,9 +207,27 @@ kvq_status upload(T **dst, const T *src, size_t n)
 
 kvq_status launch_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_E_DEVICE; }
 
+bool mse_mode(int m) { return m == KVQ_MODE_MSE || m == KVQ_MODE_MSE_QJL; }
+
 // The codebook's n values in 4 bits ([NSN] Metodologia sec. 3, double
 // quantisation): one block, lo = min, step = (max - lo) / 15, each value
 // replaced by lo + code step with code the nearest level; decided in double.
+// GSRQ tables: 2 x (256 x 32 shape values, 16 strictly increasing levels),
+// all finite.
+constexpr size_t kGsrqShape = (size_t)kvq::kVqK * 32;
+bool gsrq_tables_ok(const float *t)
+{
+    if (!t) return false;
+    for (int st = 0; st < 2; ++st) {
+        const float *S = t + st * (kGsrqShape + 16), *G = S + kGsrqShape;
+        for (size_t i = 0; i < kGsrqShape; ++i)
+            if (!std::isfinite(S[i])) return false;
+        for (int l = 0; l < 16; ++l)
+            if (!std::isfinite(G[l]) || (l > 0 && !(G[l] > G[l - 1]))) return false;
+    }
+    return true;
+}
+
 void dq4_codebook(float *v, size_t n)
 {
     double lo = v[0], hi = v[0];
@@ -256,9 +275,9 @@ kvq_status kvq_create(const kvq_config *cfg, kvq_ctx **out)
     if (!cfg) return KVQ_E_INVAL;
     if (cfg->d != kvq::kD || cfg->n_kv_heads < 1 || cfg->n_kv_heads > 4096) return KVQ_E_INVAL;
     const int mode = cfg->mode;
-    if (mode != KVQ_MODE_MSE && mode != KVQ_MODE_MSE_QJL && mode != KVQ_MODE_NSN_VQ) return KVQ_E_INVAL;
+    if (!mse_mode(mode) && mode != KVQ_MODE_NSN_VQ && mode != KVQ_MODE_GSRQ) return KVQ_E_INVAL;
     const int H = cfg->n_kv_heads;
-    if (mode != KVQ_MODE_NSN_VQ) {
+    if (mse_mode(mode)) {
         if (cfg->bits < 1 || cfg->bits > 4) return KVQ_E_INVAL;
         for (int i = 0; i < H * kvq::kD; ++i) {
             if (cfg->signs_k && cfg->signs_k[i] != 1 && cfg->signs_k[i] != -1) return KVQ_E_INVAL;
@@ -267,13 +286,14 @@ kvq_status kvq_create(const kvq_config *cfg, kvq_ctx **out)
     }
     if (mode == KVQ_MODE_MSE_QJL && !cfg->qjl_S) return KVQ_E_INVAL;
     if (mode == KVQ_MODE_NSN_VQ && !cfg->vq_codebook) return KVQ_E_INVAL;
+    if (mode == KVQ_MODE_GSRQ && !gsrq_tables_ok(cfg->gsrq_tables)) return KVQ_E_INVAL;
     if (cfg->codebook != KVQ_CODEBOOK_GAUSS && cfg->codebook != KVQ_CODEBOOK_BETA) return KVQ_E_INVAL;
-    if (cfg->codebook == KVQ_CODEBOOK_BETA && mode == KVQ_MODE_NSN_VQ) return KVQ_E_INVAL;
+    if (cfg->codebook == KVQ_CODEBOOK_BETA && !mse_mode(mode)) return KVQ_E_INVAL;
     if (cfg->rotation != KVQ_ROTATION_HADAMARD && cfg->rotation != KVQ_ROTATION_DENSE) return KVQ_E_INVAL;
     if (cfg->nsn_options & ~(KVQ_NSN_ADAPTIVE_SCALE | KVQ_NSN_DQ_CODEBOOK)) return KVQ_E_INVAL;
     if (cfg->nsn_options && mode != KVQ_MODE_NSN_VQ) return KVQ_E_INVAL;
     if (cfg->rotation == KVQ_ROTATION_DENSE) {
-        if (mode == KVQ_MODE_NSN_VQ) return KVQ_E_UNSUPPORTED;
+        if (!mse_mode(mode)) return KVQ_E_UNSUPPORTED;
         if (!cfg->rot_Q) return KVQ_E_INVAL;
         for (int i = 0; i < kvq::kD * kvq::kD; ++i)
             if (!std::isfinite(cfg->rot_Q[i]) || std::fabs(cfg->rot_Q[i]) > 1.0f) return KVQ_E_INVAL;
@@ -298,7 +318,7 @@ kvq_status kvq_create(const kvq_config *cfg, kvq_ctx **out)
     kvq_ctx *c = new (std::nothrow) kvq_ctx();
     if (!c) return KVQ_E_NOMEM;
     c->d = cfg->d;
-    c->bits = mode == KVQ_MODE_NSN_VQ ? 1 : cfg->bits;
+    c->bits = mse_mode(mode) ? cfg->bits : 1;
     c->mode = mode;
     c->rotation = cfg->rotation;
     c->nsn_options = cfg->nsn_options;
@@ -317,7 +337,7 @@ kvq_status kvq_create(const kvq_config *cfg, kvq_ctx **out)
     }
 
     kvq_status st = KVQ_OK;
-    if (mode != KVQ_MODE_NSN_VQ) {
+    if (mse_mode(mode)) {
         const size_t n = (size_t)H * kvq::kD;
         uint32_t *mask = (uint32_t *)std::calloc(2 * n / 2, sizeof(uint32_t));
         float *sg = (float *)std::malloc(2 * n * sizeof(float));
@@ -396,6 +416,22 @@ kvq_status kvq_create(const kvq_config *cfg, kvq_ctx **out)
         std::free(c16);
         std::free(cbv);
     }
+    if (st == KVQ_OK && mode == KVQ_MODE_GSRQ) {
+        // device layout: shapes [2][256][32], levels [2][16], thresholds [2][15]
+        // (midpoints of adjacent levels, in double, rounded once)
+        const size_t n = 2 * kGsrqShape + 2 * 16 + 2 * 15;
+        float *t = (float *)std::malloc(n * sizeof(float));
+        if (!t) st = KVQ_E_NOMEM;
+        for (int k = 0; st == KVQ_OK && k < 2; ++k) {
+            const float *S = cfg->gsrq_tables + k * (kGsrqShape + 16), *G = S + kGsrqShape;
+            std::memcpy(t + k * kGsrqShape, S, kGsrqShape * sizeof(float));
+            std::memcpy(t + 2 * kGsrqShape + 16 * k, G, 16 * sizeof(float));
+            for (int l = 0; l < 15; ++l)
+                t[2 * kGsrqShape + 32 + 15 * k + l] = (float)(0.5 * ((double)G[l] + (double)G[l + 1]));
+        }
+        if (st == KVQ_OK) st = upload(&c->d_gsrq, t, n);
+        std::free(t);
+    }
     if (st == KVQ_OK && cfg->rotation == KVQ_ROTATION_DENSE) {
         const size_t n = (size_t)kvq::kD * kvq::kD;
         float *qt = (float *)std::malloc(n * sizeof(float));
@@ -458,6 +494,7 @@ kvq_status kvq_codebook(int32_t bits, float *centroids, float *thresholds)
 int64_t kvq_code_bytes_per_vec(const kvq_ctx *ctx)
 {
     if (!ctx) return 0;
+    if (ctx->mode == KVQ_MODE_GSRQ) return kvq::kGsrqRec;
     return ctx->mode == KVQ_MODE_NSN_VQ ? kvq::kD / kvq::kVqSub : 16 * ctx->bits;
 }
 
@@ -465,7 +502,7 @@ kvq_status kvq_quantize(kvq_ctx *ctx, int32_t kind, const void *x_f16, int64_t B
                         int64_t T, uint8_t *codes, float *norms, uint8_t *qjl_signs,
                         float *qjl_gamma, void *stream)
 {
-    if (!ctx || ctx->mode == KVQ_MODE_NSN_VQ) return KVQ_E_INVAL;
+    if (!ctx || !mse_mode(ctx->mode)) return KVQ_E_INVAL;
     if (kind != KVQ_KIND_K && kind != KVQ_KIND_V) return KVQ_E_INVAL;
     if (B < 0 || T < 0 || H_kv != ctx->H) return KVQ_E_INVAL;
     const bool want_qjl = ctx->mode == KVQ_MODE_MSE_QJL && kind == KVQ_KIND_K;
@@ -512,7 +549,7 @@ kvq_status kvq_logits(kvq_ctx *ctx, const void *q_f16, int64_t B, int64_t H_q, i
                       const uint8_t *codes, const float *norms, const uint8_t *qjl_signs,
                       const float *qjl_gamma, float *logits, void *stream)
 {
-    if (!ctx || ctx->mode == KVQ_MODE_NSN_VQ) return KVQ_E_INVAL;
+    if (!ctx || !mse_mode(ctx->mode)) return KVQ_E_INVAL;
     if (B < 0 || T < 0 || H_q < 1 || H_q % ctx->H) return KVQ_E_INVAL;
     if (!logits_group_built(H_q / ctx->H)) return KVQ_E_UNSUPPORTED;
     const bool want_qjl = ctx->mode == KVQ_MODE_MSE_QJL;
@@ -752,6 +789,76 @@ kvq_status kvq_nsn_attn_decode_splits(kvq_ctx *ctx, const void *q_f16, int64_t B
     const kvq::NsnKV kv{k_codes, k_s1, k_s2, k_o, v_codes, v_s1, v_s2, v_o};
     return launch_status(
         kvq::launch_nsn_decode(ctx, q_f16, B, H_q, T, kv, sm_scale, out, ws, ns, (hipStream_t)stream));
+}
+
+size_t kvq_gsrq_ws_bytes(const kvq_ctx *ctx, int64_t H, int64_t T)
+{
+    if (!ctx || H < 1 || T < 1) return 0;
+    return kvq::nsn_ws_bytes(H, T);
+}
+
+kvq_status kvq_gsrq_quantize(kvq_ctx *ctx, const void *x_f16, int64_t H, int64_t T, uint8_t *codes, float *s1,
+                             float *s2, float *o, void *ws, size_t ws_bytes, void *stream)
+{
+    if (!ctx || ctx->mode != KVQ_MODE_GSRQ) return KVQ_E_INVAL;
+    if (H < 1 || T < 1 || T > (int64_t(1) << 31) || H > (int64_t(1) << 20)) return KVQ_E_INVAL;
+    if (H * ((T + 2047) / 2048) > INT32_MAX || H * ((T + 63) / 64) > INT32_MAX) return KVQ_E_INVAL;
+    if (!x_f16 || !codes || !s1 || !s2 || !o || !ws) return KVQ_E_INVAL;
+    if (!aligned(x_f16, 16) || !aligned(codes, 4) || !aligned(s1, 4) || !aligned(s2, 4) || !aligned(o, 16) ||
+        !aligned(ws, 256))
+        return KVQ_E_INVAL;
+    if (ws_bytes < kvq::nsn_ws_bytes(H, T)) return KVQ_E_WORKSPACE;
+    DeviceGuard g(ctx->device);
+    if (!g.ok) return KVQ_E_DEVICE;
+    return launch_status(kvq::launch_gsrq(ctx, x_f16, H, T, codes, s1, s2, o, ws, (hipStream_t)stream));
+}
+
+kvq_status kvq_gsrq_logits(kvq_ctx *ctx, const void *q_f16, int64_t B, int64_t H_q, int64_t T, const uint8_t *codes,
+                           const float *s1, const float *s2, const float *o, float *logits, void *stream)
+{
+    if (!ctx || ctx->mode != KVQ_MODE_GSRQ) return KVQ_E_INVAL;
+    if (B < 0 || T < 0 || !nsn_group_ok(ctx, H_q)) return KVQ_E_INVAL;
+    if (B == 0 || T == 0) return KVQ_OK;
+    if (!q_f16 || !codes || !s1 || !s2 || !o || !logits) return KVQ_E_INVAL;
+    if (!aligned(q_f16, 16) || !aligned(codes, 4) || !aligned(s1, 4) || !aligned(s2, 4) || !aligned(o, 16) ||
+        !aligned(logits, 4))
+        return KVQ_E_INVAL;
+    if (T > (int64_t(1) << 31) || B * ctx->H > 65535) return KVQ_E_INVAL;
+    DeviceGuard g(ctx->device);
+    if (!g.ok) return KVQ_E_DEVICE;
+    return launch_status(
+        kvq::launch_gsrq_logits(ctx, q_f16, B, H_q, T, codes, s1, s2, o, logits, (hipStream_t)stream));
+}
+
+kvq_status kvq_gsrq_attn_decode(kvq_ctx *ctx, const void *q_f16, int64_t B, int64_t H_q, int64_t T,
+                                const uint8_t *k_codes, const float *k_s1, const float *k_s2, const float *k_o,
+                                const uint8_t *v_codes, const float *v_s1, const float *v_s2, const float *v_o,
+                                float sm_scale, float *out, void *ws, size_t ws_bytes, int32_t n_split, void *stream)
+{
+    if (!ctx || ctx->mode != KVQ_MODE_GSRQ) return KVQ_E_INVAL;
+    if (B < 0 || T < 1 || H_q < 1 || H_q % ctx->H) return KVQ_E_INVAL;
+    const int64_t G = H_q / ctx->H;
+    if (G != 1 && G != 2 && G != 4) return KVQ_E_INVAL;
+    if (n_split < 0 || !std::isfinite(sm_scale) || sm_scale < 0.f) return KVQ_E_INVAL;
+    if (B == 0) return KVQ_OK;
+    if (!q_f16 || !k_codes || !k_s1 || !k_s2 || !k_o || !v_codes || !v_s1 || !v_s2 || !v_o || !out || !ws)
+        return KVQ_E_INVAL;
+    if (!aligned(q_f16, 16) || !aligned(k_codes, 4) || !aligned(v_codes, 4) || !aligned(k_s1, 4) ||
+        !aligned(k_s2, 4) || !aligned(v_s1, 4) || !aligned(v_s2, 4) || !aligned(k_o, 16) || !aligned(v_o, 16) ||
+        !aligned(out, 16) || !aligned(ws, 256))
+        return KVQ_E_INVAL;
+    if (T > (int64_t(1) << 31) || B * ctx->H > 65535) return KVQ_E_INVAL;
+    if (ws_bytes < kvq::nsn_decode_ws_bytes(B, H_q, T)) return KVQ_E_WORKSPACE;
+    const int64_t max_split = kvq::decode_max_splits(T);
+    int ns = n_split == 0 ? kvq::nsn_decode_auto_splits(ctx, B, T) : n_split;
+    if (ns > max_split) ns = (int)max_split;
+    if (ns < 1) ns = 1;
+    if (sm_scale == 0.f) sm_scale = 1.0f / std::sqrt((float)kvq::kD);
+    DeviceGuard g(ctx->device);
+    if (!g.ok) return KVQ_E_DEVICE;
+    const kvq::NsnKV kv{k_codes, k_s1, k_s2, k_o, v_codes, v_s1, v_s2, v_o};
+    return launch_status(
+        kvq::launch_gsrq_decode(ctx, q_f16, B, H_q, T, kv, sm_scale, out, ws, ns, (hipStream_t)stream));
 }
 
 size_t kvq_nsn_vq_dq_ws_bytes(const kvq_ctx *ctx, int64_t H, int64_t T)

@@ -47,6 +47,7 @@ struct kvq_ctx {
     _Float16 *d_vq16;     // [2][256][8] fp16 hi and lo parts of the codebook
     bool vq_exact_f16;    // codebook lo == 0
     float *d_vqbias;      // [256] -||C_j||^2 / 2
+    float *d_gsrq;        // GSRQ tables: shapes [2][256][32], levels [2][16], thresholds [2][15]
 };
 
 namespace kvq {
@@ -140,6 +141,16 @@ size_t nsn_dq_ws_bytes(int64_t H, int64_t T);       // + the dequantised means [
 hipError_t launch_nsn_vq_dq(const kvq_ctx *ctx, const void *x, int64_t H, int64_t T, uint8_t *codes, float *s2,
                             const NsnDq &dq, void *ws, hipStream_t s);
 
+// Gain-shape residual quantisation on the NSN front end: codes [H][T][12]
+// (three dwords per token), s1, s2 [H][T], means o [H][128]; ws as the NSN
+// statistics (nsn_ws_bytes).
+constexpr int kGsrqRec = 12;  // record bytes per token
+hipError_t launch_gsrq(const kvq_ctx *ctx, const void *x, int64_t H, int64_t T, uint8_t *codes, float *s1, float *s2,
+                       float *o, void *ws, hipStream_t s);
+hipError_t launch_gsrq_logits(const kvq_ctx *ctx, const void *q, int64_t B, int64_t Hq, int64_t T,
+                              const uint8_t *codes, const float *s1, const float *s2, const float *o, float *logits,
+                              hipStream_t s);
+
 // NSN-VQ encoded keys and values of one decode call (outputs of
 // kvq_nsn_vq_quantize, or of kvq_nsn_vq_quantize_dq: then s1 and o are read
 // from the 4-bit forms in kdq / vdq and ks1, ko, vs1, vo are unused).
@@ -170,6 +181,10 @@ int nsn_decode_auto_splits(const kvq_ctx *ctx, int64_t B, int64_t T);
 size_t nsn_decode_ws_bytes(int64_t B, int64_t Hq, int64_t T);
 hipError_t launch_nsn_decode(const kvq_ctx *ctx, const void *q, int64_t B, int64_t Hq, int64_t T, const NsnKV &kv,
                              float sm_scale, float *out, void *ws, int n_split, hipStream_t s);
+// Decode over GSRQ records (kc, vc: [B Hkv][T][12]) with the NSN byproducts;
+// workspace as the NSN-VQ decode.
+hipError_t launch_gsrq_decode(const kvq_ctx *ctx, const void *q, int64_t B, int64_t Hq, int64_t T, const NsnKV &kv,
+                              float sm_scale, float *out, void *ws, int n_split, hipStream_t s);
 
 // Streaming NSN-VQ cache: packed rows of T_cap tokens flushed in groups of Gs
 // tokens, each group with its own K and V means ([B Hkv][T_cap / Gs][128]

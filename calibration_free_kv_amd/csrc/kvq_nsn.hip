@@ -667,6 +667,178 @@ __global__ __launch_bounds__(kWavesN * 64) __attribute__((amdgpu_waves_per_eu(2,
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// Gain-shape residual quantisation ("GSRQ", q2bstudio: gain-shape k-means
+// stages in a residual quantisation pipeline) on the NSN front end: z as for
+// NSN-VQ, then per 32-dim sub-vector two stages, each taking the unit shape
+// of largest projection onto the running residual (lowest index on ties),
+// the gain level by counting thresholds below that projection, and
+// subtracting level x shape.  Record of a token: dword 0 = the four stage-1
+// shape indices (byte s = sub-vector s), dword 1 = the stage-2 ones, dword 2
+// = the four gain bytes c1 | c2 << 4.
+//
+// Block of 256 threads = 64 tokens of one head, four lanes per token (lane
+// 4 t + s holds coordinates [32 s, 32 s + 32)).  The Walsh-Hadamard transform
+// is H32 inside the lane and the two cross-quarter stages with lane
+// exchanges (H128 = H4 x H32 in the Sylvester order).  Every lane of a wave
+// scores the same shape at the same time, so the shapes are read as
+// wave-uniform loads (scalar cache) and each score is 32 FMAs with a scalar
+// operand.
+struct GsrqArgs {
+    const _Float16 *x;      // [H][T][128]
+    const float *o;         // [H][128] channel means
+    const float *shapes;    // [2][256][32]
+    const float *levels;    // [2][16] gain levels, then [2][15] thresholds
+    uint32_t *codes;        // [H][T][3]
+    float *s1, *s2;         // [H][T]
+};
+constexpr int kGsrqM = 32, kGsrqK = 256, kGsrqL = 16;
+
+__device__ __forceinline__ void fwht32(float (&v)[kGsrqM])
+{
+#pragma unroll
+    for (int len = 1; len < kGsrqM; len <<= 1)
+#pragma unroll
+        for (int i = 0; i < kGsrqM; ++i)
+            if (!(i & len)) {
+                const float a = v[i], b = v[i + len];
+                v[i] = a + b;
+                v[i + len] = a - b;
+            }
+}
+
+// One stage on the residual r: shape index, gain index; r -= level x shape.
+__device__ __forceinline__ void gsrq_stage(float (&r)[kGsrqM], const float *__restrict__ S, const float *lv,
+                                           const float *th, int &j_out, int &c_out)
+{
+    float best = -__builtin_inff();
+    int jb = 0;
+    for (int j = 0; j < kGsrqK; ++j) {
+        const float *Sj = S + j * kGsrqM;  // wave-uniform
+        float p = 0.0f;
+#pragma unroll
+        for (int k = 0; k < kGsrqM; ++k) p = fmaf(r[k], Sj[k], p);
+        if (p > best) {
+            best = p;
+            jb = j;
+        }
+    }
+    int c = 0;
+#pragma unroll
+    for (int l = 0; l < kGsrqL - 1; ++l) c += th[l] < best ? 1 : 0;
+    const float g = lv[c];
+    const f4_t *Sb = reinterpret_cast<const f4_t *>(S + jb * kGsrqM);
+#pragma unroll
+    for (int k4 = 0; k4 < kGsrqM / 4; ++k4) {
+        const f4_t sv = Sb[k4];
+        r[4 * k4] = fmaf(-g, sv.x, r[4 * k4]);
+        r[4 * k4 + 1] = fmaf(-g, sv.y, r[4 * k4 + 1]);
+        r[4 * k4 + 2] = fmaf(-g, sv.z, r[4 * k4 + 2]);
+        r[4 * k4 + 3] = fmaf(-g, sv.w, r[4 * k4 + 3]);
+    }
+    j_out = jb;
+    c_out = c;
+}
+
+__global__ __launch_bounds__(256) void k_gsrq_encode(GsrqArgs a, int64_t T, int64_t tiles_per_h)
+{
+    __shared__ float tab[2 * kGsrqL + 2 * (kGsrqL - 1)];
+    if (threadIdx.x < 2 * kGsrqL + 2 * (kGsrqL - 1)) tab[threadIdx.x] = a.levels[threadIdx.x];
+    __syncthreads();
+    const int64_t tile = blockIdx.x;
+    const int64_t h = tile / tiles_per_h, t0 = (tile - h * tiles_per_h) * 64;
+    const int s = threadIdx.x & 3;
+    const int64_t t = t0 + (threadIdx.x >> 2);
+    const bool valid = t < T;
+    const int64_t tt = valid ? t : t0;  // lanes past the end re-read a valid token and store nothing
+    const u4_t *xp = reinterpret_cast<const u4_t *>(a.x + (h * T + tt) * kD + kGsrqM * s);
+    uint32_t xw[kGsrqM / 2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const u4_t w = xp[i];
+        xw[4 * i] = w.x;
+        xw[4 * i + 1] = w.y;
+        xw[4 * i + 2] = w.z;
+        xw[4 * i + 3] = w.w;
+    }
+    // ||x||^2 exactly as the statistics pass forms it (norm2_f16: one chain of
+    // packed dot products over each half, then their sum), so that a_t is
+    // rounded identically and a single token gives b = 0: quarter 2 h + 1
+    // continues the chain of quarter 2 h.
+    float ch = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kGsrqM / 2; ++k) {
+        const h2_t p = __builtin_bit_cast(h2_t, xw[k]);
+        ch = __builtin_amdgcn_fdot2(p, p, ch, false);
+    }
+    float half = __shfl_xor(ch, 1);  // odd quarters: the chain of the quarter before
+#pragma unroll
+    for (int k = 0; k < kGsrqM / 2; ++k) {
+        const h2_t p = __builtin_bit_cast(h2_t, xw[k]);
+        half = __builtin_amdgcn_fdot2(p, p, half, false);
+    }
+    // quarters 1 and 3 hold the two half sums; every lane gets their sum
+    const float nb_half = __shfl_xor(half, 1);  // exchanged by every lane
+    const float hs = (s & 1) ? half : nb_half;
+    const float ss = hs + __shfl_xor(hs, 2);
+    const float nx = __builtin_sqrtf(ss);
+    const float inv = ss > 0.0f ? kSqrtD / nx : 0.0f;
+    // b = a - o (a rounded before the subtraction, as in the statistics
+    // pass), s2 = ||b|| / sqrt(d), x~ = b / s2
+    const float *oh = a.o + h * kD + kGsrqM * s;
+    float v[kGsrqM];
+    float bb = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kGsrqM / 2; ++k) {
+#pragma clang fp contract(off)
+        const h2_t p = __builtin_bit_cast(h2_t, xw[k]);
+        const float a0 = (float)p.x * inv, a1 = (float)p.y * inv;
+        v[2 * k] = a0 - oh[2 * k];
+        v[2 * k + 1] = a1 - oh[2 * k + 1];
+    }
+#pragma unroll
+    for (int k = 0; k < kGsrqM; ++k) bb = fmaf(v[k], v[k], bb);
+    bb += __shfl_xor(bb, 1);
+    bb += __shfl_xor(bb, 2);
+    const float nb = __builtin_sqrtf(bb);
+    const float sc = bb > 0.0f ? kSqrtD / nb : 0.0f;
+#pragma unroll
+    for (int k = 0; k < kGsrqM; ++k) v[k] *= sc;
+    // z = H x~ / sqrt(d): H32 in the lane, then the quarter bits
+    fwht32(v);
+#pragma unroll
+    for (int bit = 1; bit < 4; bit <<= 1) {
+        const bool up = (s & bit) != 0;
+#pragma unroll
+        for (int k = 0; k < kGsrqM; ++k) {
+            const float p = __shfl_xor(v[k], bit);
+            v[k] = up ? p - v[k] : v[k] + p;
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < kGsrqM; ++k) v[k] *= 1.0f / kSqrtD;
+    int j1, c1, j2, c2;
+    gsrq_stage(v, a.shapes, tab, tab + 2 * kGsrqL, j1, c1);
+    gsrq_stage(v, a.shapes + kGsrqK * kGsrqM, tab + kGsrqL, tab + 2 * kGsrqL + (kGsrqL - 1), j2, c2);
+    // the token's three dwords from its four lanes
+    uint32_t d0 = (uint32_t)j1 << (8 * s), d1 = (uint32_t)j2 << (8 * s), d2 = (uint32_t)(c1 | (c2 << 4)) << (8 * s);
+#pragma unroll
+    for (int m = 1; m < 4; m <<= 1) {
+        d0 |= __shfl_xor(d0, m);
+        d1 |= __shfl_xor(d1, m);
+        d2 |= __shfl_xor(d2, m);
+    }
+    if (valid) {
+        uint32_t *rec = a.codes + (h * T + t) * 3;
+        if (s < 3) rec[s] = s == 0 ? d0 : s == 1 ? d1 : d2;
+        if (s == 3) {
+            a.s1[h * T + t] = nx / kSqrtD;
+            a.s2[h * T + t] = nb / kSqrtD;
+        }
+    }
+}
+
 }  // namespace
 
 namespace {
@@ -737,5 +909,28 @@ hipError_t nsn_vq_run(const kvq_ctx *ctx, const void *x, int64_t H, int64_t T, i
     return hipGetLastError();
 }
 }  // namespace
+
+// GSRQ: channel means by the NSN statistics pass, then the encoder.
+hipError_t launch_gsrq(const kvq_ctx *ctx, const void *x, int64_t H, int64_t T, uint8_t *codes, float *s1, float *s2,
+                       float *o, void *ws, hipStream_t s)
+{
+    const int n_chunks = (int)((T + kChunk - 1) / kChunk);
+    float *part = (float *)ws;
+    hipLaunchKernelGGL(k_nsn_stats, dim3((unsigned)(H * n_chunks)), dim3(64 * kStatWaves), 0, s, (const u4_t *)x, part, T,
+                       n_chunks, T);
+    hipLaunchKernelGGL(k_nsn_mean, dim3((unsigned)H), dim3(kD * kMeanGroups), 0, s, part, o, T, n_chunks, (int64_t)kD,
+                       (uint8_t *)nullptr, (float *)nullptr);
+    GsrqArgs a{};
+    a.x = (const _Float16 *)x;
+    a.o = o;
+    a.shapes = ctx->d_gsrq;
+    a.levels = ctx->d_gsrq + 2 * kGsrqK * kGsrqM;
+    a.codes = (uint32_t *)codes;
+    a.s1 = s1;
+    a.s2 = s2;
+    const int64_t tph = (T + 63) / 64;
+    hipLaunchKernelGGL(k_gsrq_encode, dim3((unsigned)(H * tph)), dim3(256), 0, s, a, T, tph);
+    return hipGetLastError();
+}
 
 }  // namespace kvq

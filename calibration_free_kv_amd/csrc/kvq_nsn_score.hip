@@ -540,6 +540,279 @@ hipError_t decode_stream_g(const kvq_ctx *ctx, const void *q, int64_t B, int64_t
     return hipGetLastError();
 }
 
+
+// ---------------------------------------------------------------------------
+// Scoring over GSRQ records ("GSRQ", gain-shape residual quantisation, on the
+// NSN byproducts): zq of sub-vector s = G1[c1] S1[j1] + G2[c2] S2[j2], so with
+// q' = H q / sqrt(d)
+//   <q, x_hat> = s1 (s2 sum_s (G1[c1_s] T1[s][j1_s] + G2[c2_s] T2[s][j2_s]) + <q, o>),
+// T_k[s][j] = <q'_s, S_k[j]> (4 sub-vectors of 32 x 256 shapes per stage).
+constexpr int kGM = 32, kGP = kD / kGM;  // sub-vector length, sub-vectors per vector
+template <int G>
+struct GsrqTab {
+    float tab[2][kGP][kVqK][G];  // stage, sub-vector, shape, head
+    float qs[G * kD];
+    float qo[G];
+    float lv[2][16];
+};
+
+// Prologue: levels, q' and <q, o> of the G heads (one wave per head), then
+// the two tables from the shapes in global memory; ends with a barrier.
+template <int G, int NT>
+__device__ void gsrq_tables(const half_t *__restrict__ q, const float *__restrict__ obg,
+                            const float *__restrict__ gs, int64_t qbase, GsrqTab<G> &sm)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    if (tid < 32) sm.lv[tid >> 4][tid & 15] = gs[2 * kVqK * kGM + tid];
+    for (int h = wv; h < G; h += NT / 64) {
+        const h2_t pr = reinterpret_cast<const h2_t *>(q + (qbase + h) * kD)[lane];
+        const f2_t ov = reinterpret_cast<const f2_t *>(obg)[lane];
+        float x0 = (float)pr.x, x1 = (float)pr.y;
+        const float qo = wave_sum(fmaf(x1, ov.y, x0 * ov.x));
+        wave_fwht(x0, x1, lane);
+        reinterpret_cast<f2_t *>(sm.qs + h * kD)[lane] = f2_t{x0 * kInvSqrtD, x1 * kInvSqrtD};
+        if (lane == 0) sm.qo[h] = qo;
+    }
+    __syncthreads();
+    for (int e = tid; e < 2 * kVqK; e += NT) {
+        const int st = e / kVqK, j = e % kVqK;
+        const f4_t *sh = reinterpret_cast<const f4_t *>(gs + (st * kVqK + j) * kGM);
+        f4_t row[kGM / 4];
+#pragma unroll
+        for (int i = 0; i < kGM / 4; ++i) row[i] = sh[i];
+#pragma unroll
+        for (int sv = 0; sv < kGP; ++sv) {
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                const f4_t *qv = reinterpret_cast<const f4_t *>(sm.qs + h * kD + sv * kGM);
+                float acc = 0.0f;
+#pragma unroll
+                for (int i = 0; i < kGM / 4; ++i) {
+                    const f4_t a = qv[i];
+                    acc = fmaf(a.x, row[i].x, acc);
+                    acc = fmaf(a.y, row[i].y, acc);
+                    acc = fmaf(a.z, row[i].z, acc);
+                    acc = fmaf(a.w, row[i].w, acc);
+                }
+                sm.tab[st][sv][j][h] = acc;
+            }
+        }
+    }
+    __syncthreads();
+}
+
+// sum_s (G1[c1] T1[s][j1] + G2[c2] T2[s][j2]) for the G heads of one record.
+template <int G>
+__device__ __forceinline__ void gsrq_key_sum(uint32_t w0, uint32_t w1, uint32_t w2, const GsrqTab<G> &sm,
+                                             float (&acc)[G])
+{
+    typedef float fg_t __attribute__((ext_vector_type(G)));
+    fg_t sum = 0.0f;
+#pragma unroll
+    for (int sv = 0; sv < kGP; ++sv) {
+        const uint32_t j1 = (w0 >> (8 * sv)) & 0xFFu, j2 = (w1 >> (8 * sv)) & 0xFFu, g = (w2 >> (8 * sv)) & 0xFFu;
+        const float a1 = sm.lv[0][g & 15u], a2 = sm.lv[1][g >> 4];
+        sum += a1 * *reinterpret_cast<const fg_t *>(&sm.tab[0][sv][j1][0]);
+        sum += a2 * *reinterpret_cast<const fg_t *>(&sm.tab[1][sv][j2][0]);
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) acc[h] = sum[h];
+}
+
+// logits[b, g G + h, t]: block (chunk of kLogitChunk tokens, b * Hkv + g),
+// one thread per token.
+template <int G>
+__global__ __launch_bounds__(kThreadsN) void k_gsrq_logits(const half_t *__restrict__ q, const uint32_t *__restrict__ codes,
+                                                           const float *__restrict__ s1, const float *__restrict__ s2,
+                                                           const float *__restrict__ o, const float *__restrict__ gs,
+                                                           float *__restrict__ logits, int64_t Hkv, int64_t T)
+{
+    constexpr int NT = kLogitChunk / kThreadsN;
+    __shared__ GsrqTab<G> sm;
+    const int64_t bg = blockIdx.y, b = bg / Hkv, g = bg % Hkv;
+    const int64_t qbase = b * Hkv * G + g * G;
+    const int64_t c0 = (int64_t)blockIdx.x * kLogitChunk, c1 = min(T, c0 + kLogitChunk);
+    uint32_t r0[NT], r1[NT], r2[NT];
+    float a[NT], c[NT];
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+        const int64_t t = c0 + threadIdx.x + i * kThreadsN;
+        const int64_t v = bg * T + (t < c1 ? t : c0);
+        r0[i] = codes[3 * v];
+        r1[i] = codes[3 * v + 1];
+        r2[i] = codes[3 * v + 2];
+        a[i] = s1[v];
+        c[i] = s2[v];
+    }
+    gsrq_tables<G, kThreadsN>(q, o + bg * kD, gs, qbase, sm);
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+        const int64_t t = c0 + threadIdx.x + i * kThreadsN;
+        float acc[G];
+        gsrq_key_sum<G>(r0[i], r1[i], r2[i], sm, acc);
+        if (t < c1) {
+#pragma unroll
+            for (int h = 0; h < G; ++h) logits[(qbase + h) * T + t] = a[i] * fmaf(c[i], acc[h], sm.qo[h]);
+        }
+    }
+}
+
+// Decode, part 1, over GSRQ records: as k_nsn_part (64-token tiles, online
+// softmax, value sums in the code domain with lanes as dimensions), with the
+// value of a token in dimension pair (2 l, 2 l + 1) of sub-vector l / 16
+// being G1[c1] S1[j1][.] + G2[c2] S2[j2][.] (shapes staged in LDS).
+template <int G>
+struct GsrqDecSmem {
+    static constexpr int NW = 8;
+    GsrqTab<G> t;
+    float shapes[2][kVqK][kGM];
+    u4_t vrec[NW][64];
+    float wts[NW][64][G];
+};
+
+template <int G>
+__global__ __launch_bounds__(512) void k_gsrq_part(const half_t *__restrict__ q, const uint32_t *__restrict__ kc,
+                                                   const float *__restrict__ ks1, const float *__restrict__ ks2,
+                                                   const float *__restrict__ ko, const uint32_t *__restrict__ vc,
+                                                   const float *__restrict__ vs1, const float *__restrict__ vs2,
+                                                   const float *__restrict__ gs, float *__restrict__ part,
+                                                   int64_t Hkv, int64_t T, int64_t chunk, float scale2)
+{
+    using SM = GsrqDecSmem<G>;
+    constexpr int NW = SM::NW;
+    __shared__ SM sm;
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t bg = blockIdx.y, b = bg / Hkv, g = bg % Hkv;
+    const int64_t qbase = b * Hkv * G + g * G;
+    const int64_t c0 = (int64_t)blockIdx.x * chunk, c1 = min(T, c0 + chunk);
+    for (int i = threadIdx.x; i < 2 * kVqK * kGM / 4; i += 64 * NW)
+        reinterpret_cast<f4_t *>(&sm.shapes[0][0][0])[i] = reinterpret_cast<const f4_t *>(gs)[i];
+    gsrq_tables<G, 64 * NW>(q, ko + bg * kD, gs, qbase, sm.t);
+
+    float m[G], l[G], wo[G], acc[G][2];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        m[h] = -__builtin_inff();
+        l[h] = wo[h] = acc[h][0] = acc[h][1] = 0.0f;
+    }
+    const int vsub = lane >> 4, vk = 2 * (lane & 15);  // the lane's sub-vector and dimension pair in it
+    // tokens past the end of the range (and whole waves without a tile) load
+    // the range's first token, with weight 0
+    for (int64_t t0 = c0 + 64 * wv; t0 < c1; t0 += 64 * NW) {
+        const bool valid = t0 + lane < c1;
+        const int64_t v = bg * T + (valid ? t0 + lane : c0);
+        const uint32_t k0 = kc[3 * v], k1 = kc[3 * v + 1], k2 = kc[3 * v + 2];
+        const u4_t vr = u4_t{vc[3 * v], vc[3 * v + 1], vc[3 * v + 2], 0u};
+        const float a = ks1[v], c = ks2[v], e1 = vs1[v], e2 = vs2[v];
+        float ks[G];
+        gsrq_key_sum<G>(k0, k1, k2, sm.t, ks);
+        float w[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const float lg = valid ? a * fmaf(c, ks[h], sm.t.qo[h]) * scale2 : -__builtin_inff();
+            const float mn = fmaxf(m[h], wave_max(lg));
+            const float alpha = __builtin_amdgcn_exp2f(m[h] - mn);
+            const float p = __builtin_amdgcn_exp2f(lg - mn);
+            m[h] = mn;
+            l[h] = fmaf(l[h], alpha, p);
+            wo[h] = fmaf(wo[h], alpha, p * e1);
+            acc[h][0] *= alpha;
+            acc[h][1] *= alpha;
+            w[h] = p * e1 * e2;
+        }
+        sm.vrec[wv][lane] = vr;
+#pragma unroll
+        for (int h = 0; h < G; ++h) sm.wts[wv][lane][h] = w[h];
+        wave_lds_sync();
+#pragma unroll 8
+        for (int i = 0; i < 64; ++i) {
+            const u4_t r = sm.vrec[wv][i];
+            const uint32_t j1 = (r.x >> (8 * vsub)) & 0xFFu, j2 = (r.y >> (8 * vsub)) & 0xFFu;
+            const uint32_t gg = (r.z >> (8 * vsub)) & 0xFFu;
+            const float a1 = sm.t.lv[0][gg & 15u], a2 = sm.t.lv[1][gg >> 4];
+            const f2_t s1v = *reinterpret_cast<const f2_t *>(&sm.shapes[0][j1][vk]);
+            const f2_t s2v = *reinterpret_cast<const f2_t *>(&sm.shapes[1][j2][vk]);
+            const float e0 = fmaf(a2, s2v.x, a1 * s1v.x), ee1 = fmaf(a2, s2v.y, a1 * s1v.y);
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                const float wh = sm.wts[wv][i][h];
+                acc[h][0] = fmaf(wh, e0, acc[h][0]);
+                acc[h][1] = fmaf(wh, ee1, acc[h][1]);
+            }
+        }
+        wave_lds_sync();
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        l[h] = wave_sum(l[h]);
+        wo[h] = wave_sum(wo[h]);
+    }
+    // merge of the waves through the (no longer read) shape space
+    __syncthreads();
+    float *mw = &sm.shapes[0][0][0];
+    static_assert(NW * G * kPartStride <= 2 * kVqK * kGM, "wave partials fit in the shape space");
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        float *p = mw + (wv * G + h) * kPartStride;
+        *reinterpret_cast<f2_t *>(p + 2 * lane) = f2_t{acc[h][0], acc[h][1]};
+        if (lane == 0) {
+            p[kD] = m[h];
+            p[kD + 1] = l[h];
+            p[kD + 2] = wo[h];
+        }
+    }
+    __syncthreads();
+    const int64_t split = blockIdx.x, n_split = gridDim.x;
+    for (int i = threadIdx.x; i < G * kD; i += 64 * NW) {
+        const int h = i / kD, dim = i % kD;
+        float M = -__builtin_inff();
+#pragma unroll
+        for (int w2 = 0; w2 < NW; ++w2) M = fmaxf(M, mw[(w2 * G + h) * kPartStride + kD]);
+        float A = 0.0f, L = 0.0f, WO = 0.0f;
+#pragma unroll
+        for (int w2 = 0; w2 < NW; ++w2) {
+            const float *p = mw + (w2 * G + h) * kPartStride;
+            const float f = __builtin_amdgcn_exp2f(p[kD] - M);
+            A = fmaf(f, p[dim], A);
+            L = fmaf(f, p[kD + 1], L);
+            WO = fmaf(f, p[kD + 2], WO);
+        }
+        float *dst = part + ((bg * n_split + split) * G + h) * kPartStride;
+        dst[dim] = A;
+        if (dim == 0) {
+            dst[kD] = M;
+            dst[kD + 1] = L;
+            dst[kD + 2] = WO;
+        }
+    }
+}
+
+template <int G>
+hipError_t gsrq_logits_g(const kvq_ctx *ctx, const void *q, int64_t B, int64_t T, const uint8_t *codes,
+                         const float *s1, const float *s2, const float *o, float *logits, hipStream_t s)
+{
+    const int64_t n_chunks = (T + kLogitChunk - 1) / kLogitChunk;
+    hipLaunchKernelGGL(k_gsrq_logits<G>, dim3((unsigned)n_chunks, (unsigned)(B * ctx->H)), dim3(kThreadsN), 0, s,
+                       (const half_t *)q, (const uint32_t *)codes, s1, s2, o, ctx->d_gsrq, logits, (int64_t)ctx->H, T);
+    return hipGetLastError();
+}
+
+template <int G>
+hipError_t gsrq_decode_g(const kvq_ctx *ctx, const void *q, int64_t B, int64_t T, const NsnKV &kv, float sm_scale,
+                         float *out, void *ws, int n_split, hipStream_t s)
+{
+    const int64_t chunk = nsn_decode_chunk(T, n_split);
+    const int ns = (int)((T + chunk - 1) / chunk);
+    float *part = (float *)ws;
+    hipLaunchKernelGGL(k_gsrq_part<G>, dim3((unsigned)ns, (unsigned)(B * ctx->H)), dim3(512), 0, s, (const half_t *)q,
+                       (const uint32_t *)kv.kc, kv.ks1, kv.ks2, kv.ko, (const uint32_t *)kv.vc, kv.vs1, kv.vs2,
+                       ctx->d_gsrq, part, (int64_t)ctx->H, T, chunk, sm_scale * kLog2e);
+    hipLaunchKernelGGL((k_nsn_merge<G, false>), dim3((unsigned)(B * ctx->H)), dim3(64 * G), 0, s, part, kv.vo, out,
+                       (int64_t)ctx->H, ns, NsnDqIn{});
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_nsn_logits(const kvq_ctx *ctx, const void *q, int64_t B, int64_t Hq, int64_t T,
@@ -588,6 +861,30 @@ hipError_t launch_nsn_decode_stream(const kvq_ctx *ctx, const void *q, int64_t B
         case 1: return decode_stream_g<1>(ctx, q, B, T, kv, st, sm_scale, out, ws, n_split, s);
         case 2: return decode_stream_g<2>(ctx, q, B, T, kv, st, sm_scale, out, ws, n_split, s);
         case 4: return decode_stream_g<4>(ctx, q, B, T, kv, st, sm_scale, out, ws, n_split, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_gsrq_logits(const kvq_ctx *ctx, const void *q, int64_t B, int64_t Hq, int64_t T,
+                              const uint8_t *codes, const float *s1, const float *s2, const float *o, float *logits,
+                              hipStream_t s)
+{
+    switch (Hq / ctx->H) {
+        case 1: return gsrq_logits_g<1>(ctx, q, B, T, codes, s1, s2, o, logits, s);
+        case 2: return gsrq_logits_g<2>(ctx, q, B, T, codes, s1, s2, o, logits, s);
+        case 4: return gsrq_logits_g<4>(ctx, q, B, T, codes, s1, s2, o, logits, s);
+        case 8: return gsrq_logits_g<8>(ctx, q, B, T, codes, s1, s2, o, logits, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_gsrq_decode(const kvq_ctx *ctx, const void *q, int64_t B, int64_t Hq, int64_t T, const NsnKV &kv,
+                              float sm_scale, float *out, void *ws, int n_split, hipStream_t s)
+{
+    switch (Hq / ctx->H) {
+        case 1: return gsrq_decode_g<1>(ctx, q, B, T, kv, sm_scale, out, ws, n_split, s);
+        case 2: return gsrq_decode_g<2>(ctx, q, B, T, kv, sm_scale, out, ws, n_split, s);
+        case 4: return gsrq_decode_g<4>(ctx, q, B, T, kv, sm_scale, out, ws, n_split, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -23,6 +23,7 @@ KVQ_CODEBOOK_GAUSS, KVQ_CODEBOOK_BETA = 0, 1
 KVQ_ROTATION_HADAMARD, KVQ_ROTATION_DENSE = 0, 1
 KVQ_NSN_ADAPTIVE_SCALE = 1
 KVQ_NSN_DQ_CODEBOOK = 2
+KVQ_MODE_GSRQ = 3
 D = 128
 
 EXPORTS = [
@@ -33,6 +34,7 @@ EXPORTS = [
     "kvq_attn_decode_stream_ws_bytes", "kvq_attn_decode_stream", "kvq_flush", "kvq_attn_decode_noalloc",
     "kvq_nsn_flush_ws_bytes", "kvq_nsn_flush", "kvq_nsn_attn_decode_stream_ws_bytes", "kvq_nsn_attn_decode_stream",
     "kvq_nsn_vq_dq_ws_bytes", "kvq_nsn_vq_quantize_dq", "kvq_nsn_logits_dq", "kvq_nsn_attn_decode_dq",
+    "kvq_gsrq_ws_bytes", "kvq_gsrq_quantize", "kvq_gsrq_logits", "kvq_gsrq_attn_decode",
 ]
 
 
@@ -48,7 +50,7 @@ class kvq_config(C.Structure):
         ("seed", C.c_uint64), ("signs_k", C.POINTER(C.c_int8)), ("signs_v", C.POINTER(C.c_int8)),
         ("qjl_S", C.POINTER(C.c_float)), ("vq_codebook", C.POINTER(C.c_float)),
         ("device", C.c_int32), ("codebook", C.c_int32), ("rotation", C.c_int32),
-        ("rot_Q", C.POINTER(C.c_float)), ("nsn_options", C.c_int32),
+        ("rot_Q", C.POINTER(C.c_float)), ("nsn_options", C.c_int32), ("gsrq_tables", C.POINTER(C.c_float)),
     ]
 
 
@@ -110,6 +112,12 @@ def lib():
         L.kvq_nsn_logits_dq.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp]
         L.kvq_nsn_attn_decode_dq.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                              C.c_float, vp, vp, sz, i32, vp]
+        L.kvq_gsrq_ws_bytes.argtypes = [vp, i64, i64]
+        L.kvq_gsrq_ws_bytes.restype = sz
+        L.kvq_gsrq_quantize.argtypes = [vp, vp, i64, i64, vp, vp, vp, vp, vp, sz, vp]
+        L.kvq_gsrq_logits.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, vp, vp, vp]
+        L.kvq_gsrq_attn_decode.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, C.c_float, vp, vp,
+                                           sz, i32, vp]
         _lib = L
     return _lib
 
@@ -158,7 +166,7 @@ class Context:
 
     def __init__(self, n_kv_heads: int, bits: int = 3, signs_k=None, signs_v=None, mode: int = KVQ_MODE_MSE,
                  qjl_S=None, vq_codebook=None, device: int = 0, seed: int = 0, codebook: int = KVQ_CODEBOOK_GAUSS,
-                 rot_Q=None, nsn_options: int = 0):
+                 rot_Q=None, nsn_options: int = 0, gsrq_tables=None):
         self.n_kv_heads, self.bits, self.mode, self.device = n_kv_heads, bits, mode, device
         cfg = kvq_config()
         cfg.d, cfg.bits, cfg.mode, cfg.n_kv_heads, cfg.device = D, bits, mode, n_kv_heads, device
@@ -179,6 +187,10 @@ class Context:
         cfg.rotation = KVQ_ROTATION_DENSE if rot_Q is not None else KVQ_ROTATION_HADAMARD
         cfg.rot_Q = arr(rot_Q, np.float32, C.c_float)
         cfg.nsn_options = nsn_options
+        if gsrq_tables is not None:  # dict S1 [256,32], G1 [16], S2, G2 -> the flat host layout
+            gsrq_tables = np.concatenate([np.asarray(gsrq_tables[k], np.float32).ravel()
+                                          for k in ("S1", "G1", "S2", "G2")])
+        cfg.gsrq_tables = arr(gsrq_tables, np.float32, C.c_float)
         h = C.c_void_p()
         _check(lib().kvq_create(C.byref(cfg), C.byref(h)), "kvq_create")
         self.handle = h
@@ -387,6 +399,43 @@ class Context:
         kvq_nsn_attn_decode_dq(self, q, B, Hq, T, k, v, sm_scale, out, ws, n_split)
         return out
 
+    def gsrq_quantize(self, x, out=None, ws=None):
+        """GSRQ on the NSN front end: x [H,T,128] fp16 -> dict(codes [H,T,12] u8, s1, s2 [H,T],
+        o [H,128])."""
+        _dev_tensor(x, torch.float16, "x")
+        H, T, _ = x.shape
+        if ws is None:
+            ws = torch.empty(int(lib().kvq_gsrq_ws_bytes(self.handle, H, T)), dtype=torch.uint8, device=x.device)
+        if out is None:
+            out = dict(codes=torch.empty((H, T, 12), dtype=torch.uint8, device=x.device),
+                       s1=torch.empty((H, T), dtype=torch.float32, device=x.device),
+                       s2=torch.empty((H, T), dtype=torch.float32, device=x.device),
+                       o=torch.empty((H, D), dtype=torch.float32, device=x.device))
+        kvq_gsrq_quantize(self, x, H, T, out["codes"], out["s1"], out["s2"], out["o"], ws)
+        return out
+
+    def gsrq_logits(self, q, codes, s1, s2, o, out=None):
+        _dev_tensor(q, torch.float16, "q")
+        B, Hq, _ = q.shape
+        T = codes.shape[2]
+        if out is None:
+            out = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+        kvq_gsrq_logits(self, q, B, Hq, T, codes, s1, s2, o, out)
+        return out
+
+    def gsrq_attn_decode(self, q, k, v, sm_scale: float = 0.0, ws=None, out=None, n_split: int = 0):
+        """k, v: dicts of codes [B,Hkv,T,12], s1, s2 [B,Hkv,T], o [B,Hkv,128] -> out [B,Hq,128]."""
+        _dev_tensor(q, torch.float16, "q")
+        B, Hq, _ = q.shape
+        T = k["codes"].shape[2]
+        if ws is None:
+            ws = self.nsn_decode_ws(B, Hq, T)
+        if out is None:
+            out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+        kvq_gsrq_attn_decode(self, q, B, Hq, T, k["codes"], k["s1"], k["s2"], k["o"], v["codes"], v["s1"], v["s2"],
+                             v["o"], sm_scale, out, ws, n_split)
+        return out
+
     def nsn_stream_alloc(self, B, T_cap, Gs):
         """Packed arrays of a streaming NSN-VQ cache: codes [B,Hkv,T_cap,16], s1/s2
         [B,Hkv,T_cap], means o [B,Hkv,T_cap/Gs,128], for K and V."""
@@ -575,3 +624,27 @@ def kvq_nsn_attn_decode_dq(ctx: Context, q, B, H_q, T, k, v, sm_scale, out, ws, 
     _check(lib().kvq_nsn_attn_decode_dq(ctx.handle, _ptr(q), B, H_q, T, *_dq_args(k, "k_"), *_dq_args(v, "v_"),
                                         float(sm_scale), _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
                                         int(n_split), _stream(q.device)), "kvq_nsn_attn_decode_dq")
+
+
+def kvq_gsrq_quantize(ctx: Context, x, H, T, codes, s1, s2, o, ws):
+    _dev_tensor(x, torch.float16, "x")
+    _nsn_inputs(codes, s1, s2, o, "")
+    _check(lib().kvq_gsrq_quantize(ctx.handle, _ptr(x), H, T, _ptr(codes), _ptr(s1), _ptr(s2), _ptr(o), _ptr(ws),
+                                   ws.numel() * ws.element_size(), _stream(x.device)), "kvq_gsrq_quantize")
+
+
+def kvq_gsrq_logits(ctx: Context, q, B, H_q, T, codes, s1, s2, o, logits):
+    _nsn_inputs(codes, s1, s2, o, "")
+    _dev_tensor(logits, torch.float32, "logits")
+    _check(lib().kvq_gsrq_logits(ctx.handle, _ptr(q), B, H_q, T, _ptr(codes), _ptr(s1), _ptr(s2), _ptr(o),
+                                 _ptr(logits), _stream(q.device)), "kvq_gsrq_logits")
+
+
+def kvq_gsrq_attn_decode(ctx: Context, q, B, H_q, T, kc, ks1, ks2, ko, vc, vs1, vs2, vo, sm_scale, out, ws, n_split=0):
+    _nsn_inputs(kc, ks1, ks2, ko, "k_")
+    _nsn_inputs(vc, vs1, vs2, vo, "v_")
+    _dev_tensor(out, torch.float32, "out")
+    _check(lib().kvq_gsrq_attn_decode(ctx.handle, _ptr(q), B, H_q, T, _ptr(kc), _ptr(ks1), _ptr(ks2), _ptr(ko),
+                                      _ptr(vc), _ptr(vs1), _ptr(vs2), _ptr(vo), float(sm_scale), _ptr(out), _ptr(ws),
+                                      ws.numel() * ws.element_size(), int(n_split), _stream(q.device)),
+           "kvq_gsrq_attn_decode")

@@ -185,6 +185,16 @@ def random_nsn_dq_codes(seed: int, lead, d: int = D, sub: int = 8, block: int = 
                 oq=rng.integers(0, 256, size=rows + (d // 2,), dtype=np.uint8), op=op)
 
 
+def random_gsrq_codes(seed: int, lead, d: int = D):
+    """Stand-in GSRQ records (no quantizer involved): 12 uniform bytes per
+    vector [*lead, 12] (4 stage-1 and 4 stage-2 shape indices, 4 gain bytes),
+    with s1, s2 and the means drawn as random_nsn_codes draws them."""
+    e = random_nsn_codes(seed, lead, d)
+    rng = np.random.Generator(np.random.PCG64(seed + 7919))
+    e["codes"] = rng.integers(0, 256, size=tuple(lead) + (12,), dtype=np.uint8)
+    return e
+
+
 def random_orthogonal(seed: int, d: int = D):
     """A Haar-random orthogonal d x d matrix (float64): QR of a seeded N(0,1)
     matrix with the signs of R's diagonal moved into Q."""

@@ -18,6 +18,10 @@
  *        Low-Bit Vector Quantization of KV Cache" (gist.science 2505.18231),
  *        Metodologia sec. 1 (Normalize-Shift-Normalize, byproducts s1, o,
  *        s2), sec. 2 (Hadamard), sec. 3 (one global N(0,1) vector codebook).
+ *  [GSRQ] "GSRQ: Quantitzacio Residual de Forma-Guanys per a Cau KV de Menys
+ *        d'1 Bit" (q2bstudio.com): gain-shape k-means (norm kept apart from
+ *        direction) in a residual quantisation pipeline, below 1 bit per
+ *        element.
  *
  * Conventions for every call
  *  - d = 128 (head dimension).  Vectors are fp16, row-major, tokens
@@ -66,7 +70,9 @@ typedef enum {
     KVQ_E_WORKSPACE = 5    /* caller workspace smaller than required        */
 } kvq_status;
 
-enum { KVQ_MODE_MSE = 0, KVQ_MODE_MSE_QJL = 1, KVQ_MODE_NSN_VQ = 2 };
+/* KVQ_MODE_GSRQ: gain-shape residual quantisation ([GSRQ]) on the NSN front
+ * end; see kvq_gsrq_quantize. */
+enum { KVQ_MODE_MSE = 0, KVQ_MODE_MSE_QJL = 1, KVQ_MODE_NSN_VQ = 2, KVQ_MODE_GSRQ = 3 };
 enum { KVQ_KIND_K = 0, KVQ_KIND_V = 1 };
 /* Scalar codebook of the MSE modes: Lloyd-Max for N(0,1) ([PQ] sec. 2), or
  * Lloyd-Max for the exact law of a rotated unit vector's coordinate at
@@ -122,6 +128,9 @@ typedef struct {
     int32_t rotation;          /* KVQ_ROTATION_* (0 = randomized Hadamard)            */
     const float *rot_Q;        /* host [d, d] row-major orthogonal Q (ROTATION_DENSE)  */
     int32_t nsn_options;       /* KVQ_NSN_* bits (NSN_VQ mode; 0 = none)              */
+    const float *gsrq_tables;  /* host GSRQ tables (GSRQ mode): stage 1 shapes [256, 32],
+                                  its 16 gain levels, stage 2 shapes [256, 32], its 16
+                                  levels, fp32, levels strictly increasing             */
 } kvq_config;
 
 /* Create a context: validates the configuration, builds the b-bit Lloyd-Max
@@ -411,6 +420,46 @@ kvq_status kvq_nsn_attn_decode_dq(kvq_ctx *ctx, const void *q_f16, int64_t B, in
                                   const uint8_t *v_codes, const uint8_t *v_s1q, const float *v_s1p,
                                   const float *v_s2, const uint8_t *v_oq, const float *v_op, float sm_scale,
                                   float *out, void *ws, size_t ws_bytes, int32_t n_split, void *stream);
+
+/* Gain-shape residual quantisation ([GSRQ]: gain-shape k-means, which keeps
+ * a reproduction's norm apart from its direction, in a residual quantisation
+ * pipeline, below 1 bit per element).  The page gives no dimensions or front
+ * end; here the NSN front end ([NSN] Metodologia 1-2: s1, o, s2 and
+ * z = H (b / s2) / sqrt(d), as kvq_nsn_vq_quantize) feeds 4 sub-vectors of
+ * 32 dimensions, each encoded in two stages k = 1, 2 on the running residual
+ * r (r = z_s first): j = the shape of largest projection <r, S_k[j]> (lowest
+ * j on ties), c = the number of thresholds (midpoints of adjacent levels)
+ * below that projection, r -= G_k[c] S_k[j].  The context's tables
+ * (kvq_config.gsrq_tables) are the codebook.  Record of a token, 12 bytes:
+ * the 4 stage-1 shape indices, the 4 stage-2 ones, then c1 | c2 << 4 per
+ * sub-vector (24 bits per 32 elements: 0.75 bit per element, plus s1, s2).
+ *
+ * Workspace bytes kvq_gsrq_quantize needs for H heads of T tokens. */
+size_t kvq_gsrq_ws_bytes(const kvq_ctx *ctx, int64_t H, int64_t T);
+
+/* GSRQ of x_f16 [H, T, d] fp16, per head over the T tokens of the call:
+ *   codes  out [H, T, 12] bytes (4-byte aligned); s1, s2 out [H, T] fp32;
+ *   o      out [H, d] fp32 (16-byte aligned)
+ *   ws     kvq_gsrq_ws_bytes() bytes, 256-byte aligned, no initialisation.
+ * T >= 1.  Requires a context in KVQ_MODE_GSRQ. */
+kvq_status kvq_gsrq_quantize(kvq_ctx *ctx, const void *x_f16, int64_t H, int64_t T, uint8_t *codes, float *s1,
+                             float *s2, float *o, void *ws, size_t ws_bytes, void *stream);
+
+/* Logits from GSRQ records: x_hat = s1 (s2 H zq / sqrt(d) + o) with
+ * zq_s = G1[c1] S1[j1] + G2[c2] S2[j2], so with q' = H q / sqrt(d)
+ *   logits[b,h,t] = s1 (s2 sum_s (G1[c1] <q'_s, S1[j1]> + G2[c2] <q'_s, S2[j2]>) + <q_h, o_g>).
+ * Layouts as kvq_nsn_logits with 12-byte records; H_q / H_kv in {1, 2, 4, 8}. */
+kvq_status kvq_gsrq_logits(kvq_ctx *ctx, const void *q_f16, int64_t B, int64_t H_q, int64_t T, const uint8_t *codes,
+                           const float *s1, const float *s2, const float *o, float *logits, void *stream);
+
+/* One decode step over GSRQ keys and values, as kvq_nsn_attn_decode_splits
+ * (workspace kvq_nsn_attn_decode_ws_bytes(), no initialisation);
+ * H_q / H_kv in {1, 2, 4}. */
+kvq_status kvq_gsrq_attn_decode(kvq_ctx *ctx, const void *q_f16, int64_t B, int64_t H_q, int64_t T,
+                                const uint8_t *k_codes, const float *k_s1, const float *k_s2, const float *k_o,
+                                const uint8_t *v_codes, const float *v_s1, const float *v_s2, const float *v_o,
+                                float sm_scale, float *out, void *ws, size_t ws_bytes, int32_t n_split,
+                                void *stream);
 
 /* Streaming NSN-VQ cache ([NSN] Detalhes de Implementacao: recent tokens
  * stay in a full-precision window that is quantised when it fills, as in

@@ -93,6 +93,15 @@ hipError_t launch_nsn_vq_dq(const kvq_ctx *, const void *, int64_t H, int64_t T,
 hipError_t launch_nsn_logits_dq(const kvq_ctx *, const void *, int64_t B, int64_t Hq, int64_t T, const uint8_t *,
                                 const NsnDqIn &, const float *, float *, hipStream_t)
 { return rec("nsn_logits_dq", B, Hq, T); }
+hipError_t launch_gsrq(const kvq_ctx *, const void *, int64_t H, int64_t T, uint8_t *, float *, float *, float *,
+                       void *, hipStream_t)
+{ return rec("gsrq", H, T); }
+hipError_t launch_gsrq_logits(const kvq_ctx *, const void *, int64_t B, int64_t Hq, int64_t T, const uint8_t *,
+                              const float *, const float *, const float *, float *, hipStream_t)
+{ return rec("gsrq_logits", B, Hq, T); }
+hipError_t launch_gsrq_decode(const kvq_ctx *, const void *, int64_t B, int64_t Hq, int64_t T, const NsnKV &, float,
+                              float *, void *, int ns, hipStream_t)
+{ return rec("gsrq_decode", B, Hq, T, ns); }
 hipError_t launch_nsn_decode_stream(const kvq_ctx *, const void *, int64_t B, int64_t Hq, int64_t T, const NsnKV &,
                                     const NsnStream &, float, float *, void *, int ns, hipStream_t)
 { return rec("nsn_decode_stream", B, Hq, T, ns); }

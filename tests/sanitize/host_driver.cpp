@@ -262,6 +262,44 @@ int main()
         CHECK(kvq_create(&cd, &cx) == KVQ_E_INVAL);
     }
 
+    // gain-shape residual quantisation
+    {
+        std::vector<float> gt(2 * (256 * 32 + 16));
+        for (auto &v : gt) v = rnd();
+        for (int st = 0; st < 2; ++st)
+            for (int l = 0; l < 16; ++l) gt[st * (256 * 32 + 16) + 256 * 32 + l] = 0.5f + 0.25f * l;
+        kvq_config cg = base(1, KVQ_MODE_GSRQ, H);
+        kvq_ctx *gq = nullptr;
+        CHECK(kvq_create(&cg, &gq) == KVQ_E_INVAL);  // no tables
+        cg.gsrq_tables = gt.data();
+        gt[256 * 32 + 5] = gt[256 * 32 + 4];  // levels not increasing
+        CHECK(kvq_create(&cg, &gq) == KVQ_E_INVAL);
+        gt[256 * 32 + 5] = 0.5f + 0.25f * 5;
+        cg.rotation = KVQ_ROTATION_DENSE;
+        cg.rot_Q = Q.data();
+        CHECK(kvq_create(&cg, &gq) == KVQ_E_UNSUPPORTED);
+        cg.rotation = KVQ_ROTATION_HADAMARD;
+        cg.rot_Q = nullptr;
+        CHECK(kvq_create(&cg, &gq) == KVQ_OK);
+        CHECK(kvq_code_bytes_per_vec(gq) == 12);
+        const size_t gws = kvq_gsrq_ws_bytes(gq, H, T);
+        Buf gw(gws), gc(H * T * 12), gs1(H * T * 4), go(H * 512);
+        CHECK(kvq_gsrq_quantize(gq, x.p, H, T, gc.as<uint8_t>(), gs1.as<float>(), gs1.as<float>(), go.as<float>(), gw.p, gws, st0) == KVQ_OK);
+        CHECK(std::strcmp(g_last.what, "gsrq") == 0 && g_last.a == H && g_last.b == T);
+        CHECK(kvq_gsrq_quantize(gq, x.p, H, T, gc.as<uint8_t>(), gs1.as<float>(), gs1.as<float>(), go.as<float>(), gw.p, gws - 1, st0) == KVQ_E_WORKSPACE);
+        CHECK(kvq_gsrq_quantize(nsn, x.p, H, T, gc.as<uint8_t>(), gs1.as<float>(), gs1.as<float>(), go.as<float>(), gw.p, gws, st0) == KVQ_E_INVAL);
+        CHECK(kvq_quantize(gq, 0, x.p, 1, H, T, codes.as<uint8_t>(), norms.as<float>(), nullptr, nullptr, st0) == KVQ_E_INVAL);
+        CHECK(kvq_gsrq_logits(gq, q.p, 1, H * 8, T, gc.as<uint8_t>(), gs1.as<float>(), gs1.as<float>(), go.as<float>(), lg.as<float>(), st0) == KVQ_OK);
+        CHECK(kvq_gsrq_logits(gq, q.p, 1, H * 3, T, gc.as<uint8_t>(), gs1.as<float>(), gs1.as<float>(), go.as<float>(), lg.as<float>(), st0) == KVQ_E_INVAL);
+        const size_t gdw = kvq_nsn_attn_decode_ws_bytes(gq, 1, Hq, T);
+        Buf gd(gdw);
+        CHECK(kvq_gsrq_attn_decode(gq, q.p, 1, Hq, T, gc.as<uint8_t>(), gs1.as<float>(), gs1.as<float>(), go.as<float>(), gc.as<uint8_t>(), gs1.as<float>(), gs1.as<float>(), go.as<float>(), 0.f, out.as<float>(), gd.p, gdw, 0, st0) == KVQ_OK);
+        CHECK(std::strcmp(g_last.what, "gsrq_decode") == 0 && g_last.n_split >= 1);
+        CHECK(kvq_gsrq_attn_decode(gq, q.p, 1, H * 8, T, gc.as<uint8_t>(), gs1.as<float>(), gs1.as<float>(), go.as<float>(), gc.as<uint8_t>(), gs1.as<float>(), gs1.as<float>(), go.as<float>(), 0.f, out.as<float>(), gd.p, gdw, 0, st0) == KVQ_E_INVAL);
+        CHECK(kvq_gsrq_attn_decode(gq, q.p, 1, Hq, T, gc.as<uint8_t>(), gs1.as<float>(), gs1.as<float>(), go.as<float>(), gc.as<uint8_t>(), gs1.as<float>(), gs1.as<float>(), go.as<float>(), 0.f, out.as<float>(), gd.p, gdw - 1, 0, st0) == KVQ_E_WORKSPACE);
+        CHECK(kvq_destroy(gq) == KVQ_OK);
+    }
+
     // NSN-VQ streaming cache: flush groups of Gs tokens, decode over packed + window
     {
         const int64_t Gs = 128, Tc = 1024, Rc = 192, Tn = 512, Rn = 40;

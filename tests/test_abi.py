@@ -132,5 +132,10 @@ def test_null_context_calls():
     assert L.kvq_nsn_logits_dq(None, None, 1, 4, 1, None, None, None, None, None, None, None, None) == kvq.KVQ_E_INVAL
     assert L.kvq_nsn_attn_decode_dq(None, None, 1, 4, 1, None, None, None, None, None, None, None, None, None, None,
                                     None, None, 0.0, None, None, 0, 0, None) == kvq.KVQ_E_INVAL
+    assert L.kvq_gsrq_ws_bytes(None, 1, 1) == 0
+    assert L.kvq_gsrq_quantize(None, None, 1, 1, None, None, None, None, None, 0, None) == kvq.KVQ_E_INVAL
+    assert L.kvq_gsrq_logits(None, None, 1, 4, 1, None, None, None, None, None, None) == kvq.KVQ_E_INVAL
+    assert L.kvq_gsrq_attn_decode(None, None, 1, 4, 1, None, None, None, None, None, None, None, None, 0.0, None,
+                                  None, 0, 0, None) == kvq.KVQ_E_INVAL
     for s in range(6):
         assert kvq.strerror(s)
