@@ -636,6 +636,44 @@ def rows(torch, kvq, synth, dev, timer, reps, oracle_rates):
         note="graph replay; s1 read as 4-bit codes with per-block pairs")
     del kvd
 
+    # gain-shape residual quantisation on the NSN front end (12-byte records):
+    # the encoder over 8 heads x 65536 tokens, logits and decode from
+    # stand-in records
+    gl = [ln.split() for ln in open(os.path.join(ROOT, "tests", "golden", "gsrq_tables_256x32.txt"))
+          if not ln.startswith("#")]
+    gtab = dict(S1=np.array(gl[0:256], np.float32), G1=np.array(gl[256], np.float32),
+                S2=np.array(gl[257:513], np.float32), G2=np.array(gl[513], np.float32))
+    ctxg = kvq.Context(H, 1, mode=kvq.KVQ_MODE_GSRQ, gsrq_tables=gtab, device=dev.index)
+    x0 = torch.from_numpy(inp["x"]).to(dev)
+    xsn = [x0] + [x0.clone() for _ in range(3)]
+    og = ctxg.gsrq_quantize(x0)
+    wsg = torch.empty(int(kvq.lib().kvq_gsrq_ws_bytes(ctxg.handle, H, T)), dtype=torch.uint8, device=dev)
+    out["gsrq_8x65536"] = row(*timer.run(lambda i: ctxg.gsrq_quantize(xsn[i % 4], out=og, ws=wsg), reps, 4),
+                              nbytes=H * T * (2 * D + 12 + 8), flops=H * T * 2 * 4 * 256 * 32 * 2,
+                              units_per_launch=H * T, unit="vectors",
+                              note="three launches (stats, mean, search); two stages of 256 shapes per 32-dim "
+                              "sub-vector on the vector ALUs; x is read twice")
+    del xsn, x0
+    n = H * T
+    ns = rng_sets(n * 2 * (12 + 8))
+    kvg = [(dv(synth.random_gsrq_codes(110 + 2 * i, (1, H, T))), dv(synth.random_gsrq_codes(111 + 2 * i, (1, H, T))))
+           for i in range(ns)]
+
+    def glg(i):
+        e = kvg[i % ns][0]
+        ctxg.gsrq_logits(qn, e["codes"], e["s1"], e["s2"], e["o"], out=lgo)
+
+    def gdec(i):
+        ctxg.gsrq_attn_decode(qn, kvg[i % ns][0], kvg[i % ns][1], ws=wsd, out=dout)
+    last = ns - 1
+    out["gsrq_logits_8x65536_g4"] = row(*run_graph(timer, glg, reps, ns, check=same(lambda i: glg(last), lgo)),
+                                        nbytes=n * (12 + 8 + 4 * Hq // H), units_per_launch=n, unit="keys",
+                                        buffer_sets=ns, note="graph replay; 8 table lookups per key serve 4 heads")
+    out["gsrq_attn_decode_8x65536_g4"] = row(*run_graph(timer, gdec, reps, ns, check=same(lambda i: gdec(last), dout)),
+                                             nbytes=n * 2 * (12 + 8), units_per_launch=n, unit="keys",
+                                             buffer_sets=ns, note="graph replay; two launches (splits, merge)")
+    del kvg, ctxg
+
     # streaming NSN-VQ cache: 65408 packed tokens in flush groups of 128 (each
     # with its own means) plus a 100-token fp16 window, 8 KV heads, 32 query
     # heads; and the flush of one 128-token group of the window
