@@ -8,6 +8,10 @@ with kvq_quantize_kv, then one decode step of attention for its 32 query heads
 timing starts.  The steps rotate over 4 input/output sets (645 MB, more than
 twice the 256 MB last-level cache); the decode of step s reads the codes of
 set s + 2, written two steps earlier, so they are not served from that cache.
+The decode runs on a second stream (default priority) and overlaps the
+quantize of the same step: events order each decode after the quantize that
+wrote its codes and each quantize after the last decode that read the set it
+overwrites.
 
 value = (K and V vectors quantised + keys scored) per second of the whole step.
 roofline = the dominant kernel (kvq_quantize_kv): algorithmic bytes per launch
@@ -301,21 +305,51 @@ def main_step(torch, kvq, synth, args, dev, timer):
         if ev is not None:
             ev[2].record(stream)
 
+    # The timed steps put each step's decode on a second stream, where it
+    # overlaps the same step's quantize (they touch different buffer sets):
+    # decode s waits for quantize s - 2, which wrote the codes it reads, and
+    # quantize s waits for decode s - 2, the last reader of the set it
+    # overwrites.  Both streams have the default priority.
+    dstream = torch.cuda.Stream(device=dev)
+    evq = {}
+    evd = {}
+
+    def step2(s):
+        st = sets[s % nset]
+        sd = sets[(s + nset // 2) % nset]
+        if s - nset // 2 in evd:
+            stream.wait_event(evd[s - nset // 2])
+        kvq.kvq_quantize_kv(ctx, st["k"], st["v"], B, Hkv, T, st["kc"], st["kn"], st["vc"], st["vn"])
+        evq[s] = torch.cuda.Event()
+        evq[s].record(stream)
+        if s - nset // 2 in evq:
+            dstream.wait_event(evq[s - nset // 2])
+        with torch.cuda.stream(dstream):
+            kvq.kvq_attn_decode(ctx, q, B, Hq, T, sd["kc"], sd["kn"], sd["vc"], sd["vn"], 0.0, out, ws)
+        evd[s] = torch.cuda.Event()
+        evd[s].record(dstream)
+
     for s in range(args.warmup):
-        step(s)
+        step2(s)
     torch.cuda.synchronize()
-    # The K timed steps carry no events of their own (each event is a command
-    # in the stream that separates the kernels).  A second pass of K steps,
+    # The K timed steps carry no timing events of their own (an event between
+    # the kernels would order them).  A second pass of K steps on one stream,
     # right after, brackets every launch with events on the launching stream
     # for the per-kernel durations of the roofline.
     t_start, t_end = E(), E()
     torch.cuda.synchronize()
     t_start.record(stream)
+    dstream.wait_event(t_start)
     for s in range(args.steps):
-        step(args.warmup + s)
+        step2(args.warmup + s)
+    done = torch.cuda.Event()
+    done.record(dstream)
+    stream.wait_event(done)
     t_end.record(stream)
     torch.cuda.synchronize()
     ms_step = t_start.elapsed_time(t_end) / args.steps
+    evq.clear()
+    evd.clear()
     evs = [[E() for _ in range(3)] for _ in range(args.steps)]
     for s in range(args.steps):
         step(args.warmup + args.steps + s, evs[s])
