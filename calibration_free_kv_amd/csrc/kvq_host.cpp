@@ -665,7 +665,7 @@ size_t kvq_attn_decode_stream_ws_bytes(const kvq_ctx *ctx, int64_t B, int64_t H_
     if (!ctx || B < 1 || T_cap < 0 || H_q < 1) return 0;
     const int64_t bhs = B * ctx->H;
     const int64_t slots = (T_cap > 0 ? kvq::decode_max_splits(T_cap) : 0) + 1;  // splits + the window's slot
-    return ((bhs * sizeof(unsigned) + 255) / 256) * 256 + (size_t)(B * H_q) * (size_t)slots * (kvq::kD + 2) * 4;
+    return kvq::decode_count_bytes(bhs) + (size_t)(B * H_q) * (size_t)slots * (kvq::kD + 2) * 4;
 }
 
 kvq_status kvq_attn_decode_stream(kvq_ctx *ctx, const void *q_f16, int64_t B, int64_t H_q, int64_t T,

@@ -72,6 +72,12 @@ inline int64_t decode_max_splits(int64_t T)
 }
 size_t decode_ws_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t T);
 int decode_auto_splits(int64_t B, int64_t Hkv, int64_t T);
+// Arrival counters at the start of a decode workspace: one u32 per (batch,
+// KV head), rounded up to 256 bytes.
+size_t decode_count_bytes(int64_t B_Hkv);
+// The no-allocation scratch reserves a fixed counter region, so that calls of
+// different shapes never find earlier partials where their counters lie.
+constexpr size_t kNoAllocCountBytes = 65536;
 
 hipError_t launch_decode(const kvq_ctx *ctx, const void *q, int64_t B, int64_t Hq, int64_t T,
                          const uint8_t *kc, const float *kn, const uint8_t *vc, const float *vn,

@@ -5,14 +5,16 @@
 
 namespace kvq {
 
-// Decode: arrival counters [B H_kv] (rounded up to 256 bytes), split partials
+size_t decode_count_bytes(int64_t B_Hkv) { return ((size_t)B_Hkv * sizeof(uint32_t) + 255) / 256 * 256; }
+
+// Decode: arrival counters [B H_kv] (decode_count_bytes), split partials
 // [B H_q][max splits][2 + 128] fp32, then the dense rotation's rotated
 // queries [B H_q][128] fp32.
 size_t decode_ws_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t T)
 {
     const int64_t bhs = B * Hkv;
     const int64_t max_split = decode_max_splits(T);
-    return ((bhs * sizeof(unsigned) + 255) / 256) * 256 +
+    return decode_count_bytes(bhs) +
            (size_t)(B * Hq) * (size_t)max_split * (kD + 2) * sizeof(float) + (size_t)(B * Hq) * kD * sizeof(float);
 }
 
@@ -26,11 +28,14 @@ int decode_auto_splits(int64_t B, int64_t Hkv, int64_t T)
     return (int)(ns < 1 ? 1 : ns);
 }
 
-// The same layout with exactly n_split partial slots per (batch, query head).
+// The no-allocation scratch: a fixed counter region (kNoAllocCountBytes),
+// then the layout above with exactly n_split partial slots per (batch, query
+// head); SIZE_MAX when the counters of B H_kv groups do not fit their region.
 size_t noalloc_decode_bytes(int64_t B, int64_t Hq, int64_t Hkv, int n_split, bool dense)
 {
     const int64_t bhs = B * Hkv;
-    return ((bhs * sizeof(unsigned) + 255) / 256) * 256 +
+    if (decode_count_bytes(bhs) > kNoAllocCountBytes) return SIZE_MAX;
+    return kNoAllocCountBytes +
            (size_t)(B * Hq) * (size_t)n_split * (kD + 2) * sizeof(float) +
            (dense ? (size_t)(B * Hq) * kD * sizeof(float) : 0);
 }

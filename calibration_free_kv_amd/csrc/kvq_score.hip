@@ -404,8 +404,9 @@ __device__ __forceinline__ uint32_t pack_h2(_Float16 a, _Float16 b)
 }
 
 // B operands of the logits for coordinates 32 kg + 8 CB .. + 7 of one token:
-// the four coordinate pairs of the lane's window, high and low parts.
-template <int BITS, int CB>
+// the four coordinate pairs of the lane's window, high and low parts (entry e
+// of the lane's copy of the pair tables at khi[KREP e], klo[KREP e]).
+template <int BITS, int CB, int KREP>
 __device__ __forceinline__ void key_operands(const uint32_t (&win)[BITS], const uint32_t *khi, const uint32_t *klo,
                                              u4_t &bh, u4_t &bl)
 {
@@ -414,29 +415,29 @@ __device__ __forceinline__ void key_operands(const uint32_t (&win)[BITS], const 
     const uint32_t e1 = window_bits<8 * BITS * CB + 1 * NB, NB>(win);
     const uint32_t e2 = window_bits<8 * BITS * CB + 2 * NB, NB>(win);
     const uint32_t e3 = window_bits<8 * BITS * CB + 3 * NB, NB>(win);
-    bh = u4_t{khi[e0], khi[e1], khi[e2], khi[e3]};
-    bl = u4_t{klo[e0], klo[e1], klo[e2], klo[e3]};
+    bh = u4_t{khi[KREP * e0], khi[KREP * e1], khi[KREP * e2], khi[KREP * e3]};
+    bl = u4_t{klo[KREP * e0], klo[KREP * e1], klo[KREP * e2], klo[KREP * e3]};
 }
 
 // Logit partial sums of one 16-token row group (tokens 16 rg + n) over the
 // 128 coordinates: eight products, the operands of each block looked up
 // while the previous block's products run.
-template <int BITS>
+template <int BITS, int KREP>
 __device__ __forceinline__ f4_t logit_group(const uint32_t (&win)[BITS], const uint32_t *khi, const uint32_t *klo,
                                             const h8_t (&aq)[4])
 {
     f4_t d = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
     u4_t h0, l0, h1, l1;
-    key_operands<BITS, 0>(win, khi, klo, h0, l0);
-    key_operands<BITS, 1>(win, khi, klo, h1, l1);
+    key_operands<BITS, 0, KREP>(win, khi, klo, h0, l0);
+    key_operands<BITS, 1, KREP>(win, khi, klo, h1, l1);
     __builtin_amdgcn_sched_barrier(0);
     d = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[0], __builtin_bit_cast(h8_t, h0), d, 0, 0, 0);
     d = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[0], __builtin_bit_cast(h8_t, l0), d, 0, 0, 0);
-    key_operands<BITS, 2>(win, khi, klo, h0, l0);
+    key_operands<BITS, 2, KREP>(win, khi, klo, h0, l0);
     __builtin_amdgcn_sched_barrier(0);
     d = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[1], __builtin_bit_cast(h8_t, h1), d, 0, 0, 0);
     d = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[1], __builtin_bit_cast(h8_t, l1), d, 0, 0, 0);
-    key_operands<BITS, 3>(win, khi, klo, h1, l1);
+    key_operands<BITS, 3, KREP>(win, khi, klo, h1, l1);
     __builtin_amdgcn_sched_barrier(0);
     d = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[2], __builtin_bit_cast(h8_t, h0), d, 0, 0, 0);
     d = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[2], __builtin_bit_cast(h8_t, l0), d, 0, 0, 0);
@@ -476,15 +477,23 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
     extern __shared__ __align__(16) float smem[];
     // centroid tables, fp16 high part in the low half of a dword and low part
     // in the high half where one code is looked up; for a coordinate pair,
-    // the high (khi) and low (klo) parts of both centroids.  klo lies 1040
-    // bytes past khi: no paired LDS read can reach both at one address
-    // (which would return a high and a low part in adjacent registers, to be
-    // moved apart again for the two products).
-    __shared__ uint32_t ktab[260 + SM::NP], vtab[1 << BITS];
-    static_assert(SM::NP <= 260, "pair table overlaps");
-    uint32_t *khi = ktab, *klo = ktab + 260;
+    // the high (khi) and low (klo) parts of both centroids.  For b <= 3 the
+    // pair tables hold one copy per LDS bank (entry e of copy c at dword
+    // 32 e + c) and lane l reads copy l mod 32 only, so the lanes' random
+    // lookups never meet in a bank (with one copy, 2^(2b) entries over 32
+    // banks cost about 2.5 conflict cycles per lookup at b = 3).  klo lies
+    // KLO dwords past khi: more than 1020 bytes and not a multiple of 256
+    // bytes, out of reach of the paired LDS reads (ds_read2 and its stride-64
+    // form), which would return a high and a low part in adjacent registers,
+    // to be moved apart again for the two products.  The 16-dword shift keeps
+    // the lanes of a copy in distinct banks.
+    constexpr int KREP = BITS <= 3 ? 32 : 1;
+    constexpr int KLO = BITS <= 3 ? (SM::NP * KREP > 256 ? SM::NP * KREP : 256) + 16 : 260;
+    static_assert(SM::NP * KREP <= KLO && KLO * 4 > 1020 && (KLO * 4) % 256 != 0, "pair table placement");
+    __shared__ uint32_t ktab[KLO + SM::NP * KREP], vtab[1 << BITS];
 
     const int tid = threadIdx.x, lane = tid & 63;
+    const uint32_t *khi = ktab + (KREP > 1 ? (lane & 31) : 0), *klo = khi + KLO;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int kg = lane >> 4, n = lane & 15;
     uint32_t *stg = reinterpret_cast<uint32_t *>(smem + SM::stage) + wv * SM::STG;
@@ -512,6 +521,23 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
         qs = reinterpret_cast<const f2_t *>(signs_k + g * kD)[lane];
     }
     if (tid == 0) *ready = 0u;
+    // The pair tables, all copies, before the barrier (the centroids are
+    // kernel arguments at constant offsets: scalar loads; a lane picks its
+    // two with selects rather than an indexed copy of the argument).
+    for (int i = tid; i < SM::NP * KREP; i += kDecThreads) {
+        const int e = i / KREP;
+        float ca = cb.c[0], cb2 = cb.c[0];
+#pragma unroll
+        for (int k = 1; k < (1 << BITS); ++k) {
+            ca = (e & (int)cm) == k ? cb.c[k] : ca;
+            cb2 = (e >> BITS) == k ? cb.c[k] : cb2;
+        }
+        _Float16 ha, la, hb, lb;
+        split_f16(ca, ha, la);
+        split_f16(cb2, hb, lb);
+        ktab[i] = pack_h2(ha, hb);
+        ktab[KLO + i] = pack_h2(la, lb);
+    }
     __syncthreads();
     // The records of the wave's next tile are held in registers: loaded before
     // the prologue for the first tile; for the others, the keys once the
@@ -571,8 +597,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
     float *ctab = smem + SM::ctab;
     float *qf = smem + SM::qf;
     _Float16 *qh = reinterpret_cast<_Float16 *>(smem + SM::qh);
-    // centroid tables: every wave writes the same values and reads back its
-    // own (the centroids are kernel arguments at constant offsets: scalar loads)
+    // value table: every wave writes the same values and reads back its own
     if (lane == 0) {
 #pragma unroll
         for (int k = 0; k < (1 << BITS); ++k) ctab[k] = cb.c[k];
@@ -581,13 +606,6 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
     for (int i = lane; i < 8 * SM::PS; i += 64) stg[SM::PT + i] = 0u;
     if (wv == 0) reinterpret_cast<uint32_t *>(qh + 2 * G * SM::QS)[lane] = 0u;  // the zero query row
     wave_lds_sync();
-    for (int e = lane; e < SM::NP; e += 64) {
-        _Float16 ha, la, hb, lb;
-        split_f16(ctab[e & cm], ha, la);
-        split_f16(ctab[e >> BITS], hb, lb);
-        khi[e] = pack_h2(ha, hb);
-        klo[e] = pack_h2(la, lb);
-    }
     if (lane < (1 << BITS)) {
         _Float16 h, l;
         split_f16(ctab[lane], h, l);
@@ -658,7 +676,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
         float s[4];
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
-            const f4_t d = logit_group<BITS>(Kw[rg], khi, klo, aq);
+            const f4_t d = logit_group<BITS, KREP>(Kw[rg], khi, klo, aq);
             s[rg] = d[0] + d[1];
         }
         float rkb[4], lvb[4];
@@ -1004,18 +1022,18 @@ __global__ __launch_bounds__(64 * kRotWaves) void k_rotate_dense(const half_t *_
     if (tid < kRotHeads * kD && h < heads) qrot[h * kD + tid % kD] = y * 11.313708498984761f;
 }
 
-// ws: arrival counters, then the split partials of `slots` slots per (batch,
-// query head), then (dense rotation) the rotated queries.
+// ws: arrival counters (cbytes), then the split partials of `slots` slots per
+// (batch, query head), then (dense rotation) the rotated queries.
 template <int BITS, int G>
 hipError_t run_decode(const kvq_ctx *ctx, const void *q, int64_t B, int64_t Hq, int64_t T, int64_t ldt,
                       const uint8_t *kc, const float *kn, const uint8_t *vc, const float *vn, const DecodeTail *tail,
-                      float sm_scale, float *out, void *ws, int n_split, int64_t slots, hipStream_t s)
+                      float sm_scale, float *out, void *ws, int n_split, int64_t slots, size_t cbytes, hipStream_t s)
 {
     using SM = DecSmem<BITS, G>;
     const int64_t bhs = B * ctx->H;
     const float scale_log2 = sm_scale * 1.4426950408889634f;
     unsigned *counters = (unsigned *)ws;
-    float *part = (float *)((char *)ws + ((bhs * sizeof(unsigned) + 255) / 256) * 256);
+    float *part = (float *)((char *)ws + cbytes);
     int n_part = 0;
     int64_t chunk = 0;
     if (T > 0) {
@@ -1074,12 +1092,12 @@ template <int BITS>
 hipError_t dispatch_decode(const kvq_ctx *ctx, int G, const void *q, int64_t B, int64_t Hq, int64_t T, int64_t ldt,
                            const uint8_t *kc, const float *kn, const uint8_t *vc, const float *vn,
                            const DecodeTail *tail, float sm, float *out, void *ws, int ns, int64_t slots,
-                           hipStream_t s)
+                           size_t cb, hipStream_t s)
 {
     switch (G) {
-    case 1: return run_decode<BITS, 1>(ctx, q, B, Hq, T, ldt, kc, kn, vc, vn, tail, sm, out, ws, ns, slots, s);
-    case 2: return run_decode<BITS, 2>(ctx, q, B, Hq, T, ldt, kc, kn, vc, vn, tail, sm, out, ws, ns, slots, s);
-    case 4: return run_decode<BITS, 4>(ctx, q, B, Hq, T, ldt, kc, kn, vc, vn, tail, sm, out, ws, ns, slots, s);
+    case 1: return run_decode<BITS, 1>(ctx, q, B, Hq, T, ldt, kc, kn, vc, vn, tail, sm, out, ws, ns, slots, cb, s);
+    case 2: return run_decode<BITS, 2>(ctx, q, B, Hq, T, ldt, kc, kn, vc, vn, tail, sm, out, ws, ns, slots, cb, s);
+    case 4: return run_decode<BITS, 4>(ctx, q, B, Hq, T, ldt, kc, kn, vc, vn, tail, sm, out, ws, ns, slots, cb, s);
     }
     return hipErrorNotSupported;
 }
@@ -1115,14 +1133,14 @@ hipError_t launch_logits(const kvq_ctx *ctx, const void *q, int64_t B, int64_t H
 namespace {
 hipError_t decode_bits(const kvq_ctx *ctx, const void *q, int64_t B, int64_t Hq, int64_t T, int64_t ldt,
                        const uint8_t *kc, const float *kn, const uint8_t *vc, const float *vn, const DecodeTail *tail,
-                       float sm, float *out, void *ws, int ns, int64_t slots, hipStream_t s)
+                       float sm, float *out, void *ws, int ns, int64_t slots, size_t cb, hipStream_t s)
 {
     const int G = (int)(Hq / ctx->H);
     switch (ctx->bits) {
-    case 1: return dispatch_decode<1>(ctx, G, q, B, Hq, T, ldt, kc, kn, vc, vn, tail, sm, out, ws, ns, slots, s);
-    case 2: return dispatch_decode<2>(ctx, G, q, B, Hq, T, ldt, kc, kn, vc, vn, tail, sm, out, ws, ns, slots, s);
-    case 3: return dispatch_decode<3>(ctx, G, q, B, Hq, T, ldt, kc, kn, vc, vn, tail, sm, out, ws, ns, slots, s);
-    case 4: return dispatch_decode<4>(ctx, G, q, B, Hq, T, ldt, kc, kn, vc, vn, tail, sm, out, ws, ns, slots, s);
+    case 1: return dispatch_decode<1>(ctx, G, q, B, Hq, T, ldt, kc, kn, vc, vn, tail, sm, out, ws, ns, slots, cb, s);
+    case 2: return dispatch_decode<2>(ctx, G, q, B, Hq, T, ldt, kc, kn, vc, vn, tail, sm, out, ws, ns, slots, cb, s);
+    case 3: return dispatch_decode<3>(ctx, G, q, B, Hq, T, ldt, kc, kn, vc, vn, tail, sm, out, ws, ns, slots, cb, s);
+    case 4: return dispatch_decode<4>(ctx, G, q, B, Hq, T, ldt, kc, kn, vc, vn, tail, sm, out, ws, ns, slots, cb, s);
     }
     return hipErrorInvalidValue;
 }
@@ -1133,7 +1151,7 @@ hipError_t launch_decode(const kvq_ctx *ctx, const void *q, int64_t B, int64_t H
                          float sm_scale, float *out, void *ws, int n_split, hipStream_t s)
 {
     return decode_bits(ctx, q, B, Hq, T, T, kc, kn, vc, vn, nullptr, sm_scale, out, ws, n_split,
-                       decode_max_splits(T), s);
+                       decode_max_splits(T), decode_count_bytes(B * ctx->H), s);
 }
 
 hipError_t launch_decode_stream(const kvq_ctx *ctx, const void *q, int64_t B, int64_t Hq, int64_t T, int64_t ldt,
@@ -1142,7 +1160,8 @@ hipError_t launch_decode_stream(const kvq_ctx *ctx, const void *q, int64_t B, in
                                 hipStream_t s)
 {
     // no dense rotation here, so nothing follows the partials
-    return decode_bits(ctx, q, B, Hq, T, ldt, kc, kn, vc, vn, tail, sm_scale, out, ws, n_split, 0, s);
+    return decode_bits(ctx, q, B, Hq, T, ldt, kc, kn, vc, vn, tail, sm_scale, out, ws, n_split, 0,
+                       decode_count_bytes(B * ctx->H), s);
 }
 
 hipError_t noalloc_setup(int device)
@@ -1174,7 +1193,8 @@ hipError_t launch_decode_noalloc(const kvq_ctx *ctx, const void *q, int64_t B, i
         if (ctx->device >= 0 && ctx->device < kMaxDevices) p = g_scratch[ctx->device];
     }
     if (!p) return hipErrorNotInitialized;  // kvq_create sets it up
-    return decode_bits(ctx, q, B, Hq, T, T, kc, kn, vc, vn, nullptr, sm_scale, out, p, n_split, n_split, s);
+    return decode_bits(ctx, q, B, Hq, T, T, kc, kn, vc, vn, nullptr, sm_scale, out, p, n_split, n_split,
+                       kNoAllocCountBytes, s);
 }
 
 }  // namespace kvq

@@ -227,8 +227,10 @@ size_t kvq_attn_decode_ws_bytes(const kvq_ctx *ctx, int64_t B, int64_t H_q, int6
  *   out         [B, H_q, d] fp32
  *   ws          device workspace of at least kvq_attn_decode_ws_bytes() bytes.
  *               Its counter words must be zero before the first call that
- *               uses it (e.g. allocate it zero-filled); every completed call
- *               leaves them zero again.  Calls that share a workspace must be
+ *               uses it (e.g. allocate it zero-filled), and again before a
+ *               call with a larger B * H_kv (its counters then reach into
+ *               the partials of the calls before); every completed call
+ *               leaves them zero.  Calls that share a workspace must be
  *               ordered on one stream.
  * T must be >= 1.  Errors: KVQ_E_WORKSPACE if ws_bytes is too small. */
 kvq_status kvq_attn_decode(kvq_ctx *ctx, const void *q_f16, int64_t B, int64_t H_q, int64_t T,
@@ -259,7 +261,7 @@ kvq_status kvq_attn_decode_splits(kvq_ctx *ctx, const void *q_f16, int64_t B, in
  * nothing and makes no synchronising call.  Arguments, layouts and results
  * are those of kvq_attn_decode (equal to it up to fp32 rounding of a
  * different split count).
- * Limit: the scratch must hold ceil(4 B H_kv / 256) * 256 bytes of counters,
+ * Limit: the scratch holds a fixed 64 KiB of counters (B H_kv up to 16384),
  * plus 520 bytes per (batch, query head) and token split, plus (dense
  * rotation) 512 bytes per (batch, query head).  The split count of
  * kvq_attn_decode is lowered until that fits; if even one split does not

@@ -195,7 +195,7 @@ int main()
         Buf qb(Bb * Hq * 256), ob(Bb * Hq * 512);
         st = kvq_attn_decode_noalloc(mse, qb.p, Bb, Hq, 100000, codes.as<uint8_t>(), norms.as<float>(), codes.as<uint8_t>(), norms.as<float>(), 0.f, ob.as<float>(), st0);
         CHECK(st == KVQ_OK);
-        const size_t need = ((Bb * H * 4 + 255) / 256) * 256 + (size_t)Bb * Hq * g_last.n_split * 520;
+        const size_t need = 65536 + (size_t)Bb * Hq * g_last.n_split * 520;
         CHECK(need <= KVQ_NOALLOC_SCRATCH_BYTES);
         CHECK(g_last.n_split >= 1);
     }
