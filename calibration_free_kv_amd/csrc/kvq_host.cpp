@@ -180,6 +180,7 @@ void free_ctx(kvq_ctx *c)
     (void)hipFree(c->d_vq16);
     (void)hipFree(c->d_vqbias);
     (void)hipFree(c->d_gsrq);
+    (void)hipFree(c->d_gsrq16);
     std::free(c->h_signs);
     delete c;
 }
@@ -430,6 +431,23 @@ kvq_status kvq_create(const kvq_config *cfg, kvq_ctx **out)
                 t[2 * kGsrqShape + 32 + 15 * k + l] = (float)(0.5 * ((double)G[l] + (double)G[l + 1]));
         }
         if (st == KVQ_OK) st = upload(&c->d_gsrq, t, n);
+        // the shapes as exact fp16 pairs (high part, rounding of the rest) for
+        // the matrix-core search: [part][stage][cw = 2 c + h][shape j][4], the
+        // four dims 8 c + 4 h .. + 3 of shape j (so that consecutive shapes'
+        // words of one (c, h) are adjacent)
+        _Float16 *t16 = st == KVQ_OK ? (_Float16 *)std::malloc(4 * kGsrqShape * sizeof(_Float16)) : nullptr;
+        if (st == KVQ_OK && !t16) st = KVQ_E_NOMEM;
+        for (size_t k = 0; st == KVQ_OK && k < 2; ++k)
+            for (size_t j = 0; j < (size_t)kvq::kVqK; ++j)
+                for (size_t d = 0; d < 32; ++d) {
+                    const float v = t[k * kGsrqShape + j * 32 + d];
+                    const _Float16 hi = (_Float16)v;
+                    const size_t cw = d / 4, at = ((k * 8 + cw) * kvq::kVqK + j) * 4 + d % 4;
+                    t16[at] = hi;
+                    t16[2 * kGsrqShape + at] = (_Float16)(v - (float)hi);
+                }
+        if (st == KVQ_OK) st = upload(&c->d_gsrq16, t16, 4 * kGsrqShape);
+        std::free(t16);
         std::free(t);
     }
     if (st == KVQ_OK && cfg->rotation == KVQ_ROTATION_DENSE) {

@@ -48,6 +48,7 @@ struct kvq_ctx {
     bool vq_exact_f16;    // codebook lo == 0
     float *d_vqbias;      // [256] -||C_j||^2 / 2
     float *d_gsrq;        // GSRQ tables: shapes [2][256][32], levels [2][16], thresholds [2][15]
+    _Float16 *d_gsrq16;   // GSRQ shapes as fp16 high parts [2][256][32], then low parts [2][256][32]
 };
 
 namespace kvq {

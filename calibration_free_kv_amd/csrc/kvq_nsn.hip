@@ -399,6 +399,94 @@ __device__ __forceinline__ int other_half_i(int x, bool upper)
     return __builtin_bit_cast(int, other_half(__builtin_bit_cast(float, x), upper));
 }
 
+// The NSN transform of a tile row held by lane 32 h + v (half h of token v,
+// w = its 64 fp16 coordinates as pairs; oL = the same 64 channel means):
+// a = sqrt(d) x / ||x|| (||x||^2 summed as norm2_f16 does, so that a is
+// rounded exactly as in the statistics pass), b = a - o, then six butterfly
+// stages inside the lane and the stride-64 stage across the halves.  Out:
+// nx = ||x||, nb = ||b|| and z = H b / ||b||, whose sub-vector s (dims
+// 8 s .. 8 s + 7) this half holds as dims 4 h .. 4 h + 3 in zh[s] (fp16 high
+// parts) and zl[s] (the fp16 rounding of the rest).
+__device__ __forceinline__ void nsn_z(const uint32_t (&w)[32], const f4_t *oL, float &nx, float &nb, u2_t (&zh)[16],
+                                      u2_t (&zl)[16])
+{
+    // ||x||^2: this half's chain, then (half 0) + (half 1) as norm2_f16
+    float ss = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+        const h2_t p = __builtin_bit_cast(h2_t, w[k]);
+        ss = __builtin_amdgcn_fdot2(p, p, ss, false);
+    }
+    {
+        float p = ss, q = ss;
+        swap_halves(p, q);
+        ss = p + q;
+    }
+    nx = __builtin_sqrtf(ss);
+    const float inv = ss > 0.0f ? kSqrtD / nx : 0.0f;
+    float y[64];
+    {
+        // a_t is rounded as in the stats pass before o is subtracted, so
+        // a single token (o = a_t) gives b = 0 exactly
+#pragma clang fp contract(off)
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const f4_t ov = oL[k];
+            const h2_t p0 = __builtin_bit_cast(h2_t, w[2 * k]), p1 = __builtin_bit_cast(h2_t, w[2 * k + 1]);
+            y[4 * k] = (float)p0.x * inv - ov.x;
+            y[4 * k + 1] = (float)p0.y * inv - ov.y;
+            y[4 * k + 2] = (float)p1.x * inv - ov.z;
+            y[4 * k + 3] = (float)p1.y * inv - ov.w;
+        }
+    }
+    float nb2 = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 64; ++k) nb2 = fmaf(y[k], y[k], nb2);
+    {
+        float p = nb2, q = nb2;
+        swap_halves(p, q);
+        nb2 = p + q;
+    }
+#pragma unroll
+    for (int st = 1; st < 64; st <<= 1) {
+#pragma unroll
+        for (int i = 0; i < 64; i += 2 * st) {
+#pragma unroll
+            for (int j = i; j < i + st; ++j) {
+                const float p0 = y[j], p1 = y[j + st];
+                y[j] = p0 + p1;
+                y[j + st] = p0 - p1;
+            }
+        }
+    }
+    // stride-64 stage: register p = 8t + k (k < 4) with q = p + 4
+#pragma unroll
+    for (int p = 0; p < 64; ++p) {
+        if ((p & 4) != 0) continue;
+        float x0 = y[p], x1 = y[p + 4];
+        swap_halves(x0, x1);
+        y[p] = x0 + x1;
+        y[p + 4] = x0 - x1;
+    }
+    nb = __builtin_sqrtf(nb2);
+    const float invb = nb2 > 0.0f ? 1.0f / nb : 0.0f;
+    // z = H b / ||b||: this half's four dims of each sub-vector as exact
+    // fp16 hi + lo
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+        const int base = 8 * (s & 7) + 4 * (s >> 3);
+        h4_t hv, lv;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            _Float16 lo;
+            hv[j] = split_f16(y[base + j] * invb, lo);
+            lv[j] = lo;
+        }
+        zh[s] = __builtin_bit_cast(u2_t, hv);
+        zl[s] = __builtin_bit_cast(u2_t, lv);
+    }
+}
+
 // ADAPT: the adaptive scale (NSNQuant, Metodologia sec. 3, "Ajuste de
 // Escala"): s2 is stored as alpha s2 with alpha = ||z||^2 / <z, zq> = d /
 // <z, zq> (zq the selected entries; alpha = 1 when <z, zq> <= 0), so that the
@@ -461,84 +549,11 @@ __global__ __launch_bounds__(kWavesN * 64) __attribute__((amdgpu_waves_per_eu(2,
         const int nv = (int)min((int64_t)kTileN, T - t0);
         const int64_t v0 = hh * ldt + t0;
 
-        // ||x||^2: this half's chain, then (half 0) + (half 1) as norm2_f16
-        float ss = 0.0f;
-#pragma unroll
-        for (int k = 0; k < 32; ++k) {
-            const h2_t p = __builtin_bit_cast(h2_t, w[k]);
-            ss = __builtin_amdgcn_fdot2(p, p, ss, false);
-        }
-        {
-            float p = ss, q = ss;
-            swap_halves(p, q);
-            ss = p + q;
-        }
-        const float nx = __builtin_sqrtf(ss);
-        const float inv = ss > 0.0f ? kSqrtD / nx : 0.0f;
         // this half's 64 means (the slot the copy of the next tile does not write)
         const f4_t *oL = reinterpret_cast<const f4_t *>(L + kRowsN + 32 * (ord & 1)) + 16 * h;
-        float y[64];
-        {
-            // a_t is rounded as in the stats pass before o is subtracted, so
-            // a single token (o = a_t) gives b = 0 exactly
-#pragma clang fp contract(off)
-#pragma unroll
-            for (int k = 0; k < 16; ++k) {
-                const f4_t ov = oL[k];
-                const h2_t p0 = __builtin_bit_cast(h2_t, w[2 * k]), p1 = __builtin_bit_cast(h2_t, w[2 * k + 1]);
-                y[4 * k] = (float)p0.x * inv - ov.x;
-                y[4 * k + 1] = (float)p0.y * inv - ov.y;
-                y[4 * k + 2] = (float)p1.x * inv - ov.z;
-                y[4 * k + 3] = (float)p1.y * inv - ov.w;
-            }
-        }
-        float nb2 = 0.0f;
-#pragma unroll
-        for (int k = 0; k < 64; ++k) nb2 = fmaf(y[k], y[k], nb2);
-        {
-            float p = nb2, q = nb2;
-            swap_halves(p, q);
-            nb2 = p + q;
-        }
-#pragma unroll
-        for (int st = 1; st < 64; st <<= 1) {
-#pragma unroll
-            for (int i = 0; i < 64; i += 2 * st) {
-#pragma unroll
-                for (int j = i; j < i + st; ++j) {
-                    const float p0 = y[j], p1 = y[j + st];
-                    y[j] = p0 + p1;
-                    y[j + st] = p0 - p1;
-                }
-            }
-        }
-        // stride-64 stage: register p = 8t + k (k < 4) with q = p + 4
-#pragma unroll
-        for (int p = 0; p < 64; ++p) {
-            if ((p & 4) != 0) continue;
-            float x0 = y[p], x1 = y[p + 4];
-            swap_halves(x0, x1);
-            y[p] = x0 + x1;
-            y[p + 4] = x0 - x1;
-        }
-        const float nb = __builtin_sqrtf(nb2);
-        const float invb = nb2 > 0.0f ? 1.0f / nb : 0.0f;
-        // z = H b / ||b||: this half's four dims of each sub-vector as exact
-        // fp16 hi + lo
+        float nx, nb;
         u2_t zh[16], zl[16];
-#pragma unroll
-        for (int s = 0; s < 16; ++s) {
-            const int base = 8 * (s & 7) + 4 * (s >> 3);
-            h4_t hv, lv;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                _Float16 lo;
-                hv[j] = split_f16(y[base + j] * invb, lo);
-                lv[j] = lo;
-            }
-            zh[s] = __builtin_bit_cast(u2_t, hv);
-            zl[s] = __builtin_bit_cast(u2_t, lv);
-        }
+        nsn_z(w, oL, nx, nb, zh, zl);
 
         float bm[16];
         int bg[16];
@@ -678,164 +693,237 @@ __global__ __launch_bounds__(kWavesN * 64) __attribute__((amdgpu_waves_per_eu(2,
 // shape indices (byte s = sub-vector s), dword 1 = the stage-2 ones, dword 2
 // = the four gain bytes c1 | c2 << 4.
 //
-// Block of 256 threads = 64 tokens of one head, four lanes per token (lane
-// 4 t + s holds coordinates [32 s, 32 s + 32)).  The Walsh-Hadamard transform
-// is H32 inside the lane and the two cross-quarter stages with lane
-// exchanges (H128 = H4 x H32 in the Sylvester order).  Every lane of a wave
-// scores the same shape at the same time, so the shapes are read as
-// wave-uniform loads (scalar cache) and each score is 32 FMAs with a scalar
-// operand.
+// The projections are a dense contraction (per stage, 32 tokens x 256 shapes
+// x 32 dims for each sub-vector) and run on the matrix cores, in the layout
+// of the NSN-VQ search: tiles of 32 tokens, lane 32 h + v holding dims
+// 4 h .. 4 h + 3 of every 8-dim chunk of token v's z (nsn_z), the MFMA rows
+// being 32 shapes and the columns the tokens.  Per (block of 32 shapes,
+// sub-vector S) the four chunks c of S each take one v_mfma_f32_32x32x16_f16,
+// S_hi . (z_hi + z_lo) (the A operand holds the lane's four shape dims
+// twice), and each pair of chunks one more for S_lo . z_hi (the A operand
+// holds the lane's dims of both chunks): the projection to about 2^-22
+// relative, as an fp32 dot product.  (A v_mfma_f32_32x32x8_f16 per chunk for
+// S_lo . z_hi takes as many cycles as the 32x32x16 form.)  A lane then holds 16 scores
+// of its token, register 4 q + e being shape 32 mb + 8 q + 4 h + e.  Each
+// group of four (fixed q) is reduced with its position e marked in the two
+// low mantissa bits (3 - e, a change of at most 3 units in the last place,
+// far inside the 1e-5 decision band), and the groups are compared exactly in
+// increasing shape order (strictly greater wins); the two halves' winners are
+// compared last (lower index on a tie).  The gain index is a binary search
+// over the 15 thresholds; the stage-2 input is r = z - level x shape in fp32,
+// split again into fp16 high and low parts.
 struct GsrqArgs {
-    const _Float16 *x;      // [H][T][128]
-    const float *o;         // [H][128] channel means
-    const float *shapes;    // [2][256][32]
+    const u4_t *x;          // [H][T][128] fp16
+    const u2_t *shapes16;   // [part hi, lo][stage][cw][256]: u2 word = dims 8 c + 4 h .. + 3 of a shape, cw = 2 c + h
     const float *levels;    // [2][16] gain levels, then [2][15] thresholds
     uint32_t *codes;        // [H][T][3]
     float *s1, *s2;         // [H][T]
 };
 constexpr int kGsrqM = 32, kGsrqK = 256, kGsrqL = 16;
+constexpr int kGsrqShapeU2 = kGsrqK * kGsrqM / 4;  // u2 words (four fp16) per stage table
 
-__device__ __forceinline__ void fwht32(float (&v)[kGsrqM])
+// One stage for the wave's 32 tokens: zh/zl the sub-vectors (as nsn_z leaves
+// them), sh/sl the stage's shape table in LDS (u2 word 256 (2 c + h) + j =
+// dims 8 c + 4 h .. + 3 of shape j, so that the 32 lanes of a half read 32
+// consecutive words: no bank conflicts).  Out, per sub-vector S: the shape
+// index and its (marked) projection, the same in both halves.
+__device__ __forceinline__ void gsrq_search(const u2_t *sh, const u2_t *sl, const u2_t (&zh)[16],
+                                            const u2_t (&zl)[16], int v, int h, bool upper, int (&jb)[4],
+                                            float (&pb)[4])
 {
+    float bm[4];
+    int bg[4];
 #pragma unroll
-    for (int len = 1; len < kGsrqM; len <<= 1)
+    for (int S = 0; S < 4; ++S) {
+        bm[S] = -INFINITY;
+        bg[S] = 0;
+    }
+#pragma unroll 1
+    for (int mb = 0; mb < kGsrqK / 32; ++mb) {
+        const u2_t *rh = sh + 256 * h + 32 * mb + v, *rl = sl + 256 * h + 32 * mb + v;
+        f16v_t acc[4];
 #pragma unroll
-        for (int i = 0; i < kGsrqM; ++i)
-            if (!(i & len)) {
-                const float a = v[i], b = v[i + len];
-                v[i] = a + b;
-                v[i + len] = a - b;
+        for (int S = 0; S < 4; ++S) acc[S] = f16v_t{};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const u2_t ah = rh[512 * c];
+            const h8_t A16 = __builtin_bit_cast(h8_t, u4_t{ah.x, ah.y, ah.x, ah.y});
+#pragma unroll
+            for (int S = 0; S < 4; ++S) {
+                const int s = 4 * S + c;
+                const h8_t B16 = __builtin_bit_cast(h8_t, u4_t{zh[s].x, zh[s].y, zl[s].x, zl[s].y});
+                acc[S] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A16, B16, acc[S], 0, 0, 0);
             }
-}
-
-// One stage on the residual r: shape index, gain index; r -= level x shape.
-__device__ __forceinline__ void gsrq_stage(float (&r)[kGsrqM], const float *__restrict__ S, const float *lv,
-                                           const float *th, int &j_out, int &c_out)
-{
-    float best = -__builtin_inff();
-    int jb = 0;
-    for (int j = 0; j < kGsrqK; ++j) {
-        const float *Sj = S + j * kGsrqM;  // wave-uniform
-        float p = 0.0f;
+            if (c & 1) {  // S_lo . z_hi for chunks c - 1 and c
+                const u2_t l0 = rl[512 * (c - 1)], l1 = rl[512 * c];
+                const h8_t AL = __builtin_bit_cast(h8_t, u4_t{l0.x, l0.y, l1.x, l1.y});
 #pragma unroll
-        for (int k = 0; k < kGsrqM; ++k) p = fmaf(r[k], Sj[k], p);
-        if (p > best) {
-            best = p;
-            jb = j;
+                for (int S = 0; S < 4; ++S) {
+                    const int s = 4 * S + c;
+                    const h8_t BL = __builtin_bit_cast(h8_t, u4_t{zh[s - 1].x, zh[s - 1].y, zh[s].x, zh[s].y});
+                    acc[S] = __builtin_amdgcn_mfma_f32_32x32x16_f16(AL, BL, acc[S], 0, 0, 0);
+                }
+            }
+        }
+#pragma unroll
+        for (int S = 0; S < 4; ++S) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float e[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    // the element is copied out first: a bit cast applied to
+                    // a vector element directly reads element 0
+                    const float x = acc[S][4 * q + k];
+                    e[k] = __builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, x) & ~3u) | (3u - (uint32_t)k));
+                }
+                const float m = fmaxf(fmaxf(fmaxf(e[0], e[1]), e[2]), e[3]);
+                const bool better = m > bm[S];
+                bm[S] = better ? m : bm[S];
+                bg[S] = better ? 4 * mb + q : bg[S];
+            }
         }
     }
-    int c = 0;
 #pragma unroll
-    for (int l = 0; l < kGsrqL - 1; ++l) c += th[l] < best ? 1 : 0;
-    const float g = lv[c];
-    const f4_t *Sb = reinterpret_cast<const f4_t *>(S + jb * kGsrqM);
-#pragma unroll
-    for (int k4 = 0; k4 < kGsrqM / 4; ++k4) {
-        const f4_t sv = Sb[k4];
-        r[4 * k4] = fmaf(-g, sv.x, r[4 * k4]);
-        r[4 * k4 + 1] = fmaf(-g, sv.y, r[4 * k4 + 1]);
-        r[4 * k4 + 2] = fmaf(-g, sv.z, r[4 * k4 + 2]);
-        r[4 * k4 + 3] = fmaf(-g, sv.w, r[4 * k4 + 3]);
+    for (int S = 0; S < 4; ++S) {
+        const int e = 3 - (int)(__builtin_bit_cast(uint32_t, bm[S]) & 3u);
+        const int idx = 8 * bg[S] + 4 * h + e;  // 32 mb + 8 q + 4 h + e with bg = 4 mb + q
+        const float ob = other_half(bm[S], upper);
+        const int oi = other_half_i(idx, upper);
+        const bool other = ob > bm[S] || (ob == bm[S] && oi < idx);
+        jb[S] = other ? oi : idx;
+        pb[S] = other ? ob : bm[S];
     }
-    j_out = jb;
-    c_out = c;
 }
 
-__global__ __launch_bounds__(256) void k_gsrq_encode(GsrqArgs a, int64_t T, int64_t tiles_per_h)
+// number of the 15 ascending thresholds th below p
+__device__ __forceinline__ int gsrq_gain(const float *th, float p)
 {
-    __shared__ float tab[2 * kGsrqL + 2 * (kGsrqL - 1)];
-    if (threadIdx.x < 2 * kGsrqL + 2 * (kGsrqL - 1)) tab[threadIdx.x] = a.levels[threadIdx.x];
+    int c = th[7] < p ? 8 : 0;
+    c += th[c + 3] < p ? 4 : 0;
+    c += th[c + 1] < p ? 2 : 0;
+    c += th[c] < p ? 1 : 0;
+    return c;
+}
+
+// (3) the search, with the tile loop of k_nsn_vq (one workgroup of 8 waves
+// per CU claiming 32-token tiles from an LDS counter; tiles copied straight
+// into LDS with the head's means).  The block first stages both stages'
+// shape tables (fp16 high and low parts, 64 KiB), the levels and thresholds.
+__global__ __launch_bounds__(kWavesN * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gsrq_vq(
+    GsrqArgs a, const float *__restrict__ o, int64_t T, int64_t tiles_per_h, int64_t n_tiles)
+{
+    __shared__ u2_t s_sh[2 * 2 * kGsrqShapeU2];  // [part hi, lo][stage][256][8]
+    __shared__ float s_tab[2 * kGsrqL + 2 * (kGsrqL - 1)];
+    __shared__ u4_t lds[kWavesN][kBufN];
+    __shared__ int next_tile;
+    const int tid = threadIdx.x;
+    {
+        const u4_t *src = reinterpret_cast<const u4_t *>(a.shapes16);
+        u4_t *dst = reinterpret_cast<u4_t *>(s_sh);
+        for (int i = tid; i < 2 * kGsrqShapeU2; i += kWavesN * 64) dst[i] = src[i];
+        if (tid < 2 * kGsrqL + 2 * (kGsrqL - 1)) s_tab[tid] = a.levels[tid];
+    }
+    if (tid == 0) next_tile = kWavesN;
     __syncthreads();
-    const int64_t tile = blockIdx.x;
-    const int64_t h = tile / tiles_per_h, t0 = (tile - h * tiles_per_h) * 64;
-    const int s = threadIdx.x & 3;
-    const int64_t t = t0 + (threadIdx.x >> 2);
-    const bool valid = t < T;
-    const int64_t tt = valid ? t : t0;  // lanes past the end re-read a valid token and store nothing
-    const u4_t *xp = reinterpret_cast<const u4_t *>(a.x + (h * T + tt) * kD + kGsrqM * s);
-    uint32_t xw[kGsrqM / 2];
+
+    const int lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    u4_t *L = lds[wv];
+    const int v = lane & 31, h = lane >> 5;
+    const bool upper = h != 0;
+    const int64_t G = gridDim.x;
+    int64_t tile = blockIdx.x + wv * G;
+    if (tile >= n_tiles) return;  // wave-uniform
+    auto issue = [&](int64_t t, int slot) {
+        int64_t tph = tiles_per_h;
+        asm volatile("" : "+s"(tph));
+        const int64_t hq = t / tph;
+        const int64_t tq = (t - hq * tph) * kTileN;
+        const int nq = (int)min((int64_t)kTileN, T - tq);
+        nsn_tile_to_lds(a.x + (hq * T + tq) * 16, nq, o + hq * kD, L, L + kRowsN + 32 * slot, lane);
+    };
+    const u2_t *sh1 = s_sh, *sh2 = s_sh + kGsrqShapeU2;
+    const u2_t *sl1 = s_sh + 2 * kGsrqShapeU2, *sl2 = s_sh + 3 * kGsrqShapeU2;
+    const float *lv1 = s_tab, *lv2 = s_tab + kGsrqL;
+    const float *th1 = s_tab + 2 * kGsrqL, *th2 = th1 + (kGsrqL - 1);
+    uint32_t w[32];
+    int ord = 0;  // ordinal of the current tile among this wave's: its means are in slot ord % 2
+    issue(tile, 0);
+    int64_t next = blockIdx.x + nsn_take_rows(L, lane, w, &next_tile) * G;
+    if (next < n_tiles) issue(next, 1);
+    for (;;) {
+        int64_t tph = tiles_per_h;
+        asm volatile("" : "+s"(tph));
+        const int64_t hh = tile / tph;
+        const int64_t t0 = (tile - hh * tph) * kTileN;
+        const int nv = (int)min((int64_t)kTileN, T - t0);
+
+        const f4_t *oL = reinterpret_cast<const f4_t *>(L + kRowsN + 32 * (ord & 1)) + 16 * h;
+        float nx, nb;
+        u2_t zh[16], zl[16];
+        nsn_z(w, oL, nx, nb, zh, zl);
+
+        int j1[4], j2[4], c1[4], c2[4];
+        float p[4];
+        gsrq_search(sh1, sl1, zh, zl, v, h, upper, j1, p);
+        // stage-2 input: r = z - G1[c1] S1[j1] in fp32 (z and the shape from
+        // their exact fp16 parts), split again into high and low parts
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const u4_t w = xp[i];
-        xw[4 * i] = w.x;
-        xw[4 * i + 1] = w.y;
-        xw[4 * i + 2] = w.z;
-        xw[4 * i + 3] = w.w;
-    }
-    // ||x||^2 exactly as the statistics pass forms it (norm2_f16: one chain of
-    // packed dot products over each half, then their sum), so that a_t is
-    // rounded identically and a single token gives b = 0: quarter 2 h + 1
-    // continues the chain of quarter 2 h.
-    float ch = 0.0f;
+        for (int S = 0; S < 4; ++S) {
+            c1[S] = gsrq_gain(th1, p[S]);
+            const float g = lv1[c1[S]];
+            const u2_t *ch = sh1 + 256 * h + j1[S], *cl = sl1 + 256 * h + j1[S];
 #pragma unroll
-    for (int k = 0; k < kGsrqM / 2; ++k) {
-        const h2_t p = __builtin_bit_cast(h2_t, xw[k]);
-        ch = __builtin_amdgcn_fdot2(p, p, ch, false);
-    }
-    float half = __shfl_xor(ch, 1);  // odd quarters: the chain of the quarter before
+            for (int c = 0; c < 4; ++c) {
+                const int s = 4 * S + c;
+                const h4_t zhv = __builtin_bit_cast(h4_t, zh[s]), zlv = __builtin_bit_cast(h4_t, zl[s]);
+                const h4_t shv = __builtin_bit_cast(h4_t, ch[512 * c]), slv = __builtin_bit_cast(h4_t, cl[512 * c]);
+                h4_t rh, rl;
 #pragma unroll
-    for (int k = 0; k < kGsrqM / 2; ++k) {
-        const h2_t p = __builtin_bit_cast(h2_t, xw[k]);
-        half = __builtin_amdgcn_fdot2(p, p, half, false);
-    }
-    // quarters 1 and 3 hold the two half sums; every lane gets their sum
-    const float nb_half = __shfl_xor(half, 1);  // exchanged by every lane
-    const float hs = (s & 1) ? half : nb_half;
-    const float ss = hs + __shfl_xor(hs, 2);
-    const float nx = __builtin_sqrtf(ss);
-    const float inv = ss > 0.0f ? kSqrtD / nx : 0.0f;
-    // b = a - o (a rounded before the subtraction, as in the statistics
-    // pass), s2 = ||b|| / sqrt(d), x~ = b / s2
-    const float *oh = a.o + h * kD + kGsrqM * s;
-    float v[kGsrqM];
-    float bb = 0.0f;
-#pragma unroll
-    for (int k = 0; k < kGsrqM / 2; ++k) {
-#pragma clang fp contract(off)
-        const h2_t p = __builtin_bit_cast(h2_t, xw[k]);
-        const float a0 = (float)p.x * inv, a1 = (float)p.y * inv;
-        v[2 * k] = a0 - oh[2 * k];
-        v[2 * k + 1] = a1 - oh[2 * k + 1];
-    }
-#pragma unroll
-    for (int k = 0; k < kGsrqM; ++k) bb = fmaf(v[k], v[k], bb);
-    bb += __shfl_xor(bb, 1);
-    bb += __shfl_xor(bb, 2);
-    const float nb = __builtin_sqrtf(bb);
-    const float sc = bb > 0.0f ? kSqrtD / nb : 0.0f;
-#pragma unroll
-    for (int k = 0; k < kGsrqM; ++k) v[k] *= sc;
-    // z = H x~ / sqrt(d): H32 in the lane, then the quarter bits
-    fwht32(v);
-#pragma unroll
-    for (int bit = 1; bit < 4; bit <<= 1) {
-        const bool up = (s & bit) != 0;
-#pragma unroll
-        for (int k = 0; k < kGsrqM; ++k) {
-            const float p = __shfl_xor(v[k], bit);
-            v[k] = up ? p - v[k] : v[k] + p;
+                for (int k = 0; k < 4; ++k) {
+                    const float zf = (float)zhv[k] + (float)zlv[k];
+                    const float sf = (float)shv[k] + (float)slv[k];
+                    _Float16 lo;
+                    rh[k] = split_f16(fmaf(-g, sf, zf), lo);
+                    rl[k] = lo;
+                }
+                zh[s] = __builtin_bit_cast(u2_t, rh);
+                zl[s] = __builtin_bit_cast(u2_t, rl);
+            }
         }
-    }
+        gsrq_search(sh2, sl2, zh, zl, v, h, upper, j2, p);
 #pragma unroll
-    for (int k = 0; k < kGsrqM; ++k) v[k] *= 1.0f / kSqrtD;
-    int j1, c1, j2, c2;
-    gsrq_stage(v, a.shapes, tab, tab + 2 * kGsrqL, j1, c1);
-    gsrq_stage(v, a.shapes + kGsrqK * kGsrqM, tab + kGsrqL, tab + 2 * kGsrqL + (kGsrqL - 1), j2, c2);
-    // the token's three dwords from its four lanes
-    uint32_t d0 = (uint32_t)j1 << (8 * s), d1 = (uint32_t)j2 << (8 * s), d2 = (uint32_t)(c1 | (c2 << 4)) << (8 * s);
-#pragma unroll
-    for (int m = 1; m < 4; m <<= 1) {
-        d0 |= __shfl_xor(d0, m);
-        d1 |= __shfl_xor(d1, m);
-        d2 |= __shfl_xor(d2, m);
-    }
-    if (valid) {
-        uint32_t *rec = a.codes + (h * T + t) * 3;
-        if (s < 3) rec[s] = s == 0 ? d0 : s == 1 ? d1 : d2;
-        if (s == 3) {
-            a.s1[h * T + t] = nx / kSqrtD;
-            a.s2[h * T + t] = nb / kSqrtD;
+        for (int S = 0; S < 4; ++S) c2[S] = gsrq_gain(th2, p[S]);
+
+        // The next tile's rows, then the copy of the tile after it, then this
+        // tile's stores.
+        const bool has_next = next < n_tiles;
+        int64_t after = n_tiles;
+        if (has_next) {
+            after = blockIdx.x + nsn_take_rows(L, lane, w, &next_tile) * G;
+            if (after < n_tiles) issue(after, ord & 1);  // the slot of this tile, no longer read
         }
+        if (!upper && v < nv) {  // lanes of tokens past a ragged tail searched stale rows
+            const int64_t t = hh * T + t0 + v;
+            uint32_t d0 = 0, d1 = 0, d2 = 0;
+#pragma unroll
+            for (int S = 0; S < 4; ++S) {
+                d0 |= (uint32_t)j1[S] << (8 * S);
+                d1 |= (uint32_t)j2[S] << (8 * S);
+                d2 |= (uint32_t)(c1[S] | (c2[S] << 4)) << (8 * S);
+            }
+            uint32_t *rec = a.codes + t * 3;
+            rec[0] = d0;
+            rec[1] = d1;
+            rec[2] = d2;
+            a.s1[t] = nx / kSqrtD;
+            a.s2[t] = nb / kSqrtD;
+        }
+        if (!has_next) break;
+        tile = next;
+        next = after;
+        ++ord;
     }
 }
 
@@ -910,7 +998,7 @@ hipError_t nsn_vq_run(const kvq_ctx *ctx, const void *x, int64_t H, int64_t T, i
 }
 }  // namespace
 
-// GSRQ: channel means by the NSN statistics pass, then the encoder.
+// GSRQ: channel means by the NSN statistics pass, then the search.
 hipError_t launch_gsrq(const kvq_ctx *ctx, const void *x, int64_t H, int64_t T, uint8_t *codes, float *s1, float *s2,
                        float *o, void *ws, hipStream_t s)
 {
@@ -921,15 +1009,18 @@ hipError_t launch_gsrq(const kvq_ctx *ctx, const void *x, int64_t H, int64_t T, 
     hipLaunchKernelGGL(k_nsn_mean, dim3((unsigned)H), dim3(kD * kMeanGroups), 0, s, part, o, T, n_chunks, (int64_t)kD,
                        (uint8_t *)nullptr, (float *)nullptr);
     GsrqArgs a{};
-    a.x = (const _Float16 *)x;
-    a.o = o;
-    a.shapes = ctx->d_gsrq;
+    a.x = (const u4_t *)x;
+    a.shapes16 = (const u2_t *)ctx->d_gsrq16;
     a.levels = ctx->d_gsrq + 2 * kGsrqK * kGsrqM;
     a.codes = (uint32_t *)codes;
     a.s1 = s1;
     a.s2 = s2;
-    const int64_t tph = (T + 63) / 64;
-    hipLaunchKernelGGL(k_gsrq_encode, dim3((unsigned)(H * tph)), dim3(256), 0, s, a, T, tph);
+    const int64_t tiles_per_h = (T + kTileN - 1) / kTileN;
+    const int64_t n_tiles = tiles_per_h * H;
+    int64_t blocks = n_tiles;
+    if (blocks > ctx->n_cu) blocks = ctx->n_cu;  // one workgroup per CU, each with at least one tile
+    hipLaunchKernelGGL(k_gsrq_vq, dim3((unsigned)blocks), dim3(kWavesN * 64), 0, s, a, (const float *)o, T, tiles_per_h,
+                       n_tiles);
     return hipGetLastError();
 }
 
