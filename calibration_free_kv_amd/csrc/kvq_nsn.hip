@@ -796,6 +796,30 @@ __device__ __forceinline__ void gsrq_search(const u2_t *sh, const u2_t *sl, cons
     }
 }
 
+// Mixed-precision FMAs on fp16 halves held in dwords (SEL: 0 = low half, 1 =
+// high half): h2f_sum = fp32 of the two fp16 (hi + lo, exact), and
+// fma_h = a * fp16 + c in fp32, each one v_fma_mix_f32.
+template <int SEL>
+__device__ __forceinline__ float h2f_sum(uint32_t hi, uint32_t lo)
+{
+    float r;
+    if constexpr (SEL == 0)
+        asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel:[0,0,0] op_sel_hi:[1,0,1]" : "=v"(r) : "v"(hi), "v"(lo));
+    else
+        asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel:[1,0,1] op_sel_hi:[1,0,1]" : "=v"(r) : "v"(hi), "v"(lo));
+    return r;
+}
+template <int SEL>
+__device__ __forceinline__ float fma_h(float a, uint32_t h, float c)
+{
+    float r;
+    if constexpr (SEL == 0)
+        asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[0,0,0] op_sel_hi:[0,1,0]" : "=v"(r) : "v"(a), "v"(h), "v"(c));
+    else
+        asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[0,1,0] op_sel_hi:[0,1,0]" : "=v"(r) : "v"(a), "v"(h), "v"(c));
+    return r;
+}
+
 // number of the 15 ascending thresholds th below p
 __device__ __forceinline__ int gsrq_gain(const float *th, float p)
 {
@@ -867,25 +891,30 @@ __global__ __launch_bounds__(kWavesN * 64) __attribute__((amdgpu_waves_per_eu(2,
         int j1[4], j2[4], c1[4], c2[4];
         float p[4];
         gsrq_search(sh1, sl1, zh, zl, v, h, upper, j1, p);
-        // stage-2 input: r = z - G1[c1] S1[j1] in fp32 (z and the shape from
-        // their exact fp16 parts), split again into high and low parts
+        // stage-2 input: r = (z - g S_hi) - g S_lo in fp32 (z from its exact
+        // fp16 parts), split again into high and low parts
 #pragma unroll
         for (int S = 0; S < 4; ++S) {
             c1[S] = gsrq_gain(th1, p[S]);
-            const float g = lv1[c1[S]];
+            const float ng = -lv1[c1[S]];
             const u2_t *ch = sh1 + 256 * h + j1[S], *cl = sl1 + 256 * h + j1[S];
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const int s = 4 * S + c;
-                const h4_t zhv = __builtin_bit_cast(h4_t, zh[s]), zlv = __builtin_bit_cast(h4_t, zl[s]);
-                const h4_t shv = __builtin_bit_cast(h4_t, ch[512 * c]), slv = __builtin_bit_cast(h4_t, cl[512 * c]);
+                const u2_t shw = ch[512 * c], slw = cl[512 * c];
+                float r[4];
+#pragma unroll
+                for (int d = 0; d < 2; ++d) {  // dword d: dims 2 d (low half), 2 d + 1 (high half)
+                    const uint32_t zhd = d ? zh[s].y : zh[s].x, zld = d ? zl[s].y : zl[s].x;
+                    const uint32_t shd = d ? shw.y : shw.x, sld = d ? slw.y : slw.x;
+                    r[2 * d] = fma_h<0>(ng, sld, fma_h<0>(ng, shd, h2f_sum<0>(zhd, zld)));
+                    r[2 * d + 1] = fma_h<1>(ng, sld, fma_h<1>(ng, shd, h2f_sum<1>(zhd, zld)));
+                }
                 h4_t rh, rl;
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
-                    const float zf = (float)zhv[k] + (float)zlv[k];
-                    const float sf = (float)shv[k] + (float)slv[k];
                     _Float16 lo;
-                    rh[k] = split_f16(fmaf(-g, sf, zf), lo);
+                    rh[k] = split_f16(r[k], lo);
                     rl[k] = lo;
                 }
                 zh[s] = __builtin_bit_cast(u2_t, rh);
