@@ -35,21 +35,6 @@ struct HalfThresholds {
     float p[8];  // positive thresholds t_{L/2}, ..., t_{L-2} (L/2 - 1 of them)
 };
 
-// fp16 pair -> fp32 (lo + hi) and (lo - hi) in one mixed-precision FMA each:
-// the first butterfly stage fused with the widening.
-__device__ __forceinline__ float pair_sum(uint32_t p)
-{
-    float r;
-    asm("v_fma_mix_f32 %0, %1, 1.0, %1 op_sel:[0,0,1] op_sel_hi:[1,0,1]" : "=v"(r) : "v"(p));
-    return r;
-}
-__device__ __forceinline__ float pair_diff(uint32_t p)
-{
-    float r;
-    asm("v_fma_mix_f32 %0, %1, 1.0, -%1 op_sel:[0,0,1] op_sel_hi:[1,0,1]" : "=v"(r) : "v"(p));
-    return r;
-}
-
 // acc = 2 * acc + (bit of this lane in the wave mask m): appends one bit to a
 // dword that is filled most-significant bit first.
 __device__ __forceinline__ uint32_t append_bit(uint32_t acc, uint64_t m)
@@ -567,68 +552,6 @@ struct StaticFor {
     }
 };
 
-// Tile of 32 keys for the QJL kernel, two lanes per key: lane 32h + v holds
-// coordinates [64 h, 64 h + 64) of key v (so that the residual can feed the
-// matrix cores straight from registers, see below).  Chunk c of row v sits at
-// LDS slot 16 v + ((c + v) mod 16): the 16 lanes of one half that read chunk
-// 8h + k of 16 consecutive rows hit 16 different bank groups.  Copy
-// instruction j writes slots [64 j, 64 j + 64) (rows 4j .. 4j+3, one
-// contiguous KiB of HBM); the chunk a lane fetches depends on j only through
-// j mod 4.  A ninth instruction copies the head's 64 sign-mask dwords.
-__device__ __forceinline__ void qjl_tile_to_lds(const u4_t *src, int nv, const uint32_t *msk, u4_t *L, int lane)
-{
-    asm volatile("" : "+v"(lane));
-    if (nv == kTileH) {
-        uint32_t off[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int v = 4 * r + (lane >> 4);
-            off[r] = (uint32_t)((lane >> 4) * 16 + (((lane & 15) - v) & 15));
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            __builtin_amdgcn_global_load_lds(
-                (const __attribute__((address_space(1))) void *)(src + 64 * j + off[j & 3]),
-                (__attribute__((address_space(3))) void *)(L + j * 64), 16, 0, 0);
-    } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int v = 4 * j + (lane >> 4);
-            const int row = v < nv ? v : nv - 1;
-            __builtin_amdgcn_global_load_lds(
-                (const __attribute__((address_space(1))) void *)(src + row * 16 + (((lane & 15) - v) & 15)),
-                (__attribute__((address_space(3))) void *)(L + j * 64), 16, 0, 0);
-        }
-    }
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(msk + lane),
-                                     (__attribute__((address_space(3))) void *)(L + kRowsH), 4, 0, 0);
-}
-
-// Wait for the tile copy, read half row h of key v into w (lane 32h + v),
-// apply D, and draw the wave's next ticket from the LDS counter (see
-// take_rows).
-__device__ __forceinline__ int qjl_take_rows(const u4_t *L, int lane, uint32_t *w, int *counter)
-{
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("" : "+v"(lane));
-    wait_vm_n<0>();
-    const int v = lane & 31, h = lane >> 5;
-    const u4_t *M = L + kRowsH + 8 * h;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        const u4_t x = L[16 * v + ((8 * h + k + v) & 15)];
-        const u4_t m = M[k];
-        w[4 * k + 0] = x.x ^ m.x;
-        w[4 * k + 1] = x.y ^ m.y;
-        w[4 * k + 2] = x.z ^ m.z;
-        w[4 * k + 3] = x.w ^ m.w;
-    }
-    int t = 0;
-    if (lane == 0) t = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    wait_lgkm();
-    __builtin_amdgcn_wave_barrier();
-    return __builtin_amdgcn_readfirstlane(t);
-}
 
 // Append the BITS-bit indices of 32 coordinates y[0..31] (LSB-first stream of
 // 32 BITS bits) to out[0 .. BITS), from the last bit backwards, and replace
@@ -665,13 +588,11 @@ __device__ __forceinline__ void encode32(float *y, const float *P, const float *
 
 // Quantise with the 1-bit QJL residual, one workgroup of 12 waves per CU
 // (three per SIMD), tiles of 32 keys claimed as in k_quantize.
-//  - MSE part: the rotation is an in-register Walsh-Hadamard butterfly
-//    network (six stages inside the lane; the lane pair of a key holds its
-//    two halves), whose stride-64 stage pairs lanes l and l ^ 32: one gfx950
-//    half swap of registers (i, i + 32) and an add and a subtract give
-//    coordinates i, i + 64 (lanes 0-31) and 32 + i, 96 + i (lanes 32-63).  So register r of half h holds coordinate
-//    C(h, r) = 32 h + r for r < 32 and 64 + 32 h + (r - 32) for r >= 32, and
-//    each half packs two runs of 32 coordinates.
+//  - MSE part: the tile is staged and rotated as in k_quantize (the 128 x 128
+//    x 32 product of the +-1 Hadamard blocks with the fp16 inputs on the
+//    matrix cores, then one lane swap per register pair), so that lane
+//    v + 32 h holds coordinates C(h, i) = 64 h + i, i < 64, of key v and
+//    packs them as two runs of 32.
 //  - e = y / rho - c[idx] per coordinate (the factor 1/sqrt(d) of r does not
 //    change a sign), gamma = ||e|| / sqrt(d); e is split exactly into fp16
 //    hi + lo (hi by round-toward-zero conversion, i.e. its 11 leading
@@ -679,9 +600,9 @@ __device__ __forceinline__ void encode32(float *y, const float *P, const float *
 //  - The projection S e of the 32 keys runs on v_mfma_f32_32x32x16_f16 with
 //    the A operand straight from registers: the contraction may visit the
 //    coordinates in any order as long as both operands agree, so k-step s
-//    takes, in lane half h, registers 8s .. 8s+7 (coordinates C(h, 8s) ..
-//    +7, contiguous), and the B operand reads the same coordinates of the
-//    rows of S staged in LDS.  Each accumulator register of a 32 x 32 block
+//    takes, in lane half h, coordinates C(h, 8s) .. +7 (chunk 8 h + s of the
+//    key), and the B operand reads the same coordinates of the rows of S
+//    staged in LDS.  Each accumulator register of a 32 x 32 block
 //    (rows = keys, columns = outputs) gives, with one ballot, two keys' 32
 //    sign bits of the block, which are written into the key's lane.
 constexpr int kWavesJ = 12;  // waves per workgroup of the QJL kernel
@@ -705,15 +626,16 @@ __global__ __launch_bounds__(kWavesJ * 64) __attribute__((amdgpu_waves_per_eu(3,
     if (tile >= n_tiles) return;  // wave-uniform
     auto issue = [&](int64_t t) {
         const TileGeom gg = geom<kTileH>((uint32_t)(t), mp);
-        qjl_tile_to_lds(a.x + gg.v0 * 16, gg.nv, sgn + gg.h * 64, L, lane);
+        tile_to_lds(a.x + gg.v0 * 16, gg.nv, sgn + gg.h * 64, L, lane);
     };
     const int v = lane & 31, h = lane >> 5;
     float Mg[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) Mg[k] = a.mags[k];
+    const h8_t F0 = hadamard_fragment(lane, 0), F1 = hadamard_fragment(lane, 1);
     uint32_t w[32];
     issue(tile);
-    int64_t next = blockIdx.x + qjl_take_rows(L, lane, w, &next_tile) * G;
+    int64_t next = blockIdx.x + take_rows<0>(L, lane, w, &next_tile) * G;
     if (next < n_tiles) issue(next);
     for (;;) {
         const TileGeom g = geom<kTileH>((uint32_t)(tile), mp);
@@ -723,37 +645,40 @@ __global__ __launch_bounds__(kWavesJ * 64) __attribute__((amdgpu_waves_per_eu(3,
             const h2_t p = __builtin_bit_cast(h2_t, w[k]);
             ss = __builtin_amdgcn_fdot2(p, p, ss, false);
         }
-        float y[64];
+        // y = H (D .* x) on the matrix cores, as in k_quantize
+        f16_t acc[4] = {};
 #pragma unroll
-        for (int k = 0; k < 32; ++k) {
-            y[2 * k] = pair_sum(w[k]);
-            y[2 * k + 1] = pair_diff(w[k]);
-        }
+        for (int s = 0; s < 8; ++s) {
+            const u4_t bp = u4_t{w[4 * s], w[4 * s + 1], w[4 * s + 2], w[4 * s + 3]};
+            const u4_t bn = bp ^ 0x80008000u;
+            const h8_t F = (s & 1) ? F1 : F0;
 #pragma unroll
-        for (int s = 2; s < 64; s <<= 1) {
-#pragma unroll
-            for (int i = 0; i < 64; i += 2 * s) {
-#pragma unroll
-                for (int j = i; j < i + s; ++j) {
-                    const float p = y[j], q = y[j + s];
-                    y[j] = p + q;
-                    y[j + s] = p - q;
-                }
+            for (int mb = 0; mb < 4; ++mb) {
+                const bool neg = __builtin_popcount(mb & (s >> 1)) & 1;
+                acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(F, __builtin_bit_cast(h8_t, neg ? bn : bp),
+                                                                 acc[mb], 0, 0, 0);
             }
-        }
-        // stride-64 stage across the halves
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-            float p = y[i], q = y[i + 32];
-            swap_halves(p, q);
-            y[i] = p + q;
-            y[i + 32] = p - q;
         }
         {
             float p = ss, q = ss;
             swap_halves(p, q);
             ss = p + q;  // the same sum in both halves
         }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float x0 = acc[0][r], x2 = acc[2][r];
+            swap_halves(x0, x2);
+            acc[0][r] = x0;
+            acc[2][r] = x2;
+            float x1 = acc[1][r], x3 = acc[3][r];
+            swap_halves(x1, x3);
+            acc[1][r] = x1;
+            acc[3][r] = x3;
+        }
+        // y[i] = coordinate 64 h + i = 32 a + 8 q + 4 f + e locally: block a + 2 f, register 4 q + e
+        float y[64];
+#pragma unroll
+        for (int i = 0; i < 64; ++i) y[i] = acc[(i >> 5) + 2 * ((i >> 2) & 1)][4 * ((i >> 3) & 3) + (i & 3)];
         const float rho = __builtin_sqrtf(ss);
         const float r = rho > 0.0f ? rho : 1.0f;
         const float inv = rho > 0.0f ? 1.0f / rho : 0.0f;
@@ -761,7 +686,7 @@ __global__ __launch_bounds__(kWavesJ * 64) __attribute__((amdgpu_waves_per_eu(3,
 #pragma unroll
         for (int k = 0; k < 8; ++k) P[k] = ht.p[k] * r;
 
-        // codes: run 0 = coordinates 32h .. 32h+31, run 1 = 64+32h .. 64+32h+31
+        // codes: run 0 = coordinates 64h .. 64h+31, run 1 = 64h+32 .. 64h+63
         uint32_t out[2 * BITS];
 #pragma unroll
         for (int k = 0; k < 2 * BITS; ++k) out[k] = 0u;
@@ -794,7 +719,7 @@ __global__ __launch_bounds__(kWavesJ * 64) __attribute__((amdgpu_waves_per_eu(3,
             const int n = 32 * nb + v;  // output row of S read by this lane
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
-                const int ch = (s < 4 ? s : s + 4) + 4 * h;  // 16-byte chunk of the coordinates C(h, 8s..8s+7)
+                const int ch = 8 * h + s;  // 16-byte chunk of the coordinates C(h, 8s..8s+7)
                 const h8_t B = __builtin_bit_cast(h8_t, Ss[swz(n, ch)]);
                 const h8_t Ah = __builtin_bit_cast(h8_t, u4_t{eh[4 * s], eh[4 * s + 1], eh[4 * s + 2], eh[4 * s + 3]});
                 const h8_t Al = __builtin_bit_cast(h8_t, u4_t{el[4 * s], el[4 * s + 1], el[4 * s + 2], el[4 * s + 3]});
@@ -822,17 +747,14 @@ __global__ __launch_bounds__(kWavesJ * 64) __attribute__((amdgpu_waves_per_eu(3,
         const bool has_next = next < n_tiles;
         int64_t after = n_tiles;
         if (has_next) {
-            after = blockIdx.x + qjl_take_rows(L, lane, w, &next_tile) * G;
+            after = blockIdx.x + take_rows<0>(L, lane, w, &next_tile) * G;
             if (after < n_tiles) issue(after);
         }
         if (v < g.nv) {  // lanes of keys past a ragged tail encoded stale rows
             const int64_t key = g.v0 + v;
             uint32_t *dst = reinterpret_cast<uint32_t *>(a.codes + key * BITS);
 #pragma unroll
-            for (int k = 0; k < BITS; ++k) {
-                dst[h * BITS + k] = out[k];
-                dst[(2 + h) * BITS + k] = out[BITS + k];
-            }
+            for (int k = 0; k < 2 * BITS; ++k) dst[2 * h * BITS + k] = out[k];
             if (h == 0) {
                 a.norms[key] = rho;
                 a.signs[key] = u4_t{sgnw[0], sgnw[1], sgnw[2], sgnw[3]};
