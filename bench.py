@@ -16,9 +16,11 @@ overwrites.
 value = (K and V vectors quantised + keys scored) per second of the whole step.
 roofline = the dominant kernel (kvq_quantize_kv): algorithmic bytes per launch
 (fp16 input, packed codes, fp32 norms) / mean launch duration from HIP events
-recorded on the stream the kernels run on, in a second pass of as many steps
-right after the timed ones (events between the kernels would otherwise sit
-inside the timed steps).  traffic = HBM bytes per launch
+recorded on the stream the kernels run on, in a second pass right after the
+timed steps: as many launches of the kernel back to back over the same
+rotating sets, replayed from a captured HIP graph between two events (events
+between the kernels would otherwise sit inside the timed steps, and an event
+around every launch adds its own marker and dispatch gap).  traffic = HBM bytes per launch
 from the committed rocprofv3 counter record for the same kernel source, or
 null when the kernel source has changed since the counters were taken.
 
@@ -293,18 +295,6 @@ def main_step(torch, kvq, synth, args, dev, timer):
 
     E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
-    def step(s, ev=None):
-        st = sets[s % nset]
-        sd = sets[(s + nset // 2) % nset]
-        if ev is not None:
-            ev[0].record(stream)
-        kvq.kvq_quantize_kv(ctx, st["k"], st["v"], B, Hkv, T, st["kc"], st["kn"], st["vc"], st["vn"])
-        if ev is not None:
-            ev[1].record(stream)
-        kvq.kvq_attn_decode(ctx, q, B, Hq, T, sd["kc"], sd["kn"], sd["vc"], sd["vn"], 0.0, out, ws)
-        if ev is not None:
-            ev[2].record(stream)
-
     # The timed steps put each step's decode on a second stream, where it
     # overlaps the same step's quantize (they touch different buffer sets):
     # decode s waits for quantize s - 2, which wrote the codes it reads, and
@@ -333,9 +323,13 @@ def main_step(torch, kvq, synth, args, dev, timer):
         step2(s)
     torch.cuda.synchronize()
     # The K timed steps carry no timing events of their own (an event between
-    # the kernels would order them).  A second pass of K steps on one stream,
-    # right after, brackets every launch with events on the launching stream
-    # for the per-kernel durations of the roofline.
+    # the kernels would order them).  The per-kernel durations for the
+    # roofline come from a second pass right after: K launches of each kernel
+    # back to back over the same rotating sets, captured once into a HIP graph
+    # and replayed between two events on the launching stream, so neither the
+    # host's launch cost nor an event between two launches sits in the
+    # interval (an event around every launch adds its marker and the dispatch
+    # gap to each one).
     t_start, t_end = E(), E()
     torch.cuda.synchronize()
     t_start.record(stream)
@@ -350,12 +344,32 @@ def main_step(torch, kvq, synth, args, dev, timer):
     ms_step = t_start.elapsed_time(t_end) / args.steps
     evq.clear()
     evd.clear()
-    evs = [[E() for _ in range(3)] for _ in range(args.steps)]
-    for s in range(args.steps):
-        step(args.warmup + args.steps + s, evs[s])
-    torch.cuda.synchronize()
-    q_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    d_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+
+    def qlaunch(i):
+        st = sets[i % nset]
+        kvq.kvq_quantize_kv(ctx, st["k"], st["v"], B, Hkv, T, st["kc"], st["kn"], st["vc"], st["vn"])
+
+    def dlaunch(i):
+        sd = sets[i % nset]
+        kvq.kvq_attn_decode(ctx, q, B, Hq, T, sd["kc"], sd["kn"], sd["vc"], sd["vn"], 0.0, out, ws)
+
+    last = (args.steps - 1) % nset
+
+    def check_quantize():  # the replay's codes of the last set equal an eager launch's
+        got = sets[last]["kc"].clone(), sets[last]["vn"].clone()
+        qlaunch(last)
+        torch.cuda.synchronize()
+        assert torch.equal(got[0], sets[last]["kc"]) and torch.equal(got[1], sets[last]["vn"]), \
+            "graph replay differs from the eager launch"
+
+    def check_decode():
+        got = out.clone()
+        dlaunch(last)
+        torch.cuda.synchronize()
+        assert torch.equal(got, out), "graph replay differs from the eager launch"
+
+    q_ms = run_graph(timer, qlaunch, 5, args.steps, check=check_quantize)[0]
+    d_ms = run_graph(timer, dlaunch, 5, args.steps, check=check_decode)[0]
 
     qb = quant_bytes(2 * n, bits)
     db = decode_bytes(n, bits)
