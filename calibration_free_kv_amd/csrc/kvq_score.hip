@@ -539,11 +539,14 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
         ktab[KLO + i] = pack_h2(la, lb);
     }
     __syncthreads();
-    // The records of the wave's next tile are held in registers: loaded before
-    // the prologue for the first tile; for the others, the keys once the
-    // current logits are formed and the values once the current value
-    // products are issued, so that only one of the two is in flight during
-    // each phase.  Every lane loads (tokens past the end re-read the last one
+    // The records of the wave's next tile are held in registers.  For the
+    // first tile the keys are loaded before the prologue and the values once
+    // the queries are published: the launch's first burst of loads is then
+    // half as large, and the query loads queued behind it return sooner
+    // (19.1 against 19.8 us on the 8 x 32768-token layer).  For the other
+    // tiles, the keys once the current logits are formed and the values once
+    // the current value products are issued, so that only one of the two is
+    // in flight during each phase.  Every lane loads (tokens past the end re-read the last one
     // of the range), so the loads carry no lane-dependent branch.  Keys: the
     // lane's window (BITS dwords) of the records of tokens 16 rg + n, and
     // rho_K of token `lane`; values and rho_V: token `lane`.
@@ -591,7 +594,6 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
         // a wave without a tile loads the range's last token
         const int64_t t0 = t_begin + min(wv * 64, (int)(t_end - t_begin) - 1);
         fetch_k(t0, tile_last(t0));
-        fetch_v(t0, tile_last(t0));
     }
 
     float *ctab = smem + SM::ctab;
@@ -644,6 +646,10 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
     while (__hip_atomic_load(ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < (unsigned)G)
         __builtin_amdgcn_s_sleep(1);
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    {
+        const int64_t t0 = t_begin + min(wv * 64, (int)(t_end - t_begin) - 1);
+        fetch_v(t0, tile_last(t0));
+    }
     // A operand of the logits: row n is part (n & 3) of head n >> 2 (0: high,
     // 1: low, 2 and 3: zero), coordinates 32 kg + 8 cb + j.
     h8_t aq[4];
