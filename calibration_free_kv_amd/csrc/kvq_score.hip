@@ -540,10 +540,13 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
     }
     __syncthreads();
     // The records of the wave's next tile are held in registers.  For the
-    // first tile the keys are loaded before the prologue and the values once
-    // the queries are published: the launch's first burst of loads is then
-    // half as large, and the query loads queued behind it return sooner
-    // (19.1 against 19.8 us on the 8 x 32768-token layer).  For the other
+    // first tile the keys of its first two 16-token groups (and the key
+    // norms) are loaded before the prologue, the other keys and the values
+    // once the queries are published: the launch's first burst of loads is
+    // then a quarter as large, and the query loads queued behind it return
+    // sooner (18.9 us per launch on the 8 x 32768-token layer, against 19.8
+    // with every record loaded first, 19.1 with all keys first and 19.2 with
+    // one group first).  For the other
     // tiles, the keys once the current logits are formed and the values once
     // the current value products are issued, so that only one of the two is
     // in flight during each phase.  Every lane loads (tokens past the end re-read the last one
@@ -557,12 +560,14 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
     // t0 < t_end; `last` = min(63, t_end - 1 - t0), the tile's last valid
     // token (32-bit scalar arithmetic: the scalar unit has no 64-bit compare).
     auto tile_last = [&](int64_t t0) { return (uint32_t)min((int)(t_end - t0) - 1, 63); };
-    auto fetch_k = [&](int64_t t0, uint32_t last) {
+    // keys of the 16-token groups rg0 .. rg1 - 1 (and, with norm, rho_K)
+    auto fetch_k = [&](int64_t t0, uint32_t last, int rg0 = 0, int rg1 = 4, bool norm = true) {
         const int64_t v0 = bh * ldt + t0;
         const uint32_t l = min((uint32_t)lane, last);
         const char *kb = reinterpret_cast<const char *>(kc) + v0 * (16 * BITS);
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
+            if (rg < rg0 || rg >= rg1) continue;
             const uint32_t t = min((uint32_t)(16 * rg + n), last);
             // opaque, so that the lane part stays out of the (scalar) base
             uint32_t off = t * (16u * BITS) + 4u * BITS * kg;
@@ -571,7 +576,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
 #pragma unroll
             for (int i = 0; i < BITS; ++i) Kw[rg][i] = src[i];
         }
-        rk = *reinterpret_cast<const float *>(reinterpret_cast<const char *>(kn + v0) + 4 * l);
+        if (norm) rk = *reinterpret_cast<const float *>(reinterpret_cast<const char *>(kn + v0) + 4 * l);
     };
     auto fetch_v = [&](int64_t t0, uint32_t last) {
         const int64_t v0 = bh * ldt + t0;
@@ -593,7 +598,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
     {
         // a wave without a tile loads the range's last token
         const int64_t t0 = t_begin + min(wv * 64, (int)(t_end - t_begin) - 1);
-        fetch_k(t0, tile_last(t0));
+        fetch_k(t0, tile_last(t0), 0, 2, true);
     }
 
     float *ctab = smem + SM::ctab;
@@ -648,6 +653,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     {
         const int64_t t0 = t_begin + min(wv * 64, (int)(t_end - t_begin) - 1);
+        fetch_k(t0, tile_last(t0), 2, 4, false);
         fetch_v(t0, tile_last(t0));
     }
     // A operand of the logits: row n is part (n & 3) of head n >> 2 (0: high,
