@@ -168,8 +168,10 @@ constexpr int kRowsH = kTileH * 16;   // 16-byte chunks of rows per tile
 constexpr int kBufH = kRowsH + 16;    // + 256 bytes of sign masks
 
 // Direct global -> LDS copy of one tile and its head's sign masks (no VGPR
-// staging).  Row-copy instruction j writes slots [64 j, 64 j + 64), lane l at
-// slot 64 j + l: row v = 4 j + l/16 and chunk (l mod 16) ^ (v mod 16).  Each
+// staging).  The rows are read once: their copies carry the non-temporal
+// hint (cache policy 2); the masks, read by every tile of the head, do not.
+// Row-copy instruction j writes slots [64 j, 64 j + 64), lane l at slot
+// 64 j + l: row v = 4 j + l/16 and chunk (l mod 16) ^ (v mod 16).  Each
 // instruction reads one contiguous KiB (four whole rows); the chunk depends on
 // j only through j mod 4, so the address is a wave-uniform base plus one of
 // four per-lane offsets.  A ninth instruction copies the 64 mask dwords.
@@ -188,7 +190,7 @@ __device__ __forceinline__ void tile_to_lds(const u4_t *src, int nv, const uint3
             const uint32_t off = (uint32_t)(16 * r + (q ^ ((4 * j + r) & 15)));
             __builtin_amdgcn_global_load_lds(
                 (const __attribute__((address_space(1))) void *)(src + 64 * j + off),
-                (__attribute__((address_space(3))) void *)(L + j * 64), 16, 0, 0);
+                (__attribute__((address_space(3))) void *)(L + j * 64), 16, 0, 2);
         }
     } else {
 #pragma unroll
@@ -197,7 +199,7 @@ __device__ __forceinline__ void tile_to_lds(const u4_t *src, int nv, const uint3
             const int row = v < nv ? v : nv - 1;
             __builtin_amdgcn_global_load_lds(
                 (const __attribute__((address_space(1))) void *)(src + row * 16 + (q ^ (v & 15))),
-                (__attribute__((address_space(3))) void *)(L + j * 64), 16, 0, 0);
+                (__attribute__((address_space(3))) void *)(L + j * 64), 16, 0, 2);
         }
     }
     __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(msk + lane),
@@ -448,8 +450,14 @@ __global__ __launch_bounds__(kWavesQ * 64) __attribute__((amdgpu_waves_per_eu(4,
             // the lanes of the tile write its 32 records (half h of record v)
             uint2 *dst = (uint2 *)(a.codes[kt] + g.v0 * BITS) + (2 * v + h) * BITS;
 #pragma unroll
-            for (int q = 0; q < BITS; ++q) dst[q] = make_uint2(out[2 * q], out[2 * q + 1]);
-            if (h == 0) a.norms[kt][g.v0 + v] = rho;
+            // non-temporal: written once here and read by a later call, the
+            // records would otherwise sit in L2 beside the streaming input
+            // (and be written back at the end of the kernel)
+            for (int q = 0; q < BITS; ++q) {
+                __builtin_nontemporal_store(out[2 * q], reinterpret_cast<uint32_t *>(dst + q));
+                __builtin_nontemporal_store(out[2 * q + 1], reinterpret_cast<uint32_t *>(dst + q) + 1);
+            }
+            if (h == 0) __builtin_nontemporal_store(rho, &a.norms[kt][g.v0 + v]);
         }
         if (!has_next) break;
         tile = next;

@@ -1,14 +1,15 @@
 """Decode launches replayed from a captured HIP graph, and the no-allocation
 scratch across calls of different shapes.
 
-The split partials of a decode call are handed to the merging block as
-tagged words; the tag comes from a generation kept in the workspace, so a
-replayed launch (whose arguments are frozen at capture) must still tell its
-own partials from the previous replay's.  Each replay gets new inputs,
-copied eagerly into the captured buffers, and must reproduce an eager call
-on a separate workspace bit for bit (same kernels, same split count, fixed
-summation order); eager decode calls on the captured workspace run between
-the replays too.  The no-allocation entry point is called with a batch, a
+The split partials of a decode call are merged by the last block of each
+(batch, KV head) to arrive, found through an arrival counter in the
+workspace that this block sets back to zero; a replayed launch (whose
+arguments are frozen at capture) therefore finds the counters as the
+previous launch left them.  Each replay gets new inputs, copied eagerly
+into the captured buffers, and must reproduce an eager call on a separate
+workspace bit for bit (same kernels, same split count, fixed summation
+order); eager decode calls on the captured workspace run between the
+replays too.  The no-allocation entry point is called with a batch, a
 larger batch (more counter words than before) and the first batch again,
 each checked against the workspace entry point."""
 import numpy as np
