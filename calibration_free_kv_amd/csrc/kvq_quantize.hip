@@ -19,8 +19,6 @@
 // per-coordinate multiply).
 #include "kvq_internal.h"
 
-#include <type_traits>
-
 namespace kvq {
 namespace {
 
@@ -449,10 +447,10 @@ __global__ __launch_bounds__(kWavesQ * 64) __attribute__((amdgpu_waves_per_eu(4,
         if (v < g.nv) {  // lanes past a ragged tail encoded stale rows
             // the lanes of the tile write its 32 records (half h of record v)
             uint2 *dst = (uint2 *)(a.codes[kt] + g.v0 * BITS) + (2 * v + h) * BITS;
-#pragma unroll
             // non-temporal: written once here and read by a later call, the
             // records would otherwise sit in L2 beside the streaming input
             // (and be written back at the end of the kernel)
+#pragma unroll
             for (int q = 0; q < BITS; ++q) {
                 __builtin_nontemporal_store(out[2 * q], reinterpret_cast<uint32_t *>(dst + q));
                 __builtin_nontemporal_store(out[2 * q + 1], reinterpret_cast<uint32_t *>(dst + q) + 1);
@@ -516,50 +514,25 @@ __device__ __forceinline__ float centroid_mag(float a, const float *P, const flo
     }
 }
 
-// v = hi + lo (hi returned) with hi exactly representable in fp16: hi keeps the 11 leading
-// significant bits of v (values below the fp16 normal range go wholly to lo),
-// so its conversion is exact under any rounding and v - hi is exact in fp32;
-// only lo is rounded (|error| <= 2^-21 |v|).  Rounding hi to nearest instead
-// lets the compiler emit two different conversions for it (one for the stored
-// hi, one for the hi subtracted to form lo) that break exact ties differently,
-// leaving an error of one fp16 ulp.
-__device__ __forceinline__ _Float16 split_f16(float v, _Float16 &lo)
+// LDS slot of chunk c of row n of S in the QJL kernel: chunks permuted by
+// (n mod 16) xor 8 [bit 6 of n], so that the rows one 16-lane group of the
+// projection reads (n = base + 64 g + 4 q + e, q < 2 or q >= 2) fall into 16
+// distinct 16-byte bank groups.
+__device__ __forceinline__ int swz_s(int row, int chunk) { return row * 16 + (chunk ^ (row & 15) ^ ((row >> 3) & 8)); }
+
+// Packed fp16 (round(e0 - hi0), round(e1 - hi1)) for the packed fp16 high
+// parts hp of (e0, e1): one v_fma_mix per half, fp16 source times -1 plus the
+// fp32 value, rounded once to fp16 into the low or high half of the result.
+// e - hi is exact in fp32 when hi is e truncated to fp16, so this equals
+// rounding the fp32 difference.
+__device__ __forceinline__ uint32_t lo_pair(uint32_t hp, float e0, float e1)
 {
-    float h = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, v) & 0xFFFFE000u);
-    h = __builtin_fabsf(v) < 0x1p-14f ? 0.0f : h;
-    lo = (_Float16)(v - h);
-    return (_Float16)h;
+    uint32_t r;
+    asm("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel:[0,0,0] op_sel_hi:[1,0,0]\n\t"
+        "v_fma_mixhi_f16 %0, %1, -1.0, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+        : "=&v"(r) : "v"(hp), "v"(e0), "v"(e1));
+    return r;
 }
-
-__device__ __forceinline__ int swz(int row, int chunk) { return row * 16 + (chunk ^ (row & 15)); }
-
-// Write the low and high halves of a lane mask into lanes KLO and KHI of v.
-// The leading s_nop 4 gives the wait states a read of an SGPR pair needs right
-// after a VALU instruction (the compare that made the mask) wrote it: the
-// compiler cannot see into the asm, and without them the first read returned
-// the previous value.
-template <int KLO, int KHI>
-__device__ __forceinline__ uint32_t write_lane_pair(uint32_t v, uint64_t m)
-{
-    asm("s_nop 4\n\t"
-        "v_writelane_b32 %0, %1, %3\n\t"
-        "v_writelane_b32 %0, %2, %4"
-        : "+v"(v) : "s"((uint32_t)m), "s"((uint32_t)(m >> 32)), "n"(KLO), "n"(KHI));
-    return v;
-}
-
-template <int K0, int N>
-struct StaticFor {
-    template <class F>
-    __device__ __forceinline__ static void run(F &&f)
-    {
-        if constexpr (N > 0) {
-            f(std::integral_constant<int, K0>{});
-            StaticFor<K0 + 1, N - 1>::run(f);
-        }
-    }
-};
-
 
 // Append the BITS-bit indices of 32 coordinates y[0..31] (LSB-first stream of
 // 32 BITS bits) to out[0 .. BITS), from the last bit backwards, and replace
@@ -604,15 +577,16 @@ __device__ __forceinline__ void encode32(float *y, const float *P, const float *
 //  - e = y / rho - c[idx] per coordinate (the factor 1/sqrt(d) of r does not
 //    change a sign), gamma = ||e|| / sqrt(d); e is split exactly into fp16
 //    hi + lo (hi by round-toward-zero conversion, i.e. its 11 leading
-//    significant bits; lo = e - hi exactly, then rounded once).
+//    significant bits; lo = e - hi exactly, then rounded once, by one
+//    v_fma_mix per coordinate).
 //  - The projection S e of the 32 keys runs on v_mfma_f32_32x32x16_f16 with
-//    the A operand straight from registers: the contraction may visit the
-//    coordinates in any order as long as both operands agree, so k-step s
-//    takes, in lane half h, coordinates C(h, 8s) .. +7 (chunk 8 h + s of the
-//    key), and the B operand reads the same coordinates of the rows of S
-//    staged in LDS.  Each accumulator register of a 32 x 32 block
-//    (rows = keys, columns = outputs) gives, with one ballot, two keys' 32
-//    sign bits of the block, which are written into the key's lane.
+//    the B operand (columns = keys) straight from registers: the contraction
+//    may visit the coordinates in any order as long as both operands agree,
+//    so k-step s takes, in lane half h, coordinates C(h, 8s) .. +7 (chunk
+//    8 h + s of the key), and the A operand reads the same coordinates of
+//    rows of S staged in LDS.  The rows of S are assigned to the blocks so
+//    that one ballot of an accumulator register is one sign bit of every
+//    lane's own output dword, appended like the codes.
 constexpr int kWavesJ = 12;  // waves per workgroup of the QJL kernel
 
 template <int BITS, bool S_LO>
@@ -625,7 +599,7 @@ __global__ __launch_bounds__(kWavesJ * 64) __attribute__((amdgpu_waves_per_eu(3,
     __shared__ int next_tile;
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    for (int i = threadIdx.x; i < kD * 16; i += kWavesJ * 64) Ss[swz(i >> 4, i & 15)] = a.S_hi[i];
+    for (int i = threadIdx.x; i < kD * 16; i += kWavesJ * 64) Ss[swz_s(i >> 4, i & 15)] = a.S_hi[i];
     if (threadIdx.x == 0) next_tile = kWavesJ;
     __syncthreads();
     u4_t *L = lds[wv];
@@ -709,10 +683,8 @@ __global__ __launch_bounds__(kWavesJ * 64) __attribute__((amdgpu_waves_per_eu(3,
             const float e0 = y[2 * m], e1 = y[2 * m + 1];
             g2 = fmaf(e0, e0, g2);
             g2 = fmaf(e1, e1, g2);
-            const h2_t hp = __builtin_bit_cast(h2_t, __builtin_amdgcn_cvt_pkrtz(e0, e1));
-            const h2_t lp = h2_t{(_Float16)(e0 - (float)hp.x), (_Float16)(e1 - (float)hp.y)};
-            eh[m] = __builtin_bit_cast(uint32_t, hp);
-            el[m] = __builtin_bit_cast(uint32_t, lp);
+            eh[m] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(e0, e1));
+            el[m] = lo_pair(eh[m], e0, e1);
         }
         {
             float p = g2, q = g2;
@@ -720,34 +692,42 @@ __global__ __launch_bounds__(kWavesJ * 64) __attribute__((amdgpu_waves_per_eu(3,
             g2 = p + q;
         }
 
-        uint32_t sgnw[4] = {0u, 0u, 0u, 0u};
+        // Projection z = S e, S as the A operand and e as B (columns = keys):
+        // register rr of a 32 x 32 block holds, in lane v + 32 g, row
+        // 8 (rr / 4) + 4 g + rr % 4 of the block for key v.  Block (p, t)
+        // takes as its row 8 q + 4 g + e the output 32 (p + 2 g) + 16 t + 4 q + e,
+        // so the ballot of register 4 q + e carries bit 16 t + 4 q + e of the
+        // key's sign dword p in lanes 0-31 and of dword p + 2 in lanes 32-63,
+        // and is appended as it is.  Lane v + 32 h ends with dwords p + 2 h.
+        uint32_t sgnw[2];
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-            f16_t z = {};
-            const int n = 32 * nb + v;  // output row of S read by this lane
+        for (int p = 0; p < 2; ++p) {
+            uint32_t acc = 0u;
 #pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                const int ch = 8 * h + s;  // 16-byte chunk of the coordinates C(h, 8s..8s+7)
-                const h8_t B = __builtin_bit_cast(h8_t, Ss[swz(n, ch)]);
-                const h8_t Ah = __builtin_bit_cast(h8_t, u4_t{eh[4 * s], eh[4 * s + 1], eh[4 * s + 2], eh[4 * s + 3]});
-                const h8_t Al = __builtin_bit_cast(h8_t, u4_t{el[4 * s], el[4 * s + 1], el[4 * s + 2], el[4 * s + 3]});
-                z = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ah, B, z, 0, 0, 0);
-                z = __builtin_amdgcn_mfma_f32_32x32x16_f16(Al, B, z, 0, 0, 0);
-                if constexpr (S_LO) {  // S not exactly fp16: third pass with its lo part
-                    const h8_t Bl = __builtin_bit_cast(h8_t, a.S_lo[n * 16 + ch]);
-                    z = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ah, Bl, z, 0, 0, 0);
+            for (int t = 1; t >= 0; --t) {
+                const int n = 32 * (p + 2 * ((v >> 2) & 1)) + 16 * t + 4 * (v >> 3) + (v & 3);  // row of S
+                f16_t z = {};
+                // the A chunk of step s + 1 is read before the products of step s
+                // (not with the third pass, whose registers would not fit)
+                h8_t An = __builtin_bit_cast(h8_t, Ss[swz_s(n, 8 * h)]);
+#pragma unroll
+                for (int s = 0; s < 8; ++s) {
+                    const int ch = 8 * h + s;  // 16-byte chunk of the coordinates C(h, 8s..8s+7)
+                    const h8_t A = S_LO ? __builtin_bit_cast(h8_t, Ss[swz_s(n, ch)]) : An;
+                    if (!S_LO && s < 7) An = __builtin_bit_cast(h8_t, Ss[swz_s(n, ch + 1)]);
+                    const h8_t Bh = __builtin_bit_cast(h8_t, u4_t{eh[4 * s], eh[4 * s + 1], eh[4 * s + 2], eh[4 * s + 3]});
+                    const h8_t Bl = __builtin_bit_cast(h8_t, u4_t{el[4 * s], el[4 * s + 1], el[4 * s + 2], el[4 * s + 3]});
+                    z = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, Bh, z, 0, 0, 0);
+                    z = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, Bl, z, 0, 0, 0);
+                    if constexpr (S_LO) {  // S not exactly fp16: third pass with its lo part
+                        const h8_t Al = __builtin_bit_cast(h8_t, a.S_lo[n * 16 + ch]);
+                        z = __builtin_amdgcn_mfma_f32_32x32x16_f16(Al, Bh, z, 0, 0, 0);
+                    }
                 }
+#pragma unroll
+                for (int rr = 15; rr >= 0; --rr) acc = append_bit(acc, __builtin_amdgcn_ballot_w64(z[rr] >= 0.0f));
             }
-            // register rr: lanes 0-31 hold key 8(rr/4) + rr%4, lanes 32-63 key
-            // 8(rr/4) + 4 + rr%4, columns = outputs 32 nb + (lane % 32)
-            uint32_t acc = sgnw[nb];
-            StaticFor<0, 16>::run([&](auto kk) {
-                constexpr int rr = decltype(kk)::value;
-                constexpr int k0 = 8 * (rr / 4) + rr % 4;
-                const uint64_t m = __builtin_amdgcn_ballot_w64(z[rr] >= 0.0f);
-                acc = write_lane_pair<k0, k0 + 4>(acc, m);
-            });
-            sgnw[nb] = acc;
+            sgnw[p] = acc;
         }
         // The next tile's rows, then the copy of the tile after it, then this
         // tile's stores (as in k_quantize).  The rows are read only now: held
@@ -763,9 +743,9 @@ __global__ __launch_bounds__(kWavesJ * 64) __attribute__((amdgpu_waves_per_eu(3,
             uint32_t *dst = reinterpret_cast<uint32_t *>(a.codes + key * BITS);
 #pragma unroll
             for (int k = 0; k < 2 * BITS; ++k) dst[2 * h * BITS + k] = out[k];
+            reinterpret_cast<uint2 *>(a.signs + key)[h] = make_uint2(sgnw[0], sgnw[1]);
             if (h == 0) {
                 a.norms[key] = rho;
-                a.signs[key] = u4_t{sgnw[0], sgnw[1], sgnw[2], sgnw[3]};
                 a.gamma[key] = __builtin_sqrtf(g2) * 0.08838834764831845f;  // ||e|| / sqrt(d)
             }
         }
