@@ -94,6 +94,18 @@ def test_decode_batch16_full_size_sampled():
     assert err <= 2e-3
 
 
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_decode_several_tiles_per_wave(bits):
+    """One split per (batch, KV head): each wave of the block runs several
+    64-token tiles (the next tile's records loaded while the current one is
+    scored), the last one ragged."""
+    inp, ctx, k, v = quantized("l8b32k", bits, T=3001)
+    out = to_np(ctx.attn_decode(torch.from_numpy(inp["q"]).cuda(), k["codes"], k["norms"], v["codes"], v["norms"],
+                                n_split=1))
+    err = np.abs(out - decode_ref(inp, k, v, bits)).max()
+    assert err <= 2e-3, (bits, err)
+
+
 def test_decode_split_invariance():
     inp, ctx, k, v = quantized("l8b32k", 3, T=5000)
     q = torch.from_numpy(inp["q"]).cuda()
