@@ -12,6 +12,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libkvq.so")
 BUILD = os.path.join(PKG, "_build")
+# the bounds-checked debug build (KVQ_DEBUG): same sources, own objects
+OUT_DEBUG = os.path.join(PKG, "libkvq_debug.so")
+BUILD_DEBUG = os.path.join(PKG, "_build_debug")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -36,31 +39,35 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
+def _compile(src: str, debug: bool = False) -> str:
+    obj = os.path.join(BUILD_DEBUG if debug else BUILD, os.path.basename(src) + ".o")
+    cmd = [HIPCC, *FLAGS, *(["-DKVQ_DEBUG"] if debug else []), *FILE_FLAGS.get(os.path.basename(src), []),
+           "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, debug: bool = False) -> str:
+    """libkvq.so, or with debug=True the bounds-checked libkvq_debug.so."""
+    out = OUT_DEBUG if debug else OUT
+    os.makedirs(BUILD_DEBUG if debug else BUILD, exist_ok=True)
     srcs = sources()
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = OUT + ".tmp%d" % os.getpid()
+        objs = list(ex.map(lambda f: _compile(f, debug), srcs))
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), r.stderr))
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
     if verbose:
-        print("built", OUT)
-    return OUT
+        print("built", out)
+    return out
 
 
 if __name__ == "__main__":
     build(verbose=True)
+    build(verbose=True, debug=True)
     sys.exit(0)

@@ -25,6 +25,7 @@
 #include "kvq_wave.h"
 
 namespace kvq {
+KVQ_DEBUG_UNIT(dense, 5)
 namespace {
 
 typedef _Float16 h8_t __attribute__((ext_vector_type(8)));

@@ -253,6 +253,18 @@ bool decode_group_built(int64_t G) { return G == 1 || G == 2 || G == 4; }
 
 extern "C" {
 
+int32_t kvq_debug_build(void) { return KVQ_DEBUG_ON; }
+
+uint32_t kvq_debug_take(void)
+{
+    // every file's record is read (and so cleared); the first non-zero one is returned
+    const uint32_t r[] = {kvq::debug_take_quantize(), kvq::debug_take_score(), kvq::debug_take_nsn(),
+                          kvq::debug_take_nsn_score(), kvq::debug_take_dense(), kvq::debug_take_stream()};
+    for (uint32_t v : r)
+        if (v) return v;
+    return 0u;
+}
+
 const char *kvq_strerror(kvq_status s)
 {
     // a C caller may pass any int: read it as an int, not as the enum type

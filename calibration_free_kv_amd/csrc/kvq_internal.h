@@ -19,6 +19,65 @@ constexpr int kNsnPartStride = kD + 4;     // floats per NSN decode partial: acc
 // Device scratch of the no-allocation decode entry point, per device.
 constexpr size_t kNoAllocScratchBytes = size_t(KVQ_NOALLOC_SCRATCH_BYTES);
 
+// Bounds-checked debug build.  Compiled with KVQ_DEBUG defined, a failed
+// KVQ_CHECK(cond) in a kernel records the source line of its first failure
+// in a device word of the kernel's source file and the kernel carries on (no
+// trap); LDS is filled with a NaN pattern before first use, so that a read of
+// LDS nothing wrote shows in the results.  debug_take_<file>() reads the
+// word of the current device (file id in the high half, line in the low
+// half, 0 if no check failed) and clears it.  Without KVQ_DEBUG the checks
+// compile to nothing and the take functions return 0.  Each source file with
+// kernels expands KVQ_DEBUG_UNIT(name, id) once, inside namespace kvq, before
+// its first kernel.
+#ifdef KVQ_DEBUG
+#define KVQ_CHECK(cond)                                  \
+    do {                                                 \
+        if (!(cond)) ::kvq::debug_fail((unsigned)__LINE__); \
+    } while (0)
+#define KVQ_DEBUG_UNIT(NAME, ID)                                                                  \
+    namespace {                                                                                   \
+    __device__ unsigned g_debug_record;                                                           \
+    }                                                                                             \
+    __device__ __forceinline__ void debug_fail(unsigned line)                                      \
+    {                                                                                             \
+        atomicCAS(&g_debug_record, 0u, line & 0xFFFFu);                                           \
+    }                                                                                             \
+    uint32_t debug_take_##NAME()                                                                  \
+    {                                                                                             \
+        unsigned v = 0u, z = 0u;                                                                  \
+        if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_debug_record), sizeof(v), 0, hipMemcpyDeviceToHost) != hipSuccess) \
+            return 0xFFFFFFFFu;                                                                   \
+        if (v != 0u && hipMemcpyToSymbol(HIP_SYMBOL(g_debug_record), &z, sizeof(z), 0, hipMemcpyHostToDevice) != hipSuccess) \
+            return 0xFFFFFFFFu;                                                                   \
+        return v ? ((uint32_t)(ID) << 16) | v : 0u;                                               \
+    }
+#define KVQ_DEBUG_ON 1
+#else
+#define KVQ_CHECK(cond) \
+    do {                \
+    } while (0)
+#define KVQ_DEBUG_UNIT(NAME, ID) \
+    uint32_t debug_take_##NAME() { return 0u; }
+#define KVQ_DEBUG_ON 0
+#endif
+// the files with kernels: ids 1 .. 6
+uint32_t debug_take_quantize();
+uint32_t debug_take_score();
+uint32_t debug_take_nsn();
+uint32_t debug_take_nsn_score();
+uint32_t debug_take_dense();
+uint32_t debug_take_stream();
+
+// LDS words [0, n) of a block set to a NaN pattern (fp32 and fp16 pairs), by
+// its threads, before the block's first barrier (debug build only).
+#define KVQ_POISON_LDS(ptr, n_words, tid, n_threads)                                   \
+    do {                                                                               \
+        if (KVQ_DEBUG_ON) {                                                            \
+            for (int i_ = (tid); i_ < (int)(n_words); i_ += (n_threads))               \
+                reinterpret_cast<uint32_t *>(ptr)[i_] = 0x7FC07FC0u;                   \
+        }                                                                              \
+    } while (0)
+
 // Scalar codebook of one bit width, passed to kernels by value.
 struct Codebook {
     float c[16];  // centroids c_0 < ... < c_{2^b - 1}

@@ -19,6 +19,7 @@
 #include "kvq_internal.h"
 
 namespace kvq {
+KVQ_DEBUG_UNIT(nsn, 3)
 namespace {
 
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));

@@ -17,6 +17,7 @@
 #include "kvq_wave.h"
 
 namespace kvq {
+KVQ_DEBUG_UNIT(nsn_score, 4)
 namespace {
 
 typedef _Float16 half_t;

@@ -20,6 +20,7 @@
 #include "kvq_internal.h"
 
 namespace kvq {
+KVQ_DEBUG_UNIT(quantize, 1)
 namespace {
 
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
@@ -322,6 +323,9 @@ __global__ __launch_bounds__(kWavesQ * 64) __attribute__((amdgpu_waves_per_eu(4,
     // ticket k of this workgroup is tile blockIdx.x + k * gridDim.x: at any
     // moment the workgroups read one window of consecutive tiles
     const int64_t G = gridDim.x;
+    const int64_t rows = (n_tiles / mp.tiles_per_bh) * mp.T;  // vectors per tensor
+    KVQ_POISON_LDS(lds, kWavesQ * kBufH * 4, threadIdx.x, kWavesQ * 64);
+    KVQ_CHECK(n_tiles % mp.tiles_per_bh == 0 && (n_tensors == 1 || n_tensors == 2));
     if (threadIdx.x == 0) next_tile = kWavesQ;
     __syncthreads();
     int64_t tile = blockIdx.x + wv * G;
@@ -329,6 +333,8 @@ __global__ __launch_bounds__(kWavesQ * 64) __attribute__((amdgpu_waves_per_eu(4,
     auto issue = [&](int64_t t) {
         const int k = t >= n_tiles;
         const TileGeom gg = geom<kTileH>((uint32_t)(t - k * n_tiles), mp);
+        KVQ_CHECK(t >= 0 && t < total && gg.nv >= 1 && gg.v0 >= 0 && gg.v0 + gg.nv <= rows && gg.h >= 0 &&
+                  gg.h < (int)mp.H && (a.kind[k] == 0 || a.kind[k] == 1));
         tile_to_lds(a.x[k] + gg.v0 * 16, gg.nv, sgn + (a.kind[k] * (int)mp.H + gg.h) * 64, L, lane);
     };
     const h8_t F0 = hadamard_fragment(lane, 0), F1 = hadamard_fragment(lane, 1);
@@ -445,6 +451,7 @@ __global__ __launch_bounds__(kWavesQ * 64) __attribute__((amdgpu_waves_per_eu(4,
         }
         const int v = lane & 31, h = lane >> 5;
         if (v < g.nv) {  // lanes past a ragged tail encoded stale rows
+            KVQ_CHECK(g.v0 + v < rows);
             // the lanes of the tile write its 32 records (half h of record v)
             uint2 *dst = (uint2 *)(a.codes[kt] + g.v0 * BITS) + (2 * v + h) * BITS;
             // non-temporal: written once here and read by a later call, the
@@ -599,6 +606,9 @@ __global__ __launch_bounds__(kWavesJ * 64) __attribute__((amdgpu_waves_per_eu(3,
     __shared__ int next_tile;
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    KVQ_POISON_LDS(lds, kWavesJ * kBufH * 4, threadIdx.x, kWavesJ * 64);
+    KVQ_CHECK(n_tiles % mp.tiles_per_bh == 0);
+    const int64_t rows = (n_tiles / mp.tiles_per_bh) * mp.T;  // keys
     for (int i = threadIdx.x; i < kD * 16; i += kWavesJ * 64) Ss[swz_s(i >> 4, i & 15)] = a.S_hi[i];
     if (threadIdx.x == 0) next_tile = kWavesJ;
     __syncthreads();
@@ -608,6 +618,8 @@ __global__ __launch_bounds__(kWavesJ * 64) __attribute__((amdgpu_waves_per_eu(3,
     if (tile >= n_tiles) return;  // wave-uniform
     auto issue = [&](int64_t t) {
         const TileGeom gg = geom<kTileH>((uint32_t)(t), mp);
+        KVQ_CHECK(t >= 0 && t < n_tiles && gg.nv >= 1 && gg.v0 >= 0 && gg.v0 + gg.nv <= rows && gg.h >= 0 &&
+                  gg.h < (int)mp.H);
         tile_to_lds(a.x + gg.v0 * 16, gg.nv, sgn + gg.h * 64, L, lane);
     };
     const int v = lane & 31, h = lane >> 5;
@@ -740,6 +752,7 @@ __global__ __launch_bounds__(kWavesJ * 64) __attribute__((amdgpu_waves_per_eu(3,
         }
         if (v < g.nv) {  // lanes of keys past a ragged tail encoded stale rows
             const int64_t key = g.v0 + v;
+            KVQ_CHECK(key < rows);
             uint32_t *dst = reinterpret_cast<uint32_t *>(a.codes + key * BITS);
 #pragma unroll
             for (int k = 0; k < 2 * BITS; ++k) dst[2 * h * BITS + k] = out[k];

@@ -29,6 +29,7 @@
 static __device__ __align__(256) unsigned char scratch[kvq::kNoAllocScratchBytes];
 
 namespace kvq {
+KVQ_DEBUG_UNIT(score, 2)
 namespace {
 
 typedef _Float16 half_t;
@@ -218,6 +219,11 @@ __global__ __launch_bounds__(kLgThreads) void k_logits(
     const int64_t part = blockIdx.x - bh * blocks_per_bh;
     const int64_t b = bh / H;
     const int g = (int)(bh - b * H);
+    const int64_t nbh = gridDim.x / blocks_per_bh;  // B H (b, g) groups
+    KVQ_CHECK(gridDim.x % blocks_per_bh == 0 && nbh % H == 0 && Hq == G * H && T >= 1 &&
+              tokens_per_block * blocks_per_bh >= T);
+    KVQ_POISON_LDS(smem, (ctab - smem) + 16, threadIdx.x, kLgThreads);
+    if (KVQ_DEBUG_ON) __syncthreads();
 
     stage_centroids(cb, ctab);
     rotate_queries<G, kLgThreads>(q, signs, b, g, Hq, qr, Qm, lut);
@@ -248,6 +254,7 @@ __global__ __launch_bounds__(kLgThreads) void k_logits(
 
     const int64_t t_begin = part * tokens_per_block;
     const int64_t t_end = min(T, t_begin + tokens_per_block);
+    KVQ_CHECK(t_begin < t_end && bh < nbh);
     // Register prefetch: a thread loads its next token's records before it
     // scores the current one.  The loads are unconditional (indexes past the
     // range re-read its last token), so the compiler's wait before the scoring
@@ -292,6 +299,7 @@ __global__ __launch_bounds__(kLgThreads) void k_logits(
         }
 #pragma unroll
         for (int h = 0; h < G; ++h) logits[((b * Hq) + (int64_t)g * G + h) * T + t] = rho * acc[h];
+        KVQ_CHECK(t >= t_begin && t < t_end);
     }
 }
 
@@ -505,6 +513,13 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
 
     const int64_t t_begin = (int64_t)split * chunk;
     const int64_t t_end = min(T, t_begin + chunk);
+    const int64_t nbh = gridDim.x / n_split;  // B H (b, g) groups
+    KVQ_CHECK(n_split >= 1 && n_split <= kMaxSplits && gridDim.x % n_split == 0 && nbh % H == 0 && Hq == G * H &&
+              T <= ldt && n_part >= n_split && n_part <= kMaxSplits && t_begin < t_end && bh < nbh);
+    KVQ_POISON_LDS(smem, SM::total, tid, kDecThreads);
+    KVQ_POISON_LDS(ktab, KLO + SM::NP * KREP, tid, kDecThreads);
+    KVQ_POISON_LDS(vtab, 1 << BITS, tid, kDecThreads);
+    if (KVQ_DEBUG_ON) __syncthreads();
     // The prologue holds no block barrier once loads are in flight: a barrier
     // would hold every wave until the last one had issued its record loads,
     // i.e. until the memory system had accepted the whole block's tiles.
@@ -562,6 +577,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
     auto tile_last = [&](int64_t t0) { return (uint32_t)min((int)(t_end - t0) - 1, 63); };
     // keys of the 16-token groups rg0 .. rg1 - 1 (and, with norm, rho_K)
     auto fetch_k = [&](int64_t t0, uint32_t last, int rg0 = 0, int rg1 = 4, bool norm = true) {
+        KVQ_CHECK(t0 >= t_begin && t0 + (int64_t)last < t_end && last < 64);
         const int64_t v0 = bh * ldt + t0;
         const uint32_t l = min((uint32_t)lane, last);
         const char *kb = reinterpret_cast<const char *>(kc) + v0 * (16 * BITS);
@@ -579,6 +595,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
         if (norm) rk = *reinterpret_cast<const float *>(reinterpret_cast<const char *>(kn + v0) + 4 * l);
     };
     auto fetch_v = [&](int64_t t0, uint32_t last) {
+        KVQ_CHECK(t0 >= t_begin && t0 + (int64_t)last < t_end && last < 64);
         const int64_t v0 = bh * ldt + t0;
         const uint32_t l = min((uint32_t)lane, last);
         const u4_t *vs = reinterpret_cast<const u4_t *>(reinterpret_cast<const char *>(vc) + v0 * (16 * BITS) +
@@ -802,6 +819,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
     // (written through to the coherence point).
     auto st_dev = [](float *p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
     float *my = part + ((bh * n_part + split) * G) * (kD + 2);
+    KVQ_CHECK(split < n_split && (bh * n_part + split) < nbh * n_part);
     for (int idx = tid; idx < G * kD; idx += kDecThreads) {
         const int h = idx >> 7, i = idx & (kD - 1);
         float M = -INFINITY;

@@ -12,6 +12,7 @@
 #include "kvq_wave.h"
 
 namespace kvq {
+KVQ_DEBUG_UNIT(stream, 6)
 namespace {
 
 typedef _Float16 half_t;

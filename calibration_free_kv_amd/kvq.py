@@ -14,7 +14,9 @@ import numpy as np
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libkvq.so")
+# KVQ_LIB selects another build of the library for the process, e.g. the
+# bounds-checked libkvq_debug.so beside it
+LIB_PATH = os.environ.get("KVQ_LIB") or os.path.join(_PKG, "libkvq.so")
 
 KVQ_OK, KVQ_E_INVAL, KVQ_E_UNSUPPORTED, KVQ_E_DEVICE, KVQ_E_NOMEM, KVQ_E_WORKSPACE = range(6)
 KVQ_MODE_MSE, KVQ_MODE_MSE_QJL, KVQ_MODE_NSN_VQ = 0, 1, 2
@@ -35,6 +37,7 @@ EXPORTS = [
     "kvq_nsn_flush_ws_bytes", "kvq_nsn_flush", "kvq_nsn_attn_decode_stream_ws_bytes", "kvq_nsn_attn_decode_stream",
     "kvq_nsn_vq_dq_ws_bytes", "kvq_nsn_vq_quantize_dq", "kvq_nsn_logits_dq", "kvq_nsn_attn_decode_dq",
     "kvq_gsrq_ws_bytes", "kvq_gsrq_quantize", "kvq_gsrq_logits", "kvq_gsrq_attn_decode",
+    "kvq_debug_build", "kvq_debug_take",
 ]
 
 
@@ -74,6 +77,10 @@ def lib():
         L.kvq_code_bytes_per_vec.restype = i64
         L.kvq_strerror.argtypes = [C.c_int]
         L.kvq_strerror.restype = C.c_char_p
+        L.kvq_debug_build.argtypes = []
+        L.kvq_debug_build.restype = i32
+        L.kvq_debug_take.argtypes = []
+        L.kvq_debug_take.restype = C.c_uint32
         L.kvq_quantize.argtypes = [vp, i32, vp, i64, i64, i64, vp, vp, vp, vp, vp]
         L.kvq_quantize_kv.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, vp, vp, vp]
         L.kvq_logits.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, vp, vp, vp]
@@ -133,6 +140,18 @@ def kvq_codebook(bits: int):
 
 def strerror(status: int) -> str:
     return lib().kvq_strerror(status).decode()
+
+
+def debug_build() -> bool:
+    """True for the bounds-checked build (KVQ_DEBUG)."""
+    return bool(lib().kvq_debug_build())
+
+
+def debug_take() -> int:
+    """First failed bounds check on the current device since the last call
+    (file id << 16 | line; 0 if none), clearing the records (debug build;
+    0 in others).  Call it after a device synchronisation."""
+    return int(lib().kvq_debug_take())
 
 
 def _check(status: int, what: str):

@@ -172,6 +172,23 @@ int64_t kvq_code_bytes_per_vec(const kvq_ctx *ctx);
 /* Static description of a status code (never NULL). */
 const char *kvq_strerror(kvq_status s);
 
+/* Bounds-checked debug build (libkvq compiled with KVQ_DEBUG defined; the
+ * build script writes it as libkvq_debug.so beside libkvq.so).  Its kernels
+ * check the ranges of the token, record, tile and split indices they form
+ * against the shapes of the launch; a failed check does not stop the kernel
+ * but records, per kernel source file and device, the source line of the
+ * first failure.  The kernels also fill their LDS with a NaN pattern before
+ * first use, so a read of LDS that nothing wrote shows in the results.
+ * kvq_debug_build() is 1 in that build, 0 otherwise.
+ * kvq_debug_take() returns the first failure recorded on the current device
+ * since the last call (source file id 1..6 in bits 16..31, line in bits
+ * 0..15; 0 if none, 0xFFFFFFFF if the record could not be read) and clears
+ * the records; call it once the work it should cover has completed (after a
+ * device synchronisation).  In other builds it returns 0 and touches no
+ * device. */
+int32_t kvq_debug_build(void);
+uint32_t kvq_debug_take(void);
+
 /* Quantise T tokens of K or V ([PQ] sec. 2 and [TQ] Estagio 1; QJL residual:
  * [TQ] Estagio 2).
  *   kind        KVQ_KIND_K or KVQ_KIND_V (selects D)

@@ -44,6 +44,8 @@ kvq_config base(int bits, int mode, int H)
 
 int main()
 {
+    // a release build of the host code: no bounds-check records
+    CHECK(kvq_debug_build() == 0 && kvq_debug_take() == 0u);
     // tables without a context
     for (int b = 1; b <= 4; ++b) {
         float c[16], t[16];
