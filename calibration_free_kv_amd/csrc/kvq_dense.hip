@@ -77,6 +77,10 @@ __global__ __launch_bounds__(64 * kDenseWaves) void k_quantize_dense(
     __shared__ __align__(16) uint32_t stage[kDenseWaves][64 * SR];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    KVQ_CHECK(N >= 0 && Ntot >= N && n_groups * 64 >= Ntot);
+    KVQ_POISON_LDS(qs, 2 * kD * kQRow / 2, tid, 64 * kDenseWaves);
+    KVQ_POISON_LDS(stage, kDenseWaves * 64 * SR, tid, 64 * kDenseWaves);
+    if (KVQ_DEBUG_ON) __syncthreads();
     // LDS row 16 nb + a holds Q row 32 (nb / 2) + 8 (a / 4) + 4 (nb % 2) + a % 4:
     // accumulator r of tile nb in lane group kg is then output 32 (nb / 2) + 8 kg + 4 (nb % 2) + r
     for (int i = tid; i < 2 * kD * 16; i += 64 * kDenseWaves) {

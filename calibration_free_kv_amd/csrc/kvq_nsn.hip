@@ -98,6 +98,10 @@ __global__ __launch_bounds__(64 * kStatWaves) void k_nsn_stats(const u4_t *__res
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int h = blockIdx.x / n_chunks, chunk = blockIdx.x % n_chunks;
     const int64_t c0 = (int64_t)chunk * kChunk, c1 = min(T, c0 + kChunk);
+    KVQ_CHECK(c0 < c1 && T <= ldx);
+    KVQ_POISON_LDS(lds, kStatWaves * kTile * 16 * 4, threadIdx.x, 64 * kStatWaves);
+    KVQ_POISON_LDS(red, kStatWaves * kD, threadIdx.x, 64 * kStatWaves);
+    if (KVQ_DEBUG_ON) __syncthreads();
     const u4_t *xh = x + (int64_t)h * ldx * 16;  // the head's tokens (ldx apart per head)
     u4_t *L = lds[wv];
     const uint32_t *Ld = (const uint32_t *)L;
@@ -508,6 +512,12 @@ __global__ __launch_bounds__(kWavesN * 64) __attribute__((amdgpu_waves_per_eu(2,
     __shared__ u4_t lds[kWavesN][kBufN];
     __shared__ int next_tile;
     const int tid = threadIdx.x;
+    KVQ_POISON_LDS(s_cbA, 2 * kVqK * 4, tid, kWavesN * 64);
+    KVQ_POISON_LDS(s_cbl, 2 * kVqK * 2, tid, kWavesN * 64);
+    KVQ_POISON_LDS(s_bias, kVqK, tid, kWavesN * 64);
+    KVQ_POISON_LDS(lds, kWavesN * kBufN * 4, tid, kWavesN * 64);
+    KVQ_CHECK(n_tiles % tiles_per_h == 0 && tiles_per_h * kTileN >= T && T <= ldx && T <= ldt);
+    if (KVQ_DEBUG_ON) __syncthreads();
     for (int j = tid; j < kVqK; j += kWavesN * 64) {
         const u4_t c = a.cb_hi[j];
         s_cbA[2 * j] = u4_t{c.x, c.y, c.x, c.y};
@@ -535,6 +545,7 @@ __global__ __launch_bounds__(kWavesN * 64) __attribute__((amdgpu_waves_per_eu(2,
         const int64_t hq = t / tph;
         const int64_t tq = (t - hq * tph) * kTileN;
         const int nq = (int)min((int64_t)kTileN, T - tq);
+        KVQ_CHECK(t >= 0 && t < n_tiles && nq >= 1 && tq >= 0);
         nsn_tile_to_lds(a.x + (hq * ldx + tq) * 16, nq, o + hq * ldo, L, L + kRowsN + 32 * slot, lane);
     };
     uint32_t w[32];
@@ -657,6 +668,7 @@ __global__ __launch_bounds__(kWavesN * 64) __attribute__((amdgpu_waves_per_eu(2,
         const float s1v = nx / kSqrtD;
         if (!upper && v < nv) {  // lanes of tokens past a ragged tail searched stale rows
             const int64_t t = v0 + v;
+            KVQ_CHECK(t0 + v < T && hh < n_tiles / tiles_per_h);
             a.codes[t] = u4_t{code[0], code[1], code[2], code[3]};
             if (a.s1) a.s1[t] = s1v;
             a.s2[t] = s2v;
@@ -843,6 +855,11 @@ __global__ __launch_bounds__(kWavesN * 64) __attribute__((amdgpu_waves_per_eu(2,
     __shared__ u4_t lds[kWavesN][kBufN];
     __shared__ int next_tile;
     const int tid = threadIdx.x;
+    KVQ_POISON_LDS(s_sh, 2 * 2 * kGsrqShapeU2 * 2, tid, kWavesN * 64);
+    KVQ_POISON_LDS(s_tab, 2 * kGsrqL + 2 * (kGsrqL - 1), tid, kWavesN * 64);
+    KVQ_POISON_LDS(lds, kWavesN * kBufN * 4, tid, kWavesN * 64);
+    KVQ_CHECK(n_tiles % tiles_per_h == 0 && tiles_per_h * kTileN >= T);
+    if (KVQ_DEBUG_ON) __syncthreads();
     {
         const u4_t *src = reinterpret_cast<const u4_t *>(a.shapes16);
         u4_t *dst = reinterpret_cast<u4_t *>(s_sh);
@@ -866,6 +883,7 @@ __global__ __launch_bounds__(kWavesN * 64) __attribute__((amdgpu_waves_per_eu(2,
         const int64_t hq = t / tph;
         const int64_t tq = (t - hq * tph) * kTileN;
         const int nq = (int)min((int64_t)kTileN, T - tq);
+        KVQ_CHECK(t >= 0 && t < n_tiles && nq >= 1 && tq >= 0);
         nsn_tile_to_lds(a.x + (hq * T + tq) * 16, nq, o + hq * kD, L, L + kRowsN + 32 * slot, lane);
     };
     const u2_t *sh1 = s_sh, *sh2 = s_sh + kGsrqShapeU2;
@@ -936,6 +954,7 @@ __global__ __launch_bounds__(kWavesN * 64) __attribute__((amdgpu_waves_per_eu(2,
         }
         if (!upper && v < nv) {  // lanes of tokens past a ragged tail searched stale rows
             const int64_t t = hh * T + t0 + v;
+            KVQ_CHECK(t0 + v < T && hh < n_tiles / tiles_per_h);
             uint32_t d0 = 0, d1 = 0, d2 = 0;
 #pragma unroll
             for (int S = 0; S < 4; ++S) {

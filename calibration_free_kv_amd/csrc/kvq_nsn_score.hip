@@ -149,6 +149,9 @@ __global__ __launch_bounds__(kThreadsN) void k_nsn_logits(const half_t *__restri
     const int64_t bg = blockIdx.y, b = bg / Hkv, g = bg % Hkv;
     const int64_t Hq = Hkv * G, qbase = b * Hq + g * G;
     const int64_t c0 = (int64_t)blockIdx.x * kLogitChunk, c1 = min(T, c0 + kLogitChunk);
+    KVQ_CHECK(c0 < c1 && g < Hkv);
+    KVQ_POISON_LDS(&sm, sizeof(sm) / 4, threadIdx.x, kThreadsN);
+    if (KVQ_DEBUG_ON) __syncthreads();
     // the keys' loads go out before the prologue (a token past the end
     // re-reads the chunk's first one and is not stored)
     u4_t code[NT];
@@ -240,6 +243,10 @@ __global__ __launch_bounds__(64 * dec_waves<G>()) void k_nsn_part(const half_t *
     const int64_t bg = blockIdx.y, b = bg / Hkv, g = bg % Hkv;
     const int64_t qbase = b * Hkv * G + g * G;
     const int64_t c0 = (int64_t)blockIdx.x * chunk, c1 = min(T, c0 + chunk);
+    KVQ_CHECK(c0 < c1 && (DQ || T <= ldt) && (int64_t)blockIdx.x < n_part &&
+              (!GROUPED || (c0 % gsize == 0 && (c1 + gsize - 1) / gsize <= ngc)));
+    KVQ_POISON_LDS(&sm, sizeof(sm) / 4, threadIdx.x, 64 * NW);
+    if (KVQ_DEBUG_ON) __syncthreads();
     // The first tile's loads go out before the prologue, every later tile's
     // before the current one is processed.  Lanes past the end of the range
     // (and every lane of a wave the range gives no tile) load the range's

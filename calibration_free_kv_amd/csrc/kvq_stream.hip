@@ -37,6 +37,7 @@ __global__ __launch_bounds__(64 * kFlushWaves) void k_flush(const half_t *__rest
     const int kind = v >= BH * R;
     const int64_t rem = v - kind * BH * R, bh = rem / R, t = rem - bh * R;
     const int g = (int)(bh % H);
+    KVQ_CHECK(R <= R_cap && T0 >= 0 && T0 + R <= T_cap && bh < BH && t < R);
     const h2_t x = reinterpret_cast<const h2_t *>((kind ? vt : kt) + (bh * R_cap + t) * kD)[lane];
     const float x0 = (float)x.x, x1 = (float)x.y;
     const float rho = __builtin_sqrtf(wave_sum(fmaf(x1, x1, x0 * x0)));

@@ -1,13 +1,15 @@
 """The bounds-checked debug build (libkvq_debug.so, compiled with KVQ_DEBUG).
 
-A child process loads it (KVQ_LIB) and runs the MSE and QJL paths on seeded
-inputs: K and V quantised in one launch at b = 1..4 over a ragged token count,
-logits, decode with automatic splits, with one split (several tiles per wave)
-and without allocation, the streaming decode and its flush, the QJL quantiser
-and its logits.  The check records are read after every call.  No check may
-fail, and every result must equal, bit for bit, the one the release library
-gives in this process: the checks and the NaN fill of LDS change no
-arithmetic, and a kernel that read LDS it never wrote would differ."""
+A child process loads it (KVQ_LIB) and runs the paths on seeded inputs: K
+and V quantised in one launch at b = 1..4 over a ragged token count, logits,
+decode with automatic splits, with one split (several tiles per wave) and
+without allocation, the streaming decode and its flush; NSN-VQ (plain and
+adaptive scale) and GSRQ encoders with logits and decode from their records;
+the dense rotation; the QJL quantiser and its logits.  The check records
+are read after every call.  No check may fail, and every result must equal,
+bit for bit, the one the release library gives in this process: the checks
+and the NaN fill of LDS change no arithmetic, and a kernel that read LDS it
+never wrote would differ."""
 import os
 import subprocess
 import sys
@@ -69,6 +71,44 @@ def run_cases():
         for n, t in g.items():
             res["fl%s%d" % (n, bits)] = to_np(t)
         ctx.close()
+    # NSN-VQ (plain and adaptive scale), GSRQ: encoders over the 8 heads of K and
+    # V, logits and decode from their records
+    cb = np.loadtxt(os.path.join(ROOT, "tests", "golden", "vq_codebook_256x8.txt"), dtype=np.float32).reshape(256, 8)
+    lines = [ln.split() for ln in open(os.path.join(ROOT, "tests", "golden", "gsrq_tables_256x32.txt"))
+             if not ln.startswith("#")]
+    gt = dict(S1=np.array(lines[0:256], dtype=np.float32), G1=np.array(lines[256], dtype=np.float32),
+              S2=np.array(lines[257:513], dtype=np.float32), G2=np.array(lines[513], dtype=np.float32))
+    H = inp["Hkv"]
+
+    def per_head(e, rec):
+        return dict(codes=e["codes"].view(1, H, T, rec), s1=e["s1"].view(1, H, T), s2=e["s2"].view(1, H, T),
+                    o=e["o"].view(1, H, 128))
+
+    for name, ctx, rec in (("nsn", kvq.Context(H, 1, mode=kvq.KVQ_MODE_NSN_VQ, vq_codebook=cb), 16),
+                           ("nsna", kvq.Context(H, 1, mode=kvq.KVQ_MODE_NSN_VQ, vq_codebook=cb,
+                                                nsn_options=kvq.KVQ_NSN_ADAPTIVE_SCALE), 16),
+                           ("gsrq", kvq.Context(H, 1, mode=kvq.KVQ_MODE_GSRQ, gsrq_tables=gt), 12)):
+        enc = ctx.gsrq_quantize if name == "gsrq" else ctx.nsn_vq_quantize
+        ek, ev = enc(k[0]), enc(v[0])
+        take(name + " encode")
+        for n, t in ek.items():
+            res["%s_%s" % (name, n)] = to_np(t)
+        kd, vd = per_head(ek, rec), per_head(ev, rec)
+        lg = ctx.gsrq_logits(q, **kd) if name == "gsrq" else ctx.nsn_logits(q, **kd)
+        res[name + "_lg"] = to_np(lg)
+        take(name + " logits")
+        dec = ctx.gsrq_attn_decode if name == "gsrq" else ctx.nsn_attn_decode
+        res[name + "_dec"] = to_np(dec(q, kd, vd))
+        take(name + " decode")
+        ctx.close()
+    # dense rotation: quantize K and V, decode
+    ctx = kvq.Context(H, 3, rot_Q=synth.random_orthogonal(5).astype(np.float32))
+    ko, vo = ctx.quantize_kv(k, v)
+    take("dense quantize_kv")
+    res["dense_kc"], res["dense_kn"] = to_np(ko["codes"]), to_np(ko["norms"])
+    res["dense_dec"] = to_np(ctx.attn_decode(q, ko["codes"], ko["norms"], vo["codes"], vo["norms"]))
+    take("dense decode")
+    ctx.close()
     qi = synth.make("long128k_qjl", T=T)
     ctx = kvq.Context(qi["Hkv"], 2, qi["signs_k"], qi["signs_v"], mode=kvq.KVQ_MODE_MSE_QJL, qjl_S=qi["S"])
     qo = ctx.quantize(kvq.KVQ_KIND_K, torch.from_numpy(qi["k"]).cuda())
