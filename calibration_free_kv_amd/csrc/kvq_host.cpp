@@ -251,6 +251,22 @@ bool decode_group_built(int64_t G) { return G == 1 || G == 2 || G == 4; }
 
 }  // namespace
 
+// KVQ_SPLITS: a positive integer in the environment replaces the automatic
+// split count of the decode entry points (read once per process; an explicit
+// n_split still wins, and the usual clamps apply).
+static int env_splits()
+{
+    static const int v = [] {
+        const char *e = std::getenv("KVQ_SPLITS");
+        if (!e || !*e) return 0;
+        char *end = nullptr;
+        const long n = std::strtol(e, &end, 10);
+        return (*end == '\0' && n > 0 && n <= (1L << 20)) ? (int)n : 0;
+    }();
+    return v;
+}
+static int auto_splits(int automatic) { return env_splits() ? env_splits() : automatic; }
+
 extern "C" {
 
 int32_t kvq_debug_build(void) { return KVQ_DEBUG_ON; }
@@ -620,7 +636,7 @@ kvq_status kvq_attn_decode_splits(kvq_ctx *ctx, const void *q_f16, int64_t B, in
     if (T > (int64_t(1) << 31)) return KVQ_E_INVAL;
     if (ws_bytes < kvq::decode_ws_bytes(B, H_q, ctx->H, T)) return KVQ_E_WORKSPACE;
     const int64_t max_split = kvq::decode_max_splits(T);
-    int ns = n_split == 0 ? kvq::decode_auto_splits(B, ctx->H, T) : n_split;
+    int ns = n_split == 0 ? auto_splits(kvq::decode_auto_splits(B, ctx->H, T)) : n_split;
     if (ns > max_split) ns = (int)max_split;
     if (ns < 1) ns = 1;
     if (sm_scale == 0.f) sm_scale = 1.0f / std::sqrt((float)kvq::kD);
@@ -655,7 +671,7 @@ kvq_status kvq_attn_decode_noalloc(kvq_ctx *ctx, const void *q_f16, int64_t B, i
     if (T > (int64_t(1) << 31) || B * H_q > (int64_t(1) << 31)) return KVQ_E_INVAL;
     const bool dense = ctx->rotation == KVQ_ROTATION_DENSE;
     // the split count kvq_attn_decode would take, lowered until the scratch holds it
-    int64_t ns = std::min<int64_t>(kvq::decode_auto_splits(B, ctx->H, T), kvq::decode_max_splits(T));
+    int64_t ns = std::min<int64_t>(auto_splits(kvq::decode_auto_splits(B, ctx->H, T)), kvq::decode_max_splits(T));
     if (ns < 1) ns = 1;
     while (ns > 1 && kvq::noalloc_decode_bytes(B, H_q, ctx->H, (int)ns, dense) > kvq::kNoAllocScratchBytes) --ns;
     if (kvq::noalloc_decode_bytes(B, H_q, ctx->H, (int)ns, dense) > kvq::kNoAllocScratchBytes) return KVQ_E_WORKSPACE;
@@ -724,7 +740,7 @@ kvq_status kvq_attn_decode_stream(kvq_ctx *ctx, const void *q_f16, int64_t B, in
     if (ws_bytes < kvq_attn_decode_stream_ws_bytes(ctx, B, H_q, T_cap)) return KVQ_E_WORKSPACE;
     int ns = 1;
     if (T > 0) {
-        ns = kvq::decode_auto_splits(B, ctx->H, T);
+        ns = auto_splits(kvq::decode_auto_splits(B, ctx->H, T));
         const int64_t cap = std::min<int64_t>(kvq::decode_max_splits(T), kvq::kMaxSplits - 1);
         if (ns > cap) ns = (int)cap;
         if (ns < 1) ns = 1;
@@ -810,7 +826,7 @@ kvq_status kvq_nsn_attn_decode_splits(kvq_ctx *ctx, const void *q_f16, int64_t B
     if (T > (int64_t(1) << 31) || B * ctx->H > 65535) return KVQ_E_INVAL;
     if (ws_bytes < kvq::nsn_decode_ws_bytes(B, H_q, T)) return KVQ_E_WORKSPACE;
     const int64_t max_split = kvq::decode_max_splits(T);
-    int ns = n_split == 0 ? kvq::nsn_decode_auto_splits(ctx, B, T) : n_split;
+    int ns = n_split == 0 ? auto_splits(kvq::nsn_decode_auto_splits(ctx, B, T)) : n_split;
     if (ns > max_split) ns = (int)max_split;
     if (ns < 1) ns = 1;
     if (sm_scale == 0.f) sm_scale = 1.0f / std::sqrt((float)kvq::kD);
@@ -880,7 +896,7 @@ kvq_status kvq_gsrq_attn_decode(kvq_ctx *ctx, const void *q_f16, int64_t B, int6
     if (T > (int64_t(1) << 31) || B * ctx->H > 65535) return KVQ_E_INVAL;
     if (ws_bytes < kvq::nsn_decode_ws_bytes(B, H_q, T)) return KVQ_E_WORKSPACE;
     const int64_t max_split = kvq::decode_max_splits(T);
-    int ns = n_split == 0 ? kvq::nsn_decode_auto_splits(ctx, B, T) : n_split;
+    int ns = n_split == 0 ? auto_splits(kvq::nsn_decode_auto_splits(ctx, B, T)) : n_split;
     if (ns > max_split) ns = (int)max_split;
     if (ns < 1) ns = 1;
     if (sm_scale == 0.f) sm_scale = 1.0f / std::sqrt((float)kvq::kD);
@@ -958,7 +974,7 @@ kvq_status kvq_nsn_attn_decode_dq(kvq_ctx *ctx, const void *q_f16, int64_t B, in
     if (T > (int64_t(1) << 31) || B * ctx->H > 65535) return KVQ_E_INVAL;
     if (ws_bytes < kvq::nsn_decode_ws_bytes(B, H_q, T)) return KVQ_E_WORKSPACE;
     const int64_t max_split = kvq::decode_max_splits(T);
-    int ns = n_split == 0 ? kvq::nsn_decode_auto_splits(ctx, B, T) : n_split;
+    int ns = n_split == 0 ? auto_splits(kvq::nsn_decode_auto_splits(ctx, B, T)) : n_split;
     if (ns > max_split) ns = (int)max_split;
     if (ns < 1) ns = 1;
     if (sm_scale == 0.f) sm_scale = 1.0f / std::sqrt((float)kvq::kD);
@@ -1039,7 +1055,7 @@ kvq_status kvq_nsn_attn_decode_stream(kvq_ctx *ctx, const void *q_f16, int64_t B
     if (ws_bytes < kvq::nsn_stream_ws_bytes(B, H_q, T_cap)) return KVQ_E_WORKSPACE;
     int ns = 1;
     if (T > 0) {
-        ns = n_split == 0 ? kvq::nsn_decode_auto_splits(ctx, B, T) : n_split;
+        ns = n_split == 0 ? auto_splits(kvq::nsn_decode_auto_splits(ctx, B, T)) : n_split;
         const int64_t cap = std::min<int64_t>(T / 64, kvq::kMaxSplits - 1);
         if (ns > cap) ns = (int)cap;
         if (ns < 1) ns = 1;

@@ -14,9 +14,10 @@ import numpy as np
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-# KVQ_LIB selects another build of the library for the process, e.g. the
-# bounds-checked libkvq_debug.so beside it
-LIB_PATH = os.environ.get("KVQ_LIB") or os.path.join(_PKG, "libkvq.so")
+# KVQ_LIB selects another build of the library for the process; KVQ_DEBUG
+# (set, and not "0") selects the bounds-checked libkvq_debug.so beside it
+LIB_PATH = os.environ.get("KVQ_LIB") or os.path.join(
+    _PKG, "libkvq_debug.so" if os.environ.get("KVQ_DEBUG", "0") not in ("", "0") else "libkvq.so")
 
 KVQ_OK, KVQ_E_INVAL, KVQ_E_UNSUPPORTED, KVQ_E_DEVICE, KVQ_E_NOMEM, KVQ_E_WORKSPACE = range(6)
 KVQ_MODE_MSE, KVQ_MODE_MSE_QJL, KVQ_MODE_NSN_VQ = 0, 1, 2

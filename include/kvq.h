@@ -257,7 +257,10 @@ kvq_status kvq_attn_decode(kvq_ctx *ctx, const void *q_f16, int64_t B, int64_t H
 
 /* As kvq_attn_decode with an explicit number of token splits per (batch, KV
  * head) (0 = automatic).  The result does not depend on n_split beyond fp32
- * rounding.  n_split is clamped to [1, min(512, ceil(T / 64))]. */
+ * rounding.  n_split is clamped to [1, min(512, ceil(T / 64))].
+ * The automatic count (here and in every decode entry point) is about one
+ * block per compute unit, or the value of the environment variable
+ * KVQ_SPLITS when it holds a positive integer (read once per process). */
 kvq_status kvq_attn_decode_splits(kvq_ctx *ctx, const void *q_f16, int64_t B, int64_t H_q,
                                   int64_t T, const uint8_t *k_codes, const float *k_norms,
                                   const uint8_t *v_codes, const float *v_norms, float sm_scale,

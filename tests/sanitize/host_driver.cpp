@@ -183,6 +183,10 @@ int main()
     CHECK(kvq_attn_decode(mse, q.p, B, Hq, T, codes.as<uint8_t>(), norms.as<float>(), codes.as<uint8_t>(), norms.as<float>(), -1.f, out.as<float>(), ws.p, wsb, st0) == KVQ_E_INVAL);
     CHECK(kvq_attn_decode(mse, q.p, B, Hq, T, codes.as<uint8_t>(), norms.as<float>(), codes.as<uint8_t>(), norms.as<float>(), 0.f, out.as<float>(), ws.p, wsb, st0) == KVQ_OK);
     CHECK(std::strcmp(g_last.what, "decode") == 0 && g_last.n_split >= 1 && g_last.n_split <= (T + 63) / 64);
+    if (const char *e = std::getenv("KVQ_SPLITS")) {  // the automatic count replaced (then clamped)
+        const int want = std::atoi(e);
+        CHECK(want > 0 && g_last.n_split == (want < (T + 63) / 64 ? want : (T + 63) / 64));
+    }
     CHECK(kvq_attn_decode_splits(mse, q.p, B, Hq, T, codes.as<uint8_t>(), norms.as<float>(), codes.as<uint8_t>(), norms.as<float>(), 0.f, out.as<float>(), ws.p, wsb, 1000000, st0) == KVQ_OK);
     CHECK(g_last.n_split == (T + 63) / 64);
     CHECK(kvq_attn_decode(mse, q.p, B, H * 8, T, codes.as<uint8_t>(), norms.as<float>(), codes.as<uint8_t>(), norms.as<float>(), 0.f, out.as<float>(), ws.p, wsb, st0) == KVQ_E_UNSUPPORTED);

@@ -139,3 +139,23 @@ def test_null_context_calls():
                                   None, 0, 0, None) == kvq.KVQ_E_INVAL
     for s in range(6):
         assert kvq.strerror(s)
+
+
+def test_debug_build_selection():
+    """The release library reports no debug build and no check records (it
+    touches no device for them); KVQ_DEBUG selects the bounds-checked
+    libkvq_debug.so in a fresh process, KVQ_LIB any given build."""
+    import subprocess
+    import sys
+    assert kvq.debug_build() is False and kvq.debug_take() == 0
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    prog = ("import sys; sys.path.insert(0, %r)\n"
+            "from calibration_free_kv_amd import kvq\n"
+            "print(kvq.LIB_PATH.rsplit('/', 1)[-1], kvq.debug_build())\n") % root
+    for env, want in (({"KVQ_DEBUG": "1"}, "libkvq_debug.so True"), ({"KVQ_DEBUG": "0"}, "libkvq.so False"),
+                      ({"KVQ_LIB": kvq.LIB_PATH.replace("libkvq.so", "libkvq_debug.so")},
+                       "libkvq_debug.so True")):
+        e = {k: v for k, v in os.environ.items() if k not in ("KVQ_DEBUG", "KVQ_LIB")}
+        e.update(env)
+        r = subprocess.run([sys.executable, "-c", prog], env=e, capture_output=True, text=True, timeout=120)
+        assert r.returncode == 0 and r.stdout.split() == want.split(), (env, r.stdout, r.stderr[-1000:])

@@ -47,3 +47,6 @@ def test_host_side_under_sanitizers(tmp_path):
                 "-o", exe, os.path.join(SAN, "host_driver.cpp"), os.path.join(SAN, "hip_stubs.cpp"),
                 os.path.join(CSRC, "kvq_host.cpp"), os.path.join(CSRC, "kvq_layout.cpp")], tmp_path, exe)
     assert "host ok" in out
+    # the same program with the KVQ_SPLITS override of the automatic split count
+    r = subprocess.run([exe], capture_output=True, text=True, env=dict(ENV, KVQ_SPLITS="3"), timeout=300)
+    assert r.returncode == 0 and "host ok" in r.stdout, (r.stdout[-2000:], r.stderr[-4000:])
