@@ -27,8 +27,11 @@ counter record for the same kernel source, or null when the kernel source
 has changed since the counters were taken.
 
 rows = every step of the path on its own workload (all sizes full), timed the
-same way, each with its algorithmic bytes (and flops where the matrix cores
-do the work) and the fraction of the matching MI355X peak.
+same way (warmed graph replays over rotating buffer sets, the last launch
+checked against an eager one), each with its algorithmic bytes (and flops
+where the matrix cores do the work) and the fraction of the matching MI355X
+peak.  The two 4096-vector rows measure latency instead: events around each
+eager launch.
 
 cpu_baseline = the CPU oracle (plain C, double precision) on the same step,
 once on one thread and once on every host thread the process is given (the
@@ -165,6 +168,20 @@ def run_graph(timer, launch, reps, per_graph=10, check=None, warm_s=0.1):
     ms = np.array([a.elapsed_time(b) for a, b in ev]) / per_graph
     del g
     return float(ms.mean()), float(np.percentile(ms, 10)), float(np.percentile(ms, 90))
+
+
+def eager_check(timer, launch, i, outs):
+    """check() for run_graph: the tensors outs, as the replays left them,
+    equal what an eager launch(i) writes (i = the graph's last launch, the
+    last writer of outs)."""
+    torch = timer.torch
+
+    def check():
+        got = [t.clone() for t in outs]
+        launch(i)
+        torch.cuda.synchronize()
+        assert all(torch.equal(a, b) for a, b in zip(got, outs)), "graph replay differs from the eager launch"
+    return check
 
 
 def row(ms, p10, p90, nbytes=None, flops=None, **extra):
@@ -428,6 +445,11 @@ def rows(torch, kvq, synth, dev, timer, reps, oracle_rates):
     out = {}
     rng_sets = lambda total_bytes: max(2, int(np.ceil(600e6 / max(total_bytes, 1))))  # noqa: E731
 
+    def graph(launch, per_graph, outs):
+        # launches 0 .. per_graph - 1 back to back from a warmed graph replay,
+        # checked against an eager launch of the last one
+        return run_graph(timer, launch, reps, per_graph, check=eager_check(timer, launch, per_graph - 1, outs))
+
     # l8b32k: quantize K+V and decode at b = 2, 3, 4
     inp = synth.make("l8b32k")
     B, Hkv, T = inp["k"].shape[:3]
@@ -448,7 +470,7 @@ def rows(torch, kvq, synth, dev, timer, reps, oracle_rates):
             k, v = xs[i % len(xs)]
             c = cs[i % ns]
             kvq.kvq_quantize_kv(ctx, k, v, B, Hkv, T, c[0], c[1], c[2], c[3])
-        out["quantize_kv_l8b32k_b%d" % bits] = row(*timer.run(quant, reps, 4 + ns), nbytes=quant_bytes(2 * n, bits),
+        out["quantize_kv_l8b32k_b%d" % bits] = row(*graph(quant, ns, cs[ns - 1]), nbytes=quant_bytes(2 * n, bits),
                                                     units_per_launch=2 * n, unit="vectors")
         outb = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
         ws = ctx.decode_ws(B, Hq, T)
@@ -456,7 +478,7 @@ def rows(torch, kvq, synth, dev, timer, reps, oracle_rates):
         def dec(i):
             c = cs[i % ns]
             kvq.kvq_attn_decode(ctx, q, B, Hq, T, c[0], c[1], c[2], c[3], 0.0, outb, ws)
-        out["attn_decode_l8b32k_b%d" % bits] = row(*timer.run(dec, reps, 5), nbytes=decode_bytes(n, bits),
+        out["attn_decode_l8b32k_b%d" % bits] = row(*graph(dec, ns, [outb]), nbytes=decode_bytes(n, bits),
                                                     units_per_launch=n, unit="keys", buffer_sets=ns)
         del cs, ctx
     sub = {k: v[:, :, :2048] for k, v in inp.items() if k in ("k", "v")}
@@ -480,7 +502,7 @@ def rows(torch, kvq, synth, dev, timer, reps, oracle_rates):
         c = cs[i % ns]
         kvq.kvq_quantize_kv(ctx, k, v, B, Hkv, T, c[0], c[1], c[2], c[3])
     # the rotation on the matrix cores: 128 x 128 products, high and low parts of Q
-    out["quantize_kv_dense_l8b32k_b3"] = row(*timer.run(quantd, reps, 4 + ns), nbytes=quant_bytes(2 * n, 3),
+    out["quantize_kv_dense_l8b32k_b3"] = row(*graph(quantd, ns, cs[ns - 1]), nbytes=quant_bytes(2 * n, 3),
                                              flops=2 * n * 2 * 2 * D * D, units_per_launch=2 * n, unit="vectors")
     outb = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
     ws = ctx.decode_ws(B, Hq, T)
@@ -488,7 +510,7 @@ def rows(torch, kvq, synth, dev, timer, reps, oracle_rates):
     def decd(i):
         c = cs[i % ns]
         kvq.kvq_attn_decode(ctx, q, B, Hq, T, c[0], c[1], c[2], c[3], 0.0, outb, ws)
-    out["attn_decode_dense_l8b32k_b3"] = row(*timer.run(decd, reps, 5), nbytes=decode_bytes(n, 3),
+    out["attn_decode_dense_l8b32k_b3"] = row(*graph(decd, ns, [outb]), nbytes=decode_bytes(n, 3),
                                              units_per_launch=n, unit="keys", buffer_sets=ns)
     del cs, ctx
     del xs, k0, v0
@@ -511,7 +533,7 @@ def rows(torch, kvq, synth, dev, timer, reps, oracle_rates):
     def quant16(i):
         c = cs[i % ns]
         kvq.kvq_quantize_kv(ctx, k0, v0, B, Hkv, T, c[0], c[1], c[2], c[3])
-    out["quantize_kv_batch16_b3"] = row(*timer.run(quant16, reps, ns), nbytes=quant_bytes(2 * n, 3),
+    out["quantize_kv_batch16_b3"] = row(*graph(quant16, ns, cs[ns - 1]), nbytes=quant_bytes(2 * n, 3),
                                         units_per_launch=2 * n, unit="vectors")
     outb = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
     ws = ctx.decode_ws(B, Hq, T)
@@ -519,7 +541,7 @@ def rows(torch, kvq, synth, dev, timer, reps, oracle_rates):
     def dec16(i):
         c = cs[i % ns]
         kvq.kvq_attn_decode(ctx, q, B, Hq, T, c[0], c[1], c[2], c[3], 0.0, outb, ws)
-    out["attn_decode_batch16_b3"] = row(*timer.run(dec16, reps, 5), nbytes=decode_bytes(n, 3),
+    out["attn_decode_batch16_b3"] = row(*graph(dec16, ns, [outb]), nbytes=decode_bytes(n, 3),
                                         units_per_launch=n, unit="keys", buffer_sets=ns)
     del cs, k0, v0, ctx
     torch.cuda.empty_cache()
@@ -544,7 +566,7 @@ def rows(torch, kvq, synth, dev, timer, reps, oracle_rates):
         c = cs[i % ns]
         kvq.kvq_quantize(ctx, kvq.KVQ_KIND_K, ks[i % 2], B, Hkv, T, c["codes"], c["norms"], c["qjl_signs"],
                          c["qjl_gamma"])
-    out["quantize_qjl_long128k_b2"] = row(*timer.run(qjl, reps, ns), nbytes=quant_bytes(n, 2, qjl=True),
+    out["quantize_qjl_long128k_b2"] = row(*graph(qjl, ns, list(cs[ns - 1].values())), nbytes=quant_bytes(n, 2, qjl=True),
                                           flops=n * 2 * D * D, units_per_launch=n, unit="vectors",
                                           note="flops = the S r projection, 2 d^2 per key")
     lo = [torch.empty((B, Hq, T), dtype=torch.float32, device=dev) for _ in range(2)]
@@ -552,7 +574,7 @@ def rows(torch, kvq, synth, dev, timer, reps, oracle_rates):
     def lg(i):
         c = cs[i % ns]
         kvq.kvq_logits(ctx, q, B, Hq, T, c["codes"], c["norms"], c["qjl_signs"], c["qjl_gamma"], lo[i % 2])
-    out["logits_qjl_long128k_b2"] = row(*timer.run(lg, reps, 5), nbytes=lb, units_per_launch=n * Hq,
+    out["logits_qjl_long128k_b2"] = row(*graph(lg, ns, [lo[(ns - 1) % 2]]), nbytes=lb, units_per_launch=n * Hq,
                                         unit="logits", buffer_sets=ns)
     # the same workload with the dense rotation (TurboQuant's Estagio 1 + 2)
     Qd = synth.random_orthogonal(31).astype(np.float32)
@@ -563,7 +585,7 @@ def rows(torch, kvq, synth, dev, timer, reps, oracle_rates):
         c = cs[i % ns]
         kvq.kvq_quantize(ctxd, kvq.KVQ_KIND_K, ks[i % 2], B, Hkv, T, c["codes"], c["norms"], c["qjl_signs"],
                          c["qjl_gamma"])
-    out["quantize_qjl_dense_long128k_b2"] = row(*timer.run(qjld, reps, ns), nbytes=quant_bytes(n, 2, qjl=True),
+    out["quantize_qjl_dense_long128k_b2"] = row(*graph(qjld, ns, list(cs[ns - 1].values())), nbytes=quant_bytes(n, 2, qjl=True),
                                                 flops=n * 2 * (2 * D * D + 2 * D * D), units_per_launch=n,
                                                 unit="vectors",
                                                 note="flops = rotation (Q as two fp16 parts) and projection "
@@ -572,7 +594,7 @@ def rows(torch, kvq, synth, dev, timer, reps, oracle_rates):
     def lgd(i):
         c = cs[i % ns]
         kvq.kvq_logits(ctxd, q, B, Hq, T, c["codes"], c["norms"], c["qjl_signs"], c["qjl_gamma"], lo[i % 2])
-    out["logits_qjl_dense_long128k_b2"] = row(*timer.run(lgd, reps, 5), nbytes=lb, units_per_launch=n * Hq,
+    out["logits_qjl_dense_long128k_b2"] = row(*graph(lgd, ns, [lo[(ns - 1) % 2]]), nbytes=lb, units_per_launch=n * Hq,
                                               unit="logits", buffer_sets=ns)
     del ctxd
     kk = inp["k"][:, :, :1024]
@@ -612,7 +634,9 @@ def rows(torch, kvq, synth, dev, timer, reps, oracle_rates):
     xsn = [x0] + [x0.clone() for _ in range(3)]
     o = ctx.nsn_vq_quantize(x0)
     ws = torch.empty(int(kvq.lib().kvq_nsn_vq_ws_bytes(ctx.handle, H, T)), dtype=torch.uint8, device=dev)
-    out["nsn_vq_8x65536"] = row(*timer.run(lambda i: ctx.nsn_vq_quantize(xsn[i % 4], out=o, ws=ws), reps, 4),
+    def nenc(i):
+        ctx.nsn_vq_quantize(xsn[i % 4], out=o, ws=ws)
+    out["nsn_vq_8x65536"] = row(*graph(nenc, 4, list(o.values())),
                                 nbytes=nsn_bytes(H * T), flops=H * T * 16 * 256 * 8 * 2, units_per_launch=H * T,
                                 unit="vectors", note="three launches (stats, mean, search); x is read twice; "
                                 "flops = exhaustive distances 16 x 256 x 8 x 2 per vector")
@@ -622,7 +646,9 @@ def rows(torch, kvq, synth, dev, timer, reps, oracle_rates):
                      dtype=np.float32).reshape(256, 8)
     ctxa = kvq.Context(H, 1, mode=kvq.KVQ_MODE_NSN_VQ, vq_codebook=cbc, nsn_options=kvq.KVQ_NSN_ADAPTIVE_SCALE,
                        device=dev.index)
-    out["nsn_vq_adaptive_8x65536"] = row(*timer.run(lambda i: ctxa.nsn_vq_quantize(xsn[i % 4], out=o, ws=ws), reps, 4),
+    def nenca(i):
+        ctxa.nsn_vq_quantize(xsn[i % 4], out=o, ws=ws)
+    out["nsn_vq_adaptive_8x65536"] = row(*graph(nenca, 4, list(o.values())),
                                          nbytes=nsn_bytes(H * T), flops=H * T * 16 * 256 * 8 * 2,
                                          units_per_launch=H * T, unit="vectors",
                                          note="adaptive scale folded into s2, cosine-refined codebook")
@@ -658,10 +684,10 @@ def rows(torch, kvq, synth, dev, timer, reps, oracle_rates):
     last = ns - 1
     out["nsn_logits_8x65536_g4"] = row(*run_graph(timer, nlg, reps, ns, check=same(lambda i: nlg(last), lgo)),
                                        nbytes=n * (16 + 8 + 4 * Hq // H), units_per_launch=n, unit="keys",
-                                       buffer_sets=ns, note="graph replay; 16 table lookups per key serve 4 heads")
+                                       buffer_sets=ns, note="16 table lookups per key serve 4 heads")
     out["nsn_attn_decode_8x65536_g4"] = row(*run_graph(timer, ndec, reps, ns, check=same(lambda i: ndec(last), dout)),
                                             nbytes=n * 2 * (16 + 8), units_per_launch=n, unit="keys",
-                                            buffer_sets=ns, note="graph replay; two launches (splits, merge)")
+                                            buffer_sets=ns, note="two launches (splits, merge)")
     e = synth.random_nsn_codes(40, (1, H, 1024))
     f = synth.random_nsn_codes(41, (1, H, 1024))
     qh = synth.random_tensor(42, (1, Hq, D))
@@ -679,7 +705,9 @@ def rows(torch, kvq, synth, dev, timer, reps, oracle_rates):
     odq = ctx.nsn_vq_quantize_dq(x0)
     wsq = torch.empty(int(kvq.lib().kvq_nsn_vq_dq_ws_bytes(ctx.handle, H, T)), dtype=torch.uint8, device=dev)
     dq_meta = H * T * (0.5 + 8 / 32) + H * (64 + 8)  # s1 nibbles and block pairs, mean nibbles and pairs
-    out["nsn_vq_dq_8x65536"] = row(*timer.run(lambda i: ctx.nsn_vq_quantize_dq(xsn[i % 4], out=odq, ws=wsq), reps, 4),
+    def nencq(i):
+        ctx.nsn_vq_quantize_dq(xsn[i % 4], out=odq, ws=wsq)
+    out["nsn_vq_dq_8x65536"] = row(*graph(nencq, 4, list(odq.values())),
                                    nbytes=H * T * (2 * D + 16 + 4) + dq_meta, flops=H * T * 16 * 256 * 8 * 2,
                                    units_per_launch=H * T, unit="vectors",
                                    note="three launches; 4-bit s1 (32-token blocks) and means")
@@ -695,7 +723,7 @@ def rows(torch, kvq, synth, dev, timer, reps, oracle_rates):
     out["nsn_attn_decode_dq_8x65536_g4"] = row(
         *run_graph(timer, ndecq, reps, ns, check=same(lambda i: ndecq(last), dout)),
         nbytes=n * 2 * (16 + 4.75), units_per_launch=n, unit="keys", buffer_sets=ns,
-        note="graph replay; s1 read as 4-bit codes with per-block pairs")
+        note="s1 read as 4-bit codes with per-block pairs")
     del kvd
 
     # gain-shape residual quantisation on the NSN front end (12-byte records):
@@ -710,7 +738,9 @@ def rows(torch, kvq, synth, dev, timer, reps, oracle_rates):
     xsn = [x0] + [x0.clone() for _ in range(3)]
     og = ctxg.gsrq_quantize(x0)
     wsg = torch.empty(int(kvq.lib().kvq_gsrq_ws_bytes(ctxg.handle, H, T)), dtype=torch.uint8, device=dev)
-    out["gsrq_8x65536"] = row(*timer.run(lambda i: ctxg.gsrq_quantize(xsn[i % 4], out=og, ws=wsg), reps, 4),
+    def genc(i):
+        ctxg.gsrq_quantize(xsn[i % 4], out=og, ws=wsg)
+    out["gsrq_8x65536"] = row(*graph(genc, 4, list(og.values())),
                               nbytes=H * T * (2 * D + 12 + 8), flops=H * T * 2 * 4 * 256 * 32 * 2,
                               units_per_launch=H * T, unit="vectors",
                               note="three launches (stats, mean, search); two stages of 256 shapes per 32-dim "
@@ -730,10 +760,10 @@ def rows(torch, kvq, synth, dev, timer, reps, oracle_rates):
     last = ns - 1
     out["gsrq_logits_8x65536_g4"] = row(*run_graph(timer, glg, reps, ns, check=same(lambda i: glg(last), lgo)),
                                         nbytes=n * (12 + 8 + 4 * Hq // H), units_per_launch=n, unit="keys",
-                                        buffer_sets=ns, note="graph replay; 8 table lookups per key serve 4 heads")
+                                        buffer_sets=ns, note="8 table lookups per key serve 4 heads")
     out["gsrq_attn_decode_8x65536_g4"] = row(*run_graph(timer, gdec, reps, ns, check=same(lambda i: gdec(last), dout)),
                                              nbytes=n * 2 * (12 + 8), units_per_launch=n, unit="keys",
-                                             buffer_sets=ns, note="graph replay; two launches (splits, merge)")
+                                             buffer_sets=ns, note="two launches (splits, merge)")
     del kvg, ctxg
 
     # streaming NSN-VQ cache: 65408 packed tokens in flush groups of 128 (each
@@ -762,10 +792,10 @@ def rows(torch, kvq, synth, dev, timer, reps, oracle_rates):
     out["nsn_attn_decode_stream_8x65408_g4"] = row(
         *run_graph(timer, nsdec, reps, ns, check=same(lambda i: nsdec(last), dout)),
         nbytes=n * 2 * (16 + 8) + H * (T_s // Gs) * 2 * D * 4 + H * R_s * 2 * 2 * D, units_per_launch=n + H * R_s,
-        unit="keys", buffer_sets=ns, note="graph replay; per-group means; three launches (window, splits, merge)")
+        unit="keys", buffer_sets=ns, note="per-group means; three launches (window, splits, merge)")
     out["nsn_flush_group128"] = row(*run_graph(timer, nsflush, reps, ns), nbytes=2 * H * Gs * (2 * D + 24),
                                     units_per_launch=2 * H * Gs, unit="vectors", buffer_sets=ns,
-                                    note="graph replay; K and V, three launches each; latency-bound (2048 vectors)")
+                                    note="K and V, three launches each; latency-bound (2048 vectors)")
     del kvs, wins, ctx
 
     # streaming cache: decode over 32704 packed tokens (of 32768 slots) plus a
@@ -800,10 +830,10 @@ def rows(torch, kvq, synth, dev, timer, reps, oracle_rates):
     out["attn_decode_stream_l8b32k_b3"] = row(
         *run_graph(timer, sdec, reps, ns, check=same(lambda i: sdec(last), sout)),
         nbytes=n * 2 * rec_bytes(3) + Hkv * R_s * 2 * 2 * D, units_per_launch=n + Hkv * R_s, unit="keys",
-        buffer_sets=ns, note="graph replay; 32704 packed + 64 fp16 window tokens per KV head; two launches")
+        buffer_sets=ns, note="32704 packed + 64 fp16 window tokens per KV head; two launches")
     out["flush_window64_b3"] = row(*run_graph(timer, sflush, reps, ns), nbytes=quant_bytes(2 * Hkv * R_s, 3),
                                    units_per_launch=2 * Hkv * R_s, unit="vectors", buffer_sets=ns,
-                                   note="graph replay; latency-bound (1024 vectors)")
+                                   note="latency-bound (1024 vectors)")
     del pk, win, ctx
     torch.cuda.empty_cache()
     return out
