@@ -239,13 +239,15 @@ def test_dense_qjl_quantize_ragged(bits):
     assert g["norms"][1, 2, 7] == 0
 
 
-def test_dense_qjl_general_fp32_projection():
-    """An S that is not exactly fp16: the kernel adds the e_hi . S_lo pass."""
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_dense_qjl_general_fp32_projection(bits):
+    """An S that is not exactly fp16: the kernel adds the e_hi . S_lo pass
+    (these instances spill registers to scratch)."""
     inp = synth.make("long128k_qjl", T=200)
     S = np.random.default_rng(6).standard_normal((128, 128)).astype(np.float32)
     Q = rot(85)
-    ctx, g = run_dense_qjl(inp["k"], Q, S, 2, inp["signs_k"], inp["signs_v"])
-    check_dense_qjl(inp["k"], Q, S, 2, g)
+    ctx, g = run_dense_qjl(inp["k"], Q, S, bits, inp["signs_k"], inp["signs_v"])
+    print("bits=%d (code mismatches, sign mismatches) = %s" % (bits, check_dense_qjl(inp["k"], Q, S, bits, g)))
 
 
 def test_dense_qjl_full_size_sampled():

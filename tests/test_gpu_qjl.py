@@ -118,12 +118,15 @@ def test_qjl_quantize_ragged(bits):
     print("boundary sign mismatches", check_qjl(inp, bits, inp["S"], o))
 
 
-def test_qjl_general_fp32_projection():
-    """S not representable in fp16: the kernel adds the e_hi * S_lo pass."""
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_qjl_general_fp32_projection(bits):
+    """S not representable in fp16: the kernel adds the e_hi * S_lo pass
+    (at b = 3 that instance spills two registers to scratch)."""
     inp = synth.make("long128k_qjl", T=300)
     S = np.random.default_rng(5).standard_normal((128, 128)).astype(np.float32)
-    ctx, o, _ = run_qjl(inp, 2, S)
-    check_qjl(inp, 2, S, o)
+    ctx, o, _ = run_qjl(inp, bits, S)
+    check_codes(inp["k"], inp["signs_k"], bits, o["codes"], o["norms"], label="qjl codes, fp32 S")
+    check_qjl(inp, bits, S, o)
 
 
 def test_qjl_full_size_sampled():
