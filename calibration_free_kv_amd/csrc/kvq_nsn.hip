@@ -231,19 +231,23 @@ __global__ __launch_bounds__(kD * kMeanGroups) void k_nsn_mean(const float *__re
     }
 }
 
-// v = hi + lo (hi returned) with hi exactly representable in fp16: hi keeps the 11 leading
-// significant bits of v (values below the fp16 normal range go wholly to lo),
-// so its conversion is exact under any rounding and v - hi is exact in fp32;
-// only lo is rounded (|error| <= 2^-21 |v|).  Rounding hi to nearest instead
-// lets the compiler emit two different conversions for it (one for the stored
-// hi, one for the hi subtracted to form lo) that break exact ties differently,
-// leaving an error of one fp16 ulp.
-__device__ __forceinline__ _Float16 split_f16(float v, _Float16 &lo)
+// (v0, v1) = hi + lo as packed fp16 pairs.  hi is v truncated to fp16
+// (v_cvt_pkrtz: the 11 leading significant bits in the fp16 normal range, so
+// v - hi is exact in fp32), and lo = v - hi rounded once to fp16, formed by
+// mixed-precision FMAs from the packed hi itself: the hi that is subtracted is
+// the hi that is stored.  |hi + lo - v| <= 2^-21 |v| (2^-25 absolute below the
+// fp16 normal range).  Each pair costs one conversion and two FMAs.
+struct SplitPair {
+    uint32_t hi, lo;
+};
+__device__ __forceinline__ SplitPair split_pair(float v0, float v1)
 {
-    float h = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, v) & 0xFFFFE000u);
-    h = __builtin_fabsf(v) < 0x1p-14f ? 0.0f : h;
-    lo = (_Float16)(v - h);
-    return (_Float16)h;
+    const uint32_t hp = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(v0, v1));
+    uint32_t lp;
+    asm("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel:[0,0,0] op_sel_hi:[1,0,0]\n\t"
+        "v_fma_mixhi_f16 %0, %1, -1.0, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+        : "=&v"(lp) : "v"(hp), "v"(v0), "v"(v1));
+    return SplitPair{hp, lp};
 }
 
 // The 16 scores of one accumulator, each with its position r in its low
@@ -475,20 +479,15 @@ __device__ __forceinline__ void nsn_z(const uint32_t (&w)[32], const f4_t *oL, f
     }
     nb = __builtin_sqrtf(nb2);
     const float invb = nb2 > 0.0f ? 1.0f / nb : 0.0f;
-    // z = H b / ||b||: this half's four dims of each sub-vector as exact
-    // fp16 hi + lo
+    // z = H b / ||b||: this half's four dims of each sub-vector as fp16
+    // hi + lo pairs
 #pragma unroll
     for (int s = 0; s < 16; ++s) {
         const int base = 8 * (s & 7) + 4 * (s >> 3);
-        h4_t hv, lv;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            _Float16 lo;
-            hv[j] = split_f16(y[base + j] * invb, lo);
-            lv[j] = lo;
-        }
-        zh[s] = __builtin_bit_cast(u2_t, hv);
-        zl[s] = __builtin_bit_cast(u2_t, lv);
+        const SplitPair p01 = split_pair(y[base] * invb, y[base + 1] * invb);
+        const SplitPair p23 = split_pair(y[base + 2] * invb, y[base + 3] * invb);
+        zh[s] = u2_t{p01.hi, p23.hi};
+        zl[s] = u2_t{p01.lo, p23.lo};
     }
 }
 
@@ -929,15 +928,9 @@ __global__ __launch_bounds__(kWavesN * 64) __attribute__((amdgpu_waves_per_eu(2,
                     r[2 * d] = fma_h<0>(ng, sld, fma_h<0>(ng, shd, h2f_sum<0>(zhd, zld)));
                     r[2 * d + 1] = fma_h<1>(ng, sld, fma_h<1>(ng, shd, h2f_sum<1>(zhd, zld)));
                 }
-                h4_t rh, rl;
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    _Float16 lo;
-                    rh[k] = split_f16(r[k], lo);
-                    rl[k] = lo;
-                }
-                zh[s] = __builtin_bit_cast(u2_t, rh);
-                zl[s] = __builtin_bit_cast(u2_t, rl);
+                const SplitPair p01 = split_pair(r[0], r[1]), p23 = split_pair(r[2], r[3]);
+                zh[s] = u2_t{p01.hi, p23.hi};
+                zl[s] = u2_t{p01.lo, p23.lo};
             }
         }
         gsrq_search(sh2, sl2, zh, zl, v, h, upper, j2, p);
