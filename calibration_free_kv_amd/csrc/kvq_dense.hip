@@ -239,15 +239,22 @@ __device__ __forceinline__ float bucket_centroid(float a, float y, const float *
     return y > 0.0f ? m : -m;
 }
 
-// v = hi + lo with hi the 11 leading significant bits of v (exact in fp16 under
-// any rounding; values below the fp16 normal range go wholly to lo), lo = v - hi
-// exact in fp32 and rounded once to fp16.
-__device__ __forceinline__ _Float16 split_hi_lo(float v, _Float16 &lo)
+// (v0, v1) = hi + lo as packed fp16 pairs: hi = v truncated to fp16 by one
+// round-toward-zero conversion (v - hi is then exact in fp32), lo = v - hi
+// rounded once to fp16 by two mixed-precision FMAs that read the packed hi
+// itself, so the hi subtracted is the hi stored.  |hi + lo - v| <= 2^-21 |v|
+// (2^-25 absolute below the fp16 normal range); three instructions per pair.
+struct SplitPair {
+    uint32_t hi, lo;
+};
+__device__ __forceinline__ SplitPair split_pair(float v0, float v1)
 {
-    float h = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, v) & 0xFFFFE000u);
-    h = __builtin_fabsf(v) < 0x1p-14f ? 0.0f : h;
-    lo = (_Float16)(v - h);
-    return (_Float16)h;
+    const uint32_t hp = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(v0, v1));
+    uint32_t lp;
+    asm("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel:[0,0,0] op_sel_hi:[1,0,0]\n\t"
+        "v_fma_mixhi_f16 %0, %1, -1.0, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+        : "=&v"(lp) : "v"(hp), "v"(v0), "v"(v1));
+    return SplitPair{hp, lp};
 }
 
 struct DenseMags {
@@ -348,19 +355,20 @@ __global__ __launch_bounds__(64 * kDenseWaves) void k_quantize_dense_qjl(
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 uint32_t pc = 0u;
-                _Float16 hv[8], lv[8];
+                float ev[8];
 #pragma unroll
                 for (int u = 0; u < 8; ++u) {
                     const float y = D[2 * j + (u >> 2)][u & 3];
                     pc |= bucket_idx<BITS>(y, ps) << (BITS * u);
-                    const float e = y * inv - bucket_centroid<BITS>(__builtin_fabsf(y), y, ps, Mg.m);
-                    e2 = fmaf(e, e, e2);
-                    _Float16 lo;
-                    hv[u] = split_hi_lo(e, lo);
-                    lv[u] = lo;
+                    ev[u] = y * inv - bucket_centroid<BITS>(__builtin_fabsf(y), y, ps, Mg.m);
+                    e2 = fmaf(ev[u], ev[u], e2);
                 }
-                eh[j] = __builtin_bit_cast(u4_t, h8_t{hv[0], hv[1], hv[2], hv[3], hv[4], hv[5], hv[6], hv[7]});
-                el[j] = __builtin_bit_cast(u4_t, h8_t{lv[0], lv[1], lv[2], lv[3], lv[4], lv[5], lv[6], lv[7]});
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const SplitPair sp = split_pair(ev[2 * u], ev[2 * u + 1]);
+                    eh[j][u] = sp.hi;
+                    el[j][u] = sp.lo;
+                }
                 const int off = BITS * (4 * j + kg);
                 if constexpr (BITS == 4) {
                     *reinterpret_cast<uint32_t *>(row + off) = pc;
