@@ -64,7 +64,7 @@ typedef struct kvq_ctx kvq_ctx;
 typedef enum {
     KVQ_OK = 0,
     KVQ_E_INVAL = 1,       /* bad pointer, size, shape or combination      */
-    KVQ_E_UNSUPPORTED = 2, /* valid request this build does not implement  */
+    KVQ_E_UNSUPPORTED = 2, /* valid request the library does not implement */
     KVQ_E_DEVICE = 3,      /* no usable GPU, or a HIP runtime/launch error   */
     KVQ_E_NOMEM = 4,       /* host or device allocation failed              */
     KVQ_E_WORKSPACE = 5    /* caller workspace smaller than required        */
